@@ -1,0 +1,356 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU oracle for paged-KV decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or
+ * calls this file; only the tests, the smoke check and the CPU-baseline leg
+ * of the benchmark do.  It shares no code, header, table or constant with
+ * the HIP library.
+ *
+ * What it computes (one query token per head, exact attention):
+ *   FlashInfer README, "core features" item 1: single/batch attention over
+ *   sparse (paged) or dense KV storage; "vector-sparse" = page size 1.
+ *   Dao-AILab/flash-attention summary, "How it works": the method is EXACT
+ *   attention, so the plain definition softmax(q.K^T * scale).V is the
+ *   reference and every faster schedule may only change rounding.
+ *   hysenlabs review, "Installing FlashInfer and running a first decode":
+ *   q is [num_qo_heads, head_dim], k and v are [kv_len, num_kv_heads,
+ *   head_dim]; here K/V live in pages [num_pages][page_size][Hkv][D] that a
+ *   request reaches through kv_indptr / kv_indices / last_page_len (the
+ *   paged-call vocabulary of the "Pre-compiled cubins for FlashInfer"
+ *   registry quickstart).
+ *   FlashInfer README, "core features" item 3: grouped-query heads share a
+ *   kv head (head-query fusion), low-precision KV, cascade attention over a
+ *   hierarchical (shared prefix + per-request suffix) KV cache.
+ *
+ * Readings of points the pages leave open (each one is listed in the design
+ * notes as well):
+ *   - q head j reads kv head j / G with G = Hq / Hkv (contiguous groups);
+ *   - logical token t of a request lives in page kv_indices[indptr[r] + t/ps]
+ *     at slot t mod ps; the last page holds last_page_len[r] valid tokens;
+ *   - lse is the natural-log log-sum-exp of the scaled scores;
+ *   - an empty request gives o = 0, lse = -inf;
+ *   - fp8 is OCP E4M3FN (bias 7, max 448, S.1111.111 is NaN, no inf),
+ *     dequantised value = decode(code) * scale[kv_head];
+ *   - softmax is taken in two passes (max, then sums), in fp64, with dot
+ *     products summed over d in ascending order.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* dtype codes used by this file's own entry points */
+enum { OR_F16 = 0, OR_BF16 = 1, OR_E4M3 = 2, OR_F32 = 3, OR_F64 = 4 };
+
+/* ---- scalar decoders, written from the format definitions ---------------- */
+
+/* IEEE 754 binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+double oracle_f16_to_f64(uint16_t h) {
+  int s = (h >> 15) & 1, e = (h >> 10) & 0x1f, f = h & 0x3ff;
+  double v;
+  if (e == 0)
+    v = ldexp((double)f, -24); /* subnormal: f * 2^-14 * 2^-10 */
+  else if (e == 31)
+    v = f ? NAN : INFINITY;
+  else
+    v = ldexp(1.0 + (double)f / 1024.0, e - 15);
+  return s ? -v : v;
+}
+
+/* bfloat16: the upper 16 bits of an IEEE binary32 (8 exponent bits, bias
+ * 127, 7 fraction bits). */
+double oracle_bf16_to_f64(uint16_t b) {
+  int s = (b >> 15) & 1, e = (b >> 7) & 0xff, f = b & 0x7f;
+  double v;
+  if (e == 0)
+    v = ldexp((double)f, -133); /* f * 2^-126 * 2^-7 */
+  else if (e == 255)
+    v = f ? NAN : INFINITY;
+  else
+    v = ldexp(1.0 + (double)f / 128.0, e - 127);
+  return s ? -v : v;
+}
+
+/* OCP 8-bit float E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits; the
+ * all-ones exponent still encodes normal numbers except mantissa 111 (NaN);
+ * there is no infinity.  Largest finite value 1.75 * 2^8 = 448. */
+double oracle_e4m3_to_f64(uint8_t c) {
+  int s = (c >> 7) & 1, e = (c >> 3) & 0xf, m = c & 0x7;
+  double v;
+  if (e == 15 && m == 7)
+    return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9); /* m/8 * 2^(1-7) */
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+static double load_elem(const void* base, int dtype, int64_t i) {
+  switch (dtype) {
+    case OR_F16: return oracle_f16_to_f64(((const uint16_t*)base)[i]);
+    case OR_BF16: return oracle_bf16_to_f64(((const uint16_t*)base)[i]);
+    case OR_E4M3: return oracle_e4m3_to_f64(((const uint8_t*)base)[i]);
+    case OR_F32: return (double)((const float*)base)[i];
+    default: return ((const double*)base)[i];
+  }
+}
+
+/* ---- the page-table walk --------------------------------------------------
+ * Number of valid tokens of request r: (n_pages - 1) * ps + last_page_len,
+ * or 0 when the request owns no page. */
+static int64_t request_len(const int32_t* indptr, const int32_t* last, int r,
+                           int ps) {
+  int64_t n = (int64_t)indptr[r + 1] - indptr[r];
+  return n == 0 ? 0 : (n - 1) * ps + last[r];
+}
+
+/* Physical token slot (page * ps + slot) of logical token t of request r. */
+static int64_t token_slot(const int32_t* indptr, const int32_t* indices,
+                          int r, int64_t t, int ps) {
+  int64_t page = indices[indptr[r] + t / ps];
+  return page * ps + t % ps;
+}
+
+/* Writes the physical slot of every logical token of every request, in
+ * request order then token order; returns the number written.  Test hook
+ * that the GPU gather is compared against bit for bit. */
+int64_t oracle_gather_map(int batch, int page_size, const int32_t* kv_indptr,
+                          const int32_t* kv_indices,
+                          const int32_t* last_page_len, int64_t* out) {
+  int64_t k = 0;
+  for (int r = 0; r < batch; ++r) {
+    int64_t L = request_len(kv_indptr, last_page_len, r, page_size);
+    for (int64_t t = 0; t < L; ++t)
+      out[k++] = token_slot(kv_indptr, kv_indices, r, t, page_size);
+  }
+  return k;
+}
+
+/* ---- one (query row, key list) attention, the plain definition -----------
+ * x_t = sm_scale * sum_d q[d] * k_t[d]   (d ascending)
+ * M = max_t x_t ; l = sum_t exp(x_t - M) ; o[d] = sum_t exp(x_t - M) v_t[d] / l
+ * lse = M + ln l ; empty key list: o = 0, lse = -inf.
+ * Keys are given as element offsets (of the first element of each row) into
+ * the K and V pools. */
+typedef struct {
+  const void* k_pool;
+  const void* v_pool;
+  int kv_dtype;
+  int D;
+  double k_scale, v_scale;
+} kv_src;
+
+static void attend_row(const double* q, const int64_t* row_off, int64_t L,
+                       const kv_src* src, double sm_scale, double* x /*[L]*/,
+                       double* o, double* lse) {
+  const int D = src->D;
+  for (int d = 0; d < D; ++d) o[d] = 0.0;
+  if (L == 0) {
+    *lse = -INFINITY;
+    return;
+  }
+  double M = -INFINITY;
+  for (int64_t t = 0; t < L; ++t) {
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d)
+      dot += q[d] * (load_elem(src->k_pool, src->kv_dtype, row_off[t] + d) *
+                     src->k_scale);
+    x[t] = sm_scale * dot;
+    if (x[t] > M) M = x[t];
+  }
+  double l = 0.0;
+  for (int64_t t = 0; t < L; ++t) {
+    double p = exp(x[t] - M);
+    l += p;
+    for (int d = 0; d < D; ++d)
+      o[d] += p * (load_elem(src->v_pool, src->kv_dtype, row_off[t] + d) *
+                   src->v_scale);
+  }
+  for (int d = 0; d < D; ++d) o[d] /= l;
+  *lse = M + log(l);
+}
+
+/* ---- batch driver ---------------------------------------------------------
+ * Work item = (request r, kv head h); a pool of threads takes items from an
+ * atomic counter.  The arithmetic of an item does not depend on which thread
+ * runs it. */
+typedef struct {
+  int batch, Hq, Hkv, D, ps, q_dtype, kv_dtype;
+  const void* q;
+  const void* k_pages;
+  const void* v_pages;
+  /* level 0: per-request table (always present) */
+  const int32_t *indptr, *indices, *last;
+  /* optional level 1: shared prefix per group of contiguous requests */
+  int n_groups;
+  const int32_t *qo_indptr, *p_indptr, *p_indices, *p_last;
+  const float *k_scale, *v_scale;
+  double sm_scale;
+  const uint8_t* unit_mask; /* [batch*Hkv] or NULL: 1 = compute this item */
+  double* o;                /* [batch][Hq][D] */
+  double* lse;              /* [batch][Hq] */
+  int64_t next;
+  int64_t max_len;
+} job_t;
+
+static int group_of(const job_t* J, int r) {
+  for (int g = 0; g < J->n_groups; ++g)
+    if (r >= J->qo_indptr[g] && r < J->qo_indptr[g + 1]) return g;
+  return -1;
+}
+
+static void run_item(const job_t* J, int r, int h, int64_t* rows, double* x,
+                     double* qv) {
+  const int G = J->Hq / J->Hkv, D = J->D;
+  int64_t L = 0;
+  /* key list = (prefix tokens of the request's group) ++ (its own tokens);
+   * decode has no mask, so the order only fixes the summation order. */
+  int g = J->n_groups > 0 ? group_of(J, r) : -1;
+  if (g >= 0) {
+    int64_t Lp = request_len(J->p_indptr, J->p_last, g, J->ps);
+    for (int64_t t = 0; t < Lp; ++t)
+      rows[L++] = (token_slot(J->p_indptr, J->p_indices, g, t, J->ps) *
+                       J->Hkv + h) * (int64_t)D;
+  }
+  int64_t Ls = request_len(J->indptr, J->last, r, J->ps);
+  for (int64_t t = 0; t < Ls; ++t)
+    rows[L++] = (token_slot(J->indptr, J->indices, r, t, J->ps) * J->Hkv + h) *
+                (int64_t)D;
+  kv_src src = {J->k_pages, J->v_pages, J->kv_dtype, D,
+                J->k_scale ? (double)J->k_scale[h] : 1.0,
+                J->v_scale ? (double)J->v_scale[h] : 1.0};
+  for (int j = h * G; j < (h + 1) * G; ++j) {
+    int64_t qo = ((int64_t)r * J->Hq + j) * D;
+    for (int d = 0; d < D; ++d) qv[d] = load_elem(J->q, J->q_dtype, qo + d);
+    attend_row(qv, rows, L, &src, J->sm_scale, x, J->o + qo,
+               J->lse + (int64_t)r * J->Hq + j);
+  }
+}
+
+static void* worker(void* arg) {
+  job_t* J = (job_t*)arg;
+  int64_t* rows = (int64_t*)malloc(sizeof(int64_t) * (J->max_len + 1));
+  double* x = (double*)malloc(sizeof(double) * (J->max_len + 1));
+  double* qv = (double*)malloc(sizeof(double) * J->D);
+  const int64_t n_items = (int64_t)J->batch * J->Hkv;
+  for (;;) {
+    int64_t it = __atomic_fetch_add(&J->next, 1, __ATOMIC_RELAXED);
+    if (it >= n_items) break;
+    if (J->unit_mask && !J->unit_mask[it]) continue;
+    run_item(J, (int)(it / J->Hkv), (int)(it % J->Hkv), rows, x, qv);
+  }
+  free(rows);
+  free(x);
+  free(qv);
+  return NULL;
+}
+
+static int run_job(job_t* J, int num_threads) {
+  if (J->Hkv <= 0 || J->Hq % J->Hkv != 0 || J->ps <= 0 || J->D <= 0) return -1;
+  J->max_len = 0;
+  for (int r = 0; r < J->batch; ++r) {
+    int64_t L = request_len(J->indptr, J->last, r, J->ps);
+    int g = J->n_groups > 0 ? group_of(J, r) : -1;
+    if (g >= 0) L += request_len(J->p_indptr, J->p_last, g, J->ps);
+    if (L > J->max_len) J->max_len = L;
+  }
+  J->next = 0;
+  if (num_threads < 1) num_threads = 1;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * num_threads);
+  int started = 0;
+  for (int i = 0; i < num_threads; ++i)
+    if (pthread_create(&th[i], NULL, worker, J) == 0) ++started;
+  if (started == 0) worker(J);
+  for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
+  free(th);
+  return 0;
+}
+
+/* Paged decode: o[b][j][:], lse[b][j] for every request b and q head j (or
+ * only for the (b, kv head) items unit_mask selects).  Returns 0 on success. */
+int oracle_decode(int batch, int num_qo_heads, int num_kv_heads, int head_dim,
+                  int page_size, int q_dtype, int kv_dtype, const void* q,
+                  const void* k_pages, const void* v_pages,
+                  const int32_t* kv_indptr, const int32_t* kv_indices,
+                  const int32_t* last_page_len, const float* k_scale,
+                  const float* v_scale, double sm_scale,
+                  const uint8_t* unit_mask, double* o, double* lse,
+                  int num_threads) {
+  job_t J;
+  memset(&J, 0, sizeof(J));
+  J.batch = batch; J.Hq = num_qo_heads; J.Hkv = num_kv_heads; J.D = head_dim;
+  J.ps = page_size; J.q_dtype = q_dtype; J.kv_dtype = kv_dtype;
+  J.q = q; J.k_pages = k_pages; J.v_pages = v_pages;
+  J.indptr = kv_indptr; J.indices = kv_indices; J.last = last_page_len;
+  J.k_scale = k_scale; J.v_scale = v_scale; J.sm_scale = sm_scale;
+  J.unit_mask = unit_mask; J.o = o; J.lse = lse;
+  return run_job(&J, num_threads);
+}
+
+/* Cascade decode: request r of group g (qo_indptr[g] <= r < qo_indptr[g+1])
+ * attends over the group's shared prefix pages followed by its own pages,
+ * i.e. exactly the flat decode over the concatenated key list. */
+int oracle_cascade(int batch, int num_qo_heads, int num_kv_heads, int head_dim,
+                   int page_size, int q_dtype, int kv_dtype, const void* q,
+                   const void* k_pages, const void* v_pages, int n_groups,
+                   const int32_t* prefix_qo_indptr,
+                   const int32_t* prefix_kv_indptr,
+                   const int32_t* prefix_kv_indices,
+                   const int32_t* prefix_last_page_len,
+                   const int32_t* kv_indptr, const int32_t* kv_indices,
+                   const int32_t* last_page_len, const float* k_scale,
+                   const float* v_scale, double sm_scale,
+                   const uint8_t* unit_mask, double* o, double* lse,
+                   int num_threads) {
+  job_t J;
+  memset(&J, 0, sizeof(J));
+  J.batch = batch; J.Hq = num_qo_heads; J.Hkv = num_kv_heads; J.D = head_dim;
+  J.ps = page_size; J.q_dtype = q_dtype; J.kv_dtype = kv_dtype;
+  J.q = q; J.k_pages = k_pages; J.v_pages = v_pages;
+  J.indptr = kv_indptr; J.indices = kv_indices; J.last = last_page_len;
+  J.n_groups = n_groups; J.qo_indptr = prefix_qo_indptr;
+  J.p_indptr = prefix_kv_indptr; J.p_indices = prefix_kv_indices;
+  J.p_last = prefix_last_page_len;
+  J.k_scale = k_scale; J.v_scale = v_scale; J.sm_scale = sm_scale;
+  J.unit_mask = unit_mask; J.o = o; J.lse = lse;
+  return run_job(&J, num_threads);
+}
+
+/* Merge of attention states over disjoint key sets.  Since
+ * exp(lse) = sum of exp(score) over the keys, the union of sets i has
+ * lse = M + ln sum_i exp(lse_i - M) with M = max_i lse_i, and
+ * o = sum_i exp(lse_i - lse) * o_i.  If every lse_i is -inf the union is
+ * empty: o = 0, lse = -inf.
+ * states: o_in [n_states][n_rows][D] (dtype v_dtype), lse_in [n_states][n_rows]
+ * (fp32 or fp64 per s_dtype); outputs fp64. */
+int oracle_merge(int n_states, int64_t n_rows, int D, int v_dtype,
+                 const void* o_in, int s_dtype, const void* lse_in,
+                 double* o_out, double* lse_out) {
+  for (int64_t row = 0; row < n_rows; ++row) {
+    double M = -INFINITY;
+    for (int i = 0; i < n_states; ++i) {
+      double s = load_elem(lse_in, s_dtype, (int64_t)i * n_rows + row);
+      if (s > M) M = s;
+    }
+    double* o = o_out + row * D;
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    if (M == -INFINITY) {
+      lse_out[row] = -INFINITY;
+      continue;
+    }
+    double sum = 0.0;
+    for (int i = 0; i < n_states; ++i)
+      sum += exp(load_elem(lse_in, s_dtype, (int64_t)i * n_rows + row) - M);
+    double lse = M + log(sum);
+    for (int i = 0; i < n_states; ++i) {
+      double w = exp(load_elem(lse_in, s_dtype, (int64_t)i * n_rows + row) - lse);
+      for (int d = 0; d < D; ++d)
+        o[d] += w * load_elem(o_in, v_dtype,
+                              ((int64_t)i * n_rows + row) * D + d);
+    }
+    lse_out[row] = lse;
+  }
+  return 0;
+}

@@ -1,0 +1,394 @@
+"""Pins of the fp64 oracle against facts fixed outside it (CPU only).
+
+Each test pins the oracle to something other than itself: format
+definitions, closed forms, an independent dense brute force, invariants of
+the definition of attention (page permutation, page size, split + merge),
+and planted structure (GQA head map, a dominant key, NaN-poisoned tails).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from tests.helpers import f16_values, paginate, to_f16_bits
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- decoders
+
+def test_f16_decoder_all_codes(oracle_lib):
+    codes = np.arange(65536, dtype=np.uint32)
+    ref = codes.astype(np.uint16).view(np.float16).astype(np.float64)
+    got = np.array([oracle_lib.decode_scalar(int(c), "f16") for c in codes])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+    assert np.array_equal(np.signbit(ref[~nan]), np.signbit(got[~nan]))
+
+
+def test_bf16_decoder_all_codes(oracle_lib):
+    import torch
+    codes = np.arange(65536, dtype=np.int32).astype(np.uint16)
+    ref = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).double().numpy()
+    got = np.array([oracle_lib.decode_scalar(int(c), "bf16") for c in codes])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+
+
+def test_e4m3_decoder_all_codes(oracle_lib):
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([oracle_lib.decode_scalar(int(c), "e4m3") for c in codes])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+
+
+def test_e4m3_spec_points(oracle_lib):
+    pts = json.load(open(os.path.join(GOLDEN, "e4m3_points.json")))["points"]
+    for p in pts:
+        v = oracle_lib.decode_scalar(p["code"], "e4m3")
+        if p["value"] == "nan":
+            assert math.isnan(v), p
+        else:
+            assert v == p["value"] and math.copysign(1, v) == math.copysign(1, p["value"]), p
+
+
+# ------------------------------------------------------ closed-form cases
+
+def _run_dense_as_paged(oracle_lib, q, k, v, sm_scale, ps=1, seed=0):
+    """q [Hq, D], k/v [L, Hkv, D] float values exactly representable in fp16."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    Hq, D = q.shape
+    Hkv = k.shape[1]
+    rng = np.random.default_rng(seed)
+    kp, indptr, idx, last = paginate([to_f16_bits(k)], ps, Hkv, D, rng)
+    vp, _, _, _ = paginate([to_f16_bits(v)], ps, Hkv, D, np.random.default_rng(seed))
+    return oracle_lib.decode(to_f16_bits(q)[None], kp, vp, indptr, idx, last,
+                             num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                             page_size=ps, q_dtype="f16", kv_dtype="f16",
+                             sm_scale=sm_scale)
+
+
+@pytest.mark.parametrize("ps", [1, 2, 16])
+def test_hand_cases(oracle_lib, ps):
+    cases = json.load(open(os.path.join(GOLDEN, "hand_cases.json")))["cases"]
+    for c in cases:
+        o, lse = _run_dense_as_paged(oracle_lib, c["q"], c["k"], c["v"], c["sm_scale"], ps=ps)
+        np.testing.assert_allclose(o[0], np.array(c["o"]), rtol=1e-14, atol=1e-14,
+                                   err_msg=c["name"])
+        np.testing.assert_allclose(lse[0], np.array(c["lse"]), rtol=1e-14, atol=1e-14,
+                                   err_msg=c["name"])
+
+
+def test_zero_query_gives_mean_and_log_len(oracle_lib):
+    rng = np.random.default_rng(3)
+    L, Hkv, D = 37, 2, 8
+    k = f16_values(rng.standard_normal((L, Hkv, D)))
+    v = f16_values(rng.standard_normal((L, Hkv, D)))
+    q = np.zeros((4, D))
+    o, lse = _run_dense_as_paged(oracle_lib, q, k, v, 0.3, ps=4)
+    for j in range(4):
+        np.testing.assert_allclose(o[0, j], v[:, j // 2, :].mean(0), rtol=1e-13, atol=1e-15)
+        assert abs(lse[0, j] - math.log(L)) < 1e-14
+
+
+def test_identical_keys_give_mean_and_shifted_lse(oracle_lib):
+    rng = np.random.default_rng(4)
+    L, D = 20, 8
+    krow = f16_values(rng.standard_normal(D))
+    k = np.tile(krow, (L, 1, 1))
+    v = f16_values(rng.standard_normal((L, 1, D)))
+    q = f16_values(rng.standard_normal((1, D)))
+    o, lse = _run_dense_as_paged(oracle_lib, q, k, v, 0.25, ps=16)
+    x = 0.25 * float(np.dot(q[0], krow))
+    np.testing.assert_allclose(o[0, 0], v[:, 0].mean(0), rtol=1e-13, atol=1e-15)
+    assert abs(lse[0, 0] - (x + math.log(L))) < 1e-13
+
+
+def test_empty_request(oracle_lib):
+    rng = np.random.default_rng(5)
+    D, Hkv = 8, 1
+    dense = [to_f16_bits(rng.standard_normal((5, Hkv, D))), np.zeros((0, Hkv, D), np.uint16)]
+    kp, indptr, idx, last = paginate(dense, 4, Hkv, D, rng)
+    q = to_f16_bits(rng.standard_normal((2, 2, D)))
+    o, lse = oracle_lib.decode(q, kp, kp, indptr, idx, last, num_qo_heads=2,
+                               num_kv_heads=1, head_dim=D, page_size=4,
+                               q_dtype="f16", kv_dtype="f16", sm_scale=0.5)
+    assert np.all(o[1] == 0) and np.all(np.isneginf(lse[1]))
+    assert np.all(np.isfinite(o[0])) and np.all(np.isfinite(lse[0]))
+
+
+# ------------------------------------------------- dense brute force pin
+
+def _random_problem(rng, B, Hq, Hkv, D, lens, ps, scale=0.1):
+    qf = rng.standard_normal((B, Hq, D)) * scale
+    ks = [rng.standard_normal((L, Hkv, D)) for L in lens]
+    vs = [rng.standard_normal((L, Hkv, D)) for L in lens]
+    return qf, ks, vs
+
+
+@pytest.mark.parametrize("ps", [1, 3, 16])
+def test_matches_dense_brute_force(oracle_lib, ps):
+    from oracle.dense import ref_dense
+    rng = np.random.default_rng(10 + ps)
+    B, Hq, Hkv, D = 4, 8, 2, 16
+    lens = [1, 13, 0, 40]
+    qf, ks, vs = _random_problem(rng, B, Hq, Hkv, D, lens, ps)
+    kb = [to_f16_bits(k) for k in ks]
+    vb = [to_f16_bits(v) for v in vs]
+    kp, indptr, idx, last = paginate(kb, ps, Hkv, D, np.random.default_rng(1))
+    vp, _, _, _ = paginate(vb, ps, Hkv, D, np.random.default_rng(1))
+    sm = 0.37
+    o, lse = oracle_lib.decode(to_f16_bits(qf), kp, vp, indptr, idx, last,
+                               num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                               page_size=ps, q_dtype="f16", kv_dtype="f16",
+                               sm_scale=sm)
+    for r in range(B):
+        ro, rl = ref_dense(f16_values(qf[r]), f16_values(ks[r]), f16_values(vs[r]), sm)
+        np.testing.assert_allclose(o[r], ro, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse[r], rl, rtol=1e-12, atol=1e-13)
+
+
+def test_bf16_and_e4m3_match_dense(oracle_lib):
+    """Same brute force with bf16 q / e4m3 K,V and per-head scales."""
+    import torch
+    from oracle.dense import bf16_bits_to_f64, ref_dense
+    rng = np.random.default_rng(21)
+    Hq, Hkv, D, L, ps = 4, 2, 32, 29, 4
+    qf = rng.standard_normal((1, Hq, D)).astype(np.float32) * 0.2
+    qb = torch.from_numpy(qf).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    kf = rng.standard_normal((L, Hkv, D)).astype(np.float32)
+    vf = rng.standard_normal((L, Hkv, D)).astype(np.float32)
+    ksc = np.array([0.01, 0.02], np.float32)
+    vsc = np.array([0.5, 0.125], np.float32)
+    kc = torch.from_numpy(kf / ksc[None, :, None]).clamp(-448, 448).to(torch.float8_e4m3fn)
+    vc = torch.from_numpy(vf / vsc[None, :, None]).clamp(-448, 448).to(torch.float8_e4m3fn)
+    kp, indptr, idx, last = paginate([kc.view(torch.uint8).numpy()], ps, Hkv, D,
+                                     np.random.default_rng(2), fill_bits=0x7F, dtype=np.uint8)
+    vp, _, _, _ = paginate([vc.view(torch.uint8).numpy()], ps, Hkv, D,
+                           np.random.default_rng(2), fill_bits=0x7F, dtype=np.uint8)
+    o, lse = oracle_lib.decode(qb, kp, vp, indptr, idx, last, num_qo_heads=Hq,
+                               num_kv_heads=Hkv, head_dim=D, page_size=ps,
+                               q_dtype="bf16", kv_dtype="e4m3", sm_scale=0.125,
+                               k_scale=ksc, v_scale=vsc)
+    kd = kc.double().numpy() * ksc.astype(np.float64)[None, :, None]
+    vd = vc.double().numpy() * vsc.astype(np.float64)[None, :, None]
+    ro, rl = ref_dense(bf16_bits_to_f64(qb[0]), kd, vd, 0.125)
+    np.testing.assert_allclose(o[0], ro, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse[0], rl, rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------- invariants
+
+def test_page_permutation_and_page_size_invariance(oracle_lib):
+    """The oracle sums in logical token order, so the physical layout cannot
+    change a single bit of the result."""
+    rng = np.random.default_rng(7)
+    Hq, Hkv, D = 8, 4, 32
+    lens = [50, 1, 17]
+    qf, ks, vs = _random_problem(rng, 3, Hq, Hkv, D, lens, 1, scale=1.0)
+    kb = [to_f16_bits(k) for k in ks]
+    vb = [to_f16_bits(v) for v in vs]
+    outs = []
+    for ps, seed in [(1, 0), (16, 0), (16, 99), (5, 3)]:
+        kp, indptr, idx, last = paginate(kb, ps, Hkv, D, np.random.default_rng(seed))
+        vp, _, _, _ = paginate(vb, ps, Hkv, D, np.random.default_rng(seed))
+        outs.append(oracle_lib.decode(to_f16_bits(qf), kp, vp, indptr, idx, last,
+                                      num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                                      page_size=ps, q_dtype="f16", kv_dtype="f16",
+                                      sm_scale=0.2))
+    for o, lse in outs[1:]:
+        assert np.array_equal(o, outs[0][0]) and np.array_equal(lse, outs[0][1])
+
+
+def test_gqa_head_map(oracle_lib):
+    """V of kv head h is the constant h: q head j must return (j // G)."""
+    rng = np.random.default_rng(8)
+    Hq, Hkv, D, L = 16, 4, 8, 9
+    k = to_f16_bits(rng.standard_normal((L, Hkv, D)))
+    v = to_f16_bits(np.broadcast_to(np.arange(Hkv, dtype=np.float64)[None, :, None], (L, Hkv, D)))
+    kp, indptr, idx, last = paginate([k], 4, Hkv, D, np.random.default_rng(11))
+    vp, _, _, _ = paginate([v], 4, Hkv, D, np.random.default_rng(11))
+    q = to_f16_bits(rng.standard_normal((1, Hq, D)))
+    o, _ = oracle_lib.decode(q, kp, vp, indptr, idx, last, num_qo_heads=Hq,
+                             num_kv_heads=Hkv, head_dim=D, page_size=4,
+                             q_dtype="f16", kv_dtype="f16", sm_scale=0.3)
+    for j in range(Hq):
+        np.testing.assert_allclose(o[0, j], j // (Hq // Hkv), rtol=1e-14)
+
+
+def test_dominant_key_returns_its_value(oracle_lib):
+    rng = np.random.default_rng(9)
+    Hkv, D, L, t_star = 1, 16, 333, 217
+    k = rng.standard_normal((L, Hkv, D)) * 0.01
+    q = np.zeros((1, D))
+    q[0, 3] = 8.0
+    k[t_star, 0, 3] = 8.0          # score 64*sm vs |others| < 1
+    v = rng.standard_normal((L, Hkv, D))
+    o, lse = _run_dense_as_paged(oracle_lib, q, f16_values(k), f16_values(v), 1.0, ps=16)
+    np.testing.assert_allclose(o[0, 0], f16_values(v)[t_star, 0], atol=1e-20)
+
+
+def test_nan_poisoned_tails_never_read(oracle_lib):
+    """Pool pages and tail slots hold NaN; a correct walk stays finite."""
+    rng = np.random.default_rng(12)
+    Hq, Hkv, D = 4, 2, 16
+    lens = [17, 33, 1, 16]
+    qf, ks, vs = _random_problem(rng, 4, Hq, Hkv, D, lens, 16)
+    kp, indptr, idx, last = paginate([to_f16_bits(k) for k in ks], 16, Hkv, D,
+                                     np.random.default_rng(5), pool_extra=10)
+    vp, _, _, _ = paginate([to_f16_bits(v) for v in vs], 16, Hkv, D,
+                           np.random.default_rng(5), pool_extra=10)
+    assert np.isnan(kp.view(np.float16)).any()
+    o, lse = oracle_lib.decode(to_f16_bits(qf), kp, vp, indptr, idx, last,
+                               num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                               page_size=16, q_dtype="f16", kv_dtype="f16",
+                               sm_scale=0.1)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+def test_scales_are_exact_factors(oracle_lib):
+    """k_scale = 2 equals sm_scale x 2 bit for bit; v_scale = 2 doubles o."""
+    rng = np.random.default_rng(13)
+    Hq, Hkv, D, L = 4, 2, 16, 30
+    qf, ks, vs = _random_problem(rng, 1, Hq, Hkv, D, [L], 1, scale=1.0)
+    import torch
+    kc = torch.from_numpy(ks[0].astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    vc = torch.from_numpy(vs[0].astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    kp, indptr, idx, last = paginate([kc], 4, Hkv, D, np.random.default_rng(3), fill_bits=0x7F, dtype=np.uint8)
+    vp, _, _, _ = paginate([vc], 4, Hkv, D, np.random.default_rng(3), fill_bits=0x7F, dtype=np.uint8)
+    common = dict(num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=4,
+                  q_dtype="f16", kv_dtype="e4m3")
+    one = np.ones(Hkv, np.float32)
+    two = np.full(Hkv, 2.0, np.float32)
+    qb = to_f16_bits(qf)
+    o1, l1 = oracle_lib.decode(qb, kp, vp, indptr, idx, last, sm_scale=0.5,
+                               k_scale=two, v_scale=one, **common)
+    o2, l2 = oracle_lib.decode(qb, kp, vp, indptr, idx, last, sm_scale=1.0,
+                               k_scale=one, v_scale=one, **common)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    o3, l3 = oracle_lib.decode(qb, kp, vp, indptr, idx, last, sm_scale=1.0,
+                               k_scale=one, v_scale=two, **common)
+    assert np.array_equal(o3, 2 * o2) and np.array_equal(l3, l2)
+
+
+# ------------------------------------------------------------------ merge
+
+def test_split_then_merge_equals_unsplit(oracle_lib):
+    """Attention over A ++ B equals the merge of the states over A and B."""
+    rng = np.random.default_rng(14)
+    Hq, Hkv, D, L = 8, 2, 16, 101
+    qf, ks, vs = _random_problem(rng, 1, Hq, Hkv, D, [L], 1, scale=1.0)
+    kb, vb = to_f16_bits(ks[0]), to_f16_bits(vs[0])
+    qb = to_f16_bits(qf)
+    common = dict(num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=1,
+                  q_dtype="f16", kv_dtype="f16", sm_scale=0.3)
+
+    def run(lo, hi):
+        kp, ip, ix, la = paginate([kb[lo:hi]], 1, Hkv, D, np.random.default_rng(0))
+        vp, _, _, _ = paginate([vb[lo:hi]], 1, Hkv, D, np.random.default_rng(0))
+        return oracle_lib.decode(qb, kp, vp, ip, ix, la, **common)
+
+    full_o, full_l = run(0, L)
+    cuts = [0, 10, 11, 64, L]
+    parts = [run(a, b) for a, b in zip(cuts[:-1], cuts[1:])]
+    os_ = np.stack([p[0][0] for p in parts])
+    ls_ = np.stack([p[1][0] for p in parts])
+    mo, ml = oracle_lib.merge(os_, ls_)
+    np.testing.assert_allclose(mo, full_o[0], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(ml, full_l[0], rtol=1e-13, atol=1e-14)
+
+
+def test_merge_identities(oracle_lib):
+    rng = np.random.default_rng(15)
+    o = rng.standard_normal((1, 5, 8))
+    lse = rng.standard_normal((1, 5))
+    # with an empty state (o = 0, lse = -inf): identity
+    o2 = np.concatenate([o, np.zeros_like(o)])
+    l2 = np.concatenate([lse, np.full_like(lse, -np.inf)])
+    mo, ml = oracle_lib.merge(o2, l2)
+    np.testing.assert_array_equal(mo, o[0])
+    np.testing.assert_array_equal(ml, lse[0])
+    # two equal states: o unchanged, lse + ln 2
+    mo, ml = oracle_lib.merge(np.concatenate([o, o]), np.concatenate([lse, lse]))
+    np.testing.assert_allclose(mo, o[0], rtol=1e-15)
+    np.testing.assert_allclose(ml, lse[0] + math.log(2), rtol=1e-15)
+    # all empty: o = 0, lse = -inf
+    mo, ml = oracle_lib.merge(np.zeros((3, 2, 4)), np.full((3, 2), -np.inf))
+    assert np.all(mo == 0) and np.all(np.isneginf(ml))
+    # order independence within rounding
+    a = rng.standard_normal((4, 3, 8))
+    al = rng.standard_normal((4, 3)) * 5
+    m1 = oracle_lib.merge(a, al)
+    m2 = oracle_lib.merge(a[::-1], al[::-1])
+    np.testing.assert_allclose(m1[0], m2[0], rtol=1e-13)
+    np.testing.assert_allclose(m1[1], m2[1], rtol=1e-14)
+
+
+# ---------------------------------------------------------------- cascade
+
+def test_cascade_equals_flat_concatenation(oracle_lib):
+    rng = np.random.default_rng(16)
+    Hq, Hkv, D, ps = 8, 2, 16, 4
+    groups = [(2, 9), (3, 0), (1, 20)]      # (n requests, prefix length)
+    B = sum(g[0] for g in groups)
+    suf = [5, 0, 7, 1, 12, 3]
+    pre_dense = [to_f16_bits(rng.standard_normal((L, Hkv, D))) for _, L in groups]
+    pre_vd = [to_f16_bits(rng.standard_normal((L, Hkv, D))) for _, L in groups]
+    suf_k = [to_f16_bits(rng.standard_normal((L, Hkv, D))) for L in suf]
+    suf_v = [to_f16_bits(rng.standard_normal((L, Hkv, D))) for L in suf]
+    # one pool holding prefixes then suffixes
+    kp, ip, ix, la = paginate(pre_dense + suf_k, ps, Hkv, D, np.random.default_rng(4))
+    vp, _, _, _ = paginate(pre_vd + suf_v, ps, Hkv, D, np.random.default_rng(4))
+    G = len(groups)
+    p_indptr = ip[:G + 1].copy()
+    p_indices = ix[:p_indptr[-1]]
+    p_last = la[:G]
+    s_indptr = (ip[G:] - ip[G]).astype(np.int32)
+    s_indices = ix[ip[G]:]
+    s_last = la[G:]
+    qo = np.concatenate([[0], np.cumsum([g[0] for g in groups])]).astype(np.int32)
+    q = to_f16_bits(rng.standard_normal((B, Hq, D)) * 0.5)
+    common = dict(num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=ps,
+                  q_dtype="f16", kv_dtype="f16", sm_scale=0.25)
+    co, cl = oracle_lib.cascade(q, kp, vp, qo, p_indptr, p_indices, p_last,
+                                s_indptr, s_indices, s_last, **common)
+    # flat: each request's table = its group's prefix pages ++ its own pages,
+    # laid out with page size 1 so the concatenation is exact token by token
+    r = 0
+    for g, (n, _) in enumerate(groups):
+        for _ in range(n):
+            kd = np.concatenate([pre_dense[g], suf_k[r]])
+            vd = np.concatenate([pre_vd[g], suf_v[r]])
+            kp1, ip1, ix1, la1 = paginate([kd], 1, Hkv, D, np.random.default_rng(r))
+            vp1, _, _, _ = paginate([vd], 1, Hkv, D, np.random.default_rng(r))
+            fo, fl = oracle_lib.decode(q[r:r + 1], kp1, vp1, ip1, ix1, la1,
+                                       **{**common, "page_size": 1})
+            assert np.array_equal(fo[0], co[r]) and np.array_equal(fl[0], cl[r])
+            r += 1
+
+
+def test_gather_map_matches_brute_force(oracle_lib):
+    rng = np.random.default_rng(17)
+    for ps in (1, 4, 16):
+        lens = rng.integers(0, 50, size=7)
+        n = (lens + ps - 1) // ps
+        indptr = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+        indices = rng.permutation(int(n.sum()) + 5)[:int(n.sum())].astype(np.int32)
+        last = np.where(n > 0, lens - (n - 1) * ps, 0).astype(np.int32)
+        got = oracle_lib.gather_map(ps, indptr, indices, last)
+        want = []
+        for r in range(len(lens)):
+            pages = indices[indptr[r]:indptr[r + 1]]
+            for p_i, p in enumerate(pages):
+                cnt = ps if p_i < len(pages) - 1 else last[r]
+                want.extend(int(p) * ps + s for s in range(cnt))
+        assert np.array_equal(got, np.array(want, np.int64))

@@ -1,0 +1,300 @@
+"""Seeded synthetic inputs for paged-KV decode attention.
+
+This module only PLACES random data: it draws request lengths, a shuffled
+page pool, q and K/V values, casts them to their storage dtype and writes K/V
+rows into pages through the page table.  It holds none of the attention
+arithmetic; both the oracle (tests) and the GPU path (tests, bench) consume
+what it returns.
+
+Workloads (names used everywhere else):
+
+=================== =====================================================
+single_L2048_h32    1 request, 32 q heads = 32 kv heads, D 128, kv_len 2048,
+                    fp16, page_size 16, 128 pages shuffled in a 256-page pool
+                    (the README's single-request decode example shape)
+batch64_gqa4        64 requests, 32 q / 8 kv heads, kv_len ~ U{512..4096},
+                    fp16, page_size 16, pool = 1.25 x pages used
+skewed128           128 requests, 32/8: 120 lengths round(lognormal(ln 512,
+                    0.5)) clipped to [64, 2048] + 8 of 32768 at random
+                    positions, fp16, page_size 16
+cascade256          256 requests, 64/8, bf16: one shared 8192-token prefix
+                    (512 pages) + own suffix ~ U{128..512}, page_size 16
+long32_fp8_ps{1,16} 32 requests, 64/8, kv_len 32768, K/V e4m3 with a per
+                    kv-head fp32 scale (amax/448), q bf16, page_size 1 or 16
+=================== =====================================================
+
+Value recipe: numpy PCG64 ``default_rng(seed)``; q, K, V ~ N(0, 1) drawn in
+fp32, rounded to nearest-even into fp16 (numpy) or bf16 (torch CPU); e4m3 via
+torch's float8_e4m3fn after clamping to +-448.  Pool pages no request owns and
+the slots after ``last_page_len`` in a request's last page hold NaN, so any
+read of them shows up in the outputs.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+NAN_BITS = {"f16": 0x7E00, "bf16": 0x7FC0, "e4m3": 0x7F}
+STORAGE = {"f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8}
+ESIZE = {"f16": 2, "bf16": 2, "e4m3": 1}
+
+
+def cast_bits(x: np.ndarray, dtype: str, scale: Optional[np.ndarray] = None):
+    """fp32 values -> raw storage bits of ``dtype`` (RNE)."""
+    x = np.asarray(x, np.float32)
+    if dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype == "bf16":
+        return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if dtype == "e4m3":
+        if scale is not None:
+            t = t / torch.from_numpy(np.asarray(scale, np.float32))
+        # torch's cast does not saturate (it gives NaN above 448): clamp first
+        t = t.clamp(-448.0, 448.0)
+        return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    raise ValueError(dtype)
+
+
+@dataclass
+class Paged:
+    """One paged decode problem, all arrays on the host."""
+    name: str
+    batch: int
+    num_qo_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    q_dtype: str
+    kv_dtype: str
+    q: np.ndarray                   # [B, Hq, D] raw bits
+    k_pages: np.ndarray             # [num_pages, ps, Hkv, D] raw bits
+    v_pages: np.ndarray
+    kv_indptr: np.ndarray           # int32 [B+1]
+    kv_indices: np.ndarray          # int32 [nnz pages]
+    last_page_len: np.ndarray       # int32 [B]
+    kv_lens: np.ndarray             # int64 [B] (per-request own tokens)
+    sm_scale: float
+    k_scale: Optional[np.ndarray] = None   # float32 [Hkv] (e4m3 only)
+    v_scale: Optional[np.ndarray] = None
+    # cascade level (None when absent)
+    prefix_qo_indptr: Optional[np.ndarray] = None
+    prefix_kv_indptr: Optional[np.ndarray] = None
+    prefix_kv_indices: Optional[np.ndarray] = None
+    prefix_last_page_len: Optional[np.ndarray] = None
+    prefix_lens: Optional[np.ndarray] = None
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def group_size(self) -> int:
+        return self.num_qo_heads // self.num_kv_heads
+
+    @property
+    def row_bytes(self) -> int:
+        return self.head_dim * ESIZE[self.kv_dtype]
+
+    def kv_bytes(self, cascade: bool = True) -> int:
+        """Algorithmic K+V bytes: valid tokens once per (token, kv head); a
+        shared prefix counts once when ``cascade`` (else once per request)."""
+        toks = int(self.kv_lens.sum())
+        if self.prefix_lens is not None:
+            if cascade:
+                toks += int(self.prefix_lens.sum())
+            else:
+                per_req = np.repeat(self.prefix_lens, np.diff(self.prefix_qo_indptr))
+                toks += int(per_req.sum())
+        return 2 * toks * self.num_kv_heads * self.row_bytes
+
+    def other_bytes(self) -> int:
+        """q + o + lse + page indices + scales."""
+        qo = 2 * self.batch * self.num_qo_heads * self.head_dim * ESIZE[self.q_dtype]
+        lse = 4 * self.batch * self.num_qo_heads
+        idx = 4 * (len(self.kv_indices) + len(self.kv_indptr) + len(self.last_page_len))
+        if self.prefix_kv_indices is not None:
+            idx += 4 * (len(self.prefix_kv_indices) + len(self.prefix_kv_indptr)
+                        + len(self.prefix_last_page_len) + len(self.prefix_qo_indptr))
+        sc = 0 if self.k_scale is None else 8 * self.num_kv_heads
+        return qo + lse + idx + sc
+
+
+def _pages_for(lens, ps):
+    n = (np.asarray(lens, np.int64) + ps - 1) // ps
+    last = np.where(n > 0, np.asarray(lens, np.int64) - (n - 1) * ps, 0)
+    # an empty request owns no page; its last_page_len is unused (0)
+    return n, last.astype(np.int32)
+
+
+def _scatter(pool, pages_of_req, L, ps, data):
+    """Write logical rows data[t] of one request into its pages."""
+    if L == 0:
+        return
+    t = np.arange(L)
+    pool[pages_of_req[t // ps], t % ps] = data
+
+
+def build(name, kv_lens, *, Hq, Hkv, D=128, ps=16, q_dtype="f16", kv_dtype="f16",
+          seed=0, pool_pages=None, pool_factor=1.25, prefix_len=None,
+          prefix_groups=None, extra_page_sizes=(), poison=True):
+    """General generator.
+
+    kv_lens: per-request own token counts.  prefix_len: if given, one shared
+    prefix (or ``prefix_groups`` = list of (n_requests, prefix_len) for several
+    groups of contiguous requests).  extra_page_sizes: also return the SAME
+    logical data laid out with these page sizes (dict in .meta['variants']).
+    Returns a Paged (or a dict of Paged by page size when extra sizes given).
+    """
+    rng = np.random.default_rng(seed)
+    kv_lens = np.asarray(kv_lens, np.int64)
+    B = len(kv_lens)
+    groups = []
+    if prefix_groups is not None:
+        groups = list(prefix_groups)
+    elif prefix_len is not None:
+        groups = [(B, int(prefix_len))]
+    assert sum(g[0] for g in groups) in (0, B)
+    seeds = np.random.SeedSequence(seed).spawn(4 + 2 * (B + len(groups)))
+    q_rng = np.random.default_rng(seeds[0])
+    qf = q_rng.standard_normal((B, Hq, D), dtype=np.float32)
+    q_bits = cast_bits(qf, q_dtype)
+
+    # logical rows of each key list: groups' prefixes first, then requests
+    lists = [("p", g, int(glen)) for g, (_, glen) in enumerate(groups)]
+    lists += [("r", r, int(kv_lens[r])) for r in range(B)]
+    list_seeds = {lst[:2]: (seeds[4 + 2 * i], seeds[5 + 2 * i])
+                  for i, lst in enumerate(lists)}
+
+    def logical(lst, which):
+        sk, sv = list_seeds[lst[:2]]
+        r = np.random.default_rng(sk if which == "k" else sv)
+        return r.standard_normal((lst[2], Hkv, D), dtype=np.float32)
+
+    k_scale = v_scale = None
+    if kv_dtype == "e4m3":
+        amax_k = np.zeros(Hkv, np.float32)
+        amax_v = np.zeros(Hkv, np.float32)
+        for lst in lists:
+            if lst[2] == 0:
+                continue
+            amax_k = np.maximum(amax_k, np.abs(logical(lst, "k")).max(axis=(0, 2)))
+            amax_v = np.maximum(amax_v, np.abs(logical(lst, "v")).max(axis=(0, 2)))
+        k_scale = (amax_k / np.float32(448.0)).astype(np.float32)
+        v_scale = (amax_v / np.float32(448.0)).astype(np.float32)
+
+    variants = {}
+    glens = np.array([g[1] for g in groups], np.int64)
+    for vi, ps_i in enumerate((ps,) + tuple(extra_page_sizes)):
+        n_req, last_req = _pages_for(kv_lens, ps_i)
+        if groups:
+            n_pre, last_pre = _pages_for(glens, ps_i)
+        else:
+            n_pre, last_pre = np.zeros(0, np.int64), np.zeros(0, np.int32)
+        used = int(n_req.sum() + n_pre.sum())
+        if pool_pages is not None and vi == 0:
+            P = int(pool_pages)
+        else:
+            P = int(math.ceil(used * pool_factor))
+        P = max(P, used, 1)
+        perm = np.random.default_rng([seed, 7919, ps_i]).permutation(P).astype(np.int32)
+        pre_pages, req_pages, off = [], [], 0
+        for g in range(len(groups)):
+            pre_pages.append(perm[off:off + n_pre[g]])
+            off += int(n_pre[g])
+        for r in range(B):
+            req_pages.append(perm[off:off + n_req[r]])
+            off += int(n_req[r])
+        st = STORAGE[kv_dtype]
+        fill = NAN_BITS[kv_dtype] if poison else 0
+        variants[ps_i] = dict(
+            n_req=n_req, last_req=last_req, n_pre=n_pre, last_pre=last_pre,
+            pre_pages=pre_pages, req_pages=req_pages,
+            kp=np.full((P, ps_i, Hkv, D), fill, st),
+            vp=np.full((P, ps_i, Hkv, D), fill, st))
+    # one pass over the logical key lists, scattered into every variant's pool
+    for lst in lists:
+        kind, idx, L = lst
+        if L == 0:
+            continue
+        kd, vd = logical(lst, "k"), logical(lst, "v")
+        if kv_dtype == "e4m3":
+            kb = cast_bits(kd, "e4m3", k_scale[None, :, None])
+            vb = cast_bits(vd, "e4m3", v_scale[None, :, None])
+        else:
+            kb, vb = cast_bits(kd, kv_dtype), cast_bits(vd, kv_dtype)
+        del kd, vd
+        for ps_i, V in variants.items():
+            pages = V["pre_pages"][idx] if kind == "p" else V["req_pages"][idx]
+            _scatter(V["kp"], pages, L, ps_i, kb)
+            _scatter(V["vp"], pages, L, ps_i, vb)
+    out = {}
+    for ps_i, V in variants.items():
+        kv_indptr = np.zeros(B + 1, np.int32)
+        kv_indptr[1:] = np.cumsum(V["n_req"])
+        kv_indices = (np.concatenate(V["req_pages"]) if B
+                      else np.zeros(0, np.int32)).astype(np.int32)
+        w = Paged(name=name if ps_i == ps else f"{name}_ps{ps_i}", batch=B,
+                  num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=ps_i,
+                  q_dtype=q_dtype, kv_dtype=kv_dtype, q=q_bits, k_pages=V["kp"],
+                  v_pages=V["vp"], kv_indptr=kv_indptr, kv_indices=kv_indices,
+                  last_page_len=V["last_req"], kv_lens=kv_lens.copy(),
+                  sm_scale=float(np.float32(1.0 / math.sqrt(D))),
+                  k_scale=k_scale, v_scale=v_scale)
+        if groups:
+            w.prefix_qo_indptr = np.concatenate(
+                [[0], np.cumsum([g[0] for g in groups])]).astype(np.int32)
+            w.prefix_kv_indptr = np.concatenate([[0], np.cumsum(V["n_pre"])]).astype(np.int32)
+            w.prefix_kv_indices = (np.concatenate(V["pre_pages"]) if V["pre_pages"]
+                                   else np.zeros(0, np.int32)).astype(np.int32)
+            w.prefix_last_page_len = V["last_pre"].astype(np.int32)
+            w.prefix_lens = glens
+        out[ps_i] = w
+    if extra_page_sizes:
+        return out
+    return out[ps]
+
+
+# ---- the named workloads ---------------------------------------------------
+
+WORKLOADS = ("single_L2048_h32", "batch64_gqa4", "skewed128", "cascade256",
+             "long32_fp8")
+
+
+def make(name: str, seed: Optional[int] = None, small: bool = False):
+    """Named workload at full size, or a SMALL variant with the same structure
+    (same heads, dtypes, page sizes, length mix shape; several tiles and a
+    ragged tail) that the oracle finishes in seconds.
+
+    long32_fp8 returns a dict {1: Paged, 16: Paged} with identical logical data.
+    """
+    idx = WORKLOADS.index(name)
+    seed = 1000 + idx if seed is None else seed
+    rng = np.random.default_rng(seed)
+    if name == "single_L2048_h32":
+        L = 300 if small else 2048
+        return build(name, [L], Hq=32, Hkv=32, ps=16, seed=seed,
+                     pool_pages=(40 if small else 256))
+    if name == "batch64_gqa4":
+        B, lo, hi = (6, 1, 600) if small else (64, 512, 4096)
+        lens = rng.integers(lo, hi + 1, size=B)
+        return build(name, lens, Hq=32, Hkv=8, ps=16, seed=seed)
+    if name == "skewed128":
+        nshort, nlong, cl, ch, mu, Llong = ((10, 2, 8, 256, math.log(64), 2048) if small
+                                            else (120, 8, 64, 2048, math.log(512), 32768))
+        short = np.clip(np.round(rng.lognormal(mu, 0.5, size=nshort)), cl, ch).astype(np.int64)
+        lens = np.concatenate([short, np.full(nlong, Llong, np.int64)])
+        lens = lens[rng.permutation(len(lens))]
+        return build(name, lens, Hq=32, Hkv=8, ps=16, seed=seed)
+    if name == "cascade256":
+        B, lo, hi, P = (8, 1, 100, 512) if small else (256, 128, 512, 8192)
+        lens = rng.integers(lo, hi + 1, size=B)
+        return build(name, lens, Hq=64, Hkv=8, ps=16, q_dtype="bf16",
+                     kv_dtype="bf16", seed=seed, prefix_len=P)
+    if name == "long32_fp8":
+        B, L = (3, 700) if small else (32, 32768)
+        return build(name, np.full(B, L, np.int64), Hq=64, Hkv=8, ps=16,
+                     q_dtype="bf16", kv_dtype="e4m3", seed=seed,
+                     extra_page_sizes=(1,))
+    raise KeyError(name)
