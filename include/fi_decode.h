@@ -1,0 +1,223 @@
+/*
+ * fi_decode.h -- C ABI of the MI355X (gfx950) paged-KV decode attention
+ * library (libfi_decode.so).
+ *
+ * The operation (FlashInfer README, "core features" items 1-3; hysenlabs
+ * review, "Installing FlashInfer and running a first decode"; flash-attention
+ * summary, "How it works"):
+ *   for every request r and query head j, one query token q[r][j][:] attends
+ *   over that request's keys with exact attention
+ *       x_t = sm_scale * q . k_t,
+ *       o   = sum_t softmax(x)_t * v_t,
+ *       lse = ln sum_t exp(x_t)          (natural log),
+ *   where q head j reads kv head j / G (G = num_qo_heads / num_kv_heads,
+ *   grouped-query heads fused so each K/V row is read once per kv head), and
+ *   the keys of request r are reached through a page table (the kv_indptr /
+ *   kv_indices / last_page_len vocabulary of the "Pre-compiled cubins for
+ *   FlashInfer" registry quickstart):
+ *       n_r = kv_indptr[r+1] - kv_indptr[r] pages,
+ *       kv_len_r = n_r == 0 ? 0 : (n_r - 1) * page_size + last_page_len[r],
+ *       logical token t lives in page kv_indices[kv_indptr[r] + t / page_size]
+ *       at slot t % page_size.
+ *   An empty request yields o = 0 and lse = -inf.
+ *
+ * Layouts (all row-major, all device pointers unless marked host):
+ *   q, o          [batch][num_qo_heads][head_dim], dtype q_dtype (o = q dtype)
+ *   lse           [batch][num_qo_heads] fp32 (may be NULL)
+ *   k_pages,
+ *   v_pages       [num_pages][page_size][num_kv_heads][head_dim] ("NHD"),
+ *                 dtype kv_dtype; separate K and V pools
+ *   k_scale,
+ *   v_scale       [num_kv_heads] fp32, required for E4M3 KV (dequantised
+ *                 value = decode(code) * scale[kv_head]), ignored otherwise
+ *
+ * Plan / run (FlashInfer README, "core features" item 2: the plan stage
+ * schedules variable-length work on the host to balance load; the run stage
+ * executes it): fi_plan() turns the host-side lengths into a work list of
+ * (request, kv head, token chunk) tiles and uploads it into a caller-owned
+ * device workspace; fi_decode_run() / fi_cascade_decode() then only enqueue
+ * kernels on the caller's stream -- no allocation, no synchronisation, no
+ * host reads -- so they may be captured into a hipGraph (README "core
+ * features" item 5).  Re-plan whenever kv_indptr or last_page_len change;
+ * kv_indices contents and K/V data may change freely between runs.
+ *
+ * Ownership: the caller owns every device buffer and the stream.  The
+ * library owns only the plan object (host memory plus a pinned staging
+ * buffer), released by fi_plan_destroy() once the stream that fi_plan()
+ * used has been synchronised.
+ *
+ * Errors: every call returns an fi_status; nothing aborts, throws or prints
+ * across the ABI.  Arguments are validated on the host before anything is
+ * enqueued; on error nothing is launched and outputs are untouched, and
+ * fi_last_error() returns a thread-local message.  Device-resident indices
+ * (kv_indices, and the device copies of kv_indptr / last_page_len) are
+ * trusted: they must describe the same tables that were planned.
+ *
+ * Supported: head_dim 128; q in fp16 or bf16; KV in the q dtype or OCP E4M3
+ * (e4m3fn); 1 <= num_qo_heads / num_kv_heads <= 16; any page_size >= 1.
+ */
+#ifndef FI_DECODE_H_
+#define FI_DECODE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FI_OK = 0,
+  FI_ERR_INVALID_ARG = 1,         /* bad pointer, shape or table */
+  FI_ERR_UNSUPPORTED = 2,         /* valid but not built (dtype, head_dim, G) */
+  FI_ERR_WORKSPACE_TOO_SMALL = 3, /* *workspace_needed says how much */
+  FI_ERR_HIP = 4                  /* a HIP runtime call failed */
+} fi_status;
+
+typedef enum {
+  FI_F16 = 0,
+  FI_BF16 = 1,
+  FI_E4M3 = 2, /* OCP 8-bit E4M3FN: bias 7, max 448, S.1111.111 = NaN */
+  FI_F32 = 3
+} fi_dtype;
+
+/* Problem description; every pointer here is HOST memory, read during the
+ * fi_plan() call only. */
+typedef struct {
+  int32_t batch;          /* number of requests B >= 0 */
+  int32_t num_qo_heads;   /* Hq */
+  int32_t num_kv_heads;   /* Hkv, divides Hq */
+  int32_t head_dim;       /* D (128) */
+  int32_t page_size;      /* tokens per page, >= 1 */
+  fi_dtype q_dtype;       /* FI_F16 or FI_BF16; o has this dtype */
+  fi_dtype kv_dtype;      /* q_dtype or FI_E4M3 */
+  const int32_t* kv_indptr;     /* host [B+1], non-decreasing, [0] = 0 */
+  const int32_t* last_page_len; /* host [B], in [1, page_size] for non-empty */
+  /* Optional cascade level (FlashInfer README "core features" item 3 and the
+   * "Cascade Inference: shared prefix batch decoding" news item): requests
+   * are split into num_prefix_groups groups of CONTIGUOUS requests; group g
+   * = requests [prefix_qo_indptr[g], prefix_qo_indptr[g+1]) shares the prefix
+   * pages prefix_kv_indices[prefix_kv_indptr[g] ..) that precede each
+   * request's own pages.  0 groups = plain decode. */
+  int32_t num_prefix_groups;
+  const int32_t* prefix_qo_indptr;     /* host [groups+1], [0]=0, [groups]=B */
+  const int32_t* prefix_kv_indptr;     /* host [groups+1] */
+  const int32_t* prefix_last_page_len; /* host [groups] */
+  /* Tuning knob: tokens per split chunk (multiple of 32), 0 = automatic. */
+  int32_t chunk_tokens;
+} fi_problem;
+
+typedef struct fi_plan_s* fi_plan_t;
+
+/* Plan statistics, for tests and benchmarks. */
+typedef struct {
+  int64_t num_tiles;         /* decode work-list entries (workgroups) */
+  int64_t num_prefix_tiles;  /* cascade prefix work-list entries */
+  int64_t num_partials;      /* partial (o, lse) states written by tiles */
+  int64_t num_merge_units;   /* requests whose states are merged */
+  int32_t chunk_tokens;      /* split chunk chosen (tokens) */
+  int32_t prefix_chunk_tokens;
+  int32_t heads_per_tile;    /* kv heads one decode workgroup handles */
+  int32_t num_cus;
+  size_t workspace_bytes;
+} fi_plan_stats;
+
+/* Plan stage (FlashInfer README "core features" item 2).
+ * problem:        host description above.
+ * num_cus:        compute units to balance for; 0 = query the current device.
+ * workspace:      device buffer the plan's work list, merge map and partial
+ *                 states live in; NULL = only report the size needed.
+ * workspace_bytes: its size.
+ * workspace_needed: out (may be NULL): bytes the plan needs.
+ * stream:         hipStream_t the work list is uploaded on (NULL = default).
+ * plan_out:       out: the plan (NULL when workspace is NULL).
+ * Returns FI_ERR_WORKSPACE_TOO_SMALL (and sets *workspace_needed) when the
+ * workspace is too small.  The workspace must stay allocated and untouched
+ * by the caller while the plan is in use. */
+fi_status fi_plan(const fi_problem* problem, int32_t num_cus, void* workspace,
+                  size_t workspace_bytes, size_t* workspace_needed,
+                  void* stream, fi_plan_t* plan_out);
+
+/* Releases a plan (host memory only).  Synchronise the stream first. */
+fi_status fi_plan_destroy(fi_plan_t plan);
+
+/* Fills *stats (host) for a plan. */
+fi_status fi_plan_get_stats(fi_plan_t plan, fi_plan_stats* stats);
+
+/* Run stage: batch paged decode (FlashInfer README "core features" items 1
+ * and 3: paged / vector-sparse attention, head-query fusion for GQA,
+ * low-precision KV).  The plan must have been made without a cascade level.
+ * kv_indptr, kv_indices, last_page_len are DEVICE copies of the planned
+ * table.  sm_scale <= 0 selects 1/sqrt(head_dim).  lse may be NULL.
+ * Enqueues 1-2 kernels on stream. */
+fi_status fi_decode_run(fi_plan_t plan, const void* q, const void* k_pages,
+                        const void* v_pages, const int32_t* kv_indptr,
+                        const int32_t* kv_indices,
+                        const int32_t* last_page_len, const float* k_scale,
+                        const float* v_scale, float sm_scale, void* o,
+                        float* lse, void* stream);
+
+/* Run stage: cascade decode (README "core features" item 3, Cascade
+ * Attention for a hierarchical KV cache): every request attends over its
+ * group's shared prefix pages followed by its own pages; the prefix is read
+ * once per (group, kv head) for all the group's query rows and the two
+ * attention states are merged.  The plan must have been made with the same
+ * cascade level.  prefix_* and kv_* are DEVICE copies of the planned tables.
+ * Enqueues 2-3 kernels on stream. */
+fi_status fi_cascade_decode(fi_plan_t plan, const void* q, const void* k_pages,
+                            const void* v_pages,
+                            const int32_t* prefix_kv_indptr,
+                            const int32_t* prefix_kv_indices,
+                            const int32_t* prefix_last_page_len,
+                            const int32_t* kv_indptr,
+                            const int32_t* kv_indices,
+                            const int32_t* last_page_len,
+                            const float* k_scale, const float* v_scale,
+                            float sm_scale, void* o, float* lse, void* stream);
+
+/* Merge of attention states computed over DISJOINT key sets of the same
+ * query rows (the split-KV / cascade recombination): with
+ * M = max_i s_i, s = M + ln sum_i exp(s_i - M), v = sum_i exp(s_i - s) * v_i;
+ * all s_i = -inf gives v = 0, s = -inf.
+ * num_states:  1..64 states.
+ * v_states:    HOST array of num_states DEVICE pointers, each [num_rows][head_dim]
+ *              of v_dtype (FI_F16, FI_BF16 or FI_F32).
+ * s_states:    HOST array of num_states DEVICE pointers, each [num_rows] fp32
+ *              natural-log lse.
+ * v_out:       DEVICE [num_rows][head_dim] of out_dtype; s_out DEVICE
+ *              [num_rows] fp32 (may be NULL).  Rows are e.g. batch x heads.
+ * Enqueues one kernel. */
+fi_status fi_merge_states(int32_t num_states, const void* const* v_states,
+                          const float* const* s_states, int64_t num_rows,
+                          int32_t head_dim, fi_dtype v_dtype, void* v_out,
+                          float* s_out, fi_dtype out_dtype, void* stream);
+
+/* Human-readable name of a status, and the calling thread's last error. */
+const char* fi_status_string(fi_status status);
+const char* fi_last_error(void);
+
+/* ---- test hooks --------------------------------------------------------
+ * fi_debug_plan_tiles: runs the plan scheduler on the host only (no device
+ * touched) and copies the decode work list into tiles_out (host, int32,
+ * 8 words per tile: request, first kv head, t0, t1, partial slot base or -1,
+ * kind, row0, row1); *num_tiles = entries.  If capacity_tiles is too small
+ * only the count is returned.  prefix tiles follow the decode tiles. */
+fi_status fi_debug_plan_tiles(const fi_problem* problem, int32_t num_cus,
+                              int32_t* tiles_out, int64_t capacity_tiles,
+                              int64_t* num_tiles);
+
+/* fi_debug_gather: for every logical token of every request (request-major)
+ * writes its physical token slot page * page_size + slot to out_slots
+ * (device int64 [total tokens]) using the same device page walk the decode
+ * kernel uses.  token_indptr: device [batch+1] exclusive scan of kv_len. */
+fi_status fi_debug_gather(int32_t batch, int32_t page_size,
+                          const int32_t* kv_indptr, const int32_t* kv_indices,
+                          const int32_t* last_page_len,
+                          const int64_t* token_indptr, int64_t* out_slots,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FI_DECODE_H_ */

@@ -1,0 +1,317 @@
+"""Python binding of libfi_decode.so (argument marshalling only).
+
+Every step of the decode path runs in the HIP kernels behind the C ABI
+declared in include/fi_decode.h; torch only provides device memory and the
+current stream.  There is no fallback: if the shared library is missing,
+importing this package raises.
+
+    plan = Plan(kv_indptr_host, last_page_len_host, num_qo_heads=32,
+                num_kv_heads=8, page_size=16, q_dtype="f16", kv_dtype="f16")
+    o, lse = plan.run(q, k_pages, v_pages, kv_indptr, kv_indices, last_page_len)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfi_decode.so")
+
+DTYPES = {"f16": 0, "bf16": 1, "e4m3": 2, "f32": 3}
+STATUS = {0: "FI_OK", 1: "FI_ERR_INVALID_ARG", 2: "FI_ERR_UNSUPPORTED",
+          3: "FI_ERR_WORKSPACE_TOO_SMALL", 4: "FI_ERR_HIP"}
+EXPORTS = ("fi_plan", "fi_plan_destroy", "fi_plan_get_stats", "fi_decode_run",
+           "fi_cascade_decode", "fi_merge_states", "fi_status_string",
+           "fi_last_error", "fi_debug_plan_tiles", "fi_debug_gather")
+
+
+class FiError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_qo_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("q_dtype", ctypes.c_int),
+                ("kv_dtype", ctypes.c_int), ("kv_indptr", ctypes.c_void_p),
+                ("last_page_len", ctypes.c_void_p),
+                ("num_prefix_groups", ctypes.c_int32),
+                ("prefix_qo_indptr", ctypes.c_void_p),
+                ("prefix_kv_indptr", ctypes.c_void_p),
+                ("prefix_last_page_len", ctypes.c_void_p),
+                ("chunk_tokens", ctypes.c_int32)]
+
+
+class PlanStats(ctypes.Structure):
+    _fields_ = [("num_tiles", ctypes.c_int64), ("num_prefix_tiles", ctypes.c_int64),
+                ("num_partials", ctypes.c_int64), ("num_merge_units", ctypes.c_int64),
+                ("chunk_tokens", ctypes.c_int32), ("prefix_chunk_tokens", ctypes.c_int32),
+                ("heads_per_tile", ctypes.c_int32), ("num_cus", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+def _load() -> ctypes.CDLL:
+    # torch ships its own HIP runtime under the same soname (libamdhip64.so.7).
+    # Load it first so this library binds to that one runtime: device
+    # pointers and hipStream_t handles from torch are then valid here.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built: run `python -m paged_kv_decode_fi_amd.build` "
+            "(there is no non-HIP fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    F = ctypes.c_float
+    L.fi_plan.restype = ctypes.c_int
+    L.fi_plan.argtypes = [ctypes.POINTER(Problem), I32, P, SZ, ctypes.POINTER(SZ), P,
+                          ctypes.POINTER(P)]
+    L.fi_plan_destroy.restype = ctypes.c_int
+    L.fi_plan_destroy.argtypes = [P]
+    L.fi_plan_get_stats.restype = ctypes.c_int
+    L.fi_plan_get_stats.argtypes = [P, ctypes.POINTER(PlanStats)]
+    L.fi_decode_run.restype = ctypes.c_int
+    L.fi_decode_run.argtypes = [P, P, P, P, P, P, P, P, P, F, P, P, P]
+    L.fi_cascade_decode.restype = ctypes.c_int
+    L.fi_cascade_decode.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, F, P, P, P]
+    L.fi_merge_states.restype = ctypes.c_int
+    L.fi_merge_states.argtypes = [I32, ctypes.POINTER(P), ctypes.POINTER(P), I64, I32,
+                                  ctypes.c_int, P, P, ctypes.c_int, P]
+    L.fi_status_string.restype = ctypes.c_char_p
+    L.fi_status_string.argtypes = [ctypes.c_int]
+    L.fi_last_error.restype = ctypes.c_char_p
+    L.fi_last_error.argtypes = []
+    L.fi_debug_plan_tiles.restype = ctypes.c_int
+    L.fi_debug_plan_tiles.argtypes = [ctypes.POINTER(Problem), I32, P, I64,
+                                      ctypes.POINTER(I64)]
+    L.fi_debug_gather.restype = ctypes.c_int
+    L.fi_debug_gather.argtypes = [I32, I32, P, P, P, P, P, P]
+    return L
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != 0:
+        raise FiError(status, lib.fi_last_error().decode(errors="replace"))
+
+
+def _host_i32(a) -> np.ndarray:
+    if a is None:
+        return None
+    if hasattr(a, "detach"):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr(t) -> Optional[int]:
+    """Device pointer of a torch tensor (contiguous), or None."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr()
+
+
+def _np_ptr(a) -> Optional[int]:
+    return None if a is None else a.ctypes.data
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _problem(batch, Hq, Hkv, D, ps, q_dtype, kv_dtype, indptr, last, prefix, chunk):
+    pr = Problem()
+    pr.batch, pr.num_qo_heads, pr.num_kv_heads = batch, Hq, Hkv
+    pr.head_dim, pr.page_size = D, ps
+    pr.q_dtype, pr.kv_dtype = DTYPES[q_dtype], DTYPES[kv_dtype]
+    pr.kv_indptr, pr.last_page_len = _np_ptr(indptr), _np_ptr(last)
+    pr.chunk_tokens = chunk
+    keep = [indptr, last]
+    if prefix is not None:
+        qo, pip, plast = (_host_i32(x) for x in prefix)
+        pr.num_prefix_groups = len(qo) - 1
+        pr.prefix_qo_indptr, pr.prefix_kv_indptr = _np_ptr(qo), _np_ptr(pip)
+        pr.prefix_last_page_len = _np_ptr(plast)
+        keep += [qo, pip, plast]
+    return pr, keep
+
+
+def debug_plan_tiles(kv_indptr, last_page_len, *, num_qo_heads, num_kv_heads,
+                     page_size, head_dim=128, q_dtype="f16", kv_dtype="f16",
+                     prefix=None, num_cus=256, chunk_tokens=0) -> np.ndarray:
+    """Host-only: the plan's work list as an int32 [n, 8] array (request,
+    kv_head0, t0, t1, slot, kind, row0, row1)."""
+    indptr, last = _host_i32(kv_indptr), _host_i32(last_page_len)
+    pr, keep = _problem(len(indptr) - 1, num_qo_heads, num_kv_heads, head_dim,
+                        page_size, q_dtype, kv_dtype, indptr, last, prefix, chunk_tokens)
+    n = ctypes.c_int64(0)
+    _check(lib.fi_debug_plan_tiles(ctypes.byref(pr), num_cus, None, 0, ctypes.byref(n)))
+    out = np.zeros((max(n.value, 1), 8), np.int32)
+    _check(lib.fi_debug_plan_tiles(ctypes.byref(pr), num_cus, out.ctypes.data,
+                                   n.value, ctypes.byref(n)))
+    del keep
+    return out[:n.value]
+
+
+class Plan:
+    """Plan stage: host lengths -> work list in a device workspace.
+
+    kv_indptr / last_page_len are the HOST copies of the page table (numpy or
+    torch CPU).  prefix = (prefix_qo_indptr, prefix_kv_indptr,
+    prefix_last_page_len) host arrays for cascade decoding."""
+
+    def __init__(self, kv_indptr, last_page_len, *, num_qo_heads, num_kv_heads,
+                 page_size, head_dim=128, q_dtype="f16", kv_dtype="f16",
+                 prefix=None, num_cus=0, chunk_tokens=0, device=None, stream=None):
+        import torch
+        self.indptr = _host_i32(kv_indptr)
+        self.last = _host_i32(last_page_len)
+        self.batch = len(self.indptr) - 1
+        self.num_qo_heads, self.num_kv_heads = num_qo_heads, num_kv_heads
+        self.head_dim, self.page_size = head_dim, page_size
+        self.q_dtype, self.kv_dtype = q_dtype, kv_dtype
+        self.cascade = prefix is not None
+        pr, keep = _problem(self.batch, num_qo_heads, num_kv_heads, head_dim,
+                            page_size, q_dtype, kv_dtype, self.indptr, self.last,
+                            prefix, chunk_tokens)
+        need = ctypes.c_size_t(0)
+        _check(lib.fi_plan(ctypes.byref(pr), num_cus, None, 0, ctypes.byref(need), None,
+                           None))
+        dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=dev)
+        self._stream = stream
+        h = ctypes.c_void_p(None)
+        _check(lib.fi_plan(ctypes.byref(pr), num_cus, self.workspace.data_ptr(),
+                           self.workspace.numel(), ctypes.byref(need), _stream(stream),
+                           ctypes.byref(h)))
+        self.handle = h
+        del keep
+        st = PlanStats()
+        _check(lib.fi_plan_get_stats(self.handle, ctypes.byref(st)))
+        self.stats = st.as_dict()
+
+    # ---- run stage ---------------------------------------------------------
+    def _outputs(self, q, o, lse):
+        import torch
+        if o is None:
+            o = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((self.batch, self.num_qo_heads), dtype=torch.float32,
+                              device=q.device)
+        return o, lse
+
+    def _check_q(self, q):
+        import torch
+        want = {"f16": torch.float16, "bf16": torch.bfloat16}[self.q_dtype]
+        if q.dtype != want or tuple(q.shape) != (self.batch, self.num_qo_heads, self.head_dim):
+            raise ValueError(f"q must be {want} [{self.batch}, {self.num_qo_heads}, "
+                             f"{self.head_dim}], got {q.dtype} {tuple(q.shape)}")
+
+    def _check_pool(self, k_pages, v_pages):
+        es = 1 if self.kv_dtype == "e4m3" else 2
+        for t in (k_pages, v_pages):
+            row = self.page_size * self.num_kv_heads * self.head_dim * es
+            if t.numel() * t.element_size() % row:
+                raise ValueError("page pool size is not a whole number of pages")
+
+    def run(self, q, k_pages, v_pages, kv_indptr, kv_indices, last_page_len,
+            k_scale=None, v_scale=None, sm_scale: float = 0.0, o=None, lse=None,
+            stream=None):
+        """Batch paged decode.  Device tensors; returns (o, lse)."""
+        if self.cascade:
+            raise ValueError("cascade plan: use Plan.cascade_run")
+        self._check_q(q)
+        self._check_pool(k_pages, v_pages)
+        o, lse = self._outputs(q, o, lse)
+        _check(lib.fi_decode_run(self.handle, _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                                 _ptr(kv_indptr), _ptr(kv_indices), _ptr(last_page_len),
+                                 _ptr(k_scale), _ptr(v_scale), float(sm_scale), _ptr(o),
+                                 _ptr(lse), _stream(stream)))
+        return o, lse
+
+    def cascade_run(self, q, k_pages, v_pages, prefix_kv_indptr, prefix_kv_indices,
+                    prefix_last_page_len, kv_indptr, kv_indices, last_page_len,
+                    k_scale=None, v_scale=None, sm_scale: float = 0.0, o=None, lse=None,
+                    stream=None):
+        """Cascade (shared prefix + own pages) decode.  Returns (o, lse)."""
+        if not self.cascade:
+            raise ValueError("plan has no cascade level: use Plan.run")
+        self._check_q(q)
+        self._check_pool(k_pages, v_pages)
+        o, lse = self._outputs(q, o, lse)
+        _check(lib.fi_cascade_decode(self.handle, _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                                     _ptr(prefix_kv_indptr), _ptr(prefix_kv_indices),
+                                     _ptr(prefix_last_page_len), _ptr(kv_indptr),
+                                     _ptr(kv_indices), _ptr(last_page_len),
+                                     _ptr(k_scale), _ptr(v_scale), float(sm_scale),
+                                     _ptr(o), _ptr(lse), _stream(stream)))
+        return o, lse
+
+    def destroy(self):
+        if getattr(self, "handle", None):
+            import torch
+            torch.cuda.synchronize(self.workspace.device)
+            lib.fi_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def merge_states(v_states: Sequence, s_states: Sequence, out_dtype=None, v_out=None,
+                 s_out=None, stream=None):
+    """Merge attention states over disjoint key sets.  Each v [..., D] (f16,
+    bf16 or f32 device tensor), each s [...] fp32 natural-log lse with the
+    same leading shape.  Returns (v, s)."""
+    import torch
+    tdt = {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32"}
+    v0 = v_states[0]
+    rows = v0.numel() // v0.shape[-1]
+    D = v0.shape[-1]
+    for v, s in zip(v_states, s_states):
+        if v.shape != v0.shape or v.dtype != v0.dtype or s.numel() != rows or \
+                s.dtype != torch.float32:
+            raise ValueError("states must share shape/dtype; lse must be fp32 [rows]")
+    odt = v0.dtype if out_dtype is None else out_dtype
+    if v_out is None:
+        v_out = torch.empty(v0.shape, dtype=odt, device=v0.device)
+    if s_out is None:
+        s_out = torch.empty(v0.shape[:-1], dtype=torch.float32, device=v0.device)
+    n = len(v_states)
+    vp = (ctypes.c_void_p * n)(*[_ptr(v) for v in v_states])
+    sp = (ctypes.c_void_p * n)(*[_ptr(s) for s in s_states])
+    _check(lib.fi_merge_states(n, vp, sp, rows, D, DTYPES[tdt[v0.dtype]], _ptr(v_out),
+                               _ptr(s_out), DTYPES[tdt[odt]], _stream(stream)))
+    return v_out, s_out
+
+
+def debug_gather(page_size, kv_indptr, kv_indices, last_page_len, token_indptr,
+                 stream=None):
+    """Device page walk of every logical token (request-major) -> int64 slots."""
+    import torch
+    total = int(token_indptr[-1].item())
+    out = torch.empty(max(total, 1), dtype=torch.int64, device=kv_indptr.device)
+    _check(lib.fi_debug_gather(len(kv_indptr) - 1, page_size, _ptr(kv_indptr),
+                               _ptr(kv_indices), _ptr(last_page_len), _ptr(token_indptr),
+                               _ptr(out), _stream(stream)))
+    return out[:total]
+
+
+def default_sm_scale(head_dim: int = 128) -> float:
+    return 1.0 / math.sqrt(head_dim)

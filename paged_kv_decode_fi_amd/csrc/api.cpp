@@ -1,0 +1,390 @@
+// api.cpp -- the extern "C" boundary of libfi_decode.so.
+//
+// Validates every argument on the host, then only enqueues kernels on the
+// caller's stream (no allocation, no synchronisation in the run calls), so
+// that fi_decode_run / fi_cascade_decode / fi_merge_states can be captured
+// into a hipGraph (FlashInfer README, "core features" item 5).
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "fi_decode.h"
+#include "fi_internal.h"
+
+namespace fi {
+hipError_t launch_decode(const DecodeParams& p, int num_tiles, bool q_bf16, int kv,
+                         hipStream_t s);
+hipError_t launch_prefix(const DecodeParams& p, int num_tiles, bool q_bf16, int kv,
+                         hipStream_t s);
+hipError_t launch_merge_partials(const MergeParams& p, int num_units, bool o_bf16,
+                                 hipStream_t s);
+hipError_t launch_merge_states(const MergeStatesParams& p, hipStream_t s);
+hipError_t launch_gather(const int32_t* kv_indptr, const int32_t* kv_indices,
+                         const int64_t* token_indptr, int batch, int page_size,
+                         int ps_shift, int64_t* out, hipStream_t s);
+}  // namespace fi
+
+struct fi_plan_s {
+  fi::HostPlan hp;
+  char* workspace;
+  size_t workspace_bytes;
+  void* staging;  // pinned copy of the work list, merge map and request info
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fi_status fail(fi_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+fi_status hip_fail(hipError_t e, const char* what) {
+  return fail(FI_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int ps_shift_of(int ps) {
+  if (ps <= 0 || (ps & (ps - 1))) return -1;
+  int s = 0;
+  while ((1 << s) < ps) ++s;
+  return s;
+}
+
+fi_status check_dtypes(fi_dtype q, fi_dtype kv) {
+  if (q != FI_F16 && q != FI_BF16)
+    return fail(FI_ERR_UNSUPPORTED, "q_dtype must be FI_F16 or FI_BF16 (got %d)", (int)q);
+  if (kv != q && kv != FI_E4M3)
+    return fail(FI_ERR_UNSUPPORTED, "kv_dtype must equal q_dtype or be FI_E4M3 (got %d)",
+                (int)kv);
+  return FI_OK;
+}
+
+fi::PlanInput to_input(const fi_problem* p, int num_cus) {
+  fi::PlanInput in;
+  in.batch = p->batch;
+  in.Hq = p->num_qo_heads;
+  in.Hkv = p->num_kv_heads;
+  in.D = p->head_dim;
+  in.page_size = p->page_size;
+  in.q_dtype = p->q_dtype;
+  in.kv_dtype = p->kv_dtype;
+  in.kv_indptr = p->kv_indptr;
+  in.last_page_len = p->last_page_len;
+  in.num_groups = p->num_prefix_groups;
+  in.qo_indptr = p->prefix_qo_indptr;
+  in.p_indptr = p->prefix_kv_indptr;
+  in.p_last = p->prefix_last_page_len;
+  in.chunk_tokens = p->chunk_tokens;
+  in.num_cus = num_cus;
+  return in;
+}
+
+fi_status build_host_plan(const fi_problem* problem, int num_cus, fi::HostPlan* hp) {
+  if (!problem) return fail(FI_ERR_INVALID_ARG, "problem is NULL");
+  fi_status st = check_dtypes(problem->q_dtype, problem->kv_dtype);
+  if (st != FI_OK) return st;
+  char err[256] = {0};
+  int rc = fi::plan_build(to_input(problem, num_cus), hp, err, sizeof(err));
+  if (rc != 0) {
+    fi::plan_free(hp);
+    return fail(rc == 2 ? FI_ERR_UNSUPPORTED : FI_ERR_INVALID_ARG, "%s", err);
+  }
+  return FI_OK;
+}
+
+fi::DecodeParams base_params(const fi_plan_s* pl, const void* q, const void* k,
+                             const void* v, const float* ks, const float* vs,
+                             float sm_scale, void* o, float* lse) {
+  const fi::HostPlan& hp = pl->hp;
+  fi::DecodeParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.k_pages = k;
+  p.v_pages = v;
+  p.k_scale = hp.kv_dtype == FI_E4M3 ? ks : nullptr;
+  p.v_scale = hp.kv_dtype == FI_E4M3 ? vs : nullptr;
+  p.tiles = reinterpret_cast<const fi::Tile*>(pl->workspace + hp.layout.tiles_off);
+  p.req_info = reinterpret_cast<const fi::ReqInfo*>(pl->workspace + hp.layout.req_info_off);
+  p.partial_o = reinterpret_cast<float*>(pl->workspace + hp.layout.partial_o_off);
+  p.partial_lse = reinterpret_cast<float*>(pl->workspace + hp.layout.partial_lse_off);
+  p.o = o;
+  p.lse = lse;
+  const float sc = sm_scale > 0.f ? sm_scale : 1.0f / std::sqrt((float)hp.D);
+  p.sm_scale_log2 = sc * 1.4426950408889634f;
+  p.Hq = hp.Hq;
+  p.Hkv = hp.Hkv;
+  p.G = hp.G;
+  p.page_size = hp.page_size;
+  p.ps_shift = ps_shift_of(hp.page_size);
+  p.num_tiles = (int32_t)hp.num_tiles;
+  return p;
+}
+
+fi_status launch_merge(const fi_plan_s* pl, void* o, float* lse, hipStream_t s) {
+  const fi::HostPlan& hp = pl->hp;
+  if (hp.num_merge_units == 0) return FI_OK;
+  fi::MergeParams m;
+  m.partial_o = reinterpret_cast<const float*>(pl->workspace + hp.layout.partial_o_off);
+  m.partial_lse = reinterpret_cast<const float*>(pl->workspace + hp.layout.partial_lse_off);
+  m.req_info = reinterpret_cast<const fi::ReqInfo*>(pl->workspace + hp.layout.req_info_off);
+  m.merge_reqs = reinterpret_cast<const int32_t*>(pl->workspace + hp.layout.merge_reqs_off);
+  m.o = o;
+  m.lse = lse;
+  m.Hq = hp.Hq;
+  m.Hkv = hp.Hkv;
+  m.G = hp.G;
+  m.out_dtype = hp.q_dtype;
+  hipError_t e = fi::launch_merge_partials(m, (int)hp.num_merge_units, hp.q_dtype == FI_BF16, s);
+  return e == hipSuccess ? FI_OK : hip_fail(e, "merge launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fi_status_string(fi_status st) {
+  switch (st) {
+    case FI_OK: return "FI_OK";
+    case FI_ERR_INVALID_ARG: return "FI_ERR_INVALID_ARG";
+    case FI_ERR_UNSUPPORTED: return "FI_ERR_UNSUPPORTED";
+    case FI_ERR_WORKSPACE_TOO_SMALL: return "FI_ERR_WORKSPACE_TOO_SMALL";
+    case FI_ERR_HIP: return "FI_ERR_HIP";
+  }
+  return "unknown fi_status";
+}
+
+const char* fi_last_error(void) { return g_last_error.c_str(); }
+
+fi_status fi_plan(const fi_problem* problem, int32_t num_cus, void* workspace,
+                  size_t workspace_bytes, size_t* workspace_needed, void* stream,
+                  fi_plan_t* plan_out) {
+  g_last_error.clear();
+  if (plan_out) *plan_out = nullptr;
+  if (num_cus < 0) return fail(FI_ERR_INVALID_ARG, "num_cus must be >= 0");
+  if (num_cus == 0) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "querying the compute unit count");
+    num_cus = cus;
+  }
+  fi::HostPlan hp;
+  fi_status st = build_host_plan(problem, num_cus, &hp);
+  if (st != FI_OK) return st;
+  if (workspace_needed) *workspace_needed = hp.layout.total;
+  if (!workspace) {
+    fi::plan_free(&hp);
+    return FI_OK;
+  }
+  if (!plan_out) {
+    fi::plan_free(&hp);
+    return fail(FI_ERR_INVALID_ARG, "plan_out is NULL");
+  }
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) {
+    fi::plan_free(&hp);
+    return fail(FI_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  }
+  if (workspace_bytes < hp.layout.total) {
+    size_t need = hp.layout.total;
+    fi::plan_free(&hp);
+    return fail(FI_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, the plan needs %zu",
+                workspace_bytes, need);
+  }
+  const size_t meta_bytes = hp.layout.partial_o_off;
+  void* staging = nullptr;
+  hipError_t e = hipHostMalloc(&staging, meta_bytes, hipHostMallocDefault);
+  if (e != hipSuccess) {
+    fi::plan_free(&hp);
+    return hip_fail(e, "hipHostMalloc (plan staging)");
+  }
+  char* st8 = reinterpret_cast<char*>(staging);
+  memset(st8, 0, meta_bytes);
+  memcpy(st8 + hp.layout.tiles_off, hp.tiles,
+         sizeof(fi::Tile) * (hp.num_tiles + hp.num_prefix_tiles));
+  memcpy(st8 + hp.layout.req_info_off, hp.req_info, sizeof(fi::ReqInfo) * hp.batch);
+  memcpy(st8 + hp.layout.merge_reqs_off, hp.merge_reqs, sizeof(int32_t) * hp.num_merge_units);
+  memcpy(st8 + hp.layout.qo_indptr_off, hp.qo_indptr, sizeof(int32_t) * (hp.num_groups + 1));
+  e = hipMemcpyAsync(workspace, staging, meta_bytes, hipMemcpyHostToDevice,
+                     reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    (void)hipHostFree(staging);
+    fi::plan_free(&hp);
+    return hip_fail(e, "uploading the plan");
+  }
+  fi_plan_s* pl = new fi_plan_s;
+  pl->hp = hp;
+  pl->workspace = reinterpret_cast<char*>(workspace);
+  pl->workspace_bytes = workspace_bytes;
+  pl->staging = staging;
+  *plan_out = pl;
+  return FI_OK;
+}
+
+fi_status fi_plan_destroy(fi_plan_t plan) {
+  if (!plan) return FI_OK;
+  if (plan->staging) (void)hipHostFree(plan->staging);
+  fi::plan_free(&plan->hp);
+  delete plan;
+  return FI_OK;
+}
+
+fi_status fi_plan_get_stats(fi_plan_t plan, fi_plan_stats* s) {
+  if (!plan || !s) return fail(FI_ERR_INVALID_ARG, "plan and stats must be non-NULL");
+  const fi::HostPlan& hp = plan->hp;
+  s->num_tiles = hp.num_tiles;
+  s->num_prefix_tiles = hp.num_prefix_tiles;
+  s->num_partials = hp.num_partials;
+  s->num_merge_units = hp.num_merge_units;
+  s->chunk_tokens = hp.chunk_tokens;
+  s->prefix_chunk_tokens = hp.prefix_chunk_tokens;
+  s->heads_per_tile = hp.heads_per_tile;
+  s->num_cus = hp.num_cus;
+  s->workspace_bytes = hp.layout.total;
+  return FI_OK;
+}
+
+fi_status fi_decode_run(fi_plan_t plan, const void* q, const void* k_pages,
+                        const void* v_pages, const int32_t* kv_indptr,
+                        const int32_t* kv_indices, const int32_t* last_page_len,
+                        const float* k_scale, const float* v_scale, float sm_scale,
+                        void* o, float* lse, void* stream) {
+  g_last_error.clear();
+  if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
+  const fi::HostPlan& hp = plan->hp;
+  if (hp.num_groups != 0)
+    return fail(FI_ERR_INVALID_ARG, "plan has a cascade level: use fi_cascade_decode");
+  if (hp.batch == 0) return FI_OK;
+  if (!q || !o || !kv_indptr || !last_page_len)
+    return fail(FI_ERR_INVALID_ARG, "q, o, kv_indptr and last_page_len must be non-NULL");
+  const bool any_keys = hp.num_tiles > 0;
+  if (any_keys && (!k_pages || !v_pages || !kv_indices))
+    return fail(FI_ERR_INVALID_ARG, "k_pages, v_pages and kv_indices must be non-NULL");
+  if (!(sm_scale == sm_scale) || std::isinf(sm_scale))
+    return fail(FI_ERR_INVALID_ARG, "sm_scale must be finite");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  fi::DecodeParams p = base_params(plan, q, k_pages, v_pages, k_scale, v_scale, sm_scale, o, lse);
+  p.kv_indptr = kv_indptr;
+  p.kv_indices = kv_indices;
+  hipError_t e = fi::launch_decode(p, (int)hp.num_tiles, hp.q_dtype == FI_BF16,
+                                   hp.kv_dtype == FI_E4M3 ? 2 : (hp.q_dtype == FI_BF16 ? 1 : 0), s);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return launch_merge(plan, o, lse, s);
+}
+
+fi_status fi_cascade_decode(fi_plan_t plan, const void* q, const void* k_pages,
+                            const void* v_pages, const int32_t* prefix_kv_indptr,
+                            const int32_t* prefix_kv_indices,
+                            const int32_t* prefix_last_page_len, const int32_t* kv_indptr,
+                            const int32_t* kv_indices, const int32_t* last_page_len,
+                            const float* k_scale, const float* v_scale, float sm_scale,
+                            void* o, float* lse, void* stream) {
+  g_last_error.clear();
+  if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
+  const fi::HostPlan& hp = plan->hp;
+  if (hp.num_groups == 0)
+    return fail(FI_ERR_INVALID_ARG, "plan has no cascade level: use fi_decode_run");
+  if (hp.batch == 0) return FI_OK;
+  if (!q || !o || !kv_indptr || !last_page_len || !prefix_kv_indptr || !prefix_last_page_len)
+    return fail(FI_ERR_INVALID_ARG, "q, o and the indptr / last_page_len tables must be non-NULL");
+  if (!k_pages || !v_pages || (!kv_indices && hp.num_tiles > 0) ||
+      (!prefix_kv_indices && hp.num_prefix_tiles > 0))
+    return fail(FI_ERR_INVALID_ARG, "k_pages, v_pages and the index tables must be non-NULL");
+  if (!(sm_scale == sm_scale) || std::isinf(sm_scale))
+    return fail(FI_ERR_INVALID_ARG, "sm_scale must be finite");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool qbf = hp.q_dtype == FI_BF16;
+  const int kv = hp.kv_dtype == FI_E4M3 ? 2 : (qbf ? 1 : 0);
+  fi::DecodeParams p = base_params(plan, q, k_pages, v_pages, k_scale, v_scale, sm_scale, o, lse);
+  // prefix tiles read the group-level table; row -> request = the group's
+  // first request (planned copy of prefix_qo_indptr) + row / G
+  fi::DecodeParams pp = p;
+  pp.kv_indptr = prefix_kv_indptr;
+  pp.kv_indices = prefix_kv_indices;
+  pp.qo_indptr = reinterpret_cast<const int32_t*>(plan->workspace + hp.layout.qo_indptr_off);
+  hipError_t e = hipSuccess;
+  if (hp.num_prefix_tiles > 0) {
+    e = fi::launch_prefix(pp, (int)hp.num_prefix_tiles, qbf, kv, s);
+    if (e != hipSuccess) return hip_fail(e, "prefix launch");
+  }
+  p.kv_indptr = kv_indptr;
+  p.kv_indices = kv_indices;
+  e = fi::launch_decode(p, (int)hp.num_tiles, qbf, kv, s);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return launch_merge(plan, o, lse, s);
+}
+
+fi_status fi_merge_states(int32_t num_states, const void* const* v_states,
+                          const float* const* s_states, int64_t num_rows, int32_t head_dim,
+                          fi_dtype v_dtype, void* v_out, float* s_out, fi_dtype out_dtype,
+                          void* stream) {
+  g_last_error.clear();
+  if (num_states < 1 || num_states > fi::kMaxMergeStates)
+    return fail(FI_ERR_INVALID_ARG, "num_states must be in [1, %d]", fi::kMaxMergeStates);
+  if (num_rows < 0 || head_dim <= 0)
+    return fail(FI_ERR_INVALID_ARG, "num_rows must be >= 0 and head_dim > 0");
+  auto ok_dt = [](fi_dtype d) { return d == FI_F16 || d == FI_BF16 || d == FI_F32; };
+  if (!ok_dt(v_dtype) || !ok_dt(out_dtype))
+    return fail(FI_ERR_UNSUPPORTED, "merge dtypes must be FI_F16, FI_BF16 or FI_F32");
+  if (num_rows == 0) return FI_OK;
+  if (!v_states || !s_states || !v_out)
+    return fail(FI_ERR_INVALID_ARG, "v_states, s_states and v_out must be non-NULL");
+  fi::MergeStatesParams p;
+  memset(&p, 0, sizeof(p));
+  for (int i = 0; i < num_states; ++i) {
+    if (!v_states[i] || !s_states[i])
+      return fail(FI_ERR_INVALID_ARG, "state %d has a NULL pointer", i);
+    p.v[i] = v_states[i];
+    p.s[i] = s_states[i];
+  }
+  p.num_states = num_states;
+  p.num_rows = num_rows;
+  p.head_dim = head_dim;
+  p.v_dtype = v_dtype;
+  p.out_dtype = out_dtype;
+  p.v_out = v_out;
+  p.s_out = s_out;
+  hipError_t e = fi::launch_merge_states(p, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FI_OK : hip_fail(e, "merge_states launch");
+}
+
+fi_status fi_debug_plan_tiles(const fi_problem* problem, int32_t num_cus, int32_t* tiles_out,
+                              int64_t capacity_tiles, int64_t* num_tiles) {
+  g_last_error.clear();
+  if (!num_tiles) return fail(FI_ERR_INVALID_ARG, "num_tiles is NULL");
+  fi::HostPlan hp;
+  fi_status st = build_host_plan(problem, num_cus > 0 ? num_cus : 256, &hp);
+  if (st != FI_OK) return st;
+  const int64_t n = hp.num_tiles + hp.num_prefix_tiles;
+  *num_tiles = n;
+  if (tiles_out && capacity_tiles >= n)
+    memcpy(tiles_out, hp.tiles, sizeof(fi::Tile) * n);
+  fi::plan_free(&hp);
+  return FI_OK;
+}
+
+fi_status fi_debug_gather(int32_t batch, int32_t page_size, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, const int32_t* last_page_len,
+                          const int64_t* token_indptr, int64_t* out_slots, void* stream) {
+  g_last_error.clear();
+  (void)last_page_len;
+  if (batch < 0 || page_size < 1) return fail(FI_ERR_INVALID_ARG, "bad batch or page_size");
+  if (batch == 0) return FI_OK;
+  if (!kv_indptr || !kv_indices || !token_indptr || !out_slots)
+    return fail(FI_ERR_INVALID_ARG, "NULL pointer");
+  hipError_t e = fi::launch_gather(kv_indptr, kv_indices, token_indptr, batch, page_size,
+                                   ps_shift_of(page_size), out_slots,
+                                   reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FI_OK : hip_fail(e, "gather launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// fi_device.h -- gfx950 device primitives shared by the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fi_internal.h"
+
+namespace fi {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+enum KvKind { kKvF16 = 0, kKvBF16 = 1, kKvE4M3 = 2 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---- MFMA 16x16x32 (fp32 accumulate) ----------------------------------------
+// Operand layout (64 lanes, lane = 16 * g + n, g in 0..3, n in 0..15):
+//   A (16 x 32): lane holds A[n][8g .. 8g+7]
+//   B (32 x 16): lane holds B[8g .. 8g+7][n]
+//   D (16 x 16): lane holds D[4g .. 4g+3][n]
+template <bool BF16>
+__device__ __forceinline__ f32x4 mma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// ---- page walk ----------------------------------------------------------------
+// Physical token slot (page * page_size + slot) of logical token t of the
+// table row starting at kv_indices[page_base].  ps_shift = log2(page_size)
+// when page_size is a power of two, else -1.
+__device__ __forceinline__ int64_t page_slot(const int32_t* __restrict__ kv_indices,
+                                             int page_base, int t, int page_size,
+                                             int ps_shift) {
+  int pi, sl;
+  if (ps_shift >= 0) {
+    pi = t >> ps_shift;
+    sl = t & (page_size - 1);
+  } else {
+    pi = t / page_size;
+    sl = t - pi * page_size;
+  }
+  const int64_t page = kv_indices[page_base + pi];
+  return page * page_size + sl;
+}
+
+// ---- conversions ----------------------------------------------------------------
+// Two packed fp32 -> two packed 16-bit floats (round to nearest even).
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (BF16) {
+    __bf16 x = (__bf16)a, y = (__bf16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  } else {
+    _Float16 x = (_Float16)a, y = (_Float16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  }
+}
+
+// Four OCP e4m3fn codes (one dword) -> four 16-bit floats (two dwords), exact.
+// gfx950's scaled converts take the OCP encoding; scale 1.0 keeps the value.
+template <bool BF16>
+__device__ __forceinline__ u32x2 e4m3x4_to_16(uint32_t w) {
+  u32x2 r;
+  if constexpr (BF16) {
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+  } else {
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+  }
+  return r;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+template <typename T>
+__device__ __forceinline__ T ld_global(const void* base, int64_t byte_off) {
+  return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+
+}  // namespace fi

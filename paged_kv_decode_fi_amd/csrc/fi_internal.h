@@ -1,0 +1,126 @@
+// fi_internal.h -- types shared by the host runtime (plan.cpp, api.cpp) and
+// the gfx950 kernels.  No HIP headers here: plan.cpp compiles with plain g++.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fi {
+
+constexpr int kHeadDim = 128;      // head_dim the kernels are built for
+constexpr int kMaxGroup = 16;      // q heads per kv head one MFMA column tile holds
+constexpr int kBlockTokens = 32;   // tokens per inner-loop block
+constexpr int kWavesPerTile = 4;   // waves (= kv heads) per decode workgroup
+constexpr int kPrefixRowsPerWave = 32;                       // 2 column tiles
+constexpr int kPrefixRowsPerTile = kPrefixRowsPerWave * 4;   // 4 waves
+constexpr int kMaxMergeStates = 64;
+
+enum TileKind : int32_t { kDecodeTile = 0, kPrefixTile = 1 };
+
+// One entry of the work list (32 bytes, one workgroup each).
+//   decode tile: request `req`, kv heads [kv_head0, kv_head0 + waves), tokens
+//     [t0, t1) of the request's own pages; slot = partial-state slot of
+//     kv_head0 (wave w writes slot + w) or -1 when the tile's states are final.
+//   prefix tile: group `req`, kv head kv_head0, prefix tokens [t0, t1), q rows
+//     [row0, row1) of the group (row = (r - first request) * G + j % G);
+//     slot = the prefix chunk index.
+struct Tile {
+  int32_t req, kv_head0, t0, t1, slot, kind, row0, row1;
+};
+static_assert(sizeof(Tile) == 32, "tile is 32 bytes");
+
+// Per request: its partial states are slots slot_base + c * Hkv + h, for
+// state index c in [0, n_states) (prefix chunks first) and kv head h.
+// n_states <= 1 means the producing tile writes the final output.
+struct ReqInfo {
+  int32_t slot_base, n_states;
+};
+
+// Device workspace layout (byte offsets from the workspace base).
+struct WorkspaceLayout {
+  size_t tiles_off;        // Tile[num_tiles] then Tile[num_prefix_tiles]
+  size_t req_info_off;     // ReqInfo[batch]
+  size_t merge_reqs_off;   // int32[num_merge_units]
+  size_t qo_indptr_off;    // int32[num_groups + 1] (cascade only)
+  size_t partial_o_off;    // float[num_partials][G][D]
+  size_t partial_lse_off;  // float[num_partials][G]   (log2 domain)
+  size_t total;
+};
+
+// Host plan (built by plan.cpp, uploaded by api.cpp).
+struct HostPlan {
+  int32_t batch, Hq, Hkv, D, page_size, G;
+  int32_t q_dtype, kv_dtype;
+  int32_t num_groups;
+  int32_t num_cus;
+  int32_t chunk_tokens, prefix_chunk_tokens, heads_per_tile;
+  int64_t num_tiles, num_prefix_tiles, num_partials, num_merge_units;
+  Tile* tiles;          // num_tiles + num_prefix_tiles entries
+  ReqInfo* req_info;    // batch entries
+  int32_t* merge_reqs;  // num_merge_units entries
+  int32_t* qo_indptr;   // num_groups + 1 entries (cascade only)
+  WorkspaceLayout layout;
+};
+
+// Builds the plan on the host.  Returns 0 or an fi_status code with `err`
+// filled.  Memory of the arrays is malloc'ed; free with plan_free.
+struct PlanInput {
+  int32_t batch, Hq, Hkv, D, page_size;
+  int32_t q_dtype, kv_dtype;
+  const int32_t* kv_indptr;
+  const int32_t* last_page_len;
+  int32_t num_groups;
+  const int32_t* qo_indptr;
+  const int32_t* p_indptr;
+  const int32_t* p_last;
+  int32_t chunk_tokens;
+  int32_t num_cus;
+};
+int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen);
+void plan_free(HostPlan* p);
+
+// ---- kernel parameter blocks (passed by value) ----------------------------
+struct DecodeParams {
+  const void* q;
+  const void* k_pages;
+  const void* v_pages;
+  const int32_t* kv_indptr;   // page table the tile tokens index (device)
+  const int32_t* kv_indices;
+  const float* k_scale;
+  const float* v_scale;
+  const Tile* tiles;
+  const ReqInfo* req_info;
+  float* partial_o;
+  float* partial_lse;
+  void* o;
+  float* lse;
+  float sm_scale_log2;        // sm_scale * log2(e)
+  int32_t Hq, Hkv, G, page_size, ps_shift;  // ps_shift = log2(ps) or -1
+  int32_t num_tiles;
+  // prefix tiles only: first request of each group, device [groups+1]
+  const int32_t* qo_indptr;
+};
+
+struct MergeParams {
+  const float* partial_o;
+  const float* partial_lse;
+  const ReqInfo* req_info;
+  const int32_t* merge_reqs;
+  void* o;
+  float* lse;
+  int32_t Hq, Hkv, G;
+  int32_t out_dtype;
+};
+
+struct MergeStatesParams {
+  const void* v[kMaxMergeStates];
+  const float* s[kMaxMergeStates];
+  int32_t num_states;
+  int64_t num_rows;
+  int32_t head_dim;
+  int32_t v_dtype, out_dtype;
+  void* v_out;
+  float* s_out;
+};
+
+}  // namespace fi

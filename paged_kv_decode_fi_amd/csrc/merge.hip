@@ -1,0 +1,127 @@
+// merge.hip -- recombination of attention states over disjoint key sets.
+//
+// Splitting one request's keys over several workgroups (the load-balanced
+// plan of the FlashInfer README, "core features" item 2) and cascade
+// attention (item 3: shared prefix + own suffix) both need the union of
+// attention states: with s_i the log-sum-exp of key set i and v_i its
+// softmax-weighted value,
+//     s = M + ln sum_i exp(s_i - M),   M = max_i s_i,
+//     v = sum_i exp(s_i - s) v_i,
+// and an all-empty union gives v = 0, s = -inf.  Internal partial states
+// carry s in log2 units (the decode kernel's exp2 domain).
+#include "fi_device.h"
+
+namespace fi {
+
+// One wave per (merged request, q head); lane covers d = 2 lane, 2 lane + 1.
+template <bool OBF16>
+__global__ __launch_bounds__(256) void merge_partials_kernel(MergeParams p) {
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (j >= p.Hq) return;
+  const int r = p.merge_reqs[blockIdx.x];
+  const ReqInfo ri = p.req_info[r];
+  const int h = j / p.G, jj = j - h * p.G;
+  const int n = ri.n_states;
+  auto slot_of = [&](int c) { return (int64_t)ri.slot_base + (int64_t)c * p.Hkv + h; };
+  float M = -INFINITY;
+  for (int c = 0; c < n; ++c) M = fmaxf(M, p.partial_lse[slot_of(c) * p.G + jj]);
+  float a0 = 0.f, a1 = 0.f, S = 0.f;
+  if (M != -INFINITY) {
+    for (int c = 0; c < n; ++c) {
+      const int64_t sl = slot_of(c) * p.G + jj;
+      const float w = fast_exp2(p.partial_lse[sl] - M);
+      const f32x2 v = *reinterpret_cast<const f32x2*>(p.partial_o + sl * kHeadDim + 2 * lane);
+      S += w;
+      a0 += w * v.x;
+      a1 += w * v.y;
+    }
+  }
+  const float inv = S > 0.f ? 1.f / S : 0.f;
+  uint32_t* orow = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(p.o) +
+                                               ((int64_t)r * p.Hq + j) * kHeadDim);
+  orow[lane] = pack2<OBF16>(a0 * inv, a1 * inv);
+  if (lane == 0 && p.lse)
+    p.lse[(int64_t)r * p.Hq + j] = S > 0.f ? (M + fast_log2(S)) * kLn2 : -INFINITY;
+}
+
+hipError_t launch_merge_partials(const MergeParams& p, int num_units, bool o_bf16,
+                                 hipStream_t s) {
+  if (num_units <= 0) return hipSuccess;
+  dim3 grid(num_units, (p.Hq + 3) / 4);
+  if (o_bf16)
+    hipLaunchKernelGGL(merge_partials_kernel<true>, grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(merge_partials_kernel<false>, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+// ---- public K-way merge: one wave per row, natural-log lse ----------------
+__device__ __forceinline__ float load_val(const void* base, int dt, int64_t i) {
+  if (dt == 3) return reinterpret_cast<const float*>(base)[i];
+  const uint16_t u = reinterpret_cast<const uint16_t*>(base)[i];
+  if (dt == 1) return __builtin_bit_cast(float, (uint32_t)u << 16);
+  return (float)__builtin_bit_cast(_Float16, u);
+}
+
+__device__ __forceinline__ void store_val(void* base, int dt, int64_t i, float v) {
+  if (dt == 3) {
+    reinterpret_cast<float*>(base)[i] = v;
+  } else if (dt == 1) {
+    __bf16 b = (__bf16)v;
+    reinterpret_cast<uint16_t*>(base)[i] = __builtin_bit_cast(uint16_t, b);
+  } else {
+    _Float16 hv = (_Float16)v;
+    reinterpret_cast<uint16_t*>(base)[i] = __builtin_bit_cast(uint16_t, hv);
+  }
+}
+
+__global__ __launch_bounds__(256) void merge_states_kernel(MergeStatesParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= p.num_rows) return;
+  float M = -INFINITY;
+  for (int i = 0; i < p.num_states; ++i) M = fmaxf(M, p.s[i][row]);
+  float S = 0.f;
+  if (M != -INFINITY)
+    for (int i = 0; i < p.num_states; ++i) S += __expf(p.s[i][row] - M);
+  const float lse = S > 0.f ? M + __logf(S) : -INFINITY;
+  for (int d = lane; d < p.head_dim; d += 64) {
+    float acc = 0.f;
+    if (S > 0.f)
+      for (int i = 0; i < p.num_states; ++i)
+        acc += __expf(p.s[i][row] - lse) *
+               load_val(p.v[i], p.v_dtype, row * p.head_dim + d);
+    store_val(p.v_out, p.out_dtype, row * p.head_dim + d, acc);
+  }
+  if (lane == 0 && p.s_out) p.s_out[row] = lse;
+}
+
+hipError_t launch_merge_states(const MergeStatesParams& p, hipStream_t s) {
+  if (p.num_rows <= 0) return hipSuccess;
+  const int64_t blocks = (p.num_rows + 3) / 4;
+  hipLaunchKernelGGL(merge_states_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+// ---- test hook: the decode kernel's page walk, token by token --------------
+__global__ void gather_kernel(const int32_t* kv_indptr, const int32_t* kv_indices,
+                              const int64_t* token_indptr, int page_size, int ps_shift,
+                              int64_t* out) {
+  const int r = blockIdx.x;
+  const int page_base = kv_indptr[r];
+  const int64_t t_begin = token_indptr[r], L = token_indptr[r + 1] - t_begin;
+  for (int64_t t = threadIdx.x; t < L; t += blockDim.x)
+    out[t_begin + t] = page_slot(kv_indices, page_base, (int)t, page_size, ps_shift);
+}
+
+hipError_t launch_gather(const int32_t* kv_indptr, const int32_t* kv_indices,
+                         const int64_t* token_indptr, int batch, int page_size,
+                         int ps_shift, int64_t* out, hipStream_t s) {
+  if (batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_kernel, dim3(batch), dim3(256), 0, s, kv_indptr, kv_indices,
+                     token_indptr, page_size, ps_shift, out);
+  return hipGetLastError();
+}
+
+}  // namespace fi

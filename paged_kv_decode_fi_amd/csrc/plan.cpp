@@ -1,0 +1,286 @@
+// plan.cpp -- host plan scheduler (pure C++, no HIP).
+//
+// FlashInfer README, "core features" item 2: attention over variable-length
+// requests is split into a plan stage, which schedules the work on the host
+// to avoid load imbalance, and a run stage.  The README names stream-K as an
+// inspiration: long work is cut into pieces processed by different
+// workgroups and fixed up afterwards; here the fix-up is the merge of
+// (o, lse) attention states.
+//
+// Work model.  Each (request r, kv head h) has L_r keys.  A decode tile is one
+// workgroup of kWavesPerTile waves = that many consecutive kv heads of one
+// request over one token chunk [t0, t1).  The chunk length c is one value
+// for the whole batch: the smallest multiple of the 32-token block, at
+// least c_min, such that the number of waves launched stays within
+// target = num_cus * waves_per_cu (more chunks than that only adds partial
+// states to merge).  Tiles are emitted longest first so short tails fill in
+// behind long tiles.
+//
+// Cascade: the shared prefix of group g is attended once per (g, kv head) by
+// prefix tiles covering kPrefixRowsPerTile query rows each (rows = the
+// group's requests x the G q heads of that kv head); the prefix is cut into
+// chunks so that prefix tiles cover the GPU about twice.
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "fi_internal.h"
+
+namespace fi {
+namespace {
+
+int env_int(const char* name, int dflt) {
+  const char* s = getenv(name);
+  if (!s || !*s) return dflt;
+  return atoi(s);
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// kv_len from a CSR page table row
+int64_t table_len(const int32_t* indptr, const int32_t* last, int i, int ps) {
+  int64_t n = (int64_t)indptr[i + 1] - indptr[i];
+  return n == 0 ? 0 : (n - 1) * ps + last[i];
+}
+
+#define PLAN_FAIL(code, ...)                 \
+  do {                                       \
+    snprintf(err, errlen, __VA_ARGS__);      \
+    return code;                             \
+  } while (0)
+
+}  // namespace
+
+int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
+  memset(out, 0, sizeof(*out));
+  const int B = in.batch, Hkv = in.Hkv, ps = in.page_size;
+  if (B < 0) PLAN_FAIL(1, "batch must be >= 0 (got %d)", B);
+  if (in.Hq <= 0 || Hkv <= 0 || in.Hq % Hkv != 0)
+    PLAN_FAIL(1, "num_qo_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+              in.Hq, Hkv);
+  const int G = in.Hq / Hkv;
+  if (G > kMaxGroup)
+    PLAN_FAIL(2, "group size %d > %d q heads per kv head is not built", G, kMaxGroup);
+  if (in.D != kHeadDim) PLAN_FAIL(2, "head_dim %d not built (only %d)", in.D, kHeadDim);
+  if (ps <= 0) PLAN_FAIL(1, "page_size must be >= 1 (got %d)", ps);
+  if (B > 0 && (!in.kv_indptr || !in.last_page_len))
+    PLAN_FAIL(1, "kv_indptr and last_page_len (host) are required");
+  if (in.chunk_tokens < 0 || in.chunk_tokens % kBlockTokens != 0)
+    PLAN_FAIL(1, "chunk_tokens must be 0 or a positive multiple of %d", kBlockTokens);
+  if (B > 0 && in.kv_indptr[0] != 0) PLAN_FAIL(1, "kv_indptr[0] must be 0");
+  std::vector<int64_t> lens(B);
+  for (int r = 0; r < B; ++r) {
+    if (in.kv_indptr[r + 1] < in.kv_indptr[r])
+      PLAN_FAIL(1, "kv_indptr decreases at request %d", r);
+    int64_t n = (int64_t)in.kv_indptr[r + 1] - in.kv_indptr[r];
+    if (n > 0 && (in.last_page_len[r] < 1 || in.last_page_len[r] > ps))
+      PLAN_FAIL(1, "last_page_len[%d] = %d outside [1, %d]", r, in.last_page_len[r], ps);
+    lens[r] = table_len(in.kv_indptr, in.last_page_len, r, ps);
+    if (lens[r] > (int64_t)0x7fffffff - 64) PLAN_FAIL(1, "request %d too long", r);
+  }
+  const int NG = in.num_groups;
+  std::vector<int64_t> plens(NG > 0 ? NG : 0);
+  std::vector<int> group_of(B, -1);
+  if (NG < 0) PLAN_FAIL(1, "num_prefix_groups must be >= 0");
+  if (NG > 0) {
+    if (!in.qo_indptr || !in.p_indptr || !in.p_last)
+      PLAN_FAIL(1, "cascade level needs prefix_qo_indptr, prefix_kv_indptr, "
+                   "prefix_last_page_len (host)");
+    if (in.qo_indptr[0] != 0 || in.qo_indptr[NG] != B)
+      PLAN_FAIL(1, "prefix_qo_indptr must start at 0 and end at batch");
+    if (in.p_indptr[0] != 0) PLAN_FAIL(1, "prefix_kv_indptr[0] must be 0");
+    for (int g = 0; g < NG; ++g) {
+      if (in.qo_indptr[g + 1] < in.qo_indptr[g])
+        PLAN_FAIL(1, "prefix_qo_indptr decreases at group %d", g);
+      if (in.p_indptr[g + 1] < in.p_indptr[g])
+        PLAN_FAIL(1, "prefix_kv_indptr decreases at group %d", g);
+      int64_t n = (int64_t)in.p_indptr[g + 1] - in.p_indptr[g];
+      if (n > 0 && (in.p_last[g] < 1 || in.p_last[g] > ps))
+        PLAN_FAIL(1, "prefix_last_page_len[%d] outside [1, %d]", g, ps);
+      plens[g] = table_len(in.p_indptr, in.p_last, g, ps);
+      for (int r = in.qo_indptr[g]; r < in.qo_indptr[g + 1]; ++r) group_of[r] = g;
+    }
+  }
+  const int num_cus = in.num_cus > 0 ? in.num_cus : 256;
+
+  // ---- decode chunk length
+  int hpt = kWavesPerTile;
+  while (Hkv % hpt) hpt >>= 1;
+  const int64_t head_groups = Hkv / hpt;
+  const int64_t waves_per_cu = env_int("FI_WAVES_PER_CU", 16);
+  const int64_t c_min = round_up(std::max(env_int("FI_CHUNK_MIN", 64), kBlockTokens),
+                                 kBlockTokens);
+  const int64_t target_waves = std::max<int64_t>(1, num_cus * waves_per_cu);
+  int64_t Lmax = 0;
+  for (int r = 0; r < B; ++r) Lmax = std::max(Lmax, lens[r]);
+  auto waves_for = [&](int64_t c) {
+    int64_t w = 0;
+    for (int r = 0; r < B; ++r) w += std::max<int64_t>(1, ceil_div(lens[r], c));
+    return w * head_groups * hpt;
+  };
+  int64_t chunk;
+  if (in.chunk_tokens > 0) {
+    chunk = in.chunk_tokens;
+  } else {
+    int64_t hi = std::max<int64_t>(round_up(std::max<int64_t>(Lmax, 1), kBlockTokens),
+                                   kBlockTokens);
+    int64_t lo = std::min(c_min, hi);
+    if (waves_for(hi) >= target_waves) {
+      chunk = hi;                       // enough work without splitting
+    } else {
+      // smallest c in [lo, hi] (multiple of the block) with waves(c) <= target
+      int64_t a = lo / kBlockTokens, b = hi / kBlockTokens;
+      while (a < b) {
+        int64_t mid = (a + b) / 2;
+        if (waves_for(mid * kBlockTokens) <= target_waves) b = mid; else a = mid + 1;
+      }
+      chunk = a * kBlockTokens;
+    }
+  }
+
+  // ---- cascade prefix chunking
+  int64_t prefix_chunk = 0;
+  std::vector<int64_t> n_pchunks(NG > 0 ? NG : 0, 0);
+  int64_t prefix_row_tiles = 0;  // sum over groups of row tiles x Hkv
+  if (NG > 0) {
+    for (int g = 0; g < NG; ++g) {
+      int64_t rows = (int64_t)(in.qo_indptr[g + 1] - in.qo_indptr[g]) * G;
+      if (plens[g] > 0) prefix_row_tiles += ceil_div(rows, kPrefixRowsPerTile) * Hkv;
+    }
+    int64_t Lpmax = 0;
+    for (int g = 0; g < NG; ++g) Lpmax = std::max(Lpmax, plens[g]);
+    if (prefix_row_tiles > 0) {
+      const int64_t want = std::max<int64_t>(1, (int64_t)num_cus * env_int("FI_PREFIX_TILES_PER_CU", 2));
+      int64_t n_split = std::max<int64_t>(1, ceil_div(want, prefix_row_tiles));
+      prefix_chunk = round_up(ceil_div(Lpmax, n_split), kBlockTokens);
+      prefix_chunk = std::max<int64_t>(prefix_chunk, env_int("FI_PREFIX_CHUNK_MIN", 256));
+      prefix_chunk = round_up(prefix_chunk, kBlockTokens);
+    }
+    for (int g = 0; g < NG; ++g)
+      n_pchunks[g] = (plens[g] > 0 && prefix_chunk > 0) ? ceil_div(plens[g], prefix_chunk) : 0;
+  }
+
+  // ---- states per request, slots
+  std::vector<int64_t> n_dchunks(B);
+  for (int r = 0; r < B; ++r) n_dchunks[r] = lens[r] > 0 ? ceil_div(lens[r], chunk) : 0;
+  out->req_info = (ReqInfo*)malloc(sizeof(ReqInfo) * std::max(B, 1));
+  int64_t slots = 0, n_merge = 0;
+  for (int r = 0; r < B; ++r) {
+    int g = group_of[r];
+    int64_t ns = n_dchunks[r] + (g >= 0 ? n_pchunks[g] : 0);
+    out->req_info[r].n_states = (int32_t)ns;
+    out->req_info[r].slot_base = -1;
+    if (ns >= 2) {
+      out->req_info[r].slot_base = (int32_t)slots;
+      slots += ns * Hkv;
+      ++n_merge;
+    }
+    if (slots > (int64_t)0x7fffffff / (G * kHeadDim))
+      PLAN_FAIL(2, "too many partial states; raise chunk_tokens");
+  }
+  out->merge_reqs = (int32_t*)malloc(sizeof(int32_t) * std::max<int64_t>(n_merge, 1));
+  {
+    int64_t k = 0;
+    for (int r = 0; r < B; ++r)
+      if (out->req_info[r].n_states >= 2) out->merge_reqs[k++] = r;
+  }
+
+  // ---- decode tiles
+  std::vector<Tile> dt;
+  for (int r = 0; r < B; ++r) {
+    int g = group_of[r];
+    int64_t c_off = g >= 0 ? n_pchunks[g] : 0;
+    const ReqInfo& ri = out->req_info[r];
+    int64_t nc = n_dchunks[r];
+    bool need_empty = (nc == 0 && ri.n_states == 0);
+    for (int64_t c = 0; c < std::max<int64_t>(nc, need_empty ? 1 : 0); ++c) {
+      for (int64_t hg = 0; hg < head_groups; ++hg) {
+        Tile t;
+        t.req = r;
+        t.kv_head0 = (int32_t)(hg * hpt);
+        t.t0 = (int32_t)std::min<int64_t>(c * chunk, lens[r]);
+        t.t1 = (int32_t)std::min<int64_t>((c + 1) * chunk, lens[r]);
+        t.slot = ri.n_states >= 2 ? (int32_t)(ri.slot_base + (c_off + c) * Hkv + t.kv_head0) : -1;
+        t.kind = kDecodeTile;
+        t.row0 = t.row1 = 0;
+        dt.push_back(t);
+      }
+    }
+  }
+  std::stable_sort(dt.begin(), dt.end(), [](const Tile& a, const Tile& b) {
+    return (a.t1 - a.t0) > (b.t1 - b.t0);
+  });
+  // ---- prefix tiles: chunk-major, row tiles of one (group, head, chunk)
+  // adjacent so they run together and share the chunk's K/V in cache
+  std::vector<Tile> pt;
+  for (int g = 0; g < NG; ++g) {
+    int64_t rows = (int64_t)(in.qo_indptr[g + 1] - in.qo_indptr[g]) * G;
+    if (plens[g] == 0 || rows == 0) continue;
+    int64_t nrt = ceil_div(rows, kPrefixRowsPerTile);
+    for (int64_t pc = 0; pc < n_pchunks[g]; ++pc)
+      for (int h = 0; h < Hkv; ++h)
+        for (int64_t rt = 0; rt < nrt; ++rt) {
+          Tile t;
+          t.req = g;
+          t.kv_head0 = h;
+          t.t0 = (int32_t)(pc * prefix_chunk);
+          t.t1 = (int32_t)std::min<int64_t>((pc + 1) * prefix_chunk, plens[g]);
+          t.slot = (int32_t)pc;
+          t.kind = kPrefixTile;
+          t.row0 = (int32_t)(rt * kPrefixRowsPerTile);
+          t.row1 = (int32_t)std::min<int64_t>((rt + 1) * kPrefixRowsPerTile, rows);
+          pt.push_back(t);
+        }
+  }
+  out->qo_indptr = (int32_t*)malloc(sizeof(int32_t) * (NG + 1));
+  for (int g = 0; g <= NG; ++g) out->qo_indptr[g] = NG > 0 ? in.qo_indptr[g] : 0;
+  out->num_tiles = (int64_t)dt.size();
+  out->num_prefix_tiles = (int64_t)pt.size();
+  out->tiles = (Tile*)malloc(sizeof(Tile) * std::max<size_t>(dt.size() + pt.size(), 1));
+  std::copy(dt.begin(), dt.end(), out->tiles);
+  std::copy(pt.begin(), pt.end(), out->tiles + dt.size());
+
+  out->batch = B; out->Hq = in.Hq; out->Hkv = Hkv; out->D = in.D;
+  out->page_size = ps; out->G = G; out->q_dtype = in.q_dtype;
+  out->kv_dtype = in.kv_dtype; out->num_groups = NG; out->num_cus = num_cus;
+  out->chunk_tokens = (int32_t)chunk;
+  out->prefix_chunk_tokens = (int32_t)prefix_chunk;
+  out->heads_per_tile = hpt;
+  out->num_partials = slots;
+  out->num_merge_units = n_merge;
+
+  WorkspaceLayout& L = out->layout;
+  size_t off = 0;
+  L.tiles_off = off;
+  off = align256(off + sizeof(Tile) * (dt.size() + pt.size()));
+  L.req_info_off = off;
+  off = align256(off + sizeof(ReqInfo) * (size_t)std::max(B, 1));
+  L.merge_reqs_off = off;
+  off = align256(off + sizeof(int32_t) * (size_t)std::max<int64_t>(n_merge, 1));
+  L.qo_indptr_off = off;
+  off = align256(off + sizeof(int32_t) * (size_t)(NG + 1));
+  L.partial_o_off = off;
+  off = align256(off + sizeof(float) * (size_t)slots * G * kHeadDim);
+  L.partial_lse_off = off;
+  off = align256(off + sizeof(float) * (size_t)slots * G);
+  L.total = off;
+  return 0;
+}
+
+void plan_free(HostPlan* p) {
+  if (!p) return;
+  free(p->tiles);
+  free(p->req_info);
+  free(p->merge_reqs);
+  free(p->qo_indptr);
+  p->qo_indptr = nullptr;
+  p->tiles = nullptr;
+  p->req_info = nullptr;
+  p->merge_reqs = nullptr;
+}
+
+}  // namespace fi

@@ -1,0 +1,188 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol the header
+declares, validates arguments on the host, and the plan scheduler's work list
+covers every (request, kv head, token) exactly once.  No GPU is touched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def fi():
+    lib_path = os.path.join(ROOT, "paged_kv_decode_fi_amd", "libfi_decode.so")
+    if not os.path.exists(lib_path):
+        from paged_kv_decode_fi_amd import build as b
+        b.build()
+    import paged_kv_decode_fi_amd as m
+    return m
+
+
+def test_header_symbols_are_exported(fi):
+    hdr = open(os.path.join(ROOT, "include", "fi_decode.h")).read()
+    declared = set(re.findall(r"^(?:fi_status|const char\*)\s+(fi_\w+)\(", hdr, re.M))
+    assert {"fi_plan", "fi_decode_run", "fi_merge_states", "fi_cascade_decode"} <= declared
+    for name in declared:
+        assert hasattr(fi.lib, name), name
+    assert set(fi.EXPORTS) == declared
+
+
+def _problem(fi, indptr, last, **kw):
+    args = dict(num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                q_dtype="f16", kv_dtype="f16", prefix=None, chunk=0)
+    args.update(kw)
+    indptr = np.asarray(indptr, np.int32)
+    last = np.asarray(last, np.int32)
+    return fi._problem(len(indptr) - 1, args["num_qo_heads"], args["num_kv_heads"],
+                       args["head_dim"], args["page_size"], args["q_dtype"],
+                       args["kv_dtype"], indptr, last, args["prefix"], args["chunk"])
+
+
+def _status(fi, indptr, last, **kw):
+    pr, keep = _problem(fi, indptr, last, **kw)
+    n = ctypes.c_int64(0)
+    return fi.lib.fi_debug_plan_tiles(ctypes.byref(pr), 256, None, 0, ctypes.byref(n))
+
+
+def test_host_validation_errors(fi):
+    ok = _status(fi, [0, 2, 5], [3, 16])
+    assert ok == 0
+    assert _status(fi, [0, 5, 2], [3, 16]) == 1                 # indptr decreases
+    assert _status(fi, [1, 2, 5], [3, 16]) == 1                 # indptr[0] != 0
+    assert _status(fi, [0, 2, 5], [0, 16]) == 1                 # last_page_len 0
+    assert _status(fi, [0, 2, 5], [3, 17]) == 1                 # last_page_len > ps
+    assert _status(fi, [0, 2, 5], [3, 16], num_qo_heads=30) == 1  # Hq % Hkv
+    assert _status(fi, [0, 2, 5], [3, 16], head_dim=64) == 2    # not built
+    assert _status(fi, [0, 2, 5], [3, 16], num_qo_heads=256) == 2  # G = 32 > 16
+    assert _status(fi, [0, 2, 5], [3, 16], kv_dtype="bf16") == 2   # mixed dtype
+    assert _status(fi, [0, 2, 5], [3, 16], q_dtype="e4m3", kv_dtype="e4m3") == 2
+    assert _status(fi, [0, 2, 5], [3, 16], page_size=0) == 1
+    assert _status(fi, [0, 2, 5], [3, 16], chunk=48) == 1       # not a block multiple
+    msg = fi.lib.fi_last_error().decode()
+    assert "chunk_tokens" in msg
+
+
+def test_run_calls_reject_bad_arguments_before_touching_the_device(fi):
+    P = ctypes.c_void_p
+    assert fi.lib.fi_decode_run(None, *([None] * 8), 0.0, None, None, None) == 1
+    assert fi.lib.fi_cascade_decode(None, *([None] * 11), 0.0, None, None, None) == 1
+    assert fi.lib.fi_merge_states(0, None, None, 4, 128, 0, None, None, 0, None) == 1
+    assert fi.lib.fi_merge_states(65, None, None, 4, 128, 0, None, None, 0, None) == 1
+    assert fi.lib.fi_merge_states(2, None, None, 4, 128, 2, None, None, 0, None) == 2
+    assert fi.lib.fi_status_string(3) == b"FI_ERR_WORKSPACE_TOO_SMALL"
+
+
+def test_workspace_size_query_is_host_only(fi):
+    pr, keep = _problem(fi, [0, 2, 5], [3, 16])
+    need = ctypes.c_size_t(0)
+    st = fi.lib.fi_plan(ctypes.byref(pr), 256, None, 0, ctypes.byref(need), None, None)
+    assert st == 0 and need.value > 0
+
+
+def _lens(indptr, last, ps):
+    n = np.diff(indptr)
+    return np.where(n > 0, (n - 1) * ps + last, 0)
+
+
+def _check_cover(tiles, lens, Hkv, hpt, has_other_states=None):
+    seen = {}
+    empty = set()
+    for req, h0, t0, t1, slot, kind, r0, r1 in tiles:
+        if kind != 0:
+            continue
+        assert 0 <= t0 <= t1 <= lens[req]
+        if t0 == t1:
+            empty.add(req)
+        for h in range(h0, min(h0 + hpt, Hkv)):
+            for t in range(t0, t1):
+                key = (req, h, t)
+                assert key not in seen, key
+                seen[key] = slot
+    total = int(sum(lens)) * Hkv
+    assert len(seen) == total
+    for r, L in enumerate(lens):
+        if L == 0 and not (has_other_states is not None and has_other_states[r]):
+            assert r in empty      # empty requests still get their (0, -inf) written
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_plan_covers_every_token_once(fi, seed):
+    rng = np.random.default_rng(seed)
+    ps = [1, 16, 7, 16, 32, 2][seed]
+    Hkv = [8, 8, 4, 32, 2, 1][seed]
+    G = [4, 1, 8, 1, 16, 4][seed]
+    B = int(rng.integers(1, 40))
+    lens = rng.integers(0, 3000, size=B)
+    lens[rng.integers(0, B)] = 0
+    n = (lens + ps - 1) // ps
+    indptr = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    last = np.where(n > 0, lens - (n - 1) * ps, 0).astype(np.int32)
+    tiles = fi.debug_plan_tiles(indptr, last, num_qo_heads=Hkv * G, num_kv_heads=Hkv,
+                                page_size=ps, num_cus=[256, 32, 8, 256, 4, 1][seed])
+    hpt = 4
+    while Hkv % hpt:
+        hpt //= 2
+    _check_cover(tiles, _lens(indptr, last, ps), Hkv, hpt)
+    # longest tiles first
+    d = [t[3] - t[2] for t in tiles if t[5] == 0]
+    assert d == sorted(d, reverse=True)
+    # split requests: every (req, chunk, head) has its own slot; unsplit: -1
+    slots = [t[4] for t in tiles if t[4] >= 0]
+    assert len(slots) == len(set(slots))
+
+
+def test_plan_is_deterministic_and_depends_only_on_lengths(fi):
+    lens = np.array([100, 5000, 0, 17, 32768])
+    n = (lens + 15) // 16
+    indptr = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    last = np.where(n > 0, lens - (n - 1) * 16, 0).astype(np.int32)
+    a = fi.debug_plan_tiles(indptr, last, num_qo_heads=32, num_kv_heads=8, page_size=16)
+    b = fi.debug_plan_tiles(indptr, last, num_qo_heads=32, num_kv_heads=8, page_size=16)
+    assert np.array_equal(a, b)
+
+
+def test_plan_splits_long_requests(fi):
+    """The skewed mix: 8 long requests must be cut into many chunks."""
+    lens = np.array([500] * 120 + [32768] * 8)
+    n = (lens + 15) // 16
+    indptr = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    last = np.where(n > 0, lens - (n - 1) * 16, 0).astype(np.int32)
+    t = fi.debug_plan_tiles(indptr, last, num_qo_heads=32, num_kv_heads=8, page_size=16)
+    long_tiles = [x for x in t if lens[x[0]] == 32768]
+    assert len(long_tiles) >= 8 * 2 * 16
+    assert max(x[3] - x[2] for x in t) <= 2048
+
+
+def test_cascade_plan_covers_prefix_rows_once(fi):
+    G, Hkv, ps = 8, 8, 16
+    groups = [(5, 300), (3, 0), (2, 1000)]
+    B = sum(g[0] for g in groups)
+    lens = np.array([10, 0, 200, 3, 40, 7, 7, 7, 500, 1])
+    n = (lens + ps - 1) // ps
+    indptr = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    last = np.where(n > 0, lens - (n - 1) * ps, 0).astype(np.int32)
+    qo = np.concatenate([[0], np.cumsum([g[0] for g in groups])]).astype(np.int32)
+    plens = np.array([g[1] for g in groups])
+    pn = (plens + ps - 1) // ps
+    pip = np.concatenate([[0], np.cumsum(pn)]).astype(np.int32)
+    plast = np.where(pn > 0, plens - (pn - 1) * ps, 0).astype(np.int32)
+    tiles = fi.debug_plan_tiles(indptr, last, num_qo_heads=G * Hkv, num_kv_heads=Hkv,
+                                page_size=ps, prefix=(qo, pip, plast), num_cus=16)
+    req_prefix = np.repeat(plens, [g[0] for g in groups]) > 0
+    _check_cover(tiles, lens, Hkv, 4, has_other_states=req_prefix)
+    seen = set()
+    for grp, h, t0, t1, pc, kind, r0, r1 in tiles:
+        if kind != 1:
+            continue
+        assert 0 <= t0 < t1 <= plens[grp]
+        for row in range(r0, r1):
+            assert row < (qo[grp + 1] - qo[grp]) * G
+            for t in range(t0, t1):
+                key = (grp, h, row, t)
+                assert key not in seen
+                seen.add(key)
+    want = sum(g[0] * G * Hkv * g[1] for g in groups)
+    assert len(seen) == want

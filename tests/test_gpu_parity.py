@@ -1,0 +1,233 @@
+"""GPU parity of the HIP decode path (through the C ABI) against the fp64
+oracle, on seeded synthetic inputs shaped like the named workloads."""
+import numpy as np
+import pytest
+
+import workloads as W
+from tests import gpu_common as C
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fi():
+    import paged_kv_decode_fi_amd as m
+    return m
+
+
+def _variants(w):
+    return list(w.values()) if isinstance(w, dict) else [w]
+
+
+# ---------------------------------------------------------------- page walk
+
+@pytest.mark.parametrize("ps", [1, 7, 16])
+def test_gather_is_bit_exact(fi, ps):
+    import oracle
+    import torch
+    rng = np.random.default_rng(ps)
+    lens = rng.integers(0, 300, size=9)
+    n = (lens + ps - 1) // ps
+    indptr = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    indices = rng.permutation(int(n.sum()) + 11)[:int(n.sum())].astype(np.int32)
+    last = np.where(n > 0, lens - (n - 1) * ps, 0).astype(np.int32)
+    tok = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    got = fi.debug_gather(ps, C.to_dev(indptr), C.to_dev(indices), C.to_dev(last),
+                          C.to_dev(tok)).cpu().numpy()
+    want = oracle.gather_map(ps, indptr, indices, last)
+    assert np.array_equal(got, want)
+
+
+# ------------------------------------------------------- small named shapes
+
+@pytest.mark.parametrize("name", W.WORKLOADS)
+def test_small_workload_parity(fi, name):
+    for w in _variants(W.make(name, small=True)):
+        o, lse, plan = C.run_gpu(w)
+        ro, rl = C.run_oracle(w)
+        C.assert_parity(w, o, lse, ro, rl, label=f"{w.name} {plan.stats}")
+
+
+@pytest.mark.parametrize("name", ["batch64_gqa4", "skewed128", "cascade256", "long32_fp8"])
+@pytest.mark.parametrize("chunk", [32, 96])
+def test_forced_split_parity(fi, name, chunk):
+    """Small chunks force split-KV tiles and the (o, lse) merge."""
+    for w in _variants(W.make(name, small=True)):
+        o, lse, plan = C.run_gpu(w, chunk_tokens=chunk)
+        assert plan.stats["num_merge_units"] > 0
+        ro, rl = C.run_oracle(w)
+        C.assert_parity(w, o, lse, ro, rl, label=f"{w.name} chunk {chunk}")
+
+
+def test_page_size_1_and_16_agree_bitwise(fi):
+    """Same logical e4m3 data as page size 1 and 16: the kernel sums in logical
+    token order with the same plan, so the outputs are identical."""
+    ws = W.make("long32_fp8", small=True)
+    o1, l1, _ = C.run_gpu(ws[1])
+    o16, l16, _ = C.run_gpu(ws[16])
+    assert np.array_equal(o1, o16) and np.array_equal(l1, l16)
+
+
+def test_run_to_run_determinism_and_page_permutation(fi):
+    w = W.make("batch64_gqa4", small=True)
+    o1, l1, plan = C.run_gpu(w, chunk_tokens=64)
+    o2, l2, _ = C.run_gpu(w, plan=plan)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # move every page to a new place in a bigger pool: same result bit for bit
+    rng = np.random.default_rng(5)
+    P = w.k_pages.shape[0]
+    newpos = rng.permutation(P + 7)[:P]
+    kp = np.full((P + 7,) + w.k_pages.shape[1:], W.NAN_BITS["f16"], w.k_pages.dtype)
+    vp = kp.copy()
+    kp[newpos] = w.k_pages
+    vp[newpos] = w.v_pages
+    import copy
+    w2 = copy.copy(w)
+    w2.k_pages, w2.v_pages = kp, vp
+    w2.kv_indices = newpos[w.kv_indices].astype(np.int32)
+    o3, l3, _ = C.run_gpu(w2, plan=plan)
+    assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
+
+
+# ----------------------------------------------------------------- fuzz
+
+def _fuzz_case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    ps = int(rng.choice([1, 2, 16]))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    B = int(rng.integers(1, 10))
+    choices = [0, 1, max(ps - 1, 1), ps, ps + 1, int(rng.integers(2, 700))]
+    lens = [int(rng.choice(choices)) for _ in range(B)]
+    q_dtype = str(rng.choice(["f16", "bf16"]))
+    kv_dtype = str(rng.choice([q_dtype, "e4m3"]))
+    return W.build(f"fuzz{seed}", lens, Hq=Hkv * G, Hkv=Hkv, ps=ps, q_dtype=q_dtype,
+                   kv_dtype=kv_dtype, seed=seed)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_fuzz_parity(fi, seed):
+    w = _fuzz_case(seed)
+    chunk = [0, 32, 64][seed % 3]
+    o, lse, plan = C.run_gpu(w, chunk_tokens=chunk)
+    ro, rl = C.run_oracle(w)
+    C.assert_parity(w, o, lse, ro, rl,
+                    label=f"fuzz{seed} B{w.batch} G{w.group_size} Hkv{w.num_kv_heads} "
+                          f"ps{w.page_size} {w.q_dtype}/{w.kv_dtype} lens {list(w.kv_lens)}")
+
+
+# ------------------------------------------------------------ spike test
+
+def test_planted_dominant_key(fi):
+    """A key planted at a random position dominates: o must equal its V row
+    (catches a dropped or misplaced token that the tolerance alone cannot)."""
+    w = W.make("skewed128", small=True)
+    rng = np.random.default_rng(77)
+    r = int(np.argmax(w.kv_lens))
+    L = int(w.kv_lens[r])
+    t_star = int(rng.integers(0, L))
+    ps = w.page_size
+    page = w.kv_indices[w.kv_indptr[r] + t_star // ps]
+    q = w.q.view(np.float16).astype(np.float32)
+    h = 3
+    G = w.group_size
+    # K row := 4 * q of head h*G (scores ~ 4|q|^2/sqrt(D) >> others), same for all G heads
+    krow = (q[r, h * G] * 4.0).astype(np.float16)
+    w.k_pages[page, t_star % ps, h] = krow.view(np.uint16)
+    for j in range(h * G, (h + 1) * G):
+        w.q[r, j] = w.q[r, h * G]
+    o, lse, _ = C.run_gpu(w, chunk_tokens=64)
+    ro, rl = C.run_oracle(w)
+    v_star = w.v_pages[page, t_star % ps, h].view(np.float16).astype(np.float64)
+    for j in range(h * G, (h + 1) * G):
+        assert np.abs(ro[r, j] - v_star).max() < 1e-3
+        assert np.abs(o[r, j] - v_star).max() < 2e-3 + 1e-2 * np.abs(v_star).max()
+    C.assert_parity(w, o, lse, ro, rl, label="spike")
+
+
+# ----------------------------------------------------------- cascade / merge
+
+def test_cascade_matches_flat_decode(fi):
+    """fi_cascade_decode vs fi_decode_run over each request's concatenated
+    (prefix ++ own) page table."""
+    w = W.make("cascade256", small=True)
+    oc, lc, _ = C.run_gpu(w)
+    import copy
+    flat = copy.copy(w)
+    B = w.batch
+    indptr = [0]
+    idx = []
+    last = []
+    for r in range(B):
+        g = int(np.searchsorted(w.prefix_qo_indptr, r, side="right") - 1)
+        pp = w.prefix_kv_indices[w.prefix_kv_indptr[g]:w.prefix_kv_indptr[g + 1]]
+        own = w.kv_indices[w.kv_indptr[r]:w.kv_indptr[r + 1]]
+        assert w.prefix_last_page_len[g] == w.page_size   # prefix fills whole pages
+        idx.extend(pp.tolist() + own.tolist())
+        indptr.append(len(idx))
+        last.append(w.last_page_len[r] if len(own) else w.page_size)
+    flat.kv_indptr = np.array(indptr, np.int32)
+    flat.kv_indices = np.array(idx, np.int32)
+    flat.last_page_len = np.array(last, np.int32)
+    flat.prefix_kv_indptr = None
+    flat.prefix_lens = None
+    flat.kv_lens = w.kv_lens + w.prefix_lens[0]
+    of, lf, _ = C.run_gpu(flat, chunk_tokens=0)
+    ro, rl = C.run_oracle(w)
+    C.assert_parity(w, oc, lc, ro, rl, label="cascade vs oracle")
+    C.assert_parity(flat, of, lf, ro, rl, label="flat vs oracle")
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_merge_states_matches_oracle(fi, dt):
+    import oracle
+    import torch
+    rng = np.random.default_rng(3)
+    n_states, rows, D = 5, 37, 128
+    vs = rng.standard_normal((n_states, rows, D)).astype(np.float32)
+    ss = (rng.standard_normal((n_states, rows)) * 4).astype(np.float32)
+    ss[1, :5] = -np.inf
+    ss[:, 7] = -np.inf                       # an all-empty row
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+    vt = [torch.from_numpy(vs[i]).to(tdt).cuda() for i in range(n_states)]
+    st = [torch.from_numpy(ss[i]).cuda() for i in range(n_states)]
+    vo, so = fi.merge_states(vt, st, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    vin = np.stack([v.float().cpu().numpy() for v in vt]).astype(np.float64)
+    ro, rl = oracle.merge(vin, ss.astype(np.float64))
+    vo = vo.cpu().numpy().astype(np.float64)
+    so = so.cpu().numpy().astype(np.float64)
+    assert np.all(vo[7] == 0) and np.isneginf(so[7])
+    ok = ~np.isneginf(rl)
+    assert np.abs(vo - ro).max() <= 1e-5 + 1e-5 * np.abs(ro).max()
+    assert np.abs(so[ok] - rl[ok]).max() <= 1e-5
+
+
+def test_graph_capture_replays(fi):
+    """The run stage only enqueues kernels: capture it and replay it several
+    times with eager work in between; every replay equals the eager result."""
+    import torch
+    w = W.make("skewed128", small=True)
+    d = C.Dev(w)
+    plan = C.make_plan(w, chunk_tokens=64)
+    o_e, l_e = plan.run(d.q, d.k, d.v, d.indptr, d.indices, d.last, sm_scale=w.sm_scale)
+    torch.cuda.synchronize()
+    o_e, l_e = o_e.clone(), l_e.clone()
+    o = torch.empty_like(o_e)
+    lse = torch.empty_like(l_e)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        plan.run(d.q, d.k, d.v, d.indptr, d.indices, d.last, sm_scale=w.sm_scale, o=o, lse=lse)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan.run(d.q, d.k, d.v, d.indptr, d.indices, d.last, sm_scale=w.sm_scale, o=o, lse=lse)
+    for i in range(3):
+        o.fill_(0)
+        lse.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_e) and torch.equal(lse, l_e), f"replay {i}"
