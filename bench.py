@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of paged decode attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one run stage of the decode path (page walk, K/V loads, scores,
+online softmax, P.V, finalize, split-KV merge) over one batch of the named
+synthetic workload, inputs already resident in HBM.  The plan stage (host)
+is timed separately: it is computed once per batch and reused by every
+layer.  K/V copies are rotated so that the working set exceeds the 256 MB
+Infinity Cache and the measured rate is HBM traffic.
+
+Prints ONE JSON line (rank 0).  `value` is achieved KV GB/s of the whole
+step (valid tokens only, once per (token, kv head)); `roofline` reports the
+decode launch against the 8 TB/s HBM peak; `cpu_baseline` times the fp64
+oracle on the host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+ROTATE_BYTES = 1 << 30          # >= 1 GiB referenced per rotation cycle
+# traffic factor: FETCH_SIZE / WRITE_SIZE of a plain copy kernel of known
+# size read 1.0x its bytes in the calibration run (see profiles/); counters
+# are quoted per decode launch.
+TRAFFIC_KIB = None               # filled from profiles when measured
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="batch64_gqa4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rotate", action="store_true",
+                    help="time one resident copy (Infinity-Cache-hot), for context")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the K steps from one captured hipGraph")
+    ap.add_argument("--seed", type=int, default=None)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                                   f"(got {args.gpus})"}))
+        sys.exit(2)
+    import torch
+    import workloads as W
+    import paged_kv_decode_fi_amd as fi
+
+    torch.cuda.set_device(0)
+    t_gen = time.perf_counter()
+    wl = W.make(args.workload, seed=args.seed)
+    if isinstance(wl, dict):                   # long32_fp8: ps 1 and ps 16 variants
+        wl = wl[16]
+    t_gen = time.perf_counter() - t_gen
+    w = wl
+    print(f"[bench] workload {w.name}: B={w.batch} Hq={w.num_qo_heads} Hkv={w.num_kv_heads} "
+          f"ps={w.page_size} q={w.q_dtype} kv={w.kv_dtype} KV bytes={w.kv_bytes() / 1e9:.3f} GB "
+          f"(generated in {t_gen:.1f} s)", file=sys.stderr, flush=True)
+
+    def dev(a, dt=None):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a)
+        if dt is not None:
+            t = t.view(dt)
+        return t.to("cuda")
+
+    qdt = torch.float16 if w.q_dtype == "f16" else torch.bfloat16
+    pool_bytes = w.k_pages.nbytes + w.v_pages.nbytes
+    R = 1 if args.no_rotate else max(1, math.ceil(ROTATE_BYTES / pool_bytes))
+    copies = []
+    for i in range(R):
+        c = dict(q=dev(w.q, qdt), k=dev(w.k_pages), v=dev(w.v_pages),
+                 indptr=dev(w.kv_indptr), indices=dev(w.kv_indices),
+                 last=dev(w.last_page_len), ks=dev(w.k_scale), vs=dev(w.v_scale))
+        if w.prefix_kv_indptr is not None:
+            c.update(p_indptr=dev(w.prefix_kv_indptr), p_indices=dev(w.prefix_kv_indices),
+                     p_last=dev(w.prefix_last_page_len))
+        c["o"] = torch.empty_like(c["q"])
+        c["lse"] = torch.empty((w.batch, w.num_qo_heads), dtype=torch.float32, device="cuda")
+        copies.append(c)
+    cascade = w.prefix_kv_indptr is not None
+    prefix = ((w.prefix_qo_indptr, w.prefix_kv_indptr, w.prefix_last_page_len)
+              if cascade else None)
+
+    # ---- plan stage (host), timed separately; first call includes first use
+    t0 = time.perf_counter()
+    plan = fi.Plan(w.kv_indptr, w.last_page_len, num_qo_heads=w.num_qo_heads,
+                   num_kv_heads=w.num_kv_heads, page_size=w.page_size,
+                   head_dim=w.head_dim, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
+                   prefix=prefix)
+    torch.cuda.synchronize()
+    plan_first_ms = (time.perf_counter() - t0) * 1e3
+    t0 = time.perf_counter()
+    plan2 = fi.Plan(w.kv_indptr, w.last_page_len, num_qo_heads=w.num_qo_heads,
+                    num_kv_heads=w.num_kv_heads, page_size=w.page_size,
+                    head_dim=w.head_dim, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
+                    prefix=prefix)
+    torch.cuda.synchronize()
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    plan2.destroy()
+
+    def step(i):
+        c = copies[i % R]
+        if cascade:
+            plan.cascade_run(c["q"], c["k"], c["v"], c["p_indptr"], c["p_indices"],
+                             c["p_last"], c["indptr"], c["indices"], c["last"], c["ks"],
+                             c["vs"], sm_scale=w.sm_scale, o=c["o"], lse=c["lse"])
+        else:
+            plan.run(c["q"], c["k"], c["v"], c["indptr"], c["indices"], c["last"],
+                     c["ks"], c["vs"], sm_scale=w.sm_scale, o=c["o"], lse=c["lse"])
+
+    # ---- first use (separately from steady state)
+    t0 = time.perf_counter()
+    step(0)
+    torch.cuda.synchronize()
+    first_use_ms = (time.perf_counter() - t0) * 1e3
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    graph = None
+    if args.graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            step(0)
+        stream.wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(K):
+                step(i)
+        torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps between two synchronisations
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    if graph is not None:
+        ev[0][0].record(stream)
+        graph.replay()
+        ev[0][1].record(stream)
+    else:
+        for i in range(K):
+            ev[i][0].record(stream)
+            step(i)
+            ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_start
+    if graph is not None:
+        launch_ms = ev[0][0].elapsed_time(ev[0][1]) / K
+    else:
+        launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms_per_step = wall_s * 1e3 / K
+
+    # ---- HBM streaming-read ceiling measured in the same run (2 GiB buffer,
+    # larger than the Infinity Cache)
+    ceiling = None
+    try:
+        buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+        blocks = 2048
+        sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+        for _ in range(3):
+            fi.debug_stream_read(buf, sink, blocks)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            fi.debug_stream_read(buf, sink, blocks)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ceiling = buf.numel() * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del buf, sink
+    except RuntimeError as e:  # pragma: no cover - reported, not fatal
+        print(f"[bench] stream-read ceiling not measured: {e}", file=sys.stderr)
+
+    kv_bytes = w.kv_bytes()
+    alg_bytes = kv_bytes + w.other_bytes()
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = alg_bytes / (launch_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": TRAFFIC_KIB}
+
+    # ---- CPU oracle baseline on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = oracle.default_threads()
+        units = w.batch * w.num_kv_heads
+        # sample: whole (request, kv head) units, up to ~60 thread-seconds of
+        # fp64 work at the oracle's ~20 MB/s per thread
+        per_unit = kv_bytes / units
+        budget = 60 * 20e6
+        n_units = int(min(units, max(threads, budget // max(per_unit, 1))))
+        mask = np.zeros(units, np.uint8)
+        mask[np.random.default_rng(0).permutation(units)[:n_units]] = 1
+        um = mask.reshape(w.batch, w.num_kv_heads)
+        own = (w.kv_lens[:, None] * um).sum()
+        if cascade:
+            per_req_prefix = np.repeat(w.prefix_lens, np.diff(w.prefix_qo_indptr))
+            own = own + (per_req_prefix[:, None] * um).sum()
+        sample_bytes = 2 * int(own) * w.row_bytes
+        kw = dict(num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
+                  head_dim=w.head_dim, page_size=w.page_size, q_dtype=w.q_dtype,
+                  kv_dtype=w.kv_dtype, sm_scale=w.sm_scale, k_scale=w.k_scale,
+                  v_scale=w.v_scale, unit_mask=mask, threads=threads)
+        t0 = time.perf_counter()
+        if cascade:
+            oracle.cascade(w.q, w.k_pages, w.v_pages, w.prefix_qo_indptr,
+                           w.prefix_kv_indptr, w.prefix_kv_indices,
+                           w.prefix_last_page_len, w.kv_indptr, w.kv_indices,
+                           w.last_page_len, **kw)
+        else:
+            oracle.decode(w.q, w.k_pages, w.v_pages, w.kv_indptr, w.kv_indices,
+                          w.last_page_len, **kw)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s",
+               "cores": threads, "kind": "oracle",
+               "sample": f"{n_units} of {units} (request, kv head) units of {w.name}, "
+                         f"{sample_bytes / 1e6:.1f} MB of KV, {dt:.2f} s"}
+
+    st = plan.stats
+    out = {
+        "metric": "paged decode attention achieved KV GB/s and % of MI355X HBM peak",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.kv_dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "num_qo_heads": w.num_qo_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "page_size": w.page_size, "q_dtype": w.q_dtype, "kv_dtype": w.kv_dtype,
+                   "kv_len_total": int(w.kv_lens.sum()), "kv_bytes": kv_bytes,
+                   "rotated_copies": R, "graph": bool(args.graph)},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "hbm_read_ceiling_gbs": None if ceiling is None else round(ceiling, 1),
+        "pct_read_ceiling": None if ceiling is None else round(100 * value / ceiling, 2),
+        "requests_per_s": round(w.batch / (ms_per_step * 1e-3), 1),
+        "launch_ms": round(launch_ms, 5),
+        "plan_ms": round(plan_ms, 3), "plan_first_use_ms": round(plan_first_ms, 3),
+        "first_use_ms": round(first_use_ms, 3),
+        "plan": {k: st[k] for k in ("num_tiles", "num_prefix_tiles", "num_merge_units",
+                                    "chunk_tokens", "prefix_chunk_tokens", "num_cus")},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    plan.destroy()
+
+
+if __name__ == "__main__":
+    main()

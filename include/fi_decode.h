@@ -28,8 +28,9 @@
  *   v_pages       [num_pages][page_size][num_kv_heads][head_dim] ("NHD"),
  *                 dtype kv_dtype; separate K and V pools
  *   k_scale,
- *   v_scale       [num_kv_heads] fp32, required for E4M3 KV (dequantised
- *                 value = decode(code) * scale[kv_head]), ignored otherwise
+ *   v_scale       [num_kv_heads] fp32 for E4M3 KV (dequantised value =
+ *                 decode(code) * scale[kv_head]; NULL means 1.0), ignored
+ *                 for fp16/bf16 KV
  *
  * Plan / run (FlashInfer README, "core features" item 2: the plan stage
  * schedules variable-length work on the host to balance load; the run stage
@@ -215,6 +216,14 @@ fi_status fi_debug_gather(int32_t batch, int32_t page_size,
                           const int32_t* last_page_len,
                           const int64_t* token_indptr, int64_t* out_slots,
                           void* stream);
+
+/* fi_debug_stream_read: reads `bytes` (multiple of 16) of device memory at
+ * src with 16-byte loads from num_blocks workgroups of 256 threads and
+ * writes one folded word per thread to sink (device uint32
+ * [num_blocks * 256]).  A plain streaming read: the HBM bandwidth ceiling
+ * and the byte-counter calibration that decode traffic is compared to. */
+fi_status fi_debug_stream_read(const void* src, size_t bytes, uint32_t* sink,
+                               int32_t num_blocks, void* stream);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,8 @@ STATUS = {0: "FI_OK", 1: "FI_ERR_INVALID_ARG", 2: "FI_ERR_UNSUPPORTED",
           3: "FI_ERR_WORKSPACE_TOO_SMALL", 4: "FI_ERR_HIP"}
 EXPORTS = ("fi_plan", "fi_plan_destroy", "fi_plan_get_stats", "fi_decode_run",
            "fi_cascade_decode", "fi_merge_states", "fi_status_string",
-           "fi_last_error", "fi_debug_plan_tiles", "fi_debug_gather")
+           "fi_last_error", "fi_debug_plan_tiles", "fi_debug_gather",
+           "fi_debug_stream_read")
 
 
 class FiError(RuntimeError):
@@ -94,15 +95,32 @@ def _load() -> ctypes.CDLL:
                                       ctypes.POINTER(I64)]
     L.fi_debug_gather.restype = ctypes.c_int
     L.fi_debug_gather.argtypes = [I32, I32, P, P, P, P, P, P]
+    L.fi_debug_stream_read.restype = ctypes.c_int
+    L.fi_debug_stream_read.argtypes = [P, SZ, P, I32, P]
     return L
 
 
-lib = _load()
+_LIB = None
+
+
+def _get_lib() -> ctypes.CDLL:
+    """The loaded library (loaded on first use, so that the build module can
+    be imported before the library exists)."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
+
+
+def __getattr__(name):
+    if name == "lib":
+        return _get_lib()
+    raise AttributeError(name)
 
 
 def _check(status: int):
     if status != 0:
-        raise FiError(status, lib.fi_last_error().decode(errors="replace"))
+        raise FiError(status, _get_lib().fi_last_error().decode(errors="replace"))
 
 
 def _host_i32(a) -> np.ndarray:
@@ -158,9 +176,9 @@ def debug_plan_tiles(kv_indptr, last_page_len, *, num_qo_heads, num_kv_heads,
     pr, keep = _problem(len(indptr) - 1, num_qo_heads, num_kv_heads, head_dim,
                         page_size, q_dtype, kv_dtype, indptr, last, prefix, chunk_tokens)
     n = ctypes.c_int64(0)
-    _check(lib.fi_debug_plan_tiles(ctypes.byref(pr), num_cus, None, 0, ctypes.byref(n)))
+    _check(_get_lib().fi_debug_plan_tiles(ctypes.byref(pr), num_cus, None, 0, ctypes.byref(n)))
     out = np.zeros((max(n.value, 1), 8), np.int32)
-    _check(lib.fi_debug_plan_tiles(ctypes.byref(pr), num_cus, out.ctypes.data,
+    _check(_get_lib().fi_debug_plan_tiles(ctypes.byref(pr), num_cus, out.ctypes.data,
                                    n.value, ctypes.byref(n)))
     del keep
     return out[:n.value]
@@ -188,19 +206,19 @@ class Plan:
                             page_size, q_dtype, kv_dtype, self.indptr, self.last,
                             prefix, chunk_tokens)
         need = ctypes.c_size_t(0)
-        _check(lib.fi_plan(ctypes.byref(pr), num_cus, None, 0, ctypes.byref(need), None,
+        _check(_get_lib().fi_plan(ctypes.byref(pr), num_cus, None, 0, ctypes.byref(need), None,
                            None))
         dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
         self.workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=dev)
         self._stream = stream
         h = ctypes.c_void_p(None)
-        _check(lib.fi_plan(ctypes.byref(pr), num_cus, self.workspace.data_ptr(),
+        _check(_get_lib().fi_plan(ctypes.byref(pr), num_cus, self.workspace.data_ptr(),
                            self.workspace.numel(), ctypes.byref(need), _stream(stream),
                            ctypes.byref(h)))
         self.handle = h
         del keep
         st = PlanStats()
-        _check(lib.fi_plan_get_stats(self.handle, ctypes.byref(st)))
+        _check(_get_lib().fi_plan_get_stats(self.handle, ctypes.byref(st)))
         self.stats = st.as_dict()
 
     # ---- run stage ---------------------------------------------------------
@@ -236,7 +254,7 @@ class Plan:
         self._check_q(q)
         self._check_pool(k_pages, v_pages)
         o, lse = self._outputs(q, o, lse)
-        _check(lib.fi_decode_run(self.handle, _ptr(q), _ptr(k_pages), _ptr(v_pages),
+        _check(_get_lib().fi_decode_run(self.handle, _ptr(q), _ptr(k_pages), _ptr(v_pages),
                                  _ptr(kv_indptr), _ptr(kv_indices), _ptr(last_page_len),
                                  _ptr(k_scale), _ptr(v_scale), float(sm_scale), _ptr(o),
                                  _ptr(lse), _stream(stream)))
@@ -252,7 +270,7 @@ class Plan:
         self._check_q(q)
         self._check_pool(k_pages, v_pages)
         o, lse = self._outputs(q, o, lse)
-        _check(lib.fi_cascade_decode(self.handle, _ptr(q), _ptr(k_pages), _ptr(v_pages),
+        _check(_get_lib().fi_cascade_decode(self.handle, _ptr(q), _ptr(k_pages), _ptr(v_pages),
                                      _ptr(prefix_kv_indptr), _ptr(prefix_kv_indices),
                                      _ptr(prefix_last_page_len), _ptr(kv_indptr),
                                      _ptr(kv_indices), _ptr(last_page_len),
@@ -264,7 +282,7 @@ class Plan:
         if getattr(self, "handle", None):
             import torch
             torch.cuda.synchronize(self.workspace.device)
-            lib.fi_plan_destroy(self.handle)
+            _get_lib().fi_plan_destroy(self.handle)
             self.handle = None
 
     def __del__(self):
@@ -296,7 +314,7 @@ def merge_states(v_states: Sequence, s_states: Sequence, out_dtype=None, v_out=N
     n = len(v_states)
     vp = (ctypes.c_void_p * n)(*[_ptr(v) for v in v_states])
     sp = (ctypes.c_void_p * n)(*[_ptr(s) for s in s_states])
-    _check(lib.fi_merge_states(n, vp, sp, rows, D, DTYPES[tdt[v0.dtype]], _ptr(v_out),
+    _check(_get_lib().fi_merge_states(n, vp, sp, rows, D, DTYPES[tdt[v0.dtype]], _ptr(v_out),
                                _ptr(s_out), DTYPES[tdt[odt]], _stream(stream)))
     return v_out, s_out
 
@@ -307,10 +325,17 @@ def debug_gather(page_size, kv_indptr, kv_indices, last_page_len, token_indptr,
     import torch
     total = int(token_indptr[-1].item())
     out = torch.empty(max(total, 1), dtype=torch.int64, device=kv_indptr.device)
-    _check(lib.fi_debug_gather(len(kv_indptr) - 1, page_size, _ptr(kv_indptr),
+    _check(_get_lib().fi_debug_gather(len(kv_indptr) - 1, page_size, _ptr(kv_indptr),
                                _ptr(kv_indices), _ptr(last_page_len), _ptr(token_indptr),
                                _ptr(out), _stream(stream)))
     return out[:total]
+
+
+def debug_stream_read(src, sink, num_blocks, stream=None):
+    """Plain streaming read of a device tensor (bandwidth ceiling probe)."""
+    nbytes = src.numel() * src.element_size()
+    _check(_get_lib().fi_debug_stream_read(_ptr(src), nbytes - nbytes % 16, _ptr(sink),
+                                    num_blocks, _stream(stream)))
 
 
 def default_sm_scale(head_dim: int = 128) -> float:

@@ -16,8 +16,8 @@
 #include "fi_internal.h"
 
 namespace fi {
-hipError_t launch_decode(const DecodeParams& p, int num_tiles, bool q_bf16, int kv,
-                         hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, int num_tiles, int waves, bool q_bf16,
+                         int kv, hipStream_t s);
 hipError_t launch_prefix(const DecodeParams& p, int num_tiles, bool q_bf16, int kv,
                          hipStream_t s);
 hipError_t launch_merge_partials(const MergeParams& p, int num_units, bool o_bf16,
@@ -26,6 +26,8 @@ hipError_t launch_merge_states(const MergeStatesParams& p, hipStream_t s);
 hipError_t launch_gather(const int32_t* kv_indptr, const int32_t* kv_indices,
                          const int64_t* token_indptr, int batch, int page_size,
                          int ps_shift, int64_t* out, hipStream_t s);
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int blocks,
+                              hipStream_t s);
 }  // namespace fi
 
 struct fi_plan_s {
@@ -136,8 +138,7 @@ fi_status launch_merge(const fi_plan_s* pl, void* o, float* lse, hipStream_t s) 
   fi::MergeParams m;
   m.partial_o = reinterpret_cast<const float*>(pl->workspace + hp.layout.partial_o_off);
   m.partial_lse = reinterpret_cast<const float*>(pl->workspace + hp.layout.partial_lse_off);
-  m.req_info = reinterpret_cast<const fi::ReqInfo*>(pl->workspace + hp.layout.req_info_off);
-  m.merge_reqs = reinterpret_cast<const int32_t*>(pl->workspace + hp.layout.merge_reqs_off);
+  m.units = reinterpret_cast<const fi::MergeUnit*>(pl->workspace + hp.layout.merge_reqs_off);
   m.o = o;
   m.lse = lse;
   m.Hq = hp.Hq;
@@ -212,7 +213,8 @@ fi_status fi_plan(const fi_problem* problem, int32_t num_cus, void* workspace,
   memcpy(st8 + hp.layout.tiles_off, hp.tiles,
          sizeof(fi::Tile) * (hp.num_tiles + hp.num_prefix_tiles));
   memcpy(st8 + hp.layout.req_info_off, hp.req_info, sizeof(fi::ReqInfo) * hp.batch);
-  memcpy(st8 + hp.layout.merge_reqs_off, hp.merge_reqs, sizeof(int32_t) * hp.num_merge_units);
+  memcpy(st8 + hp.layout.merge_reqs_off, hp.merge_units,
+         sizeof(fi::MergeUnit) * hp.num_merge_units);
   memcpy(st8 + hp.layout.qo_indptr_off, hp.qo_indptr, sizeof(int32_t) * (hp.num_groups + 1));
   e = hipMemcpyAsync(workspace, staging, meta_bytes, hipMemcpyHostToDevice,
                      reinterpret_cast<hipStream_t>(stream));
@@ -275,7 +277,8 @@ fi_status fi_decode_run(fi_plan_t plan, const void* q, const void* k_pages,
   fi::DecodeParams p = base_params(plan, q, k_pages, v_pages, k_scale, v_scale, sm_scale, o, lse);
   p.kv_indptr = kv_indptr;
   p.kv_indices = kv_indices;
-  hipError_t e = fi::launch_decode(p, (int)hp.num_tiles, hp.q_dtype == FI_BF16,
+  hipError_t e = fi::launch_decode(p, (int)hp.num_tiles, hp.heads_per_tile,
+                                   hp.q_dtype == FI_BF16,
                                    hp.kv_dtype == FI_E4M3 ? 2 : (hp.q_dtype == FI_BF16 ? 1 : 0), s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return launch_merge(plan, o, lse, s);
@@ -318,7 +321,7 @@ fi_status fi_cascade_decode(fi_plan_t plan, const void* q, const void* k_pages,
   }
   p.kv_indptr = kv_indptr;
   p.kv_indices = kv_indices;
-  e = fi::launch_decode(p, (int)hp.num_tiles, qbf, kv, s);
+  e = fi::launch_decode(p, (int)hp.num_tiles, hp.heads_per_tile, qbf, kv, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return launch_merge(plan, o, lse, s);
 }
@@ -385,6 +388,16 @@ fi_status fi_debug_gather(int32_t batch, int32_t page_size, const int32_t* kv_in
                                    ps_shift_of(page_size), out_slots,
                                    reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? FI_OK : hip_fail(e, "gather launch");
+}
+
+fi_status fi_debug_stream_read(const void* src, size_t bytes, uint32_t* sink,
+                               int32_t num_blocks, void* stream) {
+  g_last_error.clear();
+  if (!src || !sink || num_blocks <= 0 || bytes % 16 != 0)
+    return fail(FI_ERR_INVALID_ARG, "stream_read: NULL pointer, no blocks, or bytes %% 16");
+  hipError_t e = fi::launch_stream_read(src, (int64_t)bytes, sink, num_blocks,
+                                        reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FI_OK : hip_fail(e, "stream_read launch");
 }
 
 }  // extern "C"

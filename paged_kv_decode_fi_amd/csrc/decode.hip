@@ -46,19 +46,21 @@ __device__ __forceinline__ int v_slot(int t) {
 }
 
 // Reads the transposed V operand for d-block b: lane (g, n) gets
-// V[token(g, kk)][16 b + n] for kk = 0..7.
+// V[token(g, kk)][16 b + n] for kk = 0..7, with two gfx950 transpose reads.
+// ds_read_b64_tr_b16 works per 16-lane group: lane i's element k is element
+// i % 4 of the 4 x 16-bit row addressed by lane i / 4 + 4 k of its group.  So
+// lane n addresses the d-quad n % 4 (columns 16 b + 4 (n % 4) ..) of the row
+// of contraction element kk = n / 4 (first read) or 4 + n / 4 (second).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 __device__ __forceinline__ u32x4 read_vt(const uint8_t* vt, int g, int n, int b) {
-  const uint8_t* base = vt + g * kVStride + (16 * b + n) * 2;
-  uint32_t e[8];
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-    e[kk] = *reinterpret_cast<const uint16_t*>(base + 4 * kk * kVStride);
-  u32x4 r;
-  r.x = e[0] | (e[1] << 16);
-  r.y = e[2] | (e[3] << 16);
-  r.z = e[4] | (e[5] << 16);
-  r.w = e[6] | (e[7] << 16);
-  return r;
+  const int kk = n >> 2, col = (16 * b + 4 * (n & 3)) * 2;
+  const uint8_t* a0 = vt + (4 * kk + g) * kVStride + col;
+  const uint8_t* a1 = vt + (4 * (kk + 4) + g) * kVStride + col;
+  const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
+  const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a1));
+  const u32x2 w0 = __builtin_bit_cast(u32x2, r0), w1 = __builtin_bit_cast(u32x2, r1);
+  return u32x4{w0.x, w0.y, w1.x, w1.y};
 }
 
 // Loads the q row pieces of one lane as the B operand of the 4 score steps.
@@ -85,28 +87,70 @@ __device__ __forceinline__ u32x4 k_operand(const u32x4* raw, int s) {
 }
 
 // ============================================================================
-// decode tiles
+// decode tiles (page-staged)
 // ============================================================================
-template <int KV, bool QBF16>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
-  constexpr int ES = KV == kKvE4M3 ? 1 : 2;          // bytes per K/V element
-  constexpr int ROWB = kHeadDim * ES;                // bytes per K/V row
-  constexpr int KLOADS = KV == kKvE4M3 ? 2 : 4;      // 16-B K loads per token row
-  constexpr int VLOADS = KV == kKvE4M3 ? 4 : 8;      // 16-B V loads per lane per block
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kWavesPerTile * kVTileBytes];
+// A workgroup of W waves owns W consecutive kv heads h0 .. h0+W-1 of one
+// request over a token chunk.  Per 16-token step it loads the K and V rows
+// of those heads for the 16 tokens -- W * row bytes contiguous per token, a
+// whole 32 KiB page when W = Hkv = 8 and page_size = 16 -- with 16-byte
+// non-temporal loads, 1 KiB contiguous per wave instruction, into padded LDS
+// tiles; then wave w computes kv head h0 + w from LDS:
+//   scores  S^T[token][head] = K . Q^T, MFMA 16x16x32 (K rows from LDS in A
+//           layout, q in B layout, columns past the group zero)
+//   softmax online, base 2, lazy running max (see kLazyMax)
+//   P.V     O^T[d][head] += V^T[d][token] . P^T[token][head], MFMA 16x16x16
+//           with V^T read by ds_read_b64_tr_b16 and P^T straight from the
+//           score accumulator layout.
+// Page indices run two steps ahead; the next step's K/V loads are in flight
+// in registers while the current step computes.  fp8 K stays fp8 in LDS
+// (converted after the read); fp8 V is converted to 16-bit on the LDS write.
+constexpr float kLazyMax = 8.f;
+constexpr int kStep = 16;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+template <int KV>
+struct Stage {
+  static constexpr int ROWB = KV == kKvE4M3 ? 128 : 256;  // K/V row bytes in HBM
+  static constexpr int VR = ROWB / 16;                    // 16-B vectors per row
+  static constexpr int LOADS = ROWB / 64;                 // vectors per thread per pool per step
+  static constexpr int TOK_PER_U = 64 / VR;               // token advance per load index u
+  static __host__ __device__ constexpr int k_stride(int W) { return W * ROWB + 16; }
+  static __host__ __device__ constexpr int v_stride(int W) { return W * 256 + 32; }
+  static __host__ __device__ constexpr int lds_bytes(int W) {
+    return kStep * (k_stride(W) + v_stride(W));
+  }
+};
+
+template <bool QBF16>
+__device__ __forceinline__ f32x4 mma16x16x16(u32x2 a, u32x2 b, f32x4 c) {
+  if constexpr (QBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+
+template <int KV, bool QBF16, bool PS_POW2>
+__global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams p) {
+  using S = Stage<KV>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int W = blockDim.x >> 6;                  // waves = kv heads of the tile
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const Tile tile = p.tiles[blockIdx.x];
-  const int h = tile.kv_head0 + wave;
-  if (h >= p.Hkv) return;
+  const int h0 = tile.kv_head0;
+  const int h = h0 + wave;
   const int g = lane >> 4, n = lane & 15;
   const int r = tile.req, t0 = tile.t0, t1 = tile.t1;
   const int G = p.G;
+  const int ps = p.page_size, ps_shift = p.ps_shift;
   const int page_base = p.kv_indptr[r];
-  uint8_t* vt = lds + wave * kVTileBytes;
+  const int KS = S::k_stride(W), VS = S::v_stride(W);
+  uint8_t* klds = lds;
+  uint8_t* vlds = lds + kStep * KS;
 
-  // q as the B operand of the score MFMAs
+  // q of this wave's head group as the B operand of the score MFMAs
   u32x4 qop[4];
   {
     const bool ok = n < G;
@@ -114,112 +158,131 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
                            ((int64_t)r * p.Hq + h * G + (ok ? n : 0)) * kHeadDim;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(qrow + q_dim<KV>(s, g));
+      u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * g);
       qop[s] = ok ? v : u32x4{0, 0, 0, 0};
     }
   }
   float c = p.sm_scale_log2;
   if (KV == kKvE4M3 && p.k_scale) c *= p.k_scale[h];
 
-  const char* kbase = reinterpret_cast<const char*>(p.k_pages);
-  const char* vbase = reinterpret_cast<const char*>(p.v_pages);
-  auto row_off = [&](int t) -> int64_t {
-    const int64_t slot = page_slot(p.kv_indices, page_base, t, p.page_size, p.ps_shift);
-    return (slot * p.Hkv + h) * (int64_t)ROWB;
+  // cooperative loader: load u of thread tid covers token tk0 + u * TOK_PER_U
+  // of the step and 16-byte vector vin of that token's W-head run
+  const int tk0 = tid / (S::VR * W);
+  const int vin = tid - tk0 * (S::VR * W);
+  const char* kbase = reinterpret_cast<const char*>(p.k_pages) + (int64_t)h0 * S::ROWB + 16 * vin;
+  const char* vbase = reinterpret_cast<const char*>(p.v_pages) + (int64_t)h0 * S::ROWB + 16 * vin;
+  const uint32_t slot_bytes = (uint32_t)p.Hkv * S::ROWB;
+  const int last = t1 - 1;
+  const int nsteps = (t1 - t0 + kStep - 1) / kStep;
+
+  // page of token t0 + 16 step + (lane & 15), clamped to the tile
+  auto load_page = [&](int step) -> int {
+    const int t = min(t0 + kStep * step + (lane & 15), last);
+    const int pi = PS_POW2 ? (t >> ps_shift) : (t / ps);
+    return p.kv_indices[page_base + pi];
+  };
+  u32x4 kr[S::LOADS], vr[S::LOADS];
+  auto issue = [&](int step, int pg) {
+    const int tb = t0 + kStep * step;
+#pragma unroll
+    for (int u = 0; u < S::LOADS; ++u) {
+      const int tk = tk0 + u * S::TOK_PER_U;
+      const int t = min(tb + tk, last);
+      const uint32_t page = (uint32_t)__shfl(pg, t - tb);
+      const uint32_t slot = PS_POW2 ? ((page << ps_shift) | (uint32_t)(t & (ps - 1)))
+                                    : (page * (uint32_t)ps + (uint32_t)(t % ps));
+      const uint64_t off = (uint64_t)slot * slot_bytes;
+      kr[u] = ld_stream<u32x4>(kbase, off);
+      vr[u] = ld_stream<u32x4>(vbase, off);
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int u = 0; u < S::LOADS; ++u) {
+      const int tk = tk0 + u * S::TOK_PER_U;
+      *reinterpret_cast<u32x4*>(klds + tk * KS + 16 * vin) = kr[u];
+      if constexpr (KV == kKvE4M3) {
+        const u32x2 a = e4m3x4_to_16<QBF16>(vr[u].x), b = e4m3x4_to_16<QBF16>(vr[u].y);
+        const u32x2 c2 = e4m3x4_to_16<QBF16>(vr[u].z), d = e4m3x4_to_16<QBF16>(vr[u].w);
+        uint8_t* dst = vlds + tk * VS + 32 * vin;
+        *reinterpret_cast<u32x4*>(dst) = u32x4{a.x, a.y, b.x, b.y};
+        *reinterpret_cast<u32x4*>(dst + 16) = u32x4{c2.x, c2.y, d.x, d.y};
+      } else {
+        *reinterpret_cast<u32x4*>(vlds + tk * VS + 16 * vin) = vr[u];
+      }
+    }
   };
 
   float m = -INFINITY, l = 0.f;
   f32x4 oacc[8];
 #pragma unroll
   for (int b = 0; b < 8; ++b) oacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // this lane's LDS addresses: K row of token n; V^T source row 4g + n/4 at
+  // d-quad n % 4 (transpose-read layout)
+  const uint8_t* krow = klds + n * KS + wave * S::ROWB;
+  const uint8_t* vsrc = vlds + (4 * g + (n >> 2)) * VS + wave * 256 + 8 * (n & 3);
 
-  for (int tb = t0; tb < t1; tb += kBlockTokens) {
-    const int last = t1 - 1;
-    // ---- issue K and V loads (tokens past t1 re-read the last valid token)
-    u32x4 kA[KLOADS], kB[KLOADS];
-    {
-      const int64_t oA = row_off(min(tb + n, last)), oB = row_off(min(tb + 16 + n, last));
-#pragma unroll
-      for (int j = 0; j < KLOADS; ++j) {
-        kA[j] = ld_global<u32x4>(kbase, oA + 64 * j + 16 * g);
-        kB[j] = ld_global<u32x4>(kbase, oB + 64 * j + 16 * g);
-      }
-    }
-    u32x4 vr[VLOADS];
-    int vslot[VLOADS];
-    int vcol;
-    if constexpr (KV == kKvE4M3) {
-      // lane (q8 = lane / 8, c8 = lane % 8): instruction u loads token 8u + q8
-      const int q8 = lane >> 3;
-      vcol = (lane & 7) * 32;  // 16 codes -> 32 bytes of 16-bit values
-#pragma unroll
-      for (int u = 0; u < VLOADS; ++u) {
-        const int t = 8 * u + q8;
-        vslot[u] = v_slot(t);
-        vr[u] = ld_global<u32x4>(vbase, row_off(min(tb + t, last)) + 16 * (lane & 7));
-      }
-    } else {
-      vcol = 16 * n;
-#pragma unroll
-      for (int kk = 0; kk < VLOADS; ++kk) {
-        const int t = 4 * g + (kk & 3) + 16 * (kk >> 2);
-        vslot[kk] = 4 * kk + g;
-        vr[kk] = ld_global<u32x4>(vbase, row_off(min(tb + t, last)) + 16 * n);
-      }
-    }
-
-    // ---- scores S^T[token][head]
-    f32x4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int step) {
+    const int tb = t0 + kStep * step;
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      sA = mma16x16x32<QBF16>(k_operand<KV, QBF16>(kA, s), qop[s], sA);
-      sB = mma16x16x32<QBF16>(k_operand<KV, QBF16>(kB, s), qop[s], sB);
+      u32x4 kop;
+      if constexpr (KV == kKvE4M3) {
+        const u32x2 w8 = *reinterpret_cast<const u32x2*>(krow + 32 * s + 8 * g);
+        const u32x2 a = e4m3x4_to_16<QBF16>(w8.x), b = e4m3x4_to_16<QBF16>(w8.y);
+        kop = u32x4{a.x, a.y, b.x, b.y};
+      } else {
+        kop = *reinterpret_cast<const u32x4*>(krow + 64 * s + 16 * g);
+      }
+      sc = mma16x16x32<QBF16>(kop, qop[s], sc);
     }
-    float x[8];
+    float x[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = (tb + 4 * g + i < t1) ? sA[i] * c : -INFINITY;
-      x[4 + i] = (tb + 16 + 4 * g + i < t1) ? sB[i] * c : -INFINITY;
+    for (int i = 0; i < 4; ++i) x[i] = sc[i] * c;
+    if (tb + kStep > t1) {                       // tail step: mask tokens past t1
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (tb + 4 * g + i >= t1) x[i] = -INFINITY;
     }
-    float mx = x[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    float pr[8], psum = 0.f;
+    const bool move = mx > m + kLazyMax;
+    if (__any(move)) {
+      const float m_new = move ? mx : m;
+      const float alpha = fast_exp2(m - m_new);   // m = -inf first: 0
+      l *= alpha;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pr[i] = fast_exp2(x[i] - m_use);
-      psum += pr[i];
+      for (int bb = 0; bb < 8; ++bb) oacc[bb] *= alpha;
+      m = m_new;
     }
-    l = l * alpha + psum;
-    m = m_new;
+    // every step has a valid token, so m is finite here
+    float pr[4];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) oacc[b] *= alpha;
-    const u32x4 pop = {pack2<QBF16>(pr[0], pr[1]), pack2<QBF16>(pr[2], pr[3]),
-                       pack2<QBF16>(pr[4], pr[5]), pack2<QBF16>(pr[6], pr[7])};
+    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(x[i] - m);
+    l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    const u32x2 pop = {pack2<QBF16>(pr[0], pr[1]), pack2<QBF16>(pr[2], pr[3])};
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) {
+      const s16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vsrc + 32 * bb));
+      oacc[bb] = mma16x16x16<QBF16>(__builtin_bit_cast(u32x2, vt), pop, oacc[bb]);
+    }
+  };
 
-    // ---- V rows -> LDS (as q-dtype values), then transposed operands
-    if constexpr (KV == kKvE4M3) {
-#pragma unroll
-      for (int u = 0; u < VLOADS; ++u) {
-        const u32x2 a = e4m3x4_to_16<QBF16>(vr[u].x), b2 = e4m3x4_to_16<QBF16>(vr[u].y);
-        const u32x2 c2 = e4m3x4_to_16<QBF16>(vr[u].z), d2 = e4m3x4_to_16<QBF16>(vr[u].w);
-        uint8_t* dst = vt + vslot[u] * kVStride + vcol;
-        *reinterpret_cast<u32x4*>(dst) = u32x4{a.x, a.y, b2.x, b2.y};
-        *reinterpret_cast<u32x4*>(dst + 16) = u32x4{c2.x, c2.y, d2.x, d2.y};
-      }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < VLOADS; ++kk)
-        *reinterpret_cast<u32x4*>(vt + vslot[kk] * kVStride + vcol) = vr[kk];
+  // ---- pipelined step loop
+  if (nsteps > 0) {
+    int pg1 = nsteps > 1 ? load_page(1) : 0;
+    issue(0, load_page(0));
+    for (int step = 0; step < nsteps; ++step) {
+      const int pg2 = step + 2 < nsteps ? load_page(step + 2) : 0;
+      stage();
+      __syncthreads();
+      if (step + 1 < nsteps) issue(step + 1, pg1);
+      compute(step);
+      __syncthreads();
+      pg1 = pg2;
     }
-#pragma unroll
-    for (int b = 0; b < 8; ++b)
-      oacc[b] = mma16x16x32<QBF16>(read_vt(vt, g, n, b), pop, oacc[b]);
   }
 
   // ---- finalize
@@ -308,8 +371,8 @@ __global__ __launch_bounds__(256) void prefix_kernel(DecodeParams p) {
       const int64_t slot = page_slot(p.kv_indices, page_base, t, p.page_size, p.ps_shift);
       const int64_t off = (slot * p.Hkv + h) * (int64_t)ROWB;
       if (KV != kKvE4M3 || cc < 8) {
-        kr[u] = ld_global<u32x4>(kbase, off + 16 * cc);
-        vr[u] = ld_global<u32x4>(vbase, off + 16 * cc);
+        kr[u] = ld_stream<u32x4>(kbase, off + 16 * cc);
+        vr[u] = ld_stream<u32x4>(vbase, off + 16 * cc);
       }
     }
   };
@@ -449,9 +512,28 @@ __global__ __launch_bounds__(256) void prefix_kernel(DecodeParams p) {
 
 // ---- launchers ----------------------------------------------------------------
 template <int KV, bool QBF16>
-static hipError_t launch_decode_t(const DecodeParams& p, int num_tiles, hipStream_t s) {
+static hipError_t launch_decode_t(const DecodeParams& p, int num_tiles, int waves,
+                                  hipStream_t s) {
   if (num_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_kernel<KV, QBF16>), dim3(num_tiles), dim3(256), 0, s, p);
+  const size_t lds = (size_t)Stage<KV>::lds_bytes(waves);
+  // dynamic LDS above 64 KiB must be allowed per kernel (once per process)
+  static const hipError_t attr = [] {
+    const int max_lds = Stage<KV>::lds_bytes(kWavesPerTile);
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, true>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+    return e;
+  }();
+  if (attr != hipSuccess) return attr;
+  if (p.ps_shift >= 0)
+    hipLaunchKernelGGL((decode_kernel<KV, QBF16, true>), dim3(num_tiles), dim3(64 * waves), lds,
+                       s, p);
+  else
+    hipLaunchKernelGGL((decode_kernel<KV, QBF16, false>), dim3(num_tiles), dim3(64 * waves), lds,
+                       s, p);
   return hipGetLastError();
 }
 
@@ -463,13 +545,14 @@ static hipError_t launch_prefix_t(const DecodeParams& p, int num_tiles, hipStrea
 }
 
 // q_bf16: q (and o) are bf16, else fp16.  kv: KvKind.
-hipError_t launch_decode(const DecodeParams& p, int num_tiles, bool q_bf16, int kv,
-                         hipStream_t s) {
+hipError_t launch_decode(const DecodeParams& p, int num_tiles, int waves, bool q_bf16,
+                         int kv, hipStream_t s) {
+  if (waves < 1 || waves > kWavesPerTile) return hipErrorInvalidValue;
   if (kv == kKvE4M3)
-    return q_bf16 ? launch_decode_t<kKvE4M3, true>(p, num_tiles, s)
-                  : launch_decode_t<kKvE4M3, false>(p, num_tiles, s);
-  return q_bf16 ? launch_decode_t<kKvBF16, true>(p, num_tiles, s)
-                : launch_decode_t<kKvF16, false>(p, num_tiles, s);
+    return q_bf16 ? launch_decode_t<kKvE4M3, true>(p, num_tiles, waves, s)
+                  : launch_decode_t<kKvE4M3, false>(p, num_tiles, waves, s);
+  return q_bf16 ? launch_decode_t<kKvBF16, true>(p, num_tiles, waves, s)
+                : launch_decode_t<kKvF16, false>(p, num_tiles, waves, s);
 }
 
 hipError_t launch_prefix(const DecodeParams& p, int num_tiles, bool q_bf16, int kv,

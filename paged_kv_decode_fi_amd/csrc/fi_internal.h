@@ -10,7 +10,7 @@ namespace fi {
 constexpr int kHeadDim = 128;      // head_dim the kernels are built for
 constexpr int kMaxGroup = 16;      // q heads per kv head one MFMA column tile holds
 constexpr int kBlockTokens = 32;   // tokens per inner-loop block
-constexpr int kWavesPerTile = 4;   // waves (= kv heads) per decode workgroup
+constexpr int kWavesPerTile = 8;   // waves (= kv heads) per decode workgroup
 constexpr int kPrefixRowsPerWave = 32;                       // 2 column tiles
 constexpr int kPrefixRowsPerTile = kPrefixRowsPerWave * 4;   // 4 waves
 constexpr int kMaxMergeStates = 64;
@@ -36,11 +36,17 @@ struct ReqInfo {
   int32_t slot_base, n_states;
 };
 
+// One merge work item: request r's states slot_base + c * Hkv + h,
+// c < n_states (16 bytes, read with one load).
+struct MergeUnit {
+  int32_t req, slot_base, n_states, pad;
+};
+
 // Device workspace layout (byte offsets from the workspace base).
 struct WorkspaceLayout {
   size_t tiles_off;        // Tile[num_tiles] then Tile[num_prefix_tiles]
   size_t req_info_off;     // ReqInfo[batch]
-  size_t merge_reqs_off;   // int32[num_merge_units]
+  size_t merge_reqs_off;   // MergeUnit[num_merge_units]
   size_t qo_indptr_off;    // int32[num_groups + 1] (cascade only)
   size_t partial_o_off;    // float[num_partials][G][D]
   size_t partial_lse_off;  // float[num_partials][G]   (log2 domain)
@@ -57,7 +63,7 @@ struct HostPlan {
   int64_t num_tiles, num_prefix_tiles, num_partials, num_merge_units;
   Tile* tiles;          // num_tiles + num_prefix_tiles entries
   ReqInfo* req_info;    // batch entries
-  int32_t* merge_reqs;  // num_merge_units entries
+  MergeUnit* merge_units;  // num_merge_units entries
   int32_t* qo_indptr;   // num_groups + 1 entries (cascade only)
   WorkspaceLayout layout;
 };
@@ -104,8 +110,7 @@ struct DecodeParams {
 struct MergeParams {
   const float* partial_o;
   const float* partial_lse;
-  const ReqInfo* req_info;
-  const int32_t* merge_reqs;
+  const MergeUnit* units;
   void* o;
   float* lse;
   int32_t Hq, Hkv, G;

@@ -13,28 +13,63 @@
 
 namespace fi {
 
-// One wave per (merged request, q head); lane covers d = 2 lane, 2 lane + 1.
+// One wave per (merged request, q head).  The lse of up to 64 states is read
+// by the lanes in parallel and reduced across the wave; the weighted sum of
+// the fp32 partial rows then streams the states with 2 dims per lane.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Memory round trips per wave: one for the unit record, one for the lse
+// values and the first kMergeBatch partial rows (independent loads, issued
+// together), then one per further batch.
+constexpr int kMergeBatch = 16;
+
 template <bool OBF16>
 __global__ __launch_bounds__(256) void merge_partials_kernel(MergeParams p) {
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.y * 4 + (threadIdx.x >> 6);
   if (j >= p.Hq) return;
-  const int r = p.merge_reqs[blockIdx.x];
-  const ReqInfo ri = p.req_info[r];
+  const MergeUnit u = p.units[blockIdx.x];
+  const int r = u.req;
   const int h = j / p.G, jj = j - h * p.G;
-  const int n = ri.n_states;
-  auto slot_of = [&](int c) { return (int64_t)ri.slot_base + (int64_t)c * p.Hkv + h; };
-  float M = -INFINITY;
-  for (int c = 0; c < n; ++c) M = fmaxf(M, p.partial_lse[slot_of(c) * p.G + jj]);
+  const int n = u.n_states;
+  const int64_t stride = (int64_t)p.Hkv * p.G;                  // rows between states
+  const int64_t row0 = ((int64_t)u.slot_base + h) * p.G + jj;   // state 0's row
+  const float* po = p.partial_o + row0 * kHeadDim + 2 * lane;
+  // lse of states lane, lane + 64, ... and the first batch of o rows
+  float s_lane[2];
+  s_lane[0] = lane < n ? p.partial_lse[row0 + lane * stride] : -INFINITY;
+  s_lane[1] = lane + 64 < n ? p.partial_lse[row0 + (lane + 64) * stride] : -INFINITY;
+  f32x2 v[kMergeBatch];
+#pragma unroll
+  for (int k = 0; k < kMergeBatch; ++k)
+    v[k] = k < n ? *reinterpret_cast<const f32x2*>(po + k * stride * kHeadDim) : f32x2{0.f, 0.f};
+  float M = wave_max(fmaxf(s_lane[0], s_lane[1]));
+  for (int c = lane + 128; c < n; c += 64) M = fmaxf(M, wave_max(p.partial_lse[row0 + c * stride]));
   float a0 = 0.f, a1 = 0.f, S = 0.f;
   if (M != -INFINITY) {
-    for (int c = 0; c < n; ++c) {
-      const int64_t sl = slot_of(c) * p.G + jj;
-      const float w = fast_exp2(p.partial_lse[sl] - M);
-      const f32x2 v = *reinterpret_cast<const f32x2*>(p.partial_o + sl * kHeadDim + 2 * lane);
-      S += w;
-      a0 += w * v.x;
-      a1 += w * v.y;
+    const float w0 = fast_exp2(s_lane[0] - M);   // exp2(-inf) = 0 for absent states
+    S = wave_sum(w0 + fast_exp2(s_lane[1] - M));
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const float wk = __shfl(w0, k);
+      a0 += wk * v[k].x;
+      a1 += wk * v[k].y;
+    }
+    for (int c = kMergeBatch; c < n; ++c) {
+      const float wc = fast_exp2(p.partial_lse[row0 + c * stride] - M);
+      if (c >= 128) S += wc;
+      const f32x2 vc = *reinterpret_cast<const f32x2*>(po + c * stride * kHeadDim);
+      a0 += wc * vc.x;
+      a1 += wc * vc.y;
     }
   }
   const float inv = S > 0.f ? 1.f / S : 0.f;
@@ -121,6 +156,36 @@ hipError_t launch_gather(const int32_t* kv_indptr, const int32_t* kv_indices,
   if (batch <= 0) return hipSuccess;
   hipLaunchKernelGGL(gather_kernel, dim3(batch), dim3(256), 0, s, kv_indptr, kv_indices,
                      token_indptr, page_size, ps_shift, out);
+  return hipGetLastError();
+}
+
+// ---- test hook: plain streaming read of a buffer (bandwidth ceiling and
+// counter calibration).  Each workgroup reads contiguous 64 KiB chunks with
+// 16-byte non-temporal loads (the fastest plain-read pattern measured on
+// MI355X) and folds them into one word per thread so the loads stay live.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src,
+                                                          int64_t n16, uint32_t* sink) {
+  constexpr int64_t kChunk = 4096;  // 16-byte vectors per workgroup step
+  uint32_t acc = 0;
+  for (int64_t base = (int64_t)blockIdx.x * kChunk; base < n16;
+       base += (int64_t)gridDim.x * kChunk) {
+    u32x4 v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int64_t k = base + u * 256 + threadIdx.x;
+      v[u] = k < n16 ? __builtin_nontemporal_load(src + k) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int blocks,
+                              hipStream_t s) {
+  if (bytes < 16 || blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, s,
+                     reinterpret_cast<const u32x4*>(src), bytes / 16, sink);
   return hipGetLastError();
 }
 

@@ -182,11 +182,13 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
     if (slots > (int64_t)0x7fffffff / (G * kHeadDim))
       PLAN_FAIL(2, "too many partial states; raise chunk_tokens");
   }
-  out->merge_reqs = (int32_t*)malloc(sizeof(int32_t) * std::max<int64_t>(n_merge, 1));
+  out->merge_units = (MergeUnit*)malloc(sizeof(MergeUnit) * std::max<int64_t>(n_merge, 1));
   {
     int64_t k = 0;
     for (int r = 0; r < B; ++r)
-      if (out->req_info[r].n_states >= 2) out->merge_reqs[k++] = r;
+      if (out->req_info[r].n_states >= 2)
+        out->merge_units[k++] = MergeUnit{r, out->req_info[r].slot_base,
+                                          out->req_info[r].n_states, 0};
   }
 
   // ---- decode tiles
@@ -260,7 +262,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   L.req_info_off = off;
   off = align256(off + sizeof(ReqInfo) * (size_t)std::max(B, 1));
   L.merge_reqs_off = off;
-  off = align256(off + sizeof(int32_t) * (size_t)std::max<int64_t>(n_merge, 1));
+  off = align256(off + sizeof(MergeUnit) * (size_t)std::max<int64_t>(n_merge, 1));
   L.qo_indptr_off = off;
   off = align256(off + sizeof(int32_t) * (size_t)(NG + 1));
   L.partial_o_off = off;
@@ -275,12 +277,12 @@ void plan_free(HostPlan* p) {
   if (!p) return;
   free(p->tiles);
   free(p->req_info);
-  free(p->merge_reqs);
+  free(p->merge_units);
   free(p->qo_indptr);
   p->qo_indptr = nullptr;
   p->tiles = nullptr;
   p->req_info = nullptr;
-  p->merge_reqs = nullptr;
+  p->merge_units = nullptr;
 }
 
 }  // namespace fi

@@ -87,6 +87,14 @@ def _lens(indptr, last, ps):
     return np.where(n > 0, (n - 1) * ps + last, 0)
 
 
+def _heads_per_tile(tiles, Hkv):
+    """kv heads one decode tile spans, read off the work list's head offsets."""
+    starts = {int(t[1]) for t in tiles if t[5] == 0} - {0}
+    hpt = min(starts) if starts else Hkv
+    assert Hkv % hpt == 0 and all(s % hpt == 0 for s in starts)
+    return hpt
+
+
 def _check_cover(tiles, lens, Hkv, hpt, has_other_states=None):
     seen = {}
     empty = set()
@@ -122,10 +130,7 @@ def test_plan_covers_every_token_once(fi, seed):
     last = np.where(n > 0, lens - (n - 1) * ps, 0).astype(np.int32)
     tiles = fi.debug_plan_tiles(indptr, last, num_qo_heads=Hkv * G, num_kv_heads=Hkv,
                                 page_size=ps, num_cus=[256, 32, 8, 256, 4, 1][seed])
-    hpt = 4
-    while Hkv % hpt:
-        hpt //= 2
-    _check_cover(tiles, _lens(indptr, last, ps), Hkv, hpt)
+    _check_cover(tiles, _lens(indptr, last, ps), Hkv, _heads_per_tile(tiles, Hkv))
     # longest tiles first
     d = [t[3] - t[2] for t in tiles if t[5] == 0]
     assert d == sorted(d, reverse=True)
@@ -172,7 +177,7 @@ def test_cascade_plan_covers_prefix_rows_once(fi):
     tiles = fi.debug_plan_tiles(indptr, last, num_qo_heads=G * Hkv, num_kv_heads=Hkv,
                                 page_size=ps, prefix=(qo, pip, plast), num_cus=16)
     req_prefix = np.repeat(plens, [g[0] for g in groups]) > 0
-    _check_cover(tiles, lens, Hkv, 4, has_other_states=req_prefix)
+    _check_cover(tiles, lens, Hkv, _heads_per_tile(tiles, Hkv), has_other_states=req_prefix)
     seen = set()
     for grp, h, t0, t1, pc, kind, r0, r1 in tiles:
         if kind != 1:
