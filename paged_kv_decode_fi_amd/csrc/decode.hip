@@ -291,19 +291,22 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (KV == kKvE4M3 && p.v_scale) inv *= p.v_scale[h];
   const float lse2 = lt > 0.f ? m + fast_log2(lt) : -INFINITY;
-  if (n >= G) return;
   const int j = h * G + n;
   if (tile.slot < 0) {
-    uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)r * p.Hq + j) * kHeadDim;
+    if (n < G) {
+      uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)r * p.Hq + j) * kHeadDim;
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      u32x2 w = {pack2<QBF16>(oacc[b][0] * inv, oacc[b][1] * inv),
-                 pack2<QBF16>(oacc[b][2] * inv, oacc[b][3] * inv)};
-      *reinterpret_cast<u32x2*>(orow + 16 * b + 4 * g) = w;
+      for (int b = 0; b < 8; ++b) {
+        u32x2 w = {pack2<QBF16>(oacc[b][0] * inv, oacc[b][1] * inv),
+                   pack2<QBF16>(oacc[b][2] * inv, oacc[b][3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + 16 * b + 4 * g) = w;
+      }
+      if (g == 0 && p.lse) p.lse[(int64_t)r * p.Hq + j] = lse2 * kLn2;
     }
-    if (g == 0 && p.lse) p.lse[(int64_t)r * p.Hq + j] = lse2 * kLn2;
-  } else {
-    const int64_t slot = tile.slot + wave;
+    return;
+  }
+  const int64_t slot = tile.slot + wave;
+  if (n < G) {
     float* po = p.partial_o + (slot * G + n) * kHeadDim;
 #pragma unroll
     for (int b = 0; b < 8; ++b)

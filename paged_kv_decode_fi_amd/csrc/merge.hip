@@ -13,71 +13,20 @@
 
 namespace fi {
 
-// One wave per (merged request, q head).  The lse of up to 64 states is read
-// by the lanes in parallel and reduced across the wave; the weighted sum of
-// the fp32 partial rows then streams the states with 2 dims per lane.
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-// Memory round trips per wave: one for the unit record, one for the lse
-// values and the first kMergeBatch partial rows (independent loads, issued
-// together), then one per further batch.
-constexpr int kMergeBatch = 16;
-
+// One wave per (merged request, q head); the arithmetic is merge_state_row.
 template <bool OBF16>
 __global__ __launch_bounds__(256) void merge_partials_kernel(MergeParams p) {
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.y * 4 + (threadIdx.x >> 6);
   if (j >= p.Hq) return;
   const MergeUnit u = p.units[blockIdx.x];
-  const int r = u.req;
   const int h = j / p.G, jj = j - h * p.G;
-  const int n = u.n_states;
   const int64_t stride = (int64_t)p.Hkv * p.G;                  // rows between states
   const int64_t row0 = ((int64_t)u.slot_base + h) * p.G + jj;   // state 0's row
-  const float* po = p.partial_o + row0 * kHeadDim + 2 * lane;
-  // lse of states lane, lane + 64, ... and the first batch of o rows
-  float s_lane[2];
-  s_lane[0] = lane < n ? p.partial_lse[row0 + lane * stride] : -INFINITY;
-  s_lane[1] = lane + 64 < n ? p.partial_lse[row0 + (lane + 64) * stride] : -INFINITY;
-  f32x2 v[kMergeBatch];
-#pragma unroll
-  for (int k = 0; k < kMergeBatch; ++k)
-    v[k] = k < n ? *reinterpret_cast<const f32x2*>(po + k * stride * kHeadDim) : f32x2{0.f, 0.f};
-  float M = wave_max(fmaxf(s_lane[0], s_lane[1]));
-  for (int c = lane + 128; c < n; c += 64) M = fmaxf(M, wave_max(p.partial_lse[row0 + c * stride]));
-  float a0 = 0.f, a1 = 0.f, S = 0.f;
-  if (M != -INFINITY) {
-    const float w0 = fast_exp2(s_lane[0] - M);   // exp2(-inf) = 0 for absent states
-    S = wave_sum(w0 + fast_exp2(s_lane[1] - M));
-#pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
-      const float wk = __shfl(w0, k);
-      a0 += wk * v[k].x;
-      a1 += wk * v[k].y;
-    }
-    for (int c = kMergeBatch; c < n; ++c) {
-      const float wc = fast_exp2(p.partial_lse[row0 + c * stride] - M);
-      if (c >= 128) S += wc;
-      const f32x2 vc = *reinterpret_cast<const f32x2*>(po + c * stride * kHeadDim);
-      a0 += wc * vc.x;
-      a1 += wc * vc.y;
-    }
-  }
-  const float inv = S > 0.f ? 1.f / S : 0.f;
   uint32_t* orow = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(p.o) +
-                                               ((int64_t)r * p.Hq + j) * kHeadDim);
-  orow[lane] = pack2<OBF16>(a0 * inv, a1 * inv);
-  if (lane == 0 && p.lse)
-    p.lse[(int64_t)r * p.Hq + j] = S > 0.f ? (M + fast_log2(S)) * kLn2 : -INFINITY;
+                                               ((int64_t)u.req * p.Hq + j) * kHeadDim);
+  merge_state_row<OBF16>(p.partial_o, p.partial_lse, row0, stride, u.n_states, orow,
+                         p.lse ? p.lse + (int64_t)u.req * p.Hq + j : nullptr, lane);
 }
 
 hipError_t launch_merge_partials(const MergeParams& p, int num_units, bool o_bf16,
