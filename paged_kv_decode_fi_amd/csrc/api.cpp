@@ -19,7 +19,7 @@
 namespace fi {
 hipError_t launch_decode(const DecodeParams& p, int num_tiles, int waves, bool q_bf16,
                          int kv, hipStream_t s);
-hipError_t launch_prefix(const DecodeParams& p, int num_tiles, bool q_bf16, int kv,
+hipError_t launch_prefix(const DecodeParams& p, int num_tiles, int waves, bool q_bf16, int kv,
                          hipStream_t s);
 hipError_t launch_merge_partials(const MergeParams& p, int num_units, bool o_bf16,
                                  hipStream_t s);
@@ -317,7 +317,7 @@ fi_status fi_cascade_decode(fi_plan_t plan, const void* q, const void* k_pages,
   pp.qo_indptr = reinterpret_cast<const int32_t*>(plan->workspace + hp.layout.qo_indptr_off);
   hipError_t e = hipSuccess;
   if (hp.num_prefix_tiles > 0) {
-    e = fi::launch_prefix(pp, (int)hp.num_prefix_tiles, qbf, kv, s);
+    e = fi::launch_prefix(pp, (int)hp.num_prefix_tiles, hp.prefix_waves, qbf, kv, s);
     if (e != hipSuccess) return hip_fail(e, "prefix launch");
   }
   p.kv_indptr = kv_indptr;

@@ -29,6 +29,8 @@
 //    per-kv-head scales folded into the score scale and the output.
 //  * A tile whose (request, kv head) is split over several chunks writes an
 //    fp32 partial state (o, log2-domain lse) that merge.hip combines.
+#include <type_traits>
+
 #include "fi_device.h"
 
 namespace fi {
@@ -317,90 +319,131 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
 
 // ============================================================================
 // cascade prefix tiles: many query rows x one prefix chunk of one kv head.
-// The 4 waves share each 32-token K/V block through LDS; wave w owns query
-// rows row0 + 32 w + 16 ct + n (ct = 0, 1) as the N columns of its MFMAs.
 // ============================================================================
-template <int KV, bool QBF16>
-__global__ __launch_bounds__(256) void prefix_kernel(DecodeParams p) {
-  constexpr int ES = KV == kKvE4M3 ? 1 : 2;
-  constexpr int ROWB = kHeadDim * ES;
-  constexpr int KT = kBlockTokens * kKStride;  // K tile bytes
-  constexpr int VT = kVTileBytes;              // V tile bytes
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (KT + VT)];
+// Workgroup = kPrefixWaves waves; wave w owns query rows row0 + 32 w + 16 rt + n
+// (rt = 0, 1) as the N columns of its MFMAs, so each K/V element staged in LDS
+// serves 256 rows.  Per 32-token step: the workgroup loads the step's K and V
+// rows of the tile's kv head (one 16-byte vector per thread per pool) into
+// one of two LDS buffers while the other is computed, one barrier per step;
+// scores on MFMA 16x16x32 (K operand read just in time from LDS, q in
+// registers), online softmax per row (lazy max), P.V on MFMA 16x16x16 with
+// V^T from transpose reads.  The prefix is reused across row tiles, so its
+// loads use the default (cached) policy, and the block -> tile map puts all
+// row tiles of one (head, chunk) on the same XCD (workgroups are dispatched
+// to the 8 XCDs round-robin) so they share that XCD's L2.
+constexpr int kPStep = 32;
 
+template <int KV>
+struct PStage {
+  static constexpr int ROWB = KV == kKvE4M3 ? 128 : 256;   // K row bytes kept in LDS
+  static constexpr int KS = ROWB + 16;                      // K LDS row stride
+  static constexpr int VS = 256 + 32;                       // V LDS row stride (16-bit values)
+  static constexpr int BUF = kPStep * (KS + VS);
+  static constexpr int LDS = 2 * BUF;
+};
+
+// XCD-aware map: block b runs on XCD b % 8; give each XCD a contiguous range
+// of the (chunk, head, row tile)-ordered tile list.
+__device__ __forceinline__ int xcd_tile(int b, int n) {
+  const int x = b & 7, k = b >> 3, per = n >> 3, rem = n & 7;
+  return x * per + min(x, rem) + k;
+}
+
+template <int KV, bool QBF16, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void prefix_kernel(DecodeParams p) {
+  using S = PStage<KV>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, n = lane & 15;
-  const Tile tile = p.tiles[p.num_tiles + blockIdx.x];
+  const Tile tile = p.tiles[p.num_tiles + xcd_tile(blockIdx.x, gridDim.x)];
   const int grp = tile.req, h = tile.kv_head0, t0 = tile.t0, t1 = tile.t1;
   const int G = p.G;
   const int qo0 = p.qo_indptr[grp];
   const int page_base = p.kv_indptr[grp];
+  const int ps = p.page_size, ps_shift = p.ps_shift;
 
-  // query rows of this lane's two column tiles
+  // query rows of this lane's two column tiles (B operands of the scores)
   u32x4 qop[2][4];
-  int rrow[2], rreq[2], rj[2];
   bool rok[2];
+  int rreq[2], rj[2];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const int row = tile.row0 + 32 * wave + 16 * ct + n;
-    rok[ct] = row < tile.row1;
-    rrow[ct] = row;
-    rreq[ct] = qo0 + (rok[ct] ? row : tile.row0) / G;
-    rj[ct] = h * G + (rok[ct] ? row : tile.row0) % G;
+  for (int rt = 0; rt < 2; ++rt) {
+    const int row = tile.row0 + kPrefixRowsPerWave * wave + 16 * rt + n;   // < row0 + 32 WAVES
+    rok[rt] = row < tile.row1;
+    const int rr = rok[rt] ? row : tile.row0;
+    rreq[rt] = qo0 + rr / G;
+    rj[rt] = h * G + rr % G;
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
-                           ((int64_t)rreq[ct] * p.Hq + rj[ct]) * kHeadDim;
+                           ((int64_t)rreq[rt] * p.Hq + rj[rt]) * kHeadDim;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(qrow + q_dim<kKvF16>(s, g));
-      qop[ct][s] = rok[ct] ? v : u32x4{0, 0, 0, 0};
+      u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * g);
+      qop[rt][s] = rok[rt] ? v : u32x4{0, 0, 0, 0};
     }
   }
   float c = p.sm_scale_log2;
   if (KV == kKvE4M3 && p.k_scale) c *= p.k_scale[h];
 
-  const char* kbase = reinterpret_cast<const char*>(p.k_pages);
-  const char* vbase = reinterpret_cast<const char*>(p.v_pages);
-  // cooperative loader: thread -> (token tl = tid / 16 + 16 u, chunk cc = tid % 16)
-  // f16/bf16: 16 chunks of 16 B per row; e4m3: 8 chunks of 16 B, threads with
-  // cc >= 8 idle for V/K staging.
-  const int cc = tid & 15;
-  auto load_block = [&](int tb, u32x4* kr, u32x4* vr) {
-    const int last = t1 - 1;
+  // cooperative loader: a step is 32 rows of K and 32 rows of V, i.e.
+  // 2 x 32 x VR 16-byte vectors (VR per row).  Thread tid loads vectors
+  // idx = tid + u T (T threads, u < NL): pool idx / (32 VR) (0 = K, 1 = V),
+  // token (idx % (32 VR)) / VR, chunk idx % VR.
+  constexpr bool F8 = KV == kKvE4M3;
+  constexpr int VR = S::ROWB / 16;
+  constexpr int T = 64 * WAVES;
+  constexpr int PV = 32 * VR;                       // vectors per pool per step
+  constexpr int NL = (2 * PV + T - 1) / T;
+  const char* kbase = reinterpret_cast<const char*>(p.k_pages) + (int64_t)h * S::ROWB;
+  const char* vbase = reinterpret_cast<const char*>(p.v_pages) + (int64_t)h * S::ROWB;
+  const uint32_t slot_bytes = (uint32_t)p.Hkv * S::ROWB;
+  const int last = t1 - 1;
+  auto page_of = [&](int t) -> int {
+    const int pi = ps_shift >= 0 ? (t >> ps_shift) : (t / ps);
+    return p.kv_indices[page_base + pi];
+  };
+  u32x4 vec[NL];
+  int pg[NL];   // page of each vector's token in the next step to load
+  auto pages = [&](int tb) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int t = min(tb + (tid >> 4) + 16 * u, last);
-      const int64_t slot = page_slot(p.kv_indices, page_base, t, p.page_size, p.ps_shift);
-      const int64_t off = (slot * p.Hkv + h) * (int64_t)ROWB;
-      if (KV != kKvE4M3 || cc < 8) {
-        kr[u] = ld_stream<u32x4>(kbase, off + 16 * cc);
-        vr[u] = ld_stream<u32x4>(vbase, off + 16 * cc);
-      }
+    for (int u = 0; u < NL; ++u) {
+      const int idx = tid + u * T;
+      pg[u] = page_of(min(tb + (idx % PV) / VR, last));
     }
   };
-  auto store_block = [&](int buf, const u32x4* kr, const u32x4* vr) {
-    uint8_t* kt = lds + buf * (KT + VT);
-    uint8_t* vtile = kt + KT;
+  auto load = [&](int tb) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int t = (tid >> 4) + 16 * u;
-      if constexpr (KV == kKvE4M3) {
-        if (cc < 8) {
-          const u32x2 a = e4m3x4_to_16<QBF16>(kr[u].x), b = e4m3x4_to_16<QBF16>(kr[u].y);
-          const u32x2 c2 = e4m3x4_to_16<QBF16>(kr[u].z), d = e4m3x4_to_16<QBF16>(kr[u].w);
-          uint8_t* dk = kt + t * kKStride + 32 * cc;
-          *reinterpret_cast<u32x4*>(dk) = u32x4{a.x, a.y, b.x, b.y};
-          *reinterpret_cast<u32x4*>(dk + 16) = u32x4{c2.x, c2.y, d.x, d.y};
-          const u32x2 va = e4m3x4_to_16<QBF16>(vr[u].x), vb = e4m3x4_to_16<QBF16>(vr[u].y);
-          const u32x2 vc = e4m3x4_to_16<QBF16>(vr[u].z), vd = e4m3x4_to_16<QBF16>(vr[u].w);
-          uint8_t* dv = vtile + v_slot(t) * kVStride + 32 * cc;
-          *reinterpret_cast<u32x4*>(dv) = u32x4{va.x, va.y, vb.x, vb.y};
-          *reinterpret_cast<u32x4*>(dv + 16) = u32x4{vc.x, vc.y, vd.x, vd.y};
-        }
+    for (int u = 0; u < NL; ++u) {
+      const int idx = tid + u * T;
+      if (idx >= 2 * PV) continue;
+      const int q = idx % PV;
+      const int t = min(tb + q / VR, last);
+      const uint32_t sl = ps_shift >= 0 ? (uint32_t)(t & (ps - 1)) : (uint32_t)(t % ps);
+      const uint64_t off = ((uint64_t)(uint32_t)pg[u] * (uint32_t)ps + sl) * slot_bytes +
+                           16 * (q % VR);
+      vec[u] = ld_global<u32x4>(idx < PV ? kbase : vbase, off);
+    }
+  };
+  auto store = [&](int buf) {
+    uint8_t* kt = lds + buf * S::BUF;
+    uint8_t* vt = kt + kPStep * S::KS;
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int idx = tid + u * T;
+      if (idx >= 2 * PV) continue;
+      const int q = idx % PV;
+      const int tok = q / VR, chk = q % VR;
+      if (idx < PV) {
+        *reinterpret_cast<u32x4*>(kt + tok * S::KS + 16 * chk) = vec[u];
+      } else if constexpr (F8) {
+        const u32x2 a = e4m3x4_to_16<QBF16>(vec[u].x), b = e4m3x4_to_16<QBF16>(vec[u].y);
+        const u32x2 c2 = e4m3x4_to_16<QBF16>(vec[u].z), d = e4m3x4_to_16<QBF16>(vec[u].w);
+        uint8_t* dv = vt + tok * S::VS + 32 * chk;
+        *reinterpret_cast<u32x4*>(dv) = u32x4{a.x, a.y, b.x, b.y};
+        *reinterpret_cast<u32x4*>(dv + 16) = u32x4{c2.x, c2.y, d.x, d.y};
       } else {
-        *reinterpret_cast<u32x4*>(kt + t * kKStride + 16 * cc) = kr[u];
-        *reinterpret_cast<u32x4*>(vtile + v_slot(t) * kVStride + 16 * cc) = vr[u];
+        *reinterpret_cast<u32x4*>(vt + tok * S::VS + 16 * chk) = vec[u];
       }
     }
   };
@@ -408,97 +451,132 @@ __global__ __launch_bounds__(256) void prefix_kernel(DecodeParams p) {
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
   f32x4 oacc[2][8];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct)
+  for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) oacc[ct][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < 8; ++b) oacc[rt][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 kr[2], vr[2];
-  if (t0 < t1) {
-    load_block(t0, kr, vr);
-    store_block(0, kr, vr);
-  }
-  __syncthreads();
-  int buf = 0;
-  for (int tb = t0; tb < t1; tb += kBlockTokens) {
-    const bool more = tb + kBlockTokens < t1;
-    if (more) load_block(tb + kBlockTokens, kr, vr);   // prefetch next block
-    const uint8_t* kt = lds + buf * (KT + VT);
-    const uint8_t* vtile = kt + KT;
-    // K operands (shared by both column tiles); K stored in q dtype layout
-    u32x4 kop[2][4];
+  // one 32-token step from LDS buffer buf; TAIL masks tokens past t1
+  auto compute = [&](int tb, int buf, auto tail_tag) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    const uint8_t* kt = lds + buf * S::BUF;
+    const uint8_t* vt = kt + kPStep * S::KS;
+    // ---- scores: S[tt][rt] = K(tokens 16 tt ..) . Q^T(rows of tile rt)
+    f32x4 sc[2][2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        kop[tt][s] = *reinterpret_cast<const u32x4*>(kt + (16 * tt + n) * kKStride +
-                                                     (32 * s + 8 * g) * 2);
-    u32x4 pop[2];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      f32x4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < 2; ++tt) {
+      sc[tt][0] = sc[tt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const uint8_t* krow = kt + (16 * tt + n) * S::KS;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        sA = mma16x16x32<QBF16>(kop[0][s], qop[ct][s], sA);
-        sB = mma16x16x32<QBF16>(kop[1][s], qop[ct][s], sB);
+        u32x4 kop;
+        if constexpr (F8) {
+          const u32x2 w8 = *reinterpret_cast<const u32x2*>(krow + 32 * s + 8 * g);
+          const u32x2 a = e4m3x4_to_16<QBF16>(w8.x), b = e4m3x4_to_16<QBF16>(w8.y);
+          kop = u32x4{a.x, a.y, b.x, b.y};
+        } else {
+          kop = *reinterpret_cast<const u32x4*>(krow + 64 * s + 16 * g);
+        }
+        sc[tt][0] = mma16x16x32<QBF16>(kop, qop[0][s], sc[tt][0]);
+        sc[tt][1] = mma16x16x32<QBF16>(kop, qop[1][s], sc[tt][1]);
+        // keep each operand read next to its MFMAs (register pressure)
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    // ---- online softmax per row tile.  c > 0, so the max is taken on the
+    // raw scores and the scale rides in the exponent's FMA: p = 2^(s c - m).
+    // P^T operand of the 16x16x32 P.V: contraction element kk of lane group g
+    // is token 4 g + (kk & 3) + 16 (kk >> 2) = score tile kk >> 2, entry kk & 3.
+    u32x4 pop[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
       float x[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[i] = (tb + 4 * g + i < t1) ? sA[i] * c : -INFINITY;
-        x[4 + i] = (tb + 16 + 4 * g + i < t1) ? sB[i] * c : -INFINITY;
+        x[i] = sc[0][rt][i];
+        x[4 + i] = sc[1][rt][i];
       }
-      float mx = x[0];
+      if constexpr (TAIL) {
 #pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+        for (int i = 0; i < 4; ++i) {
+          if (tb + 4 * g + i >= t1) x[i] = -INFINITY;
+          if (tb + 16 + 4 * g + i >= t1) x[4 + i] = -INFINITY;
+        }
+      }
+      float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m[ct], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m[ct] - m_use);
-      float pr[8], psum = 0.f;
+      mx *= c;
+      const bool move = mx > m[rt] + kLazyMax;
+      if (__any(move)) {
+        const float m_new = move ? mx : m[rt];
+        const float alpha = fast_exp2(m[rt] - m_new);
+        l[rt] *= alpha;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pr[i] = fast_exp2(x[i] - m_use);
-        psum += pr[i];
+        for (int b = 0; b < 8; ++b) oacc[rt][b] *= alpha;
+        m[rt] = m_new;
       }
-      l[ct] = l[ct] * alpha + psum;
-      m[ct] = m_new;
+      float pr[8];
 #pragma unroll
-      for (int b = 0; b < 8; ++b) oacc[ct][b] *= alpha;
-      pop[ct] = u32x4{pack2<QBF16>(pr[0], pr[1]), pack2<QBF16>(pr[2], pr[3]),
+      for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(__builtin_fmaf(x[i], c, -m[rt]));
+      l[rt] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+      pop[rt] = u32x4{pack2<QBF16>(pr[0], pr[1]), pack2<QBF16>(pr[2], pr[3]),
                       pack2<QBF16>(pr[4], pr[5]), pack2<QBF16>(pr[6], pr[7])};
     }
+    // ---- P.V on MFMA 16x16x32: V^T operand = two transpose reads (tokens
+    // 4 g + k and 16 + 4 g + k), shared by both row tiles
+    const uint8_t* vsrc = vt + (4 * g + (n >> 2)) * S::VS + 8 * (n & 3);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const u32x4 vop = read_vt(vtile, g, n, b);
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vsrc + 32 * b));
+      const s16x4 v1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vsrc + 16 * S::VS + 32 * b));
+      const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+      const u32x4 vop = {w0.x, w0.y, w1.x, w1.y};
       oacc[0][b] = mma16x16x32<QBF16>(vop, pop[0], oacc[0][b]);
       oacc[1][b] = mma16x16x32<QBF16>(vop, pop[1], oacc[1][b]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) {
-      __syncthreads();              // everyone is done reading buffer buf^1's old block
-      store_block(buf ^ 1, kr, vr);
-      __syncthreads();
-      buf ^= 1;
-    }
+  };
+
+  const int nsteps = (t1 - t0 + kPStep - 1) / kPStep;
+  if (nsteps > 0) {
+    pages(t0);
+    load(t0);
+    store(0);
+    if (nsteps > 1) pages(t0 + kPStep);
+    __syncthreads();
+  }
+  for (int step = 0; step < nsteps; ++step) {
+    const int tb = t0 + kPStep * step;
+    const bool more = step + 1 < nsteps;
+    if (more) load(tb + kPStep);
+    if (step + 2 < nsteps) pages(tb + 2 * kPStep);
+    if (tb + kPStep > t1)
+      compute(tb, step & 1, std::true_type{});
+    else
+      compute(tb, step & 1, std::false_type{});
+    if (more) store((step + 1) & 1);
+    __syncthreads();
   }
 
-  // ---- finalize each column tile
+  // ---- finalize each row tile
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    float lt = l[ct] + __shfl_xor(l[ct], 16);
+  for (int rt = 0; rt < 2; ++rt) {
+    float lt = l[rt] + __shfl_xor(l[rt], 16);
     lt += __shfl_xor(lt, 32);
     float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (KV == kKvE4M3 && p.v_scale) inv *= p.v_scale[h];
-    const float lse2 = lt > 0.f ? m[ct] + fast_log2(lt) : -INFINITY;
-    if (!rok[ct]) continue;
-    const int r = rreq[ct], j = rj[ct];
+    const float lse2 = lt > 0.f ? m[rt] + fast_log2(lt) : -INFINITY;
+    if (!rok[rt]) continue;
+    const int r = rreq[rt], j = rj[rt];
     const ReqInfo ri = p.req_info[r];
     if (ri.n_states <= 1) {
       uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)r * p.Hq + j) * kHeadDim;
 #pragma unroll
       for (int b = 0; b < 8; ++b) {
-        u32x2 w = {pack2<QBF16>(oacc[ct][b][0] * inv, oacc[ct][b][1] * inv),
-                   pack2<QBF16>(oacc[ct][b][2] * inv, oacc[ct][b][3] * inv)};
+        u32x2 w = {pack2<QBF16>(oacc[rt][b][0] * inv, oacc[rt][b][1] * inv),
+                   pack2<QBF16>(oacc[rt][b][2] * inv, oacc[rt][b][3] * inv)};
         *reinterpret_cast<u32x2*>(orow + 16 * b + 4 * g) = w;
       }
       if (g == 0 && p.lse) p.lse[(int64_t)r * p.Hq + j] = lse2 * kLn2;
@@ -507,7 +585,7 @@ __global__ __launch_bounds__(256) void prefix_kernel(DecodeParams p) {
       float* po = p.partial_o + (slot * G + (j - h * G)) * kHeadDim;
 #pragma unroll
       for (int b = 0; b < 8; ++b)
-        *reinterpret_cast<f32x4*>(po + 16 * b + 4 * g) = oacc[ct][b] * inv;
+        *reinterpret_cast<f32x4*>(po + 16 * b + 4 * g) = oacc[rt][b] * inv;
       if (g == 0) p.partial_lse[slot * G + (j - h * G)] = lse2;
     }
   }
@@ -541,9 +619,13 @@ static hipError_t launch_decode_t(const DecodeParams& p, int num_tiles, int wave
 }
 
 template <int KV, bool QBF16>
-static hipError_t launch_prefix_t(const DecodeParams& p, int num_tiles, hipStream_t s) {
+static hipError_t launch_prefix_t(const DecodeParams& p, int num_tiles, int waves, hipStream_t s) {
   if (num_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((prefix_kernel<KV, QBF16>), dim3(num_tiles), dim3(256), 0, s, p);
+  if (waves == 4) {
+    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, 4>), dim3(num_tiles), dim3(256), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, 8>), dim3(num_tiles), dim3(512), 0, s, p);
+  }
   return hipGetLastError();
 }
 
@@ -558,13 +640,14 @@ hipError_t launch_decode(const DecodeParams& p, int num_tiles, int waves, bool q
                 : launch_decode_t<kKvF16, false>(p, num_tiles, waves, s);
 }
 
-hipError_t launch_prefix(const DecodeParams& p, int num_tiles, bool q_bf16, int kv,
+hipError_t launch_prefix(const DecodeParams& p, int num_tiles, int waves, bool q_bf16, int kv,
                          hipStream_t s) {
+  if (waves != 4 && waves != 8) return hipErrorInvalidValue;
   if (kv == kKvE4M3)
-    return q_bf16 ? launch_prefix_t<kKvE4M3, true>(p, num_tiles, s)
-                  : launch_prefix_t<kKvE4M3, false>(p, num_tiles, s);
-  return q_bf16 ? launch_prefix_t<kKvBF16, true>(p, num_tiles, s)
-                : launch_prefix_t<kKvF16, false>(p, num_tiles, s);
+    return q_bf16 ? launch_prefix_t<kKvE4M3, true>(p, num_tiles, waves, s)
+                  : launch_prefix_t<kKvE4M3, false>(p, num_tiles, waves, s);
+  return q_bf16 ? launch_prefix_t<kKvBF16, true>(p, num_tiles, waves, s)
+                : launch_prefix_t<kKvF16, false>(p, num_tiles, waves, s);
 }
 
 }  // namespace fi

@@ -118,8 +118,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 // partial_o [.][kHeadDim] / partial_lse [.] (lse in log2 units):
 //   M = max_c s_c, S = sum_c 2^(s_c - M), o = sum_c 2^(s_c - M) o_c / S,
 //   lse = (M + log2 S) ln 2; all states empty -> o = 0, lse = -inf.
-// Memory round trips: the lse values and the first kMergeBatch rows are
-// independent loads issued together.
+// Lanes read 64 lse values at a time; partial rows are read kMergeBatch at a
+// time with independent loads issued together.
 constexpr int kMergeBatch = 16;
 template <bool OBF16>
 __device__ __forceinline__ void merge_state_row(const float* __restrict__ partial_o,
@@ -127,33 +127,35 @@ __device__ __forceinline__ void merge_state_row(const float* __restrict__ partia
                                                 int64_t row0, int64_t stride, int n,
                                                 uint32_t* orow, float* lse_out, int lane) {
   const float* po = partial_o + row0 * kHeadDim + 2 * lane;
-  float s_lane[2];
-  s_lane[0] = lane < n ? partial_lse[row0 + lane * stride] : -INFINITY;
-  s_lane[1] = lane + 64 < n ? partial_lse[row0 + (lane + 64) * stride] : -INFINITY;
-  f32x2 v[kMergeBatch];
-#pragma unroll
-  for (int k = 0; k < kMergeBatch; ++k)
-    v[k] = k < n ? *reinterpret_cast<const f32x2*>(po + k * stride * kHeadDim) : f32x2{0.f, 0.f};
-  float M = wave_max(fmaxf(s_lane[0], s_lane[1]));
-  for (int c = lane + 128; c - lane < n; c += 64)
-    M = fmaxf(M, wave_max(c < n ? partial_lse[row0 + c * stride] : -INFINITY));
+  float M = -INFINITY;
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    const int c = c0 + lane;
+    M = fmaxf(M, c < n ? partial_lse[row0 + c * stride] : -INFINITY);
+  }
+  M = wave_max(M);
   float a0 = 0.f, a1 = 0.f, S = 0.f;
   if (M != -INFINITY) {
-    const float w0 = fast_exp2(s_lane[0] - M);   // exp2(-inf) = 0 for absent states
-    S = wave_sum(w0 + fast_exp2(s_lane[1] - M));
+    for (int c0 = 0; c0 < n; c0 += 64) {
+      const int c = c0 + lane;
+      const float w = c < n ? fast_exp2(partial_lse[row0 + c * stride] - M) : 0.f;
+      S += w;
+      const int cn = min(64, n - c0);
+      for (int k0 = 0; k0 < cn; k0 += kMergeBatch) {
+        f32x2 v[kMergeBatch];
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
-      const float wk = __shfl(w0, k);
-      a0 += wk * v[k].x;
-      a1 += wk * v[k].y;
+        for (int k = 0; k < kMergeBatch; ++k)
+          v[k] = k0 + k < cn ? *reinterpret_cast<const f32x2*>(
+                                   po + (int64_t)(c0 + k0 + k) * stride * kHeadDim)
+                             : f32x2{0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) {
+          const float wk = __shfl(w, (k0 + k) & 63);
+          a0 += wk * v[k].x;
+          a1 += wk * v[k].y;
+        }
+      }
     }
-    for (int c = kMergeBatch; c < n; ++c) {
-      const float wc = fast_exp2(partial_lse[row0 + c * stride] - M);
-      if (c >= 128) S += wc;
-      const f32x2 vc = *reinterpret_cast<const f32x2*>(po + c * stride * kHeadDim);
-      a0 += wc * vc.x;
-      a1 += wc * vc.y;
-    }
+    S = wave_sum(S);
   }
   const float inv = S > 0.f ? 1.f / S : 0.f;
   orow[lane] = pack2<OBF16>(a0 * inv, a1 * inv);

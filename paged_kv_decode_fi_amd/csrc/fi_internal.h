@@ -9,10 +9,12 @@ namespace fi {
 
 constexpr int kHeadDim = 128;      // head_dim the kernels are built for
 constexpr int kMaxGroup = 16;      // q heads per kv head one MFMA column tile holds
-constexpr int kBlockTokens = 32;   // tokens per inner-loop block
+constexpr int kBlockTokens = 32;   // tokens per cascade-prefix step
+constexpr int kChunkAlign = 16;    // decode chunks are whole 16-token steps
 constexpr int kWavesPerTile = 8;   // waves (= kv heads) per decode workgroup
-constexpr int kPrefixRowsPerWave = 32;                       // 2 column tiles
-constexpr int kPrefixRowsPerTile = kPrefixRowsPerWave * 4;   // 4 waves
+constexpr int kPrefixRowsPerWave = 32;   // 2 MFMA column tiles per wave
+constexpr int kPrefixMaxWaves = 8;       // prefix workgroup: 4 or 8 waves
+constexpr int kPrefixMaxChunk = 4096;    // prefix tokens per tile (page table in LDS)
 constexpr int kMaxMergeStates = 64;
 
 enum TileKind : int32_t { kDecodeTile = 0, kPrefixTile = 1 };
@@ -59,7 +61,7 @@ struct HostPlan {
   int32_t q_dtype, kv_dtype;
   int32_t num_groups;
   int32_t num_cus;
-  int32_t chunk_tokens, prefix_chunk_tokens, heads_per_tile;
+  int32_t chunk_tokens, prefix_chunk_tokens, heads_per_tile, prefix_waves;
   int64_t num_tiles, num_prefix_tiles, num_partials, num_merge_units;
   Tile* tiles;          // num_tiles + num_prefix_tiles entries
   ReqInfo* req_info;    // batch entries

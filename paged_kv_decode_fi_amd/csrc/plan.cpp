@@ -17,7 +17,7 @@
 // behind long tiles.
 //
 // Cascade: the shared prefix of group g is attended once per (g, kv head) by
-// prefix tiles covering kPrefixRowsPerTile query rows each (rows = the
+// prefix tiles covering prefix_rows query rows each (rows = the
 // group's requests x the G q heads of that kv head); the prefix is cut into
 // chunks so that prefix tiles cover the GPU about twice.
 #include <algorithm>
@@ -69,8 +69,8 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   if (ps <= 0) PLAN_FAIL(1, "page_size must be >= 1 (got %d)", ps);
   if (B > 0 && (!in.kv_indptr || !in.last_page_len))
     PLAN_FAIL(1, "kv_indptr and last_page_len (host) are required");
-  if (in.chunk_tokens < 0 || in.chunk_tokens % kBlockTokens != 0)
-    PLAN_FAIL(1, "chunk_tokens must be 0 or a positive multiple of %d", kBlockTokens);
+  if (in.chunk_tokens < 0 || in.chunk_tokens % kChunkAlign != 0)
+    PLAN_FAIL(1, "chunk_tokens must be 0 or a positive multiple of %d", kChunkAlign);
   if (B > 0 && in.kv_indptr[0] != 0) PLAN_FAIL(1, "kv_indptr[0] must be 0");
   std::vector<int64_t> lens(B);
   for (int r = 0; r < B; ++r) {
@@ -112,8 +112,8 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   while (Hkv % hpt) hpt >>= 1;
   const int64_t head_groups = Hkv / hpt;
   const int64_t waves_per_cu = env_int("FI_WAVES_PER_CU", 16);
-  const int64_t c_min = round_up(std::max(env_int("FI_CHUNK_MIN", 64), kBlockTokens),
-                                 kBlockTokens);
+  const int64_t c_min = round_up(std::max(env_int("FI_CHUNK_MIN", 32), kChunkAlign),
+                                 kChunkAlign);
   const int64_t target_waves = std::max<int64_t>(1, num_cus * waves_per_cu);
   int64_t Lmax = 0;
   for (int r = 0; r < B; ++r) Lmax = std::max(Lmax, lens[r]);
@@ -126,30 +126,32 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   if (in.chunk_tokens > 0) {
     chunk = in.chunk_tokens;
   } else {
-    int64_t hi = std::max<int64_t>(round_up(std::max<int64_t>(Lmax, 1), kBlockTokens),
-                                   kBlockTokens);
+    int64_t hi = std::max<int64_t>(round_up(std::max<int64_t>(Lmax, 1), kChunkAlign),
+                                   kChunkAlign);
     int64_t lo = std::min(c_min, hi);
     if (waves_for(hi) >= target_waves) {
       chunk = hi;                       // enough work without splitting
     } else {
-      // smallest c in [lo, hi] (multiple of the block) with waves(c) <= target
-      int64_t a = lo / kBlockTokens, b = hi / kBlockTokens;
+      // smallest c in [lo, hi] (multiple of the step) with waves(c) <= target
+      int64_t a = lo / kChunkAlign, b = hi / kChunkAlign;
       while (a < b) {
         int64_t mid = (a + b) / 2;
-        if (waves_for(mid * kBlockTokens) <= target_waves) b = mid; else a = mid + 1;
+        if (waves_for(mid * kChunkAlign) <= target_waves) b = mid; else a = mid + 1;
       }
-      chunk = a * kBlockTokens;
+      chunk = a * kChunkAlign;
     }
   }
 
   // ---- cascade prefix chunking
+  const int prefix_waves = env_int("FI_PREFIX_WAVES", kPrefixMaxWaves) == 4 ? 4 : 8;
+  const int64_t prefix_rows = (int64_t)kPrefixRowsPerWave * prefix_waves;
   int64_t prefix_chunk = 0;
   std::vector<int64_t> n_pchunks(NG > 0 ? NG : 0, 0);
   int64_t prefix_row_tiles = 0;  // sum over groups of row tiles x Hkv
   if (NG > 0) {
     for (int g = 0; g < NG; ++g) {
       int64_t rows = (int64_t)(in.qo_indptr[g + 1] - in.qo_indptr[g]) * G;
-      if (plens[g] > 0) prefix_row_tiles += ceil_div(rows, kPrefixRowsPerTile) * Hkv;
+      if (plens[g] > 0) prefix_row_tiles += ceil_div(rows, prefix_rows) * Hkv;
     }
     int64_t Lpmax = 0;
     for (int g = 0; g < NG; ++g) Lpmax = std::max(Lpmax, plens[g]);
@@ -159,6 +161,8 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
       prefix_chunk = round_up(ceil_div(Lpmax, n_split), kBlockTokens);
       prefix_chunk = std::max<int64_t>(prefix_chunk, env_int("FI_PREFIX_CHUNK_MIN", 256));
       prefix_chunk = round_up(prefix_chunk, kBlockTokens);
+      // a prefix tile stages its chunk's page indices in LDS (<= 4096 + 2)
+      prefix_chunk = std::min<int64_t>(prefix_chunk, kPrefixMaxChunk);
     }
     for (int g = 0; g < NG; ++g)
       n_pchunks[g] = (plens[g] > 0 && prefix_chunk > 0) ? ceil_div(plens[g], prefix_chunk) : 0;
@@ -222,7 +226,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   for (int g = 0; g < NG; ++g) {
     int64_t rows = (int64_t)(in.qo_indptr[g + 1] - in.qo_indptr[g]) * G;
     if (plens[g] == 0 || rows == 0) continue;
-    int64_t nrt = ceil_div(rows, kPrefixRowsPerTile);
+    int64_t nrt = ceil_div(rows, prefix_rows);
     for (int64_t pc = 0; pc < n_pchunks[g]; ++pc)
       for (int h = 0; h < Hkv; ++h)
         for (int64_t rt = 0; rt < nrt; ++rt) {
@@ -233,8 +237,8 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
           t.t1 = (int32_t)std::min<int64_t>((pc + 1) * prefix_chunk, plens[g]);
           t.slot = (int32_t)pc;
           t.kind = kPrefixTile;
-          t.row0 = (int32_t)(rt * kPrefixRowsPerTile);
-          t.row1 = (int32_t)std::min<int64_t>((rt + 1) * kPrefixRowsPerTile, rows);
+          t.row0 = (int32_t)(rt * prefix_rows);
+          t.row1 = (int32_t)std::min<int64_t>((rt + 1) * prefix_rows, rows);
           pt.push_back(t);
         }
   }
@@ -252,6 +256,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   out->chunk_tokens = (int32_t)chunk;
   out->prefix_chunk_tokens = (int32_t)prefix_chunk;
   out->heads_per_tile = hpt;
+  out->prefix_waves = prefix_waves;
   out->num_partials = slots;
   out->num_merge_units = n_merge;
 

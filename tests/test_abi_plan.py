@@ -60,7 +60,7 @@ def test_host_validation_errors(fi):
     assert _status(fi, [0, 2, 5], [3, 16], kv_dtype="bf16") == 2   # mixed dtype
     assert _status(fi, [0, 2, 5], [3, 16], q_dtype="e4m3", kv_dtype="e4m3") == 2
     assert _status(fi, [0, 2, 5], [3, 16], page_size=0) == 1
-    assert _status(fi, [0, 2, 5], [3, 16], chunk=48) == 1       # not a block multiple
+    assert _status(fi, [0, 2, 5], [3, 16], chunk=40) == 1       # not a step multiple
     msg = fi.lib.fi_last_error().decode()
     assert "chunk_tokens" in msg
 
