@@ -349,7 +349,7 @@ __device__ __forceinline__ int xcd_tile(int b, int n) {
   return x * per + min(x, rem) + k;
 }
 
-template <int KV, bool QBF16, int WAVES>
+template <int KV, bool QBF16, int WAVES, bool PS_POW2>
 __global__ __launch_bounds__(64 * WAVES) void prefix_kernel(DecodeParams p) {
   using S = PStage<KV>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
@@ -400,7 +400,7 @@ __global__ __launch_bounds__(64 * WAVES) void prefix_kernel(DecodeParams p) {
   const uint32_t slot_bytes = (uint32_t)p.Hkv * S::ROWB;
   const int last = t1 - 1;
   auto page_of = [&](int t) -> int {
-    const int pi = ps_shift >= 0 ? (t >> ps_shift) : (t / ps);
+    const int pi = PS_POW2 ? (t >> ps_shift) : (t / ps);
     return p.kv_indices[page_base + pi];
   };
   u32x4 vec[NL];
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(64 * WAVES) void prefix_kernel(DecodeParams p) {
       if (idx >= 2 * PV) continue;
       const int q = idx % PV;
       const int t = min(tb + q / VR, last);
-      const uint32_t sl = ps_shift >= 0 ? (uint32_t)(t & (ps - 1)) : (uint32_t)(t % ps);
+      const uint32_t sl = PS_POW2 ? (uint32_t)(t & (ps - 1)) : (uint32_t)(t % ps);
       const uint64_t off = ((uint64_t)(uint32_t)pg[u] * (uint32_t)ps + sl) * slot_bytes +
                            16 * (q % VR);
       vec[u] = ld_global<u32x4>(idx < PV ? kbase : vbase, off);
@@ -455,9 +455,10 @@ __global__ __launch_bounds__(64 * WAVES) void prefix_kernel(DecodeParams p) {
 #pragma unroll
     for (int b = 0; b < 8; ++b) oacc[rt][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // one 32-token step from LDS buffer buf; TAIL masks tokens past t1
-  auto compute = [&](int tb, int buf, auto tail_tag) {
-    constexpr bool TAIL = decltype(tail_tag)::value;
+  // one 32-token step from LDS buffer buf; a tail step masks tokens past t1
+  // (a uniform branch around the masking only: one copy of the step body
+  // keeps the accumulators in place across iterations)
+  auto compute = [&](int tb, int buf, bool tail) {
     const uint8_t* kt = lds + buf * S::BUF;
     const uint8_t* vt = kt + kPStep * S::KS;
     // ---- scores: S[tt][rt] = K(tokens 16 tt ..) . Q^T(rows of tile rt)
@@ -495,7 +496,7 @@ __global__ __launch_bounds__(64 * WAVES) void prefix_kernel(DecodeParams p) {
         x[i] = sc[0][rt][i];
         x[4 + i] = sc[1][rt][i];
       }
-      if constexpr (TAIL) {
+      if (__builtin_expect(tail, 0)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if (tb + 4 * g + i >= t1) x[i] = -INFINITY;
@@ -552,10 +553,7 @@ __global__ __launch_bounds__(64 * WAVES) void prefix_kernel(DecodeParams p) {
     const bool more = step + 1 < nsteps;
     if (more) load(tb + kPStep);
     if (step + 2 < nsteps) pages(tb + 2 * kPStep);
-    if (tb + kPStep > t1)
-      compute(tb, step & 1, std::true_type{});
-    else
-      compute(tb, step & 1, std::false_type{});
+    compute(tb, step & 1, tb + kPStep > t1);
     if (more) store((step + 1) & 1);
     __syncthreads();
   }
@@ -618,14 +616,22 @@ static hipError_t launch_decode_t(const DecodeParams& p, int num_tiles, int wave
   return hipGetLastError();
 }
 
+template <int KV, bool QBF16, int W>
+static void launch_prefix_w(const DecodeParams& p, int num_tiles, hipStream_t s) {
+  if (p.ps_shift >= 0)
+    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, W, true>), dim3(num_tiles), dim3(64 * W), 0, s, p);
+  else
+    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, W, false>), dim3(num_tiles), dim3(64 * W), 0, s,
+                       p);
+}
+
 template <int KV, bool QBF16>
 static hipError_t launch_prefix_t(const DecodeParams& p, int num_tiles, int waves, hipStream_t s) {
   if (num_tiles <= 0) return hipSuccess;
-  if (waves == 4) {
-    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, 4>), dim3(num_tiles), dim3(256), 0, s, p);
-  } else {
-    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, 8>), dim3(num_tiles), dim3(512), 0, s, p);
-  }
+  if (waves == 4)
+    launch_prefix_w<KV, QBF16, 4>(p, num_tiles, s);
+  else
+    launch_prefix_w<KV, QBF16, 8>(p, num_tiles, s);
   return hipGetLastError();
 }
 
