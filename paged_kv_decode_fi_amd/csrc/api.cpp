@@ -36,6 +36,11 @@ struct fi_plan_s {
   char* workspace;
   size_t workspace_bytes;
   void* staging;  // pinned copy of the work list, merge map and request info
+  // cascade plans: the prefix kernel (MFMA-bound) runs on a side stream next
+  // to the suffix decode (HBM-bound); fork/join events order it against the
+  // caller's stream, so the pair is also capturable into a graph
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
 };
 
 namespace {
@@ -229,6 +234,16 @@ fi_status fi_plan(const fi_problem* problem, int32_t num_cus, void* workspace,
   pl->workspace = reinterpret_cast<char*>(workspace);
   pl->workspace_bytes = workspace_bytes;
   pl->staging = staging;
+  const char* ov = getenv("FI_CASCADE_OVERLAP");
+  if (hp.num_prefix_tiles > 0 && hp.num_tiles > 0 && ov && atoi(ov) != 0) {
+    e = hipStreamCreateWithFlags(&pl->side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&pl->fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&pl->join, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      fi_plan_destroy(pl);
+      return hip_fail(e, "creating the cascade side stream");
+    }
+  }
   *plan_out = pl;
   return FI_OK;
 }
@@ -236,6 +251,9 @@ fi_status fi_plan(const fi_problem* problem, int32_t num_cus, void* workspace,
 fi_status fi_plan_destroy(fi_plan_t plan) {
   if (!plan) return FI_OK;
   if (plan->staging) (void)hipHostFree(plan->staging);
+  if (plan->fork) (void)hipEventDestroy(plan->fork);
+  if (plan->join) (void)hipEventDestroy(plan->join);
+  if (plan->side) (void)hipStreamDestroy(plan->side);
   fi::plan_free(&plan->hp);
   delete plan;
   return FI_OK;
@@ -316,14 +334,26 @@ fi_status fi_cascade_decode(fi_plan_t plan, const void* q, const void* k_pages,
   pp.kv_indices = prefix_kv_indices;
   pp.qo_indptr = reinterpret_cast<const int32_t*>(plan->workspace + hp.layout.qo_indptr_off);
   hipError_t e = hipSuccess;
+  const bool overlap = plan->side != nullptr;
+  if (overlap) {
+    e = hipEventRecord(plan->fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(plan->side, plan->fork, 0);
+    if (e != hipSuccess) return hip_fail(e, "forking the prefix stream");
+  }
   if (hp.num_prefix_tiles > 0) {
-    e = fi::launch_prefix(pp, (int)hp.num_prefix_tiles, hp.prefix_waves, qbf, kv, s);
+    e = fi::launch_prefix(pp, (int)hp.num_prefix_tiles, hp.prefix_waves, qbf, kv,
+                          overlap ? plan->side : s);
     if (e != hipSuccess) return hip_fail(e, "prefix launch");
   }
   p.kv_indptr = kv_indptr;
   p.kv_indices = kv_indices;
   e = fi::launch_decode(p, (int)hp.num_tiles, hp.heads_per_tile, qbf, kv, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (overlap) {
+    e = hipEventRecord(plan->join, plan->side);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, plan->join, 0);
+    if (e != hipSuccess) return hip_fail(e, "joining the prefix stream");
+  }
   return launch_merge(plan, o, lse, s);
 }
 

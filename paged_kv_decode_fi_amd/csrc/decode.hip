@@ -320,18 +320,25 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
 // ============================================================================
 // cascade prefix tiles: many query rows x one prefix chunk of one kv head.
 // ============================================================================
-// Workgroup = kPrefixWaves waves; wave w owns query rows row0 + 32 w + 16 rt + n
+// Workgroup = WAVES waves; wave w owns query rows row0 + 32 w + 16 rt + n
 // (rt = 0, 1) as the N columns of its MFMAs, so each K/V element staged in LDS
-// serves 256 rows.  Per 32-token step: the workgroup loads the step's K and V
-// rows of the tile's kv head (one 16-byte vector per thread per pool) into
-// one of two LDS buffers while the other is computed, one barrier per step;
-// scores on MFMA 16x16x32 (K operand read just in time from LDS, q in
-// registers), online softmax per row (lazy max), P.V on MFMA 16x16x16 with
-// V^T from transpose reads.  The prefix is reused across row tiles, so its
-// loads use the default (cached) policy, and the block -> tile map puts all
-// row tiles of one (head, chunk) on the same XCD (workgroups are dispatched
-// to the 8 XCDs round-robin) so they share that XCD's L2.
+// serves 32 WAVES rows.  The tile's slice of the page table is copied to LDS
+// once.  Per 32-token step the workgroup loads the step's K and V rows of the
+// tile's kv head (NL 16-byte vectors per thread) two steps ahead into
+// registers, stores them to one of two LDS buffers after computing from the
+// other, one barrier per step.  Scores: MFMA 16x16x32 with every K operand of
+// the step read from LDS up front; the V^T operands (transpose reads) are
+// issued before the softmax so their latency hides under it.  Softmax: the
+// probabilities are formed against the running max m; only when a lane's sum
+// of them exceeds kPrefixLazySum (or is not finite: the first step, where m =
+// -inf) does the wave take the exact row max, rescale and recompute, so the
+// common step carries no max reduction.  P.V: MFMA 16x16x32.  The prefix is
+// reused across row tiles, so its loads use the default (cached) policy, and
+// the block -> tile map puts all row tiles of one (head, chunk) on the same
+// XCD (workgroups are dispatched to the 8 XCDs round-robin) so they share
+// that XCD's L2.
 constexpr int kPStep = 32;
+constexpr float kPrefixLazySum = 256.f;
 
 template <int KV>
 struct PStage {
@@ -339,7 +346,8 @@ struct PStage {
   static constexpr int KS = ROWB + 16;                      // K LDS row stride
   static constexpr int VS = 256 + 32;                       // V LDS row stride (16-bit values)
   static constexpr int BUF = kPStep * (KS + VS);
-  static constexpr int LDS = 2 * BUF;
+  static constexpr int PTAB = kPrefixMaxChunk + 2;          // page-table slots (page_size 1)
+  static constexpr int LDS = 2 * BUF + 4 * PTAB;
 };
 
 // XCD-aware map: block b runs on XCD b % 8; give each XCD a contiguous range
@@ -353,6 +361,7 @@ template <int KV, bool QBF16, int WAVES, bool PS_POW2>
 __global__ __launch_bounds__(64 * WAVES) void prefix_kernel(DecodeParams p) {
   using S = PStage<KV>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
+  int* ptab = reinterpret_cast<int*>(lds + 2 * S::BUF);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -363,6 +372,14 @@ __global__ __launch_bounds__(64 * WAVES) void prefix_kernel(DecodeParams p) {
   const int qo0 = p.qo_indptr[grp];
   const int page_base = p.kv_indptr[grp];
   const int ps = p.page_size, ps_shift = p.ps_shift;
+  auto page_idx = [&](int t) { return PS_POW2 ? (t >> ps_shift) : (t / ps); };
+  const int nsteps = (t1 - t0 + kPStep - 1) / kPStep;
+  if (nsteps <= 0) return;   // the plan emits no empty prefix tiles
+  const int pfirst = page_idx(t0);
+  {
+    const int np = page_idx(t1 - 1) - pfirst + 1;   // <= chunk / page_size + 1 < PTAB
+    for (int i = tid; i < np; i += 64 * WAVES) ptab[i] = p.kv_indices[page_base + pfirst + i];
+  }
 
   // query rows of this lane's two column tiles (B operands of the scores)
   u32x4 qop[2][4];
@@ -399,39 +416,27 @@ __global__ __launch_bounds__(64 * WAVES) void prefix_kernel(DecodeParams p) {
   const char* vbase = reinterpret_cast<const char*>(p.v_pages) + (int64_t)h * S::ROWB;
   const uint32_t slot_bytes = (uint32_t)p.Hkv * S::ROWB;
   const int last = t1 - 1;
-  auto page_of = [&](int t) -> int {
-    const int pi = PS_POW2 ? (t >> ps_shift) : (t / ps);
-    return p.kv_indices[page_base + pi];
-  };
-  u32x4 vec[NL];
-  int pg[NL];   // page of each vector's token in the next step to load
-  auto pages = [&](int tb) {
+  auto load = [&](int tb, u32x4 (&vec)[NL]) {
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
       const int idx = tid + u * T;
-      pg[u] = page_of(min(tb + (idx % PV) / VR, last));
-    }
-  };
-  auto load = [&](int tb) {
-#pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      const int idx = tid + u * T;
-      if (idx >= 2 * PV) continue;
+      if (2 * PV % T != 0 && idx >= 2 * PV) continue;
       const int q = idx % PV;
       const int t = min(tb + q / VR, last);
-      const uint32_t sl = PS_POW2 ? (uint32_t)(t & (ps - 1)) : (uint32_t)(t % ps);
-      const uint64_t off = ((uint64_t)(uint32_t)pg[u] * (uint32_t)ps + sl) * slot_bytes +
-                           16 * (q % VR);
+      const int pi = page_idx(t);
+      const uint32_t sl = PS_POW2 ? (uint32_t)(t & (ps - 1)) : (uint32_t)(t - pi * ps);
+      const uint32_t page = (uint32_t)ptab[pi - pfirst];
+      const uint64_t off = ((uint64_t)page * (uint32_t)ps + sl) * slot_bytes + 16 * (q % VR);
       vec[u] = ld_global<u32x4>(idx < PV ? kbase : vbase, off);
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, const u32x4 (&vec)[NL]) {
     uint8_t* kt = lds + buf * S::BUF;
     uint8_t* vt = kt + kPStep * S::KS;
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
       const int idx = tid + u * T;
-      if (idx >= 2 * PV) continue;
+      if (2 * PV % T != 0 && idx >= 2 * PV) continue;
       const int q = idx % PV;
       const int tok = q / VR, chk = q % VR;
       if (idx < PV) {
@@ -461,32 +466,48 @@ __global__ __launch_bounds__(64 * WAVES) void prefix_kernel(DecodeParams p) {
   auto compute = [&](int tb, int buf, bool tail) {
     const uint8_t* kt = lds + buf * S::BUF;
     const uint8_t* vt = kt + kPStep * S::KS;
-    // ---- scores: S[tt][rt] = K(tokens 16 tt ..) . Q^T(rows of tile rt)
-    f32x4 sc[2][2];
+    // ---- K operands of both token tiles (tokens 16 tt + n), all k slices
+    u32x4 kop[2][4];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      sc[tt][0] = sc[tt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
       const uint8_t* krow = kt + (16 * tt + n) * S::KS;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        u32x4 kop;
         if constexpr (F8) {
           const u32x2 w8 = *reinterpret_cast<const u32x2*>(krow + 32 * s + 8 * g);
           const u32x2 a = e4m3x4_to_16<QBF16>(w8.x), b = e4m3x4_to_16<QBF16>(w8.y);
-          kop = u32x4{a.x, a.y, b.x, b.y};
+          kop[tt][s] = u32x4{a.x, a.y, b.x, b.y};
         } else {
-          kop = *reinterpret_cast<const u32x4*>(krow + 64 * s + 16 * g);
+          kop[tt][s] = *reinterpret_cast<const u32x4*>(krow + 64 * s + 16 * g);
         }
-        sc[tt][0] = mma16x16x32<QBF16>(kop, qop[0][s], sc[tt][0]);
-        sc[tt][1] = mma16x16x32<QBF16>(kop, qop[1][s], sc[tt][1]);
-        // keep each operand read next to its MFMAs (register pressure)
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // ---- online softmax per row tile.  c > 0, so the max is taken on the
-    // raw scores and the scale rides in the exponent's FMA: p = 2^(s c - m).
-    // P^T operand of the 16x16x32 P.V: contraction element kk of lane group g
-    // is token 4 g + (kk & 3) + 16 (kk >> 2) = score tile kk >> 2, entry kk & 3.
+    // ---- V^T operands: contraction element kk of lane group g is token
+    // 4 g + (kk & 3) + 16 (kk >> 2); two transpose reads per dim block b
+    u32x4 vop[8];
+    const uint8_t* vsrc = vt + (4 * g + (n >> 2)) * S::VS + 8 * (n & 3);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vsrc + 32 * b));
+      const s16x4 v1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vsrc + 16 * S::VS + 32 * b));
+      const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+      vop[b] = u32x4{w0.x, w0.y, w1.x, w1.y};
+    }
+    // ---- scores: S[tt][rt] = K(tokens 16 tt ..) . Q^T(rows of tile rt);
+    // the four accumulators are independent, so consecutive MFMAs never wait
+    f32x4 sc[2][2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) sc[tt][0] = sc[tt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+          sc[tt][rt] = mma16x16x32<QBF16>(kop[tt][s], qop[rt][s], sc[tt][rt]);
+    // ---- softmax per row tile: lane (g, n) holds tokens 4 g + i and
+    // 16 + 4 g + i (i < 4) of row n
     u32x4 pop[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
@@ -503,59 +524,58 @@ __global__ __launch_bounds__(64 * WAVES) void prefix_kernel(DecodeParams p) {
           if (tb + 16 + 4 * g + i >= t1) x[4 + i] = -INFINITY;
         }
       }
-      float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      mx *= c;
-      const bool move = mx > m[rt] + kLazyMax;
-      if (__any(move)) {
-        const float m_new = move ? mx : m[rt];
+      float pr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(__builtin_fmaf(x[i], c, -m[rt]));
+      float sum = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+      if (__builtin_expect(__any(!(sum <= kPrefixLazySum)), 0)) {
+        // exact row max of this step (every step holds at least one valid
+        // token, so mx is finite), rescale, recompute
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mx = fmaxf(mx, x[i] * c);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m[rt], mx);
         const float alpha = fast_exp2(m[rt] - m_new);
         l[rt] *= alpha;
 #pragma unroll
         for (int b = 0; b < 8; ++b) oacc[rt][b] *= alpha;
         m[rt] = m_new;
-      }
-      float pr[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(__builtin_fmaf(x[i], c, -m[rt]));
-      l[rt] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+        for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(__builtin_fmaf(x[i], c, -m_new));
+        sum = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+      }
+      l[rt] += sum;
       pop[rt] = u32x4{pack2<QBF16>(pr[0], pr[1]), pack2<QBF16>(pr[2], pr[3]),
                       pack2<QBF16>(pr[4], pr[5]), pack2<QBF16>(pr[6], pr[7])};
     }
-    // ---- P.V on MFMA 16x16x32: V^T operand = two transpose reads (tokens
-    // 4 g + k and 16 + 4 g + k), shared by both row tiles
-    const uint8_t* vsrc = vt + (4 * g + (n >> 2)) * S::VS + 8 * (n & 3);
+    // ---- P.V on MFMA 16x16x32
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vsrc + 32 * b));
-      const s16x4 v1 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vsrc + 16 * S::VS + 32 * b));
-      const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
-      const u32x4 vop = {w0.x, w0.y, w1.x, w1.y};
-      oacc[0][b] = mma16x16x32<QBF16>(vop, pop[0], oacc[0][b]);
-      oacc[1][b] = mma16x16x32<QBF16>(vop, pop[1], oacc[1][b]);
-      __builtin_amdgcn_sched_barrier(0);
+      oacc[0][b] = mma16x16x32<QBF16>(vop[b], pop[0], oacc[0][b]);
+      oacc[1][b] = mma16x16x32<QBF16>(vop[b], pop[1], oacc[1][b]);
     }
   };
 
-  const int nsteps = (t1 - t0 + kPStep - 1) / kPStep;
-  if (nsteps > 0) {
-    pages(t0);
-    load(t0);
-    store(0);
-    if (nsteps > 1) pages(t0 + kPStep);
-    __syncthreads();
-  }
-  for (int step = 0; step < nsteps; ++step) {
+  // two register sets: the one for step s + 1 is in flight while step s is
+  // computed, the one for step s + 2 is issued at the start of step s
+  u32x4 va[NL], vb[NL];
+  __syncthreads();   // page table
+  load(t0, va);
+  store(0, va);
+  if (nsteps > 1) load(t0 + kPStep, vb);
+  __syncthreads();
+  auto step_body = [&](int step, u32x4 (&nxt)[NL], u32x4 (&aft)[NL]) {
     const int tb = t0 + kPStep * step;
-    const bool more = step + 1 < nsteps;
-    if (more) load(tb + kPStep);
-    if (step + 2 < nsteps) pages(tb + 2 * kPStep);
+    if (step + 2 < nsteps) load(tb + 2 * kPStep, aft);
     compute(tb, step & 1, tb + kPStep > t1);
-    if (more) store((step + 1) & 1);
+    if (step + 1 < nsteps) store((step + 1) & 1, nxt);
     __syncthreads();
+  };
+  for (int step = 0; step < nsteps; step += 2) {
+    step_body(step, vb, va);
+    if (step + 1 < nsteps) step_body(step + 1, va, vb);
   }
 
   // ---- finalize each row tile

@@ -56,18 +56,16 @@ __device__ __forceinline__ int64_t page_slot(const int32_t* __restrict__ kv_indi
 }
 
 // ---- conversions ----------------------------------------------------------------
-// Two packed fp32 -> two packed 16-bit floats (round to nearest even).
+// Two fp32 -> two packed 16-bit floats (round to nearest even), one packed
+// convert instruction on gfx950.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 template <bool BF16>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-  if constexpr (BF16) {
-    __bf16 x = (__bf16)a, y = (__bf16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
-  } else {
-    _Float16 x = (_Float16)a, y = (_Float16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
-  }
+  if constexpr (BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
 }
 
 // Four OCP e4m3fn codes (one dword) -> four 16-bit floats (two dwords), exact.

@@ -231,3 +231,37 @@ def test_graph_capture_replays(fi):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, o_e) and torch.equal(lse, l_e), f"replay {i}"
+
+
+@pytest.mark.gpu
+def test_cascade_graph_capture_replays(fi):
+    """The cascade run forks the prefix kernel onto the plan's side stream and
+    joins it back with events: capture the whole call into a graph and check
+    that every replay equals the eager result."""
+    import torch
+    w = W.make("cascade256", small=True)
+    d = C.Dev(w)
+    plan = C.make_plan(w)
+    args = (d.q, d.k, d.v, d.p_indptr, d.p_indices, d.p_last, d.indptr, d.indices, d.last)
+    o_e, l_e = plan.cascade_run(*args, sm_scale=w.sm_scale)
+    torch.cuda.synchronize()
+    o_e, l_e = o_e.clone(), l_e.clone()
+    o = torch.empty_like(o_e)
+    lse = torch.empty_like(l_e)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        plan.cascade_run(*args, sm_scale=w.sm_scale, o=o, lse=lse)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_e) and torch.equal(lse, l_e), "side-stream run"
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan.cascade_run(*args, sm_scale=w.sm_scale, o=o, lse=lse)
+    for i in range(3):
+        o.fill_(0)
+        lse.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_e) and torch.equal(lse, l_e), f"replay {i}"
