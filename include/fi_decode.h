@@ -217,6 +217,25 @@ fi_status fi_debug_gather(int32_t batch, int32_t page_size,
                           const int64_t* token_indptr, int64_t* out_slots,
                           void* stream);
 
+/* fi_debug_run_stage: enqueues ONE kernel of a planned run, with the launch
+ * configuration the full run uses, so that kernel can be timed or checked
+ * on its own.  Arguments as fi_cascade_decode; for a plan without a cascade
+ * level the three prefix tables may be NULL.  stage 0 = the decode kernel
+ * over the per-request pages, stage 1 = the cascade prefix kernel (plans
+ * with prefix tiles only).  Rows whose state is not split are written to o
+ * / lse as in the full run; split rows write their partial states to the
+ * workspace and are NOT merged, so their o / lse are left untouched.
+ * Errors as fi_cascade_decode, plus FI_ERR_INVALID_ARG for another stage. */
+fi_status fi_debug_run_stage(fi_plan_t plan, int32_t stage, const void* q,
+                             const void* k_pages, const void* v_pages,
+                             const int32_t* prefix_kv_indptr,
+                             const int32_t* prefix_kv_indices,
+                             const int32_t* prefix_last_page_len,
+                             const int32_t* kv_indptr, const int32_t* kv_indices,
+                             const int32_t* last_page_len, const float* k_scale,
+                             const float* v_scale, float sm_scale, void* o,
+                             float* lse, void* stream);
+
 /* fi_debug_stream_read: reads `bytes` (multiple of 16) of device memory at
  * src with 16-byte loads from num_blocks workgroups of 256 threads and
  * writes one folded word per thread to sink (device uint32

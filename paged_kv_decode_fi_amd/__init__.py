@@ -27,7 +27,7 @@ STATUS = {0: "FI_OK", 1: "FI_ERR_INVALID_ARG", 2: "FI_ERR_UNSUPPORTED",
 EXPORTS = ("fi_plan", "fi_plan_destroy", "fi_plan_get_stats", "fi_decode_run",
            "fi_cascade_decode", "fi_merge_states", "fi_status_string",
            "fi_last_error", "fi_debug_plan_tiles", "fi_debug_gather",
-           "fi_debug_stream_read")
+           "fi_debug_stream_read", "fi_debug_run_stage")
 
 
 class FiError(RuntimeError):
@@ -83,6 +83,8 @@ def _load() -> ctypes.CDLL:
     L.fi_decode_run.argtypes = [P, P, P, P, P, P, P, P, P, F, P, P, P]
     L.fi_cascade_decode.restype = ctypes.c_int
     L.fi_cascade_decode.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, F, P, P, P]
+    L.fi_debug_run_stage.restype = ctypes.c_int
+    L.fi_debug_run_stage.argtypes = [P, I32, P, P, P, P, P, P, P, P, P, P, P, F, P, P, P]
     L.fi_merge_states.restype = ctypes.c_int
     L.fi_merge_states.argtypes = [I32, ctypes.POINTER(P), ctypes.POINTER(P), I64, I32,
                                   ctypes.c_int, P, P, ctypes.c_int, P]
@@ -276,6 +278,22 @@ class Plan:
                                      _ptr(kv_indices), _ptr(last_page_len),
                                      _ptr(k_scale), _ptr(v_scale), float(sm_scale),
                                      _ptr(o), _ptr(lse), _stream(stream)))
+        return o, lse
+
+    def run_stage(self, stage, q, k_pages, v_pages, kv_indptr, kv_indices, last_page_len,
+                  prefix_kv_indptr=None, prefix_kv_indices=None, prefix_last_page_len=None,
+                  k_scale=None, v_scale=None, sm_scale: float = 0.0, o=None, lse=None,
+                  stream=None):
+        """Test / timing hook: ONE kernel of the planned run (stage 0 = decode
+        kernel, 1 = cascade prefix kernel), without the merge."""
+        self._check_q(q)
+        self._check_pool(k_pages, v_pages)
+        o, lse = self._outputs(q, o, lse)
+        _check(_get_lib().fi_debug_run_stage(
+            self.handle, int(stage), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+            _ptr(prefix_kv_indptr), _ptr(prefix_kv_indices), _ptr(prefix_last_page_len),
+            _ptr(kv_indptr), _ptr(kv_indices), _ptr(last_page_len), _ptr(k_scale),
+            _ptr(v_scale), float(sm_scale), _ptr(o), _ptr(lse), _stream(stream)))
         return o, lse
 
     def destroy(self):

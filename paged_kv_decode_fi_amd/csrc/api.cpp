@@ -274,6 +274,79 @@ fi_status fi_plan_get_stats(fi_plan_t plan, fi_plan_stats* s) {
   return FI_OK;
 }
 
+namespace {
+
+enum Stage { kStagePrefix = 1, kStageDecode = 2, kStageMerge = 4 };
+
+// Shared argument checks of the run calls; prefix tables are required only
+// when the plan has a cascade level.
+fi_status check_run_args(const fi::HostPlan& hp, const void* q, const void* k_pages,
+                         const void* v_pages, const int32_t* prefix_kv_indptr,
+                         const int32_t* prefix_kv_indices, const int32_t* prefix_last_page_len,
+                         const int32_t* kv_indptr, const int32_t* kv_indices,
+                         const int32_t* last_page_len, float sm_scale, const void* o) {
+  if (!q || !o || !kv_indptr || !last_page_len)
+    return fail(FI_ERR_INVALID_ARG, "q, o, kv_indptr and last_page_len must be non-NULL");
+  if (hp.num_groups > 0 && (!prefix_kv_indptr || !prefix_last_page_len))
+    return fail(FI_ERR_INVALID_ARG, "the prefix indptr / last_page_len tables must be non-NULL");
+  if ((hp.num_tiles > 0 || hp.num_prefix_tiles > 0) && (!k_pages || !v_pages))
+    return fail(FI_ERR_INVALID_ARG, "k_pages and v_pages must be non-NULL");
+  if ((!kv_indices && hp.num_tiles > 0) || (!prefix_kv_indices && hp.num_prefix_tiles > 0))
+    return fail(FI_ERR_INVALID_ARG, "the index tables must be non-NULL");
+  if (!(sm_scale == sm_scale) || std::isinf(sm_scale))
+    return fail(FI_ERR_INVALID_ARG, "sm_scale must be finite");
+  return FI_OK;
+}
+
+// Enqueues the selected stages of a planned run on stream s, in order
+// prefix -> decode -> merge (the prefix on the plan's side stream when the
+// plan has one).
+fi_status enqueue_run(fi_plan_t plan, int stages, const void* q, const void* k_pages,
+                      const void* v_pages, const int32_t* prefix_kv_indptr,
+                      const int32_t* prefix_kv_indices, const int32_t* kv_indptr,
+                      const int32_t* kv_indices, const float* k_scale, const float* v_scale,
+                      float sm_scale, void* o, float* lse, hipStream_t s) {
+  const fi::HostPlan& hp = plan->hp;
+  const bool qbf = hp.q_dtype == FI_BF16;
+  const int kv = hp.kv_dtype == FI_E4M3 ? 2 : (qbf ? 1 : 0);
+  fi::DecodeParams p = base_params(plan, q, k_pages, v_pages, k_scale, v_scale, sm_scale, o, lse);
+  hipError_t e = hipSuccess;
+  const bool do_prefix = (stages & kStagePrefix) && hp.num_prefix_tiles > 0;
+  const bool do_decode = (stages & kStageDecode) && hp.num_tiles > 0;
+  const bool overlap = plan->side != nullptr && do_prefix && do_decode;
+  if (overlap) {
+    e = hipEventRecord(plan->fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(plan->side, plan->fork, 0);
+    if (e != hipSuccess) return hip_fail(e, "forking the prefix stream");
+  }
+  if (do_prefix) {
+    // prefix tiles read the group-level table; row -> request = the group's
+    // first request (planned copy of prefix_qo_indptr) + row / G
+    fi::DecodeParams pp = p;
+    pp.kv_indptr = prefix_kv_indptr;
+    pp.kv_indices = prefix_kv_indices;
+    pp.qo_indptr = reinterpret_cast<const int32_t*>(plan->workspace + hp.layout.qo_indptr_off);
+    e = fi::launch_prefix(pp, (int)hp.num_prefix_tiles, hp.prefix_waves, qbf, kv,
+                          overlap ? plan->side : s);
+    if (e != hipSuccess) return hip_fail(e, "prefix launch");
+  }
+  if (do_decode) {
+    p.kv_indptr = kv_indptr;
+    p.kv_indices = kv_indices;
+    e = fi::launch_decode(p, (int)hp.num_tiles, hp.heads_per_tile, qbf, kv, s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+  }
+  if (overlap) {
+    e = hipEventRecord(plan->join, plan->side);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, plan->join, 0);
+    if (e != hipSuccess) return hip_fail(e, "joining the prefix stream");
+  }
+  if (stages & kStageMerge) return launch_merge(plan, o, lse, s);
+  return FI_OK;
+}
+
+}  // namespace
+
 fi_status fi_decode_run(fi_plan_t plan, const void* q, const void* k_pages,
                         const void* v_pages, const int32_t* kv_indptr,
                         const int32_t* kv_indices, const int32_t* last_page_len,
@@ -285,22 +358,12 @@ fi_status fi_decode_run(fi_plan_t plan, const void* q, const void* k_pages,
   if (hp.num_groups != 0)
     return fail(FI_ERR_INVALID_ARG, "plan has a cascade level: use fi_cascade_decode");
   if (hp.batch == 0) return FI_OK;
-  if (!q || !o || !kv_indptr || !last_page_len)
-    return fail(FI_ERR_INVALID_ARG, "q, o, kv_indptr and last_page_len must be non-NULL");
-  const bool any_keys = hp.num_tiles > 0;
-  if (any_keys && (!k_pages || !v_pages || !kv_indices))
-    return fail(FI_ERR_INVALID_ARG, "k_pages, v_pages and kv_indices must be non-NULL");
-  if (!(sm_scale == sm_scale) || std::isinf(sm_scale))
-    return fail(FI_ERR_INVALID_ARG, "sm_scale must be finite");
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  fi::DecodeParams p = base_params(plan, q, k_pages, v_pages, k_scale, v_scale, sm_scale, o, lse);
-  p.kv_indptr = kv_indptr;
-  p.kv_indices = kv_indices;
-  hipError_t e = fi::launch_decode(p, (int)hp.num_tiles, hp.heads_per_tile,
-                                   hp.q_dtype == FI_BF16,
-                                   hp.kv_dtype == FI_E4M3 ? 2 : (hp.q_dtype == FI_BF16 ? 1 : 0), s);
-  if (e != hipSuccess) return hip_fail(e, "decode launch");
-  return launch_merge(plan, o, lse, s);
+  fi_status st = check_run_args(hp, q, k_pages, v_pages, nullptr, nullptr, nullptr, kv_indptr,
+                                kv_indices, last_page_len, sm_scale, o);
+  if (st != FI_OK) return st;
+  return enqueue_run(plan, kStageDecode | kStageMerge, q, k_pages, v_pages, nullptr, nullptr,
+                     kv_indptr, kv_indices, k_scale, v_scale, sm_scale, o, lse,
+                     reinterpret_cast<hipStream_t>(stream));
 }
 
 fi_status fi_cascade_decode(fi_plan_t plan, const void* q, const void* k_pages,
@@ -316,45 +379,37 @@ fi_status fi_cascade_decode(fi_plan_t plan, const void* q, const void* k_pages,
   if (hp.num_groups == 0)
     return fail(FI_ERR_INVALID_ARG, "plan has no cascade level: use fi_decode_run");
   if (hp.batch == 0) return FI_OK;
-  if (!q || !o || !kv_indptr || !last_page_len || !prefix_kv_indptr || !prefix_last_page_len)
-    return fail(FI_ERR_INVALID_ARG, "q, o and the indptr / last_page_len tables must be non-NULL");
-  if (!k_pages || !v_pages || (!kv_indices && hp.num_tiles > 0) ||
-      (!prefix_kv_indices && hp.num_prefix_tiles > 0))
-    return fail(FI_ERR_INVALID_ARG, "k_pages, v_pages and the index tables must be non-NULL");
-  if (!(sm_scale == sm_scale) || std::isinf(sm_scale))
-    return fail(FI_ERR_INVALID_ARG, "sm_scale must be finite");
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const bool qbf = hp.q_dtype == FI_BF16;
-  const int kv = hp.kv_dtype == FI_E4M3 ? 2 : (qbf ? 1 : 0);
-  fi::DecodeParams p = base_params(plan, q, k_pages, v_pages, k_scale, v_scale, sm_scale, o, lse);
-  // prefix tiles read the group-level table; row -> request = the group's
-  // first request (planned copy of prefix_qo_indptr) + row / G
-  fi::DecodeParams pp = p;
-  pp.kv_indptr = prefix_kv_indptr;
-  pp.kv_indices = prefix_kv_indices;
-  pp.qo_indptr = reinterpret_cast<const int32_t*>(plan->workspace + hp.layout.qo_indptr_off);
-  hipError_t e = hipSuccess;
-  const bool overlap = plan->side != nullptr;
-  if (overlap) {
-    e = hipEventRecord(plan->fork, s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(plan->side, plan->fork, 0);
-    if (e != hipSuccess) return hip_fail(e, "forking the prefix stream");
-  }
-  if (hp.num_prefix_tiles > 0) {
-    e = fi::launch_prefix(pp, (int)hp.num_prefix_tiles, hp.prefix_waves, qbf, kv,
-                          overlap ? plan->side : s);
-    if (e != hipSuccess) return hip_fail(e, "prefix launch");
-  }
-  p.kv_indptr = kv_indptr;
-  p.kv_indices = kv_indices;
-  e = fi::launch_decode(p, (int)hp.num_tiles, hp.heads_per_tile, qbf, kv, s);
-  if (e != hipSuccess) return hip_fail(e, "decode launch");
-  if (overlap) {
-    e = hipEventRecord(plan->join, plan->side);
-    if (e == hipSuccess) e = hipStreamWaitEvent(s, plan->join, 0);
-    if (e != hipSuccess) return hip_fail(e, "joining the prefix stream");
-  }
-  return launch_merge(plan, o, lse, s);
+  fi_status st = check_run_args(hp, q, k_pages, v_pages, prefix_kv_indptr, prefix_kv_indices,
+                                prefix_last_page_len, kv_indptr, kv_indices, last_page_len,
+                                sm_scale, o);
+  if (st != FI_OK) return st;
+  return enqueue_run(plan, kStagePrefix | kStageDecode | kStageMerge, q, k_pages, v_pages,
+                     prefix_kv_indptr, prefix_kv_indices, kv_indptr, kv_indices, k_scale,
+                     v_scale, sm_scale, o, lse, reinterpret_cast<hipStream_t>(stream));
+}
+
+fi_status fi_debug_run_stage(fi_plan_t plan, int32_t stage, const void* q, const void* k_pages,
+                             const void* v_pages, const int32_t* prefix_kv_indptr,
+                             const int32_t* prefix_kv_indices,
+                             const int32_t* prefix_last_page_len, const int32_t* kv_indptr,
+                             const int32_t* kv_indices, const int32_t* last_page_len,
+                             const float* k_scale, const float* v_scale, float sm_scale,
+                             void* o, float* lse, void* stream) {
+  g_last_error.clear();
+  if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
+  const fi::HostPlan& hp = plan->hp;
+  if (stage != 0 && stage != 1)
+    return fail(FI_ERR_INVALID_ARG, "stage must be 0 (decode kernel) or 1 (prefix kernel)");
+  if (stage == 1 && hp.num_prefix_tiles == 0)
+    return fail(FI_ERR_INVALID_ARG, "the plan has no cascade prefix tiles");
+  if (hp.batch == 0) return FI_OK;
+  fi_status st = check_run_args(hp, q, k_pages, v_pages, prefix_kv_indptr, prefix_kv_indices,
+                                prefix_last_page_len, kv_indptr, kv_indices, last_page_len,
+                                sm_scale, o);
+  if (st != FI_OK) return st;
+  return enqueue_run(plan, stage == 0 ? kStageDecode : kStagePrefix, q, k_pages, v_pages,
+                     prefix_kv_indptr, prefix_kv_indices, kv_indptr, kv_indices, k_scale,
+                     v_scale, sm_scale, o, lse, reinterpret_cast<hipStream_t>(stream));
 }
 
 fi_status fi_merge_states(int32_t num_states, const void* const* v_states,

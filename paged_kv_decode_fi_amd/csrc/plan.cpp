@@ -156,7 +156,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
     int64_t Lpmax = 0;
     for (int g = 0; g < NG; ++g) Lpmax = std::max(Lpmax, plens[g]);
     if (prefix_row_tiles > 0) {
-      const int64_t want = std::max<int64_t>(1, (int64_t)num_cus * env_int("FI_PREFIX_TILES_PER_CU", 2));
+      const int64_t want = std::max<int64_t>(1, (int64_t)num_cus * env_int("FI_PREFIX_TILES_PER_CU", 1));
       int64_t n_split = std::max<int64_t>(1, ceil_div(want, prefix_row_tiles));
       prefix_chunk = round_up(ceil_div(Lpmax, n_split), kBlockTokens);
       prefix_chunk = std::max<int64_t>(prefix_chunk, env_int("FI_PREFIX_CHUNK_MIN", 256));

@@ -265,3 +265,58 @@ def test_cascade_graph_capture_replays(fi):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, o_e) and torch.equal(lse, l_e), f"replay {i}"
+
+
+@pytest.mark.gpu
+def test_run_stage_decode_equals_full_run_when_unsplit(fi):
+    """fi_debug_run_stage(0) launches the decode kernel exactly as the full
+    run does: with every request in one tile per head (no merge), its
+    outputs are bitwise those of fi_decode_run."""
+    import torch
+    w = W.make("batch64_gqa4", small=True)
+    d = C.Dev(w)
+    plan = C.make_plan(w, chunk_tokens=4096)
+    assert plan.stats["num_merge_units"] == 0
+    o_r, l_r = plan.run(d.q, d.k, d.v, d.indptr, d.indices, d.last, sm_scale=w.sm_scale)
+    o_s, l_s = plan.run_stage(0, d.q, d.k, d.v, d.indptr, d.indices, d.last,
+                              sm_scale=w.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o_r, o_s) and torch.equal(l_r, l_s)
+
+
+@pytest.mark.gpu
+def test_run_stage_prefix_alone(fi):
+    """Stage 1 = the cascade prefix kernel.  With no suffix pages and the
+    prefix in one chunk, each row's only state comes from the prefix kernel,
+    which then writes o / lse itself: equal to the full cascade run and to
+    the oracle over the prefix tokens."""
+    import torch
+    w = W.make("cascade256", small=True)
+    B = w.batch
+    w.kv_indptr = np.zeros(B + 1, np.int32)
+    w.kv_indices = np.zeros(1, np.int32)
+    w.last_page_len = np.zeros(B, np.int32)
+    d = C.Dev(w)
+    # a plan for 8 compute units keeps the 512-token prefix in one chunk
+    plan = fi.Plan(w.kv_indptr, w.last_page_len, num_qo_heads=w.num_qo_heads,
+                   num_kv_heads=w.num_kv_heads, page_size=w.page_size, head_dim=w.head_dim,
+                   q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
+                   prefix=(w.prefix_qo_indptr, w.prefix_kv_indptr, w.prefix_last_page_len),
+                   num_cus=8)
+    st = plan.stats
+    assert st["num_tiles"] == 0 and st["num_merge_units"] == 0 and st["num_prefix_tiles"] > 0
+    o_c, l_c = plan.cascade_run(d.q, d.k, d.v, d.p_indptr, d.p_indices, d.p_last, d.indptr,
+                                d.indices, d.last, sm_scale=w.sm_scale)
+    o_s, l_s = plan.run_stage(1, d.q, d.k, d.v, d.indptr, d.indices, d.last,
+                              d.p_indptr, d.p_indices, d.p_last, sm_scale=w.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o_c, o_s) and torch.equal(l_c, l_s)
+    ro, rl = C.run_oracle(w)
+    C.assert_parity(w, o_s.float().cpu().double().numpy(), l_s.cpu().double().numpy(), ro, rl,
+                    label="prefix stage vs oracle")
+    # a plan without prefix tiles rejects stage 1 in the library
+    w2 = W.make("batch64_gqa4", small=True)
+    d2 = C.Dev(w2)
+    with pytest.raises(fi.FiError):
+        C.make_plan(w2).run_stage(1, d2.q, d2.k, d2.v, d2.indptr, d2.indices, d2.last,
+                                  sm_scale=w2.sm_scale)
