@@ -202,7 +202,9 @@ const char* fi_last_error(void);
  * touched) and copies the decode work list into tiles_out (host, int32,
  * 8 words per tile: request, first kv head, t0, t1, partial slot base or -1,
  * kind, row0, row1); *num_tiles = entries.  If capacity_tiles is too small
- * only the count is returned.  prefix tiles follow the decode tiles. */
+ * only the count is returned.  prefix tiles follow the decode tiles.  For a
+ * decode tile row0 is kv_indptr[request] (its page-table base); for a prefix
+ * tile [row0, row1) is its range of the group's query rows. */
 fi_status fi_debug_plan_tiles(const fi_problem* problem, int32_t num_cus,
                               int32_t* tiles_out, int64_t capacity_tiles,
                               int64_t* num_tiles);

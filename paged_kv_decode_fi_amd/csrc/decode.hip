@@ -147,7 +147,7 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   const int r = tile.req, t0 = tile.t0, t1 = tile.t1;
   const int G = p.G;
   const int ps = p.page_size, ps_shift = p.ps_shift;
-  const int page_base = p.kv_indptr[r];
+  const int page_base = tile.row0;   // kv_indptr[r], copied by the plan
   const int KS = S::k_stride(W), VS = S::v_stride(W);
   uint8_t* klds = lds;
   uint8_t* vlds = lds + kStep * KS;

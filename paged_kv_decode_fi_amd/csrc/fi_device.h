@@ -116,17 +116,27 @@ __device__ __forceinline__ float wave_sum(float v) {
 // partial_o [.][kHeadDim] / partial_lse [.] (lse in log2 units):
 //   M = max_c s_c, S = sum_c 2^(s_c - M), o = sum_c 2^(s_c - M) o_c / S,
 //   lse = (M + log2 S) ln 2; all states empty -> o = 0, lse = -inf.
-// Lanes read 64 lse values at a time; partial rows are read kMergeBatch at a
-// time with independent loads issued together.
-constexpr int kMergeBatch = 16;
-template <bool OBF16>
+// Lanes read 64 lse values at a time; partial rows are read BATCH at a time
+// with independent loads issued together (BATCH 64 for rows with many
+// states).  The first batch of partial rows is issued before the lse pass:
+// its addresses do not depend on the lse values, so both are one round trip.
+template <bool OBF16, int BATCH>
 __device__ __forceinline__ void merge_state_row(const float* __restrict__ partial_o,
                                                 const float* __restrict__ partial_lse,
                                                 int64_t row0, int64_t stride, int n,
                                                 uint32_t* orow, float* lse_out, int lane) {
   const float* po = partial_o + row0 * kHeadDim + 2 * lane;
-  float M = -INFINITY;
-  for (int c0 = 0; c0 < n; c0 += 64) {
+  auto load_rows = [&](int c, int cnt, f32x2 (&v)[BATCH]) {
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k)
+      v[k] = k < cnt ? *reinterpret_cast<const f32x2*>(po + (int64_t)(c + k) * stride * kHeadDim)
+                     : f32x2{0.f, 0.f};
+  };
+  f32x2 v[BATCH];
+  load_rows(0, min(n, BATCH), v);
+  const float s0 = lane < n ? partial_lse[row0 + lane * stride] : -INFINITY;
+  float M = s0;
+  for (int c0 = 64; c0 < n; c0 += 64) {
     const int c = c0 + lane;
     M = fmaxf(M, c < n ? partial_lse[row0 + c * stride] : -INFINITY);
   }
@@ -135,19 +145,17 @@ __device__ __forceinline__ void merge_state_row(const float* __restrict__ partia
   if (M != -INFINITY) {
     for (int c0 = 0; c0 < n; c0 += 64) {
       const int c = c0 + lane;
-      const float w = c < n ? fast_exp2(partial_lse[row0 + c * stride] - M) : 0.f;
+      const float sc = c0 == 0 ? s0 : (c < n ? partial_lse[row0 + c * stride] : -INFINITY);
+      const float w = c < n ? fast_exp2(sc - M) : 0.f;
       S += w;
       const int cn = min(64, n - c0);
-      for (int k0 = 0; k0 < cn; k0 += kMergeBatch) {
-        f32x2 v[kMergeBatch];
+      for (int k0 = 0; k0 < cn; k0 += BATCH) {
+        if (c0 + k0 > 0) load_rows(c0 + k0, min(BATCH, cn - k0), v);
 #pragma unroll
-        for (int k = 0; k < kMergeBatch; ++k)
-          v[k] = k0 + k < cn ? *reinterpret_cast<const f32x2*>(
-                                   po + (int64_t)(c0 + k0 + k) * stride * kHeadDim)
-                             : f32x2{0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < kMergeBatch; ++k) {
-          const float wk = __shfl(w, (k0 + k) & 63);
+        for (int k = 0; k < BATCH; ++k) {
+          // uniform lane index: a scalar read of lane k0 + k's weight
+          const float wk = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), (k0 + k) & 63));
           a0 += wk * v[k].x;
           a1 += wk * v[k].y;
         }

@@ -26,6 +26,9 @@ enum TileKind : int32_t { kDecodeTile = 0, kPrefixTile = 1 };
 //   prefix tile: group `req`, kv head kv_head0, prefix tokens [t0, t1), q rows
 //     [row0, row1) of the group (row = (r - first request) * G + j % G);
 //     slot = the prefix chunk index.
+// Work-list entry.  Decode tiles: row0 = kv_indptr[req] (the request's
+// first page-table entry, known to the plan), row1 unused.  Prefix tiles:
+// query rows [row0, row1) of the group's G-row-per-request numbering.
 struct Tile {
   int32_t req, kv_head0, t0, t1, slot, kind, row0, row1;
 };

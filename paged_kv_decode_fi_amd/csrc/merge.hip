@@ -25,8 +25,13 @@ __global__ __launch_bounds__(256) void merge_partials_kernel(MergeParams p) {
   const int64_t row0 = ((int64_t)u.slot_base + h) * p.G + jj;   // state 0's row
   uint32_t* orow = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(p.o) +
                                                ((int64_t)u.req * p.Hq + j) * kHeadDim);
-  merge_state_row<OBF16>(p.partial_o, p.partial_lse, row0, stride, u.n_states, orow,
-                         p.lse ? p.lse + (int64_t)u.req * p.Hq + j : nullptr, lane);
+  float* lse_out = p.lse ? p.lse + (int64_t)u.req * p.Hq + j : nullptr;
+  if (u.n_states > 16)
+    merge_state_row<OBF16, 64>(p.partial_o, p.partial_lse, row0, stride, u.n_states, orow,
+                               lse_out, lane);
+  else
+    merge_state_row<OBF16, 16>(p.partial_o, p.partial_lse, row0, stride, u.n_states, orow,
+                               lse_out, lane);
 }
 
 hipError_t launch_merge_partials(const MergeParams& p, int num_units, bool o_bf16,

@@ -212,7 +212,8 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
         t.t1 = (int32_t)std::min<int64_t>((c + 1) * chunk, lens[r]);
         t.slot = ri.n_states >= 2 ? (int32_t)(ri.slot_base + (c_off + c) * Hkv + t.kv_head0) : -1;
         t.kind = kDecodeTile;
-        t.row0 = t.row1 = 0;
+        t.row0 = in.kv_indptr[r];   // the request's first page-table entry
+        t.row1 = 0;
         dt.push_back(t);
       }
     }

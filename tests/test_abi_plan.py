@@ -137,6 +137,10 @@ def test_plan_covers_every_token_once(fi, seed):
     # split requests: every (req, chunk, head) has its own slot; unsplit: -1
     slots = [t[4] for t in tiles if t[4] >= 0]
     assert len(slots) == len(set(slots))
+    # a decode tile carries its request's page-table base (word 6)
+    for t in tiles:
+        if t[5] == 0:
+            assert t[6] == indptr[t[0]]
 
 
 def test_plan_is_deterministic_and_depends_only_on_lengths(fi):
