@@ -108,12 +108,26 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   const int num_cus = in.num_cus > 0 ? in.num_cus : 256;
 
   // ---- decode chunk length
-  int hpt = kWavesPerTile;
+  // heads per tile: the largest of FI_HEADS_PER_TILE (default 8), 4, 2, 1
+  // dividing Hkv
+  int hpt = (int)std::min<int64_t>(kWavesPerTile, std::max<int64_t>(1, env_int("FI_HEADS_PER_TILE",
+                                                                              kWavesPerTile)));
+  while (hpt & (hpt - 1)) hpt &= hpt - 1;
   while (Hkv % hpt) hpt >>= 1;
-  const int64_t head_groups = Hkv / hpt;
   const int64_t waves_per_cu = env_int("FI_WAVES_PER_CU", 16);
   const int64_t c_min = round_up(std::max(env_int("FI_CHUNK_MIN", 32), kChunkAlign),
                                  kChunkAlign);
+  if (env_int("FI_HEADS_PER_TILE", 0) == 0) {
+    // small problems (fewer than 4 tiles per CU even at the minimum chunk):
+    // fewer heads per tile, so more, smaller workgroups spread the latency
+    auto tiles_at_min = [&](int h) {
+      int64_t t = 0;
+      for (int r = 0; r < B; ++r) t += std::max<int64_t>(1, ceil_div(lens[r], c_min));
+      return t * (Hkv / h);
+    };
+    while (hpt > 2 && tiles_at_min(hpt) < 4 * (int64_t)num_cus) hpt >>= 1;
+  }
+  const int64_t head_groups = Hkv / hpt;
   const int64_t target_waves = std::max<int64_t>(1, num_cus * waves_per_cu);
   int64_t Lmax = 0;
   for (int r = 0; r < B; ++r) Lmax = std::max(Lmax, lens[r]);
