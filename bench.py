@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="replay the K steps from one captured hipGraph")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--page-size", type=int, default=16, choices=(1, 16),
+                    help="long32_fp8 only: run the page-size-1 or page-size-16 variant")
     return ap.parse_args()
 
 
@@ -81,7 +83,7 @@ def main():
     t_gen = time.perf_counter()
     wl = W.make(args.workload, seed=args.seed)
     if isinstance(wl, dict):                   # long32_fp8: ps 1 and ps 16 variants
-        wl = wl[16]
+        wl = wl[args.page_size]
     t_gen = time.perf_counter() - t_gen
     w = wl
     print(f"[bench] workload {w.name}: B={w.batch} Hq={w.num_qo_heads} Hkv={w.num_kv_heads} "
