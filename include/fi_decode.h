@@ -104,7 +104,7 @@ typedef struct {
   const int32_t* prefix_qo_indptr;     /* host [groups+1], [0]=0, [groups]=B */
   const int32_t* prefix_kv_indptr;     /* host [groups+1] */
   const int32_t* prefix_last_page_len; /* host [groups] */
-  /* Tuning knob: tokens per split chunk (multiple of 32), 0 = automatic. */
+  /* Tuning knob: tokens per split chunk (multiple of 16), 0 = automatic. */
   int32_t chunk_tokens;
 } fi_problem;
 
@@ -121,6 +121,8 @@ typedef struct {
   int32_t heads_per_tile;    /* kv heads one decode workgroup handles */
   int32_t num_cus;
   size_t workspace_bytes;
+  int64_t num_folded;        /* cascade requests whose one suffix tile folds in
+                                their prefix states (no merge unit) */
 } fi_plan_stats;
 
 /* Plan stage (FlashInfer README "core features" item 2).

@@ -54,7 +54,7 @@ class PlanStats(ctypes.Structure):
                 ("num_partials", ctypes.c_int64), ("num_merge_units", ctypes.c_int64),
                 ("chunk_tokens", ctypes.c_int32), ("prefix_chunk_tokens", ctypes.c_int32),
                 ("heads_per_tile", ctypes.c_int32), ("num_cus", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("num_folded", ctypes.c_int64)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}

@@ -18,7 +18,7 @@
 
 namespace fi {
 hipError_t launch_decode(const DecodeParams& p, int num_tiles, int waves, bool q_bf16,
-                         int kv, hipStream_t s);
+                         int kv, bool fold, hipStream_t s);
 hipError_t launch_prefix(const DecodeParams& p, int num_tiles, int waves, bool q_bf16, int kv,
                          hipStream_t s);
 hipError_t launch_merge_partials(const MergeParams& p, int num_units, bool o_bf16,
@@ -271,6 +271,7 @@ fi_status fi_plan_get_stats(fi_plan_t plan, fi_plan_stats* s) {
   s->heads_per_tile = hp.heads_per_tile;
   s->num_cus = hp.num_cus;
   s->workspace_bytes = hp.layout.total;
+  s->num_folded = hp.num_folded;
   return FI_OK;
 }
 
@@ -333,7 +334,8 @@ fi_status enqueue_run(fi_plan_t plan, int stages, const void* q, const void* k_p
   if (do_decode) {
     p.kv_indptr = kv_indptr;
     p.kv_indices = kv_indices;
-    e = fi::launch_decode(p, (int)hp.num_tiles, hp.heads_per_tile, qbf, kv, s);
+    e = fi::launch_decode(p, (int)hp.num_tiles, hp.heads_per_tile, qbf, kv, hp.num_folded > 0,
+                          s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
   }
   if (overlap) {

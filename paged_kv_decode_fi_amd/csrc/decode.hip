@@ -132,7 +132,42 @@ __device__ __forceinline__ f32x4 mma16x16x16(u32x2 a, u32x2 b, f32x4 c) {
                                                  __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
 }
 
-template <int KV, bool QBF16, bool PS_POW2>
+// Folds nst earlier attention states of this wave's query rows into its own
+// unnormalised state.  Lane (g, n) holds, for q head n of the group, the
+// running reference M (log2 units), the mass S = sum 2^(x - M) and
+// A[b][i] = sum 2^(x - M) v[16 b + 4 g + i].  State c (fp32 normalised o_c
+// and log2-lse s_c, at partial row (slot_base + c Hkv + h) G + n) has mass
+// 2^(s_c - M) and contributes that times o_c; the reference moves up to s_c
+// when s_c is larger, so every weight stays <= 1.  One state per round trip
+// (the fold runs once per tile; its registers stay within the main loop's).
+__device__ __forceinline__ void fold_states(const float* __restrict__ partial_o,
+                                            const float* __restrict__ partial_lse,
+                                            int slot_base, int nst, int Hkv, int h, int G, int n,
+                                            int g, f32x4 (&A)[8], float& M, float& S) {
+  const int nn = n < G ? n : 0, col = 4 * g;
+  for (int c = 0; c < nst; ++c) {
+    const int64_t row = ((int64_t)slot_base + (int64_t)c * Hkv + h) * G + nn;
+    const float s = partial_lse[row];
+    const float* po = partial_o + row * kHeadDim + col;
+    f32x4 o[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) o[b] = *reinterpret_cast<const f32x4*>(po + 16 * b);
+    // branch-free (selects keep one copy of A live): new reference
+    // M' = max(M, s), old mass scaled by 2^(M - M'), state weight 2^(s - M')
+    const float Mn = fmaxf(M, s);
+    const float f = M == Mn ? 1.f : fast_exp2(M - Mn);     // M = -inf < s: 0
+    const float w = s == -INFINITY ? 0.f : fast_exp2(s - Mn);
+    S = S * f + w;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) A[b] = A[b] * f + w * o[b];
+    M = Mn;
+  }
+}
+
+// FOLD: the plan has tiles that fold earlier states into their output (a
+// separate instance: the fold costs registers the plain kernel keeps free).
+// DEPTH: steps of K/V loads in flight per workgroup.
+template <int KV, bool QBF16, bool PS_POW2, bool FOLD, int DEPTH>
 __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams p) {
   using S = Stage<KV>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -148,6 +183,8 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   const int G = p.G;
   const int ps = p.page_size, ps_shift = p.ps_shift;
   const int page_base = tile.row0;   // kv_indptr[r], copied by the plan
+  // slots of the states a final tile folds in (read now, used at the end)
+  const int fold_base = FOLD && tile.slot < 0 && tile.row1 > 0 ? p.req_info[r].slot_base : 0;
   const int KS = S::k_stride(W), VS = S::v_stride(W);
   uint8_t* klds = lds;
   uint8_t* vlds = lds + kStep * KS;
@@ -183,8 +220,10 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
     const int pi = PS_POW2 ? (t >> ps_shift) : (t / ps);
     return p.kv_indices[page_base + pi];
   };
-  u32x4 kr[S::LOADS], vr[S::LOADS];
-  auto issue = [&](int step, int pg) {
+  // DEPTH register sets of step loads (kr/vr[d]); set d holds steps d, d +
+  // DEPTH, ...
+  u32x4 kr[DEPTH][S::LOADS], vr[DEPTH][S::LOADS];
+  auto issue = [&](int step, int pg, u32x4 (&kq)[S::LOADS], u32x4 (&vq)[S::LOADS]) {
     const int tb = t0 + kStep * step;
 #pragma unroll
     for (int u = 0; u < S::LOADS; ++u) {
@@ -194,23 +233,23 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
       const uint32_t slot = PS_POW2 ? ((page << ps_shift) | (uint32_t)(t & (ps - 1)))
                                     : (page * (uint32_t)ps + (uint32_t)(t % ps));
       const uint64_t off = (uint64_t)slot * slot_bytes;
-      kr[u] = ld_stream<u32x4>(kbase, off);
-      vr[u] = ld_stream<u32x4>(vbase, off);
+      kq[u] = ld_stream<u32x4>(kbase, off);
+      vq[u] = ld_stream<u32x4>(vbase, off);
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](const u32x4 (&kq)[S::LOADS], const u32x4 (&vq)[S::LOADS]) {
 #pragma unroll
     for (int u = 0; u < S::LOADS; ++u) {
       const int tk = tk0 + u * S::TOK_PER_U;
-      *reinterpret_cast<u32x4*>(klds + tk * KS + 16 * vin) = kr[u];
+      *reinterpret_cast<u32x4*>(klds + tk * KS + 16 * vin) = kq[u];
       if constexpr (KV == kKvE4M3) {
-        const u32x2 a = e4m3x4_to_16<QBF16>(vr[u].x), b = e4m3x4_to_16<QBF16>(vr[u].y);
-        const u32x2 c2 = e4m3x4_to_16<QBF16>(vr[u].z), d = e4m3x4_to_16<QBF16>(vr[u].w);
+        const u32x2 a = e4m3x4_to_16<QBF16>(vq[u].x), b = e4m3x4_to_16<QBF16>(vq[u].y);
+        const u32x2 c2 = e4m3x4_to_16<QBF16>(vq[u].z), d = e4m3x4_to_16<QBF16>(vq[u].w);
         uint8_t* dst = vlds + tk * VS + 32 * vin;
         *reinterpret_cast<u32x4*>(dst) = u32x4{a.x, a.y, b.x, b.y};
         *reinterpret_cast<u32x4*>(dst + 16) = u32x4{c2.x, c2.y, d.x, d.y};
       } else {
-        *reinterpret_cast<u32x4*>(vlds + tk * VS + 16 * vin) = vr[u];
+        *reinterpret_cast<u32x4*>(vlds + tk * VS + 16 * vin) = vq[u];
       }
     }
   };
@@ -272,29 +311,65 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
     }
   };
 
-  // ---- pipelined step loop
-  if (nsteps > 0) {
-    int pg1 = nsteps > 1 ? load_page(1) : 0;
-    issue(0, load_page(0));
-    for (int step = 0; step < nsteps; ++step) {
-      const int pg2 = step + 2 < nsteps ? load_page(step + 2) : 0;
-      stage();
-      __syncthreads();
-      if (step + 1 < nsteps) issue(step + 1, pg1);
-      compute(step);
-      __syncthreads();
-      pg1 = pg2;
+  // ---- pipelined step loop: the loads of the next DEPTH steps are in
+  // flight while a step computes; page indices are read DEPTH + 1 steps
+  // ahead of their loads
+  if constexpr (DEPTH == 1) {
+    if (nsteps > 0) {
+      int pg1 = nsteps > 1 ? load_page(1) : 0;
+      issue(0, load_page(0), kr[0], vr[0]);
+      for (int step = 0; step < nsteps; ++step) {
+        const int pg2 = step + 2 < nsteps ? load_page(step + 2) : 0;
+        stage(kr[0], vr[0]);
+        __syncthreads();
+        if (step + 1 < nsteps) issue(step + 1, pg1, kr[0], vr[0]);
+        compute(step);
+        __syncthreads();
+        pg1 = pg2;
+      }
+    }
+  } else {
+    if (nsteps > 0) {
+      issue(0, load_page(0), kr[0], vr[0]);
+      if (nsteps > 1) issue(1, load_page(1), kr[1], vr[1]);
+      int pga = nsteps > 2 ? load_page(2) : 0;   // page of the next even step to issue
+      int pgb = nsteps > 3 ? load_page(3) : 0;   // ... odd step
+      // one body per register set: set d stages step s and refills with s + 2
+      auto body = [&](int step, int& pgn, u32x4 (&kq)[S::LOADS], u32x4 (&vq)[S::LOADS]) {
+        stage(kq, vq);
+        __syncthreads();
+        if (step + 2 < nsteps) issue(step + 2, pgn, kq, vq);
+        pgn = step + 4 < nsteps ? load_page(step + 4) : 0;
+        compute(step);
+        __syncthreads();
+      };
+      for (int step = 0; step < nsteps; step += 2) {
+        body(step, pga, kr[0], vr[0]);
+        if (step + 1 < nsteps) body(step + 1, pgb, kr[1], vr[1]);
+      }
     }
   }
 
   // ---- finalize
   float lt = l + __shfl_xor(l, 16);
   lt += __shfl_xor(lt, 32);
-  float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (KV == kKvE4M3 && p.v_scale) inv *= p.v_scale[h];
-  const float lse2 = lt > 0.f ? m + fast_log2(lt) : -INFINITY;
+  const float vs = (KV == kKvE4M3 && p.v_scale) ? p.v_scale[h] : 1.f;
   const int j = h * G + n;
   if (tile.slot < 0) {
+    // final output; a cascade request whose suffix is this one tile first
+    // folds in the states its prefix tiles left (tile.row1 of them)
+    float M = m, S = lt, osc = vs;
+    if (FOLD && tile.row1 > 0) {
+      if (KV == kKvE4M3) {
+#pragma unroll
+        for (int b = 0; b < 8; ++b) oacc[b] *= vs;
+        osc = 1.f;
+      }
+      fold_states(p.partial_o, p.partial_lse, fold_base, tile.row1, p.Hkv, h, G, n, g, oacc,
+                  M, S);
+    }
+    const float inv = (S > 0.f ? 1.f / S : 0.f) * osc;
+    const float lse2 = S > 0.f ? M + fast_log2(S) : -INFINITY;
     if (n < G) {
       uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)r * p.Hq + j) * kHeadDim;
 #pragma unroll
@@ -307,6 +382,8 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
     }
     return;
   }
+  const float inv = (lt > 0.f ? 1.f / lt : 0.f) * vs;
+  const float lse2 = lt > 0.f ? m + fast_log2(lt) : -INFINITY;
   const int64_t slot = tile.slot + wave;
   if (n < G) {
     float* po = p.partial_o + (slot * G + n) * kHeadDim;
@@ -610,30 +687,56 @@ __global__ __launch_bounds__(64 * WAVES) void prefix_kernel(DecodeParams p) {
 }
 
 // ---- launchers ----------------------------------------------------------------
-template <int KV, bool QBF16>
+// FI_DECODE_DEPTH=1 keeps one step in flight for every workgroup size (for
+// measurement); read once.
+static int getenv_depth() {
+  static const int d = [] {
+    const char* v = getenv("FI_DECODE_DEPTH");
+    return v && *v ? atoi(v) : 0;
+  }();
+  return d;
+}
+
+template <int KV, bool QBF16, bool FOLD, int DEPTH>
 static hipError_t launch_decode_t(const DecodeParams& p, int num_tiles, int waves,
                                   hipStream_t s) {
-  if (num_tiles <= 0) return hipSuccess;
   const size_t lds = (size_t)Stage<KV>::lds_bytes(waves);
   // dynamic LDS above 64 KiB must be allowed per kernel (once per process)
   static const hipError_t attr = [] {
     const int max_lds = Stage<KV>::lds_bytes(kWavesPerTile);
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, true>),
+        reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, true, FOLD, DEPTH>),
         hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+      e = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, false, FOLD, DEPTH>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
     return e;
   }();
   if (attr != hipSuccess) return attr;
   if (p.ps_shift >= 0)
-    hipLaunchKernelGGL((decode_kernel<KV, QBF16, true>), dim3(num_tiles), dim3(64 * waves), lds,
-                       s, p);
+    hipLaunchKernelGGL((decode_kernel<KV, QBF16, true, FOLD, DEPTH>), dim3(num_tiles),
+                       dim3(64 * waves), lds, s, p);
   else
-    hipLaunchKernelGGL((decode_kernel<KV, QBF16, false>), dim3(num_tiles), dim3(64 * waves), lds,
-                       s, p);
+    hipLaunchKernelGGL((decode_kernel<KV, QBF16, false, FOLD, DEPTH>), dim3(num_tiles),
+                       dim3(64 * waves), lds, s, p);
   return hipGetLastError();
+}
+
+// The fold instance (cascade suffix tiles, planned as few long 2-head
+// tiles) keeps two steps of loads in flight; the plain instance keeps one,
+// so that two 8-wave workgroups fit on a compute unit (two steps measured
+// no faster for the plain workloads).
+template <int KV, bool QBF16>
+static hipError_t launch_decode_f(const DecodeParams& p, int num_tiles, int waves, bool fold,
+                                  hipStream_t s) {
+  if (num_tiles <= 0) return hipSuccess;
+  const bool deep = fold && waves <= 4 && getenv_depth() != 1;
+  if (fold)
+    return deep ? launch_decode_t<KV, QBF16, true, 2>(p, num_tiles, waves, s)
+                : launch_decode_t<KV, QBF16, true, 1>(p, num_tiles, waves, s);
+  return deep ? launch_decode_t<KV, QBF16, false, 2>(p, num_tiles, waves, s)
+              : launch_decode_t<KV, QBF16, false, 1>(p, num_tiles, waves, s);
 }
 
 template <int KV, bool QBF16, int W>
@@ -655,15 +758,16 @@ static hipError_t launch_prefix_t(const DecodeParams& p, int num_tiles, int wave
   return hipGetLastError();
 }
 
-// q_bf16: q (and o) are bf16, else fp16.  kv: KvKind.
+// q_bf16: q (and o) are bf16, else fp16.  kv: KvKind.  fold: the work list
+// has tiles that fold earlier states into their output.
 hipError_t launch_decode(const DecodeParams& p, int num_tiles, int waves, bool q_bf16,
-                         int kv, hipStream_t s) {
+                         int kv, bool fold, hipStream_t s) {
   if (waves < 1 || waves > kWavesPerTile) return hipErrorInvalidValue;
   if (kv == kKvE4M3)
-    return q_bf16 ? launch_decode_t<kKvE4M3, true>(p, num_tiles, waves, s)
-                  : launch_decode_t<kKvE4M3, false>(p, num_tiles, waves, s);
-  return q_bf16 ? launch_decode_t<kKvBF16, true>(p, num_tiles, waves, s)
-                : launch_decode_t<kKvF16, false>(p, num_tiles, waves, s);
+    return q_bf16 ? launch_decode_f<kKvE4M3, true>(p, num_tiles, waves, fold, s)
+                  : launch_decode_f<kKvE4M3, false>(p, num_tiles, waves, fold, s);
+  return q_bf16 ? launch_decode_f<kKvBF16, true>(p, num_tiles, waves, fold, s)
+                : launch_decode_f<kKvF16, false>(p, num_tiles, waves, fold, s);
 }
 
 hipError_t launch_prefix(const DecodeParams& p, int num_tiles, int waves, bool q_bf16, int kv,

@@ -27,8 +27,11 @@ enum TileKind : int32_t { kDecodeTile = 0, kPrefixTile = 1 };
 //     [row0, row1) of the group (row = (r - first request) * G + j % G);
 //     slot = the prefix chunk index.
 // Work-list entry.  Decode tiles: row0 = kv_indptr[req] (the request's
-// first page-table entry, known to the plan), row1 unused.  Prefix tiles:
-// query rows [row0, row1) of the group's G-row-per-request numbering.
+// first page-table entry, known to the plan); row1 = number of earlier
+// states (the request's cascade prefix chunks, slots slot_base + c * Hkv + h
+// of its ReqInfo) the tile folds into its final output, 0 if none (then
+// slot = -1 means the tile's own state is final).  Prefix tiles: query rows
+// [row0, row1) of the group's G-row-per-request numbering.
 struct Tile {
   int32_t req, kv_head0, t0, t1, slot, kind, row0, row1;
 };
@@ -66,6 +69,7 @@ struct HostPlan {
   int32_t num_cus;
   int32_t chunk_tokens, prefix_chunk_tokens, heads_per_tile, prefix_waves;
   int64_t num_tiles, num_prefix_tiles, num_partials, num_merge_units;
+  int64_t num_folded;   // requests whose decode tile folds in their prefix states
   Tile* tiles;          // num_tiles + num_prefix_tiles entries
   ReqInfo* req_info;    // batch entries
   MergeUnit* merge_units;  // num_merge_units entries

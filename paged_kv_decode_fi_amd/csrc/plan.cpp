@@ -155,6 +155,28 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
       chunk = a * kChunkAlign;
     }
   }
+  // Cascade: a request with prefix states whose suffix is one chunk folds
+  // those states into its decode tile's output, so no merge pass is needed.
+  // When every such suffix is short (<= FI_FOLD_MAX_SUFFIX tokens, default
+  // 1024), cover each with one chunk, 2 kv heads per tile (small tiles, two
+  // steps of loads in flight), provided that still gives >= 4 waves per CU.
+  const bool fold_ok = env_int("FI_CASCADE_FOLD", 1) != 0;
+  if (NG > 0 && fold_ok && in.chunk_tokens == 0 && env_int("FI_HEADS_PER_TILE", 0) == 0) {
+    int64_t ls_max = 0;
+    for (int r = 0; r < B; ++r)
+      if (group_of[r] >= 0 && plens[group_of[r]] > 0) ls_max = std::max(ls_max, lens[r]);
+    const int hpt_f = Hkv % 2 == 0 ? 2 : 1;
+    if (ls_max > 0 && ls_max <= env_int("FI_FOLD_MAX_SUFFIX", 1024)) {
+      const int64_t chunk_f = round_up(ls_max, kChunkAlign);
+      int64_t w = 0;
+      for (int r = 0; r < B; ++r) w += std::max<int64_t>(1, ceil_div(lens[r], chunk_f));
+      if (w * Hkv >= 4 * (int64_t)num_cus) {
+        hpt = hpt_f;
+        chunk = chunk_f;
+      }
+    }
+  }
+  const int64_t head_groups_final = Hkv / hpt;
 
   // ---- cascade prefix chunking
   const int prefix_waves = env_int("FI_PREFIX_WAVES", kPrefixMaxWaves) == 4 ? 4 : 8;
@@ -183,19 +205,26 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   }
 
   // ---- states per request, slots
+  // A request with prefix states and a suffix that is one decode chunk is
+  // "folded": its decode tile reads the prefix states and writes the final
+  // output, so only the prefix states need slots and no merge unit is made
+  // (FI_CASCADE_FOLD=0 sends every such request through the merge kernel).
   std::vector<int64_t> n_dchunks(B);
+  std::vector<char> folded(B, 0);
   for (int r = 0; r < B; ++r) n_dchunks[r] = lens[r] > 0 ? ceil_div(lens[r], chunk) : 0;
   out->req_info = (ReqInfo*)malloc(sizeof(ReqInfo) * std::max(B, 1));
   int64_t slots = 0, n_merge = 0;
   for (int r = 0; r < B; ++r) {
     int g = group_of[r];
-    int64_t ns = n_dchunks[r] + (g >= 0 ? n_pchunks[g] : 0);
+    const int64_t np = g >= 0 ? n_pchunks[g] : 0;
+    int64_t ns = n_dchunks[r] + np;
+    folded[r] = fold_ok && np > 0 && n_dchunks[r] == 1;
     out->req_info[r].n_states = (int32_t)ns;
     out->req_info[r].slot_base = -1;
     if (ns >= 2) {
       out->req_info[r].slot_base = (int32_t)slots;
-      slots += ns * Hkv;
-      ++n_merge;
+      slots += (folded[r] ? np : ns) * Hkv;
+      if (!folded[r]) ++n_merge;
     }
     if (slots > (int64_t)0x7fffffff / (G * kHeadDim))
       PLAN_FAIL(2, "too many partial states; raise chunk_tokens");
@@ -204,7 +233,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   {
     int64_t k = 0;
     for (int r = 0; r < B; ++r)
-      if (out->req_info[r].n_states >= 2)
+      if (out->req_info[r].n_states >= 2 && !folded[r])
         out->merge_units[k++] = MergeUnit{r, out->req_info[r].slot_base,
                                           out->req_info[r].n_states, 0};
   }
@@ -218,16 +247,17 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
     int64_t nc = n_dchunks[r];
     bool need_empty = (nc == 0 && ri.n_states == 0);
     for (int64_t c = 0; c < std::max<int64_t>(nc, need_empty ? 1 : 0); ++c) {
-      for (int64_t hg = 0; hg < head_groups; ++hg) {
+      for (int64_t hg = 0; hg < head_groups_final; ++hg) {
         Tile t;
         t.req = r;
         t.kv_head0 = (int32_t)(hg * hpt);
         t.t0 = (int32_t)std::min<int64_t>(c * chunk, lens[r]);
         t.t1 = (int32_t)std::min<int64_t>((c + 1) * chunk, lens[r]);
-        t.slot = ri.n_states >= 2 ? (int32_t)(ri.slot_base + (c_off + c) * Hkv + t.kv_head0) : -1;
+        t.slot = ri.n_states >= 2 && !folded[r]
+                     ? (int32_t)(ri.slot_base + (c_off + c) * Hkv + t.kv_head0) : -1;
         t.kind = kDecodeTile;
         t.row0 = in.kv_indptr[r];   // the request's first page-table entry
-        t.row1 = 0;
+        t.row1 = folded[r] ? (int32_t)c_off : 0;   // prefix states to fold in
         dt.push_back(t);
       }
     }
@@ -274,6 +304,8 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   out->prefix_waves = prefix_waves;
   out->num_partials = slots;
   out->num_merge_units = n_merge;
+  out->num_folded = 0;
+  for (int r = 0; r < B; ++r) out->num_folded += folded[r] ? 1 : 0;
 
   WorkspaceLayout& L = out->layout;
   size_t off = 0;

@@ -195,3 +195,33 @@ def test_cascade_plan_covers_prefix_rows_once(fi):
                 seen.add(key)
     want = sum(g[0] * G * Hkv * g[1] for g in groups)
     assert len(seen) == want
+
+
+def test_cascade_single_chunk_suffix_folds_prefix_states(fi):
+    """A cascade request whose own suffix is one decode chunk gets a decode
+    tile that writes the final output (slot -1) after folding in its prefix
+    chunks' states (word 7 = their count); longer suffixes are split and go
+    through the merge (word 7 = 0)."""
+    G, Hkv, ps = 8, 8, 16
+    lens = np.array([10, 0, 200, 3000, 40])
+    B = len(lens)
+    n = (lens + ps - 1) // ps
+    indptr = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    last = np.where(n > 0, lens - (n - 1) * ps, 0).astype(np.int32)
+    qo = np.array([0, B], np.int32)
+    plen = 4096
+    pip = np.array([0, plen // ps], np.int32)
+    plast = np.array([ps], np.int32)
+    tiles = fi.debug_plan_tiles(indptr, last, num_qo_heads=G * Hkv, num_kv_heads=Hkv,
+                                page_size=ps, prefix=(qo, pip, plast), num_cus=64,
+                                chunk_tokens=256)
+    n_pchunks = len({t[2] for t in tiles if t[5] == 1})
+    assert n_pchunks >= 2
+    for req, h0, t0, t1, slot, kind, r0, r1 in tiles:
+        if kind != 0:
+            continue
+        if lens[req] <= 256:          # one chunk: folded, final output
+            assert slot == -1 and r1 == n_pchunks, (req, slot, r1)
+        else:                         # split: partial states, merged afterwards
+            assert slot >= 0 and r1 == 0, (req, slot, r1)
+    assert not any(t[0] == 1 for t in tiles if t[5] == 0)   # empty suffix: prefix only

@@ -51,10 +51,11 @@ def test_small_workload_parity(fi, name):
 @pytest.mark.parametrize("name", ["batch64_gqa4", "skewed128", "cascade256", "long32_fp8"])
 @pytest.mark.parametrize("chunk", [32, 96])
 def test_forced_split_parity(fi, name, chunk):
-    """Small chunks force split-KV tiles and the (o, lse) merge."""
+    """Small chunks force split-KV tiles and the (o, lse) merge (for cascade,
+    the merge kernel or the fold of prefix states into a one-chunk suffix)."""
     for w in _variants(W.make(name, small=True)):
         o, lse, plan = C.run_gpu(w, chunk_tokens=chunk)
-        assert plan.stats["num_merge_units"] > 0
+        assert plan.stats["num_merge_units"] + plan.stats["num_folded"] > 0
         ro, rl = C.run_oracle(w)
         C.assert_parity(w, o, lse, ro, rl, label=f"{w.name} chunk {chunk}")
 
@@ -176,6 +177,30 @@ def test_cascade_matches_flat_decode(fi):
     ro, rl = C.run_oracle(w)
     C.assert_parity(w, oc, lc, ro, rl, label="cascade vs oracle")
     C.assert_parity(flat, of, lf, ro, rl, label="flat vs oracle")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+@pytest.mark.parametrize("fold", ["1", "0"])
+def test_cascade_fold_and_merge_paths(fi, kv, fold, monkeypatch):
+    """Three prefix groups (one with an empty prefix) and suffixes shorter and
+    longer than the chunk: one-chunk suffixes fold their prefix states in the
+    decode tile (fold on), the rest go through the merge kernel; with the
+    fold off every request is merged.  e4m3 KV exercises the v_scale of the
+    folded prefix states."""
+    monkeypatch.setenv("FI_CASCADE_FOLD", fold)
+    rng = np.random.default_rng(11)
+    lens = rng.integers(0, 200, size=11)
+    lens[3] = 0
+    w = W.build("cascade_mix", lens, Hq=32, Hkv=4, ps=16, q_dtype="bf16", kv_dtype=kv,
+                seed=21, prefix_groups=[(4, 700), (3, 0), (4, 333)])
+    o, lse, plan = C.run_gpu(w, chunk_tokens=64)
+    st = plan.stats
+    if fold == "1":
+        assert st["num_folded"] > 0 and st["num_merge_units"] > 0
+    else:
+        assert st["num_folded"] == 0
+    ro, rl = C.run_oracle(w)
+    C.assert_parity(w, o, lse, ro, rl, label=f"cascade mix {kv} fold={fold} {st}")
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
