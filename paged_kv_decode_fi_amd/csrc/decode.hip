@@ -435,7 +435,7 @@ __device__ __forceinline__ int xcd_tile(int b, int n) {
 }
 
 template <int KV, bool QBF16, int WAVES, bool PS_POW2>
-__global__ __launch_bounds__(64 * WAVES) void prefix_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(DecodeParams p) {
   using S = PStage<KV>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
   int* ptab = reinterpret_cast<int*>(lds + 2 * S::BUF);

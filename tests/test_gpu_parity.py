@@ -179,6 +179,42 @@ def test_cascade_matches_flat_decode(fi):
     C.assert_parity(flat, of, lf, ro, rl, label="flat vs oracle")
 
 
+def test_split_merge_reuses_plan_with_new_data(fi):
+    """One plan serves runs over different data (the plan depends on lengths
+    only): each run must match the oracle on ITS data, so a merge that read a
+    partial state left by the previous run fails."""
+    import copy
+    w1 = W.make("batch64_gqa4", small=True)
+    w2 = copy.copy(w1)
+    rng = np.random.default_rng(99)
+    w2.q = W.cast_bits(rng.standard_normal(w1.q.shape).astype(np.float32), "f16")
+    k2 = W.cast_bits(rng.standard_normal(w1.k_pages.shape).astype(np.float32), "f16")
+    v2 = W.cast_bits(rng.standard_normal(w1.v_pages.shape).astype(np.float32), "f16")
+    w2.k_pages = np.where(w1.k_pages != W.NAN_BITS["f16"], k2, w1.k_pages)
+    w2.v_pages = np.where(w1.v_pages != W.NAN_BITS["f16"], v2, w1.v_pages)
+    plan = C.make_plan(w1, chunk_tokens=32)
+    assert plan.stats["num_merge_units"] > 0
+    for w in (w1, w2, w1, w2):
+        o, lse, _ = C.run_gpu(w, plan=plan)
+        ro, rl = C.run_oracle(w)
+        C.assert_parity(w, o, lse, ro, rl, label=f"plan reuse {plan.stats}")
+
+
+def test_merge_of_many_states_single_request(fi):
+    """One request, 32 kv heads, chunk 16: each row merges 19 states, and
+    the full-length case (2048 tokens) 128 states, more than one batch of
+    the merge kernel's 64; repeated runs are bitwise identical."""
+    for small in (True, False):
+        w = W.make("single_L2048_h32", small=small)
+        plan = C.make_plan(w, chunk_tokens=16)
+        o1, l1, _ = C.run_gpu(w, plan=plan)
+        ro, rl = C.run_oracle(w)
+        C.assert_parity(w, o1, l1, ro, rl, label=f"single chunk 16 small={small}")
+        o2, l2, _ = C.run_gpu(w, plan=plan)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+        plan.destroy()
+
+
 @pytest.mark.parametrize("kv", ["bf16", "e4m3"])
 @pytest.mark.parametrize("fold", ["1", "0"])
 def test_cascade_fold_and_merge_paths(fi, kv, fold, monkeypatch):
