@@ -164,9 +164,11 @@ fi_status fi_decode_run(fi_plan_t plan, const void* q, const void* k_pages,
  * Attention for a hierarchical KV cache): every request attends over its
  * group's shared prefix pages followed by its own pages; the prefix is read
  * once per (group, kv head) for all the group's query rows and the two
- * attention states are merged.  The plan must have been made with the same
- * cascade level.  prefix_* and kv_* are DEVICE copies of the planned tables.
- * Enqueues 2-3 kernels on stream. */
+ * attention states are merged: by the request's suffix tile when its suffix
+ * is one planned chunk, else by a merge pass.  The plan must have been made
+ * with the same cascade level.  prefix_* and kv_* are DEVICE copies of the
+ * planned tables.  Enqueues 2-3 kernels on stream (prefix, suffix, and a
+ * merge when some request needs one). */
 fi_status fi_cascade_decode(fi_plan_t plan, const void* q, const void* k_pages,
                             const void* v_pages,
                             const int32_t* prefix_kv_indptr,

@@ -10,25 +10,28 @@
 // taken base 2 with log2(e) folded into the score scale.
 //
 // MI355X mapping (one wave = 64 lanes, lane = 16 g + n):
-//  * A decode workgroup is 4 waves; wave w owns kv head kv_head0 + w of one
-//    request over a token chunk, so the G query heads that share the kv head
-//    read each K/V row once.
-//  * Scores: per 32-token block, S^T[token][head] = K . Q^T on MFMA
-//    16x16x32 -- K rows go straight from HBM into the A operand (lane n
-//    loads token n, 16 contiguous bytes per lane, 64 contiguous bytes per row
-//    per instruction), q sits in the B operand for the whole tile
-//    (columns n >= G are zero).  The D layout leaves lane (g, n) with
-//    tokens 4g..4g+3 (+16) of head n, so the row max needs only two
-//    cross-lane exchanges and P^T is already in B-operand layout.
-//  * P.V: O^T[d][head] += V^T[d][token] . P^T[token][head] on MFMA.  V rows
-//    are loaded coalesced (4 rows x 256 B per instruction), written to a
-//    per-wave LDS tile and read back transposed (8 u16 per operand) in the
-//    token order the P operand uses; the LDS row stride of 288 B keeps the 4
-//    lane groups on disjoint banks.
-//  * E4M3 K/V are converted to the q dtype in registers (exact) with the
-//    per-kv-head scales folded into the score scale and the output.
+//  * decode_kernel: a workgroup is W waves (W = kv heads per tile, 1..8) of
+//    one request over a token chunk; wave w computes kv head kv_head0 + w,
+//    so the G query heads that share it read each K/V row once.  Per
+//    16-token step the workgroup streams the step's K and V rows of its W
+//    heads (W x row bytes contiguous per token: a whole 32 KiB page at
+//    W = Hkv = 8, page_size 16) with 16-byte non-temporal loads into padded
+//    LDS tiles; the next step's loads are in flight while a step computes.
+//  * Scores S^T[token][head] = K . Q^T on MFMA 16x16x32 (K from LDS in the A
+//    operand, q in the B operand for the whole tile, columns n >= G zero).
+//    The D layout leaves lane (g, n) with tokens 4g..4g+3 of head n, so the
+//    row max needs two cross-lane exchanges and P^T is already in B-operand
+//    layout.
+//  * P.V: O^T[d][head] += V^T[d][token] . P^T[token][head] on MFMA 16x16x16,
+//    V^T read from LDS with gfx950's ds_read_b64_tr_b16 transpose read.
+//  * E4M3 K/V are converted to the q dtype (exact) with the per-kv-head
+//    scales folded into the score scale and the output.
 //  * A tile whose (request, kv head) is split over several chunks writes an
-//    fp32 partial state (o, log2-domain lse) that merge.hip combines.
+//    fp32 partial state (o, log2-domain lse) that merge.hip combines; a
+//    cascade suffix tile folds its request's prefix states in instead.
+//  * prefix_kernel (cascade): many query rows (the G heads of every request
+//    of a group) against one chunk of the shared prefix, K/V staged in LDS
+//    and shared by 8 waves x 32 rows; described above the kernel.
 #include <type_traits>
 
 #include "fi_device.h"

@@ -8,18 +8,20 @@
 // (o, lse) attention states.
 //
 // Work model.  Each (request r, kv head h) has L_r keys.  A decode tile is one
-// workgroup of kWavesPerTile waves = that many consecutive kv heads of one
-// request over one token chunk [t0, t1).  The chunk length c is one value
-// for the whole batch: the smallest multiple of the 32-token block, at
-// least c_min, such that the number of waves launched stays within
-// target = num_cus * waves_per_cu (more chunks than that only adds partial
-// states to merge).  Tiles are emitted longest first so short tails fill in
-// behind long tiles.
+// workgroup of W waves = W consecutive kv heads of one request over one
+// token chunk [t0, t1) (W = 8 when Hkv allows, fewer for small problems).
+// The chunk length c is one value for the whole batch: the smallest
+// multiple of the 16-token step, at least c_min, such that the waves
+// launched stay within target = num_cus * waves_per_cu, one round of
+// resident waves (more chunks than that only adds partial states to merge).
+// Tiles are emitted longest first so short tails fill in behind long tiles.
 //
 // Cascade: the shared prefix of group g is attended once per (g, kv head) by
-// prefix tiles covering prefix_rows query rows each (rows = the
-// group's requests x the G q heads of that kv head); the prefix is cut into
-// chunks so that prefix tiles cover the GPU about twice.
+// prefix tiles covering prefix_rows query rows each (rows = the group's
+// requests x the G q heads of that kv head); the prefix is cut into chunks
+// so that there is about one prefix tile per CU.  A request whose own suffix
+// is one decode chunk folds the prefix chunks' states into its decode tile's
+// output; others are merged by the merge kernel.
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>
