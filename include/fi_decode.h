@@ -228,10 +228,12 @@ fi_status fi_debug_gather(int32_t batch, int32_t page_size,
  * on its own.  Arguments as fi_cascade_decode; for a plan without a cascade
  * level the three prefix tables may be NULL.  stage 0 = the decode kernel
  * over the per-request pages, stage 1 = the cascade prefix kernel (plans
- * with prefix tiles only).  Rows whose state is not split are written to o
- * / lse as in the full run; split rows write their partial states to the
- * workspace and are NOT merged, so their o / lse are left untouched.
- * Errors as fi_cascade_decode, plus FI_ERR_INVALID_ARG for another stage. */
+ * with prefix tiles only), stage 2 = the merge of split requests' states
+ * (nothing when the plan has no merge unit).  Rows whose state is not split
+ * are written to o / lse as in the full run; split rows write their partial
+ * states to the workspace, which stage 2 merges into o / lse.  Stages 1, 0, 2
+ * in that order are the full run.  Errors as fi_cascade_decode, plus
+ * FI_ERR_INVALID_ARG for another stage. */
 fi_status fi_debug_run_stage(fi_plan_t plan, int32_t stage, const void* q,
                              const void* k_pages, const void* v_pages,
                              const int32_t* prefix_kv_indptr,

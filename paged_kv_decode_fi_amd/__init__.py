@@ -285,7 +285,8 @@ class Plan:
                   k_scale=None, v_scale=None, sm_scale: float = 0.0, o=None, lse=None,
                   stream=None):
         """Test / timing hook: ONE kernel of the planned run (stage 0 = decode
-        kernel, 1 = cascade prefix kernel), without the merge."""
+        kernel, 1 = cascade prefix kernel, 2 = merge of split states);
+        stages 1, 0, 2 in order are the full run."""
         self._check_q(q)
         self._check_pool(k_pages, v_pages)
         o, lse = self._outputs(q, o, lse)

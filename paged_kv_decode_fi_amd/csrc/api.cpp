@@ -400,8 +400,9 @@ fi_status fi_debug_run_stage(fi_plan_t plan, int32_t stage, const void* q, const
   g_last_error.clear();
   if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
   const fi::HostPlan& hp = plan->hp;
-  if (stage != 0 && stage != 1)
-    return fail(FI_ERR_INVALID_ARG, "stage must be 0 (decode kernel) or 1 (prefix kernel)");
+  if (stage < 0 || stage > 2)
+    return fail(FI_ERR_INVALID_ARG,
+                "stage must be 0 (decode kernel), 1 (prefix kernel) or 2 (merge kernel)");
   if (stage == 1 && hp.num_prefix_tiles == 0)
     return fail(FI_ERR_INVALID_ARG, "the plan has no cascade prefix tiles");
   if (hp.batch == 0) return FI_OK;
@@ -409,7 +410,8 @@ fi_status fi_debug_run_stage(fi_plan_t plan, int32_t stage, const void* q, const
                                 prefix_last_page_len, kv_indptr, kv_indices, last_page_len,
                                 sm_scale, o);
   if (st != FI_OK) return st;
-  return enqueue_run(plan, stage == 0 ? kStageDecode : kStagePrefix, q, k_pages, v_pages,
+  const int which = stage == 0 ? kStageDecode : stage == 1 ? kStagePrefix : kStageMerge;
+  return enqueue_run(plan, which, q, k_pages, v_pages,
                      prefix_kv_indptr, prefix_kv_indices, kv_indptr, kv_indices, k_scale,
                      v_scale, sm_scale, o, lse, reinterpret_cast<hipStream_t>(stream));
 }

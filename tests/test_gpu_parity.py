@@ -345,6 +345,30 @@ def test_run_stage_decode_equals_full_run_when_unsplit(fi):
     assert torch.equal(o_r, o_s) and torch.equal(l_r, l_s)
 
 
+@pytest.mark.parametrize("name", ["batch64_gqa4", "cascade256"])
+def test_run_stages_in_order_equal_the_run(fi, name):
+    """Stages 1 (prefix), 0 (decode), 2 (merge) enqueued one by one are the
+    full run, bit for bit (the benchmark times its dominant kernel this
+    way); split states are merged by stage 2."""
+    import torch
+    w = W.make(name, small=True)
+    d = C.Dev(w)
+    plan = C.make_plan(w, chunk_tokens=32)
+    st = plan.stats
+    assert st["num_merge_units"] > 0
+    o_r, l_r, _ = C.run_gpu(w, d=d, plan=plan)
+    o = torch.zeros_like(d.q)
+    lse = torch.zeros((w.batch, w.num_qo_heads), dtype=torch.float32, device="cuda")
+    args = (d.q, d.k, d.v, d.indptr, d.indices, d.last)
+    pre = ((d.p_indptr, d.p_indices, d.p_last) if plan.cascade else (None, None, None))
+    for sg in ((1, 0, 2) if plan.cascade else (0, 2)):
+        plan.run_stage(sg, *args, *pre, d.k_scale, d.v_scale, sm_scale=w.sm_scale, o=o,
+                       lse=lse)
+    torch.cuda.synchronize()
+    assert np.array_equal(o.float().cpu().double().numpy(), o_r)
+    assert np.array_equal(lse.cpu().double().numpy(), l_r)
+
+
 @pytest.mark.gpu
 def test_run_stage_prefix_alone(fi):
     """Stage 1 = the cascade prefix kernel.  With no suffix pages and the
