@@ -36,11 +36,6 @@ struct fi_plan_s {
   char* workspace;
   size_t workspace_bytes;
   void* staging;  // pinned copy of the work list, merge map and request info
-  // cascade plans: the prefix kernel (MFMA-bound) runs on a side stream next
-  // to the suffix decode (HBM-bound); fork/join events order it against the
-  // caller's stream, so the pair is also capturable into a graph
-  hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
 };
 
 namespace {
@@ -234,16 +229,6 @@ fi_status fi_plan(const fi_problem* problem, int32_t num_cus, void* workspace,
   pl->workspace = reinterpret_cast<char*>(workspace);
   pl->workspace_bytes = workspace_bytes;
   pl->staging = staging;
-  const char* ov = getenv("FI_CASCADE_OVERLAP");
-  if (hp.num_prefix_tiles > 0 && hp.num_tiles > 0 && ov && atoi(ov) != 0) {
-    e = hipStreamCreateWithFlags(&pl->side, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&pl->fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&pl->join, hipEventDisableTiming);
-    if (e != hipSuccess) {
-      fi_plan_destroy(pl);
-      return hip_fail(e, "creating the cascade side stream");
-    }
-  }
   *plan_out = pl;
   return FI_OK;
 }
@@ -251,9 +236,6 @@ fi_status fi_plan(const fi_problem* problem, int32_t num_cus, void* workspace,
 fi_status fi_plan_destroy(fi_plan_t plan) {
   if (!plan) return FI_OK;
   if (plan->staging) (void)hipHostFree(plan->staging);
-  if (plan->fork) (void)hipEventDestroy(plan->fork);
-  if (plan->join) (void)hipEventDestroy(plan->join);
-  if (plan->side) (void)hipStreamDestroy(plan->side);
   fi::plan_free(&plan->hp);
   delete plan;
   return FI_OK;
@@ -300,8 +282,8 @@ fi_status check_run_args(const fi::HostPlan& hp, const void* q, const void* k_pa
 }
 
 // Enqueues the selected stages of a planned run on stream s, in order
-// prefix -> decode -> merge (the prefix on the plan's side stream when the
-// plan has one).
+// prefix -> decode -> merge (a folded suffix tile reads the prefix states, so
+// the prefix kernel always completes first).
 fi_status enqueue_run(fi_plan_t plan, int stages, const void* q, const void* k_pages,
                       const void* v_pages, const int32_t* prefix_kv_indptr,
                       const int32_t* prefix_kv_indices, const int32_t* kv_indptr,
@@ -314,12 +296,6 @@ fi_status enqueue_run(fi_plan_t plan, int stages, const void* q, const void* k_p
   hipError_t e = hipSuccess;
   const bool do_prefix = (stages & kStagePrefix) && hp.num_prefix_tiles > 0;
   const bool do_decode = (stages & kStageDecode) && hp.num_tiles > 0;
-  const bool overlap = plan->side != nullptr && do_prefix && do_decode;
-  if (overlap) {
-    e = hipEventRecord(plan->fork, s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(plan->side, plan->fork, 0);
-    if (e != hipSuccess) return hip_fail(e, "forking the prefix stream");
-  }
   if (do_prefix) {
     // prefix tiles read the group-level table; row -> request = the group's
     // first request (planned copy of prefix_qo_indptr) + row / G
@@ -327,8 +303,7 @@ fi_status enqueue_run(fi_plan_t plan, int stages, const void* q, const void* k_p
     pp.kv_indptr = prefix_kv_indptr;
     pp.kv_indices = prefix_kv_indices;
     pp.qo_indptr = reinterpret_cast<const int32_t*>(plan->workspace + hp.layout.qo_indptr_off);
-    e = fi::launch_prefix(pp, (int)hp.num_prefix_tiles, hp.prefix_waves, qbf, kv,
-                          overlap ? plan->side : s);
+    e = fi::launch_prefix(pp, (int)hp.num_prefix_tiles, hp.prefix_waves, qbf, kv, s);
     if (e != hipSuccess) return hip_fail(e, "prefix launch");
   }
   if (do_decode) {
@@ -337,11 +312,6 @@ fi_status enqueue_run(fi_plan_t plan, int stages, const void* q, const void* k_p
     e = fi::launch_decode(p, (int)hp.num_tiles, hp.heads_per_tile, qbf, kv, hp.num_folded > 0,
                           s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
-  }
-  if (overlap) {
-    e = hipEventRecord(plan->join, plan->side);
-    if (e == hipSuccess) e = hipStreamWaitEvent(s, plan->join, 0);
-    if (e != hipSuccess) return hip_fail(e, "joining the prefix stream");
   }
   if (stages & kStageMerge) return launch_merge(plan, o, lse, s);
   return FI_OK;

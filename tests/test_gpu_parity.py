@@ -296,9 +296,9 @@ def test_graph_capture_replays(fi):
 
 @pytest.mark.gpu
 def test_cascade_graph_capture_replays(fi):
-    """The cascade run forks the prefix kernel onto the plan's side stream and
-    joins it back with events: capture the whole call into a graph and check
-    that every replay equals the eager result."""
+    """The cascade run (prefix, folded suffix, merge launches) only enqueues
+    kernels: capture it from a side stream into a graph and check that every
+    replay equals the eager result."""
     import torch
     w = W.make("cascade256", small=True)
     d = C.Dev(w)
