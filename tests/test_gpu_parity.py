@@ -94,7 +94,7 @@ def test_run_to_run_determinism_and_page_permutation(fi):
 
 def _fuzz_case(seed):
     rng = np.random.default_rng(1000 + seed)
-    ps = int(rng.choice([1, 2, 16]))
+    ps = int(rng.choice([1, 2, 3, 7, 16]))
     G = int(rng.choice([1, 2, 4, 8, 16]))
     Hkv = int(rng.choice([1, 2, 4, 8]))
     B = int(rng.integers(1, 10))
@@ -115,6 +115,37 @@ def test_fuzz_parity(fi, seed):
     C.assert_parity(w, o, lse, ro, rl,
                     label=f"fuzz{seed} B{w.batch} G{w.group_size} Hkv{w.num_kv_heads} "
                           f"ps{w.page_size} {w.q_dtype}/{w.kv_dtype} lens {list(w.kv_lens)}")
+
+
+def _cascade_fuzz_case(seed):
+    """Random cascade: 1-3 prefix groups (some with an empty prefix), page
+    sizes including non-powers of two, group sizes 1-16, 16-bit or e4m3 KV."""
+    rng = np.random.default_rng(5000 + seed)
+    ps = int(rng.choice([1, 3, 8, 16]))
+    G = int(rng.choice([1, 4, 8, 16]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    q_dtype = str(rng.choice(["f16", "bf16"]))
+    kv_dtype = str(rng.choice([q_dtype, "e4m3"]))
+    groups = []
+    for _ in range(int(rng.integers(1, 4))):
+        groups.append((int(rng.integers(1, 5)), int(rng.choice([0, 1, ps, 300, 1000]))))
+    B = sum(g[0] for g in groups)
+    lens = [int(rng.choice([0, 1, ps + 1, int(rng.integers(2, 400))])) for _ in range(B)]
+    return W.build(f"cfuzz{seed}", lens, Hq=Hkv * G, Hkv=Hkv, ps=ps, q_dtype=q_dtype,
+                   kv_dtype=kv_dtype, seed=seed, prefix_groups=groups)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_cascade_fuzz_parity(fi, seed):
+    w = _cascade_fuzz_case(seed)
+    chunk = [0, 32, 64][seed % 3]
+    o, lse, plan = C.run_gpu(w, chunk_tokens=chunk)
+    ro, rl = C.run_oracle(w)
+    C.assert_parity(w, o, lse, ro, rl,
+                    label=f"cfuzz{seed} B{w.batch} G{w.group_size} Hkv{w.num_kv_heads} "
+                          f"ps{w.page_size} {w.q_dtype}/{w.kv_dtype} groups "
+                          f"{list(zip(np.diff(w.prefix_qo_indptr), w.prefix_lens))} "
+                          f"lens {list(w.kv_lens)} {plan.stats}")
 
 
 # ------------------------------------------------------------ spike test
