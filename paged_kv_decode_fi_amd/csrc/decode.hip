@@ -38,58 +38,14 @@
 
 namespace fi {
 
-constexpr int kVStride = 288;                      // bytes per LDS V row
-constexpr int kVTileBytes = kBlockTokens * kVStride;  // 9216 per wave
-constexpr int kKStride = 272;                      // bytes per LDS K row (prefix)
-
-// LDS slot of block-relative token t: the P.V contraction index of lane
-// group g, element kk is token 4g + (kk & 3) + 16 (kk >> 2); its V row is
-// stored at slot 4 kk + g.
-__device__ __forceinline__ int v_slot(int t) {
-  const int g = (t & 15) >> 2, i = t & 3, hh = t >> 4;
-  return 4 * (i + 4 * hh) + g;
-}
-
-// Reads the transposed V operand for d-block b: lane (g, n) gets
-// V[token(g, kk)][16 b + n] for kk = 0..7, with two gfx950 transpose reads.
-// ds_read_b64_tr_b16 works per 16-lane group: lane i's element k is element
-// i % 4 of the 4 x 16-bit row addressed by lane i / 4 + 4 k of its group.  So
-// lane n addresses the d-quad n % 4 (columns 16 b + 4 (n % 4) ..) of the row
-// of contraction element kk = n / 4 (first read) or 4 + n / 4 (second).
+// gfx950 transpose read of 16-bit LDS data (ds_read_b64_tr_b16), used for
+// the V^T operand of P.V.  It works per 16-lane group: lane i's element k is
+// element i % 4 of the 4 x 16-bit row addressed by lane i / 4 + 4 k of its
+// group (layout measured with a probe).  So a lane that addresses the d-quad
+// n % 4 of the row holding contraction element kk = n / 4 receives, over its
+// four elements, that d column for four consecutive contraction elements.
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-__device__ __forceinline__ u32x4 read_vt(const uint8_t* vt, int g, int n, int b) {
-  const int kk = n >> 2, col = (16 * b + 4 * (n & 3)) * 2;
-  const uint8_t* a0 = vt + (4 * kk + g) * kVStride + col;
-  const uint8_t* a1 = vt + (4 * (kk + 4) + g) * kVStride + col;
-  const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
-  const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a1));
-  const u32x2 w0 = __builtin_bit_cast(u32x2, r0), w1 = __builtin_bit_cast(u32x2, r1);
-  return u32x4{w0.x, w0.y, w1.x, w1.y};
-}
-
-// Loads the q row pieces of one lane as the B operand of the 4 score steps.
-// Step s holds d = dmap(s, g) .. +7; zero for columns past the group.
-template <int KV>
-__device__ __forceinline__ int q_dim(int s, int g) {
-  if constexpr (KV == kKvE4M3) return 64 * (s >> 1) + 16 * g + 8 * (s & 1);
-  else return 32 * s + 8 * g;
-}
-
-// K operand for score step s from the raw 16-byte loads of one token row.
-// f16/bf16: load s is step s.  e4m3: load j covers steps 2j (low 8 codes) and
-// 2j+1 (high 8 codes).
-template <int KV, bool QBF16>
-__device__ __forceinline__ u32x4 k_operand(const u32x4* raw, int s) {
-  if constexpr (KV == kKvE4M3) {
-    const u32x4 w = raw[s >> 1];
-    const uint32_t lo = (s & 1) ? w.z : w.x, hi = (s & 1) ? w.w : w.y;
-    const u32x2 a = e4m3x4_to_16<QBF16>(lo), b = e4m3x4_to_16<QBF16>(hi);
-    return u32x4{a.x, a.y, b.x, b.y};
-  } else {
-    return raw[s];
-  }
-}
 
 // ============================================================================
 // decode tiles (page-staged)

@@ -129,14 +129,13 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
     };
     while (hpt > 2 && tiles_at_min(hpt) < 4 * (int64_t)num_cus) hpt >>= 1;
   }
-  const int64_t head_groups = Hkv / hpt;
   const int64_t target_waves = std::max<int64_t>(1, num_cus * waves_per_cu);
   int64_t Lmax = 0;
   for (int r = 0; r < B; ++r) Lmax = std::max(Lmax, lens[r]);
   auto waves_for = [&](int64_t c) {
     int64_t w = 0;
     for (int r = 0; r < B; ++r) w += std::max<int64_t>(1, ceil_div(lens[r], c));
-    return w * head_groups * hpt;
+    return w * Hkv;   // hpt waves per tile, Hkv / hpt tiles per chunk
   };
   int64_t chunk;
   if (in.chunk_tokens > 0) {
@@ -178,7 +177,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
       }
     }
   }
-  const int64_t head_groups_final = Hkv / hpt;
+  const int64_t head_groups = Hkv / hpt;   // decode tiles per (request, chunk)
 
   // ---- cascade prefix chunking
   const int prefix_waves = env_int("FI_PREFIX_WAVES", kPrefixMaxWaves) == 4 ? 4 : 8;
@@ -249,7 +248,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
     int64_t nc = n_dchunks[r];
     bool need_empty = (nc == 0 && ri.n_states == 0);
     for (int64_t c = 0; c < std::max<int64_t>(nc, need_empty ? 1 : 0); ++c) {
-      for (int64_t hg = 0; hg < head_groups_final; ++hg) {
+      for (int64_t hg = 0; hg < head_groups; ++hg) {
         Tile t;
         t.req = r;
         t.kv_head0 = (int32_t)(hg * hpt);
