@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <new>
 #include <string>
 
 #include "fi_decode.h"
@@ -97,7 +98,13 @@ fi_status build_host_plan(const fi_problem* problem, int num_cus, fi::HostPlan* 
   fi_status st = check_dtypes(problem->q_dtype, problem->kv_dtype);
   if (st != FI_OK) return st;
   char err[256] = {0};
-  int rc = fi::plan_build(to_input(problem, num_cus), hp, err, sizeof(err));
+  int rc;
+  try {   // no exception crosses the C ABI
+    rc = fi::plan_build(to_input(problem, num_cus), hp, err, sizeof(err));
+  } catch (const std::bad_alloc&) {
+    fi::plan_free(hp);
+    return fail(FI_ERR_INVALID_ARG, "out of host memory while planning");
+  }
   if (rc != 0) {
     fi::plan_free(hp);
     return fail(rc == 2 ? FI_ERR_UNSUPPORTED : FI_ERR_INVALID_ARG, "%s", err);
@@ -224,7 +231,13 @@ fi_status fi_plan(const fi_problem* problem, int32_t num_cus, void* workspace,
     fi::plan_free(&hp);
     return hip_fail(e, "uploading the plan");
   }
-  fi_plan_s* pl = new fi_plan_s;
+  fi_plan_s* pl = new (std::nothrow) fi_plan_s;
+  if (!pl) {
+    (void)hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));   // staging in use
+    (void)hipHostFree(staging);
+    fi::plan_free(&hp);
+    return fail(FI_ERR_INVALID_ARG, "out of host memory for the plan object");
+  }
   pl->hp = hp;
   pl->workspace = reinterpret_cast<char*>(workspace);
   pl->workspace_bytes = workspace_bytes;

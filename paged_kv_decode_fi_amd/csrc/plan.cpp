@@ -214,6 +214,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   std::vector<char> folded(B, 0);
   for (int r = 0; r < B; ++r) n_dchunks[r] = lens[r] > 0 ? ceil_div(lens[r], chunk) : 0;
   out->req_info = (ReqInfo*)malloc(sizeof(ReqInfo) * std::max(B, 1));
+  if (!out->req_info) PLAN_FAIL(1, "out of host memory");
   int64_t slots = 0, n_merge = 0;
   for (int r = 0; r < B; ++r) {
     int g = group_of[r];
@@ -231,6 +232,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
       PLAN_FAIL(2, "too many partial states; raise chunk_tokens");
   }
   out->merge_units = (MergeUnit*)malloc(sizeof(MergeUnit) * std::max<int64_t>(n_merge, 1));
+  if (!out->merge_units) PLAN_FAIL(1, "out of host memory");
   {
     int64_t k = 0;
     for (int r = 0; r < B; ++r)
@@ -289,10 +291,12 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
         }
   }
   out->qo_indptr = (int32_t*)malloc(sizeof(int32_t) * (NG + 1));
+  if (!out->qo_indptr) PLAN_FAIL(1, "out of host memory");
   for (int g = 0; g <= NG; ++g) out->qo_indptr[g] = NG > 0 ? in.qo_indptr[g] : 0;
   out->num_tiles = (int64_t)dt.size();
   out->num_prefix_tiles = (int64_t)pt.size();
   out->tiles = (Tile*)malloc(sizeof(Tile) * std::max<size_t>(dt.size() + pt.size(), 1));
+  if (!out->tiles) PLAN_FAIL(1, "out of host memory");
   std::copy(dt.begin(), dt.end(), out->tiles);
   std::copy(pt.begin(), pt.end(), out->tiles + dt.size());
 
