@@ -133,13 +133,34 @@ def _host_i32(a) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
 
 
-def _ptr(t) -> Optional[int]:
-    """Device pointer of a torch tensor (contiguous), or None."""
+def _ptr(t, name: str = "tensor", dtype=None) -> Optional[int]:
+    """Device pointer of a contiguous GPU torch tensor (of `dtype` when
+    given), or None.  A host tensor would reach the kernels as a host
+    address, so it is rejected here."""
     if t is None:
         return None
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a GPU tensor")
     if not t.is_contiguous():
-        raise ValueError("tensors passed to the library must be contiguous")
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     return t.data_ptr()
+
+
+def _tables(kv_indptr, kv_indices, last_page_len, prefix=None):
+    """Device pointers of the page tables (int32 GPU tensors)."""
+    import torch
+    names = ("kv_indptr", "kv_indices", "last_page_len")
+    out = [_ptr(t, n, torch.int32) for t, n in zip((kv_indptr, kv_indices, last_page_len), names)]
+    if prefix is not None:
+        out = [_ptr(t, "prefix_" + n, torch.int32) for t, n in zip(prefix, names)] + out
+    return out
+
+
+def _scales(k_scale, v_scale):
+    import torch
+    return _ptr(k_scale, "k_scale", torch.float32), _ptr(v_scale, "v_scale", torch.float32)
 
 
 def _np_ptr(a) -> Optional[int]:
@@ -228,9 +249,14 @@ class Plan:
         import torch
         if o is None:
             o = torch.empty_like(q)
+        elif o.dtype != q.dtype or o.shape != q.shape:
+            raise ValueError(f"o must be {q.dtype} {tuple(q.shape)}, got {o.dtype} "
+                             f"{tuple(o.shape)}")
         if lse is None:
             lse = torch.empty((self.batch, self.num_qo_heads), dtype=torch.float32,
                               device=q.device)
+        elif lse.dtype != torch.float32 or tuple(lse.shape) != (self.batch, self.num_qo_heads):
+            raise ValueError(f"lse must be float32 [{self.batch}, {self.num_qo_heads}]")
         return o, lse
 
     def _check_q(self, q):
@@ -256,10 +282,11 @@ class Plan:
         self._check_q(q)
         self._check_pool(k_pages, v_pages)
         o, lse = self._outputs(q, o, lse)
-        _check(_get_lib().fi_decode_run(self.handle, _ptr(q), _ptr(k_pages), _ptr(v_pages),
-                                 _ptr(kv_indptr), _ptr(kv_indices), _ptr(last_page_len),
-                                 _ptr(k_scale), _ptr(v_scale), float(sm_scale), _ptr(o),
-                                 _ptr(lse), _stream(stream)))
+        _check(_get_lib().fi_decode_run(self.handle, _ptr(q, "q"), _ptr(k_pages, "k_pages"),
+                                        _ptr(v_pages, "v_pages"),
+                                        *_tables(kv_indptr, kv_indices, last_page_len),
+                                        *_scales(k_scale, v_scale), float(sm_scale),
+                                        _ptr(o, "o"), _ptr(lse, "lse"), _stream(stream)))
         return o, lse
 
     def cascade_run(self, q, k_pages, v_pages, prefix_kv_indptr, prefix_kv_indices,
@@ -272,12 +299,12 @@ class Plan:
         self._check_q(q)
         self._check_pool(k_pages, v_pages)
         o, lse = self._outputs(q, o, lse)
-        _check(_get_lib().fi_cascade_decode(self.handle, _ptr(q), _ptr(k_pages), _ptr(v_pages),
-                                     _ptr(prefix_kv_indptr), _ptr(prefix_kv_indices),
-                                     _ptr(prefix_last_page_len), _ptr(kv_indptr),
-                                     _ptr(kv_indices), _ptr(last_page_len),
-                                     _ptr(k_scale), _ptr(v_scale), float(sm_scale),
-                                     _ptr(o), _ptr(lse), _stream(stream)))
+        _check(_get_lib().fi_cascade_decode(
+            self.handle, _ptr(q, "q"), _ptr(k_pages, "k_pages"), _ptr(v_pages, "v_pages"),
+            *_tables(kv_indptr, kv_indices, last_page_len,
+                     (prefix_kv_indptr, prefix_kv_indices, prefix_last_page_len)),
+            *_scales(k_scale, v_scale), float(sm_scale), _ptr(o, "o"), _ptr(lse, "lse"),
+            _stream(stream)))
         return o, lse
 
     def run_stage(self, stage, q, k_pages, v_pages, kv_indptr, kv_indices, last_page_len,
@@ -291,10 +318,12 @@ class Plan:
         self._check_pool(k_pages, v_pages)
         o, lse = self._outputs(q, o, lse)
         _check(_get_lib().fi_debug_run_stage(
-            self.handle, int(stage), _ptr(q), _ptr(k_pages), _ptr(v_pages),
-            _ptr(prefix_kv_indptr), _ptr(prefix_kv_indices), _ptr(prefix_last_page_len),
-            _ptr(kv_indptr), _ptr(kv_indices), _ptr(last_page_len), _ptr(k_scale),
-            _ptr(v_scale), float(sm_scale), _ptr(o), _ptr(lse), _stream(stream)))
+            self.handle, int(stage), _ptr(q, "q"), _ptr(k_pages, "k_pages"),
+            _ptr(v_pages, "v_pages"),
+            *_tables(kv_indptr, kv_indices, last_page_len,
+                     (prefix_kv_indptr, prefix_kv_indices, prefix_last_page_len)),
+            *_scales(k_scale, v_scale), float(sm_scale), _ptr(o, "o"), _ptr(lse, "lse"),
+            _stream(stream)))
         return o, lse
 
     def destroy(self):

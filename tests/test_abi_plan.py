@@ -225,3 +225,14 @@ def test_cascade_single_chunk_suffix_folds_prefix_states(fi):
         else:                         # split: partial states, merged afterwards
             assert slot >= 0 and r1 == 0, (req, slot, r1)
     assert not any(t[0] == 1 for t in tiles if t[5] == 0)   # empty suffix: prefix only
+
+
+def test_binding_rejects_host_and_mistyped_tensors(fi):
+    """The binding passes device pointers only: a host tensor (its address
+    would reach the kernels) or a mistyped table is refused before any call."""
+    import torch
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fi._ptr(torch.zeros(4), "q")
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fi._tables(torch.zeros(3, dtype=torch.int32), None, None)
+    assert fi._ptr(None) is None
