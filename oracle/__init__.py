@@ -69,10 +69,12 @@ def lib() -> ctypes.CDLL:
         L.oracle_gather_map.argtypes = [I, I, P, P, P, P]
         L.oracle_decode.restype = I
         L.oracle_decode.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P,
-                                    D, P, P, P, I]
+                                    D, P, P, P, I, I, D, D]
         L.oracle_cascade.restype = I
         L.oracle_cascade.argtypes = [I, I, I, I, I, I, I, P, P, P, I, P, P, P, P,
-                                     P, P, P, P, P, D, P, P, P, I]
+                                     P, P, P, P, P, D, P, P, P, I, I, D, D]
+        L.oracle_rope_rotate.restype = None
+        L.oracle_rope_rotate.argtypes = [P, I, D, D, D, P]
         L.oracle_merge.restype = I
         L.oracle_merge.argtypes = [I, I64, I, I, P, I, P, P, P]
         _lib = L
@@ -123,11 +125,31 @@ def gather_map(page_size, kv_indptr, kv_indices, last_page_len) -> np.ndarray:
     return out[:total]
 
 
+def _rope_args(rope):
+    """rope = None or (theta, scale) -> (on, theta, scale) for the C oracle."""
+    if rope is None:
+        return 0, 1.0, 1.0
+    theta, scale = rope
+    return 1, float(theta), float(scale)
+
+
+def rope_rotate(x, pos, theta=1e4, scale=1.0):
+    """The oracle's rotate-half RoPE of one fp64 vector at position pos."""
+    x = _c(x, np.float64)
+    out = np.empty_like(x)
+    lib().oracle_rope_rotate(_ptr(x), len(x), float(pos), float(theta), float(scale),
+                             _ptr(out))
+    return out
+
+
 def decode(q, k_pages, v_pages, kv_indptr, kv_indices, last_page_len, *,
            num_qo_heads, num_kv_heads, head_dim, page_size, q_dtype, kv_dtype,
-           sm_scale, k_scale=None, v_scale=None, unit_mask=None, threads=None):
+           sm_scale, k_scale=None, v_scale=None, unit_mask=None, threads=None,
+           rope=None):
     """fp64 paged decode.  q/k_pages/v_pages are raw storage arrays (uint16 for
     f16/bf16 bits, uint8 for e4m3 codes, float32/float64 otherwise).
+    rope = (theta, scale) applies LLaMA-style rotate-half RoPE (keys at their
+    logical index, the query at kv_len - 1).
     Returns (o [B, Hq, D] fp64, lse [B, Hq] fp64)."""
     indptr = _c(kv_indptr, np.int32)
     B = len(indptr) - 1
@@ -142,7 +164,7 @@ def decode(q, k_pages, v_pages, kv_indptr, kv_indices, last_page_len, *,
                              _ptr(k_pages), _ptr(v_pages), _ptr(indptr),
                              _ptr(indices), _ptr(last), _ptr(ks), _ptr(vs),
                              float(sm_scale), _ptr(um), _ptr(o), _ptr(lse),
-                             threads or default_threads())
+                             threads or default_threads(), *_rope_args(rope))
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments")
     return o, lse
@@ -152,8 +174,9 @@ def cascade(q, k_pages, v_pages, prefix_qo_indptr, prefix_kv_indptr,
             prefix_kv_indices, prefix_last_page_len, kv_indptr, kv_indices,
             last_page_len, *, num_qo_heads, num_kv_heads, head_dim, page_size,
             q_dtype, kv_dtype, sm_scale, k_scale=None, v_scale=None,
-            unit_mask=None, threads=None):
-    """fp64 cascade decode: shared prefix of each request group ++ own pages."""
+            unit_mask=None, threads=None, rope=None):
+    """fp64 cascade decode: shared prefix of each request group ++ own pages
+    (with rope: prefix tokens at positions 0.., own tokens after them)."""
     indptr = _c(kv_indptr, np.int32)
     B = len(indptr) - 1
     qo_ip = _c(prefix_qo_indptr, np.int32)
@@ -170,7 +193,8 @@ def cascade(q, k_pages, v_pages, prefix_qo_indptr, prefix_kv_indptr,
                               _ptr(ka), _ptr(va), G, _ptr(qoa), _ptr(pia),
                               _ptr(pxa), _ptr(pla), _ptr(ia), _ptr(xa), _ptr(la),
                               _ptr(ksa), _ptr(vsa), float(sm_scale), _ptr(uma),
-                              _ptr(o), _ptr(lse), threads or default_threads())
+                              _ptr(o), _ptr(lse), threads or default_threads(),
+                              *_rope_args(rope))
     if rc != 0:
         raise ValueError("oracle_cascade rejected its arguments")
     return o, lse

@@ -32,7 +32,15 @@
  *   - fp8 is OCP E4M3FN (bias 7, max 448, S.1111.111 is NaN, no inf),
  *     dequantised value = decode(code) * scale[kv_head];
  *   - softmax is taken in two passes (max, then sums), in fp64, with dot
- *     products summed over d in ascending order.
+ *     products summed over d in ascending order;
+ *   - "LLaMA style RoPE on-the-fly" (README decode example with
+ *     pos_encoding_mode="ROPE_LLAMA"; "core features" item 3, fused-RoPE
+ *     attention) -- the pages give no formula; read as rotate-half: for
+ *     i < D/2, angle_i = (pos / rope_scale) * rope_theta^(-2 i / D) and the
+ *     pair (x_i, x_{i+D/2}) turns by angle_i; key t of a request's key list
+ *     (cascade: the group's prefix tokens, then the request's own) sits at
+ *     position t, the query at position L - 1 (the token being decoded is
+ *     the last one in the cache); V is not rotated.
  */
 #include <math.h>
 #include <pthread.h>
@@ -142,21 +150,50 @@ typedef struct {
   double k_scale, v_scale;
 } kv_src;
 
+/* Rotate-half RoPE of one D-vector at position pos (see the readings
+ * above): out_i = x_i cos a_i - x_{i+D/2} sin a_i,
+ * out_{i+D/2} = x_{i+D/2} cos a_i + x_i sin a_i, a_i = (pos / scale) *
+ * theta^(-2 i / D).  out may not alias x. */
+void oracle_rope_rotate(const double* x, int D, double pos, double theta, double scale,
+                        double* out) {
+  const int half = D / 2;
+  for (int i = 0; i < half; ++i) {
+    const double a = (pos / scale) * pow(theta, -2.0 * i / D);
+    const double c = cos(a), s = sin(a);
+    out[i] = x[i] * c - x[i + half] * s;
+    out[i + half] = x[i + half] * c + x[i] * s;
+  }
+}
+
+typedef struct {
+  int on;
+  double theta, scale;
+} rope_t;
+
 static void attend_row(const double* q, const int64_t* row_off, int64_t L,
-                       const kv_src* src, double sm_scale, double* x /*[L]*/,
-                       double* o, double* lse) {
+                       const kv_src* src, double sm_scale, const rope_t* rope,
+                       double* x /*[L]*/, double* o, double* lse) {
   const int D = src->D;
   for (int d = 0; d < D; ++d) o[d] = 0.0;
   if (L == 0) {
     *lse = -INFINITY;
     return;
   }
+  double qr[512], kr[512], kraw[512];   /* D <= 512 */
+  if (rope->on)
+    oracle_rope_rotate(q, D, (double)(L - 1), rope->theta, rope->scale, qr);
+  else
+    for (int d = 0; d < D; ++d) qr[d] = q[d];
   double M = -INFINITY;
   for (int64_t t = 0; t < L; ++t) {
-    double dot = 0.0;
     for (int d = 0; d < D; ++d)
-      dot += q[d] * (load_elem(src->k_pool, src->kv_dtype, row_off[t] + d) *
-                     src->k_scale);
+      kraw[d] = load_elem(src->k_pool, src->kv_dtype, row_off[t] + d) * src->k_scale;
+    if (rope->on)
+      oracle_rope_rotate(kraw, D, (double)t, rope->theta, rope->scale, kr);
+    else
+      for (int d = 0; d < D; ++d) kr[d] = kraw[d];
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d) dot += qr[d] * kr[d];
     x[t] = sm_scale * dot;
     if (x[t] > M) M = x[t];
   }
@@ -188,6 +225,7 @@ typedef struct {
   const int32_t *qo_indptr, *p_indptr, *p_indices, *p_last;
   const float *k_scale, *v_scale;
   double sm_scale;
+  rope_t rope;
   const uint8_t* unit_mask; /* [batch*Hkv] or NULL: 1 = compute this item */
   double* o;                /* [batch][Hq][D] */
   double* lse;              /* [batch][Hq] */
@@ -224,7 +262,7 @@ static void run_item(const job_t* J, int r, int h, int64_t* rows, double* x,
   for (int j = h * G; j < (h + 1) * G; ++j) {
     int64_t qo = ((int64_t)r * J->Hq + j) * D;
     for (int d = 0; d < D; ++d) qv[d] = load_elem(J->q, J->q_dtype, qo + d);
-    attend_row(qv, rows, L, &src, J->sm_scale, x, J->o + qo,
+    attend_row(qv, rows, L, &src, J->sm_scale, &J->rope, x, J->o + qo,
                J->lse + (int64_t)r * J->Hq + j);
   }
 }
@@ -248,7 +286,10 @@ static void* worker(void* arg) {
 }
 
 static int run_job(job_t* J, int num_threads) {
-  if (J->Hkv <= 0 || J->Hq % J->Hkv != 0 || J->ps <= 0 || J->D <= 0) return -1;
+  if (J->Hkv <= 0 || J->Hq % J->Hkv != 0 || J->ps <= 0 || J->D <= 0 || J->D > 512 ||
+      (J->D & 1))
+    return -1;
+  if (J->rope.on && !(J->rope.theta > 0.0 && J->rope.scale > 0.0)) return -1;
   J->max_len = 0;
   for (int r = 0; r < J->batch; ++r) {
     int64_t L = request_len(J->indptr, J->last, r, J->ps);
@@ -277,9 +318,10 @@ int oracle_decode(int batch, int num_qo_heads, int num_kv_heads, int head_dim,
                   const int32_t* last_page_len, const float* k_scale,
                   const float* v_scale, double sm_scale,
                   const uint8_t* unit_mask, double* o, double* lse,
-                  int num_threads) {
+                  int num_threads, int rope, double rope_theta, double rope_scale) {
   job_t J;
   memset(&J, 0, sizeof(J));
+  J.rope.on = rope; J.rope.theta = rope_theta; J.rope.scale = rope_scale;
   J.batch = batch; J.Hq = num_qo_heads; J.Hkv = num_kv_heads; J.D = head_dim;
   J.ps = page_size; J.q_dtype = q_dtype; J.kv_dtype = kv_dtype;
   J.q = q; J.k_pages = k_pages; J.v_pages = v_pages;
@@ -303,9 +345,10 @@ int oracle_cascade(int batch, int num_qo_heads, int num_kv_heads, int head_dim,
                    const int32_t* last_page_len, const float* k_scale,
                    const float* v_scale, double sm_scale,
                    const uint8_t* unit_mask, double* o, double* lse,
-                   int num_threads) {
+                   int num_threads, int rope, double rope_theta, double rope_scale) {
   job_t J;
   memset(&J, 0, sizeof(J));
+  J.rope.on = rope; J.rope.theta = rope_theta; J.rope.scale = rope_scale;
   J.batch = batch; J.Hq = num_qo_heads; J.Hkv = num_kv_heads; J.D = head_dim;
   J.ps = page_size; J.q_dtype = q_dtype; J.kv_dtype = kv_dtype;
   J.q = q; J.k_pages = k_pages; J.v_pages = v_pages;

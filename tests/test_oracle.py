@@ -392,3 +392,111 @@ def test_gather_map_matches_brute_force(oracle_lib):
                 cnt = ps if p_i < len(pages) - 1 else last[r]
                 want.extend(int(p) * ps + s for s in range(cnt))
         assert np.array_equal(got, np.array(want, np.int64))
+
+
+# ------------------------------------------------------------- RoPE pins
+# The pages name LLaMA-style RoPE on-the-fly but give no formula; the
+# oracle's reading (rotate-half, angle_i = pos / scale * theta^(-2i/D)) is
+# pinned here by identities and by a complex-number restatement written
+# independently of the oracle's real-valued rotation.
+
+def _rope_complex(x, pos, theta=1e4, scale=1.0):
+    """Rotate-half RoPE as a complex multiplication: the pair (x_i, x_{i+D/2})
+    is the complex number x_i + i x_{i+D/2}, turned by e^{i angle_i}."""
+    x = np.asarray(x, np.float64)
+    h = len(x) // 2
+    ang = (pos / scale) * theta ** (-2.0 * np.arange(h) / len(x))
+    z = (x[:h] + 1j * x[h:]) * np.exp(1j * ang)
+    return np.concatenate([z.real, z.imag])
+
+
+def test_rope_rotation_pins(oracle_lib):
+    rng = np.random.default_rng(31)
+    D = 128
+    x = rng.standard_normal(D)
+    y = rng.standard_normal(D)
+    # position 0 is the identity
+    assert np.array_equal(oracle_lib.rope_rotate(x, 0), x)
+    for pos, theta, scale in [(1, 1e4, 1.0), (37, 1e4, 1.0), (4095, 5e5, 1.0),
+                              (32767, 1e4, 1.0), (1000, 1e4, 4.0)]:
+        r = oracle_lib.rope_rotate(x, pos, theta, scale)
+        # the angle reaches pos radians: one ulp of it is ~pos * 1.1e-16
+        np.testing.assert_allclose(r, _rope_complex(x, pos, theta, scale), rtol=0,
+                                   atol=1e-13 + 4e-16 * pos * np.abs(x).max())
+        assert abs(np.linalg.norm(r) - np.linalg.norm(x)) < 1e-12   # a rotation
+    # the scale divides the position
+    np.testing.assert_allclose(oracle_lib.rope_rotate(x, 1000, 1e4, 4.0),
+                               oracle_lib.rope_rotate(x, 250, 1e4, 1.0), rtol=0, atol=1e-13)
+    # scores depend only on the position difference
+    for p1, p2, c in [(5, 9, 100), (4000, 17, 3), (0, 2047, 2048)]:
+        a = np.dot(oracle_lib.rope_rotate(x, p1), oracle_lib.rope_rotate(y, p2))
+        b = np.dot(oracle_lib.rope_rotate(x, p1 + c), oracle_lib.rope_rotate(y, p2 + c))
+        assert abs(a - b) < 1e-11
+    # a planted sign or pairing mistake does not pass the complex restatement
+    wrong = x.copy()
+    h = D // 2
+    ang = 37 * 1e4 ** (-2.0 * np.arange(h) / D)
+    wrong[:h] = x[:h] * np.cos(ang) + x[h:] * np.sin(ang)
+    wrong[h:] = x[h:] * np.cos(ang) - x[:h] * np.sin(ang)
+    assert np.abs(wrong - _rope_complex(x, 37)).max() > 1e-3
+
+
+def test_rope_decode_equals_plain_decode_of_prerotated_data(oracle_lib):
+    """Decode with RoPE = plain decode (no RoPE) over keys pre-rotated at
+    their logical index and queries at kv_len - 1, the rotations done here
+    with the complex restatement and stored as fp64 -- pins the position each
+    key and query gets and that V is not rotated."""
+    rng = np.random.default_rng(32)
+    Hq, Hkv, D, ps = 4, 2, 128, 3
+    lens = [1, 7, 40]
+    kd = [f16_values(rng.standard_normal((L, Hkv, D))) for L in lens]
+    vd = [f16_values(rng.standard_normal((L, Hkv, D))) for L in lens]
+    q = f16_values(rng.standard_normal((len(lens), Hq, D)))
+    kp, indptr, idx, last = paginate([to_f16_bits(k) for k in kd], ps, Hkv, D,
+                                     np.random.default_rng(1))
+    vp, _, _, _ = paginate([to_f16_bits(v) for v in vd], ps, Hkv, D, np.random.default_rng(1))
+    kw = dict(num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=ps, sm_scale=0.09)
+    o_r, l_r = oracle_lib.decode(to_f16_bits(q), kp, vp, indptr, idx, last, q_dtype="f16",
+                                 kv_dtype="f16", rope=(1e4, 1.0), **kw)
+    kr = [np.stack([[_rope_complex(k[t, h], t) for h in range(Hkv)] for t in range(len(k))])
+          for k in kd]
+    qr = np.stack([[_rope_complex(q[r, j], lens[r] - 1) for j in range(Hq)]
+                   for r in range(len(lens))])
+    kp2, indptr2, idx2, last2 = paginate(kr, ps, Hkv, D, np.random.default_rng(1),
+                                         fill_bits=np.nan, dtype=np.float64)
+    vp2, _, _, _ = paginate(vd, ps, Hkv, D, np.random.default_rng(1), fill_bits=np.nan,
+                            dtype=np.float64)
+    o_p, l_p = oracle_lib.decode(qr, kp2, vp2, indptr2, idx2, last2, q_dtype="f64",
+                                 kv_dtype="f64", **kw)
+    np.testing.assert_allclose(o_r, o_p, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l_r, l_p, rtol=0, atol=1e-12)
+    # a single key at position 0 with the query at position 0: RoPE is the identity
+    o_0, l_0 = oracle_lib.decode(to_f16_bits(q), kp, vp, indptr, idx, last, q_dtype="f16",
+                                 kv_dtype="f16", **kw)
+    assert np.array_equal(o_r[0], o_0[0]) and np.array_equal(l_r[0], l_0[0])
+
+
+def test_rope_cascade_is_flat_over_concatenated_keys(oracle_lib):
+    """With RoPE the group's prefix tokens take positions 0 .. P-1 and the
+    request's own tokens follow: cascade = flat decode over the concatenated
+    table, bit for bit."""
+    rng = np.random.default_rng(33)
+    Hq, Hkv, D, ps = 2, 1, 128, 4
+    P, lens = 10, [3, 0, 9]
+    pre = to_f16_bits(rng.standard_normal((P, Hkv, D)))
+    own = [to_f16_bits(rng.standard_normal((L, Hkv, D))) for L in lens]
+    q = to_f16_bits(rng.standard_normal((len(lens), Hq, D)))
+    pool, indptr, idx, last = paginate([pre] + own, ps, Hkv, D, np.random.default_rng(2))
+    n_pre = (P + ps - 1) // ps
+    kw = dict(num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=ps, q_dtype="f16",
+              kv_dtype="f16", sm_scale=0.1, rope=(1e4, 1.0))
+    p_indptr = np.array([0, n_pre], np.int32)
+    own_indptr = (indptr[1:] - n_pre).astype(np.int32)
+    o_c, l_c = oracle_lib.cascade(q, pool, pool, np.array([0, len(lens)], np.int32), p_indptr,
+                                  idx[:n_pre], last[:1], own_indptr, idx[n_pre:], last[1:], **kw)
+    # flat tables: the prefix pages then the request's own pages
+    assert P % ps != 0     # the prefix's last page is partial: flat needs whole pages
+    flat_dense = [np.concatenate([pre, o]) for o in own]
+    fpool, findptr, fidx, flast = paginate(flat_dense, ps, Hkv, D, np.random.default_rng(3))
+    o_f, l_f = oracle_lib.decode(q, fpool, fpool, findptr, fidx, flast, **kw)
+    assert np.array_equal(o_c, o_f) and np.array_equal(l_c, l_f)
