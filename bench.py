@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--page-size", type=int, default=16, choices=(1, 16),
                     help="long32_fp8 only: run the page-size-1 or page-size-16 variant")
+    ap.add_argument("--rope", action="store_true",
+                    help="plain decode workloads: LLaMA-style RoPE on the fly "
+                         "(theta 1e4, scale 1)")
     return ap.parse_args()
 
 
@@ -117,19 +120,25 @@ def main():
     prefix = ((w.prefix_qo_indptr, w.prefix_kv_indptr, w.prefix_last_page_len)
               if cascade else None)
 
+    if args.rope and cascade:
+        print(json.dumps({"error": "--rope applies to plain decode workloads only"}))
+        sys.exit(2)
+    rope_kw = dict(pos_encoding="rope_llama", rope_theta=1e4, rope_scale=1.0) if args.rope else {}
+    traffic_key = w.name + ("+rope" if args.rope else "")
+
     # ---- plan stage (host), timed separately; first call includes first use
     t0 = time.perf_counter()
     plan = fi.Plan(w.kv_indptr, w.last_page_len, num_qo_heads=w.num_qo_heads,
                    num_kv_heads=w.num_kv_heads, page_size=w.page_size,
                    head_dim=w.head_dim, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
-                   prefix=prefix)
+                   prefix=prefix, **rope_kw)
     torch.cuda.synchronize()
     plan_first_ms = (time.perf_counter() - t0) * 1e3
     t0 = time.perf_counter()
     plan2 = fi.Plan(w.kv_indptr, w.last_page_len, num_qo_heads=w.num_qo_heads,
                     num_kv_heads=w.num_kv_heads, page_size=w.page_size,
                     head_dim=w.head_dim, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
-                    prefix=prefix)
+                    prefix=prefix, **rope_kw)
     torch.cuda.synchronize()
     plan_ms = (time.perf_counter() - t0) * 1e3
     plan2.destroy()
@@ -249,14 +258,14 @@ def main():
         roofline = {"bound": "mfma", "kernel": "prefix_kernel", "achieved": round(achieved, 1),
                     "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
-                    "traffic": measured_traffic(w.name), "kernel_ms": round(kernel_ms, 5),
+                    "traffic": measured_traffic(traffic_key), "kernel_ms": round(kernel_ms, 5),
                     "per_launch": {"flops": flops}}
     else:
         achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "kernel": "decode_kernel", "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": measured_traffic(w.name), "kernel_ms": round(kernel_ms, 5),
+                    "traffic": measured_traffic(traffic_key), "kernel_ms": round(kernel_ms, 5),
                     "per_launch": {"algorithmic_bytes": alg_bytes}}
 
     # ---- CPU oracle baseline on a bounded sample of the same workload
@@ -281,7 +290,8 @@ def main():
         kw = dict(num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
                   head_dim=w.head_dim, page_size=w.page_size, q_dtype=w.q_dtype,
                   kv_dtype=w.kv_dtype, sm_scale=w.sm_scale, k_scale=w.k_scale,
-                  v_scale=w.v_scale, unit_mask=mask, threads=threads)
+                  v_scale=w.v_scale, unit_mask=mask, threads=threads,
+                  rope=(1e4, 1.0) if args.rope else None)
         t0 = time.perf_counter()
         if cascade:
             oracle.cascade(w.q, w.k_pages, w.v_pages, w.prefix_qo_indptr,
@@ -310,7 +320,8 @@ def main():
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "page_size": w.page_size, "q_dtype": w.q_dtype, "kv_dtype": w.kv_dtype,
                    "kv_len_total": int(w.kv_lens.sum()), "kv_bytes": kv_bytes,
-                   "rotated_copies": R, "graph": bool(args.graph)},
+                   "rotated_copies": R, "graph": bool(args.graph),
+                   "pos_encoding": "rope_llama" if args.rope else "none"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "hbm_read_ceiling_gbs": None if ceiling is None else round(ceiling, 1),
         "pct_read_ceiling": None if ceiling is None else round(100 * value / ceiling, 2),

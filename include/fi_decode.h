@@ -106,7 +106,20 @@ typedef struct {
   const int32_t* prefix_last_page_len; /* host [groups] */
   /* Tuning knob: tokens per split chunk (multiple of 16), 0 = automatic. */
   int32_t chunk_tokens;
+  /* Position encoding (FlashInfer README decode example, pos_encoding_mode;
+   * "core features" item 3, fused RoPE): FI_POS_NONE (0) or
+   * FI_POS_ROPE_LLAMA, LLaMA-style RoPE applied on the fly to q and to the
+   * cached (unrotated) keys: rotate-half over head_dim, the pair
+   * (x_i, x_{i+D/2}) turned by angle_i = pos / rope_scale *
+   * rope_theta^(-2 i / D); key t of a request sits at position t, the query
+   * at kv_len - 1.  Plain decode only (a cascade plan with RoPE is
+   * FI_ERR_UNSUPPORTED). */
+  int32_t pos_encoding;
+  float rope_theta;       /* <= 0: 1e4 */
+  float rope_scale;       /* <= 0: 1 */
 } fi_problem;
+
+enum { FI_POS_NONE = 0, FI_POS_ROPE_LLAMA = 1 };
 
 typedef struct fi_plan_s* fi_plan_t;
 

@@ -46,7 +46,8 @@ class Problem(ctypes.Structure):
                 ("prefix_qo_indptr", ctypes.c_void_p),
                 ("prefix_kv_indptr", ctypes.c_void_p),
                 ("prefix_last_page_len", ctypes.c_void_p),
-                ("chunk_tokens", ctypes.c_int32)]
+                ("chunk_tokens", ctypes.c_int32), ("pos_encoding", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float), ("rope_scale", ctypes.c_float)]
 
 
 class PlanStats(ctypes.Structure):
@@ -173,8 +174,14 @@ def _stream(stream) -> Optional[int]:
     return s.cuda_stream
 
 
-def _problem(batch, Hq, Hkv, D, ps, q_dtype, kv_dtype, indptr, last, prefix, chunk):
+POS_ENCODINGS = {"none": 0, "rope_llama": 1}
+
+
+def _problem(batch, Hq, Hkv, D, ps, q_dtype, kv_dtype, indptr, last, prefix, chunk,
+             pos_encoding="none", rope_theta=0.0, rope_scale=0.0):
     pr = Problem()
+    pr.pos_encoding = POS_ENCODINGS[pos_encoding]
+    pr.rope_theta, pr.rope_scale = rope_theta, rope_scale
     pr.batch, pr.num_qo_heads, pr.num_kv_heads = batch, Hq, Hkv
     pr.head_dim, pr.page_size = D, ps
     pr.q_dtype, pr.kv_dtype = DTYPES[q_dtype], DTYPES[kv_dtype]
@@ -192,12 +199,14 @@ def _problem(batch, Hq, Hkv, D, ps, q_dtype, kv_dtype, indptr, last, prefix, chu
 
 def debug_plan_tiles(kv_indptr, last_page_len, *, num_qo_heads, num_kv_heads,
                      page_size, head_dim=128, q_dtype="f16", kv_dtype="f16",
-                     prefix=None, num_cus=256, chunk_tokens=0) -> np.ndarray:
+                     prefix=None, num_cus=256, chunk_tokens=0,
+                     pos_encoding="none") -> np.ndarray:
     """Host-only: the plan's work list as an int32 [n, 8] array (request,
     kv_head0, t0, t1, slot, kind, row0, row1)."""
     indptr, last = _host_i32(kv_indptr), _host_i32(last_page_len)
     pr, keep = _problem(len(indptr) - 1, num_qo_heads, num_kv_heads, head_dim,
-                        page_size, q_dtype, kv_dtype, indptr, last, prefix, chunk_tokens)
+                        page_size, q_dtype, kv_dtype, indptr, last, prefix, chunk_tokens,
+                        pos_encoding)
     n = ctypes.c_int64(0)
     _check(_get_lib().fi_debug_plan_tiles(ctypes.byref(pr), num_cus, None, 0, ctypes.byref(n)))
     out = np.zeros((max(n.value, 1), 8), np.int32)
@@ -212,11 +221,14 @@ class Plan:
 
     kv_indptr / last_page_len are the HOST copies of the page table (numpy or
     torch CPU).  prefix = (prefix_qo_indptr, prefix_kv_indptr,
-    prefix_last_page_len) host arrays for cascade decoding."""
+    prefix_last_page_len) host arrays for cascade decoding.  pos_encoding =
+    "rope_llama" applies LLaMA-style RoPE to q and the keys on the fly
+    (rope_theta / rope_scale <= 0: 1e4 / 1)."""
 
     def __init__(self, kv_indptr, last_page_len, *, num_qo_heads, num_kv_heads,
                  page_size, head_dim=128, q_dtype="f16", kv_dtype="f16",
-                 prefix=None, num_cus=0, chunk_tokens=0, device=None, stream=None):
+                 prefix=None, num_cus=0, chunk_tokens=0, device=None, stream=None,
+                 pos_encoding="none", rope_theta=0.0, rope_scale=0.0):
         import torch
         self.indptr = _host_i32(kv_indptr)
         self.last = _host_i32(last_page_len)
@@ -225,9 +237,10 @@ class Plan:
         self.head_dim, self.page_size = head_dim, page_size
         self.q_dtype, self.kv_dtype = q_dtype, kv_dtype
         self.cascade = prefix is not None
+        self.pos_encoding = pos_encoding
         pr, keep = _problem(self.batch, num_qo_heads, num_kv_heads, head_dim,
                             page_size, q_dtype, kv_dtype, self.indptr, self.last,
-                            prefix, chunk_tokens)
+                            prefix, chunk_tokens, pos_encoding, rope_theta, rope_scale)
         need = ctypes.c_size_t(0)
         _check(_get_lib().fi_plan(ctypes.byref(pr), num_cus, None, 0, ctypes.byref(need), None,
                            None))

@@ -30,6 +30,7 @@ hipError_t launch_gather(const int32_t* kv_indptr, const int32_t* kv_indices,
                          int ps_shift, int64_t* out, hipStream_t s);
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int blocks,
                               hipStream_t s);
+hipError_t launch_rope_table(void* table, int rows, float theta, float scale, hipStream_t s);
 }  // namespace fi
 
 struct fi_plan_s {
@@ -90,6 +91,9 @@ fi::PlanInput to_input(const fi_problem* p, int num_cus) {
   in.p_last = p->prefix_last_page_len;
   in.chunk_tokens = p->chunk_tokens;
   in.num_cus = num_cus;
+  in.pos_encoding = p->pos_encoding;
+  in.rope_theta = p->rope_theta;
+  in.rope_scale = p->rope_scale;
   return in;
 }
 
@@ -137,6 +141,10 @@ fi::DecodeParams base_params(const fi_plan_s* pl, const void* q, const void* k,
   p.page_size = hp.page_size;
   p.ps_shift = ps_shift_of(hp.page_size);
   p.num_tiles = (int32_t)hp.num_tiles;
+  if (hp.rope) {
+    p.rope_table = pl->workspace + hp.layout.rope_off;
+    p.rope_rows = hp.rope_rows;
+  }
   return p;
 }
 
@@ -226,7 +234,12 @@ fi_status fi_plan(const fi_problem* problem, int32_t num_cus, void* workspace,
   memcpy(st8 + hp.layout.qo_indptr_off, hp.qo_indptr, sizeof(int32_t) * (hp.num_groups + 1));
   e = hipMemcpyAsync(workspace, staging, meta_bytes, hipMemcpyHostToDevice,
                      reinterpret_cast<hipStream_t>(stream));
+  if (e == hipSuccess && hp.rope)   // the (cos, sin) table, built on the device
+    e = fi::launch_rope_table(reinterpret_cast<char*>(workspace) + hp.layout.rope_off,
+                              hp.rope_rows, hp.rope_theta, hp.rope_scale,
+                              reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
+    (void)hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
     (void)hipHostFree(staging);
     fi::plan_free(&hp);
     return hip_fail(e, "uploading the plan");

@@ -123,11 +123,89 @@ __device__ __forceinline__ void fold_states(const float* __restrict__ partial_o,
   }
 }
 
+// ---- RoPE ---------------------------------------------------------------------
+// The rotation is applied in its relative form: turning q by the angle of
+// its position p and key t by that of t is, for the dot product, the same as
+// turning the key alone by the angle of t - p (rotations compose and are
+// orthogonal).  So q enters the score MFMAs as stored, and each key is turned
+// back by its distance d = p - t >= 0 from the query.
+//
+// Table (fp32, built on the device in fp64): row d, frequency i holds
+// (cos, sin) of d / scale * theta^(-2 i / D).  A step reads one row, d0 =
+// p - (first token of the step); key n of the step is at distance d0 - n,
+// whose (cos, sin) follow from rows d0 and n by the angle-difference
+// identities (rows 0..15 stay in LDS for the whole tile).
+template <bool BF16>
+__device__ __forceinline__ float lo16(uint32_t w) {
+  if constexpr (BF16) return __builtin_bit_cast(float, w << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffff));
+}
+template <bool BF16>
+__device__ __forceinline__ float hi16(uint32_t w) {
+  if constexpr (BF16) return __builtin_bit_cast(float, w & 0xffff0000u);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// Turns 8 + 8 partner elements of one key (a: dims f..f+7, b: dims
+// f+64..f+71, 16-bit) back by the angle of distance d0 - n, in fp32, and
+// writes the result as a 16-bit high part plus a 16-bit residual, so that
+// two MFMAs against the same q carry the rotated key to about fp32 accuracy.
+// base / off: the (cos, sin) pairs of frequencies f..f+7 at distances d0 and n.
+template <bool BF16>
+__device__ __forceinline__ void rope_key8(u32x4 a, u32x4 b, const float4* base,
+                                          const float4* off, u32x4& ahi, u32x4& alo,
+                                          u32x4& bhi, u32x4& blo) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float4 bs = base[k], of = off[k];   // frequencies f + 2k, f + 2k + 1
+    float ra[2], rb[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float cb = e ? bs.z : bs.x, sb = e ? bs.w : bs.y;
+      const float co = e ? of.z : of.x, so = e ? of.w : of.y;
+      const float c = __builtin_fmaf(cb, co, sb * so);    // cos((d0 - n) w)
+      const float sn = __builtin_fmaf(sb, co, -cb * so);  // sin((d0 - n) w)
+      const float x = e ? hi16<BF16>(a[k]) : lo16<BF16>(a[k]);
+      const float y = e ? hi16<BF16>(b[k]) : lo16<BF16>(b[k]);
+      ra[e] = __builtin_fmaf(x, c, y * sn);
+      rb[e] = __builtin_fmaf(y, c, -x * sn);
+    }
+    ahi[k] = pack2<BF16>(ra[0], ra[1]);
+    bhi[k] = pack2<BF16>(rb[0], rb[1]);
+    alo[k] = pack2<BF16>(ra[0] - lo16<BF16>(ahi[k]), ra[1] - hi16<BF16>(ahi[k]));
+    blo[k] = pack2<BF16>(rb[0] - lo16<BF16>(bhi[k]), rb[1] - hi16<BF16>(bhi[k]));
+  }
+}
+
+// (cos, sin) table of the plan: one thread per (distance, frequency), angle
+// in fp64 from the definition, stored as two fp32.
+__global__ void rope_table_kernel(float2* table, int rows, double theta, double scale) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)rows * (kHeadDim / 2)) return;
+  const int d = (int)(i / (kHeadDim / 2)), f = (int)(i % (kHeadDim / 2));
+  const double ang = (d / scale) * pow(theta, -2.0 * f / kHeadDim);
+  table[i] = float2{(float)cos(ang), (float)sin(ang)};
+}
+
+hipError_t launch_rope_table(void* table, int rows, float theta, float scale, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t n = (int64_t)rows * (kHeadDim / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<float2*>(table), rows, (double)theta, (double)scale);
+  return hipGetLastError();
+}
+
 // FOLD: the plan has tiles that fold earlier states into their output (a
 // separate instance: the fold costs registers the plain kernel keeps free).
-// DEPTH: steps of K/V loads in flight per workgroup.
-template <int KV, bool QBF16, bool PS_POW2, bool FOLD, int DEPTH>
+// DEPTH: steps of K/V loads in flight per workgroup.  ROPE: every key is
+// turned by its distance from the query (LLaMA-style RoPE, relative form)
+// before the score MFMAs; the LDS after K and V holds the step's table row
+// and table rows 0..15.
+constexpr int kRopeLdsStride = kRopeRowBytes + 16;   // rows 0..15, bank-conflict-free
+constexpr int kRopeLds = kRopeRowBytes + kStep * kRopeLdsStride;
+template <int KV, bool QBF16, bool PS_POW2, bool FOLD, int DEPTH, bool ROPE>
 __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams p) {
+  static_assert(!ROPE || (DEPTH == 1 && !FOLD), "RoPE runs with one step in flight, no fold");
   using S = Stage<KV>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int W = blockDim.x >> 6;                  // waves = kv heads of the tile
@@ -147,6 +225,7 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   const int KS = S::k_stride(W), VS = S::v_stride(W);
   uint8_t* klds = lds;
   uint8_t* vlds = lds + kStep * KS;
+  uint8_t* rlds = lds + kStep * (KS + VS);   // RoPE: step row, then rows 0..15
 
   // q of this wave's head group as the B operand of the score MFMAs
   u32x4 qop[4];
@@ -160,6 +239,8 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
       qop[s] = ok ? v : u32x4{0, 0, 0, 0};
     }
   }
+  // RoPE: the query sits at position kv_len - 1
+  const int qpos = ROPE ? p.req_info[r].kv_len - 1 : 0;
   float c = p.sm_scale_log2;
   if (KV == kKvE4M3 && p.k_scale) c *= p.k_scale[h];
 
@@ -182,6 +263,32 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   // DEPTH register sets of step loads (kr/vr[d]); set d holds steps d, d +
   // DEPTH, ...
   u32x4 kr[DEPTH][S::LOADS], vr[DEPTH][S::LOADS];
+  // RoPE: table row d0 of a step (32 vectors of 16 B) goes through the
+  // registers of threads 0..31 like K and V; rows 0..15 are staged once
+  const u32x4* rtab = reinterpret_cast<const u32x4*>(p.rope_table);
+  u32x4 rr;
+  auto issue_rope = [&](int step) {
+    if constexpr (ROPE)
+      if (tid < kRopeRowBytes / 16) rr = rtab[(int64_t)(qpos - t0 - kStep * step) * 32 + tid];
+  };
+  auto stage_rope = [&]() {
+    if constexpr (ROPE)
+      if (tid < kRopeRowBytes / 16) reinterpret_cast<u32x4*>(rlds)[tid] = rr;
+  };
+  if constexpr (ROPE) {
+    constexpr int kVec = kStep * kRopeRowBytes / 16;   // 512 vectors of rows 0..15
+    u32x4 o16[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (tid + u * 64 * W < kVec) o16[u] = rtab[tid + u * 64 * W];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = tid + u * 64 * W;
+      if (idx < kVec)
+        *reinterpret_cast<u32x4*>(rlds + kRopeRowBytes + (idx >> 5) * kRopeLdsStride +
+                                  16 * (idx & 31)) = o16[u];
+    }
+  }
   auto issue = [&](int step, int pg, u32x4 (&kq)[S::LOADS], u32x4 (&vq)[S::LOADS]) {
     const int tb = t0 + kStep * step;
 #pragma unroll
@@ -225,17 +332,33 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   auto compute = [&](int step) {
     const int tb = t0 + kStep * step;
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4 kop;
+    // lane (g, n): dims 32 s + 8 g .. +7 of key n of the step
+    auto kop_of = [&](int s) -> u32x4 {
       if constexpr (KV == kKvE4M3) {
         const u32x2 w8 = *reinterpret_cast<const u32x2*>(krow + 32 * s + 8 * g);
         const u32x2 a = e4m3x4_to_16<QBF16>(w8.x), b = e4m3x4_to_16<QBF16>(w8.y);
-        kop = u32x4{a.x, a.y, b.x, b.y};
+        return u32x4{a.x, a.y, b.x, b.y};
       } else {
-        kop = *reinterpret_cast<const u32x4*>(krow + 64 * s + 16 * g);
+        return *reinterpret_cast<const u32x4*>(krow + 64 * s + 16 * g);
       }
-      sc = mma16x16x32<QBF16>(kop, qop[s], sc);
+    };
+    if constexpr (ROPE) {
+      // dims of kop(j) (frequencies 32 j + 8 g ..) pair with kop(j + 2)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float4* base = reinterpret_cast<const float4*>(rlds + 256 * j + 64 * g);
+        const float4* off = reinterpret_cast<const float4*>(
+            rlds + kRopeRowBytes + n * kRopeLdsStride + 256 * j + 64 * g);
+        u32x4 ahi, alo, bhi, blo;
+        rope_key8<QBF16>(kop_of(j), kop_of(j + 2), base, off, ahi, alo, bhi, blo);
+        sc = mma16x16x32<QBF16>(ahi, qop[j], sc);
+        sc = mma16x16x32<QBF16>(alo, qop[j], sc);
+        sc = mma16x16x32<QBF16>(bhi, qop[j + 2], sc);
+        sc = mma16x16x32<QBF16>(blo, qop[j + 2], sc);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sc = mma16x16x32<QBF16>(kop_of(s), qop[s], sc);
     }
     float x[4];
 #pragma unroll
@@ -277,11 +400,16 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
     if (nsteps > 0) {
       int pg1 = nsteps > 1 ? load_page(1) : 0;
       issue(0, load_page(0), kr[0], vr[0]);
+      issue_rope(0);
       for (int step = 0; step < nsteps; ++step) {
         const int pg2 = step + 2 < nsteps ? load_page(step + 2) : 0;
         stage(kr[0], vr[0]);
+        stage_rope();
         __syncthreads();
-        if (step + 1 < nsteps) issue(step + 1, pg1, kr[0], vr[0]);
+        if (step + 1 < nsteps) {
+          issue(step + 1, pg1, kr[0], vr[0]);
+          issue_rope(step + 1);
+        }
         compute(step);
         __syncthreads();
         pg1 = pg2;
@@ -656,28 +784,29 @@ static int getenv_depth() {
   return d;
 }
 
-template <int KV, bool QBF16, bool FOLD, int DEPTH>
+template <int KV, bool QBF16, bool FOLD, int DEPTH, bool ROPE = false>
 static hipError_t launch_decode_t(const DecodeParams& p, int num_tiles, int waves,
                                   hipStream_t s) {
-  const size_t lds = (size_t)Stage<KV>::lds_bytes(waves);
+  constexpr int rope_lds = ROPE ? kRopeLds : 0;
+  const size_t lds = (size_t)Stage<KV>::lds_bytes(waves) + rope_lds;
   // dynamic LDS above 64 KiB must be allowed per kernel (once per process)
   static const hipError_t attr = [] {
-    const int max_lds = Stage<KV>::lds_bytes(kWavesPerTile);
+    const int max_lds = Stage<KV>::lds_bytes(kWavesPerTile) + rope_lds;
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, true, FOLD, DEPTH>),
+        reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, true, FOLD, DEPTH, ROPE>),
         hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
     if (e == hipSuccess)
       e = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, false, FOLD, DEPTH>),
+          reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, false, FOLD, DEPTH, ROPE>),
           hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
     return e;
   }();
   if (attr != hipSuccess) return attr;
   if (p.ps_shift >= 0)
-    hipLaunchKernelGGL((decode_kernel<KV, QBF16, true, FOLD, DEPTH>), dim3(num_tiles),
+    hipLaunchKernelGGL((decode_kernel<KV, QBF16, true, FOLD, DEPTH, ROPE>), dim3(num_tiles),
                        dim3(64 * waves), lds, s, p);
   else
-    hipLaunchKernelGGL((decode_kernel<KV, QBF16, false, FOLD, DEPTH>), dim3(num_tiles),
+    hipLaunchKernelGGL((decode_kernel<KV, QBF16, false, FOLD, DEPTH, ROPE>), dim3(num_tiles),
                        dim3(64 * waves), lds, s, p);
   return hipGetLastError();
 }
@@ -690,6 +819,7 @@ template <int KV, bool QBF16>
 static hipError_t launch_decode_f(const DecodeParams& p, int num_tiles, int waves, bool fold,
                                   hipStream_t s) {
   if (num_tiles <= 0) return hipSuccess;
+  if (p.rope_table) return launch_decode_t<KV, QBF16, false, 1, true>(p, num_tiles, waves, s);
   const bool deep = fold && waves <= 4 && getenv_depth() != 1;
   if (fold)
     return deep ? launch_decode_t<KV, QBF16, true, 2>(p, num_tiles, waves, s)

@@ -42,7 +42,13 @@ static_assert(sizeof(Tile) == 32, "tile is 32 bytes");
 // n_states <= 1 means the producing tile writes the final output.
 struct ReqInfo {
   int32_t slot_base, n_states;
+  int32_t kv_len, pad;   // own tokens (the RoPE query position is kv_len - 1)
 };
+static_assert(sizeof(ReqInfo) == 16, "request info is 16 bytes");
+
+// RoPE table: for distance d < rows and frequency i < kHeadDim / 2, the
+// fp32 pair (cos, sin) of d / scale * theta^(-2 i / kHeadDim).
+constexpr int kRopeRowBytes = kHeadDim / 2 * 8;   // 512
 
 // One merge work item: request r's states slot_base + c * Hkv + h,
 // c < n_states (16 bytes, read with one load).
@@ -58,6 +64,7 @@ struct WorkspaceLayout {
   size_t qo_indptr_off;    // int32[num_groups + 1] (cascade only)
   size_t partial_o_off;    // float[num_partials][G][D]
   size_t partial_lse_off;  // float[num_partials][G]   (log2 domain)
+  size_t rope_off;         // uint32[rope_rows][kHeadDim / 2] (RoPE plans)
   size_t total;
 };
 
@@ -70,6 +77,9 @@ struct HostPlan {
   int32_t chunk_tokens, prefix_chunk_tokens, heads_per_tile, prefix_waves;
   int64_t num_tiles, num_prefix_tiles, num_partials, num_merge_units;
   int64_t num_folded;   // requests whose decode tile folds in their prefix states
+  int32_t rope;         // FI_POS_ROPE_LLAMA or 0
+  int32_t rope_rows;    // positions in the RoPE table (longest request)
+  float rope_theta, rope_scale;
   Tile* tiles;          // num_tiles + num_prefix_tiles entries
   ReqInfo* req_info;    // batch entries
   MergeUnit* merge_units;  // num_merge_units entries
@@ -90,6 +100,8 @@ struct PlanInput {
   const int32_t* p_last;
   int32_t chunk_tokens;
   int32_t num_cus;
+  int32_t pos_encoding;
+  float rope_theta, rope_scale;
 };
 int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen);
 void plan_free(HostPlan* p);
@@ -114,6 +126,9 @@ struct DecodeParams {
   int32_t num_tiles;
   // prefix tiles only: first request of each group, device [groups+1]
   const int32_t* qo_indptr;
+  // RoPE plans: the (cos, sin) table, rope_rows x kHeadDim / 2 fp32 pairs
+  const void* rope_table;
+  int32_t rope_rows;
 };
 
 struct MergeParams {

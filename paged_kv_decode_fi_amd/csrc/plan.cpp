@@ -108,6 +108,15 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
     }
   }
   const int num_cus = in.num_cus > 0 ? in.num_cus : 256;
+  if (in.pos_encoding != 0 && in.pos_encoding != 1)
+    PLAN_FAIL(1, "pos_encoding must be FI_POS_NONE or FI_POS_ROPE_LLAMA (got %d)",
+              in.pos_encoding);
+  const bool rope = in.pos_encoding == 1;
+  if (rope && NG > 0)
+    PLAN_FAIL(2, "RoPE with a cascade level is not built (plain decode only)");
+  if (rope && (!(in.rope_theta == in.rope_theta) || !(in.rope_scale == in.rope_scale) ||
+               in.rope_theta > 1e30f || in.rope_scale > 1e30f))
+    PLAN_FAIL(1, "rope_theta and rope_scale must be finite");
 
   // ---- decode chunk length
   // heads per tile: the largest of FI_HEADS_PER_TILE (default 8), 4, 2, 1
@@ -223,6 +232,8 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
     folded[r] = fold_ok && np > 0 && n_dchunks[r] == 1;
     out->req_info[r].n_states = (int32_t)ns;
     out->req_info[r].slot_base = -1;
+    out->req_info[r].kv_len = (int32_t)lens[r];
+    out->req_info[r].pad = 0;
     if (ns >= 2) {
       out->req_info[r].slot_base = (int32_t)slots;
       slots += (folded[r] ? np : ns) * Hkv;
@@ -326,6 +337,13 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   off = align256(off + sizeof(float) * (size_t)slots * G * kHeadDim);
   L.partial_lse_off = off;
   off = align256(off + sizeof(float) * (size_t)slots * G);
+  out->rope = rope ? 1 : 0;
+  out->rope_theta = in.rope_theta > 0.f ? in.rope_theta : 1e4f;
+  out->rope_scale = in.rope_scale > 0.f ? in.rope_scale : 1.f;
+  // distances 0 .. Lmax - 1, and at least the 16 rows every tile stages
+  out->rope_rows = rope ? (int32_t)std::max<int64_t>(Lmax, kChunkAlign) : 0;
+  L.rope_off = off;
+  off = align256(off + (size_t)kRopeRowBytes * (size_t)out->rope_rows);
   L.total = off;
   return 0;
 }

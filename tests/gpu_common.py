@@ -51,7 +51,8 @@ class Dev:
             self.p_last = to_dev(w.prefix_last_page_len)
 
 
-def make_plan(w, chunk_tokens=0, cascade=None):
+def make_plan(w, chunk_tokens=0, cascade=None, rope=None):
+    """rope = None or (theta, scale): a plan with LLaMA-style RoPE."""
     import paged_kv_decode_fi_amd as fi
     cascade = (w.prefix_kv_indptr is not None) if cascade is None else cascade
     prefix = ((w.prefix_qo_indptr, w.prefix_kv_indptr, w.prefix_last_page_len)
@@ -59,14 +60,17 @@ def make_plan(w, chunk_tokens=0, cascade=None):
     return fi.Plan(w.kv_indptr, w.last_page_len, num_qo_heads=w.num_qo_heads,
                    num_kv_heads=w.num_kv_heads, page_size=w.page_size,
                    head_dim=w.head_dim, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
-                   prefix=prefix, chunk_tokens=chunk_tokens)
+                   prefix=prefix, chunk_tokens=chunk_tokens,
+                   pos_encoding="none" if rope is None else "rope_llama",
+                   rope_theta=0.0 if rope is None else rope[0],
+                   rope_scale=0.0 if rope is None else rope[1])
 
 
-def run_gpu(w, d=None, plan=None, chunk_tokens=0):
+def run_gpu(w, d=None, plan=None, chunk_tokens=0, rope=None):
     """Runs the HIP path; returns (o float64 numpy, lse float64 numpy, plan)."""
     torch = torch_mod()
     d = d or Dev(w)
-    plan = plan or make_plan(w, chunk_tokens)
+    plan = plan or make_plan(w, chunk_tokens, rope=rope)
     if plan.cascade:
         o, lse = plan.cascade_run(d.q, d.k, d.v, d.p_indptr, d.p_indices, d.p_last,
                                   d.indptr, d.indices, d.last, d.k_scale, d.v_scale,
@@ -78,9 +82,9 @@ def run_gpu(w, d=None, plan=None, chunk_tokens=0):
     return o.float().cpu().double().numpy(), lse.cpu().double().numpy(), plan
 
 
-def run_oracle(w, unit_mask=None):
+def run_oracle(w, unit_mask=None, rope=None):
     import oracle
-    kw = dict(num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
+    kw = dict(rope=rope, num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
               head_dim=w.head_dim, page_size=w.page_size, q_dtype=w.q_dtype,
               kv_dtype=w.kv_dtype, sm_scale=w.sm_scale, k_scale=w.k_scale,
               v_scale=w.v_scale, unit_mask=unit_mask)

@@ -32,13 +32,15 @@ def test_header_symbols_are_exported(fi):
 
 def _problem(fi, indptr, last, **kw):
     args = dict(num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
-                q_dtype="f16", kv_dtype="f16", prefix=None, chunk=0)
+                q_dtype="f16", kv_dtype="f16", prefix=None, chunk=0,
+                pos_encoding="none", rope_theta=0.0, rope_scale=0.0)
     args.update(kw)
     indptr = np.asarray(indptr, np.int32)
     last = np.asarray(last, np.int32)
     return fi._problem(len(indptr) - 1, args["num_qo_heads"], args["num_kv_heads"],
                        args["head_dim"], args["page_size"], args["q_dtype"],
-                       args["kv_dtype"], indptr, last, args["prefix"], args["chunk"])
+                       args["kv_dtype"], indptr, last, args["prefix"], args["chunk"],
+                       args["pos_encoding"], args["rope_theta"], args["rope_scale"])
 
 
 def _status(fi, indptr, last, **kw):
@@ -63,6 +65,46 @@ def test_host_validation_errors(fi):
     assert _status(fi, [0, 2, 5], [3, 16], chunk=40) == 1       # not a step multiple
     msg = fi.lib.fi_last_error().decode()
     assert "chunk_tokens" in msg
+
+
+def _workspace(fi, indptr, last, **kw):
+    pr, keep = _problem(fi, indptr, last, **kw)
+    need = ctypes.c_size_t(0)
+    st = fi.lib.fi_plan(ctypes.byref(pr), 256, None, 0, ctypes.byref(need), None, None)
+    return st, need.value
+
+
+def test_rope_plan_rules(fi):
+    """RoPE plans: the mode is validated, a cascade level is refused as not
+    built, non-finite parameters are refused, and the workspace grows by one
+    (cos, sin) table row of 64 fp32 pairs per distance 0 .. longest - 1 (at
+    least 16 rows: every tile stages rows 0..15)."""
+    indptr, last = [0, 2, 5], [3, 16]           # lengths 19 and 48
+    assert _status(fi, indptr, last, pos_encoding="rope_llama") == 0
+    pr, keep = _problem(fi, indptr, last)
+    pr.pos_encoding = 2
+    n = ctypes.c_int64(0)
+    assert fi.lib.fi_debug_plan_tiles(ctypes.byref(pr), 256, None, 0, ctypes.byref(n)) == 1
+    assert "pos_encoding" in fi.lib.fi_last_error().decode()
+    prefix = (np.array([0, 2], np.int32), np.array([0, 1], np.int32),
+              np.array([16], np.int32))
+    assert _status(fi, indptr, last, pos_encoding="rope_llama", prefix=prefix) == 2
+    assert "RoPE" in fi.lib.fi_last_error().decode()
+    assert _status(fi, indptr, last, pos_encoding="rope_llama", rope_theta=float("nan")) == 1
+    assert _status(fi, indptr, last, pos_encoding="rope_llama", rope_scale=float("inf")) == 1
+    st0, ws0 = _workspace(fi, indptr, last)
+    st1, ws1 = _workspace(fi, indptr, last, pos_encoding="rope_llama")
+    assert st0 == 0 and st1 == 0
+    assert 48 * 512 <= ws1 - ws0 <= 48 * 512 + 256
+    st0, ws0 = _workspace(fi, [0, 1], [3])
+    st1, ws1 = _workspace(fi, [0, 1], [3], pos_encoding="rope_llama")
+    assert st0 == 0 and st1 == 0 and 16 * 512 <= ws1 - ws0 <= 16 * 512 + 256
+    # the work list does not depend on the position encoding
+    a = fi.debug_plan_tiles(np.array(indptr), np.array(last), num_qo_heads=32,
+                            num_kv_heads=8, page_size=16)
+    b = fi.debug_plan_tiles(np.array(indptr), np.array(last), num_qo_heads=32,
+                            num_kv_heads=8, page_size=16, pos_encoding="rope_llama")
+    assert np.array_equal(a, b)
 
 
 def test_run_calls_reject_bad_arguments_before_touching_the_device(fi):

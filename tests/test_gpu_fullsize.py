@@ -50,11 +50,11 @@ def _sample_units(w, n_random, seed):
     return flat
 
 
-def _run_nan_filled(w):
+def _run_nan_filled(w, rope=None):
     """The benchmark's launch: default plan, outputs pre-filled with NaN."""
     import torch
     d = C.Dev(w)
-    plan = C.make_plan(w)
+    plan = C.make_plan(w, rope=rope)
     o = torch.full((w.batch, w.num_qo_heads, w.head_dim), float("nan"),
                    dtype=C.qdtype(w), device="cuda")
     lse = torch.full((w.batch, w.num_qo_heads), float("nan"), dtype=torch.float32,
@@ -77,17 +77,18 @@ def _every_row_written(w, o, lse):
     assert np.all(np.isfinite(lse)), "an lse entry was not written (or is not finite)"
 
 
-def _check(w, name, n_random=24):
-    o, lse, plan = _run_nan_filled(w)
+def _check(w, name, n_random=24, rope=None):
+    o, lse, plan = _run_nan_filled(w, rope)
     st = plan.stats
     print(f"{w.name}: tiles {st['num_tiles']} prefix tiles {st['num_prefix_tiles']} "
           f"merge units {st['num_merge_units']} chunk {st['chunk_tokens']}", flush=True)
     _every_row_written(w, o, lse)
     mask = _sample_units(w, n_random, seed=zlib.crc32(name.encode()))
-    ro, rl = C.run_oracle(w, unit_mask=mask)
+    ro, rl = C.run_oracle(w, unit_mask=mask, rope=rope)
     rows = C.rows_of_units(w, mask)
     C.assert_parity(w, o, lse, ro, rl, rows=rows,
-                    label=f"{w.name} full size, {int(mask.sum())} sampled units")
+                    label=f"{w.name} full size, {int(mask.sum())} sampled units"
+                          + ("" if rope is None else f", RoPE {rope}"))
     plan.destroy()
     return o, lse
 
@@ -103,6 +104,18 @@ def test_full_size_sampled_parity(fi_lib, name):
 def test_full_size_long_fp8_sampled_parity(fi_lib, ps):
     ws = _workload("long32_fp8")
     _check(ws[ps], f"long32_fp8_ps{ps}", n_random=8)
+
+
+@pytest.mark.parametrize("name", ["batch64_gqa4", "skewed128"])
+def test_full_size_rope_sampled_parity(fi_lib, name):
+    """The same launches with LLaMA-style RoPE on the fly (skewed128 reaches
+    position 32767 and splits those requests over many tiles)."""
+    _check(_workload(name), name + "_rope", n_random=12, rope=(1e4, 1.0))
+
+
+def test_full_size_rope_fp8_sampled_parity(fi_lib):
+    _check(_workload("long32_fp8")[16], "long32_fp8_ps16_rope", n_random=4,
+           rope=(5e5, 1.0))
 
 
 def test_full_size_split_rows_cover_every_chunk(fi_lib):
