@@ -131,10 +131,10 @@ __device__ __forceinline__ void fold_states(const float* __restrict__ partial_o,
 // back by its distance d = p - t >= 0 from the query.
 //
 // Table (fp32, built on the device in fp64): row d, frequency i holds
-// (cos, sin) of d / scale * theta^(-2 i / D).  A step reads one row, d0 =
-// p - (first token of the step); key n of the step is at distance d0 - n,
-// whose (cos, sin) follow from rows d0 and n by the angle-difference
-// identities (rows 0..15 stay in LDS for the whole tile).
+// (cos, sin) of d / scale * theta^(-2 i / D).  A step needs the rows of
+// distances d0 - n, n < 16 (d0 = p - first token of the step); the
+// workgroup builds them in LDS from row d0 and rows 0..15 by the
+// angle-difference identities, each (n, i) once.
 template <bool BF16>
 __device__ __forceinline__ float lo16(uint32_t w) {
   if constexpr (BF16) return __builtin_bit_cast(float, w << 16);
@@ -146,34 +146,47 @@ __device__ __forceinline__ float hi16(uint32_t w) {
   else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
-// Turns 8 + 8 partner elements of one key (a: dims f..f+7, b: dims
-// f+64..f+71, 16-bit) back by the angle of distance d0 - n, in fp32, and
-// writes the result as a 16-bit high part plus a 16-bit residual, so that
-// two MFMAs against the same q carry the rotated key to about fp32 accuracy.
-// base / off: the (cos, sin) pairs of frequencies f..f+7 at distances d0 and n.
+// (x0 - h.lo, x1 - h.hi) rounded to the 16-bit type, h = the pair (x0, x1)
+// already rounded.  f16: one mixed-precision FMA per half (the f16 operand
+// is widened inside the instruction, the result rounded to f16 in place).
 template <bool BF16>
-__device__ __forceinline__ void rope_key8(u32x4 a, u32x4 b, const float4* base,
-                                          const float4* off, u32x4& ahi, u32x4& alo,
-                                          u32x4& bhi, u32x4& blo) {
+__device__ __forceinline__ uint32_t residual2(uint32_t h, float x0, float x1) {
+  if constexpr (BF16) {
+    return pack2<true>(x0 - lo16<true>(h), x1 - hi16<true>(h));
+  } else {
+    uint32_t r;
+    asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, -%1, 1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=&v"(r)
+        : "v"(h), "v"(x0), "v"(x1));
+    return r;
+  }
+}
+
+// Turns 8 + 8 partner elements of one key (a: dims f..f+7, b: dims
+// f+64..f+71, 16-bit) back by its distance, (cos, sin) of frequencies
+// f..f+7 in cs, in fp32; writes the result as a 16-bit high part plus a
+// 16-bit residual, so that two MFMAs against the same q carry the rotated
+// key to about fp32 accuracy.
+template <bool BF16>
+__device__ __forceinline__ void rope_key8(u32x4 a, u32x4 b, const float4* cs, u32x4& ahi,
+                                          u32x4& alo, u32x4& bhi, u32x4& blo) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const float4 bs = base[k], of = off[k];   // frequencies f + 2k, f + 2k + 1
+    const float4 t = cs[k];   // frequencies f + 2k, f + 2k + 1
     float ra[2], rb[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const float cb = e ? bs.z : bs.x, sb = e ? bs.w : bs.y;
-      const float co = e ? of.z : of.x, so = e ? of.w : of.y;
-      const float c = __builtin_fmaf(cb, co, sb * so);    // cos((d0 - n) w)
-      const float sn = __builtin_fmaf(sb, co, -cb * so);  // sin((d0 - n) w)
+      const float c = e ? t.z : t.x, sn = e ? t.w : t.y;
       const float x = e ? hi16<BF16>(a[k]) : lo16<BF16>(a[k]);
       const float y = e ? hi16<BF16>(b[k]) : lo16<BF16>(b[k]);
-      ra[e] = __builtin_fmaf(x, c, y * sn);
-      rb[e] = __builtin_fmaf(y, c, -x * sn);
+      ra[e] = __builtin_fmaf(x, c, __builtin_fmaf(y, sn, 0.f));
+      rb[e] = __builtin_fmaf(y, c, __builtin_fmaf(-x, sn, 0.f));
     }
     ahi[k] = pack2<BF16>(ra[0], ra[1]);
     bhi[k] = pack2<BF16>(rb[0], rb[1]);
-    alo[k] = pack2<BF16>(ra[0] - lo16<BF16>(ahi[k]), ra[1] - hi16<BF16>(ahi[k]));
-    blo[k] = pack2<BF16>(rb[0] - lo16<BF16>(bhi[k]), rb[1] - hi16<BF16>(bhi[k]));
+    alo[k] = residual2<BF16>(ahi[k], ra[0], ra[1]);
+    blo[k] = residual2<BF16>(bhi[k], rb[0], rb[1]);
   }
 }
 
@@ -199,13 +212,13 @@ hipError_t launch_rope_table(void* table, int rows, float theta, float scale, hi
 // separate instance: the fold costs registers the plain kernel keeps free).
 // DEPTH: steps of K/V loads in flight per workgroup.  ROPE: every key is
 // turned by its distance from the query (LLaMA-style RoPE, relative form)
-// before the score MFMAs; the LDS after K and V holds the step's table row
-// and table rows 0..15.
-constexpr int kRopeLdsStride = kRopeRowBytes + 16;   // rows 0..15, bank-conflict-free
-constexpr int kRopeLds = kRopeRowBytes + kStep * kRopeLdsStride;
+// before the score MFMAs; the LDS after K and V holds the step's 16 rows
+// (padded: conflict-free reads of one row per lane) and table rows 0..15.
+constexpr int kRopeLdsStride = kRopeRowBytes + 16;
+constexpr int kRopeLds = kStep * kRopeLdsStride + kStep * kRopeRowBytes;
 template <int KV, bool QBF16, bool PS_POW2, bool FOLD, int DEPTH, bool ROPE>
 __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams p) {
-  static_assert(!ROPE || (DEPTH == 1 && !FOLD), "RoPE runs with one step in flight, no fold");
+  static_assert(!ROPE || !FOLD, "RoPE plans have no cascade level to fold");
   using S = Stage<KV>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int W = blockDim.x >> 6;                  // waves = kv heads of the tile
@@ -225,7 +238,8 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   const int KS = S::k_stride(W), VS = S::v_stride(W);
   uint8_t* klds = lds;
   uint8_t* vlds = lds + kStep * KS;
-  uint8_t* rlds = lds + kStep * (KS + VS);   // RoPE: step row, then rows 0..15
+  uint8_t* rlds = lds + kStep * (KS + VS);   // RoPE: the step's rows
+  const float2* r16 = reinterpret_cast<const float2*>(rlds + kStep * kRopeLdsStride);
 
   // q of this wave's head group as the B operand of the score MFMAs
   u32x4 qop[4];
@@ -263,31 +277,36 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   // DEPTH register sets of step loads (kr/vr[d]); set d holds steps d, d +
   // DEPTH, ...
   u32x4 kr[DEPTH][S::LOADS], vr[DEPTH][S::LOADS];
-  // RoPE: table row d0 of a step (32 vectors of 16 B) goes through the
-  // registers of threads 0..31 like K and V; rows 0..15 are staged once
-  const u32x4* rtab = reinterpret_cast<const u32x4*>(p.rope_table);
-  u32x4 rr;
-  auto issue_rope = [&](int step) {
-    if constexpr (ROPE)
-      if (tid < kRopeRowBytes / 16) rr = rtab[(int64_t)(qpos - t0 - kStep * step) * 32 + tid];
+  // RoPE: thread (wave w, lane i) builds entries (n, i) of the step's rows
+  // for n = w, w + W, ...: it holds (cos, sin) at distance d0 for frequency
+  // i (2 registers per step in flight) and reads rows n from LDS
+  const float2* rtab = reinterpret_cast<const float2*>(p.rope_table);
+  float2 rr[DEPTH];
+  auto issue_rope = [&](int step, float2& rq) {
+    if constexpr (ROPE) rq = rtab[(int64_t)(qpos - t0 - kStep * step) * 64 + lane];
   };
-  auto stage_rope = [&]() {
-    if constexpr (ROPE)
-      if (tid < kRopeRowBytes / 16) reinterpret_cast<u32x4*>(rlds)[tid] = rr;
+  auto stage_rope = [&](const float2& rq) {
+    if constexpr (ROPE) {
+      for (int nn = wave; nn < kStep; nn += W) {
+        const float2 o = r16[nn * 64 + lane];
+        const float c = __builtin_fmaf(rq.x, o.x, rq.y * o.y);    // cos((d0 - n) w)
+        const float sn = __builtin_fmaf(rq.y, o.x, -rq.x * o.y);  // sin((d0 - n) w)
+        *reinterpret_cast<float2*>(rlds + nn * kRopeLdsStride + 8 * lane) = float2{c, sn};
+      }
+    }
   };
   if constexpr (ROPE) {
-    constexpr int kVec = kStep * kRopeRowBytes / 16;   // 512 vectors of rows 0..15
+    constexpr int kVec = kStep * kRopeRowBytes / 16;   // rows 0..15: 512 vectors
+    const u32x4* src = reinterpret_cast<const u32x4*>(p.rope_table);
+    u32x4* dst = reinterpret_cast<u32x4*>(rlds + kStep * kRopeLdsStride);
     u32x4 o16[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (tid + u * 64 * W < kVec) o16[u] = rtab[tid + u * 64 * W];
+      if (tid + u * 64 * W < kVec) o16[u] = src[tid + u * 64 * W];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int idx = tid + u * 64 * W;
-      if (idx < kVec)
-        *reinterpret_cast<u32x4*>(rlds + kRopeRowBytes + (idx >> 5) * kRopeLdsStride +
-                                  16 * (idx & 31)) = o16[u];
-    }
+    for (int u = 0; u < 8; ++u)
+      if (tid + u * 64 * W < kVec) dst[tid + u * 64 * W] = o16[u];
+    __syncthreads();   // rows 0..15 are read across waves by the first stage
   }
   auto issue = [&](int step, int pg, u32x4 (&kq)[S::LOADS], u32x4 (&vq)[S::LOADS]) {
     const int tb = t0 + kStep * step;
@@ -346,11 +365,10 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
       // dims of kop(j) (frequencies 32 j + 8 g ..) pair with kop(j + 2)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const float4* base = reinterpret_cast<const float4*>(rlds + 256 * j + 64 * g);
-        const float4* off = reinterpret_cast<const float4*>(
-            rlds + kRopeRowBytes + n * kRopeLdsStride + 256 * j + 64 * g);
+        const float4* cs =
+            reinterpret_cast<const float4*>(rlds + n * kRopeLdsStride + 256 * j + 64 * g);
         u32x4 ahi, alo, bhi, blo;
-        rope_key8<QBF16>(kop_of(j), kop_of(j + 2), base, off, ahi, alo, bhi, blo);
+        rope_key8<QBF16>(kop_of(j), kop_of(j + 2), cs, ahi, alo, bhi, blo);
         sc = mma16x16x32<QBF16>(ahi, qop[j], sc);
         sc = mma16x16x32<QBF16>(alo, qop[j], sc);
         sc = mma16x16x32<QBF16>(bhi, qop[j + 2], sc);
@@ -400,15 +418,15 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
     if (nsteps > 0) {
       int pg1 = nsteps > 1 ? load_page(1) : 0;
       issue(0, load_page(0), kr[0], vr[0]);
-      issue_rope(0);
+      issue_rope(0, rr[0]);
       for (int step = 0; step < nsteps; ++step) {
         const int pg2 = step + 2 < nsteps ? load_page(step + 2) : 0;
         stage(kr[0], vr[0]);
-        stage_rope();
+        stage_rope(rr[0]);
         __syncthreads();
         if (step + 1 < nsteps) {
           issue(step + 1, pg1, kr[0], vr[0]);
-          issue_rope(step + 1);
+          issue_rope(step + 1, rr[0]);
         }
         compute(step);
         __syncthreads();
@@ -418,21 +436,30 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   } else {
     if (nsteps > 0) {
       issue(0, load_page(0), kr[0], vr[0]);
-      if (nsteps > 1) issue(1, load_page(1), kr[1], vr[1]);
+      issue_rope(0, rr[0]);
+      if (nsteps > 1) {
+        issue(1, load_page(1), kr[1], vr[1]);
+        issue_rope(1, rr[DEPTH - 1]);
+      }
       int pga = nsteps > 2 ? load_page(2) : 0;   // page of the next even step to issue
       int pgb = nsteps > 3 ? load_page(3) : 0;   // ... odd step
       // one body per register set: set d stages step s and refills with s + 2
-      auto body = [&](int step, int& pgn, u32x4 (&kq)[S::LOADS], u32x4 (&vq)[S::LOADS]) {
+      auto body = [&](int step, int& pgn, u32x4 (&kq)[S::LOADS], u32x4 (&vq)[S::LOADS],
+                      float2& rq) {
         stage(kq, vq);
+        stage_rope(rq);
         __syncthreads();
-        if (step + 2 < nsteps) issue(step + 2, pgn, kq, vq);
+        if (step + 2 < nsteps) {
+          issue(step + 2, pgn, kq, vq);
+          issue_rope(step + 2, rq);
+        }
         pgn = step + 4 < nsteps ? load_page(step + 4) : 0;
         compute(step);
         __syncthreads();
       };
       for (int step = 0; step < nsteps; step += 2) {
-        body(step, pga, kr[0], vr[0]);
-        if (step + 1 < nsteps) body(step + 1, pgb, kr[1], vr[1]);
+        body(step, pga, kr[0], vr[0], rr[0]);
+        if (step + 1 < nsteps) body(step + 1, pgb, kr[1], vr[1], rr[DEPTH - 1]);
       }
     }
   }
@@ -819,7 +846,9 @@ template <int KV, bool QBF16>
 static hipError_t launch_decode_f(const DecodeParams& p, int num_tiles, int waves, bool fold,
                                   hipStream_t s) {
   if (num_tiles <= 0) return hipSuccess;
-  if (p.rope_table) return launch_decode_t<KV, QBF16, false, 1, true>(p, num_tiles, waves, s);
+  if (p.rope_table)
+    return getenv_depth() == 1 ? launch_decode_t<KV, QBF16, false, 1, true>(p, num_tiles, waves, s)
+                               : launch_decode_t<KV, QBF16, false, 2, true>(p, num_tiles, waves, s);
   const bool deep = fold && waves <= 4 && getenv_depth() != 1;
   if (fold)
     return deep ? launch_decode_t<KV, QBF16, true, 2>(p, num_tiles, waves, s)

@@ -119,10 +119,13 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
     PLAN_FAIL(1, "rope_theta and rope_scale must be finite");
 
   // ---- decode chunk length
-  // heads per tile: the largest of FI_HEADS_PER_TILE (default 8), 4, 2, 1
+  // heads per tile: the largest of FI_HEADS_PER_TILE (default 8; 4 with
+  // RoPE, whose kernel holds 3 waves per SIMD: three 4-wave workgroups fill
+  // a CU where one 8-wave workgroup would leave a third of it idle), 4, 2, 1
   // dividing Hkv
+  const int hpt_default = rope ? kWavesPerTile / 2 : kWavesPerTile;
   int hpt = (int)std::min<int64_t>(kWavesPerTile, std::max<int64_t>(1, env_int("FI_HEADS_PER_TILE",
-                                                                              kWavesPerTile)));
+                                                                              hpt_default)));
   while (hpt & (hpt - 1)) hpt &= hpt - 1;
   while (Hkv % hpt) hpt >>= 1;
   const int64_t waves_per_cu = env_int("FI_WAVES_PER_CU", 16);

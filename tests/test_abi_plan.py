@@ -99,12 +99,17 @@ def test_rope_plan_rules(fi):
     st0, ws0 = _workspace(fi, [0, 1], [3])
     st1, ws1 = _workspace(fi, [0, 1], [3], pos_encoding="rope_llama")
     assert st0 == 0 and st1 == 0 and 16 * 512 <= ws1 - ws0 <= 16 * 512 + 256
-    # the work list does not depend on the position encoding
-    a = fi.debug_plan_tiles(np.array(indptr), np.array(last), num_qo_heads=32,
-                            num_kv_heads=8, page_size=16)
-    b = fi.debug_plan_tiles(np.array(indptr), np.array(last), num_qo_heads=32,
-                            num_kv_heads=8, page_size=16, pos_encoding="rope_llama")
-    assert np.array_equal(a, b)
+    # a large batch: RoPE tiles span 4 kv heads (8 without), and both work
+    # lists cover every (request, kv head, token) once
+    lens = np.full(64, 2048)
+    ip = np.concatenate([[0], np.cumsum(lens // 16)]).astype(np.int32)
+    la = np.full(64, 16, np.int32)
+    for enc, want in (("none", 8), ("rope_llama", 4)):
+        t = fi.debug_plan_tiles(ip, la, num_qo_heads=32, num_kv_heads=8, page_size=16,
+                                pos_encoding=enc)
+        hpt = _heads_per_tile(t, 8)
+        assert hpt == want, (enc, hpt)
+        _check_cover(t, lens, 8, hpt)
 
 
 def test_run_calls_reject_bad_arguments_before_touching_the_device(fi):
