@@ -73,6 +73,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_cascade.restype = I
         L.oracle_cascade.argtypes = [I, I, I, I, I, I, I, P, P, P, I, P, P, P, P,
                                      P, P, P, P, P, D, P, P, P, I, I, D, D]
+        L.oracle_append.restype = I
+        L.oracle_append.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P,
+                                    D, I, P, P, P, I, I, D, D]
         L.oracle_rope_rotate.restype = None
         L.oracle_rope_rotate.argtypes = [P, I, D, D, D, P]
         L.oracle_merge.restype = I
@@ -167,6 +170,36 @@ def decode(q, k_pages, v_pages, kv_indptr, kv_indices, last_page_len, *,
                              threads or default_threads(), *_rope_args(rope))
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments")
+    return o, lse
+
+
+def append(q, k_pages, v_pages, qo_indptr, kv_indptr, kv_indices, last_page_len, *,
+           num_qo_heads, num_kv_heads, head_dim, page_size, q_dtype, kv_dtype,
+           sm_scale, causal=True, k_scale=None, v_scale=None, unit_mask=None,
+           threads=None, rope=None):
+    """fp64 batch append attention.  Request r's query tokens
+    qo_indptr[r] .. qo_indptr[r+1]-1 are the last ones of its keys: token i of
+    n sits at position L - n + i and (causal) attends keys 0 .. L - n + i.
+    q is [total_q, Hq, D] storage; returns (o [total_q, Hq, D], lse
+    [total_q, Hq]) fp64.  unit_mask selects (request, kv head) items."""
+    indptr = _c(kv_indptr, np.int32)
+    qo = _c(qo_indptr, np.int32)
+    B = len(indptr) - 1
+    nq = int(qo[-1]) if len(qo) else 0
+    o = np.zeros((nq, num_qo_heads, head_dim), np.float64)
+    lse = np.full((nq, num_qo_heads), np.nan, np.float64)
+    q, k_pages, v_pages = _c(q), _c(k_pages), _c(v_pages)
+    indices, last = _c(kv_indices, np.int32), _c(last_page_len, np.int32)
+    ks, vs = _c(k_scale, np.float32), _c(v_scale, np.float32)
+    um = _c(unit_mask, np.uint8)
+    rc = lib().oracle_append(B, num_qo_heads, num_kv_heads, head_dim, page_size,
+                             DTYPE_CODE[q_dtype], DTYPE_CODE[kv_dtype], _ptr(q),
+                             _ptr(k_pages), _ptr(v_pages), _ptr(qo), _ptr(indptr),
+                             _ptr(indices), _ptr(last), _ptr(ks), _ptr(vs),
+                             float(sm_scale), int(bool(causal)), _ptr(um), _ptr(o),
+                             _ptr(lse), threads or default_threads(), *_rope_args(rope))
+    if rc != 0:
+        raise ValueError("oracle_append rejected its arguments")
     return o, lse
 
 

@@ -48,3 +48,30 @@ def ref_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float):
         o[j] = (w[:, None] * v[:, h, :]).sum(0) / w.sum()
         lse[j] = np.log(w.sum())
     return o, lse
+
+
+def ref_dense_append(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float,
+                     causal: bool = True):
+    """Append attention over a dense K/V: q [n, Hq, D] are the last n of the
+    L tokens of k/v [L, Hkv, D] (float64).  With the causal mask, query i
+    sees keys 0 .. L - n + i (a lower-triangular mask aligned to the bottom
+    right of the n x L score matrix).  Returns (o [n, Hq, D], lse [n, Hq]).
+    No max subtraction: callers keep |x| small."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    n, Hq, D = q.shape
+    L, Hkv, _ = k.shape
+    G = Hq // Hkv
+    allowed = np.ones((n, L), bool)
+    if causal:
+        allowed = np.tril(allowed, k=L - n)
+    o = np.zeros((n, Hq, D))
+    lse = np.full((n, Hq), -np.inf)
+    for j in range(Hq):
+        h = j // G
+        x = sm_scale * (q[:, j, :] @ k[:, h, :].T)        # [n, L]
+        w = np.where(allowed, np.exp(x), 0.0)
+        o[:, j] = (w @ v[:, h, :]) / w.sum(1, keepdims=True)
+        lse[:, j] = np.log(w.sum(1))
+    return o, lse

@@ -41,6 +41,14 @@
  *     (cascade: the group's prefix tokens, then the request's own) sits at
  *     position t, the query at position L - 1 (the token being decoded is
  *     the last one in the cache); V is not rotated.
+ *   - append attention (README example: single_prefill_with_kv_cache with
+ *     causal=True, where "the last 128 tokens in the KV-Cache are the new
+ *     tokens"; "check out ... batch decode/append/prefill"): request r has
+ *     n_r = qo_indptr[r+1] - qo_indptr[r] query tokens, which are the LAST
+ *     n_r of its L keys, so query i (0-based) sits at position L - n_r + i;
+ *     with the causal mask it attends keys 0 .. L - n_r + i, without it all
+ *     L keys.  n_r <= L is required.  Query rows are stored token-major
+ *     ([total_q][Hq][D]) and so are o and lse.
  */
 #include <math.h>
 #include <pthread.h>
@@ -170,9 +178,11 @@ typedef struct {
   double theta, scale;
 } rope_t;
 
+/* One query row over keys 0 .. L-1 of row_off; with RoPE the query sits at
+ * position qpos. */
 static void attend_row(const double* q, const int64_t* row_off, int64_t L,
                        const kv_src* src, double sm_scale, const rope_t* rope,
-                       double* x /*[L]*/, double* o, double* lse) {
+                       double qpos, double* x /*[L]*/, double* o, double* lse) {
   const int D = src->D;
   for (int d = 0; d < D; ++d) o[d] = 0.0;
   if (L == 0) {
@@ -181,7 +191,7 @@ static void attend_row(const double* q, const int64_t* row_off, int64_t L,
   }
   double qr[512], kr[512], kraw[512];   /* D <= 512 */
   if (rope->on)
-    oracle_rope_rotate(q, D, (double)(L - 1), rope->theta, rope->scale, qr);
+    oracle_rope_rotate(q, D, qpos, rope->theta, rope->scale, qr);
   else
     for (int d = 0; d < D; ++d) qr[d] = q[d];
   double M = -INFINITY;
@@ -226,6 +236,9 @@ typedef struct {
   const float *k_scale, *v_scale;
   double sm_scale;
   rope_t rope;
+  /* append mode (app_qo_indptr != NULL): query tokens per request */
+  const int32_t* app_qo_indptr;
+  int causal;
   const uint8_t* unit_mask; /* [batch*Hkv] or NULL: 1 = compute this item */
   double* o;                /* [batch][Hq][D] */
   double* lse;              /* [batch][Hq] */
@@ -259,10 +272,25 @@ static void run_item(const job_t* J, int r, int h, int64_t* rows, double* x,
   kv_src src = {J->k_pages, J->v_pages, J->kv_dtype, D,
                 J->k_scale ? (double)J->k_scale[h] : 1.0,
                 J->v_scale ? (double)J->v_scale[h] : 1.0};
+  if (J->app_qo_indptr) {
+    /* append: query token i of the request at position L - n + i */
+    const int64_t q0 = J->app_qo_indptr[r], n = J->app_qo_indptr[r + 1] - q0;
+    for (int64_t i = 0; i < n; ++i) {
+      const int64_t pos = L - n + i;
+      const int64_t keys = J->causal ? pos + 1 : L;
+      for (int j = h * G; j < (h + 1) * G; ++j) {
+        int64_t qo = ((q0 + i) * J->Hq + j) * D;
+        for (int d = 0; d < D; ++d) qv[d] = load_elem(J->q, J->q_dtype, qo + d);
+        attend_row(qv, rows, keys, &src, J->sm_scale, &J->rope, (double)pos, x,
+                   J->o + qo, J->lse + (q0 + i) * J->Hq + j);
+      }
+    }
+    return;
+  }
   for (int j = h * G; j < (h + 1) * G; ++j) {
     int64_t qo = ((int64_t)r * J->Hq + j) * D;
     for (int d = 0; d < D; ++d) qv[d] = load_elem(J->q, J->q_dtype, qo + d);
-    attend_row(qv, rows, L, &src, J->sm_scale, &J->rope, x, J->o + qo,
+    attend_row(qv, rows, L, &src, J->sm_scale, &J->rope, (double)(L - 1), x, J->o + qo,
                J->lse + (int64_t)r * J->Hq + j);
   }
 }
@@ -293,6 +321,10 @@ static int run_job(job_t* J, int num_threads) {
   J->max_len = 0;
   for (int r = 0; r < J->batch; ++r) {
     int64_t L = request_len(J->indptr, J->last, r, J->ps);
+    if (J->app_qo_indptr) {
+      const int64_t n = (int64_t)J->app_qo_indptr[r + 1] - J->app_qo_indptr[r];
+      if (n < 0 || n > L) return -1;
+    }
     int g = J->n_groups > 0 ? group_of(J, r) : -1;
     if (g >= 0) L += request_len(J->p_indptr, J->p_last, g, J->ps);
     if (L > J->max_len) J->max_len = L;
@@ -357,6 +389,31 @@ int oracle_cascade(int batch, int num_qo_heads, int num_kv_heads, int head_dim,
   J.p_indptr = prefix_kv_indptr; J.p_indices = prefix_kv_indices;
   J.p_last = prefix_last_page_len;
   J.k_scale = k_scale; J.v_scale = v_scale; J.sm_scale = sm_scale;
+  J.unit_mask = unit_mask; J.o = o; J.lse = lse;
+  return run_job(&J, num_threads);
+}
+
+/* Append attention: request r's qo_indptr[r+1] - qo_indptr[r] query tokens
+ * are the last ones of its key list (see the readings at the top); o and lse
+ * are [total_q][Hq][D] and [total_q][Hq], rows in query-token order. */
+int oracle_append(int batch, int num_qo_heads, int num_kv_heads, int head_dim,
+                  int page_size, int q_dtype, int kv_dtype, const void* q,
+                  const void* k_pages, const void* v_pages, const int32_t* qo_indptr,
+                  const int32_t* kv_indptr, const int32_t* kv_indices,
+                  const int32_t* last_page_len, const float* k_scale,
+                  const float* v_scale, double sm_scale, int causal,
+                  const uint8_t* unit_mask, double* o, double* lse,
+                  int num_threads, int rope, double rope_theta, double rope_scale) {
+  if (!qo_indptr) return -1;
+  job_t J;
+  memset(&J, 0, sizeof(J));
+  J.rope.on = rope; J.rope.theta = rope_theta; J.rope.scale = rope_scale;
+  J.batch = batch; J.Hq = num_qo_heads; J.Hkv = num_kv_heads; J.D = head_dim;
+  J.ps = page_size; J.q_dtype = q_dtype; J.kv_dtype = kv_dtype;
+  J.q = q; J.k_pages = k_pages; J.v_pages = v_pages;
+  J.indptr = kv_indptr; J.indices = kv_indices; J.last = last_page_len;
+  J.k_scale = k_scale; J.v_scale = v_scale; J.sm_scale = sm_scale;
+  J.app_qo_indptr = qo_indptr; J.causal = causal != 0;
   J.unit_mask = unit_mask; J.o = o; J.lse = lse;
   return run_job(&J, num_threads);
 }

@@ -500,3 +500,140 @@ def test_rope_cascade_is_flat_over_concatenated_keys(oracle_lib):
     fpool, findptr, fidx, flast = paginate(flat_dense, ps, Hkv, D, np.random.default_rng(3))
     o_f, l_f = oracle_lib.decode(q, fpool, fpool, findptr, fidx, flast, **kw)
     assert np.array_equal(o_c, o_f) and np.array_equal(l_c, l_f)
+
+
+# ------------------------------------------------------------- append
+# FlashInfer README example: append attention = single_prefill_with_kv_cache
+# with causal=True where the last qo_len tokens of the KV cache are the new
+# tokens; the batch form takes qo_indptr over the requests' query tokens.
+
+def _append_problem(rng, lens, nq, Hq, Hkv, D, ps, scale=0.1):
+    ks = [rng.standard_normal((L, Hkv, D)) for L in lens]
+    vs = [rng.standard_normal((L, Hkv, D)) for L in lens]
+    qo = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    qf = rng.standard_normal((int(qo[-1]), Hq, D)) * scale
+    kp, indptr, idx, last = paginate([to_f16_bits(k) for k in ks], ps, Hkv, D,
+                                     np.random.default_rng(7))
+    vp, _, _, _ = paginate([to_f16_bits(v) for v in vs], ps, Hkv, D, np.random.default_rng(7))
+    return qf, ks, vs, qo, kp, vp, indptr, idx, last
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("ps", [1, 5, 16])
+def test_append_matches_dense_brute_force(oracle_lib, causal, ps):
+    """Against the NumPy brute force with an explicit bottom-right-aligned
+    lower-triangular mask (oracle/dense.py)."""
+    from oracle.dense import ref_dense_append
+    rng = np.random.default_rng(50 + ps)
+    Hq, Hkv, D = 4, 2, 16
+    lens, nq = [9, 20, 5, 33], [3, 20, 0, 7]
+    qf, ks, vs, qo, kp, vp, indptr, idx, last = _append_problem(rng, lens, nq, Hq, Hkv, D, ps)
+    sm = 0.41
+    o, lse = oracle_lib.append(to_f16_bits(qf), kp, vp, qo, indptr, idx, last,
+                               num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=ps,
+                               q_dtype="f16", kv_dtype="f16", sm_scale=sm, causal=causal)
+    for r in range(len(lens)):
+        a, b = qo[r], qo[r + 1]
+        if a == b:
+            continue
+        ro, rl = ref_dense_append(f16_values(qf[a:b]), f16_values(ks[r]), f16_values(vs[r]),
+                                  sm, causal=causal)
+        np.testing.assert_allclose(o[a:b], ro, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse[a:b], rl, rtol=1e-12, atol=1e-13)
+
+
+def test_append_closed_forms(oracle_lib):
+    """Causal prefill of a whole request (qo_len = kv_len): row 0 sees only
+    key 0, so o = v_0 and lse = sm_scale q.k_0 exactly; a one-token append
+    is plain decode, bit for bit; without the mask every row is plain
+    decode of that row over all keys, bit for bit."""
+    rng = np.random.default_rng(60)
+    Hq, Hkv, D, ps = 2, 1, 128, 4
+    lens = [6, 11]
+    qf, ks, vs, qo, kp, vp, indptr, idx, last = _append_problem(rng, lens, lens, Hq, Hkv, D, ps)
+    kw = dict(num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=ps, q_dtype="f16",
+              kv_dtype="f16", sm_scale=0.2)
+    qb = to_f16_bits(qf)
+    o, lse = oracle_lib.append(qb, kp, vp, qo, indptr, idx, last, **kw)
+    for r in range(2):
+        row0 = qo[r]
+        for j in range(Hq):
+            np.testing.assert_array_equal(o[row0, j], f16_values(vs[r][0, 0]))
+            x0 = 0.2 * float(np.dot(f16_values(qf[row0, j]), f16_values(ks[r][0, 0])))
+            assert abs(lse[row0, j] - x0) < 1e-12
+    # the last row of a causal prefill sees every key: plain decode
+    last_rows = qb[qo[1:] - 1]
+    od, ld = oracle_lib.decode(last_rows, kp, vp, indptr, idx, last, **kw)
+    assert np.array_equal(o[qo[1:] - 1], od) and np.array_equal(lse[qo[1:] - 1], ld)
+    # one-token append = decode
+    one = np.array([0, 1, 2], np.int32)
+    o1, l1 = oracle_lib.append(last_rows, kp, vp, one, indptr, idx, last, **kw)
+    assert np.array_equal(o1, od) and np.array_equal(l1, ld)
+    # non-causal: each row is decode of that row over all the request's keys
+    onc, lnc = oracle_lib.append(qb, kp, vp, qo, indptr, idx, last, causal=False, **kw)
+    for r in range(2):
+        rows = qb[qo[r]:qo[r + 1]]
+        sub_ip = np.repeat(indptr[r:r + 2][None], len(rows), 0)
+        for i in range(len(rows)):
+            od_i, ld_i = oracle_lib.decode(rows[i][None], kp, vp, sub_ip[i], idx, last[r:r + 1],
+                                           **kw)
+            assert np.array_equal(onc[qo[r] + i], od_i[0])
+            assert np.array_equal(lnc[qo[r] + i], ld_i[0])
+
+
+def test_append_causal_row_equals_decode_of_truncated_request(oracle_lib):
+    """Causal query i of n sits at position L - n + i: it equals plain
+    decode of the request cut to its first L - n + i + 1 tokens (same pages,
+    shorter last page), bit for bit -- also with RoPE, whose query position
+    is then that of the cut request's last token."""
+    rng = np.random.default_rng(61)
+    Hq, Hkv, D, ps = 4, 2, 128, 3
+    L, n = 17, 6
+    qf, ks, vs, qo, kp, vp, indptr, idx, last = _append_problem(rng, [L], [n], Hq, Hkv, D, ps)
+    qb = to_f16_bits(qf)
+    for rope in (None, (1e4, 1.0)):
+        kw = dict(num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=ps, q_dtype="f16",
+                  kv_dtype="f16", sm_scale=0.15, rope=rope)
+        o, lse = oracle_lib.append(qb, kp, vp, qo, indptr, idx, last, **kw)
+        for i in range(n):
+            keys = L - n + i + 1
+            npg = (keys + ps - 1) // ps
+            ip = np.array([0, npg], np.int32)
+            la = np.array([keys - (npg - 1) * ps], np.int32)
+            od, ld = oracle_lib.decode(qb[i][None], kp, vp, ip, idx[:npg], la, **kw)
+            assert np.array_equal(o[i], od[0]) and np.array_equal(lse[i], ld[0]), (rope, i)
+
+
+def test_append_mask_hides_later_keys(oracle_lib):
+    """Changing the keys and values after query i's position leaves row i
+    bit-identical under the causal mask and changes it without the mask."""
+    rng = np.random.default_rng(62)
+    Hq, Hkv, D, ps = 2, 2, 32, 4
+    L, n = 12, 5
+    qf, ks, vs, qo, kp, vp, indptr, idx, last = _append_problem(rng, [L], [n], Hq, Hkv, D, ps)
+    kw = dict(num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=ps, q_dtype="f16",
+              kv_dtype="f16", sm_scale=0.3)
+    qb = to_f16_bits(qf)
+    o1, l1 = oracle_lib.append(qb, kp, vp, qo, indptr, idx, last, **kw)
+    n1, _ = oracle_lib.append(qb, kp, vp, qo, indptr, idx, last, causal=False, **kw)
+    kp2, vp2 = kp.copy(), vp.copy()
+    t = L - n + 2                      # first key hidden from rows 0 and 1
+    for tt in range(t, L):
+        pg, sl = idx[tt // ps], tt % ps
+        kp2[pg, sl] = to_f16_bits(rng.standard_normal((Hkv, D)))
+        vp2[pg, sl] = to_f16_bits(rng.standard_normal((Hkv, D)))
+    o2, l2 = oracle_lib.append(qb, kp2, vp2, qo, indptr, idx, last, **kw)
+    n2, _ = oracle_lib.append(qb, kp2, vp2, qo, indptr, idx, last, causal=False, **kw)
+    assert np.array_equal(o1[:2], o2[:2]) and np.array_equal(l1[:2], l2[:2])
+    assert not np.array_equal(o1[2:], o2[2:])
+    assert not np.array_equal(n1[:2], n2[:2])
+
+
+def test_append_rejects_more_queries_than_keys(oracle_lib):
+    rng = np.random.default_rng(63)
+    qf, ks, vs, qo, kp, vp, indptr, idx, last = _append_problem(rng, [3], [3], 2, 1, 8, 2)
+    qo = np.array([0, 4], np.int32)
+    with pytest.raises(ValueError):
+        oracle_lib.append(to_f16_bits(np.zeros((4, 2, 8))), kp, vp, qo, indptr, idx, last,
+                          num_qo_heads=2, num_kv_heads=1, head_dim=8, page_size=2,
+                          q_dtype="f16", kv_dtype="f16", sm_scale=0.1)
