@@ -117,6 +117,18 @@ typedef struct {
   int32_t pos_encoding;
   float rope_theta;       /* <= 0: 1e4 */
   float rope_scale;       /* <= 0: 1 */
+  /* Append mode (FlashInfer README append example:
+   * single_prefill_with_kv_cache(q, k, v, causal=True), "the last 128 tokens
+   * in the KV-Cache are the new tokens"; batch form over qo_indptr):
+   * qo_indptr != NULL gives request r the query tokens
+   * [qo_indptr[r], qo_indptr[r+1]) of q [total_q][Hq][D], which are the LAST
+   * n_r = qo_indptr[r+1] - qo_indptr[r] <= kv_len_r tokens of its keys:
+   * query i sits at position kv_len_r - n_r + i and, with causal != 0,
+   * attends keys 0 .. kv_len_r - n_r + i (all kv_len_r keys otherwise).
+   * Run with fi_append_run.  Not combined with a cascade level or RoPE
+   * (FI_ERR_UNSUPPORTED).  NULL = decode (one query per request). */
+  const int32_t* qo_indptr;   /* host [B+1], [0] = 0, non-decreasing, or NULL */
+  int32_t causal;
 } fi_problem;
 
 enum { FI_POS_NONE = 0, FI_POS_ROPE_LLAMA = 1 };
@@ -126,7 +138,8 @@ typedef struct fi_plan_s* fi_plan_t;
 /* Plan statistics, for tests and benchmarks. */
 typedef struct {
   int64_t num_tiles;         /* decode work-list entries (workgroups) */
-  int64_t num_prefix_tiles;  /* cascade prefix work-list entries */
+  int64_t num_prefix_tiles;  /* multi-row work-list entries (cascade prefix
+                                tiles, or the tiles of an append plan) */
   int64_t num_partials;      /* partial (o, lse) states written by tiles */
   int64_t num_merge_units;   /* requests whose states are merged */
   int32_t chunk_tokens;      /* split chunk chosen (tokens) */
@@ -193,6 +206,24 @@ fi_status fi_cascade_decode(fi_plan_t plan, const void* q, const void* k_pages,
                             const float* k_scale, const float* v_scale,
                             float sm_scale, void* o, float* lse, void* stream);
 
+/* Run stage: batch append attention (README append example; see
+ * fi_problem.qo_indptr): every query token of request r attends over r's
+ * pages up to its causal limit (all of them without the mask).  The query
+ * rows (token, q head) of one (request, kv head) are processed in 256-row
+ * MFMA tiles over key chunks; tokens whose keys span several chunks are
+ * merged by a merge pass.  The plan must have been made in append mode.
+ * q: DEVICE [total_q][Hq][D] (q_dtype), o: DEVICE [total_q][Hq][D] (q_dtype),
+ * lse: DEVICE [total_q][Hq] fp32 natural log, or NULL; kv_* are DEVICE
+ * copies of the planned tables; k_scale / v_scale as fi_decode_run.
+ * Enqueues 1-2 kernels on stream; capturable.  Errors: FI_ERR_INVALID_ARG
+ * for a NULL plan / required pointer, non-finite sm_scale or a plan not made
+ * in append mode. */
+fi_status fi_append_run(fi_plan_t plan, const void* q, const void* k_pages,
+                        const void* v_pages, const int32_t* kv_indptr,
+                        const int32_t* kv_indices, const int32_t* last_page_len,
+                        const float* k_scale, const float* v_scale, float sm_scale,
+                        void* o, float* lse, void* stream);
+
 /* Merge of attention states computed over DISJOINT key sets of the same
  * query rows (the split-KV / cascade recombination): with
  * M = max_i s_i, s = M + ln sum_i exp(s_i - M), v = sum_i exp(s_i - s) * v_i;
@@ -241,7 +272,8 @@ fi_status fi_debug_gather(int32_t batch, int32_t page_size,
  * on its own.  Arguments as fi_cascade_decode; for a plan without a cascade
  * level the three prefix tables may be NULL.  stage 0 = the decode kernel
  * over the per-request pages, stage 1 = the cascade prefix kernel (plans
- * with prefix tiles only), stage 2 = the merge of split requests' states
+ * with prefix tiles only; for an append plan, its multi-row kernel over the
+ * per-request pages), stage 2 = the merge of split requests' states
  * (nothing when the plan has no merge unit).  Rows whose state is not split
  * are written to o / lse as in the full run; split rows write their partial
  * states to the workspace, which stage 2 merges into o / lse.  Stages 1, 0, 2

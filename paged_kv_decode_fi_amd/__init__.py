@@ -27,7 +27,7 @@ STATUS = {0: "FI_OK", 1: "FI_ERR_INVALID_ARG", 2: "FI_ERR_UNSUPPORTED",
 EXPORTS = ("fi_plan", "fi_plan_destroy", "fi_plan_get_stats", "fi_decode_run",
            "fi_cascade_decode", "fi_merge_states", "fi_status_string",
            "fi_last_error", "fi_debug_plan_tiles", "fi_debug_gather",
-           "fi_debug_stream_read", "fi_debug_run_stage")
+           "fi_debug_stream_read", "fi_debug_run_stage", "fi_append_run")
 
 
 class FiError(RuntimeError):
@@ -47,7 +47,8 @@ class Problem(ctypes.Structure):
                 ("prefix_kv_indptr", ctypes.c_void_p),
                 ("prefix_last_page_len", ctypes.c_void_p),
                 ("chunk_tokens", ctypes.c_int32), ("pos_encoding", ctypes.c_int32),
-                ("rope_theta", ctypes.c_float), ("rope_scale", ctypes.c_float)]
+                ("rope_theta", ctypes.c_float), ("rope_scale", ctypes.c_float),
+                ("qo_indptr", ctypes.c_void_p), ("causal", ctypes.c_int32)]
 
 
 class PlanStats(ctypes.Structure):
@@ -83,6 +84,8 @@ def _load() -> ctypes.CDLL:
     L.fi_decode_run.restype = ctypes.c_int
     L.fi_decode_run.argtypes = [P, P, P, P, P, P, P, P, P, F, P, P, P]
     L.fi_cascade_decode.restype = ctypes.c_int
+    L.fi_append_run.restype = ctypes.c_int
+    L.fi_append_run.argtypes = [P, P, P, P, P, P, P, P, P, F, P, P, P]
     L.fi_cascade_decode.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, F, P, P, P]
     L.fi_debug_run_stage.restype = ctypes.c_int
     L.fi_debug_run_stage.argtypes = [P, I32, P, P, P, P, P, P, P, P, P, P, P, F, P, P, P]
@@ -178,8 +181,11 @@ POS_ENCODINGS = {"none": 0, "rope_llama": 1}
 
 
 def _problem(batch, Hq, Hkv, D, ps, q_dtype, kv_dtype, indptr, last, prefix, chunk,
-             pos_encoding="none", rope_theta=0.0, rope_scale=0.0):
+             pos_encoding="none", rope_theta=0.0, rope_scale=0.0, qo_indptr=None, causal=True):
     pr = Problem()
+    if qo_indptr is not None:
+        qo_indptr = _host_i32(qo_indptr)
+        pr.qo_indptr, pr.causal = _np_ptr(qo_indptr), int(bool(causal))
     pr.pos_encoding = POS_ENCODINGS[pos_encoding]
     pr.rope_theta, pr.rope_scale = rope_theta, rope_scale
     pr.batch, pr.num_qo_heads, pr.num_kv_heads = batch, Hq, Hkv
@@ -187,7 +193,7 @@ def _problem(batch, Hq, Hkv, D, ps, q_dtype, kv_dtype, indptr, last, prefix, chu
     pr.q_dtype, pr.kv_dtype = DTYPES[q_dtype], DTYPES[kv_dtype]
     pr.kv_indptr, pr.last_page_len = _np_ptr(indptr), _np_ptr(last)
     pr.chunk_tokens = chunk
-    keep = [indptr, last]
+    keep = [indptr, last, qo_indptr]
     if prefix is not None:
         qo, pip, plast = (_host_i32(x) for x in prefix)
         pr.num_prefix_groups = len(qo) - 1
@@ -200,13 +206,13 @@ def _problem(batch, Hq, Hkv, D, ps, q_dtype, kv_dtype, indptr, last, prefix, chu
 def debug_plan_tiles(kv_indptr, last_page_len, *, num_qo_heads, num_kv_heads,
                      page_size, head_dim=128, q_dtype="f16", kv_dtype="f16",
                      prefix=None, num_cus=256, chunk_tokens=0,
-                     pos_encoding="none") -> np.ndarray:
+                     pos_encoding="none", qo_indptr=None, causal=True) -> np.ndarray:
     """Host-only: the plan's work list as an int32 [n, 8] array (request,
     kv_head0, t0, t1, slot, kind, row0, row1)."""
     indptr, last = _host_i32(kv_indptr), _host_i32(last_page_len)
     pr, keep = _problem(len(indptr) - 1, num_qo_heads, num_kv_heads, head_dim,
                         page_size, q_dtype, kv_dtype, indptr, last, prefix, chunk_tokens,
-                        pos_encoding)
+                        pos_encoding, qo_indptr=qo_indptr, causal=causal)
     n = ctypes.c_int64(0)
     _check(_get_lib().fi_debug_plan_tiles(ctypes.byref(pr), num_cus, None, 0, ctypes.byref(n)))
     out = np.zeros((max(n.value, 1), 8), np.int32)
@@ -223,12 +229,16 @@ class Plan:
     torch CPU).  prefix = (prefix_qo_indptr, prefix_kv_indptr,
     prefix_last_page_len) host arrays for cascade decoding.  pos_encoding =
     "rope_llama" applies LLaMA-style RoPE to q and the keys on the fly
-    (rope_theta / rope_scale <= 0: 1e4 / 1)."""
+    (rope_theta / rope_scale <= 0: 1e4 / 1).  qo_indptr (host [B+1]) makes an
+    append plan: request r's query tokens qo_indptr[r] .. qo_indptr[r+1]-1
+    are the last ones of its keys (causal mask unless causal=False); run it
+    with Plan.append_run."""
 
     def __init__(self, kv_indptr, last_page_len, *, num_qo_heads, num_kv_heads,
                  page_size, head_dim=128, q_dtype="f16", kv_dtype="f16",
                  prefix=None, num_cus=0, chunk_tokens=0, device=None, stream=None,
-                 pos_encoding="none", rope_theta=0.0, rope_scale=0.0):
+                 pos_encoding="none", rope_theta=0.0, rope_scale=0.0, qo_indptr=None,
+                 causal=True):
         import torch
         self.indptr = _host_i32(kv_indptr)
         self.last = _host_i32(last_page_len)
@@ -238,9 +248,14 @@ class Plan:
         self.q_dtype, self.kv_dtype = q_dtype, kv_dtype
         self.cascade = prefix is not None
         self.pos_encoding = pos_encoding
+        self.append = qo_indptr is not None
+        self.qo_indptr = _host_i32(qo_indptr) if self.append else None
+        # rows of q / o / lse: query tokens (append) or requests
+        self.num_rows = int(self.qo_indptr[-1]) if self.append else self.batch
         pr, keep = _problem(self.batch, num_qo_heads, num_kv_heads, head_dim,
                             page_size, q_dtype, kv_dtype, self.indptr, self.last,
-                            prefix, chunk_tokens, pos_encoding, rope_theta, rope_scale)
+                            prefix, chunk_tokens, pos_encoding, rope_theta, rope_scale,
+                            self.qo_indptr, causal)
         need = ctypes.c_size_t(0)
         _check(_get_lib().fi_plan(ctypes.byref(pr), num_cus, None, 0, ctypes.byref(need), None,
                            None))
@@ -266,17 +281,18 @@ class Plan:
             raise ValueError(f"o must be {q.dtype} {tuple(q.shape)}, got {o.dtype} "
                              f"{tuple(o.shape)}")
         if lse is None:
-            lse = torch.empty((self.batch, self.num_qo_heads), dtype=torch.float32,
+            lse = torch.empty((self.num_rows, self.num_qo_heads), dtype=torch.float32,
                               device=q.device)
-        elif lse.dtype != torch.float32 or tuple(lse.shape) != (self.batch, self.num_qo_heads):
-            raise ValueError(f"lse must be float32 [{self.batch}, {self.num_qo_heads}]")
+        elif lse.dtype != torch.float32 or tuple(lse.shape) != (self.num_rows, self.num_qo_heads):
+            raise ValueError(f"lse must be float32 [{self.num_rows}, {self.num_qo_heads}]")
         return o, lse
 
     def _check_q(self, q):
         import torch
         want = {"f16": torch.float16, "bf16": torch.bfloat16}[self.q_dtype]
-        if q.dtype != want or tuple(q.shape) != (self.batch, self.num_qo_heads, self.head_dim):
-            raise ValueError(f"q must be {want} [{self.batch}, {self.num_qo_heads}, "
+        if q.dtype != want or tuple(q.shape) != (self.num_rows, self.num_qo_heads,
+                                                 self.head_dim):
+            raise ValueError(f"q must be {want} [{self.num_rows}, {self.num_qo_heads}, "
                              f"{self.head_dim}], got {q.dtype} {tuple(q.shape)}")
 
     def _check_pool(self, k_pages, v_pages):
@@ -290,12 +306,29 @@ class Plan:
             k_scale=None, v_scale=None, sm_scale: float = 0.0, o=None, lse=None,
             stream=None):
         """Batch paged decode.  Device tensors; returns (o, lse)."""
-        if self.cascade:
-            raise ValueError("cascade plan: use Plan.cascade_run")
+        if self.cascade or self.append:
+            raise ValueError("cascade / append plan: use Plan.cascade_run / Plan.append_run")
         self._check_q(q)
         self._check_pool(k_pages, v_pages)
         o, lse = self._outputs(q, o, lse)
         _check(_get_lib().fi_decode_run(self.handle, _ptr(q, "q"), _ptr(k_pages, "k_pages"),
+                                        _ptr(v_pages, "v_pages"),
+                                        *_tables(kv_indptr, kv_indices, last_page_len),
+                                        *_scales(k_scale, v_scale), float(sm_scale),
+                                        _ptr(o, "o"), _ptr(lse, "lse"), _stream(stream)))
+        return o, lse
+
+    def append_run(self, q, k_pages, v_pages, kv_indptr, kv_indices, last_page_len,
+                   k_scale=None, v_scale=None, sm_scale: float = 0.0, o=None, lse=None,
+                   stream=None):
+        """Batch append attention: q [total_q, Hq, D] device tensor (query
+        tokens of every request, in qo_indptr order).  Returns (o, lse)."""
+        if not self.append:
+            raise ValueError("plan is not an append plan (make it with qo_indptr)")
+        self._check_q(q)
+        self._check_pool(k_pages, v_pages)
+        o, lse = self._outputs(q, o, lse)
+        _check(_get_lib().fi_append_run(self.handle, _ptr(q, "q"), _ptr(k_pages, "k_pages"),
                                         _ptr(v_pages, "v_pages"),
                                         *_tables(kv_indptr, kv_indices, last_page_len),
                                         *_scales(k_scale, v_scale), float(sm_scale),

@@ -20,7 +20,8 @@
 namespace fi {
 hipError_t launch_decode(const DecodeParams& p, int num_tiles, int waves, bool q_bf16,
                          int kv, bool fold, hipStream_t s);
-hipError_t launch_prefix(const DecodeParams& p, int num_tiles, int waves, bool q_bf16, int kv,
+hipError_t launch_prefix(const DecodeParams& p, int num_tiles, int waves, bool append,
+                         bool q_bf16, int kv,
                          hipStream_t s);
 hipError_t launch_merge_partials(const MergeParams& p, int num_units, bool o_bf16,
                                  hipStream_t s);
@@ -92,6 +93,8 @@ fi::PlanInput to_input(const fi_problem* p, int num_cus) {
   in.chunk_tokens = p->chunk_tokens;
   in.num_cus = num_cus;
   in.pos_encoding = p->pos_encoding;
+  in.append_qo_indptr = p->qo_indptr;
+  in.causal = p->causal;
   in.rope_theta = p->rope_theta;
   in.rope_scale = p->rope_scale;
   return in;
@@ -228,10 +231,10 @@ fi_status fi_plan(const fi_problem* problem, int32_t num_cus, void* workspace,
   memset(st8, 0, meta_bytes);
   memcpy(st8 + hp.layout.tiles_off, hp.tiles,
          sizeof(fi::Tile) * (hp.num_tiles + hp.num_prefix_tiles));
-  memcpy(st8 + hp.layout.req_info_off, hp.req_info, sizeof(fi::ReqInfo) * hp.batch);
+  memcpy(st8 + hp.layout.req_info_off, hp.req_info, sizeof(fi::ReqInfo) * hp.num_req_info);
   memcpy(st8 + hp.layout.merge_reqs_off, hp.merge_units,
          sizeof(fi::MergeUnit) * hp.num_merge_units);
-  memcpy(st8 + hp.layout.qo_indptr_off, hp.qo_indptr, sizeof(int32_t) * (hp.num_groups + 1));
+  memcpy(st8 + hp.layout.qo_indptr_off, hp.qo_indptr, sizeof(int32_t) * hp.qo_len);
   e = hipMemcpyAsync(workspace, staging, meta_bytes, hipMemcpyHostToDevice,
                      reinterpret_cast<hipStream_t>(stream));
   if (e == hipSuccess && hp.rope)   // the (cos, sin) table, built on the device
@@ -300,7 +303,10 @@ fi_status check_run_args(const fi::HostPlan& hp, const void* q, const void* k_pa
     return fail(FI_ERR_INVALID_ARG, "the prefix indptr / last_page_len tables must be non-NULL");
   if ((hp.num_tiles > 0 || hp.num_prefix_tiles > 0) && (!k_pages || !v_pages))
     return fail(FI_ERR_INVALID_ARG, "k_pages and v_pages must be non-NULL");
-  if ((!kv_indices && hp.num_tiles > 0) || (!prefix_kv_indices && hp.num_prefix_tiles > 0))
+  // append tiles read the per-request table
+  const bool own_rows = hp.num_tiles > 0 || (hp.append && hp.num_prefix_tiles > 0);
+  if ((!kv_indices && own_rows) ||
+      (!prefix_kv_indices && !hp.append && hp.num_prefix_tiles > 0))
     return fail(FI_ERR_INVALID_ARG, "the index tables must be non-NULL");
   if (!(sm_scale == sm_scale) || std::isinf(sm_scale))
     return fail(FI_ERR_INVALID_ARG, "sm_scale must be finite");
@@ -324,12 +330,15 @@ fi_status enqueue_run(fi_plan_t plan, int stages, const void* q, const void* k_p
   const bool do_decode = (stages & kStageDecode) && hp.num_tiles > 0;
   if (do_prefix) {
     // prefix tiles read the group-level table; row -> request = the group's
-    // first request (planned copy of prefix_qo_indptr) + row / G
+    // first request (planned copy of prefix_qo_indptr) + row / G.  Append
+    // tiles read the request's own table; row -> query token = the
+    // request's first token (planned copy of qo_indptr) + row / G.
     fi::DecodeParams pp = p;
-    pp.kv_indptr = prefix_kv_indptr;
-    pp.kv_indices = prefix_kv_indices;
+    pp.kv_indptr = hp.append ? kv_indptr : prefix_kv_indptr;
+    pp.kv_indices = hp.append ? kv_indices : prefix_kv_indices;
     pp.qo_indptr = reinterpret_cast<const int32_t*>(plan->workspace + hp.layout.qo_indptr_off);
-    e = fi::launch_prefix(pp, (int)hp.num_prefix_tiles, hp.prefix_waves, qbf, kv, s);
+    e = fi::launch_prefix(pp, (int)hp.num_prefix_tiles, hp.prefix_waves, hp.append != 0, qbf,
+                          kv, s);
     if (e != hipSuccess) return hip_fail(e, "prefix launch");
   }
   if (do_decode) {
@@ -355,6 +364,7 @@ fi_status fi_decode_run(fi_plan_t plan, const void* q, const void* k_pages,
   const fi::HostPlan& hp = plan->hp;
   if (hp.num_groups != 0)
     return fail(FI_ERR_INVALID_ARG, "plan has a cascade level: use fi_cascade_decode");
+  if (hp.append) return fail(FI_ERR_INVALID_ARG, "append plan: use fi_append_run");
   if (hp.batch == 0) return FI_OK;
   fi_status st = check_run_args(hp, q, k_pages, v_pages, nullptr, nullptr, nullptr, kv_indptr,
                                 kv_indices, last_page_len, sm_scale, o);
@@ -374,6 +384,7 @@ fi_status fi_cascade_decode(fi_plan_t plan, const void* q, const void* k_pages,
   g_last_error.clear();
   if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
   const fi::HostPlan& hp = plan->hp;
+  if (hp.append) return fail(FI_ERR_INVALID_ARG, "append plan: use fi_append_run");
   if (hp.num_groups == 0)
     return fail(FI_ERR_INVALID_ARG, "plan has no cascade level: use fi_decode_run");
   if (hp.batch == 0) return FI_OK;
@@ -384,6 +395,24 @@ fi_status fi_cascade_decode(fi_plan_t plan, const void* q, const void* k_pages,
   return enqueue_run(plan, kStagePrefix | kStageDecode | kStageMerge, q, k_pages, v_pages,
                      prefix_kv_indptr, prefix_kv_indices, kv_indptr, kv_indices, k_scale,
                      v_scale, sm_scale, o, lse, reinterpret_cast<hipStream_t>(stream));
+}
+
+fi_status fi_append_run(fi_plan_t plan, const void* q, const void* k_pages,
+                        const void* v_pages, const int32_t* kv_indptr,
+                        const int32_t* kv_indices, const int32_t* last_page_len,
+                        const float* k_scale, const float* v_scale, float sm_scale,
+                        void* o, float* lse, void* stream) {
+  g_last_error.clear();
+  if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
+  const fi::HostPlan& hp = plan->hp;
+  if (!hp.append) return fail(FI_ERR_INVALID_ARG, "plan is not an append plan");
+  if (hp.total_q == 0) return FI_OK;
+  fi_status st = check_run_args(hp, q, k_pages, v_pages, nullptr, nullptr, nullptr, kv_indptr,
+                                kv_indices, last_page_len, sm_scale, o);
+  if (st != FI_OK) return st;
+  return enqueue_run(plan, kStagePrefix | kStageMerge, q, k_pages, v_pages, nullptr, nullptr,
+                     kv_indptr, kv_indices, k_scale, v_scale, sm_scale, o, lse,
+                     reinterpret_cast<hipStream_t>(stream));
 }
 
 fi_status fi_debug_run_stage(fi_plan_t plan, int32_t stage, const void* q, const void* k_pages,
@@ -400,8 +429,8 @@ fi_status fi_debug_run_stage(fi_plan_t plan, int32_t stage, const void* q, const
     return fail(FI_ERR_INVALID_ARG,
                 "stage must be 0 (decode kernel), 1 (prefix kernel) or 2 (merge kernel)");
   if (stage == 1 && hp.num_prefix_tiles == 0)
-    return fail(FI_ERR_INVALID_ARG, "the plan has no cascade prefix tiles");
-  if (hp.batch == 0) return FI_OK;
+    return fail(FI_ERR_INVALID_ARG, "the plan has no cascade prefix or append tiles");
+  if (hp.batch == 0 || (hp.append && hp.total_q == 0)) return FI_OK;
   fi_status st = check_run_args(hp, q, k_pages, v_pages, prefix_kv_indptr, prefix_kv_indices,
                                 prefix_last_page_len, kv_indptr, kv_indices, last_page_len,
                                 sm_scale, o);

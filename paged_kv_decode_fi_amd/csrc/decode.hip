@@ -528,6 +528,13 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
 // the block -> tile map puts all row tiles of one (head, chunk) on the same
 // XCD (workgroups are dispatched to the 8 XCDs round-robin) so they share
 // that XCD's L2.
+//
+// The same kernel runs append tiles (APPEND): the rows are the query tokens
+// of one request (token-major, G heads each) over that request's own pages;
+// row i may attend keys below its limit (ReqInfo.kv_len of its token: its
+// causal limit, or all keys without the mask), so a step that reaches past
+// the smallest limit of the wave's rows masks per row, and a wave skips
+// steps past the largest limit of its rows.
 constexpr int kPStep = 32;
 constexpr float kPrefixLazySum = 256.f;
 
@@ -548,9 +555,13 @@ __device__ __forceinline__ int xcd_tile(int b, int n) {
   return x * per + min(x, rem) + k;
 }
 
-template <int KV, bool QBF16, int WAVES, bool PS_POW2>
+template <int KV, bool QBF16, int WAVES, bool PS_POW2, bool APPEND>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(DecodeParams p) {
   using S = PStage<KV>;
+  // append rows may attend a handful of keys, where rounding p to bf16 for
+  // P.V (8 bits) alone moves o by more than the accuracy bar: bf16 append
+  // tiles carry p as a bf16 high part plus a bf16 residual
+  constexpr bool SPLITP = APPEND && QBF16;
   __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
   int* ptab = reinterpret_cast<int*>(lds + 2 * S::BUF);
   const int tid = threadIdx.x;
@@ -591,6 +602,26 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
       qop[rt][s] = rok[rt] ? v : u32x4{0, 0, 0, 0};
     }
   }
+  // key limit of each of this lane's rows within the tile (t1, or the
+  // row's causal limit), and over the wave's valid rows the smallest (steps
+  // reaching past it mask per row) and the largest (steps from there on
+  // have no key for any row: skipped)
+  int lim[2], lo = 0x7fffffff, hi = -0x7fffffff - 1;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    lim[rt] = APPEND ? min(p.req_info[rreq[rt]].kv_len, t1) : t1;
+    if (rok[rt]) {
+      lo = min(lo, lim[rt]);
+      hi = max(hi, lim[rt]);
+    }
+  }
+#pragma unroll
+  for (int k = 1; k < 16; k <<= 1) {
+    lo = min(lo, __shfl_xor(lo, k));
+    hi = max(hi, __shfl_xor(hi, k));
+  }
+  const int wave_lo = __builtin_amdgcn_readfirstlane(lo);
+  const int wave_hi = __builtin_amdgcn_readfirstlane(hi);
   float c = p.sm_scale_log2;
   if (KV == kKvE4M3 && p.k_scale) c *= p.k_scale[h];
 
@@ -651,9 +682,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
 #pragma unroll
     for (int b = 0; b < 8; ++b) oacc[rt][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // one 32-token step from LDS buffer buf; a tail step masks tokens past t1
-  // (a uniform branch around the masking only: one copy of the step body
-  // keeps the accumulators in place across iterations)
+  // one 32-token step from LDS buffer buf; a step reaching past the
+  // smallest row limit masks tokens at or past each row's limit (a uniform
+  // branch around the masking only: one copy of the step body keeps the
+  // accumulators in place across iterations)
   auto compute = [&](int tb, int buf, bool tail) {
     const uint8_t* kt = lds + buf * S::BUF;
     const uint8_t* vt = kt + kPStep * S::KS;
@@ -699,7 +731,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
           sc[tt][rt] = mma16x16x32<QBF16>(kop[tt][s], qop[rt][s], sc[tt][rt]);
     // ---- softmax per row tile: lane (g, n) holds tokens 4 g + i and
     // 16 + 4 g + i (i < 4) of row n
-    u32x4 pop[2];
+    u32x4 pop[2], plo[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       float x[8];
@@ -711,8 +743,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
       if (__builtin_expect(tail, 0)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          if (tb + 4 * g + i >= t1) x[i] = -INFINITY;
-          if (tb + 16 + 4 * g + i >= t1) x[4 + i] = -INFINITY;
+          if (tb + 4 * g + i >= lim[rt]) x[i] = -INFINITY;
+          if (tb + 16 + 4 * g + i >= lim[rt]) x[4 + i] = -INFINITY;
         }
       }
       float pr[8];
@@ -720,32 +752,45 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
       for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(__builtin_fmaf(x[i], c, -m[rt]));
       float sum = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
       if (__builtin_expect(__any(!(sum <= kPrefixLazySum)), 0)) {
-        // exact row max of this step (every step holds at least one valid
-        // token, so mx is finite), rescale, recompute
+        // exact row max of this step, rescale, recompute (a row with no key
+        // so far -- all masked -- keeps m = -inf and gets p = 0)
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 8; ++i) mx = fmaxf(mx, x[i] * c);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m[rt], mx);
-        const float alpha = fast_exp2(m[rt] - m_new);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m[rt] - m_use);
         l[rt] *= alpha;
 #pragma unroll
         for (int b = 0; b < 8; ++b) oacc[rt][b] *= alpha;
         m[rt] = m_new;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(__builtin_fmaf(x[i], c, -m_new));
+        for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(__builtin_fmaf(x[i], c, -m_use));
         sum = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
       }
       l[rt] += sum;
       pop[rt] = u32x4{pack2<QBF16>(pr[0], pr[1]), pack2<QBF16>(pr[2], pr[3]),
                       pack2<QBF16>(pr[4], pr[5]), pack2<QBF16>(pr[6], pr[7])};
+      if constexpr (SPLITP) {
+        // bf16 keeps 8 bits of p: the residual p - bf16(p) goes through a
+        // second P.V product
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          plo[rt][k] = pack2<true>(pr[2 * k] - lo16<true>(pop[rt][k]),
+                                   pr[2 * k + 1] - hi16<true>(pop[rt][k]));
+      }
     }
     // ---- P.V on MFMA 16x16x32
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       oacc[0][b] = mma16x16x32<QBF16>(vop[b], pop[0], oacc[0][b]);
       oacc[1][b] = mma16x16x32<QBF16>(vop[b], pop[1], oacc[1][b]);
+      if constexpr (SPLITP) {
+        oacc[0][b] = mma16x16x32<QBF16>(vop[b], plo[0], oacc[0][b]);
+        oacc[1][b] = mma16x16x32<QBF16>(vop[b], plo[1], oacc[1][b]);
+      }
     }
   };
 
@@ -760,7 +805,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
   auto step_body = [&](int step, u32x4 (&nxt)[NL], u32x4 (&aft)[NL]) {
     const int tb = t0 + kPStep * step;
     if (step + 2 < nsteps) load(tb + 2 * kPStep, aft);
-    compute(tb, step & 1, tb + kPStep > t1);
+    if (tb < wave_hi) compute(tb, step & 1, tb + kPStep > wave_lo);
     if (step + 1 < nsteps) store((step + 1) & 1, nxt);
     __syncthreads();
   };
@@ -857,22 +902,26 @@ static hipError_t launch_decode_f(const DecodeParams& p, int num_tiles, int wave
               : launch_decode_t<KV, QBF16, false, 1>(p, num_tiles, waves, s);
 }
 
-template <int KV, bool QBF16, int W>
+template <int KV, bool QBF16, int W, bool APPEND>
 static void launch_prefix_w(const DecodeParams& p, int num_tiles, hipStream_t s) {
   if (p.ps_shift >= 0)
-    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, W, true>), dim3(num_tiles), dim3(64 * W), 0, s, p);
+    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, W, true, APPEND>), dim3(num_tiles),
+                       dim3(64 * W), 0, s, p);
   else
-    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, W, false>), dim3(num_tiles), dim3(64 * W), 0, s,
-                       p);
+    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, W, false, APPEND>), dim3(num_tiles),
+                       dim3(64 * W), 0, s, p);
 }
 
 template <int KV, bool QBF16>
-static hipError_t launch_prefix_t(const DecodeParams& p, int num_tiles, int waves, hipStream_t s) {
+static hipError_t launch_prefix_t(const DecodeParams& p, int num_tiles, int waves, bool append,
+                                  hipStream_t s) {
   if (num_tiles <= 0) return hipSuccess;
   if (waves == 4)
-    launch_prefix_w<KV, QBF16, 4>(p, num_tiles, s);
+    append ? launch_prefix_w<KV, QBF16, 4, true>(p, num_tiles, s)
+           : launch_prefix_w<KV, QBF16, 4, false>(p, num_tiles, s);
   else
-    launch_prefix_w<KV, QBF16, 8>(p, num_tiles, s);
+    append ? launch_prefix_w<KV, QBF16, 8, true>(p, num_tiles, s)
+           : launch_prefix_w<KV, QBF16, 8, false>(p, num_tiles, s);
   return hipGetLastError();
 }
 
@@ -888,14 +937,15 @@ hipError_t launch_decode(const DecodeParams& p, int num_tiles, int waves, bool q
                 : launch_decode_f<kKvF16, false>(p, num_tiles, waves, fold, s);
 }
 
-hipError_t launch_prefix(const DecodeParams& p, int num_tiles, int waves, bool q_bf16, int kv,
-                         hipStream_t s) {
+// append: append tiles (rows limited by ReqInfo.kv_len), else cascade prefix.
+hipError_t launch_prefix(const DecodeParams& p, int num_tiles, int waves, bool append,
+                         bool q_bf16, int kv, hipStream_t s) {
   if (waves != 4 && waves != 8) return hipErrorInvalidValue;
   if (kv == kKvE4M3)
-    return q_bf16 ? launch_prefix_t<kKvE4M3, true>(p, num_tiles, waves, s)
-                  : launch_prefix_t<kKvE4M3, false>(p, num_tiles, waves, s);
-  return q_bf16 ? launch_prefix_t<kKvBF16, true>(p, num_tiles, waves, s)
-                : launch_prefix_t<kKvF16, false>(p, num_tiles, waves, s);
+    return q_bf16 ? launch_prefix_t<kKvE4M3, true>(p, num_tiles, waves, append, s)
+                  : launch_prefix_t<kKvE4M3, false>(p, num_tiles, waves, append, s);
+  return q_bf16 ? launch_prefix_t<kKvBF16, true>(p, num_tiles, waves, append, s)
+                : launch_prefix_t<kKvF16, false>(p, num_tiles, waves, append, s);
 }
 
 }  // namespace fi

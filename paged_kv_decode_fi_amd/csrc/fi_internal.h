@@ -17,7 +17,7 @@ constexpr int kPrefixMaxWaves = 8;       // prefix workgroup: 4 or 8 waves
 constexpr int kPrefixMaxChunk = 4096;    // prefix tokens per tile (page table in LDS)
 constexpr int kMaxMergeStates = 64;
 
-enum TileKind : int32_t { kDecodeTile = 0, kPrefixTile = 1 };
+enum TileKind : int32_t { kDecodeTile = 0, kPrefixTile = 1, kAppendTile = 2 };
 
 // One entry of the work list (32 bytes, one workgroup each).
 //   decode tile: request `req`, kv heads [kv_head0, kv_head0 + waves), tokens
@@ -31,18 +31,24 @@ enum TileKind : int32_t { kDecodeTile = 0, kPrefixTile = 1 };
 // states (the request's cascade prefix chunks, slots slot_base + c * Hkv + h
 // of its ReqInfo) the tile folds into its final output, 0 if none (then
 // slot = -1 means the tile's own state is final).  Prefix tiles: query rows
-// [row0, row1) of the group's G-row-per-request numbering.
+// [row0, row1) of the group's G-row-per-request numbering.  Append tiles
+// (the same multi-row kernel): request `req`, kv head kv_head0, keys
+// [t0, t1) of the request, query rows [row0, row1) of its n query tokens
+// (row = token * G + head in the group), slot = the key chunk index.
 struct Tile {
   int32_t req, kv_head0, t0, t1, slot, kind, row0, row1;
 };
 static_assert(sizeof(Tile) == 32, "tile is 32 bytes");
 
-// Per request: its partial states are slots slot_base + c * Hkv + h, for
-// state index c in [0, n_states) (prefix chunks first) and kv head h.
-// n_states <= 1 means the producing tile writes the final output.
+// Per output row group (a request in decode and cascade plans, a query
+// token in append plans): its partial states are slots slot_base + c * Hkv
+// + h, for state index c in [0, n_states) (prefix chunks first) and kv head
+// h.  n_states <= 1 means the producing tile writes the final output.
+// kv_len: keys the query attends (its position + 1; the RoPE query
+// position is kv_len - 1; append: the causal limit).
 struct ReqInfo {
   int32_t slot_base, n_states;
-  int32_t kv_len, pad;   // own tokens (the RoPE query position is kv_len - 1)
+  int32_t kv_len, pad;
 };
 static_assert(sizeof(ReqInfo) == 16, "request info is 16 bytes");
 
@@ -61,7 +67,7 @@ struct WorkspaceLayout {
   size_t tiles_off;        // Tile[num_tiles] then Tile[num_prefix_tiles]
   size_t req_info_off;     // ReqInfo[batch]
   size_t merge_reqs_off;   // MergeUnit[num_merge_units]
-  size_t qo_indptr_off;    // int32[num_groups + 1] (cascade only)
+  size_t qo_indptr_off;    // int32[qo_len]: cascade group starts or append query starts
   size_t partial_o_off;    // float[num_partials][G][D]
   size_t partial_lse_off;  // float[num_partials][G]   (log2 domain)
   size_t rope_off;         // uint32[rope_rows][kHeadDim / 2] (RoPE plans)
@@ -77,13 +83,18 @@ struct HostPlan {
   int32_t chunk_tokens, prefix_chunk_tokens, heads_per_tile, prefix_waves;
   int64_t num_tiles, num_prefix_tiles, num_partials, num_merge_units;
   int64_t num_folded;   // requests whose decode tile folds in their prefix states
+  int32_t append;       // append plan: multi-token queries over each request's keys
+  int32_t causal;       // append: causal mask
+  int64_t total_q;      // append: query tokens (rows of o)
+  int64_t num_req_info; // ReqInfo entries (batch, or total_q for append)
+  int32_t qo_len;       // qo_indptr entries (groups + 1, or batch + 1 for append)
   int32_t rope;         // FI_POS_ROPE_LLAMA or 0
   int32_t rope_rows;    // positions in the RoPE table (longest request)
   float rope_theta, rope_scale;
   Tile* tiles;          // num_tiles + num_prefix_tiles entries
   ReqInfo* req_info;    // batch entries
   MergeUnit* merge_units;  // num_merge_units entries
-  int32_t* qo_indptr;   // num_groups + 1 entries (cascade only)
+  int32_t* qo_indptr;   // qo_len entries (cascade group starts / append query starts)
   WorkspaceLayout layout;
 };
 
@@ -102,6 +113,8 @@ struct PlanInput {
   int32_t num_cus;
   int32_t pos_encoding;
   float rope_theta, rope_scale;
+  const int32_t* append_qo_indptr;   // host [batch + 1] or NULL (decode)
+  int32_t causal;
 };
 int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen);
 void plan_free(HostPlan* p);

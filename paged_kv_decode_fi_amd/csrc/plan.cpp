@@ -22,6 +22,14 @@
 // so that there is about one prefix tile per CU.  A request whose own suffix
 // is one decode chunk folds the prefix chunks' states into its decode tile's
 // output; others are merged by the merge kernel.
+//
+// Append (FlashInfer README append example; batch form over qo_indptr):
+// request r's n_r query tokens are the last n_r of its L_r keys.  Query rows
+// (token, head in the group) of one (request, kv head) are cut into tiles of
+// prefix_rows rows; each row tile needs the keys up to its last row's causal
+// limit, cut into chunks of one length for the batch (one tile per CU when
+// there is not already that much work).  Query tokens with several chunks
+// get partial states and a merge unit each.
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>
@@ -54,6 +62,157 @@ int64_t table_len(const int32_t* indptr, const int32_t* last, int i, int ps) {
     snprintf(err, errlen, __VA_ARGS__);      \
     return code;                             \
   } while (0)
+
+int plan_append(const PlanInput& in, const std::vector<int64_t>& lens, int num_cus,
+                HostPlan* out, char* err, size_t errlen) {
+  const int B = in.batch, Hkv = in.Hkv, G = in.Hq / in.Hkv;
+  const int32_t* qo = in.append_qo_indptr;
+  if (B > 0 && qo[0] != 0) PLAN_FAIL(1, "qo_indptr[0] must be 0");
+  for (int r = 0; r < B; ++r) {
+    const int64_t n = (int64_t)qo[r + 1] - qo[r];
+    if (n < 0) PLAN_FAIL(1, "qo_indptr decreases at request %d", r);
+    if (n > lens[r])
+      PLAN_FAIL(1, "request %d has %lld query tokens but %lld keys (the queries are the "
+                   "last tokens of the cache)", r, (long long)n, (long long)lens[r]);
+  }
+  const int64_t total_q = B > 0 ? qo[B] : 0;
+  const bool causal = in.causal != 0;
+  const int waves = env_int("FI_PREFIX_WAVES", kPrefixMaxWaves) == 4 ? 4 : 8;
+  const int64_t R = (int64_t)kPrefixRowsPerWave * waves;   // rows per tile
+  // row tiles: (request, rows [row0, row1), keys needed by the last row)
+  struct RowTile {
+    int r;
+    int64_t row0, row1, keys;
+  };
+  std::vector<RowTile> rts;
+  for (int r = 0; r < B; ++r) {
+    const int64_t n = (int64_t)qo[r + 1] - qo[r], rows = n * G;
+    for (int64_t a = 0; a < rows; a += R) {
+      const int64_t b = std::min(a + R, rows), i_last = (b - 1) / G;
+      rts.push_back(RowTile{r, a, b, causal ? lens[r] - n + i_last + 1 : lens[r]});
+    }
+  }
+  int64_t kmax = 0;
+  for (const RowTile& t : rts) kmax = std::max(kmax, t.keys);
+  auto tiles_for = [&](int64_t c) {
+    int64_t w = 0;
+    for (const RowTile& t : rts) w += ceil_div(t.keys, c);
+    return w * Hkv;
+  };
+  int64_t chunk;
+  const int64_t hi = std::min<int64_t>(round_up(std::max<int64_t>(kmax, 1), kBlockTokens),
+                                       kPrefixMaxChunk);
+  if (in.chunk_tokens > 0) {
+    chunk = std::min<int64_t>(round_up(in.chunk_tokens, kBlockTokens), kPrefixMaxChunk);
+  } else {
+    const int64_t want =
+        std::max<int64_t>(1, (int64_t)num_cus * env_int("FI_PREFIX_TILES_PER_CU", 1));
+    if (rts.empty() || tiles_for(hi) >= want) {
+      chunk = hi;
+    } else {
+      // smallest c in [lo, hi] (whole 32-token steps) with tiles(c) <= want
+      const int64_t lo = std::min<int64_t>(
+          round_up(std::max(env_int("FI_PREFIX_CHUNK_MIN", 256), kBlockTokens), kBlockTokens),
+          hi);
+      int64_t a = lo / kBlockTokens, b = hi / kBlockTokens;
+      while (a < b) {
+        const int64_t mid = (a + b) / 2;
+        if (tiles_for(mid * kBlockTokens) <= want) b = mid; else a = mid + 1;
+      }
+      chunk = a * kBlockTokens;
+    }
+  }
+
+  // per query token: states (chunks of its row tile), slots, merge units
+  out->req_info = (ReqInfo*)malloc(sizeof(ReqInfo) * (size_t)std::max<int64_t>(total_q, 1));
+  if (!out->req_info) PLAN_FAIL(1, "out of host memory");
+  std::vector<MergeUnit> mu;
+  int64_t slots = 0;
+  for (const RowTile& t : rts) {
+    const int64_t n = (int64_t)qo[t.r + 1] - qo[t.r];
+    const int64_t nc = ceil_div(t.keys, chunk);
+    for (int64_t i = t.row0 / G; i <= (t.row1 - 1) / G; ++i) {
+      ReqInfo& ri = out->req_info[qo[t.r] + i];
+      ri.n_states = (int32_t)nc;
+      ri.slot_base = -1;
+      ri.kv_len = (int32_t)(causal ? lens[t.r] - n + i + 1 : lens[t.r]);
+      ri.pad = 0;
+      if (nc >= 2) {
+        ri.slot_base = (int32_t)slots;
+        slots += nc * Hkv;
+        mu.push_back(MergeUnit{(int32_t)(qo[t.r] + i), ri.slot_base, (int32_t)nc, 0});
+      }
+      if (slots > (int64_t)0x7fffffff / (G * kHeadDim))
+        PLAN_FAIL(2, "too many partial states; raise chunk_tokens");
+    }
+  }
+  // tiles: the row tiles of one (request, chunk, kv head) adjacent, so they
+  // run together and share that chunk's K/V in cache
+  std::vector<Tile> at;
+  for (size_t k = 0; k < rts.size();) {
+    size_t e = k;
+    int64_t ncmax = 0;
+    while (e < rts.size() && rts[e].r == rts[k].r) ncmax = std::max(ncmax, ceil_div(rts[e++].keys, chunk));
+    for (int64_t c = 0; c < ncmax; ++c)
+      for (int h = 0; h < Hkv; ++h)
+        for (size_t j = k; j < e; ++j) {
+          if (c * chunk >= rts[j].keys) continue;
+          Tile t;
+          t.req = rts[j].r;
+          t.kv_head0 = h;
+          t.t0 = (int32_t)(c * chunk);
+          t.t1 = (int32_t)std::min<int64_t>((c + 1) * chunk, rts[j].keys);
+          t.slot = (int32_t)c;
+          t.kind = kAppendTile;
+          t.row0 = (int32_t)rts[j].row0;
+          t.row1 = (int32_t)rts[j].row1;
+          at.push_back(t);
+        }
+    k = e;
+  }
+  out->qo_indptr = (int32_t*)malloc(sizeof(int32_t) * (size_t)(B + 1));
+  out->merge_units = (MergeUnit*)malloc(sizeof(MergeUnit) * std::max<size_t>(mu.size(), 1));
+  out->tiles = (Tile*)malloc(sizeof(Tile) * std::max<size_t>(at.size(), 1));
+  if (!out->qo_indptr || !out->merge_units || !out->tiles) PLAN_FAIL(1, "out of host memory");
+  for (int r = 0; r <= B; ++r) out->qo_indptr[r] = B > 0 ? qo[r] : 0;
+  std::copy(mu.begin(), mu.end(), out->merge_units);
+  std::copy(at.begin(), at.end(), out->tiles);
+
+  out->batch = B; out->Hq = in.Hq; out->Hkv = Hkv; out->D = in.D;
+  out->page_size = in.page_size; out->G = G; out->q_dtype = in.q_dtype;
+  out->kv_dtype = in.kv_dtype; out->num_groups = 0; out->num_cus = num_cus;
+  out->chunk_tokens = (int32_t)chunk;
+  out->prefix_chunk_tokens = (int32_t)chunk;
+  out->heads_per_tile = 1;
+  out->prefix_waves = waves;
+  out->num_tiles = 0;
+  out->num_prefix_tiles = (int64_t)at.size();
+  out->num_partials = slots;
+  out->num_merge_units = (int64_t)mu.size();
+  out->append = 1;
+  out->causal = causal ? 1 : 0;
+  out->total_q = total_q;
+  out->num_req_info = total_q;
+  out->qo_len = B + 1;
+
+  WorkspaceLayout& L = out->layout;
+  size_t off = 0;
+  L.tiles_off = off;
+  off = align256(off + sizeof(Tile) * at.size());
+  L.req_info_off = off;
+  off = align256(off + sizeof(ReqInfo) * (size_t)std::max<int64_t>(total_q, 1));
+  L.merge_reqs_off = off;
+  off = align256(off + sizeof(MergeUnit) * std::max<size_t>(mu.size(), 1));
+  L.qo_indptr_off = off;
+  off = align256(off + sizeof(int32_t) * (size_t)(B + 1));
+  L.partial_o_off = off;
+  off = align256(off + sizeof(float) * (size_t)slots * G * kHeadDim);
+  L.partial_lse_off = off;
+  off = align256(off + sizeof(float) * (size_t)slots * G);
+  L.rope_off = off;
+  L.total = off;
+  return 0;
+}
 
 }  // namespace
 
@@ -108,6 +267,11 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
     }
   }
   const int num_cus = in.num_cus > 0 ? in.num_cus : 256;
+  if (in.append_qo_indptr) {
+    if (NG > 0) PLAN_FAIL(2, "append with a cascade level is not built");
+    if (in.pos_encoding != 0) PLAN_FAIL(2, "append with RoPE is not built");
+    return plan_append(in, lens, num_cus, out, err, errlen);
+  }
   if (in.pos_encoding != 0 && in.pos_encoding != 1)
     PLAN_FAIL(1, "pos_encoding must be FI_POS_NONE or FI_POS_ROPE_LLAMA (got %d)",
               in.pos_encoding);
@@ -325,6 +489,8 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   out->num_merge_units = n_merge;
   out->num_folded = 0;
   for (int r = 0; r < B; ++r) out->num_folded += folded[r] ? 1 : 0;
+  out->num_req_info = B;
+  out->qo_len = NG + 1;
 
   WorkspaceLayout& L = out->layout;
   size_t off = 0;

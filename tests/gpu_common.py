@@ -120,6 +120,14 @@ def assert_parity(w, o, lse, ro, rl, rows=None, label=""):
     dl = np.abs(lse[~empty] - rl[~empty])
     msg = (f"{label}: max|err| {err.max() if err.size else 0:.3e} "
            f"(bad {int(bad.sum())}/{bad.size}), max|dlse| {dl.max() if dl.size else 0:.3e}")
+    if bad.any():
+        # where: (selected row, dim) of the worst excess over the bound, with
+        # the reference value there
+        ex = err - (TOL_FP8 if w.kv_dtype == "e4m3" else TOL_ABS + TOL_REL * np.abs(ro))
+        k = np.unravel_index(int(np.argmax(ex)), ex.shape)
+        sel = np.argwhere(rows)[k[0]]
+        msg += (f"; worst at (row {int(sel[0])}, head {int(sel[1])}, dim {int(k[1])}): "
+                f"got {o[k]:.5f} want {ro[k]:.5f}")
     print(msg)
     assert not bad.any(), msg
     assert dl.size == 0 or dl.max() <= TOL_LSE, msg

@@ -283,3 +283,76 @@ def test_binding_rejects_host_and_mistyped_tensors(fi):
     with pytest.raises(ValueError, match="GPU tensor"):
         fi._tables(torch.zeros(3, dtype=torch.int32), None, None)
     assert fi._ptr(None) is None
+
+
+def _append_cover(tiles, lens, nq, G, Hkv, causal):
+    """Every (query token, q head, key below its limit) is covered by exactly
+    one append tile; tiles reach no key that none of their rows may see."""
+    qo = np.concatenate([[0], np.cumsum(nq)])
+    seen = {}
+    for req, h, t0, t1, slot, kind, r0, r1 in tiles:
+        assert kind == 2
+        n, L = nq[req], lens[req]
+        assert 0 <= r0 < r1 <= n * G and 0 <= t0 < t1 <= L
+        last_lim = L - n + (r1 - 1) // G + 1 if causal else L
+        assert t1 <= last_lim
+        for row in range(r0, r1):
+            i, gg = divmod(row, G)
+            lim = L - n + i + 1 if causal else L
+            for t in range(t0, min(t1, lim)):
+                key = (qo[req] + i, h * G + gg, t)
+                assert key not in seen, key
+                seen[key] = slot
+    want = sum((L - n + i + 1 if causal else L) * G * Hkv
+               for L, n in zip(lens, nq) for i in range(n))
+    assert len(seen) == want
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("chunk", [0, 32, 64])
+def test_append_plan_covers_every_visible_key_once(fi, causal, chunk):
+    rng = np.random.default_rng(80 + chunk)
+    ps, Hkv, G = 16, 2, 4
+    lens = np.array([300, 5, 129, 64, 0, 77])
+    nq = np.array([70, 5, 1, 64, 0, 0])
+    n = (lens + ps - 1) // ps
+    ip = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    la = np.where(n > 0, lens - (n - 1) * ps, 0).astype(np.int32)
+    qo = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    t = fi.debug_plan_tiles(ip, la, num_qo_heads=Hkv * G, num_kv_heads=Hkv, page_size=ps,
+                            qo_indptr=qo, causal=causal, chunk_tokens=chunk, num_cus=8)
+    _append_cover(t, lens, nq, G, Hkv, causal)
+    if chunk:
+        assert np.all(t[:, 3] - t[:, 2] <= chunk)
+    del rng
+
+
+def test_append_plan_rules(fi):
+    ip = np.array([0, 2, 5], np.int32)
+    la = np.array([3, 16], np.int32)                 # lengths 19 and 48
+    ok = np.array([0, 19, 20], np.int32)
+    assert _status(fi, ip, la) == 0
+    pr, keep = _problem(fi, ip, la)
+    q_ok = ok.copy()
+    pr.qo_indptr, pr.causal = q_ok.ctypes.data, 1
+    n = ctypes.c_int64(0)
+    assert fi.lib.fi_debug_plan_tiles(ctypes.byref(pr), 256, None, 0, ctypes.byref(n)) == 0
+    for bad in ([0, 20, 21], [1, 2, 3], [0, 5, 4]):   # 20 > 19 keys; [0] != 0; decreasing
+        q_bad = np.array(bad, np.int32)
+        pr.qo_indptr = q_bad.ctypes.data
+        assert fi.lib.fi_debug_plan_tiles(ctypes.byref(pr), 256, None, 0, ctypes.byref(n)) == 1
+    pr.qo_indptr = q_ok.ctypes.data
+    pr.pos_encoding = 1
+    assert fi.lib.fi_debug_plan_tiles(ctypes.byref(pr), 256, None, 0, ctypes.byref(n)) == 2
+    prefix = (np.array([0, 2], np.int32), np.array([0, 1], np.int32), np.array([16], np.int32))
+    pr2, keep2 = _problem(fi, ip, la, prefix=prefix)
+    pr2.qo_indptr, pr2.causal = q_ok.ctypes.data, 1
+    assert fi.lib.fi_debug_plan_tiles(ctypes.byref(pr2), 256, None, 0, ctypes.byref(n)) == 2
+    # a one-token append of every request is one row tile per (request, kv
+    # head) over all its keys when that is already a CU's worth of tiles
+    lens = np.full(64, 512)
+    ip3 = np.concatenate([[0], np.cumsum(lens // 16)]).astype(np.int32)
+    t = fi.debug_plan_tiles(ip3, np.full(64, 16, np.int32), num_qo_heads=32, num_kv_heads=8,
+                            page_size=16, qo_indptr=np.arange(65, dtype=np.int32))
+    assert len(t) == 64 * 8 and np.all(t[:, 2] == 0) and np.all(t[:, 3] == 512)
+    assert np.all(t[:, 6] == 0) and np.all(t[:, 7] == 4)

@@ -87,6 +87,10 @@ class Paged:
     prefix_kv_indices: Optional[np.ndarray] = None
     prefix_last_page_len: Optional[np.ndarray] = None
     prefix_lens: Optional[np.ndarray] = None
+    # append problems: request r's query tokens qo_indptr[r] .. qo_indptr[r+1]-1
+    # (q is then [total_q, Hq, D]), the last ones of its keys
+    qo_indptr: Optional[np.ndarray] = None
+    causal: bool = True
     meta: dict = field(default_factory=dict)
 
     @property
@@ -109,10 +113,28 @@ class Paged:
                 toks += int(per_req.sum())
         return 2 * toks * self.num_kv_heads * self.row_bytes
 
+    @property
+    def num_rows(self) -> int:
+        """Rows of q / o / lse: query tokens (append) or requests."""
+        return int(self.qo_indptr[-1]) if self.qo_indptr is not None else self.batch
+
+    def visible_keys(self) -> int:
+        """Sum over query tokens of the keys each attends (append problems)."""
+        n = np.diff(self.qo_indptr).astype(np.int64)
+        L = self.kv_lens.astype(np.int64)
+        if not self.causal:
+            return int((n * L).sum())
+        # query i of n sees L - n + i + 1 keys
+        return int((n * (L - n) + n * (n + 1) // 2).sum())
+
+    def append_flops(self) -> int:
+        """4 D flops per (query token, q head, visible key): q.k and p.v."""
+        return 4 * self.head_dim * self.num_qo_heads * self.visible_keys()
+
     def other_bytes(self) -> int:
         """q + o + lse + page indices + scales."""
-        qo = 2 * self.batch * self.num_qo_heads * self.head_dim * ESIZE[self.q_dtype]
-        lse = 4 * self.batch * self.num_qo_heads
+        qo = 2 * self.num_rows * self.num_qo_heads * self.head_dim * ESIZE[self.q_dtype]
+        lse = 4 * self.num_rows * self.num_qo_heads
         idx = 4 * (len(self.kv_indices) + len(self.kv_indptr) + len(self.last_page_len))
         if self.prefix_kv_indices is not None:
             idx += 4 * (len(self.prefix_kv_indices) + len(self.prefix_kv_indptr)
@@ -256,6 +278,25 @@ def build(name, kv_lens, *, Hq, Hkv, D=128, ps=16, q_dtype="f16", kv_dtype="f16"
     return out[ps]
 
 
+def build_append(name, kv_lens, q_lens, *, Hq, Hkv, D=128, ps=16, q_dtype="f16",
+                 kv_dtype="f16", seed=0, causal=True, **kw):
+    """Append problem: the paged K/V of ``build`` (kv_lens include the new
+    tokens) and q [sum(q_lens), Hq, D] drawn from its own seeded stream."""
+    q_lens = np.asarray(q_lens, np.int64)
+    assert np.all(q_lens <= np.asarray(kv_lens)) and np.all(q_lens >= 0)
+    w = build(name, kv_lens, Hq=Hq, Hkv=Hkv, D=D, ps=ps, q_dtype=q_dtype,
+              kv_dtype=kv_dtype, seed=seed, **kw)
+    qo = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    q_rng = np.random.default_rng(np.random.SeedSequence([seed, 4231]))
+    qf = q_rng.standard_normal((int(qo[-1]), Hq, D), dtype=np.float32)
+    ws = w.values() if isinstance(w, dict) else [w]
+    for v in ws:
+        v.q = cast_bits(qf, q_dtype)
+        v.qo_indptr = qo
+        v.causal = bool(causal)
+    return w
+
+
 # ---- the named workloads ---------------------------------------------------
 
 WORKLOADS = ("single_L2048_h32", "batch64_gqa4", "skewed128", "cascade256",
@@ -297,4 +338,25 @@ def make(name: str, seed: Optional[int] = None, small: bool = False):
         return build(name, np.full(B, L, np.int64), Hq=64, Hkv=8, ps=16,
                      q_dtype="bf16", kv_dtype="e4m3", seed=seed,
                      extra_page_sizes=(1,))
+    raise KeyError(name)
+
+
+# Append workloads (FlashInfer README append example: kv_len 2048, 32 q and
+# 32 kv heads, head_dim 128, fp16, the last 128 cache tokens are the query,
+# causal mask; and a batch of 16 such requests with GQA 32/8 and the length
+# mix of batch64_gqa4).
+APPEND_WORKLOADS = ("append_single_q128", "append_batch16_q128")
+
+
+def make_append(name: str, seed: Optional[int] = None, small: bool = False):
+    idx = APPEND_WORKLOADS.index(name)
+    seed = 2000 + idx if seed is None else seed
+    rng = np.random.default_rng(seed)
+    if name == "append_single_q128":
+        L, n = (300, 40) if small else (2048, 128)
+        return build_append(name, [L], [n], Hq=32, Hkv=32, ps=16, seed=seed)
+    if name == "append_batch16_q128":
+        B, lo, hi, n = (4, 1, 600, 48) if small else (16, 512, 4096, 128)
+        lens = rng.integers(lo, hi + 1, size=B)
+        return build_append(name, lens, np.minimum(lens, n), Hq=32, Hkv=8, ps=16, seed=seed)
     raise KeyError(name)
