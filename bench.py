@@ -2,6 +2,11 @@
 """Benchmark of paged decode attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--page-size 1|16] [--rope]
+
+NAME is one of the decode workloads (default batch64_gqa4) or an append
+workload (append_single_q128, append_batch16_q128: multi-token causal
+queries, timed the same way, roofline against MFMA peak).
 
 One step = one run stage of the decode path (page walk, K/V loads, scores,
 online softmax, P.V, finalize, split-KV merge) over one batch of the named
@@ -84,7 +89,8 @@ def main():
 
     torch.cuda.set_device(0)
     t_gen = time.perf_counter()
-    wl = W.make(args.workload, seed=args.seed)
+    append = args.workload in W.APPEND_WORKLOADS
+    wl = (W.make_append if append else W.make)(args.workload, seed=args.seed)
     if isinstance(wl, dict):                   # long32_fp8: ps 1 and ps 16 variants
         wl = wl[args.page_size]
     t_gen = time.perf_counter() - t_gen
@@ -114,15 +120,20 @@ def main():
             c.update(p_indptr=dev(w.prefix_kv_indptr), p_indices=dev(w.prefix_kv_indices),
                      p_last=dev(w.prefix_last_page_len))
         c["o"] = torch.empty_like(c["q"])
-        c["lse"] = torch.empty((w.batch, w.num_qo_heads), dtype=torch.float32, device="cuda")
+        c["lse"] = torch.empty((w.num_rows, w.num_qo_heads), dtype=torch.float32,
+                               device="cuda")
         copies.append(c)
     cascade = w.prefix_kv_indptr is not None
     prefix = ((w.prefix_qo_indptr, w.prefix_kv_indptr, w.prefix_last_page_len)
               if cascade else None)
 
-    if args.rope and cascade:
+    if args.rope and (cascade or append):
         print(json.dumps({"error": "--rope applies to plain decode workloads only"}))
         sys.exit(2)
+    if append:
+        rope_extra = dict(qo_indptr=w.qo_indptr, causal=w.causal)
+    else:
+        rope_extra = {}
     rope_kw = dict(pos_encoding="rope_llama", rope_theta=1e4, rope_scale=1.0) if args.rope else {}
     traffic_key = w.name + ("+rope" if args.rope else "")
 
@@ -131,21 +142,24 @@ def main():
     plan = fi.Plan(w.kv_indptr, w.last_page_len, num_qo_heads=w.num_qo_heads,
                    num_kv_heads=w.num_kv_heads, page_size=w.page_size,
                    head_dim=w.head_dim, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
-                   prefix=prefix, **rope_kw)
+                   prefix=prefix, **rope_kw, **rope_extra)
     torch.cuda.synchronize()
     plan_first_ms = (time.perf_counter() - t0) * 1e3
     t0 = time.perf_counter()
     plan2 = fi.Plan(w.kv_indptr, w.last_page_len, num_qo_heads=w.num_qo_heads,
                     num_kv_heads=w.num_kv_heads, page_size=w.page_size,
                     head_dim=w.head_dim, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
-                    prefix=prefix, **rope_kw)
+                    prefix=prefix, **rope_kw, **rope_extra)
     torch.cuda.synchronize()
     plan_ms = (time.perf_counter() - t0) * 1e3
     plan2.destroy()
 
     def step(i):
         c = copies[i % R]
-        if cascade:
+        if append:
+            plan.append_run(c["q"], c["k"], c["v"], c["indptr"], c["indices"], c["last"],
+                            c["ks"], c["vs"], sm_scale=w.sm_scale, o=c["o"], lse=c["lse"])
+        elif cascade:
             plan.cascade_run(c["q"], c["k"], c["v"], c["p_indptr"], c["p_indices"],
                              c["p_last"], c["indptr"], c["indices"], c["last"], c["ks"],
                              c["vs"], sm_scale=w.sm_scale, o=c["o"], lse=c["lse"])
@@ -202,8 +216,8 @@ def main():
     # as its separate kernels (cascade: prefix, suffix decode, merge; else
     # decode, merge -- the same launches as the run call) with one event
     # pair on the launch stream around the dominant kernel only
-    kstage = 1 if cascade else 0
-    stages = (1, 0, 2) if cascade else (0, 2)
+    kstage = 1 if cascade or append else 0
+    stages = (1, 0, 2) if cascade else (1, 2) if append else (0, 2)
 
     def sstep(i, stage):
         c = copies[i % R]
@@ -250,10 +264,14 @@ def main():
     kv_bytes = w.kv_bytes()
     alg_bytes = kv_bytes + w.other_bytes()
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    if cascade:
-        # prefix kernel: q.K^T and P.V over every (row, prefix token) pair
-        rows = np.diff(w.prefix_qo_indptr) * w.num_qo_heads
-        flops = 4.0 * w.head_dim * float((rows * w.prefix_lens).sum())
+    if cascade or append:
+        if cascade:
+            # prefix kernel: q.K^T and P.V over every (row, prefix token) pair
+            rows = np.diff(w.prefix_qo_indptr) * w.num_qo_heads
+            flops = 4.0 * w.head_dim * float((rows * w.prefix_lens).sum())
+        else:
+            # append: the same over every (query token, q head, visible key)
+            flops = float(w.append_flops())
         achieved = flops / (kernel_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "kernel": "prefix_kernel", "achieved": round(achieved, 1),
                     "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -278,6 +296,11 @@ def main():
         # fp64 work at the oracle's ~20 MB/s per thread
         per_unit = kv_bytes / units
         budget = 60 * 20e6
+        if append:
+            # each key is visited once per query row that sees it: budget in
+            # (query row, key) pairs at ~1.5e5 per thread-second
+            per_unit = w.group_size * w.visible_keys() / units
+            budget = 60 * 1.5e5
         n_units = int(min(units, max(threads, budget // max(per_unit, 1))))
         mask = np.zeros(units, np.uint8)
         mask[np.random.default_rng(0).permutation(units)[:n_units]] = 1
@@ -293,7 +316,10 @@ def main():
                   v_scale=w.v_scale, unit_mask=mask, threads=threads,
                   rope=(1e4, 1.0) if args.rope else None)
         t0 = time.perf_counter()
-        if cascade:
+        if append:
+            oracle.append(w.q, w.k_pages, w.v_pages, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                          w.last_page_len, causal=w.causal, **kw)
+        elif cascade:
             oracle.cascade(w.q, w.k_pages, w.v_pages, w.prefix_qo_indptr,
                            w.prefix_kv_indptr, w.prefix_kv_indices,
                            w.prefix_last_page_len, w.kv_indptr, w.kv_indices,
@@ -321,7 +347,8 @@ def main():
                    "page_size": w.page_size, "q_dtype": w.q_dtype, "kv_dtype": w.kv_dtype,
                    "kv_len_total": int(w.kv_lens.sum()), "kv_bytes": kv_bytes,
                    "rotated_copies": R, "graph": bool(args.graph),
-                   "pos_encoding": "rope_llama" if args.rope else "none"},
+                   "pos_encoding": "rope_llama" if args.rope else "none",
+                   **({"query_tokens": w.num_rows, "causal": w.causal} if append else {})},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "hbm_read_ceiling_gbs": None if ceiling is None else round(ceiling, 1),
         "pct_read_ceiling": None if ceiling is None else round(100 * value / ceiling, 2),

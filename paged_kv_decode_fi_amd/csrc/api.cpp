@@ -23,7 +23,7 @@ hipError_t launch_decode(const DecodeParams& p, int num_tiles, int waves, bool q
 hipError_t launch_prefix(const DecodeParams& p, int num_tiles, int waves, bool append,
                          bool q_bf16, int kv,
                          hipStream_t s);
-hipError_t launch_merge_partials(const MergeParams& p, int num_units, bool o_bf16,
+hipError_t launch_merge_partials(const MergeParams& p, int num_units, bool o_bf16, bool wide,
                                  hipStream_t s);
 hipError_t launch_merge_states(const MergeStatesParams& p, hipStream_t s);
 hipError_t launch_gather(const int32_t* kv_indptr, const int32_t* kv_indices,
@@ -164,7 +164,8 @@ fi_status launch_merge(const fi_plan_s* pl, void* o, float* lse, hipStream_t s) 
   m.Hkv = hp.Hkv;
   m.G = hp.G;
   m.out_dtype = hp.q_dtype;
-  hipError_t e = fi::launch_merge_partials(m, (int)hp.num_merge_units, hp.q_dtype == FI_BF16, s);
+  hipError_t e = fi::launch_merge_partials(m, (int)hp.num_merge_units, hp.q_dtype == FI_BF16,
+                                          hp.merge_wide != 0, s);
   return e == hipSuccess ? FI_OK : hip_fail(e, "merge launch");
 }
 

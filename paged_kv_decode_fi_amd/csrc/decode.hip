@@ -568,7 +568,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, n = lane & 15;
-  const Tile tile = p.tiles[p.num_tiles + xcd_tile(blockIdx.x, gridDim.x)];
+  // cascade: contiguous tile ranges per XCD; append: the plan interleaves
+  // its list so that block b and b + 8 (same XCD) share a key chunk
+  const Tile tile =
+      p.tiles[p.num_tiles + (APPEND ? (int)blockIdx.x : xcd_tile(blockIdx.x, gridDim.x))];
   const int grp = tile.req, h = tile.kv_head0, t0 = tile.t0, t1 = tile.t1;
   const int G = p.G;
   const int qo0 = p.qo_indptr[grp];

@@ -84,6 +84,7 @@ struct HostPlan {
   int64_t num_tiles, num_prefix_tiles, num_partials, num_merge_units;
   int64_t num_folded;   // requests whose decode tile folds in their prefix states
   int32_t append;       // append plan: multi-token queries over each request's keys
+  int32_t merge_wide;   // many merge units with few states: the wide merge kernel
   int32_t causal;       // append: causal mask
   int64_t total_q;      // append: query tokens (rows of o)
   int64_t num_req_info; // ReqInfo entries (batch, or total_q for append)

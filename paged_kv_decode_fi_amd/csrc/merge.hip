@@ -34,9 +34,67 @@ __global__ __launch_bounds__(256) void merge_partials_kernel(MergeParams p) {
                                lse_out, lane);
 }
 
-hipError_t launch_merge_partials(const MergeParams& p, int num_units, bool o_bf16,
+// Many units with few states each (append plans: one unit per query
+// token): one workgroup per (unit, 32 q heads), 8 threads per head with 16
+// dims each, every state's rows loaded by all threads at once.  One wave per
+// (unit, head) would spend most of its short life waiting on two dependent
+// round trips.
+template <bool OBF16>
+__global__ __launch_bounds__(256) void merge_units_wide_kernel(MergeParams p) {
+  const int t = threadIdx.x;
+  const int j = blockIdx.y * 32 + (t >> 3);
+  if (j >= p.Hq) return;
+  const int d0 = 16 * (t & 7);
+  const MergeUnit u = p.units[blockIdx.x];
+  const int h = j / p.G, jj = j - h * p.G;
+  const int64_t stride = (int64_t)p.Hkv * p.G;                  // rows between states
+  const int64_t row0 = ((int64_t)u.slot_base + h) * p.G + jj;   // state 0's row
+  const int n = u.n_states;
+  float M = -INFINITY;
+  for (int c = 0; c < n; ++c) M = fmaxf(M, p.partial_lse[row0 + c * stride]);
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  float S = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll 4
+    for (int c = 0; c < n; ++c) {
+      const float w = fast_exp2(p.partial_lse[row0 + c * stride] - M);
+      S += w;
+      const f32x4* src =
+          reinterpret_cast<const f32x4*>(p.partial_o + (row0 + c * stride) * kHeadDim + d0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 v = src[k];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[4 * k + i] += w * v[i];
+      }
+    }
+  }
+  const float inv = S > 0.f ? 1.f / S : 0.f;
+  u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.o) +
+                                        ((int64_t)u.req * p.Hq + j) * kHeadDim + d0);
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    dst[k] = u32x4{pack2<OBF16>(acc[8 * k] * inv, acc[8 * k + 1] * inv),
+                   pack2<OBF16>(acc[8 * k + 2] * inv, acc[8 * k + 3] * inv),
+                   pack2<OBF16>(acc[8 * k + 4] * inv, acc[8 * k + 5] * inv),
+                   pack2<OBF16>(acc[8 * k + 6] * inv, acc[8 * k + 7] * inv)};
+  if ((t & 7) == 0 && p.lse)
+    p.lse[(int64_t)u.req * p.Hq + j] = S > 0.f ? (M + fast_log2(S)) * kLn2 : -INFINITY;
+}
+
+hipError_t launch_merge_partials(const MergeParams& p, int num_units, bool o_bf16, bool wide,
                                  hipStream_t s) {
   if (num_units <= 0) return hipSuccess;
+  if (wide) {
+    dim3 grid(num_units, (p.Hq + 31) / 32);
+    if (o_bf16)
+      hipLaunchKernelGGL(merge_units_wide_kernel<true>, grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(merge_units_wide_kernel<false>, grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
   dim3 grid(num_units, (p.Hq + 3) / 4);
   if (o_bf16)
     hipLaunchKernelGGL(merge_partials_kernel<true>, grid, dim3(256), 0, s, p);

@@ -77,8 +77,15 @@ int plan_append(const PlanInput& in, const std::vector<int64_t>& lens, int num_c
   }
   const int64_t total_q = B > 0 ? qo[B] : 0;
   const bool causal = in.causal != 0;
-  const int waves = env_int("FI_PREFIX_WAVES", kPrefixMaxWaves) == 4 ? 4 : 8;
+  // 4-wave (128-row) tiles when no (request, kv head) has more rows: an
+  // 8-wave tile would leave half its waves without rows; two 4-wave
+  // workgroups fit a CU
+  int64_t rows_max = 0;
+  for (int r = 0; r < B; ++r) rows_max = std::max<int64_t>(rows_max, (int64_t)(qo[r + 1] - qo[r]) * G);
+  const int waves = env_int("FI_PREFIX_WAVES", rows_max <= 4 * kPrefixRowsPerWave ? 4 : 8) == 4
+                        ? 4 : 8;
   const int64_t R = (int64_t)kPrefixRowsPerWave * waves;   // rows per tile
+  const int64_t slots_per_cu = waves == 4 ? 2 : 1;
   // row tiles: (request, rows [row0, row1), keys needed by the last row)
   struct RowTile {
     int r;
@@ -105,14 +112,16 @@ int plan_append(const PlanInput& in, const std::vector<int64_t>& lens, int num_c
   if (in.chunk_tokens > 0) {
     chunk = std::min<int64_t>(round_up(in.chunk_tokens, kBlockTokens), kPrefixMaxChunk);
   } else {
-    const int64_t want =
-        std::max<int64_t>(1, (int64_t)num_cus * env_int("FI_PREFIX_TILES_PER_CU", 1));
+    // about FI_APPEND_TILES_PCT / 100 (1.25) tiles per resident workgroup, so
+    // unequal requests even out; chunks of at least FI_APPEND_CHUNK_MIN keys
+    const int64_t want = std::max<int64_t>(
+        1, (int64_t)num_cus * slots_per_cu * env_int("FI_APPEND_TILES_PCT", 125) / 100);
     if (rts.empty() || tiles_for(hi) >= want) {
       chunk = hi;
     } else {
       // smallest c in [lo, hi] (whole 32-token steps) with tiles(c) <= want
       const int64_t lo = std::min<int64_t>(
-          round_up(std::max(env_int("FI_PREFIX_CHUNK_MIN", 256), kBlockTokens), kBlockTokens),
+          round_up(std::max(env_int("FI_APPEND_CHUNK_MIN", 128), kBlockTokens), kBlockTokens),
           hi);
       int64_t a = lo / kBlockTokens, b = hi / kBlockTokens;
       while (a < b) {
@@ -123,14 +132,26 @@ int plan_append(const PlanInput& in, const std::vector<int64_t>& lens, int num_c
     }
   }
 
+  // per request: its longest row tile's keys cut into ceil(keys / chunk)
+  // chunks of near-equal length (whole 32-token steps), so no tile is a
+  // short remainder; every row tile of the request uses the same boundaries
+  // (up to its own last key), so the row tiles of a chunk read the same K/V
+  std::vector<int64_t> req_cl(B, kBlockTokens);
+  for (const RowTile& t : rts) {
+    const int64_t nc = ceil_div(t.keys, chunk);
+    req_cl[t.r] = std::max(req_cl[t.r], round_up(ceil_div(t.keys, nc), kBlockTokens));
+  }
+  auto chunk_len = [&](const RowTile& t) { return req_cl[t.r]; };
+  auto n_chunks = [&](const RowTile& t) { return ceil_div(t.keys, req_cl[t.r]); };
   // per query token: states (chunks of its row tile), slots, merge units
   out->req_info = (ReqInfo*)malloc(sizeof(ReqInfo) * (size_t)std::max<int64_t>(total_q, 1));
   if (!out->req_info) PLAN_FAIL(1, "out of host memory");
   std::vector<MergeUnit> mu;
-  int64_t slots = 0;
+  int64_t slots = 0, max_states = 0;
   for (const RowTile& t : rts) {
     const int64_t n = (int64_t)qo[t.r + 1] - qo[t.r];
-    const int64_t nc = ceil_div(t.keys, chunk);
+    const int64_t nc = n_chunks(t);
+    max_states = std::max(max_states, nc);
     for (int64_t i = t.row0 / G; i <= (t.row1 - 1) / G; ++i) {
       ReqInfo& ri = out->req_info[qo[t.r] + i];
       ri.n_states = (int32_t)nc;
@@ -146,29 +167,54 @@ int plan_append(const PlanInput& in, const std::vector<int64_t>& lens, int num_c
         PLAN_FAIL(2, "too many partial states; raise chunk_tokens");
     }
   }
-  // tiles: the row tiles of one (request, chunk, kv head) adjacent, so they
-  // run together and share that chunk's K/V in cache
-  std::vector<Tile> at;
+  // tiles: groups = (request, chunk, kv head), each holding its row tiles;
+  // groups longest first (the kernel takes tiles in list order), and in
+  // rounds of 8 groups the list interleaves row tiles (group x's row tile k
+  // at 8 k + x of the round), so the row tiles of one group land on blocks
+  // 8 apart -- the same XCD, dispatched together, sharing the chunk in L2
+  struct Group {
+    int64_t len;
+    std::vector<Tile> tiles;
+  };
+  std::vector<Group> groups;
   for (size_t k = 0; k < rts.size();) {
     size_t e = k;
+    while (e < rts.size() && rts[e].r == rts[k].r) ++e;
     int64_t ncmax = 0;
-    while (e < rts.size() && rts[e].r == rts[k].r) ncmax = std::max(ncmax, ceil_div(rts[e++].keys, chunk));
+    for (size_t j = k; j < e; ++j) ncmax = std::max(ncmax, n_chunks(rts[j]));
     for (int64_t c = 0; c < ncmax; ++c)
-      for (int h = 0; h < Hkv; ++h)
+      for (int h = 0; h < Hkv; ++h) {
+        Group gr{0, {}};
         for (size_t j = k; j < e; ++j) {
-          if (c * chunk >= rts[j].keys) continue;
+          if (c >= n_chunks(rts[j])) continue;
+          const int64_t cl = chunk_len(rts[j]);
           Tile t;
           t.req = rts[j].r;
           t.kv_head0 = h;
-          t.t0 = (int32_t)(c * chunk);
-          t.t1 = (int32_t)std::min<int64_t>((c + 1) * chunk, rts[j].keys);
+          t.t0 = (int32_t)std::min<int64_t>(c * cl, rts[j].keys);
+          t.t1 = (int32_t)std::min<int64_t>((c + 1) * cl, rts[j].keys);
           t.slot = (int32_t)c;
           t.kind = kAppendTile;
           t.row0 = (int32_t)rts[j].row0;
           t.row1 = (int32_t)rts[j].row1;
-          at.push_back(t);
+          if (t.t1 <= t.t0) continue;
+          gr.len = std::max<int64_t>(gr.len, t.t1 - t.t0);
+          gr.tiles.push_back(t);
         }
+        if (!gr.tiles.empty()) groups.push_back(std::move(gr));
+      }
     k = e;
+  }
+  std::stable_sort(groups.begin(), groups.end(),
+                   [](const Group& a, const Group& b) { return a.len > b.len; });
+  std::vector<Tile> at;
+  for (size_t g0 = 0; g0 < groups.size(); g0 += 8) {
+    const size_t g1 = std::min(groups.size(), g0 + 8);
+    size_t kmax = 0;
+    for (size_t g = g0; g < g1; ++g) kmax = std::max(kmax, groups[g].tiles.size());
+    for (size_t k = 0; k < kmax; ++k)
+      for (size_t g = g0; g < g1; ++g)
+        if (k < groups[g].tiles.size()) at.push_back(groups[g].tiles[k]);
   }
   out->qo_indptr = (int32_t*)malloc(sizeof(int32_t) * (size_t)(B + 1));
   out->merge_units = (MergeUnit*)malloc(sizeof(MergeUnit) * std::max<size_t>(mu.size(), 1));
@@ -191,6 +237,7 @@ int plan_append(const PlanInput& in, const std::vector<int64_t>& lens, int num_c
   out->num_merge_units = (int64_t)mu.size();
   out->append = 1;
   out->causal = causal ? 1 : 0;
+  out->merge_wide = mu.size() >= 128 && max_states <= 8;
   out->total_q = total_q;
   out->num_req_info = total_q;
   out->qo_len = B + 1;
@@ -487,6 +534,11 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   out->prefix_waves = prefix_waves;
   out->num_partials = slots;
   out->num_merge_units = n_merge;
+  {
+    int32_t ms = 0;
+    for (int64_t k = 0; k < n_merge; ++k) ms = std::max(ms, out->merge_units[k].n_states);
+    out->merge_wide = n_merge >= 128 && ms <= 8;   // many units, few states each
+  }
   out->num_folded = 0;
   for (int r = 0; r < B; ++r) out->num_folded += folded[r] ? 1 : 0;
   out->num_req_info = B;

@@ -348,11 +348,14 @@ def test_append_plan_rules(fi):
     pr2, keep2 = _problem(fi, ip, la, prefix=prefix)
     pr2.qo_indptr, pr2.causal = q_ok.ctypes.data, 1
     assert fi.lib.fi_debug_plan_tiles(ctypes.byref(pr2), 256, None, 0, ctypes.byref(n)) == 2
-    # a one-token append of every request is one row tile per (request, kv
-    # head) over all its keys when that is already a CU's worth of tiles
+    # a one-token append of every request: one 4-row tile per (request, kv
+    # head); 128-row (4-wave) tiles, two per CU: 512 tiles already give
+    # 1.25 tiles per resident workgroup's worth (640) within one chunk's
+    # split, so each covers all 512 keys
     lens = np.full(64, 512)
     ip3 = np.concatenate([[0], np.cumsum(lens // 16)]).astype(np.int32)
     t = fi.debug_plan_tiles(ip3, np.full(64, 16, np.int32), num_qo_heads=32, num_kv_heads=8,
                             page_size=16, qo_indptr=np.arange(65, dtype=np.int32))
-    assert len(t) == 64 * 8 and np.all(t[:, 2] == 0) and np.all(t[:, 3] == 512)
+    assert len(t) == 64 * 8 and set(t[:, 3] - t[:, 2]) == {512}
     assert np.all(t[:, 6] == 0) and np.all(t[:, 7] == 4)
+    _append_cover(t, lens, np.ones(64, np.int64), 4, 8, True)

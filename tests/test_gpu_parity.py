@@ -436,3 +436,17 @@ def test_run_stage_prefix_alone(fi):
     with pytest.raises(fi.FiError):
         C.make_plan(w2).run_stage(1, d2.q, d2.k, d2.v, d2.indptr, d2.indices, d2.last,
                                   sm_scale=w2.sm_scale)
+
+
+@pytest.mark.parametrize("q_dtype", ["f16", "bf16"])
+def test_many_split_requests_take_the_wide_merge(fi, q_dtype):
+    """>= 128 split requests go through the merge kernel's wide form (one
+    workgroup per request and 32 q heads); same bar as every other path."""
+    rng = np.random.default_rng(3)
+    lens = rng.integers(40, 200, size=150)
+    w = W.build("wide_merge", lens, Hq=16, Hkv=4, ps=16, q_dtype=q_dtype, kv_dtype=q_dtype,
+                seed=4)
+    o, lse, plan = C.run_gpu(w, chunk_tokens=32)
+    assert plan.stats["num_merge_units"] >= 128
+    ro, rl = C.run_oracle(w)
+    C.assert_parity(w, o, lse, ro, rl, label=f"wide merge {q_dtype} {plan.stats}")
