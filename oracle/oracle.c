@@ -115,16 +115,24 @@ static double load_elem(const void* base, int dtype, int64_t i) {
 
 /* ---- the page-table walk --------------------------------------------------
  * Number of valid tokens of request r: (n_pages - 1) * ps + last_page_len,
- * or 0 when the request owns no page. */
+ * or 0 when the request owns no page.  Ragged layout (FlashInfer README
+ * "core features" item 1 and the hysenlabs review's feature list name a
+ * ragged KV cache next to the paged one; read as each request's tokens
+ * stored contiguously, rows indptr[r] .. indptr[r+1]-1 of one
+ * [total_tokens][Hkv][D] array): indices == NULL and last == NULL, and
+ * indptr counts tokens. */
 static int64_t request_len(const int32_t* indptr, const int32_t* last, int r,
                            int ps) {
   int64_t n = (int64_t)indptr[r + 1] - indptr[r];
+  if (!last) return n;   /* ragged */
   return n == 0 ? 0 : (n - 1) * ps + last[r];
 }
 
-/* Physical token slot (page * ps + slot) of logical token t of request r. */
+/* Physical token slot (page * ps + slot) of logical token t of request r
+ * (ragged: its row indptr[r] + t). */
 static int64_t token_slot(const int32_t* indptr, const int32_t* indices,
                           int r, int64_t t, int ps) {
+  if (!indices) return (int64_t)indptr[r] + t;
   int64_t page = indices[indptr[r] + t / ps];
   return page * ps + t % ps;
 }
@@ -318,6 +326,9 @@ static int run_job(job_t* J, int num_threads) {
       (J->D & 1))
     return -1;
   if (J->rope.on && !(J->rope.theta > 0.0 && J->rope.scale > 0.0)) return -1;
+  /* a level is either paged (indices and last) or ragged (neither) */
+  if ((J->indices == NULL) != (J->last == NULL)) return -1;
+  if (J->n_groups > 0 && ((J->p_indices == NULL) != (J->p_last == NULL))) return -1;
   J->max_len = 0;
   for (int r = 0; r < J->batch; ++r) {
     int64_t L = request_len(J->indptr, J->last, r, J->ps);

@@ -637,3 +637,82 @@ def test_append_rejects_more_queries_than_keys(oracle_lib):
         oracle_lib.append(to_f16_bits(np.zeros((4, 2, 8))), kp, vp, qo, indptr, idx, last,
                           num_qo_heads=2, num_kv_heads=1, head_dim=8, page_size=2,
                           q_dtype="f16", kv_dtype="f16", sm_scale=0.1)
+
+
+# ------------------------------------------------------------- ragged KV
+# FlashInfer README "core features" item 1 names a ragged KV cache beside
+# the paged one: every request's tokens contiguous in one [total, Hkv, D]
+# array, kv_indptr counting tokens, no page indices.
+
+def _ragged_from_dense(dense_list):
+    indptr = np.concatenate([[0], np.cumsum([len(d) for d in dense_list])]).astype(np.int32)
+    pool = np.concatenate(dense_list)[:, None] if len(dense_list) else None
+    return pool, indptr
+
+
+def test_ragged_equals_paged_page_size_1_identity(oracle_lib):
+    """A ragged table is the page-size-1 table whose indices are the rows
+    themselves: decode, cascade and append agree bit for bit."""
+    rng = np.random.default_rng(90)
+    Hq, Hkv, D = 8, 2, 64
+    lens = [5, 0, 33, 17]
+    ks = [to_f16_bits(rng.standard_normal((L, Hkv, D))) for L in lens]
+    vs = [to_f16_bits(rng.standard_normal((L, Hkv, D))) for L in lens]
+    kp, ip = _ragged_from_dense(ks)
+    vp, _ = _ragged_from_dense(vs)
+    ident = np.arange(int(ip[-1]), dtype=np.int32)
+    ones = np.ones(len(lens), np.int32)
+    q = to_f16_bits(rng.standard_normal((len(lens), Hq, D)))
+    kw = dict(num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=1, q_dtype="f16",
+              kv_dtype="f16", sm_scale=0.13)
+    o_r, l_r = oracle_lib.decode(q, kp, vp, ip, None, None, **kw)
+    o_p, l_p = oracle_lib.decode(q, kp, vp, ip, ident, ones, **kw)
+    assert np.array_equal(o_r, o_p) and np.array_equal(l_r, l_p)
+    # cascade: a ragged prefix (the first 9 rows of request 2's data as a
+    # shared prefix of requests 0..3) over ragged own rows
+    pre = to_f16_bits(rng.standard_normal((9, Hkv, D)))
+    kp2, ip2 = _ragged_from_dense([pre] + ks)
+    vp2, _ = _ragged_from_dense([pre] + vs)
+    own_ip = (ip2[1:] - ip2[1]).astype(np.int32) + ip2[1]
+    own_ip = np.concatenate([[ip2[1]], own_ip[1:]]).astype(np.int32)
+    qo_g = np.array([0, len(lens)], np.int32)
+    p_ip = np.array([0, 9], np.int32)
+    o_c, l_c = oracle_lib.cascade(q, kp2, vp2, qo_g, p_ip, None, None, own_ip, None, None, **kw)
+    ident2 = np.arange(int(ip2[-1]), dtype=np.int32)
+    o_cp, l_cp = oracle_lib.cascade(q, kp2, vp2, qo_g, p_ip, ident2, np.ones(1, np.int32), own_ip,
+                                    ident2, ones, **kw)
+    assert np.array_equal(o_c, o_cp) and np.array_equal(l_c, l_cp)
+    # append
+    qo = np.array([0, 2, 2, 10, 27], np.int32)
+    qa = to_f16_bits(rng.standard_normal((27, Hq, D)))
+    o_a, l_a = oracle_lib.append(qa, kp, vp, qo, ip, None, None, **kw)
+    o_ap, l_ap = oracle_lib.append(qa, kp, vp, qo, ip, ident, ones, **kw)
+    assert np.array_equal(o_a, o_ap) and np.array_equal(l_a, l_ap)
+
+
+def test_ragged_matches_dense_brute_force(oracle_lib):
+    from oracle.dense import ref_dense
+    rng = np.random.default_rng(91)
+    Hq, Hkv, D = 4, 2, 16
+    lens = [7, 1, 40]
+    ks = [rng.standard_normal((L, Hkv, D)) for L in lens]
+    vs = [rng.standard_normal((L, Hkv, D)) for L in lens]
+    qf = rng.standard_normal((len(lens), Hq, D)) * 0.1
+    kp, ip = _ragged_from_dense([to_f16_bits(k) for k in ks])
+    vp, _ = _ragged_from_dense([to_f16_bits(v) for v in vs])
+    o, lse = oracle_lib.decode(to_f16_bits(qf), kp, vp, ip, None, None, num_qo_heads=Hq,
+                               num_kv_heads=Hkv, head_dim=D, page_size=1, q_dtype="f16",
+                               kv_dtype="f16", sm_scale=0.3)
+    for r in range(len(lens)):
+        ro, rl = ref_dense(f16_values(qf[r]), f16_values(ks[r]), f16_values(vs[r]), 0.3)
+        np.testing.assert_allclose(o[r], ro, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse[r], rl, rtol=1e-12, atol=1e-13)
+
+
+def test_mixed_paged_and_ragged_tables_are_rejected(oracle_lib):
+    kp = np.zeros((4, 1, 1, 8), np.uint16)
+    with pytest.raises(ValueError):
+        oracle_lib.decode(np.zeros((1, 1, 8), np.uint16), kp, kp, np.array([0, 2], np.int32),
+                          None, np.array([1], np.int32), num_qo_heads=1, num_kv_heads=1,
+                          head_dim=8, page_size=1, q_dtype="f16", kv_dtype="f16",
+                          sm_scale=0.1)
