@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--page-size", type=int, default=16, choices=(1, 16),
                     help="long32_fp8 only: run the page-size-1 or page-size-16 variant")
+    ap.add_argument("--ragged", action="store_true",
+                    help="the same workload in the ragged KV layout (contiguous rows per "
+                         "request, no page table)")
     ap.add_argument("--rope", action="store_true",
                     help="plain decode workloads: LLaMA-style RoPE on the fly "
                          "(theta 1e4, scale 1)")
@@ -93,6 +96,8 @@ def main():
     wl = (W.make_append if append else W.make)(args.workload, seed=args.seed)
     if isinstance(wl, dict):                   # long32_fp8: ps 1 and ps 16 variants
         wl = wl[args.page_size]
+    if args.ragged:
+        wl = W.to_ragged(wl)
     t_gen = time.perf_counter() - t_gen
     w = wl
     print(f"[bench] workload {w.name}: B={w.batch} Hq={w.num_qo_heads} Hkv={w.num_kv_heads} "
@@ -114,10 +119,11 @@ def main():
     copies = []
     for i in range(R):
         c = dict(q=dev(w.q, qdt), k=dev(w.k_pages), v=dev(w.v_pages),
-                 indptr=dev(w.kv_indptr), indices=dev(w.kv_indices),
+                 indptr=dev(w.kv_indptr), indices=None if args.ragged else dev(w.kv_indices),
                  last=dev(w.last_page_len), ks=dev(w.k_scale), vs=dev(w.v_scale))
         if w.prefix_kv_indptr is not None:
-            c.update(p_indptr=dev(w.prefix_kv_indptr), p_indices=dev(w.prefix_kv_indices),
+            c.update(p_indptr=dev(w.prefix_kv_indptr),
+                     p_indices=None if args.ragged else dev(w.prefix_kv_indices),
                      p_last=dev(w.prefix_last_page_len))
         c["o"] = torch.empty_like(c["q"])
         c["lse"] = torch.empty((w.num_rows, w.num_qo_heads), dtype=torch.float32,
@@ -130,10 +136,9 @@ def main():
     if args.rope and (cascade or append):
         print(json.dumps({"error": "--rope applies to plain decode workloads only"}))
         sys.exit(2)
+    rope_extra = dict(kv_layout="ragged") if args.ragged else {}
     if append:
-        rope_extra = dict(qo_indptr=w.qo_indptr, causal=w.causal)
-    else:
-        rope_extra = {}
+        rope_extra.update(qo_indptr=w.qo_indptr, causal=w.causal)
     rope_kw = dict(pos_encoding="rope_llama", rope_theta=1e4, rope_scale=1.0) if args.rope else {}
     traffic_key = w.name + ("+rope" if args.rope else "")
 
@@ -315,17 +320,20 @@ def main():
                   kv_dtype=w.kv_dtype, sm_scale=w.sm_scale, k_scale=w.k_scale,
                   v_scale=w.v_scale, unit_mask=mask, threads=threads,
                   rope=(1e4, 1.0) if args.rope else None)
+        # the ragged layout has no index tables
+        kv_idx = None if args.ragged else w.kv_indices
+        p_idx = None if args.ragged else w.prefix_kv_indices
         t0 = time.perf_counter()
         if append:
-            oracle.append(w.q, w.k_pages, w.v_pages, w.qo_indptr, w.kv_indptr, w.kv_indices,
+            oracle.append(w.q, w.k_pages, w.v_pages, w.qo_indptr, w.kv_indptr, kv_idx,
                           w.last_page_len, causal=w.causal, **kw)
         elif cascade:
             oracle.cascade(w.q, w.k_pages, w.v_pages, w.prefix_qo_indptr,
-                           w.prefix_kv_indptr, w.prefix_kv_indices,
-                           w.prefix_last_page_len, w.kv_indptr, w.kv_indices,
+                           w.prefix_kv_indptr, p_idx,
+                           w.prefix_last_page_len, w.kv_indptr, kv_idx,
                            w.last_page_len, **kw)
         else:
-            oracle.decode(w.q, w.k_pages, w.v_pages, w.kv_indptr, w.kv_indices,
+            oracle.decode(w.q, w.k_pages, w.v_pages, w.kv_indptr, kv_idx,
                           w.last_page_len, **kw)
         dt = time.perf_counter() - t0
         cpu = {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s",
@@ -348,6 +356,7 @@ def main():
                    "kv_len_total": int(w.kv_lens.sum()), "kv_bytes": kv_bytes,
                    "rotated_copies": R, "graph": bool(args.graph),
                    "pos_encoding": "rope_llama" if args.rope else "none",
+                   "kv_layout": "ragged" if args.ragged else "paged",
                    **({"query_tokens": w.num_rows, "causal": w.causal} if append else {})},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "hbm_read_ceiling_gbs": None if ceiling is None else round(ceiling, 1),

@@ -129,9 +129,19 @@ typedef struct {
    * (FI_ERR_UNSUPPORTED).  NULL = decode (one query per request). */
   const int32_t* qo_indptr;   /* host [B+1], [0] = 0, non-decreasing, or NULL */
   int32_t causal;
+  /* KV layout (README "core features" item 1: paged and ragged KV cache):
+   * FI_KV_PAGED (0): NHD pages reached through kv_indptr / kv_indices /
+   * last_page_len as described above.  FI_KV_RAGGED (1): each request's
+   * tokens are contiguous rows kv_indptr[r] .. kv_indptr[r+1]-1 of K and V
+   * [total_tokens][Hkv][D] (kv_indptr counts rows and need not start at 0;
+   * page_size must be 1; last_page_len and the run calls' kv_indices /
+   * last_page_len may be NULL).  A cascade level's prefix tables follow the
+   * same layout, in the same K and V arrays. */
+  int32_t kv_layout;
 } fi_problem;
 
 enum { FI_POS_NONE = 0, FI_POS_ROPE_LLAMA = 1 };
+enum { FI_KV_PAGED = 0, FI_KV_RAGGED = 1 };
 
 typedef struct fi_plan_s* fi_plan_t;
 

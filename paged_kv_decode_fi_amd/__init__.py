@@ -48,7 +48,8 @@ class Problem(ctypes.Structure):
                 ("prefix_last_page_len", ctypes.c_void_p),
                 ("chunk_tokens", ctypes.c_int32), ("pos_encoding", ctypes.c_int32),
                 ("rope_theta", ctypes.c_float), ("rope_scale", ctypes.c_float),
-                ("qo_indptr", ctypes.c_void_p), ("causal", ctypes.c_int32)]
+                ("qo_indptr", ctypes.c_void_p), ("causal", ctypes.c_int32),
+                ("kv_layout", ctypes.c_int32)]
 
 
 class PlanStats(ctypes.Structure):
@@ -178,11 +179,14 @@ def _stream(stream) -> Optional[int]:
 
 
 POS_ENCODINGS = {"none": 0, "rope_llama": 1}
+KV_LAYOUTS = {"paged": 0, "ragged": 1}
 
 
 def _problem(batch, Hq, Hkv, D, ps, q_dtype, kv_dtype, indptr, last, prefix, chunk,
-             pos_encoding="none", rope_theta=0.0, rope_scale=0.0, qo_indptr=None, causal=True):
+             pos_encoding="none", rope_theta=0.0, rope_scale=0.0, qo_indptr=None, causal=True,
+             kv_layout="paged"):
     pr = Problem()
+    pr.kv_layout = KV_LAYOUTS[kv_layout]
     if qo_indptr is not None:
         qo_indptr = _host_i32(qo_indptr)
         pr.qo_indptr, pr.causal = _np_ptr(qo_indptr), int(bool(causal))
@@ -191,11 +195,12 @@ def _problem(batch, Hq, Hkv, D, ps, q_dtype, kv_dtype, indptr, last, prefix, chu
     pr.batch, pr.num_qo_heads, pr.num_kv_heads = batch, Hq, Hkv
     pr.head_dim, pr.page_size = D, ps
     pr.q_dtype, pr.kv_dtype = DTYPES[q_dtype], DTYPES[kv_dtype]
-    pr.kv_indptr, pr.last_page_len = _np_ptr(indptr), _np_ptr(last)
+    pr.kv_indptr = _np_ptr(indptr)
+    pr.last_page_len = _np_ptr(last) if last is not None else None
     pr.chunk_tokens = chunk
     keep = [indptr, last, qo_indptr]
     if prefix is not None:
-        qo, pip, plast = (_host_i32(x) for x in prefix)
+        qo, pip, plast = (_host_i32(x) for x in prefix)   # plast None when ragged
         pr.num_prefix_groups = len(qo) - 1
         pr.prefix_qo_indptr, pr.prefix_kv_indptr = _np_ptr(qo), _np_ptr(pip)
         pr.prefix_last_page_len = _np_ptr(plast)
@@ -206,13 +211,15 @@ def _problem(batch, Hq, Hkv, D, ps, q_dtype, kv_dtype, indptr, last, prefix, chu
 def debug_plan_tiles(kv_indptr, last_page_len, *, num_qo_heads, num_kv_heads,
                      page_size, head_dim=128, q_dtype="f16", kv_dtype="f16",
                      prefix=None, num_cus=256, chunk_tokens=0,
-                     pos_encoding="none", qo_indptr=None, causal=True) -> np.ndarray:
+                     pos_encoding="none", qo_indptr=None, causal=True,
+                     kv_layout="paged") -> np.ndarray:
     """Host-only: the plan's work list as an int32 [n, 8] array (request,
     kv_head0, t0, t1, slot, kind, row0, row1)."""
     indptr, last = _host_i32(kv_indptr), _host_i32(last_page_len)
     pr, keep = _problem(len(indptr) - 1, num_qo_heads, num_kv_heads, head_dim,
                         page_size, q_dtype, kv_dtype, indptr, last, prefix, chunk_tokens,
-                        pos_encoding, qo_indptr=qo_indptr, causal=causal)
+                        pos_encoding, qo_indptr=qo_indptr, causal=causal,
+                        kv_layout=kv_layout)
     n = ctypes.c_int64(0)
     _check(_get_lib().fi_debug_plan_tiles(ctypes.byref(pr), num_cus, None, 0, ctypes.byref(n)))
     out = np.zeros((max(n.value, 1), 8), np.int32)
@@ -232,13 +239,15 @@ class Plan:
     (rope_theta / rope_scale <= 0: 1e4 / 1).  qo_indptr (host [B+1]) makes an
     append plan: request r's query tokens qo_indptr[r] .. qo_indptr[r+1]-1
     are the last ones of its keys (causal mask unless causal=False); run it
-    with Plan.append_run."""
+    with Plan.append_run.  kv_layout="ragged": each request's tokens are
+    contiguous rows kv_indptr[r] .. kv_indptr[r+1]-1 of K and V (page_size 1,
+    last_page_len and kv_indices may be None)."""
 
     def __init__(self, kv_indptr, last_page_len, *, num_qo_heads, num_kv_heads,
                  page_size, head_dim=128, q_dtype="f16", kv_dtype="f16",
                  prefix=None, num_cus=0, chunk_tokens=0, device=None, stream=None,
                  pos_encoding="none", rope_theta=0.0, rope_scale=0.0, qo_indptr=None,
-                 causal=True):
+                 causal=True, kv_layout="paged"):
         import torch
         self.indptr = _host_i32(kv_indptr)
         self.last = _host_i32(last_page_len)
@@ -255,7 +264,7 @@ class Plan:
         pr, keep = _problem(self.batch, num_qo_heads, num_kv_heads, head_dim,
                             page_size, q_dtype, kv_dtype, self.indptr, self.last,
                             prefix, chunk_tokens, pos_encoding, rope_theta, rope_scale,
-                            self.qo_indptr, causal)
+                            self.qo_indptr, causal, kv_layout)
         need = ctypes.c_size_t(0)
         _check(_get_lib().fi_plan(ctypes.byref(pr), num_cus, None, 0, ctypes.byref(need), None,
                            None))

@@ -95,6 +95,7 @@ fi::PlanInput to_input(const fi_problem* p, int num_cus) {
   in.pos_encoding = p->pos_encoding;
   in.append_qo_indptr = p->qo_indptr;
   in.causal = p->causal;
+  in.ragged = p->kv_layout;
   in.rope_theta = p->rope_theta;
   in.rope_scale = p->rope_scale;
   return in;
@@ -148,6 +149,7 @@ fi::DecodeParams base_params(const fi_plan_s* pl, const void* q, const void* k,
     p.rope_table = pl->workspace + hp.layout.rope_off;
     p.rope_rows = hp.rope_rows;
   }
+  p.ragged = hp.ragged;
   return p;
 }
 
@@ -298,16 +300,16 @@ fi_status check_run_args(const fi::HostPlan& hp, const void* q, const void* k_pa
                          const int32_t* prefix_kv_indices, const int32_t* prefix_last_page_len,
                          const int32_t* kv_indptr, const int32_t* kv_indices,
                          const int32_t* last_page_len, float sm_scale, const void* o) {
-  if (!q || !o || !kv_indptr || !last_page_len)
+  if (!q || !o || !kv_indptr || (!hp.ragged && !last_page_len))
     return fail(FI_ERR_INVALID_ARG, "q, o, kv_indptr and last_page_len must be non-NULL");
-  if (hp.num_groups > 0 && (!prefix_kv_indptr || !prefix_last_page_len))
+  if (hp.num_groups > 0 && (!prefix_kv_indptr || (!hp.ragged && !prefix_last_page_len)))
     return fail(FI_ERR_INVALID_ARG, "the prefix indptr / last_page_len tables must be non-NULL");
   if ((hp.num_tiles > 0 || hp.num_prefix_tiles > 0) && (!k_pages || !v_pages))
     return fail(FI_ERR_INVALID_ARG, "k_pages and v_pages must be non-NULL");
   // append tiles read the per-request table
   const bool own_rows = hp.num_tiles > 0 || (hp.append && hp.num_prefix_tiles > 0);
-  if ((!kv_indices && own_rows) ||
-      (!prefix_kv_indices && !hp.append && hp.num_prefix_tiles > 0))
+  if (!hp.ragged && ((!kv_indices && own_rows) ||
+                     (!prefix_kv_indices && !hp.append && hp.num_prefix_tiles > 0)))
     return fail(FI_ERR_INVALID_ARG, "the index tables must be non-NULL");
   if (!(sm_scale == sm_scale) || std::isinf(sm_scale))
     return fail(FI_ERR_INVALID_ARG, "sm_scale must be finite");

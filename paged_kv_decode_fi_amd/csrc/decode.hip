@@ -272,7 +272,7 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   auto load_page = [&](int step) -> int {
     const int t = min(t0 + kStep * step + (lane & 15), last);
     const int pi = PS_POW2 ? (t >> ps_shift) : (t / ps);
-    return p.kv_indices[page_base + pi];
+    return p.ragged ? page_base + pi : p.kv_indices[page_base + pi];
   };
   // DEPTH register sets of step loads (kr/vr[d]); set d holds steps d, d +
   // DEPTH, ...
@@ -583,7 +583,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
   const int pfirst = page_idx(t0);
   {
     const int np = page_idx(t1 - 1) - pfirst + 1;   // <= chunk / page_size + 1 < PTAB
-    for (int i = tid; i < np; i += 64 * WAVES) ptab[i] = p.kv_indices[page_base + pfirst + i];
+    for (int i = tid; i < np; i += 64 * WAVES)
+      ptab[i] = p.ragged ? page_base + pfirst + i : p.kv_indices[page_base + pfirst + i];
   }
 
   // query rows of this lane's two column tiles (B operands of the scores)

@@ -85,6 +85,7 @@ struct HostPlan {
   int64_t num_folded;   // requests whose decode tile folds in their prefix states
   int32_t append;       // append plan: multi-token queries over each request's keys
   int32_t merge_wide;   // many merge units with few states: the wide merge kernel
+  int32_t ragged;       // ragged KV layout
   int32_t causal;       // append: causal mask
   int64_t total_q;      // append: query tokens (rows of o)
   int64_t num_req_info; // ReqInfo entries (batch, or total_q for append)
@@ -116,6 +117,7 @@ struct PlanInput {
   float rope_theta, rope_scale;
   const int32_t* append_qo_indptr;   // host [batch + 1] or NULL (decode)
   int32_t causal;
+  int32_t ragged;   // rows kv_indptr[r] + t, no page indices
 };
 int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen);
 void plan_free(HostPlan* p);
@@ -143,6 +145,9 @@ struct DecodeParams {
   // RoPE plans: the (cos, sin) table, rope_rows x kHeadDim / 2 fp32 pairs
   const void* rope_table;
   int32_t rope_rows;
+  // ragged KV: token t of a request is row kv_indptr[r] + t (page size 1,
+  // kv_indices not read)
+  int32_t ragged;
 };
 
 struct MergeParams {

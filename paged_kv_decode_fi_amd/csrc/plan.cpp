@@ -51,9 +51,11 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// kv_len from a CSR page table row
+// kv_len from a CSR page table row (ragged: last == NULL, indptr counts
+// tokens)
 int64_t table_len(const int32_t* indptr, const int32_t* last, int i, int ps) {
   int64_t n = (int64_t)indptr[i + 1] - indptr[i];
+  if (!last) return n;
   return n == 0 ? 0 : (n - 1) * ps + last[i];
 }
 
@@ -237,6 +239,7 @@ int plan_append(const PlanInput& in, const std::vector<int64_t>& lens, int num_c
   out->num_merge_units = (int64_t)mu.size();
   out->append = 1;
   out->causal = causal ? 1 : 0;
+  out->ragged = in.ragged;
   out->merge_wide = mu.size() >= 128 && max_states <= 8;
   out->total_q = total_q;
   out->num_req_info = total_q;
@@ -275,19 +278,25 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
     PLAN_FAIL(2, "group size %d > %d q heads per kv head is not built", G, kMaxGroup);
   if (in.D != kHeadDim) PLAN_FAIL(2, "head_dim %d not built (only %d)", in.D, kHeadDim);
   if (ps <= 0) PLAN_FAIL(1, "page_size must be >= 1 (got %d)", ps);
-  if (B > 0 && (!in.kv_indptr || !in.last_page_len))
+  if (in.ragged != 0 && in.ragged != 1) PLAN_FAIL(1, "kv_layout must be FI_KV_PAGED or FI_KV_RAGGED");
+  if (in.ragged && ps != 1) PLAN_FAIL(1, "a ragged KV layout has page_size 1 (got %d)", ps);
+  const int32_t* last_tab = in.ragged ? nullptr : in.last_page_len;
+  if (B > 0 && (!in.kv_indptr || (!in.ragged && !in.last_page_len)))
     PLAN_FAIL(1, "kv_indptr and last_page_len (host) are required");
   if (in.chunk_tokens < 0 || in.chunk_tokens % kChunkAlign != 0)
     PLAN_FAIL(1, "chunk_tokens must be 0 or a positive multiple of %d", kChunkAlign);
-  if (B > 0 && in.kv_indptr[0] != 0) PLAN_FAIL(1, "kv_indptr[0] must be 0");
+  // paged tables index kv_indices from 0; a ragged table's entries are the
+  // requests' first rows in K / V, anywhere
+  if (B > 0 && !in.ragged && in.kv_indptr[0] != 0) PLAN_FAIL(1, "kv_indptr[0] must be 0");
+  if (B > 0 && in.kv_indptr[0] < 0) PLAN_FAIL(1, "kv_indptr[0] must be >= 0");
   std::vector<int64_t> lens(B);
   for (int r = 0; r < B; ++r) {
     if (in.kv_indptr[r + 1] < in.kv_indptr[r])
       PLAN_FAIL(1, "kv_indptr decreases at request %d", r);
     int64_t n = (int64_t)in.kv_indptr[r + 1] - in.kv_indptr[r];
-    if (n > 0 && (in.last_page_len[r] < 1 || in.last_page_len[r] > ps))
-      PLAN_FAIL(1, "last_page_len[%d] = %d outside [1, %d]", r, in.last_page_len[r], ps);
-    lens[r] = table_len(in.kv_indptr, in.last_page_len, r, ps);
+    if (n > 0 && last_tab && (last_tab[r] < 1 || last_tab[r] > ps))
+      PLAN_FAIL(1, "last_page_len[%d] = %d outside [1, %d]", r, last_tab[r], ps);
+    lens[r] = table_len(in.kv_indptr, last_tab, r, ps);
     if (lens[r] > (int64_t)0x7fffffff - 64) PLAN_FAIL(1, "request %d too long", r);
   }
   const int NG = in.num_groups;
@@ -295,21 +304,22 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   std::vector<int> group_of(B, -1);
   if (NG < 0) PLAN_FAIL(1, "num_prefix_groups must be >= 0");
   if (NG > 0) {
-    if (!in.qo_indptr || !in.p_indptr || !in.p_last)
+    if (!in.qo_indptr || !in.p_indptr || (!in.ragged && !in.p_last))
       PLAN_FAIL(1, "cascade level needs prefix_qo_indptr, prefix_kv_indptr, "
                    "prefix_last_page_len (host)");
     if (in.qo_indptr[0] != 0 || in.qo_indptr[NG] != B)
       PLAN_FAIL(1, "prefix_qo_indptr must start at 0 and end at batch");
-    if (in.p_indptr[0] != 0) PLAN_FAIL(1, "prefix_kv_indptr[0] must be 0");
+    if (!in.ragged && in.p_indptr[0] != 0) PLAN_FAIL(1, "prefix_kv_indptr[0] must be 0");
+    if (in.p_indptr[0] < 0) PLAN_FAIL(1, "prefix_kv_indptr[0] must be >= 0");
     for (int g = 0; g < NG; ++g) {
       if (in.qo_indptr[g + 1] < in.qo_indptr[g])
         PLAN_FAIL(1, "prefix_qo_indptr decreases at group %d", g);
       if (in.p_indptr[g + 1] < in.p_indptr[g])
         PLAN_FAIL(1, "prefix_kv_indptr decreases at group %d", g);
       int64_t n = (int64_t)in.p_indptr[g + 1] - in.p_indptr[g];
-      if (n > 0 && (in.p_last[g] < 1 || in.p_last[g] > ps))
+      if (n > 0 && !in.ragged && (in.p_last[g] < 1 || in.p_last[g] > ps))
         PLAN_FAIL(1, "prefix_last_page_len[%d] outside [1, %d]", g, ps);
-      plens[g] = table_len(in.p_indptr, in.p_last, g, ps);
+      plens[g] = table_len(in.p_indptr, in.ragged ? nullptr : in.p_last, g, ps);
       for (int r = in.qo_indptr[g]; r < in.qo_indptr[g + 1]; ++r) group_of[r] = g;
     }
   }
@@ -543,6 +553,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   for (int r = 0; r < B; ++r) out->num_folded += folded[r] ? 1 : 0;
   out->num_req_info = B;
   out->qo_len = NG + 1;
+  out->ragged = in.ragged;
 
   WorkspaceLayout& L = out->layout;
   size_t off = 0;

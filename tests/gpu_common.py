@@ -41,14 +41,19 @@ class Dev:
         self.k = to_dev(w.k_pages)
         self.v = to_dev(w.v_pages)
         self.indptr = to_dev(w.kv_indptr)
-        self.indices = to_dev(w.kv_indices)
+        # ragged layout: the kernels get no index or last-page tables
+        self.indices = None if is_ragged(w) else to_dev(w.kv_indices)
         self.last = to_dev(w.last_page_len)
         self.k_scale = to_dev(w.k_scale)
         self.v_scale = to_dev(w.v_scale)
         if w.prefix_kv_indptr is not None:
             self.p_indptr = to_dev(w.prefix_kv_indptr)
-            self.p_indices = to_dev(w.prefix_kv_indices)
+            self.p_indices = None if is_ragged(w) else to_dev(w.prefix_kv_indices)
             self.p_last = to_dev(w.prefix_last_page_len)
+
+
+def is_ragged(w):
+    return bool(w.meta.get("ragged"))
 
 
 def make_plan(w, chunk_tokens=0, cascade=None, rope=None):
@@ -63,7 +68,8 @@ def make_plan(w, chunk_tokens=0, cascade=None, rope=None):
                    prefix=prefix, chunk_tokens=chunk_tokens,
                    pos_encoding="none" if rope is None else "rope_llama",
                    rope_theta=0.0 if rope is None else rope[0],
-                   rope_scale=0.0 if rope is None else rope[1])
+                   rope_scale=0.0 if rope is None else rope[1],
+                   kv_layout="ragged" if is_ragged(w) else "paged")
 
 
 def run_gpu(w, d=None, plan=None, chunk_tokens=0, rope=None):
@@ -84,17 +90,18 @@ def run_gpu(w, d=None, plan=None, chunk_tokens=0, rope=None):
 
 def run_oracle(w, unit_mask=None, rope=None):
     import oracle
+    ragged = is_ragged(w)
     kw = dict(rope=rope, num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
               head_dim=w.head_dim, page_size=w.page_size, q_dtype=w.q_dtype,
               kv_dtype=w.kv_dtype, sm_scale=w.sm_scale, k_scale=w.k_scale,
               v_scale=w.v_scale, unit_mask=unit_mask)
     if w.prefix_kv_indptr is not None:
         return oracle.cascade(w.q, w.k_pages, w.v_pages, w.prefix_qo_indptr,
-                              w.prefix_kv_indptr, w.prefix_kv_indices,
-                              w.prefix_last_page_len, w.kv_indptr, w.kv_indices,
-                              w.last_page_len, **kw)
-    return oracle.decode(w.q, w.k_pages, w.v_pages, w.kv_indptr, w.kv_indices,
-                         w.last_page_len, **kw)
+                              w.prefix_kv_indptr, None if ragged else w.prefix_kv_indices,
+                              w.prefix_last_page_len, w.kv_indptr,
+                              None if ragged else w.kv_indices, w.last_page_len, **kw)
+    return oracle.decode(w.q, w.k_pages, w.v_pages, w.kv_indptr,
+                         None if ragged else w.kv_indices, w.last_page_len, **kw)
 
 
 def rows_of_units(w, unit_mask):

@@ -135,10 +135,15 @@ class Paged:
         """q + o + lse + page indices + scales."""
         qo = 2 * self.num_rows * self.num_qo_heads * self.head_dim * ESIZE[self.q_dtype]
         lse = 4 * self.num_rows * self.num_qo_heads
-        idx = 4 * (len(self.kv_indices) + len(self.kv_indptr) + len(self.last_page_len))
-        if self.prefix_kv_indices is not None:
-            idx += 4 * (len(self.prefix_kv_indices) + len(self.prefix_kv_indptr)
-                        + len(self.prefix_last_page_len) + len(self.prefix_qo_indptr))
+        if self.meta.get("ragged"):   # row offsets only
+            idx = 4 * len(self.kv_indptr)
+            if self.prefix_kv_indptr is not None:
+                idx += 4 * (len(self.prefix_kv_indptr) + len(self.prefix_qo_indptr))
+        else:
+            idx = 4 * (len(self.kv_indices) + len(self.kv_indptr) + len(self.last_page_len))
+            if self.prefix_kv_indices is not None:
+                idx += 4 * (len(self.prefix_kv_indices) + len(self.prefix_kv_indptr)
+                            + len(self.prefix_last_page_len) + len(self.prefix_qo_indptr))
         sc = 0 if self.k_scale is None else 8 * self.num_kv_heads
         return qo + lse + idx + sc
 
@@ -360,3 +365,46 @@ def make_append(name: str, seed: Optional[int] = None, small: bool = False):
         lens = rng.integers(lo, hi + 1, size=B)
         return build_append(name, lens, np.minimum(lens, n), Hq=32, Hkv=8, ps=16, seed=seed)
     raise KeyError(name)
+
+
+def to_ragged(w: Paged) -> Paged:
+    """The same logical problem in the ragged KV layout: every key list
+    (cascade prefixes first, then the requests) contiguous in K / V
+    [total, 1, Hkv, D] (page size 1), the indptr tables counting rows;
+    kv_indices / prefix_kv_indices hold the identity rows (for the oracle's
+    page-size-1 reading; the ragged kernels do not read them) and the
+    last-page tables are None."""
+    import copy
+    Hkv, D, ps = w.num_kv_heads, w.head_dim, w.page_size
+    kp = w.k_pages.reshape(-1, Hkv, D)
+    vp = w.v_pages.reshape(-1, Hkv, D)
+
+    def rows(indptr, indices, last, i):
+        n = int(indptr[i + 1] - indptr[i])
+        L = 0 if n == 0 else (n - 1) * ps + int(last[i])
+        t = np.arange(L)
+        return indices[indptr[i] + t // ps].astype(np.int64) * ps + t % ps
+
+    parts = []
+    ng = 0 if w.prefix_kv_indptr is None else len(w.prefix_kv_indptr) - 1
+    for g in range(ng):
+        parts.append(rows(w.prefix_kv_indptr, w.prefix_kv_indices, w.prefix_last_page_len, g))
+    for r in range(w.batch):
+        parts.append(rows(w.kv_indptr, w.kv_indices, w.last_page_len, r))
+    sizes = [len(x) for x in parts]
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    allrows = np.concatenate(parts) if parts else np.zeros(0, np.int64)
+    r = copy.copy(w)
+    r.name = w.name + "_ragged"
+    r.page_size = 1
+    r.k_pages = np.ascontiguousarray(kp[allrows][:, None])
+    r.v_pages = np.ascontiguousarray(vp[allrows][:, None])
+    r.kv_indptr = offs[ng:].copy()
+    r.kv_indices = np.arange(int(offs[-1]), dtype=np.int32)
+    r.last_page_len = None
+    if ng:
+        r.prefix_kv_indptr = offs[:ng + 1].copy()
+        r.prefix_kv_indices = r.kv_indices
+        r.prefix_last_page_len = None
+    r.meta = dict(w.meta, ragged=True)
+    return r
