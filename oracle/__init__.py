@@ -69,13 +69,13 @@ def lib() -> ctypes.CDLL:
         L.oracle_gather_map.argtypes = [I, I, P, P, P, P]
         L.oracle_decode.restype = I
         L.oracle_decode.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P,
-                                    D, P, P, P, I, I, D, D]
+                                    D, P, P, P, I, I, D, D, I]
         L.oracle_cascade.restype = I
         L.oracle_cascade.argtypes = [I, I, I, I, I, I, I, P, P, P, I, P, P, P, P,
-                                     P, P, P, P, P, D, P, P, P, I, I, D, D]
+                                     P, P, P, P, P, D, P, P, P, I, I, D, D, I]
         L.oracle_append.restype = I
         L.oracle_append.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P,
-                                    D, I, P, P, P, I, I, D, D]
+                                    D, I, P, P, P, I, I, D, D, I]
         L.oracle_rope_rotate.restype = None
         L.oracle_rope_rotate.argtypes = [P, I, D, D, D, P]
         L.oracle_merge.restype = I
@@ -136,6 +136,13 @@ def _rope_args(rope):
     return 1, float(theta), float(scale)
 
 
+def _hnd(kv_layout):
+    """kv_layout "NHD" (pages [P][ps][Hkv][D]) or "HND" ([P][Hkv][ps][D])."""
+    if kv_layout not in ("NHD", "HND"):
+        raise ValueError(kv_layout)
+    return int(kv_layout == "HND")
+
+
 def rope_rotate(x, pos, theta=1e4, scale=1.0):
     """The oracle's rotate-half RoPE of one fp64 vector at position pos."""
     x = _c(x, np.float64)
@@ -148,7 +155,7 @@ def rope_rotate(x, pos, theta=1e4, scale=1.0):
 def decode(q, k_pages, v_pages, kv_indptr, kv_indices, last_page_len, *,
            num_qo_heads, num_kv_heads, head_dim, page_size, q_dtype, kv_dtype,
            sm_scale, k_scale=None, v_scale=None, unit_mask=None, threads=None,
-           rope=None):
+           rope=None, kv_layout="NHD"):
     """fp64 paged decode.  q/k_pages/v_pages are raw storage arrays (uint16 for
     f16/bf16 bits, uint8 for e4m3 codes, float32/float64 otherwise).
     rope = (theta, scale) applies LLaMA-style rotate-half RoPE (keys at their
@@ -167,7 +174,8 @@ def decode(q, k_pages, v_pages, kv_indptr, kv_indices, last_page_len, *,
                              _ptr(k_pages), _ptr(v_pages), _ptr(indptr),
                              _ptr(indices), _ptr(last), _ptr(ks), _ptr(vs),
                              float(sm_scale), _ptr(um), _ptr(o), _ptr(lse),
-                             threads or default_threads(), *_rope_args(rope))
+                             threads or default_threads(), *_rope_args(rope),
+                             _hnd(kv_layout))
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments")
     return o, lse
@@ -176,7 +184,7 @@ def decode(q, k_pages, v_pages, kv_indptr, kv_indices, last_page_len, *,
 def append(q, k_pages, v_pages, qo_indptr, kv_indptr, kv_indices, last_page_len, *,
            num_qo_heads, num_kv_heads, head_dim, page_size, q_dtype, kv_dtype,
            sm_scale, causal=True, k_scale=None, v_scale=None, unit_mask=None,
-           threads=None, rope=None):
+           threads=None, rope=None, kv_layout="NHD"):
     """fp64 batch append attention.  Request r's query tokens
     qo_indptr[r] .. qo_indptr[r+1]-1 are the last ones of its keys: token i of
     n sits at position L - n + i and (causal) attends keys 0 .. L - n + i.
@@ -197,7 +205,8 @@ def append(q, k_pages, v_pages, qo_indptr, kv_indptr, kv_indices, last_page_len,
                              _ptr(k_pages), _ptr(v_pages), _ptr(qo), _ptr(indptr),
                              _ptr(indices), _ptr(last), _ptr(ks), _ptr(vs),
                              float(sm_scale), int(bool(causal)), _ptr(um), _ptr(o),
-                             _ptr(lse), threads or default_threads(), *_rope_args(rope))
+                             _ptr(lse), threads or default_threads(), *_rope_args(rope),
+                             _hnd(kv_layout))
     if rc != 0:
         raise ValueError("oracle_append rejected its arguments")
     return o, lse
@@ -207,7 +216,7 @@ def cascade(q, k_pages, v_pages, prefix_qo_indptr, prefix_kv_indptr,
             prefix_kv_indices, prefix_last_page_len, kv_indptr, kv_indices,
             last_page_len, *, num_qo_heads, num_kv_heads, head_dim, page_size,
             q_dtype, kv_dtype, sm_scale, k_scale=None, v_scale=None,
-            unit_mask=None, threads=None, rope=None):
+            unit_mask=None, threads=None, rope=None, kv_layout="NHD"):
     """fp64 cascade decode: shared prefix of each request group ++ own pages
     (with rope: prefix tokens at positions 0.., own tokens after them)."""
     indptr = _c(kv_indptr, np.int32)
@@ -227,7 +236,7 @@ def cascade(q, k_pages, v_pages, prefix_qo_indptr, prefix_kv_indptr,
                               _ptr(pxa), _ptr(pla), _ptr(ia), _ptr(xa), _ptr(la),
                               _ptr(ksa), _ptr(vsa), float(sm_scale), _ptr(uma),
                               _ptr(o), _ptr(lse), threads or default_threads(),
-                              *_rope_args(rope))
+                              *_rope_args(rope), _hnd(kv_layout))
     if rc != 0:
         raise ValueError("oracle_cascade rejected its arguments")
     return o, lse

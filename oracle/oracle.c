@@ -41,6 +41,9 @@
  *     (cascade: the group's prefix tokens, then the request's own) sits at
  *     position t, the query at position L - 1 (the token being decoded is
  *     the last one in the cache); V is not rotated.
+ *   - page layout: NHD pages [num_pages][page_size][Hkv][D] by default; HND
+ *     (the other value of the registry quickstart's kv_layout argument)
+ *     stores each page head-major, [num_pages][Hkv][page_size][D];
  *   - append attention (README example: single_prefill_with_kv_cache with
  *     causal=True, where "the last 128 tokens in the KV-Cache are the new
  *     tokens"; "check out ... batch decode/append/prefill"): request r has
@@ -247,6 +250,7 @@ typedef struct {
   /* append mode (app_qo_indptr != NULL): query tokens per request */
   const int32_t* app_qo_indptr;
   int causal;
+  int hnd; /* pages head-major: [page][Hkv][ps][D] */
   const uint8_t* unit_mask; /* [batch*Hkv] or NULL: 1 = compute this item */
   double* o;                /* [batch][Hq][D] */
   double* lse;              /* [batch][Hq] */
@@ -260,6 +264,14 @@ static int group_of(const job_t* J, int r) {
   return -1;
 }
 
+/* Element offset of the row of (physical token slot, kv head): NHD pages
+ * keep a token's heads together, HND pages a head's tokens. */
+static int64_t row_offset(const job_t* J, int64_t slot, int h) {
+  if (!J->hnd) return (slot * J->Hkv + h) * (int64_t)J->D;
+  const int64_t page = slot / J->ps, sl = slot % J->ps;
+  return ((page * J->Hkv + h) * J->ps + sl) * (int64_t)J->D;
+}
+
 static void run_item(const job_t* J, int r, int h, int64_t* rows, double* x,
                      double* qv) {
   const int G = J->Hq / J->Hkv, D = J->D;
@@ -270,13 +282,11 @@ static void run_item(const job_t* J, int r, int h, int64_t* rows, double* x,
   if (g >= 0) {
     int64_t Lp = request_len(J->p_indptr, J->p_last, g, J->ps);
     for (int64_t t = 0; t < Lp; ++t)
-      rows[L++] = (token_slot(J->p_indptr, J->p_indices, g, t, J->ps) *
-                       J->Hkv + h) * (int64_t)D;
+      rows[L++] = row_offset(J, token_slot(J->p_indptr, J->p_indices, g, t, J->ps), h);
   }
   int64_t Ls = request_len(J->indptr, J->last, r, J->ps);
   for (int64_t t = 0; t < Ls; ++t)
-    rows[L++] = (token_slot(J->indptr, J->indices, r, t, J->ps) * J->Hkv + h) *
-                (int64_t)D;
+    rows[L++] = row_offset(J, token_slot(J->indptr, J->indices, r, t, J->ps), h);
   kv_src src = {J->k_pages, J->v_pages, J->kv_dtype, D,
                 J->k_scale ? (double)J->k_scale[h] : 1.0,
                 J->v_scale ? (double)J->v_scale[h] : 1.0};
@@ -361,9 +371,11 @@ int oracle_decode(int batch, int num_qo_heads, int num_kv_heads, int head_dim,
                   const int32_t* last_page_len, const float* k_scale,
                   const float* v_scale, double sm_scale,
                   const uint8_t* unit_mask, double* o, double* lse,
-                  int num_threads, int rope, double rope_theta, double rope_scale) {
+                  int num_threads, int rope, double rope_theta, double rope_scale,
+                  int hnd) {
   job_t J;
   memset(&J, 0, sizeof(J));
+  J.hnd = hnd;
   J.rope.on = rope; J.rope.theta = rope_theta; J.rope.scale = rope_scale;
   J.batch = batch; J.Hq = num_qo_heads; J.Hkv = num_kv_heads; J.D = head_dim;
   J.ps = page_size; J.q_dtype = q_dtype; J.kv_dtype = kv_dtype;
@@ -388,9 +400,11 @@ int oracle_cascade(int batch, int num_qo_heads, int num_kv_heads, int head_dim,
                    const int32_t* last_page_len, const float* k_scale,
                    const float* v_scale, double sm_scale,
                    const uint8_t* unit_mask, double* o, double* lse,
-                   int num_threads, int rope, double rope_theta, double rope_scale) {
+                   int num_threads, int rope, double rope_theta, double rope_scale,
+                  int hnd) {
   job_t J;
   memset(&J, 0, sizeof(J));
+  J.hnd = hnd;
   J.rope.on = rope; J.rope.theta = rope_theta; J.rope.scale = rope_scale;
   J.batch = batch; J.Hq = num_qo_heads; J.Hkv = num_kv_heads; J.D = head_dim;
   J.ps = page_size; J.q_dtype = q_dtype; J.kv_dtype = kv_dtype;
@@ -414,10 +428,12 @@ int oracle_append(int batch, int num_qo_heads, int num_kv_heads, int head_dim,
                   const int32_t* last_page_len, const float* k_scale,
                   const float* v_scale, double sm_scale, int causal,
                   const uint8_t* unit_mask, double* o, double* lse,
-                  int num_threads, int rope, double rope_theta, double rope_scale) {
+                  int num_threads, int rope, double rope_theta, double rope_scale,
+                  int hnd) {
   if (!qo_indptr) return -1;
   job_t J;
   memset(&J, 0, sizeof(J));
+  J.hnd = hnd;
   J.rope.on = rope; J.rope.theta = rope_theta; J.rope.scale = rope_scale;
   J.batch = batch; J.Hq = num_qo_heads; J.Hkv = num_kv_heads; J.D = head_dim;
   J.ps = page_size; J.q_dtype = q_dtype; J.kv_dtype = kv_dtype;

@@ -716,3 +716,43 @@ def test_mixed_paged_and_ragged_tables_are_rejected(oracle_lib):
                           None, np.array([1], np.int32), num_qo_heads=1, num_kv_heads=1,
                           head_dim=8, page_size=1, q_dtype="f16", kv_dtype="f16",
                           sm_scale=0.1)
+
+
+# ------------------------------------------------------------- HND pages
+# The registry quickstart passes kv_layout with the cache; the other layout
+# to NHD stores a page head-major: [num_pages][Hkv][page_size][D].
+
+def test_hnd_pages_equal_nhd_pages_transposed(oracle_lib):
+    """The same logical data with every page transposed to head-major gives
+    bit-identical decode, cascade and append results."""
+    rng = np.random.default_rng(95)
+    Hq, Hkv, D, ps = 8, 4, 32, 5
+    lens = [12, 0, 31, 5]
+    ks = [to_f16_bits(rng.standard_normal((L, Hkv, D))) for L in lens]
+    vs = [to_f16_bits(rng.standard_normal((L, Hkv, D))) for L in lens]
+    kp, ip, idx, last = paginate(ks, ps, Hkv, D, np.random.default_rng(4))
+    vp, _, _, _ = paginate(vs, ps, Hkv, D, np.random.default_rng(4))
+    kh = np.ascontiguousarray(kp.transpose(0, 2, 1, 3))
+    vh = np.ascontiguousarray(vp.transpose(0, 2, 1, 3))
+    q = to_f16_bits(rng.standard_normal((len(lens), Hq, D)))
+    kw = dict(num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=ps, q_dtype="f16",
+              kv_dtype="f16", sm_scale=0.21)
+    a = oracle_lib.decode(q, kp, vp, ip, idx, last, **kw)
+    b = oracle_lib.decode(q, kh, vh, ip, idx, last, kv_layout="HND", **kw)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    # a different layout really reads different rows
+    c = oracle_lib.decode(q, kp, vp, ip, idx, last, kv_layout="HND", **kw)
+    assert not np.array_equal(a[0], c[0])
+    qo = np.array([0, 3, 3, 10, 15], np.int32)
+    qa = to_f16_bits(rng.standard_normal((15, Hq, D)))
+    a = oracle_lib.append(qa, kp, vp, qo, ip, idx, last, **kw)
+    b = oracle_lib.append(qa, kh, vh, qo, ip, idx, last, kv_layout="HND", **kw)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    # cascade: request 2's pages as the prefix of every request
+    n2 = ip[3] - ip[2]
+    p_ip = np.array([0, n2], np.int32)
+    qo_g = np.array([0, len(lens)], np.int32)
+    a = oracle_lib.cascade(q, kp, vp, qo_g, p_ip, idx[ip[2]:ip[3]], last[2:3], ip, idx, last, **kw)
+    b = oracle_lib.cascade(q, kh, vh, qo_g, p_ip, idx[ip[2]:ip[3]], last[2:3], ip, idx, last,
+                           kv_layout="HND", **kw)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
