@@ -74,6 +74,8 @@ def parse():
     ap.add_argument("--ragged", action="store_true",
                     help="the same workload in the ragged KV layout (contiguous rows per "
                          "request, no page table)")
+    ap.add_argument("--hnd", action="store_true",
+                    help="the same workload with head-major pages [P][Hkv][ps][D]")
     ap.add_argument("--rope", action="store_true",
                     help="plain decode workloads: LLaMA-style RoPE on the fly "
                          "(theta 1e4, scale 1)")
@@ -98,6 +100,8 @@ def main():
         wl = wl[args.page_size]
     if args.ragged:
         wl = W.to_ragged(wl)
+    elif args.hnd:
+        wl = W.to_hnd(wl)
     t_gen = time.perf_counter() - t_gen
     w = wl
     print(f"[bench] workload {w.name}: B={w.batch} Hq={w.num_qo_heads} Hkv={w.num_kv_heads} "
@@ -136,7 +140,8 @@ def main():
     if args.rope and (cascade or append):
         print(json.dumps({"error": "--rope applies to plain decode workloads only"}))
         sys.exit(2)
-    rope_extra = dict(kv_layout="ragged") if args.ragged else {}
+    rope_extra = (dict(kv_layout="ragged") if args.ragged else
+                  dict(kv_layout="paged_hnd") if args.hnd else {})
     if append:
         rope_extra.update(qo_indptr=w.qo_indptr, causal=w.causal)
     rope_kw = dict(pos_encoding="rope_llama", rope_theta=1e4, rope_scale=1.0) if args.rope else {}
@@ -323,6 +328,7 @@ def main():
         # the ragged layout has no index tables
         kv_idx = None if args.ragged else w.kv_indices
         p_idx = None if args.ragged else w.prefix_kv_indices
+        kw["kv_layout"] = "HND" if args.hnd else "NHD"
         t0 = time.perf_counter()
         if append:
             oracle.append(w.q, w.k_pages, w.v_pages, w.qo_indptr, w.kv_indptr, kv_idx,
@@ -356,7 +362,8 @@ def main():
                    "kv_len_total": int(w.kv_lens.sum()), "kv_bytes": kv_bytes,
                    "rotated_copies": R, "graph": bool(args.graph),
                    "pos_encoding": "rope_llama" if args.rope else "none",
-                   "kv_layout": "ragged" if args.ragged else "paged",
+                   "kv_layout": ("ragged" if args.ragged else
+                                 "paged_hnd" if args.hnd else "paged"),
                    **({"query_tokens": w.num_rows, "causal": w.causal} if append else {})},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "hbm_read_ceiling_gbs": None if ceiling is None else round(ceiling, 1),

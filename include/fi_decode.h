@@ -136,12 +136,14 @@ typedef struct {
    * [total_tokens][Hkv][D] (kv_indptr counts rows and need not start at 0;
    * page_size must be 1; last_page_len and the run calls' kv_indices /
    * last_page_len may be NULL).  A cascade level's prefix tables follow the
-   * same layout, in the same K and V arrays. */
+   * same layout, in the same K and V arrays.  FI_KV_PAGED_HND (2): pages as
+   * FI_KV_PAGED but head-major, [num_pages][Hkv][page_size][D] (the other
+   * value of the registry quickstart's kv_layout argument). */
   int32_t kv_layout;
 } fi_problem;
 
 enum { FI_POS_NONE = 0, FI_POS_ROPE_LLAMA = 1 };
-enum { FI_KV_PAGED = 0, FI_KV_RAGGED = 1 };
+enum { FI_KV_PAGED = 0, FI_KV_RAGGED = 1, FI_KV_PAGED_HND = 2 };
 
 typedef struct fi_plan_s* fi_plan_t;
 

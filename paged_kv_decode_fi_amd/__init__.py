@@ -179,7 +179,7 @@ def _stream(stream) -> Optional[int]:
 
 
 POS_ENCODINGS = {"none": 0, "rope_llama": 1}
-KV_LAYOUTS = {"paged": 0, "ragged": 1}
+KV_LAYOUTS = {"paged": 0, "ragged": 1, "paged_hnd": 2}
 
 
 def _problem(batch, Hq, Hkv, D, ps, q_dtype, kv_dtype, indptr, last, prefix, chunk,
@@ -241,7 +241,8 @@ class Plan:
     are the last ones of its keys (causal mask unless causal=False); run it
     with Plan.append_run.  kv_layout="ragged": each request's tokens are
     contiguous rows kv_indptr[r] .. kv_indptr[r+1]-1 of K and V (page_size 1,
-    last_page_len and kv_indices may be None)."""
+    last_page_len and kv_indices may be None); "paged_hnd": head-major pages
+    [num_pages][Hkv][page_size][D]."""
 
     def __init__(self, kv_indptr, last_page_len, *, num_qo_heads, num_kv_heads,
                  page_size, head_dim=128, q_dtype="f16", kv_dtype="f16",

@@ -95,7 +95,9 @@ fi::PlanInput to_input(const fi_problem* p, int num_cus) {
   in.pos_encoding = p->pos_encoding;
   in.append_qo_indptr = p->qo_indptr;
   in.causal = p->causal;
-  in.ragged = p->kv_layout;
+  in.ragged = p->kv_layout == FI_KV_RAGGED;
+  in.hnd = p->kv_layout == FI_KV_PAGED_HND;
+  if (p->kv_layout < 0 || p->kv_layout > FI_KV_PAGED_HND) in.ragged = in.hnd = -1;
   in.rope_theta = p->rope_theta;
   in.rope_scale = p->rope_scale;
   return in;
@@ -150,6 +152,13 @@ fi::DecodeParams base_params(const fi_plan_s* pl, const void* q, const void* k,
     p.rope_rows = hp.rope_rows;
   }
   p.ragged = hp.ragged;
+  {
+    const uint32_t rowb = hp.kv_dtype == FI_E4M3 ? 128u : 256u;
+    const uint32_t ps = (uint32_t)hp.page_size, hkv = (uint32_t)hp.Hkv;
+    p.page_bytes = ps * hkv * rowb;
+    p.slot_stride = hp.hnd ? rowb : hkv * rowb;
+    p.head_stride = hp.hnd ? ps * rowb : rowb;
+  }
   return p;
 }
 

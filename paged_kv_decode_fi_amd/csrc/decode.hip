@@ -262,9 +262,11 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   // of the step and 16-byte vector vin of that token's W-head run
   const int tk0 = tid / (S::VR * W);
   const int vin = tid - tk0 * (S::VR * W);
-  const char* kbase = reinterpret_cast<const char*>(p.k_pages) + (int64_t)h0 * S::ROWB + 16 * vin;
-  const char* vbase = reinterpret_cast<const char*>(p.v_pages) + (int64_t)h0 * S::ROWB + 16 * vin;
-  const uint32_t slot_bytes = (uint32_t)p.Hkv * S::ROWB;
+  // vector vin = head vin / VR of the tile's run, 16-byte chunk vin % VR
+  const int vh = vin / S::VR, vc = vin - vh * S::VR;
+  const int64_t hoff = (int64_t)(h0 + vh) * p.head_stride + 16 * vc;
+  const char* kbase = reinterpret_cast<const char*>(p.k_pages) + hoff;
+  const char* vbase = reinterpret_cast<const char*>(p.v_pages) + hoff;
   const int last = t1 - 1;
   const int nsteps = (t1 - t0 + kStep - 1) / kStep;
 
@@ -315,9 +317,8 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
       const int tk = tk0 + u * S::TOK_PER_U;
       const int t = min(tb + tk, last);
       const uint32_t page = (uint32_t)__shfl(pg, t - tb);
-      const uint32_t slot = PS_POW2 ? ((page << ps_shift) | (uint32_t)(t & (ps - 1)))
-                                    : (page * (uint32_t)ps + (uint32_t)(t % ps));
-      const uint64_t off = (uint64_t)slot * slot_bytes;
+      const uint32_t sl = PS_POW2 ? (uint32_t)(t & (ps - 1)) : (uint32_t)(t % ps);
+      const uint64_t off = (uint64_t)page * p.page_bytes + sl * p.slot_stride;
       kq[u] = ld_stream<u32x4>(kbase, off);
       vq[u] = ld_stream<u32x4>(vbase, off);
     }
@@ -404,10 +405,18 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
     for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(x[i] - m);
     l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
     const u32x2 pop = {pack2<QBF16>(pr[0], pr[1]), pack2<QBF16>(pr[2], pr[3])};
+    // bf16 V: p also as a bf16 residual (bf16 keeps 8 bits of p; with a few
+    // comparable keys that alone moves o past the accuracy bar)
+    u32x2 plo;
+    if constexpr (KV == kKvBF16)
+      plo = u32x2{pack2<true>(pr[0] - lo16<true>(pop.x), pr[1] - hi16<true>(pop.x)),
+                  pack2<true>(pr[2] - lo16<true>(pop.y), pr[3] - hi16<true>(pop.y))};
 #pragma unroll
     for (int bb = 0; bb < 8; ++bb) {
       const s16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vsrc + 32 * bb));
       oacc[bb] = mma16x16x16<QBF16>(__builtin_bit_cast(u32x2, vt), pop, oacc[bb]);
+      if constexpr (KV == kKvBF16)
+        oacc[bb] = mma16x16x16<QBF16>(__builtin_bit_cast(u32x2, vt), plo, oacc[bb]);
     }
   };
 
@@ -558,10 +567,14 @@ __device__ __forceinline__ int xcd_tile(int b, int n) {
 template <int KV, bool QBF16, int WAVES, bool PS_POW2, bool APPEND>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(DecodeParams p) {
   using S = PStage<KV>;
-  // append rows may attend a handful of keys, where rounding p to bf16 for
-  // P.V (8 bits) alone moves o by more than the accuracy bar: bf16 append
-  // tiles carry p as a bf16 high part plus a bf16 residual
-  constexpr bool SPLITP = APPEND && QBF16;
+  // bf16 append tiles: P.V takes p as a bf16 high part plus a bf16
+  // residual -- bf16 keeps 8 bits of p, and when a few keys carry
+  // comparable weight (the first rows of a prefill see a handful of keys)
+  // that rounding alone moves o past the accuracy bar.  Cascade prefix tiles
+  // keep one bf16 p: their rows see a long shared prefix, and both the
+  // residual products and a per-tile choice (both paths' registers: 256
+  // VGPRs with spills) cost the MFMA-bound prefix kernel more than a tenth.
+  constexpr bool SPLITP = APPEND && KV == kKvBF16;
   __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
   int* ptab = reinterpret_cast<int*>(lds + 2 * S::BUF);
   const int tid = threadIdx.x;
@@ -638,9 +651,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
   constexpr int T = 64 * WAVES;
   constexpr int PV = 32 * VR;                       // vectors per pool per step
   constexpr int NL = (2 * PV + T - 1) / T;
-  const char* kbase = reinterpret_cast<const char*>(p.k_pages) + (int64_t)h * S::ROWB;
-  const char* vbase = reinterpret_cast<const char*>(p.v_pages) + (int64_t)h * S::ROWB;
-  const uint32_t slot_bytes = (uint32_t)p.Hkv * S::ROWB;
+  const char* kbase = reinterpret_cast<const char*>(p.k_pages) + (int64_t)h * p.head_stride;
+  const char* vbase = reinterpret_cast<const char*>(p.v_pages) + (int64_t)h * p.head_stride;
   const int last = t1 - 1;
   auto load = [&](int tb, u32x4 (&vec)[NL]) {
 #pragma unroll
@@ -652,7 +664,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
       const int pi = page_idx(t);
       const uint32_t sl = PS_POW2 ? (uint32_t)(t & (ps - 1)) : (uint32_t)(t - pi * ps);
       const uint32_t page = (uint32_t)ptab[pi - pfirst];
-      const uint64_t off = ((uint64_t)page * (uint32_t)ps + sl) * slot_bytes + 16 * (q % VR);
+      const uint64_t off =
+          (uint64_t)page * p.page_bytes + sl * p.slot_stride + 16 * (q % VR);
       vec[u] = ld_global<u32x4>(idx < PV ? kbase : vbase, off);
     }
   };
@@ -787,13 +800,19 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
       }
     }
     // ---- P.V on MFMA 16x16x32
+    if constexpr (SPLITP) {
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      oacc[0][b] = mma16x16x32<QBF16>(vop[b], pop[0], oacc[0][b]);
-      oacc[1][b] = mma16x16x32<QBF16>(vop[b], pop[1], oacc[1][b]);
-      if constexpr (SPLITP) {
+      for (int b = 0; b < 8; ++b) {
+        oacc[0][b] = mma16x16x32<QBF16>(vop[b], pop[0], oacc[0][b]);
+        oacc[1][b] = mma16x16x32<QBF16>(vop[b], pop[1], oacc[1][b]);
         oacc[0][b] = mma16x16x32<QBF16>(vop[b], plo[0], oacc[0][b]);
         oacc[1][b] = mma16x16x32<QBF16>(vop[b], plo[1], oacc[1][b]);
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        oacc[0][b] = mma16x16x32<QBF16>(vop[b], pop[0], oacc[0][b]);
+        oacc[1][b] = mma16x16x32<QBF16>(vop[b], pop[1], oacc[1][b]);
       }
     }
   };

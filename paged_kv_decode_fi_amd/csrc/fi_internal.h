@@ -86,6 +86,7 @@ struct HostPlan {
   int32_t append;       // append plan: multi-token queries over each request's keys
   int32_t merge_wide;   // many merge units with few states: the wide merge kernel
   int32_t ragged;       // ragged KV layout
+  int32_t hnd;          // HND pages
   int32_t causal;       // append: causal mask
   int64_t total_q;      // append: query tokens (rows of o)
   int64_t num_req_info; // ReqInfo entries (batch, or total_q for append)
@@ -118,6 +119,7 @@ struct PlanInput {
   const int32_t* append_qo_indptr;   // host [batch + 1] or NULL (decode)
   int32_t causal;
   int32_t ragged;   // rows kv_indptr[r] + t, no page indices
+  int32_t hnd;      // pages head-major: [page][Hkv][page_size][D]
 };
 int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen);
 void plan_free(HostPlan* p);
@@ -148,6 +150,11 @@ struct DecodeParams {
   // ragged KV: token t of a request is row kv_indptr[r] + t (page size 1,
   // kv_indices not read)
   int32_t ragged;
+  // K/V row of (page, slot, kv head) at page * page_bytes + slot *
+  // slot_stride + head * head_stride bytes: NHD pages (slot_stride = Hkv
+  // rows, head_stride = 1 row) or HND pages (slot_stride = 1 row,
+  // head_stride = page_size rows)
+  uint32_t page_bytes, slot_stride, head_stride;
 };
 
 struct MergeParams {

@@ -240,6 +240,7 @@ int plan_append(const PlanInput& in, const std::vector<int64_t>& lens, int num_c
   out->append = 1;
   out->causal = causal ? 1 : 0;
   out->ragged = in.ragged;
+  out->hnd = in.hnd;
   out->merge_wide = mu.size() >= 128 && max_states <= 8;
   out->total_q = total_q;
   out->num_req_info = total_q;
@@ -278,7 +279,11 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
     PLAN_FAIL(2, "group size %d > %d q heads per kv head is not built", G, kMaxGroup);
   if (in.D != kHeadDim) PLAN_FAIL(2, "head_dim %d not built (only %d)", in.D, kHeadDim);
   if (ps <= 0) PLAN_FAIL(1, "page_size must be >= 1 (got %d)", ps);
-  if (in.ragged != 0 && in.ragged != 1) PLAN_FAIL(1, "kv_layout must be FI_KV_PAGED or FI_KV_RAGGED");
+  if ((in.ragged != 0 && in.ragged != 1) || (in.hnd != 0 && in.hnd != 1) ||
+      (in.ragged && in.hnd))
+    PLAN_FAIL(1, "kv_layout must be FI_KV_PAGED, FI_KV_RAGGED or FI_KV_PAGED_HND");
+  if ((int64_t)ps * Hkv * kHeadDim * 2 > 0x7fffffff)
+    PLAN_FAIL(2, "a page of %d tokens x %d kv heads is too large", ps, Hkv);
   if (in.ragged && ps != 1) PLAN_FAIL(1, "a ragged KV layout has page_size 1 (got %d)", ps);
   const int32_t* last_tab = in.ragged ? nullptr : in.last_page_len;
   if (B > 0 && (!in.kv_indptr || (!in.ragged && !in.last_page_len)))
@@ -554,6 +559,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   out->num_req_info = B;
   out->qo_len = NG + 1;
   out->ragged = in.ragged;
+  out->hnd = in.hnd;
 
   WorkspaceLayout& L = out->layout;
   size_t off = 0;

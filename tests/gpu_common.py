@@ -56,6 +56,10 @@ def is_ragged(w):
     return bool(w.meta.get("ragged"))
 
 
+def is_hnd(w):
+    return bool(w.meta.get("hnd"))
+
+
 def make_plan(w, chunk_tokens=0, cascade=None, rope=None):
     """rope = None or (theta, scale): a plan with LLaMA-style RoPE."""
     import paged_kv_decode_fi_amd as fi
@@ -69,7 +73,8 @@ def make_plan(w, chunk_tokens=0, cascade=None, rope=None):
                    pos_encoding="none" if rope is None else "rope_llama",
                    rope_theta=0.0 if rope is None else rope[0],
                    rope_scale=0.0 if rope is None else rope[1],
-                   kv_layout="ragged" if is_ragged(w) else "paged")
+                   kv_layout="ragged" if is_ragged(w) else
+                   "paged_hnd" if is_hnd(w) else "paged")
 
 
 def run_gpu(w, d=None, plan=None, chunk_tokens=0, rope=None):
@@ -91,7 +96,7 @@ def run_gpu(w, d=None, plan=None, chunk_tokens=0, rope=None):
 def run_oracle(w, unit_mask=None, rope=None):
     import oracle
     ragged = is_ragged(w)
-    kw = dict(rope=rope, num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
+    kw = dict(rope=rope, kv_layout="HND" if is_hnd(w) else "NHD", num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
               head_dim=w.head_dim, page_size=w.page_size, q_dtype=w.q_dtype,
               kv_dtype=w.kv_dtype, sm_scale=w.sm_scale, k_scale=w.k_scale,
               v_scale=w.v_scale, unit_mask=unit_mask)

@@ -408,3 +408,14 @@ def to_ragged(w: Paged) -> Paged:
         r.prefix_last_page_len = None
     r.meta = dict(w.meta, ragged=True)
     return r
+
+
+def to_hnd(w: Paged) -> Paged:
+    """The same problem with head-major (HND) pages [num_pages][Hkv][ps][D]."""
+    import copy
+    r = copy.copy(w)
+    r.name = w.name + "_hnd"
+    r.k_pages = np.ascontiguousarray(w.k_pages.transpose(0, 2, 1, 3))
+    r.v_pages = np.ascontiguousarray(w.v_pages.transpose(0, 2, 1, 3))
+    r.meta = dict(w.meta, hnd=True)
+    return r
