@@ -23,10 +23,13 @@
  *
  * Layouts (all row-major, all device pointers unless marked host):
  *   q, o          [batch][num_qo_heads][head_dim], dtype q_dtype (o = q dtype)
+ *                 (append plans: [total_q][num_qo_heads][head_dim])
  *   lse           [batch][num_qo_heads] fp32 (may be NULL)
  *   k_pages,
  *   v_pages       [num_pages][page_size][num_kv_heads][head_dim] ("NHD"),
- *                 dtype kv_dtype; separate K and V pools
+ *                 dtype kv_dtype; separate K and V pools (fi_problem's
+ *                 kv_layout also selects head-major "HND" pages or the
+ *                 ragged layout)
  *   k_scale,
  *   v_scale       [num_kv_heads] fp32 for E4M3 KV (dequantised value =
  *                 decode(code) * scale[kv_head]; NULL means 1.0), ignored
@@ -36,10 +39,10 @@
  * schedules variable-length work on the host to balance load; the run stage
  * executes it): fi_plan() turns the host-side lengths into a work list of
  * (request, kv head, token chunk) tiles and uploads it into a caller-owned
- * device workspace; fi_decode_run() / fi_cascade_decode() then only enqueue
- * kernels on the caller's stream -- no allocation, no synchronisation, no
- * host reads -- so they may be captured into a hipGraph (README "core
- * features" item 5).  Re-plan whenever kv_indptr or last_page_len change;
+ * device workspace; fi_decode_run() / fi_cascade_decode() / fi_append_run()
+ * then only enqueue kernels on the caller's stream -- no allocation, no
+ * synchronisation, no host reads -- so they may be captured into a hipGraph
+ * (README "core features" item 5).  Re-plan whenever kv_indptr or last_page_len change;
  * kv_indices contents and K/V data may change freely between runs.
  *
  * Ownership: the caller owns every device buffer and the stream.  The
@@ -55,7 +58,9 @@
  * trusted: they must describe the same tables that were planned.
  *
  * Supported: head_dim 128; q in fp16 or bf16; KV in the q dtype or OCP E4M3
- * (e4m3fn); 1 <= num_qo_heads / num_kv_heads <= 16; any page_size >= 1.
+ * (e4m3fn); 1 <= num_qo_heads / num_kv_heads <= 16; any page_size >= 1;
+ * LLaMA-style RoPE on the fly for plain decode; batch append (causal or
+ * not) on the same page tables.
  */
 #ifndef FI_DECODE_H_
 #define FI_DECODE_H_

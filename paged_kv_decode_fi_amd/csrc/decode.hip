@@ -1,4 +1,5 @@
-// decode.hip -- gfx950 paged decode attention and cascade prefix kernels.
+// decode.hip -- gfx950 paged decode attention, cascade prefix and append
+// kernels.
 //
 // Computes, for one query token per head, exact attention over the keys a
 // request reaches through its page table (FlashInfer README "core features"
@@ -29,9 +30,16 @@
 //  * A tile whose (request, kv head) is split over several chunks writes an
 //    fp32 partial state (o, log2-domain lse) that merge.hip combines; a
 //    cascade suffix tile folds its request's prefix states in instead.
-//  * prefix_kernel (cascade): many query rows (the G heads of every request
-//    of a group) against one chunk of the shared prefix, K/V staged in LDS
-//    and shared by 8 waves x 32 rows; described above the kernel.
+//  * LLaMA-style RoPE (README decode example, pos_encoding_mode): the
+//    decode kernel turns each key by its distance from the query before the
+//    score MFMAs (described above rope_key8).
+//  * prefix_kernel: many query rows against one chunk of one key list, K/V
+//    staged in LDS and shared by 8 waves x 32 rows -- the G heads of every
+//    request of a cascade group against the shared prefix, or the query
+//    tokens of an append request (README append example, causal mask)
+//    against its own keys; described above the kernel.
+//  * K/V rows are addressed by page, slot and head strides: NHD or HND
+//    pages, or the ragged layout (page size 1, no page table).
 #include <type_traits>
 
 #include "fi_device.h"
