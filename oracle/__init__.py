@@ -73,6 +73,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_cascade.restype = I
         L.oracle_cascade.argtypes = [I, I, I, I, I, I, I, P, P, P, I, P, P, P, P,
                                      P, P, P, P, P, D, P, P, P, I, I, D, D, I]
+        L.oracle_cascade_levels.restype = I
+        L.oracle_cascade_levels.argtypes = [I, I, I, I, I, I, I, P, P, P, I, P, P, P, P, P,
+                                            P, P, P, P, P, D, P, P, P, I, I, D, D, I]
         L.oracle_append.restype = I
         L.oracle_append.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P,
                                     D, I, P, P, P, I, I, D, D, I]
@@ -178,6 +181,48 @@ def decode(q, k_pages, v_pages, kv_indptr, kv_indices, last_page_len, *,
                              _hnd(kv_layout))
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments")
+    return o, lse
+
+
+def cascade_levels(q, k_pages, v_pages, levels, kv_indptr, kv_indices, last_page_len, *,
+                   num_qo_heads, num_kv_heads, head_dim, page_size, q_dtype, kv_dtype,
+                   sm_scale, k_scale=None, v_scale=None, unit_mask=None, threads=None,
+                   rope=None, kv_layout="NHD"):
+    """fp64 multi-level cascade: levels = [(qo_indptr, kv_indptr, kv_indices,
+    last_page_len), ...] outermost first (qo_indptr partitions the requests
+    into contiguous groups); request r attends over its group's prefix at
+    every level in order, then its own pages."""
+    indptr = _c(kv_indptr, np.int32)
+    B = len(indptr) - 1
+    o = np.zeros((B, num_qo_heads, head_dim), np.float64)
+    lse = np.full((B, num_qo_heads), np.nan, np.float64)
+    keep = []
+    ptrs = {k: [] for k in ("qo", "ip", "ix", "la")}
+    ng = []
+    for (qo, ip, ix, la) in levels:
+        arrs = [_c(qo, np.int32), _c(ip, np.int32), _c(ix, np.int32), _c(la, np.int32)]
+        keep += arrs
+        ng.append(len(arrs[0]) - 1)
+        for key, a in zip(("qo", "ip", "ix", "la"), arrs):
+            ptrs[key].append(_ptr(a))
+    nl = len(levels)
+    PP = ctypes.c_void_p * max(nl, 1)
+    cp = {k: PP(*v) for k, v in ptrs.items()}
+    ng_a = np.asarray(ng if ng else [0], np.int32)
+    a = [_c(q), _c(k_pages), _c(v_pages), indptr, _c(kv_indices, np.int32),
+         _c(last_page_len, np.int32), _c(k_scale, np.float32), _c(v_scale, np.float32),
+         _c(unit_mask, np.uint8)]
+    rc = lib().oracle_cascade_levels(
+        B, num_qo_heads, num_kv_heads, head_dim, page_size, DTYPE_CODE[q_dtype],
+        DTYPE_CODE[kv_dtype], _ptr(a[0]), _ptr(a[1]), _ptr(a[2]), nl, _ptr(ng_a),
+        ctypes.cast(cp["qo"], ctypes.c_void_p), ctypes.cast(cp["ip"], ctypes.c_void_p),
+        ctypes.cast(cp["ix"], ctypes.c_void_p), ctypes.cast(cp["la"], ctypes.c_void_p),
+        _ptr(a[3]), _ptr(a[4]), _ptr(a[5]), _ptr(a[6]), _ptr(a[7]), float(sm_scale),
+        _ptr(a[8]), _ptr(o), _ptr(lse), threads or default_threads(), *_rope_args(rope),
+        _hnd(kv_layout))
+    del keep
+    if rc != 0:
+        raise ValueError("oracle_cascade_levels rejected its arguments")
     return o, lse
 
 

@@ -59,6 +59,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#define ORACLE_MAX_LEVELS 8
+
 /* dtype codes used by this file's own entry points */
 enum { OR_F16 = 0, OR_BF16 = 1, OR_E4M3 = 2, OR_F32 = 3, OR_F64 = 4 };
 
@@ -241,9 +243,13 @@ typedef struct {
   const void* v_pages;
   /* level 0: per-request table (always present) */
   const int32_t *indptr, *indices, *last;
-  /* optional level 1: shared prefix per group of contiguous requests */
-  int n_groups;
-  const int32_t *qo_indptr, *p_indptr, *p_indices, *p_last;
+  /* optional shared levels, outermost first: level l splits the requests
+   * into groups of contiguous requests, each sharing a prefix table */
+  int n_levels;
+  struct {
+    int n_groups;
+    const int32_t *qo_indptr, *p_indptr, *p_indices, *p_last;
+  } lv[ORACLE_MAX_LEVELS];
   const float *k_scale, *v_scale;
   double sm_scale;
   rope_t rope;
@@ -258,9 +264,9 @@ typedef struct {
   int64_t max_len;
 } job_t;
 
-static int group_of(const job_t* J, int r) {
-  for (int g = 0; g < J->n_groups; ++g)
-    if (r >= J->qo_indptr[g] && r < J->qo_indptr[g + 1]) return g;
+static int group_of(const job_t* J, int l, int r) {
+  for (int g = 0; g < J->lv[l].n_groups; ++g)
+    if (r >= J->lv[l].qo_indptr[g] && r < J->lv[l].qo_indptr[g + 1]) return g;
   return -1;
 }
 
@@ -276,13 +282,16 @@ static void run_item(const job_t* J, int r, int h, int64_t* rows, double* x,
                      double* qv) {
   const int G = J->Hq / J->Hkv, D = J->D;
   int64_t L = 0;
-  /* key list = (prefix tokens of the request's group) ++ (its own tokens);
-   * decode has no mask, so the order only fixes the summation order. */
-  int g = J->n_groups > 0 ? group_of(J, r) : -1;
-  if (g >= 0) {
-    int64_t Lp = request_len(J->p_indptr, J->p_last, g, J->ps);
+  /* key list = (prefix tokens of the request's group at each shared level,
+   * outermost first) ++ (its own tokens); decode has no mask, so the order
+   * only fixes the summation order (and, with RoPE, the positions). */
+  for (int l = 0; l < J->n_levels; ++l) {
+    const int g = group_of(J, l, r);
+    if (g < 0) continue;
+    const int64_t Lp = request_len(J->lv[l].p_indptr, J->lv[l].p_last, g, J->ps);
     for (int64_t t = 0; t < Lp; ++t)
-      rows[L++] = row_offset(J, token_slot(J->p_indptr, J->p_indices, g, t, J->ps), h);
+      rows[L++] = row_offset(
+          J, token_slot(J->lv[l].p_indptr, J->lv[l].p_indices, g, t, J->ps), h);
   }
   int64_t Ls = request_len(J->indptr, J->last, r, J->ps);
   for (int64_t t = 0; t < Ls; ++t)
@@ -338,7 +347,9 @@ static int run_job(job_t* J, int num_threads) {
   if (J->rope.on && !(J->rope.theta > 0.0 && J->rope.scale > 0.0)) return -1;
   /* a level is either paged (indices and last) or ragged (neither) */
   if ((J->indices == NULL) != (J->last == NULL)) return -1;
-  if (J->n_groups > 0 && ((J->p_indices == NULL) != (J->p_last == NULL))) return -1;
+  if (J->n_levels < 0 || J->n_levels > ORACLE_MAX_LEVELS) return -1;
+  for (int l = 0; l < J->n_levels; ++l)
+    if ((J->lv[l].p_indices == NULL) != (J->lv[l].p_last == NULL)) return -1;
   J->max_len = 0;
   for (int r = 0; r < J->batch; ++r) {
     int64_t L = request_len(J->indptr, J->last, r, J->ps);
@@ -346,8 +357,10 @@ static int run_job(job_t* J, int num_threads) {
       const int64_t n = (int64_t)J->app_qo_indptr[r + 1] - J->app_qo_indptr[r];
       if (n < 0 || n > L) return -1;
     }
-    int g = J->n_groups > 0 ? group_of(J, r) : -1;
-    if (g >= 0) L += request_len(J->p_indptr, J->p_last, g, J->ps);
+    for (int l = 0; l < J->n_levels; ++l) {
+      const int g = group_of(J, l, r);
+      if (g >= 0) L += request_len(J->lv[l].p_indptr, J->lv[l].p_last, g, J->ps);
+    }
     if (L > J->max_len) J->max_len = L;
   }
   J->next = 0;
@@ -410,9 +423,46 @@ int oracle_cascade(int batch, int num_qo_heads, int num_kv_heads, int head_dim,
   J.ps = page_size; J.q_dtype = q_dtype; J.kv_dtype = kv_dtype;
   J.q = q; J.k_pages = k_pages; J.v_pages = v_pages;
   J.indptr = kv_indptr; J.indices = kv_indices; J.last = last_page_len;
-  J.n_groups = n_groups; J.qo_indptr = prefix_qo_indptr;
-  J.p_indptr = prefix_kv_indptr; J.p_indices = prefix_kv_indices;
-  J.p_last = prefix_last_page_len;
+  J.n_levels = n_groups > 0 ? 1 : 0;
+  J.lv[0].n_groups = n_groups; J.lv[0].qo_indptr = prefix_qo_indptr;
+  J.lv[0].p_indptr = prefix_kv_indptr; J.lv[0].p_indices = prefix_kv_indices;
+  J.lv[0].p_last = prefix_last_page_len;
+  J.k_scale = k_scale; J.v_scale = v_scale; J.sm_scale = sm_scale;
+  J.unit_mask = unit_mask; J.o = o; J.lse = lse;
+  return run_job(&J, num_threads);
+}
+
+/* Multi-level cascade: n_levels shared levels, outermost first; level l has
+ * n_groups[l] groups of contiguous requests (qo_indptr[l]) with prefix
+ * tables indptr[l] / indices[l] / last[l]; request r attends over the
+ * prefix of its group at every level, in level order, then its own pages --
+ * the flat decode over the concatenated key list. */
+int oracle_cascade_levels(int batch, int num_qo_heads, int num_kv_heads, int head_dim,
+                          int page_size, int q_dtype, int kv_dtype, const void* q,
+                          const void* k_pages, const void* v_pages, int n_levels,
+                          const int32_t* n_groups, const int32_t* const* qo_indptr,
+                          const int32_t* const* p_indptr, const int32_t* const* p_indices,
+                          const int32_t* const* p_last, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, const int32_t* last_page_len,
+                          const float* k_scale, const float* v_scale, double sm_scale,
+                          const uint8_t* unit_mask, double* o, double* lse,
+                          int num_threads, int rope, double rope_theta, double rope_scale,
+                          int hnd) {
+  if (n_levels < 0 || n_levels > ORACLE_MAX_LEVELS) return -1;
+  job_t J;
+  memset(&J, 0, sizeof(J));
+  J.hnd = hnd;
+  J.rope.on = rope; J.rope.theta = rope_theta; J.rope.scale = rope_scale;
+  J.batch = batch; J.Hq = num_qo_heads; J.Hkv = num_kv_heads; J.D = head_dim;
+  J.ps = page_size; J.q_dtype = q_dtype; J.kv_dtype = kv_dtype;
+  J.q = q; J.k_pages = k_pages; J.v_pages = v_pages;
+  J.indptr = kv_indptr; J.indices = kv_indices; J.last = last_page_len;
+  J.n_levels = n_levels;
+  for (int l = 0; l < n_levels; ++l) {
+    J.lv[l].n_groups = n_groups[l]; J.lv[l].qo_indptr = qo_indptr[l];
+    J.lv[l].p_indptr = p_indptr[l]; J.lv[l].p_indices = p_indices[l];
+    J.lv[l].p_last = p_last[l];
+  }
   J.k_scale = k_scale; J.v_scale = v_scale; J.sm_scale = sm_scale;
   J.unit_mask = unit_mask; J.o = o; J.lse = lse;
   return run_job(&J, num_threads);

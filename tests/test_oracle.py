@@ -756,3 +756,65 @@ def test_hnd_pages_equal_nhd_pages_transposed(oracle_lib):
     b = oracle_lib.cascade(q, kh, vh, qo_g, p_ip, idx[ip[2]:ip[3]], last[2:3], ip, idx, last,
                            kv_layout="HND", **kw)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ------------------------------------------------------ multi-level cascade
+# README "core features" item 3: cascade attention over a hierarchical KV
+# cache; here with several shared levels (outermost first), each splitting
+# the requests into contiguous groups that share a prefix.
+
+def test_multilevel_cascade_is_flat_over_concatenated_keys(oracle_lib):
+    rng = np.random.default_rng(97)
+    Hq, Hkv, D, ps = 4, 2, 32, 4
+    own_lens = [3, 0, 9, 5, 1]
+    B = len(own_lens)
+    # level 0: one group of all requests; level 1: groups {0,1}, {2,3,4}
+    # (not nested in anything but level 0); level 2: {0}, {1,2}, {3,4}
+    levels_groups = [[(0, 5)], [(0, 2), (2, 5)], [(0, 1), (1, 3), (3, 5)]]
+    prefix_lens = [[6], [4, 0], [2, 7, 3]]
+    dense = []
+    level_dense = []
+    for lg, pl in zip(levels_groups, prefix_lens):
+        level_dense.append([to_f16_bits(rng.standard_normal((L, Hkv, D))) for L in pl])
+    own = [to_f16_bits(rng.standard_normal((L, Hkv, D))) for L in own_lens]
+    q = to_f16_bits(rng.standard_normal((B, Hq, D)))
+    # one pool holding every list: level prefixes, then own lists
+    lists = [x for ld in level_dense for x in ld] + own
+    pool, ip_all, idx_all, last_all = paginate(lists, ps, Hkv, D, np.random.default_rng(5))
+    levels = []
+    k = 0
+    for lg, ld in zip(levels_groups, level_dense):
+        n = len(ld)
+        sub = slice(k, k + n)
+        ip = (ip_all[k:k + n + 1] - ip_all[k]).astype(np.int32)
+        ix = idx_all[ip_all[k]:ip_all[k + n]]
+        qo = np.array([lg[0][0]] + [g[1] for g in lg], np.int32)
+        levels.append((qo, ip, ix, last_all[sub]))
+        k += n
+    own_ip = (ip_all[k:] - ip_all[k]).astype(np.int32)
+    own_ix = idx_all[ip_all[k]:]
+    kw = dict(num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=ps, q_dtype="f16",
+              kv_dtype="f16", sm_scale=0.17)
+    o_m, l_m = oracle_lib.cascade_levels(q, pool, pool, levels, own_ip, own_ix, last_all[k:], **kw)
+    # flat: each request's concatenated list
+    flat = []
+    for r in range(B):
+        parts = []
+        for li, lg in enumerate(levels_groups):
+            g = [gi for gi, (a, b) in enumerate(lg) if a <= r < b][0]
+            parts.append(level_dense[li][g])
+        parts.append(own[r])
+        flat.append(np.concatenate(parts))
+    fpool, fip, fix, flast = paginate(flat, ps, Hkv, D, np.random.default_rng(6))
+    o_f, l_f = oracle_lib.decode(q, fpool, fpool, fip, fix, flast, **kw)
+    assert np.array_equal(o_m, o_f) and np.array_equal(l_m, l_f)
+    # one level through the multi-level entry = the single-level cascade
+    lv = levels[1]
+    o1, l1 = oracle_lib.cascade_levels(q, pool, pool, [lv], own_ip, own_ix, last_all[k:], **kw)
+    o2, l2 = oracle_lib.cascade(q, pool, pool, lv[0], lv[1], lv[2], lv[3], own_ip, own_ix,
+                                last_all[k:], **kw)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # no shared level = plain decode
+    o0, l0 = oracle_lib.cascade_levels(q, pool, pool, [], own_ip, own_ix, last_all[k:], **kw)
+    od, ld = oracle_lib.decode(q, pool, pool, own_ip, own_ix, last_all[k:], **kw)
+    assert np.array_equal(o0, od) and np.array_equal(l0, ld)
