@@ -87,6 +87,17 @@ typedef enum {
   FI_F32 = 3
 } fi_dtype;
 
+/* One shared cascade level (host tables): num_groups groups of CONTIGUOUS
+ * requests, group g = requests [qo_indptr[g], qo_indptr[g+1]) sharing the
+ * prefix table kv_indptr[g] .. (pages as the per-request table, or rows in
+ * the ragged layout) with last_page_len[g]. */
+typedef struct {
+  int32_t num_groups;
+  const int32_t* qo_indptr;       /* host [num_groups+1], [0] = 0, [num_groups] = B */
+  const int32_t* kv_indptr;       /* host [num_groups+1] */
+  const int32_t* last_page_len;   /* host [num_groups] (NULL when ragged) */
+} fi_cascade_level;
+
 /* Problem description; every pointer here is HOST memory, read during the
  * fi_plan() call only. */
 typedef struct {
@@ -145,6 +156,13 @@ typedef struct {
    * FI_KV_PAGED but head-major, [num_pages][Hkv][page_size][D] (the other
    * value of the registry quickstart's kv_layout argument). */
   int32_t kv_layout;
+  /* Several shared cascade levels (README "core features" item 3: cascade
+   * attention over a hierarchical KV cache), outermost first: request r
+   * attends over its group's prefix at every level in order, then its own
+   * pages.  Give either these (num_prefix_groups = 0) or the single-level
+   * fields above; run with fi_cascade_decode_levels.  At most 8 levels. */
+  int32_t num_cascade_levels;
+  const fi_cascade_level* cascade_levels;   /* host [num_cascade_levels] */
 } fi_problem;
 
 enum { FI_POS_NONE = 0, FI_POS_ROPE_LLAMA = 1 };
@@ -222,6 +240,25 @@ fi_status fi_cascade_decode(fi_plan_t plan, const void* q, const void* k_pages,
                             const int32_t* last_page_len,
                             const float* k_scale, const float* v_scale,
                             float sm_scale, void* o, float* lse, void* stream);
+
+/* Run stage: cascade decode with the plan's num_levels shared levels
+ * (fi_problem.cascade_levels, outermost first): level l's prefix tiles read
+ * DEVICE tables level_kv_indptr[l] / level_kv_indices[l] /
+ * level_last_page_len[l] (the three arrays are HOST arrays of num_levels
+ * device pointers); the states of every level and of the request's own
+ * pages are merged (folded into a one-chunk suffix tile, or by the merge
+ * pass).  Enqueues one prefix kernel per level with tiles, the suffix
+ * decode and the merge; capturable.  Errors as fi_cascade_decode, plus
+ * FI_ERR_INVALID_ARG when num_levels differs from the plan's. */
+fi_status fi_cascade_decode_levels(fi_plan_t plan, const void* q, const void* k_pages,
+                                   const void* v_pages, int32_t num_levels,
+                                   const int32_t* const* level_kv_indptr,
+                                   const int32_t* const* level_kv_indices,
+                                   const int32_t* const* level_last_page_len,
+                                   const int32_t* kv_indptr, const int32_t* kv_indices,
+                                   const int32_t* last_page_len, const float* k_scale,
+                                   const float* v_scale, float sm_scale, void* o, float* lse,
+                                   void* stream);
 
 /* Run stage: batch append attention (README append example; see
  * fi_problem.qo_indptr): every query token of request r attends over r's

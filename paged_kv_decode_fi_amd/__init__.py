@@ -27,13 +27,19 @@ STATUS = {0: "FI_OK", 1: "FI_ERR_INVALID_ARG", 2: "FI_ERR_UNSUPPORTED",
 EXPORTS = ("fi_plan", "fi_plan_destroy", "fi_plan_get_stats", "fi_decode_run",
            "fi_cascade_decode", "fi_merge_states", "fi_status_string",
            "fi_last_error", "fi_debug_plan_tiles", "fi_debug_gather",
-           "fi_debug_stream_read", "fi_debug_run_stage", "fi_append_run")
+           "fi_debug_stream_read", "fi_debug_run_stage", "fi_append_run",
+           "fi_cascade_decode_levels")
 
 
 class FiError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS.get(status, status)}: {message}")
         self.status = status
+
+
+class CascadeLevel(ctypes.Structure):
+    _fields_ = [("num_groups", ctypes.c_int32), ("qo_indptr", ctypes.c_void_p),
+                ("kv_indptr", ctypes.c_void_p), ("last_page_len", ctypes.c_void_p)]
 
 
 class Problem(ctypes.Structure):
@@ -49,7 +55,8 @@ class Problem(ctypes.Structure):
                 ("chunk_tokens", ctypes.c_int32), ("pos_encoding", ctypes.c_int32),
                 ("rope_theta", ctypes.c_float), ("rope_scale", ctypes.c_float),
                 ("qo_indptr", ctypes.c_void_p), ("causal", ctypes.c_int32),
-                ("kv_layout", ctypes.c_int32)]
+                ("kv_layout", ctypes.c_int32), ("num_cascade_levels", ctypes.c_int32),
+                ("cascade_levels", ctypes.c_void_p)]
 
 
 class PlanStats(ctypes.Structure):
@@ -87,6 +94,8 @@ def _load() -> ctypes.CDLL:
     L.fi_cascade_decode.restype = ctypes.c_int
     L.fi_append_run.restype = ctypes.c_int
     L.fi_append_run.argtypes = [P, P, P, P, P, P, P, P, P, F, P, P, P]
+    L.fi_cascade_decode_levels.restype = ctypes.c_int
+    L.fi_cascade_decode_levels.argtypes = [P, P, P, P, I32, P, P, P, P, P, P, P, P, F, P, P, P]
     L.fi_cascade_decode.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, F, P, P, P]
     L.fi_debug_run_stage.restype = ctypes.c_int
     L.fi_debug_run_stage.argtypes = [P, I32, P, P, P, P, P, P, P, P, P, P, P, F, P, P, P]
@@ -184,8 +193,20 @@ KV_LAYOUTS = {"paged": 0, "ragged": 1, "paged_hnd": 2}
 
 def _problem(batch, Hq, Hkv, D, ps, q_dtype, kv_dtype, indptr, last, prefix, chunk,
              pos_encoding="none", rope_theta=0.0, rope_scale=0.0, qo_indptr=None, causal=True,
-             kv_layout="paged"):
+             kv_layout="paged", levels=None):
     pr = Problem()
+    lv_keep = []
+    if levels:
+        arr = (CascadeLevel * len(levels))()
+        for i, (qo, ip, la) in enumerate(levels):
+            qo, ip, la = _host_i32(qo), _host_i32(ip), _host_i32(la)
+            arr[i].num_groups = len(qo) - 1
+            arr[i].qo_indptr, arr[i].kv_indptr = _np_ptr(qo), _np_ptr(ip)
+            arr[i].last_page_len = _np_ptr(la) if la is not None else None
+            lv_keep += [qo, ip, la]
+        pr.num_cascade_levels = len(levels)
+        pr.cascade_levels = ctypes.cast(arr, ctypes.c_void_p)
+        lv_keep.append(arr)
     pr.kv_layout = KV_LAYOUTS[kv_layout]
     if qo_indptr is not None:
         qo_indptr = _host_i32(qo_indptr)
@@ -198,7 +219,7 @@ def _problem(batch, Hq, Hkv, D, ps, q_dtype, kv_dtype, indptr, last, prefix, chu
     pr.kv_indptr = _np_ptr(indptr)
     pr.last_page_len = _np_ptr(last) if last is not None else None
     pr.chunk_tokens = chunk
-    keep = [indptr, last, qo_indptr]
+    keep = [indptr, last, qo_indptr] + lv_keep
     if prefix is not None:
         qo, pip, plast = (_host_i32(x) for x in prefix)   # plast None when ragged
         pr.num_prefix_groups = len(qo) - 1
@@ -212,14 +233,14 @@ def debug_plan_tiles(kv_indptr, last_page_len, *, num_qo_heads, num_kv_heads,
                      page_size, head_dim=128, q_dtype="f16", kv_dtype="f16",
                      prefix=None, num_cus=256, chunk_tokens=0,
                      pos_encoding="none", qo_indptr=None, causal=True,
-                     kv_layout="paged") -> np.ndarray:
+                     kv_layout="paged", levels=None) -> np.ndarray:
     """Host-only: the plan's work list as an int32 [n, 8] array (request,
     kv_head0, t0, t1, slot, kind, row0, row1)."""
     indptr, last = _host_i32(kv_indptr), _host_i32(last_page_len)
     pr, keep = _problem(len(indptr) - 1, num_qo_heads, num_kv_heads, head_dim,
                         page_size, q_dtype, kv_dtype, indptr, last, prefix, chunk_tokens,
                         pos_encoding, qo_indptr=qo_indptr, causal=causal,
-                        kv_layout=kv_layout)
+                        kv_layout=kv_layout, levels=levels)
     n = ctypes.c_int64(0)
     _check(_get_lib().fi_debug_plan_tiles(ctypes.byref(pr), num_cus, None, 0, ctypes.byref(n)))
     out = np.zeros((max(n.value, 1), 8), np.int32)
@@ -242,13 +263,15 @@ class Plan:
     with Plan.append_run.  kv_layout="ragged": each request's tokens are
     contiguous rows kv_indptr[r] .. kv_indptr[r+1]-1 of K and V (page_size 1,
     last_page_len and kv_indices may be None); "paged_hnd": head-major pages
-    [num_pages][Hkv][page_size][D]."""
+    [num_pages][Hkv][page_size][D].  levels = [(qo_indptr, kv_indptr,
+    last_page_len), ...] host tables of several shared cascade levels,
+    outermost first (in place of prefix); run with Plan.cascade_run_levels."""
 
     def __init__(self, kv_indptr, last_page_len, *, num_qo_heads, num_kv_heads,
                  page_size, head_dim=128, q_dtype="f16", kv_dtype="f16",
                  prefix=None, num_cus=0, chunk_tokens=0, device=None, stream=None,
                  pos_encoding="none", rope_theta=0.0, rope_scale=0.0, qo_indptr=None,
-                 causal=True, kv_layout="paged"):
+                 causal=True, kv_layout="paged", levels=None):
         import torch
         self.indptr = _host_i32(kv_indptr)
         self.last = _host_i32(last_page_len)
@@ -256,7 +279,8 @@ class Plan:
         self.num_qo_heads, self.num_kv_heads = num_qo_heads, num_kv_heads
         self.head_dim, self.page_size = head_dim, page_size
         self.q_dtype, self.kv_dtype = q_dtype, kv_dtype
-        self.cascade = prefix is not None
+        self.cascade = prefix is not None or bool(levels)
+        self.num_levels = len(levels) if levels else (1 if prefix is not None else 0)
         self.pos_encoding = pos_encoding
         self.append = qo_indptr is not None
         self.qo_indptr = _host_i32(qo_indptr) if self.append else None
@@ -265,7 +289,7 @@ class Plan:
         pr, keep = _problem(self.batch, num_qo_heads, num_kv_heads, head_dim,
                             page_size, q_dtype, kv_dtype, self.indptr, self.last,
                             prefix, chunk_tokens, pos_encoding, rope_theta, rope_scale,
-                            self.qo_indptr, causal, kv_layout)
+                            self.qo_indptr, causal, kv_layout, levels)
         need = ctypes.c_size_t(0)
         _check(_get_lib().fi_plan(ctypes.byref(pr), num_cus, None, 0, ctypes.byref(need), None,
                            None))
@@ -361,6 +385,31 @@ class Plan:
                      (prefix_kv_indptr, prefix_kv_indices, prefix_last_page_len)),
             *_scales(k_scale, v_scale), float(sm_scale), _ptr(o, "o"), _ptr(lse, "lse"),
             _stream(stream)))
+        return o, lse
+
+    def cascade_run_levels(self, q, k_pages, v_pages, level_tables, kv_indptr, kv_indices,
+                           last_page_len, k_scale=None, v_scale=None, sm_scale: float = 0.0,
+                           o=None, lse=None, stream=None):
+        """Cascade decode over several shared levels: level_tables =
+        [(kv_indptr, kv_indices, last_page_len), ...] device tensors,
+        outermost first.  Returns (o, lse)."""
+        import torch
+        if len(level_tables) != self.num_levels:
+            raise ValueError(f"the plan has {self.num_levels} levels")
+        self._check_q(q)
+        self._check_pool(k_pages, v_pages)
+        o, lse = self._outputs(q, o, lse)
+        n = max(len(level_tables), 1)
+        arrs = [(ctypes.c_void_p * n)() for _ in range(3)]
+        for i, (ip, ix, la) in enumerate(level_tables):
+            arrs[0][i] = _ptr(ip, f"level {i} kv_indptr", torch.int32)
+            arrs[1][i] = _ptr(ix, f"level {i} kv_indices", torch.int32)
+            arrs[2][i] = _ptr(la, f"level {i} last_page_len", torch.int32)
+        _check(_get_lib().fi_cascade_decode_levels(
+            self.handle, _ptr(q, "q"), _ptr(k_pages, "k_pages"), _ptr(v_pages, "v_pages"),
+            len(level_tables), *(ctypes.cast(a, ctypes.c_void_p) for a in arrs),
+            *_tables(kv_indptr, kv_indices, last_page_len), *_scales(k_scale, v_scale),
+            float(sm_scale), _ptr(o, "o"), _ptr(lse, "lse"), _stream(stream)))
         return o, lse
 
     def run_stage(self, stage, q, k_pages, v_pages, kv_indptr, kv_indices, last_page_len,

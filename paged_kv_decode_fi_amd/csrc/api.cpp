@@ -86,10 +86,21 @@ fi::PlanInput to_input(const fi_problem* p, int num_cus) {
   in.kv_dtype = p->kv_dtype;
   in.kv_indptr = p->kv_indptr;
   in.last_page_len = p->last_page_len;
-  in.num_groups = p->num_prefix_groups;
-  in.qo_indptr = p->prefix_qo_indptr;
-  in.p_indptr = p->prefix_kv_indptr;
-  in.p_last = p->prefix_last_page_len;
+  // shared cascade levels: the single-level fields, or the level array
+  in.num_levels = 0;
+  if (p->num_cascade_levels > 0 && p->num_prefix_groups == 0) {
+    in.num_levels = p->cascade_levels ? p->num_cascade_levels : -1;
+    if (!p->cascade_levels) return in;
+    for (int l = 0; l < p->num_cascade_levels && l < fi::kMaxLevels; ++l) {
+      const fi_cascade_level& c = p->cascade_levels[l];
+      in.levels[l] = {c.num_groups, c.qo_indptr, c.kv_indptr, c.last_page_len};
+    }
+  } else if (p->num_cascade_levels > 0 || p->num_prefix_groups != 0) {
+    in.num_levels = 1;
+    in.levels[0] = {p->num_prefix_groups, p->prefix_qo_indptr, p->prefix_kv_indptr,
+                    p->prefix_last_page_len};
+    if (p->num_cascade_levels > 0) in.num_levels = -1;   // both forms given: rejected
+  }
   in.chunk_tokens = p->chunk_tokens;
   in.num_cus = num_cus;
   in.pos_encoding = p->pos_encoding;
@@ -247,6 +258,9 @@ fi_status fi_plan(const fi_problem* problem, int32_t num_cus, void* workspace,
   memcpy(st8 + hp.layout.merge_reqs_off, hp.merge_units,
          sizeof(fi::MergeUnit) * hp.num_merge_units);
   memcpy(st8 + hp.layout.qo_indptr_off, hp.qo_indptr, sizeof(int32_t) * hp.qo_len);
+  if (hp.num_levels >= 2)
+    memcpy(st8 + hp.layout.state_off_off, hp.state_off,
+           sizeof(int32_t) * (size_t)hp.num_levels * hp.batch);
   e = hipMemcpyAsync(workspace, staging, meta_bytes, hipMemcpyHostToDevice,
                      reinterpret_cast<hipStream_t>(stream));
   if (e == hipSuccess && hp.rope)   // the (cos, sin) table, built on the device
@@ -302,23 +316,48 @@ namespace {
 
 enum Stage { kStagePrefix = 1, kStageDecode = 2, kStageMerge = 4 };
 
-// Shared argument checks of the run calls; prefix tables are required only
-// when the plan has a cascade level.
+// Device tables of the shared cascade levels, outermost first.
+struct LevelTables {
+  int n = 0;
+  const int32_t* indptr[fi::kMaxLevels] = {};
+  const int32_t* indices[fi::kMaxLevels] = {};
+  const int32_t* last[fi::kMaxLevels] = {};
+};
+
+LevelTables one_level(const int32_t* indptr, const int32_t* indices, const int32_t* last) {
+  LevelTables t;
+  t.n = 1;
+  t.indptr[0] = indptr;
+  t.indices[0] = indices;
+  t.last[0] = last;
+  return t;
+}
+
+// Shared argument checks of the run calls; level tables are required only
+// for levels with groups.
 fi_status check_run_args(const fi::HostPlan& hp, const void* q, const void* k_pages,
-                         const void* v_pages, const int32_t* prefix_kv_indptr,
-                         const int32_t* prefix_kv_indices, const int32_t* prefix_last_page_len,
+                         const void* v_pages, const LevelTables& lv,
                          const int32_t* kv_indptr, const int32_t* kv_indices,
                          const int32_t* last_page_len, float sm_scale, const void* o) {
   if (!q || !o || !kv_indptr || (!hp.ragged && !last_page_len))
     return fail(FI_ERR_INVALID_ARG, "q, o, kv_indptr and last_page_len must be non-NULL");
-  if (hp.num_groups > 0 && (!prefix_kv_indptr || (!hp.ragged && !prefix_last_page_len)))
-    return fail(FI_ERR_INVALID_ARG, "the prefix indptr / last_page_len tables must be non-NULL");
+  if (!hp.append && lv.n < hp.num_levels)
+    return fail(FI_ERR_INVALID_ARG, "the plan has %d cascade levels, %d sets of tables given",
+                hp.num_levels, lv.n);
+  for (int l = 0; l < hp.num_levels && !hp.append; ++l) {
+    if (hp.level_groups[l] == 0) continue;
+    if (!lv.indptr[l] || (!hp.ragged && !lv.last[l]))
+      return fail(FI_ERR_INVALID_ARG,
+                  "the prefix indptr / last_page_len tables must be non-NULL (level %d)", l);
+    if (!hp.ragged && !lv.indices[l] &&
+        hp.level_tile_off[l + 1] > hp.level_tile_off[l])
+      return fail(FI_ERR_INVALID_ARG, "the index tables must be non-NULL (level %d)", l);
+  }
   if ((hp.num_tiles > 0 || hp.num_prefix_tiles > 0) && (!k_pages || !v_pages))
     return fail(FI_ERR_INVALID_ARG, "k_pages and v_pages must be non-NULL");
   // append tiles read the per-request table
   const bool own_rows = hp.num_tiles > 0 || (hp.append && hp.num_prefix_tiles > 0);
-  if (!hp.ragged && ((!kv_indices && own_rows) ||
-                     (!prefix_kv_indices && !hp.append && hp.num_prefix_tiles > 0)))
+  if (!hp.ragged && !kv_indices && own_rows)
     return fail(FI_ERR_INVALID_ARG, "the index tables must be non-NULL");
   if (!(sm_scale == sm_scale) || std::isinf(sm_scale))
     return fail(FI_ERR_INVALID_ARG, "sm_scale must be finite");
@@ -326,11 +365,10 @@ fi_status check_run_args(const fi::HostPlan& hp, const void* q, const void* k_pa
 }
 
 // Enqueues the selected stages of a planned run on stream s, in order
-// prefix -> decode -> merge (a folded suffix tile reads the prefix states, so
-// the prefix kernel always completes first).
+// prefix (level by level) -> decode -> merge (a folded suffix tile reads
+// the prefix states, so the prefix kernels always complete first).
 fi_status enqueue_run(fi_plan_t plan, int stages, const void* q, const void* k_pages,
-                      const void* v_pages, const int32_t* prefix_kv_indptr,
-                      const int32_t* prefix_kv_indices, const int32_t* kv_indptr,
+                      const void* v_pages, const LevelTables& lv, const int32_t* kv_indptr,
                       const int32_t* kv_indices, const float* k_scale, const float* v_scale,
                       float sm_scale, void* o, float* lse, hipStream_t s) {
   const fi::HostPlan& hp = plan->hp;
@@ -340,18 +378,35 @@ fi_status enqueue_run(fi_plan_t plan, int stages, const void* q, const void* k_p
   hipError_t e = hipSuccess;
   const bool do_prefix = (stages & kStagePrefix) && hp.num_prefix_tiles > 0;
   const bool do_decode = (stages & kStageDecode) && hp.num_tiles > 0;
-  if (do_prefix) {
-    // prefix tiles read the group-level table; row -> request = the group's
-    // first request (planned copy of prefix_qo_indptr) + row / G.  Append
-    // tiles read the request's own table; row -> query token = the
-    // request's first token (planned copy of qo_indptr) + row / G.
+  const int32_t* qo_all = reinterpret_cast<const int32_t*>(plan->workspace + hp.layout.qo_indptr_off);
+  if (do_prefix && hp.append) {
+    // append tiles read the request's own table; row -> query token = the
+    // request's first token (planned copy of qo_indptr) + row / G
     fi::DecodeParams pp = p;
-    pp.kv_indptr = hp.append ? kv_indptr : prefix_kv_indptr;
-    pp.kv_indices = hp.append ? kv_indices : prefix_kv_indices;
-    pp.qo_indptr = reinterpret_cast<const int32_t*>(plan->workspace + hp.layout.qo_indptr_off);
-    e = fi::launch_prefix(pp, (int)hp.num_prefix_tiles, hp.prefix_waves, hp.append != 0, qbf,
-                          kv, s);
-    if (e != hipSuccess) return hip_fail(e, "prefix launch");
+    pp.kv_indptr = kv_indptr;
+    pp.kv_indices = kv_indices;
+    pp.qo_indptr = qo_all;
+    e = fi::launch_prefix(pp, (int)hp.num_prefix_tiles, hp.prefix_waves, true, qbf, kv, s);
+    if (e != hipSuccess) return hip_fail(e, "append launch");
+  } else if (do_prefix) {
+    // prefix tiles of level l read that level's table; row -> request = the
+    // group's first request (planned copy of the level's qo_indptr) + row / G
+    for (int l = 0; l < hp.num_levels; ++l) {
+      const int64_t n = hp.level_tile_off[l + 1] - hp.level_tile_off[l];
+      if (n == 0) continue;
+      fi::DecodeParams pp = p;
+      pp.kv_indptr = lv.indptr[l];
+      pp.kv_indices = lv.indices[l];
+      pp.qo_indptr = qo_all + hp.level_qo_start[l];
+      pp.state_off = hp.num_levels >= 2
+                         ? reinterpret_cast<const int32_t*>(plan->workspace +
+                                                            hp.layout.state_off_off) +
+                               (int64_t)l * hp.batch
+                         : nullptr;
+      pp.num_tiles = (int32_t)(hp.num_tiles + hp.level_tile_off[l]);
+      e = fi::launch_prefix(pp, (int)n, hp.prefix_waves, false, qbf, kv, s);
+      if (e != hipSuccess) return hip_fail(e, "prefix launch");
+    }
   }
   if (do_decode) {
     p.kv_indptr = kv_indptr;
@@ -378,11 +433,12 @@ fi_status fi_decode_run(fi_plan_t plan, const void* q, const void* k_pages,
     return fail(FI_ERR_INVALID_ARG, "plan has a cascade level: use fi_cascade_decode");
   if (hp.append) return fail(FI_ERR_INVALID_ARG, "append plan: use fi_append_run");
   if (hp.batch == 0) return FI_OK;
-  fi_status st = check_run_args(hp, q, k_pages, v_pages, nullptr, nullptr, nullptr, kv_indptr,
-                                kv_indices, last_page_len, sm_scale, o);
+  const LevelTables none;
+  fi_status st = check_run_args(hp, q, k_pages, v_pages, none, kv_indptr, kv_indices,
+                                last_page_len, sm_scale, o);
   if (st != FI_OK) return st;
-  return enqueue_run(plan, kStageDecode | kStageMerge, q, k_pages, v_pages, nullptr, nullptr,
-                     kv_indptr, kv_indices, k_scale, v_scale, sm_scale, o, lse,
+  return enqueue_run(plan, kStageDecode | kStageMerge, q, k_pages, v_pages, none, kv_indptr,
+                     kv_indices, k_scale, v_scale, sm_scale, o, lse,
                      reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -399,14 +455,51 @@ fi_status fi_cascade_decode(fi_plan_t plan, const void* q, const void* k_pages,
   if (hp.append) return fail(FI_ERR_INVALID_ARG, "append plan: use fi_append_run");
   if (hp.num_groups == 0)
     return fail(FI_ERR_INVALID_ARG, "plan has no cascade level: use fi_decode_run");
+  if (hp.num_levels != 1)
+    return fail(FI_ERR_INVALID_ARG, "plan has %d cascade levels: use fi_cascade_decode_levels",
+                hp.num_levels);
   if (hp.batch == 0) return FI_OK;
-  fi_status st = check_run_args(hp, q, k_pages, v_pages, prefix_kv_indptr, prefix_kv_indices,
-                                prefix_last_page_len, kv_indptr, kv_indices, last_page_len,
-                                sm_scale, o);
+  const LevelTables lv = one_level(prefix_kv_indptr, prefix_kv_indices, prefix_last_page_len);
+  fi_status st = check_run_args(hp, q, k_pages, v_pages, lv, kv_indptr, kv_indices,
+                                last_page_len, sm_scale, o);
   if (st != FI_OK) return st;
-  return enqueue_run(plan, kStagePrefix | kStageDecode | kStageMerge, q, k_pages, v_pages,
-                     prefix_kv_indptr, prefix_kv_indices, kv_indptr, kv_indices, k_scale,
-                     v_scale, sm_scale, o, lse, reinterpret_cast<hipStream_t>(stream));
+  return enqueue_run(plan, kStagePrefix | kStageDecode | kStageMerge, q, k_pages, v_pages, lv,
+                     kv_indptr, kv_indices, k_scale, v_scale, sm_scale, o, lse,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+fi_status fi_cascade_decode_levels(fi_plan_t plan, const void* q, const void* k_pages,
+                                   const void* v_pages, int32_t num_levels,
+                                   const int32_t* const* level_kv_indptr,
+                                   const int32_t* const* level_kv_indices,
+                                   const int32_t* const* level_last_page_len,
+                                   const int32_t* kv_indptr, const int32_t* kv_indices,
+                                   const int32_t* last_page_len, const float* k_scale,
+                                   const float* v_scale, float sm_scale, void* o, float* lse,
+                                   void* stream) {
+  g_last_error.clear();
+  if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
+  const fi::HostPlan& hp = plan->hp;
+  if (hp.append) return fail(FI_ERR_INVALID_ARG, "append plan: use fi_append_run");
+  if (num_levels != hp.num_levels)
+    return fail(FI_ERR_INVALID_ARG, "the plan has %d cascade levels, got %d", hp.num_levels,
+                num_levels);
+  if (num_levels > 0 && (!level_kv_indptr || !level_kv_indices || !level_last_page_len))
+    return fail(FI_ERR_INVALID_ARG, "the level table arrays must be non-NULL");
+  if (hp.batch == 0) return FI_OK;
+  LevelTables lv;
+  lv.n = num_levels;
+  for (int l = 0; l < num_levels; ++l) {
+    lv.indptr[l] = level_kv_indptr[l];
+    lv.indices[l] = level_kv_indices[l];
+    lv.last[l] = level_last_page_len[l];
+  }
+  fi_status st = check_run_args(hp, q, k_pages, v_pages, lv, kv_indptr, kv_indices,
+                                last_page_len, sm_scale, o);
+  if (st != FI_OK) return st;
+  return enqueue_run(plan, kStagePrefix | kStageDecode | kStageMerge, q, k_pages, v_pages, lv,
+                     kv_indptr, kv_indices, k_scale, v_scale, sm_scale, o, lse,
+                     reinterpret_cast<hipStream_t>(stream));
 }
 
 fi_status fi_append_run(fi_plan_t plan, const void* q, const void* k_pages,
@@ -419,11 +512,12 @@ fi_status fi_append_run(fi_plan_t plan, const void* q, const void* k_pages,
   const fi::HostPlan& hp = plan->hp;
   if (!hp.append) return fail(FI_ERR_INVALID_ARG, "plan is not an append plan");
   if (hp.total_q == 0) return FI_OK;
-  fi_status st = check_run_args(hp, q, k_pages, v_pages, nullptr, nullptr, nullptr, kv_indptr,
-                                kv_indices, last_page_len, sm_scale, o);
+  const LevelTables none;
+  fi_status st = check_run_args(hp, q, k_pages, v_pages, none, kv_indptr, kv_indices,
+                                last_page_len, sm_scale, o);
   if (st != FI_OK) return st;
-  return enqueue_run(plan, kStagePrefix | kStageMerge, q, k_pages, v_pages, nullptr, nullptr,
-                     kv_indptr, kv_indices, k_scale, v_scale, sm_scale, o, lse,
+  return enqueue_run(plan, kStagePrefix | kStageMerge, q, k_pages, v_pages, none, kv_indptr,
+                     kv_indices, k_scale, v_scale, sm_scale, o, lse,
                      reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -442,14 +536,17 @@ fi_status fi_debug_run_stage(fi_plan_t plan, int32_t stage, const void* q, const
                 "stage must be 0 (decode kernel), 1 (prefix kernel) or 2 (merge kernel)");
   if (stage == 1 && hp.num_prefix_tiles == 0)
     return fail(FI_ERR_INVALID_ARG, "the plan has no cascade prefix or append tiles");
+  if (hp.num_levels > 1)
+    return fail(FI_ERR_INVALID_ARG, "stage hook: plans with one cascade level at most");
   if (hp.batch == 0 || (hp.append && hp.total_q == 0)) return FI_OK;
-  fi_status st = check_run_args(hp, q, k_pages, v_pages, prefix_kv_indptr, prefix_kv_indices,
-                                prefix_last_page_len, kv_indptr, kv_indices, last_page_len,
-                                sm_scale, o);
+  const LevelTables lv = hp.num_levels == 1
+                             ? one_level(prefix_kv_indptr, prefix_kv_indices, prefix_last_page_len)
+                             : LevelTables();
+  fi_status st = check_run_args(hp, q, k_pages, v_pages, lv, kv_indptr, kv_indices,
+                                last_page_len, sm_scale, o);
   if (st != FI_OK) return st;
   const int which = stage == 0 ? kStageDecode : stage == 1 ? kStagePrefix : kStageMerge;
-  return enqueue_run(plan, which, q, k_pages, v_pages,
-                     prefix_kv_indptr, prefix_kv_indices, kv_indptr, kv_indices, k_scale,
+  return enqueue_run(plan, which, q, k_pages, v_pages, lv, kv_indptr, kv_indices, k_scale,
                      v_scale, sm_scale, o, lse, reinterpret_cast<hipStream_t>(stream));
 }
 

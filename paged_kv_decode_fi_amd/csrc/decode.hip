@@ -866,7 +866,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
       }
       if (g == 0 && p.lse) p.lse[(int64_t)r * p.Hq + j] = lse2 * kLn2;
     } else {
-      const int64_t slot = ri.slot_base + (int64_t)tile.slot * p.Hkv + h;
+      // state index: this level's chunk after the request's earlier levels
+      const int c = tile.slot + (p.state_off ? p.state_off[r] : 0);
+      const int64_t slot = ri.slot_base + (int64_t)c * p.Hkv + h;
       float* po = p.partial_o + (slot * G + (j - h * G)) * kHeadDim;
 #pragma unroll
       for (int b = 0; b < 8; ++b)

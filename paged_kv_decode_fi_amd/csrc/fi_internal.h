@@ -16,6 +16,7 @@ constexpr int kPrefixRowsPerWave = 32;   // 2 MFMA column tiles per wave
 constexpr int kPrefixMaxWaves = 8;       // prefix workgroup: 4 or 8 waves
 constexpr int kPrefixMaxChunk = 4096;    // prefix tokens per tile (page table in LDS)
 constexpr int kMaxMergeStates = 64;
+constexpr int kMaxLevels = 8;            // shared cascade levels
 
 enum TileKind : int32_t { kDecodeTile = 0, kPrefixTile = 1, kAppendTile = 2 };
 
@@ -68,6 +69,7 @@ struct WorkspaceLayout {
   size_t req_info_off;     // ReqInfo[batch]
   size_t merge_reqs_off;   // MergeUnit[num_merge_units]
   size_t qo_indptr_off;    // int32[qo_len]: cascade group starts or append query starts
+  size_t state_off_off;    // int32[num_levels * batch] (levels >= 2)
   size_t partial_o_off;    // float[num_partials][G][D]
   size_t partial_lse_off;  // float[num_partials][G]   (log2 domain)
   size_t rope_off;         // uint32[rope_rows][kHeadDim / 2] (RoPE plans)
@@ -90,7 +92,16 @@ struct HostPlan {
   int32_t causal;       // append: causal mask
   int64_t total_q;      // append: query tokens (rows of o)
   int64_t num_req_info; // ReqInfo entries (batch, or total_q for append)
-  int32_t qo_len;       // qo_indptr entries (groups + 1, or batch + 1 for append)
+  int32_t qo_len;       // qo_indptr entries (levels' groups + 1 each, or batch + 1)
+  // shared cascade levels, outermost first: level l's group starts are
+  // qo_indptr[level_qo_start[l] ..], its prefix tiles are prefix tiles
+  // level_tile_off[l] .. level_tile_off[l + 1] - 1, and a request's states
+  // from it start at state index state_off[l * batch + r] (levels >= 2 only)
+  int32_t num_levels;
+  int32_t level_groups[kMaxLevels];
+  int32_t level_qo_start[kMaxLevels];
+  int64_t level_tile_off[kMaxLevels + 1];
+  int32_t* state_off;   // num_levels * batch entries when num_levels >= 2
   int32_t rope;         // FI_POS_ROPE_LLAMA or 0
   int32_t rope_rows;    // positions in the RoPE table (longest request)
   float rope_theta, rope_scale;
@@ -108,10 +119,14 @@ struct PlanInput {
   int32_t q_dtype, kv_dtype;
   const int32_t* kv_indptr;
   const int32_t* last_page_len;
-  int32_t num_groups;
-  const int32_t* qo_indptr;
-  const int32_t* p_indptr;
-  const int32_t* p_last;
+  // shared cascade levels, outermost first (host tables)
+  int32_t num_levels;
+  struct Level {
+    int32_t num_groups;
+    const int32_t* qo_indptr;   // groups of contiguous requests
+    const int32_t* p_indptr;
+    const int32_t* p_last;
+  } levels[kMaxLevels];
   int32_t chunk_tokens;
   int32_t num_cus;
   int32_t pos_encoding;
@@ -150,6 +165,9 @@ struct DecodeParams {
   // ragged KV: token t of a request is row kv_indptr[r] + t (page size 1,
   // kv_indices not read)
   int32_t ragged;
+  // prefix tiles of a cascade with several levels: request r's states from
+  // this level start at state index state_off[r] (NULL: 0)
+  const int32_t* state_off;
   // K/V row of (page, slot, kv head) at page * page_bytes + slot *
   // slot_stride + head * head_stride bytes: NHD pages (slot_stride = Hkv
   // rows, head_stride = 1 row) or HND pages (slot_stride = 1 row,

@@ -304,30 +304,48 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
     lens[r] = table_len(in.kv_indptr, last_tab, r, ps);
     if (lens[r] > (int64_t)0x7fffffff - 64) PLAN_FAIL(1, "request %d too long", r);
   }
-  const int NG = in.num_groups;
-  std::vector<int64_t> plens(NG > 0 ? NG : 0);
-  std::vector<int> group_of(B, -1);
-  if (NG < 0) PLAN_FAIL(1, "num_prefix_groups must be >= 0");
-  if (NG > 0) {
-    if (!in.qo_indptr || !in.p_indptr || (!in.ragged && !in.p_last))
-      PLAN_FAIL(1, "cascade level needs prefix_qo_indptr, prefix_kv_indptr, "
-                   "prefix_last_page_len (host)");
-    if (in.qo_indptr[0] != 0 || in.qo_indptr[NG] != B)
-      PLAN_FAIL(1, "prefix_qo_indptr must start at 0 and end at batch");
-    if (!in.ragged && in.p_indptr[0] != 0) PLAN_FAIL(1, "prefix_kv_indptr[0] must be 0");
-    if (in.p_indptr[0] < 0) PLAN_FAIL(1, "prefix_kv_indptr[0] must be >= 0");
-    for (int g = 0; g < NG; ++g) {
-      if (in.qo_indptr[g + 1] < in.qo_indptr[g])
-        PLAN_FAIL(1, "prefix_qo_indptr decreases at group %d", g);
-      if (in.p_indptr[g + 1] < in.p_indptr[g])
-        PLAN_FAIL(1, "prefix_kv_indptr decreases at group %d", g);
-      int64_t n = (int64_t)in.p_indptr[g + 1] - in.p_indptr[g];
-      if (n > 0 && !in.ragged && (in.p_last[g] < 1 || in.p_last[g] > ps))
-        PLAN_FAIL(1, "prefix_last_page_len[%d] outside [1, %d]", g, ps);
-      plens[g] = table_len(in.p_indptr, in.ragged ? nullptr : in.p_last, g, ps);
-      for (int r = in.qo_indptr[g]; r < in.qo_indptr[g + 1]; ++r) group_of[r] = g;
+  // ---- shared (cascade) levels, outermost first; each splits the requests
+  // into groups of contiguous requests sharing a prefix table
+  const int NL = in.num_levels;
+  if (NL < 0)
+    PLAN_FAIL(1, "cascade levels: give either the single-level prefix fields or a non-NULL "
+                 "level array, not both");
+  if (NL > kMaxLevels) PLAN_FAIL(2, "%d cascade levels (at most %d are built)", NL, kMaxLevels);
+  std::vector<std::vector<int64_t>> plens(NL);       // [level][group] prefix tokens
+  std::vector<std::vector<int>> group_of(NL, std::vector<int>(B, -1));
+  int NG = 0;                                         // groups over all levels
+  for (int l = 0; l < NL; ++l) {
+    const PlanInput::Level& lv = in.levels[l];
+    const int ng = lv.num_groups;
+    if (ng < 0) PLAN_FAIL(1, "num_prefix_groups must be >= 0 (level %d)", l);
+    NG += ng;
+    plens[l].assign(ng, 0);
+    if (ng == 0) continue;
+    if (!lv.qo_indptr || !lv.p_indptr || (!in.ragged && !lv.p_last))
+      PLAN_FAIL(1, "cascade level %d needs prefix_qo_indptr, prefix_kv_indptr, "
+                   "prefix_last_page_len (host)", l);
+    if (lv.qo_indptr[0] != 0 || lv.qo_indptr[ng] != B)
+      PLAN_FAIL(1, "prefix_qo_indptr must start at 0 and end at batch (level %d)", l);
+    if (!in.ragged && lv.p_indptr[0] != 0)
+      PLAN_FAIL(1, "prefix_kv_indptr[0] must be 0 (level %d)", l);
+    if (lv.p_indptr[0] < 0) PLAN_FAIL(1, "prefix_kv_indptr[0] must be >= 0 (level %d)", l);
+    for (int g = 0; g < ng; ++g) {
+      if (lv.qo_indptr[g + 1] < lv.qo_indptr[g])
+        PLAN_FAIL(1, "prefix_qo_indptr decreases at group %d (level %d)", g, l);
+      if (lv.p_indptr[g + 1] < lv.p_indptr[g])
+        PLAN_FAIL(1, "prefix_kv_indptr decreases at group %d (level %d)", g, l);
+      int64_t n = (int64_t)lv.p_indptr[g + 1] - lv.p_indptr[g];
+      if (n > 0 && !in.ragged && (lv.p_last[g] < 1 || lv.p_last[g] > ps))
+        PLAN_FAIL(1, "prefix_last_page_len[%d] outside [1, %d] (level %d)", g, ps, l);
+      plens[l][g] = table_len(lv.p_indptr, in.ragged ? nullptr : lv.p_last, g, ps);
+      for (int r = lv.qo_indptr[g]; r < lv.qo_indptr[g + 1]; ++r) group_of[l][r] = g;
     }
   }
+  auto has_prefix = [&](int r) {
+    for (int l = 0; l < NL; ++l)
+      if (group_of[l][r] >= 0 && plens[l][group_of[l][r]] > 0) return true;
+    return false;
+  };
   const int num_cus = in.num_cus > 0 ? in.num_cus : 256;
   if (in.append_qo_indptr) {
     if (NG > 0) PLAN_FAIL(2, "append with a cascade level is not built");
@@ -403,7 +421,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   if (NG > 0 && fold_ok && in.chunk_tokens == 0 && env_int("FI_HEADS_PER_TILE", 0) == 0) {
     int64_t ls_max = 0;
     for (int r = 0; r < B; ++r)
-      if (group_of[r] >= 0 && plens[group_of[r]] > 0) ls_max = std::max(ls_max, lens[r]);
+      if (has_prefix(r)) ls_max = std::max(ls_max, lens[r]);
     const int hpt_f = Hkv % 2 == 0 ? 2 : 1;
     if (ls_max > 0 && ls_max <= env_int("FI_FOLD_MAX_SUFFIX", 1024)) {
       const int64_t chunk_f = round_up(ls_max, kChunkAlign);
@@ -421,27 +439,39 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   const int prefix_waves = env_int("FI_PREFIX_WAVES", kPrefixMaxWaves) == 4 ? 4 : 8;
   const int64_t prefix_rows = (int64_t)kPrefixRowsPerWave * prefix_waves;
   int64_t prefix_chunk = 0;
-  std::vector<int64_t> n_pchunks(NG > 0 ? NG : 0, 0);
-  int64_t prefix_row_tiles = 0;  // sum over groups of row tiles x Hkv
-  if (NG > 0) {
-    for (int g = 0; g < NG; ++g) {
-      int64_t rows = (int64_t)(in.qo_indptr[g + 1] - in.qo_indptr[g]) * G;
-      if (plens[g] > 0) prefix_row_tiles += ceil_div(rows, prefix_rows) * Hkv;
+  std::vector<std::vector<int64_t>> n_pchunks(NL);   // [level][group] chunks
+  int64_t prefix_row_tiles = 0;  // sum over levels and groups of row tiles x Hkv
+  int64_t Lpmax = 0;
+  for (int l = 0; l < NL; ++l)
+    for (int g = 0; g < in.levels[l].num_groups; ++g) {
+      const int64_t rows =
+          (int64_t)(in.levels[l].qo_indptr[g + 1] - in.levels[l].qo_indptr[g]) * G;
+      if (plens[l][g] > 0) prefix_row_tiles += ceil_div(rows, prefix_rows) * Hkv;
+      Lpmax = std::max(Lpmax, plens[l][g]);
     }
-    int64_t Lpmax = 0;
-    for (int g = 0; g < NG; ++g) Lpmax = std::max(Lpmax, plens[g]);
-    if (prefix_row_tiles > 0) {
-      const int64_t want = std::max<int64_t>(1, (int64_t)num_cus * env_int("FI_PREFIX_TILES_PER_CU", 1));
-      int64_t n_split = std::max<int64_t>(1, ceil_div(want, prefix_row_tiles));
-      prefix_chunk = round_up(ceil_div(Lpmax, n_split), kBlockTokens);
-      prefix_chunk = std::max<int64_t>(prefix_chunk, env_int("FI_PREFIX_CHUNK_MIN", 256));
-      prefix_chunk = round_up(prefix_chunk, kBlockTokens);
-      // a prefix tile stages its chunk's page indices in LDS (<= 4096 + 2)
-      prefix_chunk = std::min<int64_t>(prefix_chunk, kPrefixMaxChunk);
-    }
-    for (int g = 0; g < NG; ++g)
-      n_pchunks[g] = (plens[g] > 0 && prefix_chunk > 0) ? ceil_div(plens[g], prefix_chunk) : 0;
+  if (prefix_row_tiles > 0) {
+    const int64_t want = std::max<int64_t>(1, (int64_t)num_cus * env_int("FI_PREFIX_TILES_PER_CU", 1));
+    int64_t n_split = std::max<int64_t>(1, ceil_div(want, prefix_row_tiles));
+    prefix_chunk = round_up(ceil_div(Lpmax, n_split), kBlockTokens);
+    prefix_chunk = std::max<int64_t>(prefix_chunk, env_int("FI_PREFIX_CHUNK_MIN", 256));
+    prefix_chunk = round_up(prefix_chunk, kBlockTokens);
+    // a prefix tile stages its chunk's page indices in LDS (<= 4096 + 2)
+    prefix_chunk = std::min<int64_t>(prefix_chunk, kPrefixMaxChunk);
   }
+  for (int l = 0; l < NL; ++l) {
+    n_pchunks[l].assign(in.levels[l].num_groups, 0);
+    for (int g = 0; g < in.levels[l].num_groups; ++g)
+      n_pchunks[l][g] =
+          (plens[l][g] > 0 && prefix_chunk > 0) ? ceil_div(plens[l][g], prefix_chunk) : 0;
+  }
+  // request r's prefix states: level by level, outermost first
+  std::vector<int64_t> np_of(B, 0);
+  std::vector<int32_t> state_off((size_t)std::max(NL, 1) * std::max(B, 1), 0);
+  for (int r = 0; r < B; ++r)
+    for (int l = 0; l < NL; ++l) {
+      state_off[(size_t)l * B + r] = (int32_t)np_of[r];
+      if (group_of[l][r] >= 0) np_of[r] += n_pchunks[l][group_of[l][r]];
+    }
 
   // ---- states per request, slots
   // A request with prefix states and a suffix that is one decode chunk is
@@ -455,8 +485,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   if (!out->req_info) PLAN_FAIL(1, "out of host memory");
   int64_t slots = 0, n_merge = 0;
   for (int r = 0; r < B; ++r) {
-    int g = group_of[r];
-    const int64_t np = g >= 0 ? n_pchunks[g] : 0;
+    const int64_t np = np_of[r];
     int64_t ns = n_dchunks[r] + np;
     folded[r] = fold_ok && np > 0 && n_dchunks[r] == 1;
     out->req_info[r].n_states = (int32_t)ns;
@@ -484,8 +513,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   // ---- decode tiles
   std::vector<Tile> dt;
   for (int r = 0; r < B; ++r) {
-    int g = group_of[r];
-    int64_t c_off = g >= 0 ? n_pchunks[g] : 0;
+    const int64_t c_off = np_of[r];
     const ReqInfo& ri = out->req_info[r];
     int64_t nc = n_dchunks[r];
     bool need_empty = (nc == 0 && ri.n_states == 0);
@@ -508,31 +536,47 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   std::stable_sort(dt.begin(), dt.end(), [](const Tile& a, const Tile& b) {
     return (a.t1 - a.t0) > (b.t1 - b.t0);
   });
-  // ---- prefix tiles: chunk-major, row tiles of one (group, head, chunk)
-  // adjacent so they run together and share the chunk's K/V in cache
+  // ---- prefix tiles, level by level: chunk-major, row tiles of one
+  // (group, head, chunk) adjacent so they run together and share the chunk's
+  // K/V in cache
   std::vector<Tile> pt;
-  for (int g = 0; g < NG; ++g) {
-    int64_t rows = (int64_t)(in.qo_indptr[g + 1] - in.qo_indptr[g]) * G;
-    if (plens[g] == 0 || rows == 0) continue;
-    int64_t nrt = ceil_div(rows, prefix_rows);
-    for (int64_t pc = 0; pc < n_pchunks[g]; ++pc)
-      for (int h = 0; h < Hkv; ++h)
-        for (int64_t rt = 0; rt < nrt; ++rt) {
-          Tile t;
-          t.req = g;
-          t.kv_head0 = h;
-          t.t0 = (int32_t)(pc * prefix_chunk);
-          t.t1 = (int32_t)std::min<int64_t>((pc + 1) * prefix_chunk, plens[g]);
-          t.slot = (int32_t)pc;
-          t.kind = kPrefixTile;
-          t.row0 = (int32_t)(rt * prefix_rows);
-          t.row1 = (int32_t)std::min<int64_t>((rt + 1) * prefix_rows, rows);
-          pt.push_back(t);
-        }
+  out->num_levels = NL;
+  int32_t qo_entries = 0;
+  for (int l = 0; l < NL; ++l) {
+    out->level_tile_off[l] = (int64_t)pt.size();
+    out->level_qo_start[l] = qo_entries;
+    out->level_groups[l] = in.levels[l].num_groups;
+    qo_entries += in.levels[l].num_groups + 1;
+    for (int g = 0; g < in.levels[l].num_groups; ++g) {
+      const int64_t rows =
+          (int64_t)(in.levels[l].qo_indptr[g + 1] - in.levels[l].qo_indptr[g]) * G;
+      if (plens[l][g] == 0 || rows == 0) continue;
+      const int64_t nrt = ceil_div(rows, prefix_rows);
+      for (int64_t pc = 0; pc < n_pchunks[l][g]; ++pc)
+        for (int h = 0; h < Hkv; ++h)
+          for (int64_t rt = 0; rt < nrt; ++rt) {
+            Tile t;
+            t.req = g;
+            t.kv_head0 = h;
+            t.t0 = (int32_t)(pc * prefix_chunk);
+            t.t1 = (int32_t)std::min<int64_t>((pc + 1) * prefix_chunk, plens[l][g]);
+            t.slot = (int32_t)pc;   // chunk of this level; + state_off[l][r]
+            t.kind = kPrefixTile;
+            t.row0 = (int32_t)(rt * prefix_rows);
+            t.row1 = (int32_t)std::min<int64_t>((rt + 1) * prefix_rows, rows);
+            pt.push_back(t);
+          }
+    }
   }
-  out->qo_indptr = (int32_t*)malloc(sizeof(int32_t) * (NG + 1));
-  if (!out->qo_indptr) PLAN_FAIL(1, "out of host memory");
-  for (int g = 0; g <= NG; ++g) out->qo_indptr[g] = NG > 0 ? in.qo_indptr[g] : 0;
+  out->level_tile_off[NL] = (int64_t)pt.size();
+  out->qo_indptr = (int32_t*)malloc(sizeof(int32_t) * (size_t)std::max(qo_entries, 1));
+  out->state_off = (int32_t*)malloc(sizeof(int32_t) * state_off.size());
+  if (!out->qo_indptr || !out->state_off) PLAN_FAIL(1, "out of host memory");
+  out->qo_indptr[0] = 0;
+  for (int l = 0; l < NL; ++l)
+    for (int g = 0; g <= in.levels[l].num_groups; ++g)
+      out->qo_indptr[out->level_qo_start[l] + g] = in.levels[l].qo_indptr[g];
+  std::copy(state_off.begin(), state_off.end(), out->state_off);
   out->num_tiles = (int64_t)dt.size();
   out->num_prefix_tiles = (int64_t)pt.size();
   out->tiles = (Tile*)malloc(sizeof(Tile) * std::max<size_t>(dt.size() + pt.size(), 1));
@@ -557,7 +601,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   out->num_folded = 0;
   for (int r = 0; r < B; ++r) out->num_folded += folded[r] ? 1 : 0;
   out->num_req_info = B;
-  out->qo_len = NG + 1;
+  out->qo_len = std::max(qo_entries, 1);
   out->ragged = in.ragged;
   out->hnd = in.hnd;
 
@@ -570,7 +614,9 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   L.merge_reqs_off = off;
   off = align256(off + sizeof(MergeUnit) * (size_t)std::max<int64_t>(n_merge, 1));
   L.qo_indptr_off = off;
-  off = align256(off + sizeof(int32_t) * (size_t)(NG + 1));
+  off = align256(off + sizeof(int32_t) * (size_t)out->qo_len);
+  L.state_off_off = off;
+  off = align256(off + sizeof(int32_t) * state_off.size());
   L.partial_o_off = off;
   off = align256(off + sizeof(float) * (size_t)slots * G * kHeadDim);
   L.partial_lse_off = off;
@@ -592,7 +638,9 @@ void plan_free(HostPlan* p) {
   free(p->req_info);
   free(p->merge_units);
   free(p->qo_indptr);
+  free(p->state_off);
   p->qo_indptr = nullptr;
+  p->state_off = nullptr;
   p->tiles = nullptr;
   p->req_info = nullptr;
   p->merge_units = nullptr;

@@ -359,3 +359,59 @@ def test_append_plan_rules(fi):
     assert len(t) == 64 * 8 and set(t[:, 3] - t[:, 2]) == {512}
     assert np.all(t[:, 6] == 0) and np.all(t[:, 7] == 4)
     _append_cover(t, lens, np.ones(64, np.int64), 4, 8, True)
+
+
+def test_multilevel_cascade_plan(fi):
+    """Several shared levels: every (level, group, kv head, prefix token) is
+    covered once by that level's prefix tiles, every row of the group's
+    requests by each tile's rows; both level forms at once, and more than 8
+    levels, are refused."""
+    ps, Hkv, G = 16, 2, 4
+    own = np.array([5, 0, 40, 17])
+    n = (own + ps - 1) // ps
+    ip = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    la = np.where(n > 0, own - (n - 1) * ps, 0).astype(np.int32)
+
+    def level(groups):
+        qo = np.concatenate([[0], np.cumsum([g[0] for g in groups])]).astype(np.int32)
+        pl = np.array([g[1] for g in groups])
+        pn = (pl + ps - 1) // ps
+        pip = np.concatenate([[0], np.cumsum(pn)]).astype(np.int32)
+        pla = np.where(pn > 0, pl - (pn - 1) * ps, 0).astype(np.int32)
+        return (qo, pip, pla), pl
+
+    specs = [[(4, 700)], [(2, 30), (2, 0)], [(1, 3), (3, 50)]]
+    levels, plens = zip(*[level(s) for s in specs])
+    t = fi.debug_plan_tiles(ip, la, num_qo_heads=Hkv * G, num_kv_heads=Hkv, page_size=ps,
+                            levels=list(levels), chunk_tokens=32)
+    pre = t[t[:, 5] == 1]
+    # prefix tiles come level by level; within a level, cover each (group,
+    # head, token) once over all row tiles
+    k = 0
+    for li, (qo, pip, pla) in enumerate(levels):
+        ng = len(qo) - 1
+        want = {(g, h, tt, row) for g in range(ng) for h in range(Hkv)
+                for tt in range(int(plens[li][g])) for row in range((qo[g + 1] - qo[g]) * G)}
+        got = set()
+        while k < len(pre) and len(got) < len(want):
+            req, h, t0, t1, slot, kind, r0, r1 = pre[k]
+            for tt in range(t0, t1):
+                for row in range(r0, r1):
+                    key = (req, h, tt, row)
+                    assert key not in got, (li, key)
+                    got.add(key)
+            k += 1
+        assert got == want, li
+    assert k == len(pre)
+    pr, keep = _problem(fi, ip, la, prefix=(levels[0][0], levels[0][1], levels[0][2]))
+    arr = (fi.CascadeLevel * 1)()
+    arr[0].num_groups = 1
+    arr[0].qo_indptr = levels[0][0].ctypes.data
+    arr[0].kv_indptr = levels[0][1].ctypes.data
+    arr[0].last_page_len = levels[0][2].ctypes.data
+    pr.num_cascade_levels, pr.cascade_levels = 1, ctypes.cast(arr, ctypes.c_void_p)
+    nn = ctypes.c_int64(0)
+    assert fi.lib.fi_debug_plan_tiles(ctypes.byref(pr), 256, None, 0, ctypes.byref(nn)) == 1
+    with pytest.raises(fi.FiError):
+        fi.debug_plan_tiles(ip, la, num_qo_heads=Hkv * G, num_kv_heads=Hkv, page_size=ps,
+                            levels=[levels[0]] * 9)

@@ -419,3 +419,69 @@ def to_hnd(w: Paged) -> Paged:
     r.v_pages = np.ascontiguousarray(w.v_pages.transpose(0, 2, 1, 3))
     r.meta = dict(w.meta, hnd=True)
     return r
+
+
+def build_multilevel(name, kv_lens, levels, *, Hq, Hkv, D=128, ps=16, q_dtype="f16",
+                     kv_dtype="f16", seed=0):
+    """Cascade with several shared levels, outermost first: levels[l] is a
+    list of (n_requests, prefix_len) groups of contiguous requests covering
+    the batch.  Returns a Paged whose meta["levels"] holds, per level,
+    (qo_indptr, kv_indptr, kv_indices, last_page_len, prefix_lens) into the
+    same page pools; the request tables are the usual fields."""
+    rng = np.random.default_rng(seed)
+    kv_lens = np.asarray(kv_lens, np.int64)
+    B = len(kv_lens)
+    lists = []          # (level or -1, index, length)
+    for l, groups in enumerate(levels):
+        assert sum(g[0] for g in groups) == B
+        for gi, (_, plen) in enumerate(groups):
+            lists.append((l, gi, int(plen)))
+    lists += [(-1, r, int(kv_lens[r])) for r in range(B)]
+    data = {(l, i): (rng.standard_normal((L, Hkv, D), dtype=np.float32),
+                     rng.standard_normal((L, Hkv, D), dtype=np.float32)) for l, i, L in lists}
+    k_scale = v_scale = None
+    if kv_dtype == "e4m3":
+        amk = np.max([np.abs(k).max(axis=(0, 2)) for k, _ in data.values() if len(k)], axis=0)
+        amv = np.max([np.abs(v).max(axis=(0, 2)) for _, v in data.values() if len(v)], axis=0)
+        k_scale = (amk / np.float32(448.0)).astype(np.float32)
+        v_scale = (amv / np.float32(448.0)).astype(np.float32)
+    npages = [(L + ps - 1) // ps for _, _, L in lists]
+    P = int(math.ceil(sum(npages) * 1.25)) + 1
+    perm = rng.permutation(P).astype(np.int32)
+    st = STORAGE[kv_dtype]
+    kp = np.full((P, ps, Hkv, D), NAN_BITS[kv_dtype], st)
+    vp = kp.copy()
+    pages_of = {}
+    off = 0
+    for (l, i, L), n in zip(lists, npages):
+        pages = perm[off:off + n]
+        off += n
+        pages_of[(l, i)] = pages
+        k, v = data[(l, i)]
+        if L:
+            kb = cast_bits(k, kv_dtype, None if k_scale is None else k_scale[None, :, None])
+            vb = cast_bits(v, kv_dtype, None if v_scale is None else v_scale[None, :, None])
+            _scatter(kp, pages, L, ps, kb)
+            _scatter(vp, pages, L, ps, vb)
+
+    def table(keys):
+        lens = [len(data[k][0]) for k in keys]
+        n = [(L + ps - 1) // ps for L in lens]
+        ip = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+        ix = (np.concatenate([pages_of[k] for k in keys]) if keys else
+              np.zeros(0, np.int32)).astype(np.int32)
+        last = np.array([L - (m - 1) * ps if m else 0 for L, m in zip(lens, n)], np.int32)
+        return ip, ix, last, np.asarray(lens, np.int64)
+
+    lv = []
+    for l, groups in enumerate(levels):
+        qo = np.concatenate([[0], np.cumsum([g[0] for g in groups])]).astype(np.int32)
+        ip, ix, last, plens = table([(l, gi) for gi in range(len(groups))])
+        lv.append((qo, ip, ix, last, plens))
+    ip, ix, last, _ = table([(-1, r) for r in range(B)])
+    q = cast_bits(rng.standard_normal((B, Hq, D), dtype=np.float32), q_dtype)
+    return Paged(name=name, batch=B, num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                 page_size=ps, q_dtype=q_dtype, kv_dtype=kv_dtype, q=q, k_pages=kp,
+                 v_pages=vp, kv_indptr=ip, kv_indices=ix, last_page_len=last,
+                 kv_lens=kv_lens.copy(), sm_scale=float(np.float32(1.0 / math.sqrt(D))),
+                 k_scale=k_scale, v_scale=v_scale, meta={"levels": lv})
