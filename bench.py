@@ -76,6 +76,8 @@ def parse():
                          "request, no page table)")
     ap.add_argument("--hnd", action="store_true",
                     help="the same workload with head-major pages [P][Hkv][ps][D]")
+    ap.add_argument("--head-dim", type=int, default=128, choices=(64, 128, 256),
+                    help="the same workload at another head_dim (256: plain decode only)")
     ap.add_argument("--rope", action="store_true",
                     help="plain decode workloads: LLaMA-style RoPE on the fly "
                          "(theta 1e4, scale 1)")
@@ -95,7 +97,8 @@ def main():
     torch.cuda.set_device(0)
     t_gen = time.perf_counter()
     append = args.workload in W.APPEND_WORKLOADS
-    wl = (W.make_append if append else W.make)(args.workload, seed=args.seed)
+    wl = (W.make_append if append else W.make)(args.workload, seed=args.seed,
+                                               head_dim=args.head_dim)
     if isinstance(wl, dict):                   # long32_fp8: ps 1 and ps 16 variants
         wl = wl[args.page_size]
     if args.ragged:
@@ -145,7 +148,8 @@ def main():
     if append:
         rope_extra.update(qo_indptr=w.qo_indptr, causal=w.causal)
     rope_kw = dict(pos_encoding="rope_llama", rope_theta=1e4, rope_scale=1.0) if args.rope else {}
-    traffic_key = w.name + ("+rope" if args.rope else "")
+    traffic_key = (w.name + ("+rope" if args.rope else "") +
+                   (f"+d{w.head_dim}" if w.head_dim != 128 else ""))
 
     # ---- plan stage (host), timed separately; first call includes first use
     t0 = time.perf_counter()

@@ -57,7 +57,8 @@
  * (kv_indices, and the device copies of kv_indptr / last_page_len) are
  * trusted: they must describe the same tables that were planned.
  *
- * Supported: head_dim 128; q in fp16 or bf16; KV in the q dtype or OCP E4M3
+ * Supported: head_dim 64, 128 or 256 (256: decode without a cascade level;
+ * RoPE: 128 only); q in fp16 or bf16; KV in the q dtype or OCP E4M3
  * (e4m3fn); 1 <= num_qo_heads / num_kv_heads <= 16; any page_size >= 1;
  * LLaMA-style RoPE on the fly for plain decode; batch append (causal or
  * not) on the same page tables.
@@ -104,7 +105,7 @@ typedef struct {
   int32_t batch;          /* number of requests B >= 0 */
   int32_t num_qo_heads;   /* Hq */
   int32_t num_kv_heads;   /* Hkv, divides Hq */
-  int32_t head_dim;       /* D (128) */
+  int32_t head_dim;       /* D: 64, 128 or 256 */
   int32_t page_size;      /* tokens per page, >= 1 */
   fi_dtype q_dtype;       /* FI_F16 or FI_BF16; o has this dtype */
   fi_dtype kv_dtype;      /* q_dtype or FI_E4M3 */
@@ -134,8 +135,8 @@ typedef struct {
   float rope_theta;       /* <= 0: 1e4 */
   float rope_scale;       /* <= 0: 1 */
   /* Append mode (FlashInfer README append example:
-   * single_prefill_with_kv_cache(q, k, v, causal=True), "the last 128 tokens
-   * in the KV-Cache are the new tokens"; batch form over qo_indptr):
+   * single_prefill_with_kv_cache(q, k, v, causal=True), its queries being
+   * the newest 128 tokens of the KV cache; batch form over qo_indptr):
    * qo_indptr != NULL gives request r the query tokens
    * [qo_indptr[r], qo_indptr[r+1]) of q [total_q][Hq][D], which are the LAST
    * n_r = qo_indptr[r+1] - qo_indptr[r] <= kv_len_r tokens of its keys:

@@ -45,8 +45,9 @@
  *     (the other value of the registry quickstart's kv_layout argument)
  *     stores each page head-major, [num_pages][Hkv][page_size][D];
  *   - append attention (README example: single_prefill_with_kv_cache with
- *     causal=True, where "the last 128 tokens in the KV-Cache are the new
- *     tokens"; "check out ... batch decode/append/prefill"): request r has
+ *     causal=True, whose queries are the newest 128 tokens of the KV cache;
+ *     the README also points to batch forms of decode, append and
+ *     prefill): request r has
  *     n_r = qo_indptr[r+1] - qo_indptr[r] query tokens, which are the LAST
  *     n_r of its L keys, so query i (0-based) sits at position L - n_r + i;
  *     with the causal mask it attends keys 0 .. L - n_r + i, without it all

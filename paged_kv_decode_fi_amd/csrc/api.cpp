@@ -19,12 +19,11 @@
 
 namespace fi {
 hipError_t launch_decode(const DecodeParams& p, int num_tiles, int waves, bool q_bf16,
-                         int kv, bool fold, hipStream_t s);
+                         int kv, bool fold, int head_dim, hipStream_t s);
 hipError_t launch_prefix(const DecodeParams& p, int num_tiles, int waves, bool append,
-                         bool q_bf16, int kv,
-                         hipStream_t s);
+                         bool q_bf16, int kv, int head_dim, hipStream_t s);
 hipError_t launch_merge_partials(const MergeParams& p, int num_units, bool o_bf16, bool wide,
-                                 hipStream_t s);
+                                 int head_dim, hipStream_t s);
 hipError_t launch_merge_states(const MergeStatesParams& p, hipStream_t s);
 hipError_t launch_gather(const int32_t* kv_indptr, const int32_t* kv_indices,
                          const int64_t* token_indptr, int batch, int page_size,
@@ -164,7 +163,7 @@ fi::DecodeParams base_params(const fi_plan_s* pl, const void* q, const void* k,
   }
   p.ragged = hp.ragged;
   {
-    const uint32_t rowb = hp.kv_dtype == FI_E4M3 ? 128u : 256u;
+    const uint32_t rowb = (uint32_t)hp.D * (hp.kv_dtype == FI_E4M3 ? 1u : 2u);
     const uint32_t ps = (uint32_t)hp.page_size, hkv = (uint32_t)hp.Hkv;
     p.page_bytes = ps * hkv * rowb;
     p.slot_stride = hp.hnd ? rowb : hkv * rowb;
@@ -187,7 +186,7 @@ fi_status launch_merge(const fi_plan_s* pl, void* o, float* lse, hipStream_t s) 
   m.G = hp.G;
   m.out_dtype = hp.q_dtype;
   hipError_t e = fi::launch_merge_partials(m, (int)hp.num_merge_units, hp.q_dtype == FI_BF16,
-                                          hp.merge_wide != 0, s);
+                                          hp.merge_wide != 0, hp.D, s);
   return e == hipSuccess ? FI_OK : hip_fail(e, "merge launch");
 }
 
@@ -386,7 +385,8 @@ fi_status enqueue_run(fi_plan_t plan, int stages, const void* q, const void* k_p
     pp.kv_indptr = kv_indptr;
     pp.kv_indices = kv_indices;
     pp.qo_indptr = qo_all;
-    e = fi::launch_prefix(pp, (int)hp.num_prefix_tiles, hp.prefix_waves, true, qbf, kv, s);
+    e = fi::launch_prefix(pp, (int)hp.num_prefix_tiles, hp.prefix_waves, true, qbf, kv, hp.D,
+                          s);
     if (e != hipSuccess) return hip_fail(e, "append launch");
   } else if (do_prefix) {
     // prefix tiles of level l read that level's table; row -> request = the
@@ -404,7 +404,7 @@ fi_status enqueue_run(fi_plan_t plan, int stages, const void* q, const void* k_p
                                (int64_t)l * hp.batch
                          : nullptr;
       pp.num_tiles = (int32_t)(hp.num_tiles + hp.level_tile_off[l]);
-      e = fi::launch_prefix(pp, (int)n, hp.prefix_waves, false, qbf, kv, s);
+      e = fi::launch_prefix(pp, (int)n, hp.prefix_waves, false, qbf, kv, hp.D, s);
       if (e != hipSuccess) return hip_fail(e, "prefix launch");
     }
   }
@@ -412,7 +412,7 @@ fi_status enqueue_run(fi_plan_t plan, int stages, const void* q, const void* k_p
     p.kv_indptr = kv_indptr;
     p.kv_indices = kv_indices;
     e = fi::launch_decode(p, (int)hp.num_tiles, hp.heads_per_tile, qbf, kv, hp.num_folded > 0,
-                          s);
+                          hp.D, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
   }
   if (stages & kStageMerge) return launch_merge(plan, o, lse, s);

@@ -76,14 +76,14 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr float kLazyMax = 8.f;
 constexpr int kStep = 16;
 
-template <int KV>
+template <int KV, int D>
 struct Stage {
-  static constexpr int ROWB = KV == kKvE4M3 ? 128 : 256;  // K/V row bytes in HBM
+  static constexpr int ROWB = KV == kKvE4M3 ? D : 2 * D;  // K/V row bytes in HBM
   static constexpr int VR = ROWB / 16;                    // 16-B vectors per row
   static constexpr int LOADS = ROWB / 64;                 // vectors per thread per pool per step
   static constexpr int TOK_PER_U = 64 / VR;               // token advance per load index u
   static __host__ __device__ constexpr int k_stride(int W) { return W * ROWB + 16; }
-  static __host__ __device__ constexpr int v_stride(int W) { return W * 256 + 32; }
+  static __host__ __device__ constexpr int v_stride(int W) { return W * 2 * D + 32; }
   static __host__ __device__ constexpr int lds_bytes(int W) {
     return kStep * (k_stride(W) + v_stride(W));
   }
@@ -107,18 +107,19 @@ __device__ __forceinline__ f32x4 mma16x16x16(u32x2 a, u32x2 b, f32x4 c) {
 // 2^(s_c - M) and contributes that times o_c; the reference moves up to s_c
 // when s_c is larger, so every weight stays <= 1.  One state per round trip
 // (the fold runs once per tile; its registers stay within the main loop's).
+template <int D>
 __device__ __forceinline__ void fold_states(const float* __restrict__ partial_o,
                                             const float* __restrict__ partial_lse,
                                             int slot_base, int nst, int Hkv, int h, int G, int n,
-                                            int g, f32x4 (&A)[8], float& M, float& S) {
+                                            int g, f32x4 (&A)[D / 16], float& M, float& S) {
   const int nn = n < G ? n : 0, col = 4 * g;
   for (int c = 0; c < nst; ++c) {
     const int64_t row = ((int64_t)slot_base + (int64_t)c * Hkv + h) * G + nn;
     const float s = partial_lse[row];
-    const float* po = partial_o + row * kHeadDim + col;
-    f32x4 o[8];
+    const float* po = partial_o + row * D + col;
+    f32x4 o[D / 16];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) o[b] = *reinterpret_cast<const f32x4*>(po + 16 * b);
+    for (int b = 0; b < D / 16; ++b) o[b] = *reinterpret_cast<const f32x4*>(po + 16 * b);
     // branch-free (selects keep one copy of A live): new reference
     // M' = max(M, s), old mass scaled by 2^(M - M'), state weight 2^(s - M')
     const float Mn = fmaxf(M, s);
@@ -126,7 +127,7 @@ __device__ __forceinline__ void fold_states(const float* __restrict__ partial_o,
     const float w = s == -INFINITY ? 0.f : fast_exp2(s - Mn);
     S = S * f + w;
 #pragma unroll
-    for (int b = 0; b < 8; ++b) A[b] = A[b] * f + w * o[b];
+    for (int b = 0; b < D / 16; ++b) A[b] = A[b] * f + w * o[b];
     M = Mn;
   }
 }
@@ -224,10 +225,11 @@ hipError_t launch_rope_table(void* table, int rows, float theta, float scale, hi
 // (padded: conflict-free reads of one row per lane) and table rows 0..15.
 constexpr int kRopeLdsStride = kRopeRowBytes + 16;
 constexpr int kRopeLds = kStep * kRopeLdsStride + kStep * kRopeRowBytes;
-template <int KV, bool QBF16, bool PS_POW2, bool FOLD, int DEPTH, bool ROPE>
+template <int KV, bool QBF16, bool PS_POW2, bool FOLD, int DEPTH, bool ROPE, int D>
 __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams p) {
   static_assert(!ROPE || !FOLD, "RoPE plans have no cascade level to fold");
-  using S = Stage<KV>;
+  static_assert(!ROPE || D == kHeadDim, "the RoPE table is built for head_dim 128");
+  using S = Stage<KV, D>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int W = blockDim.x >> 6;                  // waves = kv heads of the tile
   const int tid = threadIdx.x;
@@ -250,13 +252,13 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   const float2* r16 = reinterpret_cast<const float2*>(rlds + kStep * kRopeLdsStride);
 
   // q of this wave's head group as the B operand of the score MFMAs
-  u32x4 qop[4];
+  u32x4 qop[D / 32];
   {
     const bool ok = n < G;
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
-                           ((int64_t)r * p.Hq + h * G + (ok ? n : 0)) * kHeadDim;
+                           ((int64_t)r * p.Hq + h * G + (ok ? n : 0)) * D;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < D / 32; ++s) {
       u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * g);
       qop[s] = ok ? v : u32x4{0, 0, 0, 0};
     }
@@ -349,13 +351,13 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   };
 
   float m = -INFINITY, l = 0.f;
-  f32x4 oacc[8];
+  f32x4 oacc[D / 16];
 #pragma unroll
-  for (int b = 0; b < 8; ++b) oacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < D / 16; ++b) oacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   // this lane's LDS addresses: K row of token n; V^T source row 4g + n/4 at
   // d-quad n % 4 (transpose-read layout)
   const uint8_t* krow = klds + n * KS + wave * S::ROWB;
-  const uint8_t* vsrc = vlds + (4 * g + (n >> 2)) * VS + wave * 256 + 8 * (n & 3);
+  const uint8_t* vsrc = vlds + (4 * g + (n >> 2)) * VS + wave * (2 * D) + 8 * (n & 3);
 
   auto compute = [&](int step) {
     const int tb = t0 + kStep * step;
@@ -385,7 +387,7 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
       }
     } else {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) sc = mma16x16x32<QBF16>(kop_of(s), qop[s], sc);
+      for (int s = 0; s < D / 32; ++s) sc = mma16x16x32<QBF16>(kop_of(s), qop[s], sc);
     }
     float x[4];
 #pragma unroll
@@ -404,7 +406,7 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
       const float alpha = fast_exp2(m - m_new);   // m = -inf first: 0
       l *= alpha;
 #pragma unroll
-      for (int bb = 0; bb < 8; ++bb) oacc[bb] *= alpha;
+      for (int bb = 0; bb < D / 16; ++bb) oacc[bb] *= alpha;
       m = m_new;
     }
     // every step has a valid token, so m is finite here
@@ -420,7 +422,7 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
       plo = u32x2{pack2<true>(pr[0] - lo16<true>(pop.x), pr[1] - hi16<true>(pop.x)),
                   pack2<true>(pr[2] - lo16<true>(pop.y), pr[3] - hi16<true>(pop.y))};
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb) {
+    for (int bb = 0; bb < D / 16; ++bb) {
       const s16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vsrc + 32 * bb));
       oacc[bb] = mma16x16x16<QBF16>(__builtin_bit_cast(u32x2, vt), pop, oacc[bb]);
       if constexpr (KV == kKvBF16)
@@ -493,18 +495,18 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
     if (FOLD && tile.row1 > 0) {
       if (KV == kKvE4M3) {
 #pragma unroll
-        for (int b = 0; b < 8; ++b) oacc[b] *= vs;
+        for (int b = 0; b < D / 16; ++b) oacc[b] *= vs;
         osc = 1.f;
       }
-      fold_states(p.partial_o, p.partial_lse, fold_base, tile.row1, p.Hkv, h, G, n, g, oacc,
+      fold_states<D>(p.partial_o, p.partial_lse, fold_base, tile.row1, p.Hkv, h, G, n, g, oacc,
                   M, S);
     }
     const float inv = (S > 0.f ? 1.f / S : 0.f) * osc;
     const float lse2 = S > 0.f ? M + fast_log2(S) : -INFINITY;
     if (n < G) {
-      uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)r * p.Hq + j) * kHeadDim;
+      uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)r * p.Hq + j) * D;
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
+      for (int b = 0; b < D / 16; ++b) {
         u32x2 w = {pack2<QBF16>(oacc[b][0] * inv, oacc[b][1] * inv),
                    pack2<QBF16>(oacc[b][2] * inv, oacc[b][3] * inv)};
         *reinterpret_cast<u32x2*>(orow + 16 * b + 4 * g) = w;
@@ -517,9 +519,9 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   const float lse2 = lt > 0.f ? m + fast_log2(lt) : -INFINITY;
   const int64_t slot = tile.slot + wave;
   if (n < G) {
-    float* po = p.partial_o + (slot * G + n) * kHeadDim;
+    float* po = p.partial_o + (slot * G + n) * D;
 #pragma unroll
-    for (int b = 0; b < 8; ++b)
+    for (int b = 0; b < D / 16; ++b)
       *reinterpret_cast<f32x4*>(po + 16 * b + 4 * g) = oacc[b] * inv;
     if (g == 0) p.partial_lse[slot * G + n] = lse2;
   }
@@ -555,11 +557,11 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
 constexpr int kPStep = 32;
 constexpr float kPrefixLazySum = 256.f;
 
-template <int KV>
+template <int KV, int D>
 struct PStage {
-  static constexpr int ROWB = KV == kKvE4M3 ? 128 : 256;   // K row bytes kept in LDS
+  static constexpr int ROWB = KV == kKvE4M3 ? D : 2 * D;    // K row bytes kept in LDS
   static constexpr int KS = ROWB + 16;                      // K LDS row stride
-  static constexpr int VS = 256 + 32;                       // V LDS row stride (16-bit values)
+  static constexpr int VS = 2 * D + 32;                     // V LDS row stride (16-bit values)
   static constexpr int BUF = kPStep * (KS + VS);
   static constexpr int PTAB = kPrefixMaxChunk + 2;          // page-table slots (page_size 1)
   static constexpr int LDS = 2 * BUF + 4 * PTAB;
@@ -572,9 +574,10 @@ __device__ __forceinline__ int xcd_tile(int b, int n) {
   return x * per + min(x, rem) + k;
 }
 
-template <int KV, bool QBF16, int WAVES, bool PS_POW2, bool APPEND>
+template <int KV, bool QBF16, int WAVES, bool PS_POW2, bool APPEND, int D>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(DecodeParams p) {
-  using S = PStage<KV>;
+  static_assert(D == 64 || D == 128, "two row tiles of 256 dims do not fit the registers");
+  using S = PStage<KV, D>;
   // bf16 append tiles: P.V takes p as a bf16 high part plus a bf16
   // residual -- bf16 keeps 8 bits of p, and when a few keys carry
   // comparable weight (the first rows of a prefill see a handful of keys)
@@ -609,7 +612,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
   }
 
   // query rows of this lane's two column tiles (B operands of the scores)
-  u32x4 qop[2][4];
+  u32x4 qop[2][D / 32];
   bool rok[2];
   int rreq[2], rj[2];
 #pragma unroll
@@ -620,9 +623,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
     rreq[rt] = qo0 + rr / G;
     rj[rt] = h * G + rr % G;
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
-                           ((int64_t)rreq[rt] * p.Hq + rj[rt]) * kHeadDim;
+                           ((int64_t)rreq[rt] * p.Hq + rj[rt]) * D;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < D / 32; ++s) {
       u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * g);
       qop[rt][s] = rok[rt] ? v : u32x4{0, 0, 0, 0};
     }
@@ -701,11 +704,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
   };
 
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-  f32x4 oacc[2][8];
+  f32x4 oacc[2][D / 16];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) oacc[rt][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < D / 16; ++b) oacc[rt][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // one 32-token step from LDS buffer buf; a step reaching past the
   // smallest row limit masks tokens at or past each row's limit (a uniform
@@ -715,12 +718,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
     const uint8_t* kt = lds + buf * S::BUF;
     const uint8_t* vt = kt + kPStep * S::KS;
     // ---- K operands of both token tiles (tokens 16 tt + n), all k slices
-    u32x4 kop[2][4];
+    u32x4 kop[2][D / 32];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const uint8_t* krow = kt + (16 * tt + n) * S::KS;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < D / 32; ++s) {
         if constexpr (F8) {
           const u32x2 w8 = *reinterpret_cast<const u32x2*>(krow + 32 * s + 8 * g);
           const u32x2 a = e4m3x4_to_16<QBF16>(w8.x), b = e4m3x4_to_16<QBF16>(w8.y);
@@ -732,10 +735,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
     }
     // ---- V^T operands: contraction element kk of lane group g is token
     // 4 g + (kk & 3) + 16 (kk >> 2); two transpose reads per dim block b
-    u32x4 vop[8];
+    u32x4 vop[D / 16];
     const uint8_t* vsrc = vt + (4 * g + (n >> 2)) * S::VS + 8 * (n & 3);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
+    for (int b = 0; b < D / 16; ++b) {
       const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vsrc + 32 * b));
       const s16x4 v1 =
           __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vsrc + 16 * S::VS + 32 * b));
@@ -748,7 +751,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) sc[tt][0] = sc[tt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < D / 32; ++s)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -789,7 +792,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
         const float alpha = fast_exp2(m[rt] - m_use);
         l[rt] *= alpha;
 #pragma unroll
-        for (int b = 0; b < 8; ++b) oacc[rt][b] *= alpha;
+        for (int b = 0; b < D / 16; ++b) oacc[rt][b] *= alpha;
         m[rt] = m_new;
 #pragma unroll
         for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(__builtin_fmaf(x[i], c, -m_use));
@@ -810,7 +813,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
     // ---- P.V on MFMA 16x16x32
     if constexpr (SPLITP) {
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
+      for (int b = 0; b < D / 16; ++b) {
         oacc[0][b] = mma16x16x32<QBF16>(vop[b], pop[0], oacc[0][b]);
         oacc[1][b] = mma16x16x32<QBF16>(vop[b], pop[1], oacc[1][b]);
         oacc[0][b] = mma16x16x32<QBF16>(vop[b], plo[0], oacc[0][b]);
@@ -818,7 +821,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
       }
     } else {
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
+      for (int b = 0; b < D / 16; ++b) {
         oacc[0][b] = mma16x16x32<QBF16>(vop[b], pop[0], oacc[0][b]);
         oacc[1][b] = mma16x16x32<QBF16>(vop[b], pop[1], oacc[1][b]);
       }
@@ -857,9 +860,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
     const int r = rreq[rt], j = rj[rt];
     const ReqInfo ri = p.req_info[r];
     if (ri.n_states <= 1) {
-      uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)r * p.Hq + j) * kHeadDim;
+      uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)r * p.Hq + j) * D;
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
+      for (int b = 0; b < D / 16; ++b) {
         u32x2 w = {pack2<QBF16>(oacc[rt][b][0] * inv, oacc[rt][b][1] * inv),
                    pack2<QBF16>(oacc[rt][b][2] * inv, oacc[rt][b][3] * inv)};
         *reinterpret_cast<u32x2*>(orow + 16 * b + 4 * g) = w;
@@ -869,9 +872,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
       // state index: this level's chunk after the request's earlier levels
       const int c = tile.slot + (p.state_off ? p.state_off[r] : 0);
       const int64_t slot = ri.slot_base + (int64_t)c * p.Hkv + h;
-      float* po = p.partial_o + (slot * G + (j - h * G)) * kHeadDim;
+      float* po = p.partial_o + (slot * G + (j - h * G)) * D;
 #pragma unroll
-      for (int b = 0; b < 8; ++b)
+      for (int b = 0; b < D / 16; ++b)
         *reinterpret_cast<f32x4*>(po + 16 * b + 4 * g) = oacc[rt][b] * inv;
       if (g == 0) p.partial_lse[slot * G + (j - h * G)] = lse2;
     }
@@ -889,29 +892,29 @@ static int getenv_depth() {
   return d;
 }
 
-template <int KV, bool QBF16, bool FOLD, int DEPTH, bool ROPE = false>
+template <int KV, bool QBF16, bool FOLD, int DEPTH, bool ROPE, int D>
 static hipError_t launch_decode_t(const DecodeParams& p, int num_tiles, int waves,
                                   hipStream_t s) {
   constexpr int rope_lds = ROPE ? kRopeLds : 0;
-  const size_t lds = (size_t)Stage<KV>::lds_bytes(waves) + rope_lds;
+  const size_t lds = (size_t)Stage<KV, D>::lds_bytes(waves) + rope_lds;
   // dynamic LDS above 64 KiB must be allowed per kernel (once per process)
   static const hipError_t attr = [] {
-    const int max_lds = Stage<KV>::lds_bytes(kWavesPerTile) + rope_lds;
+    const int max_lds = Stage<KV, D>::lds_bytes(kWavesPerTile) + rope_lds;
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, true, FOLD, DEPTH, ROPE>),
+        reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, true, FOLD, DEPTH, ROPE, D>),
         hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
     if (e == hipSuccess)
       e = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, false, FOLD, DEPTH, ROPE>),
+          reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, false, FOLD, DEPTH, ROPE, D>),
           hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
     return e;
   }();
   if (attr != hipSuccess) return attr;
   if (p.ps_shift >= 0)
-    hipLaunchKernelGGL((decode_kernel<KV, QBF16, true, FOLD, DEPTH, ROPE>), dim3(num_tiles),
+    hipLaunchKernelGGL((decode_kernel<KV, QBF16, true, FOLD, DEPTH, ROPE, D>), dim3(num_tiles),
                        dim3(64 * waves), lds, s, p);
   else
-    hipLaunchKernelGGL((decode_kernel<KV, QBF16, false, FOLD, DEPTH, ROPE>), dim3(num_tiles),
+    hipLaunchKernelGGL((decode_kernel<KV, QBF16, false, FOLD, DEPTH, ROPE, D>), dim3(num_tiles),
                        dim3(64 * waves), lds, s, p);
   return hipGetLastError();
 }
@@ -919,66 +922,98 @@ static hipError_t launch_decode_t(const DecodeParams& p, int num_tiles, int wave
 // The fold instance (cascade suffix tiles, planned as few long 2-head
 // tiles) keeps two steps of loads in flight; the plain instance keeps one,
 // so that two 8-wave workgroups fit on a compute unit (two steps measured
-// no faster for the plain workloads).
-template <int KV, bool QBF16>
+// no faster for the plain workloads).  head_dim 256 is built for plain
+// decode only (no RoPE table, no cascade level), one step in flight: its
+// K/V registers of one step already take 64 VGPRs.
+template <int KV, bool QBF16, int D>
 static hipError_t launch_decode_f(const DecodeParams& p, int num_tiles, int waves, bool fold,
                                   hipStream_t s) {
   if (num_tiles <= 0) return hipSuccess;
-  if (p.rope_table)
-    return getenv_depth() == 1 ? launch_decode_t<KV, QBF16, false, 1, true>(p, num_tiles, waves, s)
-                               : launch_decode_t<KV, QBF16, false, 2, true>(p, num_tiles, waves, s);
-  const bool deep = fold && waves <= 4 && getenv_depth() != 1;
-  if (fold)
-    return deep ? launch_decode_t<KV, QBF16, true, 2>(p, num_tiles, waves, s)
-                : launch_decode_t<KV, QBF16, true, 1>(p, num_tiles, waves, s);
-  return deep ? launch_decode_t<KV, QBF16, false, 2>(p, num_tiles, waves, s)
-              : launch_decode_t<KV, QBF16, false, 1>(p, num_tiles, waves, s);
+  if constexpr (D == 256) {
+    if (fold || p.rope_table) return hipErrorInvalidValue;
+    return launch_decode_t<KV, QBF16, false, 1, false, D>(p, num_tiles, waves, s);
+  } else {
+    if (p.rope_table) {
+      if constexpr (D != kHeadDim) return hipErrorInvalidValue;
+      else
+        return getenv_depth() == 1
+                   ? launch_decode_t<KV, QBF16, false, 1, true, D>(p, num_tiles, waves, s)
+                   : launch_decode_t<KV, QBF16, false, 2, true, D>(p, num_tiles, waves, s);
+    }
+    const bool deep = fold && waves <= 4 && getenv_depth() != 1;
+    if (fold)
+      return deep ? launch_decode_t<KV, QBF16, true, 2, false, D>(p, num_tiles, waves, s)
+                  : launch_decode_t<KV, QBF16, true, 1, false, D>(p, num_tiles, waves, s);
+    return deep ? launch_decode_t<KV, QBF16, false, 2, false, D>(p, num_tiles, waves, s)
+                : launch_decode_t<KV, QBF16, false, 1, false, D>(p, num_tiles, waves, s);
+  }
 }
 
-template <int KV, bool QBF16, int W, bool APPEND>
+template <int KV, bool QBF16, int W, bool APPEND, int D>
 static void launch_prefix_w(const DecodeParams& p, int num_tiles, hipStream_t s) {
   if (p.ps_shift >= 0)
-    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, W, true, APPEND>), dim3(num_tiles),
+    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, W, true, APPEND, D>), dim3(num_tiles),
                        dim3(64 * W), 0, s, p);
   else
-    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, W, false, APPEND>), dim3(num_tiles),
+    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, W, false, APPEND, D>), dim3(num_tiles),
                        dim3(64 * W), 0, s, p);
 }
 
-template <int KV, bool QBF16>
+template <int KV, bool QBF16, int D>
 static hipError_t launch_prefix_t(const DecodeParams& p, int num_tiles, int waves, bool append,
                                   hipStream_t s) {
   if (num_tiles <= 0) return hipSuccess;
   if (waves == 4)
-    append ? launch_prefix_w<KV, QBF16, 4, true>(p, num_tiles, s)
-           : launch_prefix_w<KV, QBF16, 4, false>(p, num_tiles, s);
+    append ? launch_prefix_w<KV, QBF16, 4, true, D>(p, num_tiles, s)
+           : launch_prefix_w<KV, QBF16, 4, false, D>(p, num_tiles, s);
   else
-    append ? launch_prefix_w<KV, QBF16, 8, true>(p, num_tiles, s)
-           : launch_prefix_w<KV, QBF16, 8, false>(p, num_tiles, s);
+    append ? launch_prefix_w<KV, QBF16, 8, true, D>(p, num_tiles, s)
+           : launch_prefix_w<KV, QBF16, 8, false, D>(p, num_tiles, s);
   return hipGetLastError();
 }
 
-// q_bf16: q (and o) are bf16, else fp16.  kv: KvKind.  fold: the work list
-// has tiles that fold earlier states into their output.
-hipError_t launch_decode(const DecodeParams& p, int num_tiles, int waves, bool q_bf16,
-                         int kv, bool fold, hipStream_t s) {
-  if (waves < 1 || waves > kWavesPerTile) return hipErrorInvalidValue;
+template <int D>
+static hipError_t launch_decode_d(const DecodeParams& p, int num_tiles, int waves, bool q_bf16,
+                                  int kv, bool fold, hipStream_t s) {
   if (kv == kKvE4M3)
-    return q_bf16 ? launch_decode_f<kKvE4M3, true>(p, num_tiles, waves, fold, s)
-                  : launch_decode_f<kKvE4M3, false>(p, num_tiles, waves, fold, s);
-  return q_bf16 ? launch_decode_f<kKvBF16, true>(p, num_tiles, waves, fold, s)
-                : launch_decode_f<kKvF16, false>(p, num_tiles, waves, fold, s);
+    return q_bf16 ? launch_decode_f<kKvE4M3, true, D>(p, num_tiles, waves, fold, s)
+                  : launch_decode_f<kKvE4M3, false, D>(p, num_tiles, waves, fold, s);
+  return q_bf16 ? launch_decode_f<kKvBF16, true, D>(p, num_tiles, waves, fold, s)
+                : launch_decode_f<kKvF16, false, D>(p, num_tiles, waves, fold, s);
 }
 
-// append: append tiles (rows limited by ReqInfo.kv_len), else cascade prefix.
-hipError_t launch_prefix(const DecodeParams& p, int num_tiles, int waves, bool append,
-                         bool q_bf16, int kv, hipStream_t s) {
-  if (waves != 4 && waves != 8) return hipErrorInvalidValue;
+template <int D>
+static hipError_t launch_prefix_d(const DecodeParams& p, int num_tiles, int waves, bool append,
+                                  bool q_bf16, int kv, hipStream_t s) {
   if (kv == kKvE4M3)
-    return q_bf16 ? launch_prefix_t<kKvE4M3, true>(p, num_tiles, waves, append, s)
-                  : launch_prefix_t<kKvE4M3, false>(p, num_tiles, waves, append, s);
-  return q_bf16 ? launch_prefix_t<kKvBF16, true>(p, num_tiles, waves, append, s)
-                : launch_prefix_t<kKvF16, false>(p, num_tiles, waves, append, s);
+    return q_bf16 ? launch_prefix_t<kKvE4M3, true, D>(p, num_tiles, waves, append, s)
+                  : launch_prefix_t<kKvE4M3, false, D>(p, num_tiles, waves, append, s);
+  return q_bf16 ? launch_prefix_t<kKvBF16, true, D>(p, num_tiles, waves, append, s)
+                : launch_prefix_t<kKvF16, false, D>(p, num_tiles, waves, append, s);
+}
+
+// q_bf16: q (and o) are bf16, else fp16.  kv: KvKind.  fold: the work list
+// has tiles that fold earlier states into their output.  head_dim: 64, 128
+// or 256.
+hipError_t launch_decode(const DecodeParams& p, int num_tiles, int waves, bool q_bf16,
+                         int kv, bool fold, int head_dim, hipStream_t s) {
+  if (waves < 1 || waves > kWavesPerTile) return hipErrorInvalidValue;
+  switch (head_dim) {
+    case 64: return launch_decode_d<64>(p, num_tiles, waves, q_bf16, kv, fold, s);
+    case 128: return launch_decode_d<128>(p, num_tiles, waves, q_bf16, kv, fold, s);
+    case 256: return launch_decode_d<256>(p, num_tiles, waves, q_bf16, kv, fold, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// append: append tiles (rows limited by ReqInfo.kv_len), else cascade
+// prefix.  head_dim: 64 or 128.
+hipError_t launch_prefix(const DecodeParams& p, int num_tiles, int waves, bool append,
+                         bool q_bf16, int kv, int head_dim, hipStream_t s) {
+  if (waves != 4 && waves != 8) return hipErrorInvalidValue;
+  if (head_dim == 64) return launch_prefix_d<64>(p, num_tiles, waves, append, q_bf16, kv, s);
+  if (head_dim == 128) return launch_prefix_d<128>(p, num_tiles, waves, append, q_bf16, kv, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fi

@@ -7,7 +7,9 @@
 
 namespace fi {
 
-constexpr int kHeadDim = 128;      // head_dim the kernels are built for
+// head_dim of the RoPE table and of the one-wave merge; the decode kernel is
+// built for head_dim 64, 128 and 256, the multi-row kernel for 64 and 128
+constexpr int kHeadDim = 128;
 constexpr int kMaxGroup = 16;      // q heads per kv head one MFMA column tile holds
 constexpr int kBlockTokens = 32;   // tokens per cascade-prefix step
 constexpr int kChunkAlign = 16;    // decode chunks are whole 16-token steps

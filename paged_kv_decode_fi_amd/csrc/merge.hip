@@ -35,16 +35,17 @@ __global__ __launch_bounds__(256) void merge_partials_kernel(MergeParams p) {
 }
 
 // Many units with few states each (append plans: one unit per query
-// token): one workgroup per (unit, 32 q heads), 8 threads per head with 16
-// dims each, every state's rows loaded by all threads at once.  One wave per
-// (unit, head) would spend most of its short life waiting on two dependent
-// round trips.
-template <bool OBF16>
+// token), and every head_dim other than 128: one workgroup per (unit,
+// 256 / (D / 16) q heads), D / 16 threads per head with 16 dims each, every
+// state's rows loaded by all threads at once.  One wave per (unit, head)
+// would spend most of its short life waiting on two dependent round trips.
+template <bool OBF16, int D>
 __global__ __launch_bounds__(256) void merge_units_wide_kernel(MergeParams p) {
+  constexpr int TPH = D / 16;   // threads per head
   const int t = threadIdx.x;
-  const int j = blockIdx.y * 32 + (t >> 3);
+  const int j = blockIdx.y * (256 / TPH) + t / TPH;
   if (j >= p.Hq) return;
-  const int d0 = 16 * (t & 7);
+  const int d0 = 16 * (t % TPH);
   const MergeUnit u = p.units[blockIdx.x];
   const int h = j / p.G, jj = j - h * p.G;
   const int64_t stride = (int64_t)p.Hkv * p.G;                  // rows between states
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(256) void merge_units_wide_kernel(MergeParams p) {
       const float w = fast_exp2(p.partial_lse[row0 + c * stride] - M);
       S += w;
       const f32x4* src =
-          reinterpret_cast<const f32x4*>(p.partial_o + (row0 + c * stride) * kHeadDim + d0);
+          reinterpret_cast<const f32x4*>(p.partial_o + (row0 + c * stride) * D + d0);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const f32x4 v = src[k];
@@ -73,26 +74,39 @@ __global__ __launch_bounds__(256) void merge_units_wide_kernel(MergeParams p) {
   }
   const float inv = S > 0.f ? 1.f / S : 0.f;
   u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.o) +
-                                        ((int64_t)u.req * p.Hq + j) * kHeadDim + d0);
+                                        ((int64_t)u.req * p.Hq + j) * D + d0);
 #pragma unroll
   for (int k = 0; k < 2; ++k)
     dst[k] = u32x4{pack2<OBF16>(acc[8 * k] * inv, acc[8 * k + 1] * inv),
                    pack2<OBF16>(acc[8 * k + 2] * inv, acc[8 * k + 3] * inv),
                    pack2<OBF16>(acc[8 * k + 4] * inv, acc[8 * k + 5] * inv),
                    pack2<OBF16>(acc[8 * k + 6] * inv, acc[8 * k + 7] * inv)};
-  if ((t & 7) == 0 && p.lse)
+  if (t % TPH == 0 && p.lse)
     p.lse[(int64_t)u.req * p.Hq + j] = S > 0.f ? (M + fast_log2(S)) * kLn2 : -INFINITY;
 }
 
+template <int D>
+static void launch_wide(const MergeParams& p, int num_units, bool o_bf16, hipStream_t s) {
+  constexpr int HPB = 256 / (D / 16);   // heads per workgroup
+  dim3 grid(num_units, (p.Hq + HPB - 1) / HPB);
+  if (o_bf16)
+    hipLaunchKernelGGL((merge_units_wide_kernel<true, D>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((merge_units_wide_kernel<false, D>), grid, dim3(256), 0, s, p);
+}
+
+// wide: the workgroup-per-unit kernel (required for head_dim != 128).
 hipError_t launch_merge_partials(const MergeParams& p, int num_units, bool o_bf16, bool wide,
-                                 hipStream_t s) {
+                                 int head_dim, hipStream_t s) {
   if (num_units <= 0) return hipSuccess;
+  if (head_dim != kHeadDim && !wide) return hipErrorInvalidValue;
   if (wide) {
-    dim3 grid(num_units, (p.Hq + 31) / 32);
-    if (o_bf16)
-      hipLaunchKernelGGL(merge_units_wide_kernel<true>, grid, dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL(merge_units_wide_kernel<false>, grid, dim3(256), 0, s, p);
+    switch (head_dim) {
+      case 64: launch_wide<64>(p, num_units, o_bf16, s); break;
+      case 128: launch_wide<128>(p, num_units, o_bf16, s); break;
+      case 256: launch_wide<256>(p, num_units, o_bf16, s); break;
+      default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
   }
   dim3 grid(num_units, (p.Hq + 3) / 4);

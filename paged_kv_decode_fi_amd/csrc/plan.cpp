@@ -165,7 +165,7 @@ int plan_append(const PlanInput& in, const std::vector<int64_t>& lens, int num_c
         slots += nc * Hkv;
         mu.push_back(MergeUnit{(int32_t)(qo[t.r] + i), ri.slot_base, (int32_t)nc, 0});
       }
-      if (slots > (int64_t)0x7fffffff / (G * kHeadDim))
+      if (slots > (int64_t)0x7fffffff / (G * in.D))
         PLAN_FAIL(2, "too many partial states; raise chunk_tokens");
     }
   }
@@ -241,7 +241,7 @@ int plan_append(const PlanInput& in, const std::vector<int64_t>& lens, int num_c
   out->causal = causal ? 1 : 0;
   out->ragged = in.ragged;
   out->hnd = in.hnd;
-  out->merge_wide = mu.size() >= 128 && max_states <= 8;
+  out->merge_wide = (mu.size() >= 128 && max_states <= 8) || in.D != kHeadDim;
   out->total_q = total_q;
   out->num_req_info = total_q;
   out->qo_len = B + 1;
@@ -257,7 +257,7 @@ int plan_append(const PlanInput& in, const std::vector<int64_t>& lens, int num_c
   L.qo_indptr_off = off;
   off = align256(off + sizeof(int32_t) * (size_t)(B + 1));
   L.partial_o_off = off;
-  off = align256(off + sizeof(float) * (size_t)slots * G * kHeadDim);
+  off = align256(off + sizeof(float) * (size_t)slots * G * in.D);
   L.partial_lse_off = off;
   off = align256(off + sizeof(float) * (size_t)slots * G);
   L.rope_off = off;
@@ -277,12 +277,13 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   const int G = in.Hq / Hkv;
   if (G > kMaxGroup)
     PLAN_FAIL(2, "group size %d > %d q heads per kv head is not built", G, kMaxGroup);
-  if (in.D != kHeadDim) PLAN_FAIL(2, "head_dim %d not built (only %d)", in.D, kHeadDim);
+  if (in.D != 64 && in.D != 128 && in.D != 256)
+    PLAN_FAIL(2, "head_dim %d not built (64, 128 or 256)", in.D);
   if (ps <= 0) PLAN_FAIL(1, "page_size must be >= 1 (got %d)", ps);
   if ((in.ragged != 0 && in.ragged != 1) || (in.hnd != 0 && in.hnd != 1) ||
       (in.ragged && in.hnd))
     PLAN_FAIL(1, "kv_layout must be FI_KV_PAGED, FI_KV_RAGGED or FI_KV_PAGED_HND");
-  if ((int64_t)ps * Hkv * kHeadDim * 2 > 0x7fffffff)
+  if ((int64_t)ps * Hkv * in.D * 2 > 0x7fffffff)
     PLAN_FAIL(2, "a page of %d tokens x %d kv heads is too large", ps, Hkv);
   if (in.ragged && ps != 1) PLAN_FAIL(1, "a ragged KV layout has page_size 1 (got %d)", ps);
   const int32_t* last_tab = in.ragged ? nullptr : in.last_page_len;
@@ -347,6 +348,10 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
     return false;
   };
   const int num_cus = in.num_cus > 0 ? in.num_cus : 256;
+  // head_dim 256: the multi-row kernel's two row tiles of 256 dims do not
+  // fit its registers, so neither append nor a cascade level is built
+  if (in.D == 256 && (in.append_qo_indptr || NG > 0))
+    PLAN_FAIL(2, "head_dim 256 is built for decode without a cascade level only");
   if (in.append_qo_indptr) {
     if (NG > 0) PLAN_FAIL(2, "append with a cascade level is not built");
     if (in.pos_encoding != 0) PLAN_FAIL(2, "append with RoPE is not built");
@@ -358,6 +363,8 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   const bool rope = in.pos_encoding == 1;
   if (rope && NG > 0)
     PLAN_FAIL(2, "RoPE with a cascade level is not built (plain decode only)");
+  if (rope && in.D != kHeadDim)
+    PLAN_FAIL(2, "RoPE is built for head_dim %d only (got %d)", kHeadDim, in.D);
   if (rope && (!(in.rope_theta == in.rope_theta) || !(in.rope_scale == in.rope_scale) ||
                in.rope_theta > 1e30f || in.rope_scale > 1e30f))
     PLAN_FAIL(1, "rope_theta and rope_scale must be finite");
@@ -497,7 +504,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
       slots += (folded[r] ? np : ns) * Hkv;
       if (!folded[r]) ++n_merge;
     }
-    if (slots > (int64_t)0x7fffffff / (G * kHeadDim))
+    if (slots > (int64_t)0x7fffffff / (G * in.D))
       PLAN_FAIL(2, "too many partial states; raise chunk_tokens");
   }
   out->merge_units = (MergeUnit*)malloc(sizeof(MergeUnit) * std::max<int64_t>(n_merge, 1));
@@ -596,7 +603,9 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   {
     int32_t ms = 0;
     for (int64_t k = 0; k < n_merge; ++k) ms = std::max(ms, out->merge_units[k].n_states);
-    out->merge_wide = n_merge >= 128 && ms <= 8;   // many units, few states each
+    // many units with few states each; the one-wave merge is built for
+    // head_dim 128 only
+    out->merge_wide = (n_merge >= 128 && ms <= 8) || in.D != kHeadDim;
   }
   out->num_folded = 0;
   for (int r = 0; r < B; ++r) out->num_folded += folded[r] ? 1 : 0;
@@ -618,7 +627,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   L.state_off_off = off;
   off = align256(off + sizeof(int32_t) * state_off.size());
   L.partial_o_off = off;
-  off = align256(off + sizeof(float) * (size_t)slots * G * kHeadDim);
+  off = align256(off + sizeof(float) * (size_t)slots * G * in.D);
   L.partial_lse_off = off;
   off = align256(off + sizeof(float) * (size_t)slots * G);
   out->rope = rope ? 1 : 0;

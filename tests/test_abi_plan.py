@@ -57,7 +57,7 @@ def test_host_validation_errors(fi):
     assert _status(fi, [0, 2, 5], [0, 16]) == 1                 # last_page_len 0
     assert _status(fi, [0, 2, 5], [3, 17]) == 1                 # last_page_len > ps
     assert _status(fi, [0, 2, 5], [3, 16], num_qo_heads=30) == 1  # Hq % Hkv
-    assert _status(fi, [0, 2, 5], [3, 16], head_dim=64) == 2    # not built
+    assert _status(fi, [0, 2, 5], [3, 16], head_dim=96) == 2    # not built
     assert _status(fi, [0, 2, 5], [3, 16], num_qo_heads=256) == 2  # G = 32 > 16
     assert _status(fi, [0, 2, 5], [3, 16], kv_dtype="bf16") == 2   # mixed dtype
     assert _status(fi, [0, 2, 5], [3, 16], q_dtype="e4m3", kv_dtype="e4m3") == 2
@@ -65,6 +65,39 @@ def test_host_validation_errors(fi):
     assert _status(fi, [0, 2, 5], [3, 16], chunk=40) == 1       # not a step multiple
     msg = fi.lib.fi_last_error().decode()
     assert "chunk_tokens" in msg
+
+
+def test_head_dim_rules(fi):
+    """head_dim 64, 128 and 256 are built for decode; 64 and 128 for a
+    cascade level and append (the multi-row kernel); RoPE for 128 only."""
+    indptr, last = [0, 2, 5], [3, 16]
+    prefix = (np.array([0, 2], np.int32), np.array([0, 1], np.int32),
+              np.array([16], np.int32))
+    for D in (64, 128, 256):
+        assert _status(fi, indptr, last, head_dim=D) == 0
+    for D in (32, 96, 512):
+        assert _status(fi, indptr, last, head_dim=D) == 2
+        assert "head_dim" in fi.lib.fi_last_error().decode()
+    assert _status(fi, indptr, last, head_dim=64, prefix=prefix) == 0
+    assert _status(fi, indptr, last, head_dim=256, prefix=prefix) == 2
+    assert "256" in fi.lib.fi_last_error().decode()
+    assert _status(fi, indptr, last, head_dim=64, pos_encoding="rope_llama") == 2
+    assert "RoPE" in fi.lib.fi_last_error().decode()
+    for D, want in ((64, 0), (256, 2)):
+        pr, keep = _problem(fi, indptr, last, head_dim=D)
+        qo = np.array([0, 1, 3], np.int32)
+        pr.qo_indptr, pr.causal = qo.ctypes.data, 1
+        n = ctypes.c_int64(0)
+        assert fi.lib.fi_debug_plan_tiles(ctypes.byref(pr), 256, None, 0, ctypes.byref(n)) == want
+
+
+def test_head_dim_workspace_scales(fi):
+    """The partial states hold head_dim floats per row: a split plan's
+    workspace grows with head_dim."""
+    indptr, last = [0, 40], [16]                  # one request of 640 tokens
+    sizes = [_workspace(fi, indptr, last, head_dim=D, chunk=64) for D in (64, 128, 256)]
+    assert all(st == 0 for st, _ in sizes)
+    assert sizes[0][1] < sizes[1][1] < sizes[2][1]
 
 
 def _workspace(fi, indptr, last, **kw):

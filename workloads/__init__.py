@@ -308,10 +308,11 @@ WORKLOADS = ("single_L2048_h32", "batch64_gqa4", "skewed128", "cascade256",
              "long32_fp8")
 
 
-def make(name: str, seed: Optional[int] = None, small: bool = False):
+def make(name: str, seed: Optional[int] = None, small: bool = False, head_dim: int = 128):
     """Named workload at full size, or a SMALL variant with the same structure
     (same heads, dtypes, page sizes, length mix shape; several tiles and a
-    ragged tail) that the oracle finishes in seconds.
+    ragged tail) that the oracle finishes in seconds.  head_dim other than
+    128 keeps every other parameter and the seeded length draw.
 
     long32_fp8 returns a dict {1: Paged, 16: Paged} with identical logical data.
     """
@@ -320,27 +321,27 @@ def make(name: str, seed: Optional[int] = None, small: bool = False):
     rng = np.random.default_rng(seed)
     if name == "single_L2048_h32":
         L = 300 if small else 2048
-        return build(name, [L], Hq=32, Hkv=32, ps=16, seed=seed,
+        return build(name, [L], Hq=32, Hkv=32, D=head_dim, ps=16, seed=seed,
                      pool_pages=(40 if small else 256))
     if name == "batch64_gqa4":
         B, lo, hi = (6, 1, 600) if small else (64, 512, 4096)
         lens = rng.integers(lo, hi + 1, size=B)
-        return build(name, lens, Hq=32, Hkv=8, ps=16, seed=seed)
+        return build(name, lens, Hq=32, Hkv=8, D=head_dim, ps=16, seed=seed)
     if name == "skewed128":
         nshort, nlong, cl, ch, mu, Llong = ((10, 2, 8, 256, math.log(64), 2048) if small
                                             else (120, 8, 64, 2048, math.log(512), 32768))
         short = np.clip(np.round(rng.lognormal(mu, 0.5, size=nshort)), cl, ch).astype(np.int64)
         lens = np.concatenate([short, np.full(nlong, Llong, np.int64)])
         lens = lens[rng.permutation(len(lens))]
-        return build(name, lens, Hq=32, Hkv=8, ps=16, seed=seed)
+        return build(name, lens, Hq=32, Hkv=8, D=head_dim, ps=16, seed=seed)
     if name == "cascade256":
         B, lo, hi, P = (8, 1, 100, 512) if small else (256, 128, 512, 8192)
         lens = rng.integers(lo, hi + 1, size=B)
-        return build(name, lens, Hq=64, Hkv=8, ps=16, q_dtype="bf16",
+        return build(name, lens, Hq=64, Hkv=8, D=head_dim, ps=16, q_dtype="bf16",
                      kv_dtype="bf16", seed=seed, prefix_len=P)
     if name == "long32_fp8":
         B, L = (3, 700) if small else (32, 32768)
-        return build(name, np.full(B, L, np.int64), Hq=64, Hkv=8, ps=16,
+        return build(name, np.full(B, L, np.int64), Hq=64, Hkv=8, D=head_dim, ps=16,
                      q_dtype="bf16", kv_dtype="e4m3", seed=seed,
                      extra_page_sizes=(1,))
     raise KeyError(name)
@@ -353,17 +354,19 @@ def make(name: str, seed: Optional[int] = None, small: bool = False):
 APPEND_WORKLOADS = ("append_single_q128", "append_batch16_q128")
 
 
-def make_append(name: str, seed: Optional[int] = None, small: bool = False):
+def make_append(name: str, seed: Optional[int] = None, small: bool = False,
+                head_dim: int = 128):
     idx = APPEND_WORKLOADS.index(name)
     seed = 2000 + idx if seed is None else seed
     rng = np.random.default_rng(seed)
     if name == "append_single_q128":
         L, n = (300, 40) if small else (2048, 128)
-        return build_append(name, [L], [n], Hq=32, Hkv=32, ps=16, seed=seed)
+        return build_append(name, [L], [n], Hq=32, Hkv=32, D=head_dim, ps=16, seed=seed)
     if name == "append_batch16_q128":
         B, lo, hi, n = (4, 1, 600, 48) if small else (16, 512, 4096, 128)
         lens = rng.integers(lo, hi + 1, size=B)
-        return build_append(name, lens, np.minimum(lens, n), Hq=32, Hkv=8, ps=16, seed=seed)
+        return build_append(name, lens, np.minimum(lens, n), Hq=32, Hkv=8, D=head_dim,
+                            ps=16, seed=seed)
     raise KeyError(name)
 
 
