@@ -203,15 +203,15 @@ __device__ __forceinline__ void rope_key8(u32x4 a, u32x4 b, const float4* cs, u3
 // in fp64 from the definition, stored as two fp32.
 __global__ void rope_table_kernel(float2* table, int rows, double theta, double scale) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)rows * (kHeadDim / 2)) return;
-  const int d = (int)(i / (kHeadDim / 2)), f = (int)(i % (kHeadDim / 2));
-  const double ang = (d / scale) * pow(theta, -2.0 * f / kHeadDim);
+  if (i >= (int64_t)rows * (kRopeHeadDim / 2)) return;
+  const int d = (int)(i / (kRopeHeadDim / 2)), f = (int)(i % (kRopeHeadDim / 2));
+  const double ang = (d / scale) * pow(theta, -2.0 * f / kRopeHeadDim);
   table[i] = float2{(float)cos(ang), (float)sin(ang)};
 }
 
 hipError_t launch_rope_table(void* table, int rows, float theta, float scale, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  const int64_t n = (int64_t)rows * (kHeadDim / 2);
+  const int64_t n = (int64_t)rows * (kRopeHeadDim / 2);
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                      reinterpret_cast<float2*>(table), rows, (double)theta, (double)scale);
   return hipGetLastError();
@@ -228,7 +228,7 @@ constexpr int kRopeLds = kStep * kRopeLdsStride + kStep * kRopeRowBytes;
 template <int KV, bool QBF16, bool PS_POW2, bool FOLD, int DEPTH, bool ROPE, int D>
 __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams p) {
   static_assert(!ROPE || !FOLD, "RoPE plans have no cascade level to fold");
-  static_assert(!ROPE || D == kHeadDim, "the RoPE table is built for head_dim 128");
+  static_assert(!ROPE || D == kRopeHeadDim, "the RoPE table is built for head_dim 128");
   using S = Stage<KV, D>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int W = blockDim.x >> 6;                  // waves = kv heads of the tile
@@ -934,7 +934,7 @@ static hipError_t launch_decode_f(const DecodeParams& p, int num_tiles, int wave
     return launch_decode_t<KV, QBF16, false, 1, false, D>(p, num_tiles, waves, s);
   } else {
     if (p.rope_table) {
-      if constexpr (D != kHeadDim) return hipErrorInvalidValue;
+      if constexpr (D != kRopeHeadDim) return hipErrorInvalidValue;
       else
         return getenv_depth() == 1
                    ? launch_decode_t<KV, QBF16, false, 1, true, D>(p, num_tiles, waves, s)

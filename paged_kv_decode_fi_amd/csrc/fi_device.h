@@ -112,28 +112,40 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // Merge of n attention states over disjoint key sets for one query row,
-// by one wave (2 dims per lane).  State c lives at row row0 + c * stride of
-// partial_o [.][kHeadDim] / partial_lse [.] (lse in log2 units):
+// by one wave (D / 64 dims per lane).  State c lives at row row0 + c * stride
+// of partial_o [.][D] / partial_lse [.] (lse in log2 units):
 //   M = max_c s_c, S = sum_c 2^(s_c - M), o = sum_c 2^(s_c - M) o_c / S,
 //   lse = (M + log2 S) ln 2; all states empty -> o = 0, lse = -inf.
 // Lanes read 64 lse values at a time; partial rows are read BATCH at a time
-// with independent loads issued together (BATCH 64 for rows with many
-// states).  The first batch of partial rows is issued before the lse pass:
-// its addresses do not depend on the lse values, so both are one round trip.
-template <bool OBF16, int BATCH>
+// (half of it at head_dim 256, for registers) with independent loads issued
+// together (BATCH 64 for rows with many states).  The first batch of partial
+// rows is issued before the lse pass: its addresses do not depend on the lse
+// values, so both are one round trip.
+template <int NV> struct LaneVec;
+template <> struct LaneVec<1> { using T = float; };
+template <> struct LaneVec<2> { using T = f32x2; };
+template <> struct LaneVec<4> { using T = f32x4; };
+
+template <bool OBF16, int BATCH, int D>
 __device__ __forceinline__ void merge_state_row(const float* __restrict__ partial_o,
                                                 const float* __restrict__ partial_lse,
                                                 int64_t row0, int64_t stride, int n,
-                                                uint32_t* orow, float* lse_out, int lane) {
-  const float* po = partial_o + row0 * kHeadDim + 2 * lane;
-  auto load_rows = [&](int c, int cnt, f32x2 (&v)[BATCH]) {
-#pragma unroll
-    for (int k = 0; k < BATCH; ++k)
-      v[k] = k < cnt ? *reinterpret_cast<const f32x2*>(po + (int64_t)(c + k) * stride * kHeadDim)
-                     : f32x2{0.f, 0.f};
+                                                uint16_t* orow, float* lse_out, int lane) {
+  constexpr int NV = D / 64;                          // dims per lane
+  constexpr int EB = NV == 4 ? BATCH / 2 : BATCH;     // rows per batch
+  using V = typename LaneVec<NV>::T;
+  auto elem = [](const V& x, int i) -> float {
+    if constexpr (NV == 1) return x;
+    else return x[i];
   };
-  f32x2 v[BATCH];
-  load_rows(0, min(n, BATCH), v);
+  const float* po = partial_o + row0 * D + NV * lane;
+  auto load_rows = [&](int c, int cnt, V (&v)[EB]) {
+#pragma unroll
+    for (int k = 0; k < EB; ++k)
+      v[k] = k < cnt ? *reinterpret_cast<const V*>(po + (int64_t)(c + k) * stride * D) : V{};
+  };
+  V v[EB];
+  load_rows(0, min(n, EB), v);
   const float s0 = lane < n ? partial_lse[row0 + lane * stride] : -INFINITY;
   float M = s0;
   for (int c0 = 64; c0 < n; c0 += 64) {
@@ -141,7 +153,10 @@ __device__ __forceinline__ void merge_state_row(const float* __restrict__ partia
     M = fmaxf(M, c < n ? partial_lse[row0 + c * stride] : -INFINITY);
   }
   M = wave_max(M);
-  float a0 = 0.f, a1 = 0.f, S = 0.f;
+  float a[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) a[i] = 0.f;
+  float S = 0.f;
   if (M != -INFINITY) {
     for (int c0 = 0; c0 < n; c0 += 64) {
       const int c = c0 + lane;
@@ -149,22 +164,29 @@ __device__ __forceinline__ void merge_state_row(const float* __restrict__ partia
       const float w = c < n ? fast_exp2(sc - M) : 0.f;
       S += w;
       const int cn = min(64, n - c0);
-      for (int k0 = 0; k0 < cn; k0 += BATCH) {
-        if (c0 + k0 > 0) load_rows(c0 + k0, min(BATCH, cn - k0), v);
+      for (int k0 = 0; k0 < cn; k0 += EB) {
+        if (c0 + k0 > 0) load_rows(c0 + k0, min(EB, cn - k0), v);
 #pragma unroll
-        for (int k = 0; k < BATCH; ++k) {
+        for (int k = 0; k < EB; ++k) {
           // uniform lane index: a scalar read of lane k0 + k's weight
           const float wk = __builtin_bit_cast(
               float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), (k0 + k) & 63));
-          a0 += wk * v[k].x;
-          a1 += wk * v[k].y;
+#pragma unroll
+          for (int i = 0; i < NV; ++i) a[i] += wk * elem(v[k], i);
         }
       }
     }
     S = wave_sum(S);
   }
   const float inv = S > 0.f ? 1.f / S : 0.f;
-  orow[lane] = pack2<OBF16>(a0 * inv, a1 * inv);
+  if constexpr (NV == 1) {
+    orow[lane] = (uint16_t)(pack2<OBF16>(a[0] * inv, 0.f) & 0xffffu);
+  } else if constexpr (NV == 2) {
+    reinterpret_cast<uint32_t*>(orow)[lane] = pack2<OBF16>(a[0] * inv, a[1] * inv);
+  } else {
+    reinterpret_cast<u32x2*>(orow)[lane] =
+        u32x2{pack2<OBF16>(a[0] * inv, a[1] * inv), pack2<OBF16>(a[2] * inv, a[3] * inv)};
+  }
   if (lane == 0 && lse_out) *lse_out = S > 0.f ? (M + fast_log2(S)) * kLn2 : -INFINITY;
 }
 

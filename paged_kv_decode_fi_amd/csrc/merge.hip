@@ -14,7 +14,7 @@
 namespace fi {
 
 // One wave per (merged request, q head); the arithmetic is merge_state_row.
-template <bool OBF16>
+template <bool OBF16, int D>
 __global__ __launch_bounds__(256) void merge_partials_kernel(MergeParams p) {
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.y * 4 + (threadIdx.x >> 6);
@@ -23,19 +23,18 @@ __global__ __launch_bounds__(256) void merge_partials_kernel(MergeParams p) {
   const int h = j / p.G, jj = j - h * p.G;
   const int64_t stride = (int64_t)p.Hkv * p.G;                  // rows between states
   const int64_t row0 = ((int64_t)u.slot_base + h) * p.G + jj;   // state 0's row
-  uint32_t* orow = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(p.o) +
-                                               ((int64_t)u.req * p.Hq + j) * kHeadDim);
+  uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)u.req * p.Hq + j) * D;
   float* lse_out = p.lse ? p.lse + (int64_t)u.req * p.Hq + j : nullptr;
   if (u.n_states > 16)
-    merge_state_row<OBF16, 64>(p.partial_o, p.partial_lse, row0, stride, u.n_states, orow,
-                               lse_out, lane);
+    merge_state_row<OBF16, 64, D>(p.partial_o, p.partial_lse, row0, stride, u.n_states, orow,
+                                  lse_out, lane);
   else
-    merge_state_row<OBF16, 16>(p.partial_o, p.partial_lse, row0, stride, u.n_states, orow,
-                               lse_out, lane);
+    merge_state_row<OBF16, 16, D>(p.partial_o, p.partial_lse, row0, stride, u.n_states, orow,
+                                  lse_out, lane);
 }
 
 // Many units with few states each (append plans: one unit per query
-// token), and every head_dim other than 128: one workgroup per (unit,
+// token): one workgroup per (unit,
 // 256 / (D / 16) q heads), D / 16 threads per head with 16 dims each, every
 // state's rows loaded by all threads at once.  One wave per (unit, head)
 // would spend most of its short life waiting on two dependent round trips.
@@ -86,34 +85,35 @@ __global__ __launch_bounds__(256) void merge_units_wide_kernel(MergeParams p) {
 }
 
 template <int D>
-static void launch_wide(const MergeParams& p, int num_units, bool o_bf16, hipStream_t s) {
-  constexpr int HPB = 256 / (D / 16);   // heads per workgroup
-  dim3 grid(num_units, (p.Hq + HPB - 1) / HPB);
-  if (o_bf16)
-    hipLaunchKernelGGL((merge_units_wide_kernel<true, D>), grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((merge_units_wide_kernel<false, D>), grid, dim3(256), 0, s, p);
-}
-
-// wide: the workgroup-per-unit kernel (required for head_dim != 128).
-hipError_t launch_merge_partials(const MergeParams& p, int num_units, bool o_bf16, bool wide,
-                                 int head_dim, hipStream_t s) {
-  if (num_units <= 0) return hipSuccess;
-  if (head_dim != kHeadDim && !wide) return hipErrorInvalidValue;
+static void launch_merge_d(const MergeParams& p, int num_units, bool o_bf16, bool wide,
+                           hipStream_t s) {
   if (wide) {
-    switch (head_dim) {
-      case 64: launch_wide<64>(p, num_units, o_bf16, s); break;
-      case 128: launch_wide<128>(p, num_units, o_bf16, s); break;
-      case 256: launch_wide<256>(p, num_units, o_bf16, s); break;
-      default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    constexpr int HPB = 256 / (D / 16);   // heads per workgroup
+    dim3 grid(num_units, (p.Hq + HPB - 1) / HPB);
+    if (o_bf16)
+      hipLaunchKernelGGL((merge_units_wide_kernel<true, D>), grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((merge_units_wide_kernel<false, D>), grid, dim3(256), 0, s, p);
+    return;
   }
   dim3 grid(num_units, (p.Hq + 3) / 4);
   if (o_bf16)
-    hipLaunchKernelGGL(merge_partials_kernel<true>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((merge_partials_kernel<true, D>), grid, dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(merge_partials_kernel<false>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((merge_partials_kernel<false, D>), grid, dim3(256), 0, s, p);
+}
+
+// wide: the workgroup-per-unit kernel (many units, few states each), else
+// one wave per (unit, q head).
+hipError_t launch_merge_partials(const MergeParams& p, int num_units, bool o_bf16, bool wide,
+                                 int head_dim, hipStream_t s) {
+  if (num_units <= 0) return hipSuccess;
+  switch (head_dim) {
+    case 64: launch_merge_d<64>(p, num_units, o_bf16, wide, s); break;
+    case 128: launch_merge_d<128>(p, num_units, o_bf16, wide, s); break;
+    case 256: launch_merge_d<256>(p, num_units, o_bf16, wide, s); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -241,7 +241,7 @@ int plan_append(const PlanInput& in, const std::vector<int64_t>& lens, int num_c
   out->causal = causal ? 1 : 0;
   out->ragged = in.ragged;
   out->hnd = in.hnd;
-  out->merge_wide = (mu.size() >= 128 && max_states <= 8) || in.D != kHeadDim;
+  out->merge_wide = mu.size() >= 128 && max_states <= 8;
   out->total_q = total_q;
   out->num_req_info = total_q;
   out->qo_len = B + 1;
@@ -363,8 +363,8 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   const bool rope = in.pos_encoding == 1;
   if (rope && NG > 0)
     PLAN_FAIL(2, "RoPE with a cascade level is not built (plain decode only)");
-  if (rope && in.D != kHeadDim)
-    PLAN_FAIL(2, "RoPE is built for head_dim %d only (got %d)", kHeadDim, in.D);
+  if (rope && in.D != kRopeHeadDim)
+    PLAN_FAIL(2, "RoPE is built for head_dim %d only (got %d)", kRopeHeadDim, in.D);
   if (rope && (!(in.rope_theta == in.rope_theta) || !(in.rope_scale == in.rope_scale) ||
                in.rope_theta > 1e30f || in.rope_scale > 1e30f))
     PLAN_FAIL(1, "rope_theta and rope_scale must be finite");
@@ -603,9 +603,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   {
     int32_t ms = 0;
     for (int64_t k = 0; k < n_merge; ++k) ms = std::max(ms, out->merge_units[k].n_states);
-    // many units with few states each; the one-wave merge is built for
-    // head_dim 128 only
-    out->merge_wide = (n_merge >= 128 && ms <= 8) || in.D != kHeadDim;
+    out->merge_wide = n_merge >= 128 && ms <= 8;   // many units, few states each
   }
   out->num_folded = 0;
   for (int r = 0; r < B; ++r) out->num_folded += folded[r] ? 1 : 0;

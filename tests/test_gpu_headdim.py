@@ -43,6 +43,25 @@ def test_decode_parity(fi, D, dt, chunk):
 
 
 @pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("kind", ["many_states", "many_units"])
+def test_merge_paths(fi, D, kind):
+    """The one-wave merge past 64 states (a 2600-token request in 32-token
+    chunks: 82 states, two rounds of lse reads) and the workgroup merge
+    (160 requests of 4 chunks each: >= 128 units with <= 8 states)."""
+    if kind == "many_states":
+        lens = [2600, 5, 300]
+    else:
+        lens = list(np.random.default_rng(D).integers(97, 129, size=160))
+    w = W.build(f"m{D}{kind}", lens, Hq=16, Hkv=4, D=D, ps=16, q_dtype="bf16", kv_dtype="bf16",
+                seed=D + len(kind))
+    o, lse, plan = C.run_gpu(w, chunk_tokens=32)
+    ro, rl = C.run_oracle(w)
+    st = plan.stats
+    C.assert_parity(w, o, lse, ro, rl, label=f"D{D} {kind} {st}")
+    assert st["num_merge_units"] == (2 if kind == "many_states" else 160)
+
+
+@pytest.mark.parametrize("D", [64, 256])
 @pytest.mark.parametrize("seed", range(6))
 def test_decode_fuzz_parity(fi, D, seed):
     """Group sizes 1..16, 1..8 kv heads, page sizes 1, 3 (not a power of
