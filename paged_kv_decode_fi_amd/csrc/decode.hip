@@ -16,8 +16,9 @@
 //    so the G query heads that share it read each K/V row once.  Per
 //    16-token step the workgroup streams the step's K and V rows of its W
 //    heads (W x row bytes contiguous per token: a whole 32 KiB page at
-//    W = Hkv = 8, page_size 16) with 16-byte non-temporal loads into padded
-//    LDS tiles; the next step's loads are in flight while a step computes.
+//    W = Hkv = 8, page_size 16, D 128 fp16) with 16-byte non-temporal loads
+//    into padded LDS tiles; the next step's loads are in flight while a
+//    step computes.
 //  * Scores S^T[token][head] = K . Q^T on MFMA 16x16x32 (K from LDS in the A
 //    operand, q in the B operand for the whole tile, columns n >= G zero).
 //    The D layout leaves lane (g, n) with tokens 4g..4g+3 of head n, so the
@@ -40,6 +41,9 @@
 //    against its own keys; described above the kernel.
 //  * K/V rows are addressed by page, slot and head strides: NHD or HND
 //    pages, or the ragged layout (page size 1, no page table).
+//  * head_dim D is a template parameter: D / 32 q operands and D / 16 output
+//    blocks per lane; decode for D = 64, 128, 256, prefix_kernel for 64 and
+//    128 (at 256 its two row tiles would not fit the registers).
 #include <type_traits>
 
 #include "fi_device.h"
@@ -61,9 +65,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // A workgroup of W waves owns W consecutive kv heads h0 .. h0+W-1 of one
 // request over a token chunk.  Per 16-token step it loads the K and V rows
 // of those heads for the 16 tokens -- W * row bytes contiguous per token, a
-// whole 32 KiB page when W = Hkv = 8 and page_size = 16 -- with 16-byte
-// non-temporal loads, 1 KiB contiguous per wave instruction, into padded LDS
-// tiles; then wave w computes kv head h0 + w from LDS:
+// whole 32 KiB page when W = Hkv = 8, page_size = 16 and D = 128 in fp16 --
+// with 16-byte non-temporal loads, 1 KiB contiguous per wave instruction,
+// into padded LDS tiles; then wave w computes kv head h0 + w from LDS:
 //   scores  S^T[token][head] = K . Q^T, MFMA 16x16x32 (K rows from LDS in A
 //           layout, q in B layout, columns past the group zero)
 //   softmax online, base 2, lazy running max (see kLazyMax)
