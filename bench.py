@@ -39,33 +39,37 @@ MFMA_PEAK_TFLOPS = 2500.0      # dense bf16 / fp16 MFMA
 ROTATE_BYTES = 1 << 30          # >= 1 GiB referenced per rotation cycle
 DECODE_SRC = os.path.join(ROOT, "paged_kv_decode_fi_amd", "csrc", "decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SRCS = [DECODE_SRC] + [os.path.join(ROOT, "paged_kv_decode_fi_amd", "csrc", f)
+                              for f in ("fi_device.h", "fi_internal.h")]
 
 
 def kernel_source_hash() -> str:
-    """sha256[:16] of decode.hip's code: every line with its // comment and
-    trailing blanks removed, blank lines dropped -- a comment edit keeps the
-    hash, any change to the code does not."""
+    """sha256[:16] of the kernels' code (decode.hip and the two headers it
+    includes): every line with its // comment and trailing blanks removed,
+    blank lines dropped -- a comment edit keeps the hash, any change to the
+    code does not."""
     import hashlib
     import re
     lines = []
-    for ln in open(DECODE_SRC, encoding="utf-8").read().splitlines():
-        ln = re.sub(r"//.*$", "", ln).rstrip()
-        if ln:
-            lines.append(ln)
+    for path in KERNEL_SRCS:
+        for ln in open(path, encoding="utf-8").read().splitlines():
+            ln = re.sub(r"//.*$", "", ln).rstrip()
+            if ln:
+                lines.append(ln)
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
     """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE runs (already scaled by the streaming-read calibration), or
-    None when there is no measurement for this workload or the kernel code
-    in decode.hip has changed since it was taken."""
+    None when there is no measurement for this workload or the kernels'
+    code has changed since it was taken."""
     try:
         rec = json.load(open(TRAFFIC_FILE))[workload]
         sha = kernel_source_hash()
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("decode_code_sha256_16") != sha:
+    if rec.get("kernel_code_sha256_16") != sha:
         return None
     return int(rec["fetch_bytes_per_launch"]) + int(rec["write_bytes_per_launch"])
 
