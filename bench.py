@@ -94,7 +94,7 @@ def parse():
     ap.add_argument("--hnd", action="store_true",
                     help="the same workload with head-major pages [P][Hkv][ps][D]")
     ap.add_argument("--head-dim", type=int, default=128, choices=(64, 128, 256),
-                    help="the same workload at another head_dim (256: plain decode only)")
+                    help="the same workload at another head_dim")
     ap.add_argument("--rope", action="store_true",
                     help="plain decode workloads: LLaMA-style RoPE on the fly "
                          "(theta 1e4, scale 1)")

@@ -35,15 +35,15 @@
 //    decode kernel turns each key by its distance from the query before the
 //    score MFMAs (described above rope_key8).
 //  * prefix_kernel: many query rows against one chunk of one key list, K/V
-//    staged in LDS and shared by 8 waves x 32 rows -- the G heads of every
-//    request of a cascade group against the shared prefix, or the query
-//    tokens of an append request (README append example, causal mask)
-//    against its own keys; described above the kernel.
+//    staged in LDS and shared by 8 waves x 32 rows (16 at head_dim 256) --
+//    the G heads of every request of a cascade group against the shared
+//    prefix, or the query tokens of an append request (README append
+//    example, causal mask) against its own keys; described above the kernel.
 //  * K/V rows are addressed by page, slot and head strides: NHD or HND
 //    pages, or the ragged layout (page size 1, no page table).
-//  * head_dim D is a template parameter: D / 32 q operands and D / 16 output
-//    blocks per lane; decode for D = 64, 128, 256, prefix_kernel for 64 and
-//    128 (at 256 its two row tiles would not fit the registers).
+//  * head_dim D (64, 128, 256) is a template parameter: D / 32 q operands
+//    and D / 16 output blocks per lane; at 256 prefix_kernel gives each wave
+//    one 16-row column tile instead of two (registers).
 #include <type_traits>
 
 #include "fi_device.h"
@@ -534,9 +534,9 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
 // ============================================================================
 // cascade prefix tiles: many query rows x one prefix chunk of one kv head.
 // ============================================================================
-// Workgroup = WAVES waves; wave w owns query rows row0 + 32 w + 16 rt + n
-// (rt = 0, 1) as the N columns of its MFMAs, so each K/V element staged in LDS
-// serves 32 WAVES rows.  The tile's slice of the page table is copied to LDS
+// Workgroup = WAVES waves; wave w owns query rows row0 + 16 RT w + 16 rt + n
+// (rt < RT: 2 row tiles, 1 at head_dim 256) as the N columns of its MFMAs,
+// so each K/V element staged in LDS serves 16 RT WAVES rows.  The tile's slice of the page table is copied to LDS
 // once.  Per 32-token step the workgroup loads the step's K and V rows of the
 // tile's kv head (NL 16-byte vectors per thread) two steps ahead into
 // registers, stores them to one of two LDS buffers after computing from the
@@ -580,7 +580,8 @@ __device__ __forceinline__ int xcd_tile(int b, int n) {
 
 template <int KV, bool QBF16, int WAVES, bool PS_POW2, bool APPEND, int D>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(DecodeParams p) {
-  static_assert(D == 64 || D == 128, "two row tiles of 256 dims do not fit the registers");
+  // row tiles (16 query rows each) per wave: two, one at D = 256
+  constexpr int RT = prefix_rows_per_wave(D) / 16;
   using S = PStage<KV, D>;
   // bf16 append tiles: P.V takes p as a bf16 high part plus a bf16
   // residual -- bf16 keeps 8 bits of p, and when a few keys carry
@@ -616,12 +617,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
   }
 
   // query rows of this lane's two column tiles (B operands of the scores)
-  u32x4 qop[2][D / 32];
-  bool rok[2];
-  int rreq[2], rj[2];
+  u32x4 qop[RT][D / 32];
+  bool rok[RT];
+  int rreq[RT], rj[RT];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int row = tile.row0 + kPrefixRowsPerWave * wave + 16 * rt + n;   // < row0 + 32 WAVES
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = tile.row0 + 16 * RT * wave + 16 * rt + n;   // < row0 + 16 RT WAVES
     rok[rt] = row < tile.row1;
     const int rr = rok[rt] ? row : tile.row0;
     rreq[rt] = qo0 + rr / G;
@@ -638,9 +639,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
   // row's causal limit), and over the wave's valid rows the smallest (steps
   // reaching past it mask per row) and the largest (steps from there on
   // have no key for any row: skipped)
-  int lim[2], lo = 0x7fffffff, hi = -0x7fffffff - 1;
+  int lim[RT], lo = 0x7fffffff, hi = -0x7fffffff - 1;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int rt = 0; rt < RT; ++rt) {
     lim[rt] = APPEND ? min(p.req_info[rreq[rt]].kv_len, t1) : t1;
     if (rok[rt]) {
       lo = min(lo, lim[rt]);
@@ -707,10 +708,15 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
     }
   };
 
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-  f32x4 oacc[2][D / 16];
+  float m[RT], l[RT];
+  f32x4 oacc[RT][D / 16];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < RT; ++rt) {
+    m[rt] = -INFINITY;
+    l[rt] = 0.f;
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int b = 0; b < D / 16; ++b) oacc[rt][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -751,21 +757,23 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
     }
     // ---- scores: S[tt][rt] = K(tokens 16 tt ..) . Q^T(rows of tile rt);
     // the four accumulators are independent, so consecutive MFMAs never wait
-    f32x4 sc[2][2];
+    f32x4 sc[2][RT];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) sc[tt][0] = sc[tt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) sc[tt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
           sc[tt][rt] = mma16x16x32<QBF16>(kop[tt][s], qop[rt][s], sc[tt][rt]);
     // ---- softmax per row tile: lane (g, n) holds tokens 4 g + i and
     // 16 + 4 g + i (i < 4) of row n
-    u32x4 pop[2], plo[2];
+    u32x4 pop[RT], plo[RT];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
       float x[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -818,17 +826,19 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
     if constexpr (SPLITP) {
 #pragma unroll
       for (int b = 0; b < D / 16; ++b) {
-        oacc[0][b] = mma16x16x32<QBF16>(vop[b], pop[0], oacc[0][b]);
-        oacc[1][b] = mma16x16x32<QBF16>(vop[b], pop[1], oacc[1][b]);
-        oacc[0][b] = mma16x16x32<QBF16>(vop[b], plo[0], oacc[0][b]);
-        oacc[1][b] = mma16x16x32<QBF16>(vop[b], plo[1], oacc[1][b]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          oacc[rt][b] = mma16x16x32<QBF16>(vop[b], pop[rt], oacc[rt][b]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          oacc[rt][b] = mma16x16x32<QBF16>(vop[b], plo[rt], oacc[rt][b]);
       }
     } else {
 #pragma unroll
-      for (int b = 0; b < D / 16; ++b) {
-        oacc[0][b] = mma16x16x32<QBF16>(vop[b], pop[0], oacc[0][b]);
-        oacc[1][b] = mma16x16x32<QBF16>(vop[b], pop[1], oacc[1][b]);
-      }
+      for (int b = 0; b < D / 16; ++b)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          oacc[rt][b] = mma16x16x32<QBF16>(vop[b], pop[rt], oacc[rt][b]);
     }
   };
 
@@ -854,7 +864,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(
 
   // ---- finalize each row tile
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int rt = 0; rt < RT; ++rt) {
     float lt = l[rt] + __shfl_xor(l[rt], 16);
     lt += __shfl_xor(lt, 32);
     float inv = lt > 0.f ? 1.f / lt : 0.f;
@@ -926,16 +936,17 @@ static hipError_t launch_decode_t(const DecodeParams& p, int num_tiles, int wave
 // The fold instance (cascade suffix tiles, planned as few long 2-head
 // tiles) keeps two steps of loads in flight; the plain instance keeps one,
 // so that two 8-wave workgroups fit on a compute unit (two steps measured
-// no faster for the plain workloads).  head_dim 256 is built for plain
-// decode only (no RoPE table, no cascade level), one step in flight: its
-// K/V registers of one step already take 64 VGPRs.
+// no faster for the plain workloads).  head_dim 256 keeps one step in
+// flight in both instances (its K/V registers of one step already take 64
+// VGPRs) and has no RoPE table.
 template <int KV, bool QBF16, int D>
 static hipError_t launch_decode_f(const DecodeParams& p, int num_tiles, int waves, bool fold,
                                   hipStream_t s) {
   if (num_tiles <= 0) return hipSuccess;
   if constexpr (D == 256) {
-    if (fold || p.rope_table) return hipErrorInvalidValue;
-    return launch_decode_t<KV, QBF16, false, 1, false, D>(p, num_tiles, waves, s);
+    if (p.rope_table) return hipErrorInvalidValue;
+    return fold ? launch_decode_t<KV, QBF16, true, 1, false, D>(p, num_tiles, waves, s)
+                : launch_decode_t<KV, QBF16, false, 1, false, D>(p, num_tiles, waves, s);
   } else {
     if (p.rope_table) {
       if constexpr (D != kRopeHeadDim) return hipErrorInvalidValue;
@@ -1011,13 +1022,16 @@ hipError_t launch_decode(const DecodeParams& p, int num_tiles, int waves, bool q
 }
 
 // append: append tiles (rows limited by ReqInfo.kv_len), else cascade
-// prefix.  head_dim: 64 or 128.
+// prefix.  head_dim: 64, 128 or 256.
 hipError_t launch_prefix(const DecodeParams& p, int num_tiles, int waves, bool append,
                          bool q_bf16, int kv, int head_dim, hipStream_t s) {
   if (waves != 4 && waves != 8) return hipErrorInvalidValue;
-  if (head_dim == 64) return launch_prefix_d<64>(p, num_tiles, waves, append, q_bf16, kv, s);
-  if (head_dim == 128) return launch_prefix_d<128>(p, num_tiles, waves, append, q_bf16, kv, s);
-  return hipErrorInvalidValue;
+  switch (head_dim) {
+    case 64: return launch_prefix_d<64>(p, num_tiles, waves, append, q_bf16, kv, s);
+    case 128: return launch_prefix_d<128>(p, num_tiles, waves, append, q_bf16, kv, s);
+    case 256: return launch_prefix_d<256>(p, num_tiles, waves, append, q_bf16, kv, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace fi

@@ -7,15 +7,17 @@
 
 namespace fi {
 
-// head_dim of the RoPE table (RoPE plans); the decode kernel is built for
-// head_dim 64, 128 and 256, the multi-row kernel for 64 and 128, the merges
-// for all three
+// head_dim of the RoPE table (RoPE plans); the kernels are built for
+// head_dim 64, 128 and 256
 constexpr int kRopeHeadDim = 128;
 constexpr int kMaxGroup = 16;      // q heads per kv head one MFMA column tile holds
 constexpr int kBlockTokens = 32;   // tokens per cascade-prefix step
 constexpr int kChunkAlign = 16;    // decode chunks are whole 16-token steps
 constexpr int kWavesPerTile = 8;   // waves (= kv heads) per decode workgroup
 constexpr int kPrefixRowsPerWave = 32;   // 2 MFMA column tiles per wave
+// query rows per wave of the multi-row kernel at head_dim D: two 16-row
+// column tiles, one at D = 256 (registers)
+constexpr int prefix_rows_per_wave(int D) { return D == 256 ? 16 : kPrefixRowsPerWave; }
 constexpr int kPrefixMaxWaves = 8;       // prefix workgroup: 4 or 8 waves
 constexpr int kPrefixMaxChunk = 4096;    // prefix tokens per tile (page table in LDS)
 constexpr int kMaxMergeStates = 64;

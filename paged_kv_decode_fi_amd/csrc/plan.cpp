@@ -84,9 +84,11 @@ int plan_append(const PlanInput& in, const std::vector<int64_t>& lens, int num_c
   // workgroups fit a CU
   int64_t rows_max = 0;
   for (int r = 0; r < B; ++r) rows_max = std::max<int64_t>(rows_max, (int64_t)(qo[r + 1] - qo[r]) * G);
-  const int waves = env_int("FI_PREFIX_WAVES", rows_max <= 4 * kPrefixRowsPerWave ? 4 : 8) == 4
-                        ? 4 : 8;
-  const int64_t R = (int64_t)kPrefixRowsPerWave * waves;   // rows per tile
+  // (at head_dim 256 the 4-wave instance holds a CU alone: 8 waves)
+  const int rpw = prefix_rows_per_wave(in.D);
+  const int waves =
+      env_int("FI_PREFIX_WAVES", rows_max <= 4 * rpw && in.D != 256 ? 4 : 8) == 4 ? 4 : 8;
+  const int64_t R = (int64_t)rpw * waves;   // rows per tile
   const int64_t slots_per_cu = waves == 4 ? 2 : 1;
   // row tiles: (request, rows [row0, row1), keys needed by the last row)
   struct RowTile {
@@ -348,10 +350,6 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
     return false;
   };
   const int num_cus = in.num_cus > 0 ? in.num_cus : 256;
-  // head_dim 256: the multi-row kernel's two row tiles of 256 dims do not
-  // fit its registers, so neither append nor a cascade level is built
-  if (in.D == 256 && (in.append_qo_indptr || NG > 0))
-    PLAN_FAIL(2, "head_dim 256 is built for decode without a cascade level only");
   if (in.append_qo_indptr) {
     if (NG > 0) PLAN_FAIL(2, "append with a cascade level is not built");
     if (in.pos_encoding != 0) PLAN_FAIL(2, "append with RoPE is not built");
@@ -444,7 +442,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
 
   // ---- cascade prefix chunking
   const int prefix_waves = env_int("FI_PREFIX_WAVES", kPrefixMaxWaves) == 4 ? 4 : 8;
-  const int64_t prefix_rows = (int64_t)kPrefixRowsPerWave * prefix_waves;
+  const int64_t prefix_rows = (int64_t)prefix_rows_per_wave(in.D) * prefix_waves;
   int64_t prefix_chunk = 0;
   std::vector<std::vector<int64_t>> n_pchunks(NL);   // [level][group] chunks
   int64_t prefix_row_tiles = 0;  // sum over levels and groups of row tiles x Hkv

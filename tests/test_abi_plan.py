@@ -68,8 +68,8 @@ def test_host_validation_errors(fi):
 
 
 def test_head_dim_rules(fi):
-    """head_dim 64, 128 and 256 are built for decode; 64 and 128 for a
-    cascade level and append (the multi-row kernel); RoPE for 128 only."""
+    """head_dim 64, 128 and 256 are built for decode, a cascade level and
+    append; RoPE for 128 only."""
     indptr, last = [0, 2, 5], [3, 16]
     prefix = (np.array([0, 2], np.int32), np.array([0, 1], np.int32),
               np.array([16], np.int32))
@@ -78,12 +78,11 @@ def test_head_dim_rules(fi):
     for D in (32, 96, 512):
         assert _status(fi, indptr, last, head_dim=D) == 2
         assert "head_dim" in fi.lib.fi_last_error().decode()
-    assert _status(fi, indptr, last, head_dim=64, prefix=prefix) == 0
-    assert _status(fi, indptr, last, head_dim=256, prefix=prefix) == 2
-    assert "256" in fi.lib.fi_last_error().decode()
+    for D in (64, 256):
+        assert _status(fi, indptr, last, head_dim=D, prefix=prefix) == 0
     assert _status(fi, indptr, last, head_dim=64, pos_encoding="rope_llama") == 2
     assert "RoPE" in fi.lib.fi_last_error().decode()
-    for D, want in ((64, 0), (256, 2)):
+    for D, want in ((64, 0), (256, 0)):
         pr, keep = _problem(fi, indptr, last, head_dim=D)
         qo = np.array([0, 1, 3], np.int32)
         pr.qo_indptr, pr.causal = qo.ctypes.data, 1
@@ -343,7 +342,8 @@ def _append_cover(tiles, lens, nq, G, Hkv, causal):
 
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("chunk", [0, 32, 64])
-def test_append_plan_covers_every_visible_key_once(fi, causal, chunk):
+@pytest.mark.parametrize("head_dim", [128, 256])
+def test_append_plan_covers_every_visible_key_once(fi, causal, chunk, head_dim):
     rng = np.random.default_rng(80 + chunk)
     ps, Hkv, G = 16, 2, 4
     lens = np.array([300, 5, 129, 64, 0, 77])
@@ -353,10 +353,14 @@ def test_append_plan_covers_every_visible_key_once(fi, causal, chunk):
     la = np.where(n > 0, lens - (n - 1) * ps, 0).astype(np.int32)
     qo = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
     t = fi.debug_plan_tiles(ip, la, num_qo_heads=Hkv * G, num_kv_heads=Hkv, page_size=ps,
-                            qo_indptr=qo, causal=causal, chunk_tokens=chunk, num_cus=8)
+                            qo_indptr=qo, causal=causal, chunk_tokens=chunk, num_cus=8,
+                            head_dim=head_dim)
     _append_cover(t, lens, nq, G, Hkv, causal)
     if chunk:
         assert np.all(t[:, 3] - t[:, 2] <= chunk)
+    # rows per tile: 8 waves x 32 rows, 16 at head_dim 256 (4-wave tiles
+    # when every request has few rows, at head_dim <= 128 only)
+    assert np.all(t[:, 7] - t[:, 6] <= (128 if head_dim == 256 else 256))
     del rng
 
 

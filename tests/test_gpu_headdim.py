@@ -2,10 +2,11 @@
 is a parameter of the decode call, 128 in its example; q is [num_qo_heads,
 head_dim], k and v [kv_len, num_kv_heads, head_dim]).
 
-head_dim 64 runs every path the library builds for 128 except RoPE (plain and
-chunked decode, a cascade level with fold and merge, several levels, append);
-head_dim 256 runs plain and chunked decode.  Every case is compared element
-by element with the fp64 oracle, which takes head_dim as a parameter."""
+Both run every path the library builds for 128 except RoPE: plain and
+chunked decode, a cascade level with fold and merge, several levels, append
+(at 256 the multi-row kernel has one 16-row column tile per wave).  Every
+case is compared element by element with the fp64 oracle, which takes
+head_dim as a parameter."""
 import numpy as np
 import pytest
 
@@ -87,30 +88,32 @@ def test_decode_fuzz_parity(fi, D, seed):
                           f"{layout} lens {list(w.kv_lens)} chunk {chunk}")
 
 
+@pytest.mark.parametrize("D", [64, 256])
 @pytest.mark.parametrize("dt", DTYPES, ids=lambda t: f"{t[0]}-{t[1]}")
-def test_cascade_d64_parity(fi, dt):
-    """One shared-prefix level at head_dim 64: the default plan folds the
-    prefix states into the suffix tiles; chunk 32 merges them instead."""
+def test_cascade_parity(fi, D, dt):
+    """One shared-prefix level: the default plan folds the prefix states
+    into the suffix tiles; chunk 32 merges them instead."""
     rng = np.random.default_rng(500 + DTYPES.index(dt))
     lens = list(rng.integers(1, 120, size=8))
-    w = W.build("casc64", lens, Hq=32, Hkv=8, D=64, ps=16, q_dtype=dt[0], kv_dtype=dt[1],
+    w = W.build(f"casc{D}", lens, Hq=32, Hkv=8, D=D, ps=16, q_dtype=dt[0], kv_dtype=dt[1],
                 seed=3, prefix_len=300)
     ro, rl = C.run_oracle(w)
     for chunk in (0, 32):
         o, lse, plan = C.run_gpu(w, chunk_tokens=chunk)
-        C.assert_parity(w, o, lse, ro, rl, label=f"cascade D64 {dt} chunk {chunk} {plan.stats}")
+        C.assert_parity(w, o, lse, ro, rl, label=f"cascade D{D} {dt} chunk {chunk} {plan.stats}")
 
 
+@pytest.mark.parametrize("D", [64, 256])
 @pytest.mark.parametrize("chunk", [0, 32])
-def test_cascade_levels_d64_parity(fi, chunk):
+def test_cascade_levels_parity(fi, D, chunk):
     import oracle
     import torch
-    w = W.build_multilevel("lv64", [9, 0, 130, 1, 64, 300], [[(6, 100)], [(3, 0), (3, 77)]],
-                           Hq=16, Hkv=2, D=64, ps=16, q_dtype="bf16", kv_dtype="bf16", seed=5)
+    w = W.build_multilevel(f"lv{D}", [9, 0, 130, 1, 64, 300], [[(6, 100)], [(3, 0), (3, 77)]],
+                           Hq=16, Hkv=2, D=D, ps=16, q_dtype="bf16", kv_dtype="bf16", seed=5)
     lv = w.meta["levels"]
     d = C.Dev(w)
     plan = fi.Plan(w.kv_indptr, w.last_page_len, num_qo_heads=w.num_qo_heads,
-                   num_kv_heads=w.num_kv_heads, page_size=w.page_size, head_dim=64,
+                   num_kv_heads=w.num_kv_heads, page_size=w.page_size, head_dim=D,
                    q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, chunk_tokens=chunk,
                    levels=[(qo, ip, la) for (qo, ip, ix, la, _) in lv])
     tabs = [(C.to_dev(ip), C.to_dev(ix), C.to_dev(la)) for (qo, ip, ix, la, _) in lv]
@@ -121,38 +124,40 @@ def test_cascade_levels_d64_parity(fi, chunk):
                                    [(qo, ip, ix, la) for (qo, ip, ix, la, _) in lv],
                                    w.kv_indptr, w.kv_indices, w.last_page_len,
                                    num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
-                                   head_dim=64, page_size=w.page_size, q_dtype=w.q_dtype,
+                                   head_dim=D, page_size=w.page_size, q_dtype=w.q_dtype,
                                    kv_dtype=w.kv_dtype, sm_scale=w.sm_scale)
     C.assert_parity(w, o.float().cpu().double().numpy(), lse.cpu().double().numpy(), ro, rl,
-                    label=f"two levels D64 chunk {chunk} {plan.stats}")
+                    label=f"two levels D{D} chunk {chunk} {plan.stats}")
 
 
+@pytest.mark.parametrize("D", [64, 256])
 @pytest.mark.parametrize("dt", DTYPES, ids=lambda t: f"{t[0]}-{t[1]}")
 @pytest.mark.parametrize("causal", [True, False])
-def test_append_d64_parity(fi, dt, causal):
+@pytest.mark.parametrize("chunk", [0, 64])
+def test_append_parity(fi, D, dt, causal, chunk):
     import oracle
     import torch
     rng = np.random.default_rng(900 + DTYPES.index(dt) + 10 * causal)
     lens = rng.integers(1, 400, size=4)
     q_lens = np.minimum(lens, [1, 60, 200, int(lens[3])])
-    w = W.build_append("app64", lens, q_lens, Hq=16, Hkv=4, D=64, ps=16, q_dtype=dt[0],
+    w = W.build_append(f"app{D}", lens, q_lens, Hq=16, Hkv=4, D=D, ps=16, q_dtype=dt[0],
                        kv_dtype=dt[1], seed=9, causal=causal)
     d = C.Dev(w)
     plan = fi.Plan(w.kv_indptr, w.last_page_len, num_qo_heads=w.num_qo_heads,
-                   num_kv_heads=w.num_kv_heads, page_size=w.page_size, head_dim=64,
+                   num_kv_heads=w.num_kv_heads, page_size=w.page_size, head_dim=D,
                    q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, qo_indptr=w.qo_indptr,
-                   causal=w.causal, chunk_tokens=64)
+                   causal=w.causal, chunk_tokens=chunk)
     o, lse = plan.append_run(d.q, d.k, d.v, d.indptr, d.indices, d.last, d.k_scale, d.v_scale,
                              sm_scale=w.sm_scale)
     torch.cuda.synchronize()
     ro, rl = oracle.append(w.q, w.k_pages, w.v_pages, w.qo_indptr, w.kv_indptr, w.kv_indices,
                            w.last_page_len, num_qo_heads=w.num_qo_heads,
-                           num_kv_heads=w.num_kv_heads, head_dim=64, page_size=w.page_size,
+                           num_kv_heads=w.num_kv_heads, head_dim=D, page_size=w.page_size,
                            q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, sm_scale=w.sm_scale,
                            causal=w.causal, k_scale=w.k_scale, v_scale=w.v_scale)
     C.assert_parity(w, o.float().cpu().double().numpy(), lse.cpu().double().numpy(), ro, rl,
                     rows=np.ones((w.num_rows, w.num_qo_heads), bool),
-                    label=f"append D64 {dt} causal {causal} {plan.stats}")
+                    label=f"append D{D} {dt} causal {causal} chunk {chunk} {plan.stats}")
 
 
 @pytest.mark.parametrize("D", [64, 256])
