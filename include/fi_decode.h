@@ -57,7 +57,7 @@
  * (kv_indices, and the device copies of kv_indptr / last_page_len) are
  * trusted: they must describe the same tables that were planned.
  *
- * Supported: head_dim 64, 128 or 256 (RoPE: 128 only); q in fp16 or bf16;
+ * Supported: head_dim 64, 128 or 256; q in fp16 or bf16;
  * KV in the q dtype or OCP E4M3 (e4m3fn); 1 <= num_qo_heads / num_kv_heads
  * <= 16; any page_size >= 1; LLaMA-style RoPE on the fly for plain decode;
  * batch append (causal or not) on the same page tables.

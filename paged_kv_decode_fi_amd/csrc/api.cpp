@@ -30,7 +30,8 @@ hipError_t launch_gather(const int32_t* kv_indptr, const int32_t* kv_indices,
                          int ps_shift, int64_t* out, hipStream_t s);
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int blocks,
                               hipStream_t s);
-hipError_t launch_rope_table(void* table, int rows, float theta, float scale, hipStream_t s);
+hipError_t launch_rope_table(void* table, int rows, int head_dim, float theta, float scale,
+                             hipStream_t s);
 }  // namespace fi
 
 struct fi_plan_s {
@@ -264,7 +265,7 @@ fi_status fi_plan(const fi_problem* problem, int32_t num_cus, void* workspace,
                      reinterpret_cast<hipStream_t>(stream));
   if (e == hipSuccess && hp.rope)   // the (cos, sin) table, built on the device
     e = fi::launch_rope_table(reinterpret_cast<char*>(workspace) + hp.layout.rope_off,
-                              hp.rope_rows, hp.rope_theta, hp.rope_scale,
+                              hp.rope_rows, hp.D, hp.rope_theta, hp.rope_scale,
                               reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     (void)hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
@@ -352,11 +353,12 @@ fi_status check_run_args(const fi::HostPlan& hp, const void* q, const void* k_pa
         hp.level_tile_off[l + 1] > hp.level_tile_off[l])
       return fail(FI_ERR_INVALID_ARG, "the index tables must be non-NULL (level %d)", l);
   }
-  if ((hp.num_tiles > 0 || hp.num_prefix_tiles > 0) && (!k_pages || !v_pages))
+  // (a batch whose every key list is empty reads no K/V and no index)
+  if ((hp.has_keys || (!hp.append && hp.num_prefix_tiles > 0)) && (!k_pages || !v_pages))
     return fail(FI_ERR_INVALID_ARG, "k_pages and v_pages must be non-NULL");
   // append tiles read the per-request table
   const bool own_rows = hp.num_tiles > 0 || (hp.append && hp.num_prefix_tiles > 0);
-  if (!hp.ragged && !kv_indices && own_rows)
+  if (!hp.ragged && !kv_indices && own_rows && hp.has_keys)
     return fail(FI_ERR_INVALID_ARG, "the index tables must be non-NULL");
   if (!(sm_scale == sm_scale) || std::isinf(sm_scale))
     return fail(FI_ERR_INVALID_ARG, "sm_scale must be finite");

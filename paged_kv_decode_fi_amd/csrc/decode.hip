@@ -44,6 +44,7 @@
 //  * head_dim D (64, 128, 256) is a template parameter: D / 32 q operands
 //    and D / 16 output blocks per lane; at 256 prefix_kernel gives each wave
 //    one 16-row column tile instead of two (registers).
+#include <algorithm>
 #include <type_traits>
 
 #include "fi_device.h"
@@ -205,19 +206,21 @@ __device__ __forceinline__ void rope_key8(u32x4 a, u32x4 b, const float4* cs, u3
 
 // (cos, sin) table of the plan: one thread per (distance, frequency), angle
 // in fp64 from the definition, stored as two fp32.
-__global__ void rope_table_kernel(float2* table, int rows, double theta, double scale) {
+__global__ void rope_table_kernel(float2* table, int rows, int D, double theta, double scale) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)rows * (kRopeHeadDim / 2)) return;
-  const int d = (int)(i / (kRopeHeadDim / 2)), f = (int)(i % (kRopeHeadDim / 2));
-  const double ang = (d / scale) * pow(theta, -2.0 * f / kRopeHeadDim);
+  if (i >= (int64_t)rows * (D / 2)) return;
+  const int d = (int)(i / (D / 2)), f = (int)(i % (D / 2));
+  const double ang = (d / scale) * pow(theta, -2.0 * f / D);
   table[i] = float2{(float)cos(ang), (float)sin(ang)};
 }
 
-hipError_t launch_rope_table(void* table, int rows, float theta, float scale, hipStream_t s) {
+hipError_t launch_rope_table(void* table, int rows, int head_dim, float theta, float scale,
+                             hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  const int64_t n = (int64_t)rows * (kRopeHeadDim / 2);
+  const int64_t n = (int64_t)rows * (head_dim / 2);
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     reinterpret_cast<float2*>(table), rows, (double)theta, (double)scale);
+                     reinterpret_cast<float2*>(table), rows, head_dim, (double)theta,
+                     (double)scale);
   return hipGetLastError();
 }
 
@@ -227,13 +230,19 @@ hipError_t launch_rope_table(void* table, int rows, float theta, float scale, hi
 // turned by its distance from the query (LLaMA-style RoPE, relative form)
 // before the score MFMAs; the LDS after K and V holds the step's 16 rows
 // (padded: conflict-free reads of one row per lane) and table rows 0..15.
-constexpr int kRopeLdsStride = kRopeRowBytes + 16;
-constexpr int kRopeLds = kStep * kRopeLdsStride + kStep * kRopeRowBytes;
+template <int D>
+struct RopeLds {
+  static constexpr int FREQ = D / 2;                 // frequencies (table row entries)
+  static constexpr int ROW = rope_row_bytes(D);      // table row bytes
+  static constexpr int STRIDE = ROW + 16;            // the step's rows in LDS (padded)
+  static constexpr int BYTES = kStep * STRIDE + kStep * ROW;
+  static constexpr int FPL = (FREQ + 63) / 64;       // frequencies per lane
+};
 template <int KV, bool QBF16, bool PS_POW2, bool FOLD, int DEPTH, bool ROPE, int D>
 __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams p) {
   static_assert(!ROPE || !FOLD, "RoPE plans have no cascade level to fold");
-  static_assert(!ROPE || D == kRopeHeadDim, "the RoPE table is built for head_dim 128");
   using S = Stage<KV, D>;
+  using RL = RopeLds<D>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int W = blockDim.x >> 6;                  // waves = kv heads of the tile
   const int tid = threadIdx.x;
@@ -253,7 +262,7 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   uint8_t* klds = lds;
   uint8_t* vlds = lds + kStep * KS;
   uint8_t* rlds = lds + kStep * (KS + VS);   // RoPE: the step's rows
-  const float2* r16 = reinterpret_cast<const float2*>(rlds + kStep * kRopeLdsStride);
+  const float2* r16 = reinterpret_cast<const float2*>(rlds + kStep * RL::STRIDE);
 
   // q of this wave's head group as the B operand of the score MFMAs
   u32x4 qop[D / 32];
@@ -293,34 +302,53 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   // DEPTH register sets of step loads (kr/vr[d]); set d holds steps d, d +
   // DEPTH, ...
   u32x4 kr[DEPTH][S::LOADS], vr[DEPTH][S::LOADS];
-  // RoPE: thread (wave w, lane i) builds entries (n, i) of the step's rows
-  // for n = w, w + W, ...: it holds (cos, sin) at distance d0 for frequency
-  // i (2 registers per step in flight) and reads rows n from LDS
-  const float2* rtab = reinterpret_cast<const float2*>(p.rope_table);
-  float2 rr[DEPTH];
-  auto issue_rope = [&](int step, float2& rq) {
-    if constexpr (ROPE) rq = rtab[(int64_t)(qpos - t0 - kStep * step) * 64 + lane];
+  // RoPE: thread (wave w, lane i) builds entries (n, f) of the step's rows
+  // for n = w, w + W, ... and frequencies f = i + 64 k < D / 2: it holds
+  // (cos, sin) at distance d0 for those frequencies (2 registers each per
+  // step in flight) and reads rows n from LDS
+  struct RopeRow {
+    float2 v[RL::FPL];
   };
-  auto stage_rope = [&](const float2& rq) {
+  const float2* rtab = reinterpret_cast<const float2*>(p.rope_table);
+  RopeRow rr[DEPTH];
+  auto issue_rope = [&](int step, RopeRow& rq) {
+    if constexpr (ROPE) {
+#pragma unroll
+      for (int k = 0; k < RL::FPL; ++k) {
+        const int f = lane + 64 * k;
+        if (RL::FREQ % 64 == 0 || f < RL::FREQ)
+          rq.v[k] = rtab[(int64_t)(qpos - t0 - kStep * step) * RL::FREQ + f];
+      }
+    }
+  };
+  auto stage_rope = [&](const RopeRow& rq) {
     if constexpr (ROPE) {
       for (int nn = wave; nn < kStep; nn += W) {
-        const float2 o = r16[nn * 64 + lane];
-        const float c = __builtin_fmaf(rq.x, o.x, rq.y * o.y);    // cos((d0 - n) w)
-        const float sn = __builtin_fmaf(rq.y, o.x, -rq.x * o.y);  // sin((d0 - n) w)
-        *reinterpret_cast<float2*>(rlds + nn * kRopeLdsStride + 8 * lane) = float2{c, sn};
+#pragma unroll
+        for (int k = 0; k < RL::FPL; ++k) {
+          const int f = lane + 64 * k;
+          if (RL::FREQ % 64 == 0 || f < RL::FREQ) {
+            const float2 o = r16[nn * RL::FREQ + f];
+            const float2 q = rq.v[k];
+            const float c = __builtin_fmaf(q.x, o.x, q.y * o.y);    // cos((d0 - n) w)
+            const float sn = __builtin_fmaf(q.y, o.x, -q.x * o.y);  // sin((d0 - n) w)
+            *reinterpret_cast<float2*>(rlds + nn * RL::STRIDE + 8 * f) = float2{c, sn};
+          }
+        }
       }
     }
   };
   if constexpr (ROPE) {
-    constexpr int kVec = kStep * kRopeRowBytes / 16;   // rows 0..15: 512 vectors
+    constexpr int kVec = kStep * RL::ROW / 16;   // rows 0..15 in 16-byte vectors
+    constexpr int kPer = (kVec + 63) / 64;       // per thread at W = 1
     const u32x4* src = reinterpret_cast<const u32x4*>(p.rope_table);
-    u32x4* dst = reinterpret_cast<u32x4*>(rlds + kStep * kRopeLdsStride);
-    u32x4 o16[8];
+    u32x4* dst = reinterpret_cast<u32x4*>(rlds + kStep * RL::STRIDE);
+    u32x4 o16[kPer];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < kPer; ++u)
       if (tid + u * 64 * W < kVec) o16[u] = src[tid + u * 64 * W];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < kPer; ++u)
       if (tid + u * 64 * W < kVec) dst[tid + u * 64 * W] = o16[u];
     __syncthreads();   // rows 0..15 are read across waves by the first stage
   }
@@ -377,17 +405,18 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
       }
     };
     if constexpr (ROPE) {
-      // dims of kop(j) (frequencies 32 j + 8 g ..) pair with kop(j + 2)
+      // dims of kop(j) (frequencies 32 j + 8 g ..) pair with kop(j + D / 64)
+      constexpr int HALF = D / 64;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < HALF; ++j) {
         const float4* cs =
-            reinterpret_cast<const float4*>(rlds + n * kRopeLdsStride + 256 * j + 64 * g);
+            reinterpret_cast<const float4*>(rlds + n * RL::STRIDE + 256 * j + 64 * g);
         u32x4 ahi, alo, bhi, blo;
-        rope_key8<QBF16>(kop_of(j), kop_of(j + 2), cs, ahi, alo, bhi, blo);
+        rope_key8<QBF16>(kop_of(j), kop_of(j + HALF), cs, ahi, alo, bhi, blo);
         sc = mma16x16x32<QBF16>(ahi, qop[j], sc);
         sc = mma16x16x32<QBF16>(alo, qop[j], sc);
-        sc = mma16x16x32<QBF16>(bhi, qop[j + 2], sc);
-        sc = mma16x16x32<QBF16>(blo, qop[j + 2], sc);
+        sc = mma16x16x32<QBF16>(bhi, qop[j + HALF], sc);
+        sc = mma16x16x32<QBF16>(blo, qop[j + HALF], sc);
       }
     } else {
 #pragma unroll
@@ -468,7 +497,7 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
       int pgb = nsteps > 3 ? load_page(3) : 0;   // ... odd step
       // one body per register set: set d stages step s and refills with s + 2
       auto body = [&](int step, int& pgn, u32x4 (&kq)[S::LOADS], u32x4 (&vq)[S::LOADS],
-                      float2& rq) {
+                      RopeRow& rq) {
         stage(kq, vq);
         stage_rope(rq);
         __syncthreads();
@@ -906,14 +935,18 @@ static int getenv_depth() {
   return d;
 }
 
+constexpr int kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
+
 template <int KV, bool QBF16, bool FOLD, int DEPTH, bool ROPE, int D>
 static hipError_t launch_decode_t(const DecodeParams& p, int num_tiles, int waves,
                                   hipStream_t s) {
-  constexpr int rope_lds = ROPE ? kRopeLds : 0;
+  constexpr int rope_lds = ROPE ? RopeLds<D>::BYTES : 0;
   const size_t lds = (size_t)Stage<KV, D>::lds_bytes(waves) + rope_lds;
+  // (head_dim 256 with RoPE: at most 4 kv heads per tile fit)
+  if (lds > (size_t)kMaxLds) return hipErrorInvalidValue;
   // dynamic LDS above 64 KiB must be allowed per kernel (once per process)
   static const hipError_t attr = [] {
-    const int max_lds = Stage<KV, D>::lds_bytes(kWavesPerTile) + rope_lds;
+    const int max_lds = std::min(Stage<KV, D>::lds_bytes(kWavesPerTile) + rope_lds, kMaxLds);
     hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, true, FOLD, DEPTH, ROPE, D>),
         hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
@@ -944,17 +977,14 @@ static hipError_t launch_decode_f(const DecodeParams& p, int num_tiles, int wave
                                   hipStream_t s) {
   if (num_tiles <= 0) return hipSuccess;
   if constexpr (D == 256) {
-    if (p.rope_table) return hipErrorInvalidValue;
+    if (p.rope_table) return launch_decode_t<KV, QBF16, false, 1, true, D>(p, num_tiles, waves, s);
     return fold ? launch_decode_t<KV, QBF16, true, 1, false, D>(p, num_tiles, waves, s)
                 : launch_decode_t<KV, QBF16, false, 1, false, D>(p, num_tiles, waves, s);
   } else {
-    if (p.rope_table) {
-      if constexpr (D != kRopeHeadDim) return hipErrorInvalidValue;
-      else
-        return getenv_depth() == 1
-                   ? launch_decode_t<KV, QBF16, false, 1, true, D>(p, num_tiles, waves, s)
-                   : launch_decode_t<KV, QBF16, false, 2, true, D>(p, num_tiles, waves, s);
-    }
+    if (p.rope_table)
+      return getenv_depth() == 1
+                 ? launch_decode_t<KV, QBF16, false, 1, true, D>(p, num_tiles, waves, s)
+                 : launch_decode_t<KV, QBF16, false, 2, true, D>(p, num_tiles, waves, s);
     const bool deep = fold && waves <= 4 && getenv_depth() != 1;
     if (fold)
       return deep ? launch_decode_t<KV, QBF16, true, 2, false, D>(p, num_tiles, waves, s)

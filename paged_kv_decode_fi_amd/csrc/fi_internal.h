@@ -7,9 +7,7 @@
 
 namespace fi {
 
-// head_dim of the RoPE table (RoPE plans); the kernels are built for
-// head_dim 64, 128 and 256
-constexpr int kRopeHeadDim = 128;
+// the kernels are built for head_dim 64, 128 and 256
 constexpr int kMaxGroup = 16;      // q heads per kv head one MFMA column tile holds
 constexpr int kBlockTokens = 32;   // tokens per cascade-prefix step
 constexpr int kChunkAlign = 16;    // decode chunks are whole 16-token steps
@@ -58,9 +56,9 @@ struct ReqInfo {
 };
 static_assert(sizeof(ReqInfo) == 16, "request info is 16 bytes");
 
-// RoPE table: for distance d < rows and frequency i < kRopeHeadDim / 2, the
-// fp32 pair (cos, sin) of d / scale * theta^(-2 i / kRopeHeadDim).
-constexpr int kRopeRowBytes = kRopeHeadDim / 2 * 8;   // 512
+// RoPE table: for distance d < rows and frequency i < D / 2, the fp32 pair
+// (cos, sin) of d / scale * theta^(-2 i / D); a row is D / 2 pairs.
+constexpr int rope_row_bytes(int D) { return D / 2 * 8; }
 
 // One merge work item: request r's states slot_base + c * Hkv + h,
 // c < n_states (16 bytes, read with one load).
@@ -77,7 +75,7 @@ struct WorkspaceLayout {
   size_t state_off_off;    // int32[num_levels * batch] (levels >= 2)
   size_t partial_o_off;    // float[num_partials][G][D]
   size_t partial_lse_off;  // float[num_partials][G]   (log2 domain)
-  size_t rope_off;         // uint32[rope_rows][kRopeHeadDim / 2] (RoPE plans)
+  size_t rope_off;         // float2[rope_rows][D / 2] (RoPE plans)
   size_t total;
 };
 
@@ -95,6 +93,7 @@ struct HostPlan {
   int32_t ragged;       // ragged KV layout
   int32_t hnd;          // HND pages
   int32_t causal;       // append: causal mask
+  int32_t has_keys;     // some request has kv_len > 0 (its own pages)
   int64_t total_q;      // append: query tokens (rows of o)
   int64_t num_req_info; // ReqInfo entries (batch, or total_q for append)
   int32_t qo_len;       // qo_indptr entries (levels' groups + 1 each, or batch + 1)
@@ -164,7 +163,7 @@ struct DecodeParams {
   int32_t num_tiles;
   // prefix tiles only: first request of each group, device [groups+1]
   const int32_t* qo_indptr;
-  // RoPE plans: the (cos, sin) table, rope_rows x kRopeHeadDim / 2 fp32 pairs
+  // RoPE plans: the (cos, sin) table, rope_rows x D / 2 fp32 pairs
   const void* rope_table;
   int32_t rope_rows;
   // ragged KV: token t of a request is row kv_indptr[r] + t (page size 1,

@@ -229,6 +229,7 @@ int plan_append(const PlanInput& in, const std::vector<int64_t>& lens, int num_c
   std::copy(at.begin(), at.end(), out->tiles);
 
   out->batch = B; out->Hq = in.Hq; out->Hkv = Hkv; out->D = in.D;
+  out->has_keys = std::any_of(lens.begin(), lens.end(), [](int64_t L) { return L > 0; });
   out->page_size = in.page_size; out->G = G; out->q_dtype = in.q_dtype;
   out->kv_dtype = in.kv_dtype; out->num_groups = 0; out->num_cus = num_cus;
   out->chunk_tokens = (int32_t)chunk;
@@ -361,8 +362,6 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   const bool rope = in.pos_encoding == 1;
   if (rope && NG > 0)
     PLAN_FAIL(2, "RoPE with a cascade level is not built (plain decode only)");
-  if (rope && in.D != kRopeHeadDim)
-    PLAN_FAIL(2, "RoPE is built for head_dim %d only (got %d)", kRopeHeadDim, in.D);
   if (rope && (!(in.rope_theta == in.rope_theta) || !(in.rope_scale == in.rope_scale) ||
                in.rope_theta > 1e30f || in.rope_scale > 1e30f))
     PLAN_FAIL(1, "rope_theta and rope_scale must be finite");
@@ -375,6 +374,9 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   const int hpt_default = rope ? kWavesPerTile / 2 : kWavesPerTile;
   int hpt = (int)std::min<int64_t>(kWavesPerTile, std::max<int64_t>(1, env_int("FI_HEADS_PER_TILE",
                                                                               hpt_default)));
+  // (head_dim 256 with RoPE: the step's K/V rows of 8 heads and the
+  // table rows exceed the LDS, so at most 4)
+  if (rope && in.D == 256) hpt = std::min(hpt, kWavesPerTile / 2);
   while (hpt & (hpt - 1)) hpt &= hpt - 1;
   while (Hkv % hpt) hpt >>= 1;
   const int64_t waves_per_cu = env_int("FI_WAVES_PER_CU", 16);
@@ -590,6 +592,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   std::copy(pt.begin(), pt.end(), out->tiles + dt.size());
 
   out->batch = B; out->Hq = in.Hq; out->Hkv = Hkv; out->D = in.D;
+  out->has_keys = std::any_of(lens.begin(), lens.end(), [](int64_t L) { return L > 0; });
   out->page_size = ps; out->G = G; out->q_dtype = in.q_dtype;
   out->kv_dtype = in.kv_dtype; out->num_groups = NG; out->num_cus = num_cus;
   out->chunk_tokens = (int32_t)chunk;
@@ -632,7 +635,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   // distances 0 .. Lmax - 1, and at least the 16 rows every tile stages
   out->rope_rows = rope ? (int32_t)std::max<int64_t>(Lmax, kChunkAlign) : 0;
   L.rope_off = off;
-  off = align256(off + (size_t)kRopeRowBytes * (size_t)out->rope_rows);
+  off = align256(off + (size_t)rope_row_bytes(in.D) * (size_t)out->rope_rows);
   L.total = off;
   return 0;
 }

@@ -68,8 +68,8 @@ def test_host_validation_errors(fi):
 
 
 def test_head_dim_rules(fi):
-    """head_dim 64, 128 and 256 are built for decode, a cascade level and
-    append; RoPE for 128 only."""
+    """head_dim 64, 128 and 256 are built for decode (with or without RoPE),
+    a cascade level and append."""
     indptr, last = [0, 2, 5], [3, 16]
     prefix = (np.array([0, 2], np.int32), np.array([0, 1], np.int32),
               np.array([16], np.int32))
@@ -80,14 +80,25 @@ def test_head_dim_rules(fi):
         assert "head_dim" in fi.lib.fi_last_error().decode()
     for D in (64, 256):
         assert _status(fi, indptr, last, head_dim=D, prefix=prefix) == 0
-    assert _status(fi, indptr, last, head_dim=64, pos_encoding="rope_llama") == 2
-    assert "RoPE" in fi.lib.fi_last_error().decode()
+    for D in (64, 256):
+        assert _status(fi, indptr, last, head_dim=D, pos_encoding="rope_llama") == 0
     for D, want in ((64, 0), (256, 0)):
         pr, keep = _problem(fi, indptr, last, head_dim=D)
         qo = np.array([0, 1, 3], np.int32)
         pr.qo_indptr, pr.causal = qo.ctypes.data, 1
         n = ctypes.c_int64(0)
         assert fi.lib.fi_debug_plan_tiles(ctypes.byref(pr), 256, None, 0, ctypes.byref(n)) == want
+
+
+def test_rope_table_rows_scale_with_head_dim(fi):
+    """The RoPE table holds head_dim / 2 (cos, sin) fp32 pairs per distance:
+    its rows are 4 * head_dim bytes."""
+    indptr, last = [0, 63], [16]                   # one request of 1,008 tokens
+    for D in (64, 128, 256):
+        st0, ws0 = _workspace(fi, indptr, last, head_dim=D)
+        st1, ws1 = _workspace(fi, indptr, last, head_dim=D, pos_encoding="rope_llama")
+        assert st0 == st1 == 0
+        assert ws1 - ws0 >= 1008 * 4 * D and ws1 - ws0 < 1008 * 4 * D + 4096
 
 
 def test_head_dim_workspace_scales(fi):

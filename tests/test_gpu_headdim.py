@@ -2,11 +2,11 @@
 is a parameter of the decode call, 128 in its example; q is [num_qo_heads,
 head_dim], k and v [kv_len, num_kv_heads, head_dim]).
 
-Both run every path the library builds for 128 except RoPE: plain and
-chunked decode, a cascade level with fold and merge, several levels, append
-(at 256 the multi-row kernel has one 16-row column tile per wave).  Every
-case is compared element by element with the fp64 oracle, which takes
-head_dim as a parameter."""
+Both run every path the library builds for 128: plain and chunked decode,
+RoPE decode (a table row of head_dim / 2 frequencies), a cascade level with
+fold and merge, several levels, append (at 256 the multi-row kernel has one
+16-row column tile per wave).  Every case is compared element by element
+with the fp64 oracle, which takes head_dim as a parameter."""
 import numpy as np
 import pytest
 
@@ -41,6 +41,46 @@ def test_decode_parity(fi, D, dt, chunk):
     C.assert_parity(w, o, lse, ro, rl, label=f"D{D} {dt} chunk {chunk} {plan.stats}")
     if chunk:
         assert plan.stats["num_merge_units"] > 0
+
+
+@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("dt", DTYPES, ids=lambda t: f"{t[0]}-{t[1]}")
+@pytest.mark.parametrize("chunk", [0, 32])
+def test_rope_decode_parity(fi, D, dt, chunk):
+    rng = np.random.default_rng(3 * D + DTYPES.index(dt))
+    lens = [900, 1, 33, 0, 250, 16] + list(rng.integers(1, 400, size=3))
+    w = W.build(f"r{D}", lens, Hq=32, Hkv=8, D=D, ps=16, q_dtype=dt[0], kv_dtype=dt[1],
+                seed=7 * D + DTYPES.index(dt))
+    rope = (1e4, 1.0)
+    o, lse, plan = C.run_gpu(w, chunk_tokens=chunk, rope=rope)
+    ro, rl = C.run_oracle(w, rope=rope)
+    C.assert_parity(w, o, lse, ro, rl, label=f"RoPE D{D} {dt} chunk {chunk} {plan.stats}")
+    po, _ = C.run_oracle(w)
+    assert np.abs(po - ro).max() > 10 * (C.TOL_ABS + C.TOL_REL), "RoPE had no effect"
+
+
+@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("seed", range(6))
+def test_rope_fuzz_parity(fi, D, seed):
+    rng = np.random.default_rng(17000 + 5 * D + seed)
+    G = int(rng.choice([1, 4, 8]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    B = int(rng.integers(1, 7))
+    ps = int(rng.choice([1, 3, 16]))
+    q_dtype, kv_dtype = DTYPES[seed % 4]
+    rope = (float(rng.choice([1e4, 5e5])), float(rng.choice([1.0, 8.0, 0.5])))
+    w = W.build(f"rfz{D}_{seed}", _lens(rng, B, 900), Hq=Hkv * G, Hkv=Hkv, D=D, ps=ps,
+                q_dtype=q_dtype, kv_dtype=kv_dtype, seed=seed)
+    if seed % 3 == 1:
+        w = W.to_hnd(w)
+    elif seed % 3 == 2:
+        w = W.to_ragged(w)
+    chunk = [0, 32][seed % 2]
+    o, lse, plan = C.run_gpu(w, chunk_tokens=chunk, rope=rope)
+    ro, rl = C.run_oracle(w, rope=rope)
+    C.assert_parity(w, o, lse, ro, rl,
+                    label=f"RoPE D{D} fuzz{seed} G{G} Hkv{Hkv} ps{ps} {q_dtype}/{kv_dtype} "
+                          f"rope {rope} lens {list(w.kv_lens)} chunk {chunk}")
 
 
 @pytest.mark.parametrize("D", [64, 256])

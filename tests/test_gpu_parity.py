@@ -450,3 +450,22 @@ def test_many_split_requests_take_the_wide_merge(fi, q_dtype):
     assert plan.stats["num_merge_units"] >= 128
     ro, rl = C.run_oracle(w)
     C.assert_parity(w, o, lse, ro, rl, label=f"wide merge {q_dtype} {plan.stats}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("rope", [False, True])
+def test_all_requests_empty(fi, rope):
+    """A batch whose every key list is empty reads no K/V and no page index:
+    the index table and the pools may be empty (NULL); every row is o = 0,
+    lse = -inf."""
+    import torch
+    plan = fi.Plan(np.zeros(4, np.int32), np.zeros(3, np.int32), num_qo_heads=8,
+                   num_kv_heads=2, page_size=16,
+                   pos_encoding="rope_llama" if rope else "none")
+    q = torch.randn(3, 8, 128, device="cuda").half()
+    empty = torch.empty(0, device="cuda", dtype=torch.int32)
+    k = torch.empty(0, 16, 2, 128, device="cuda", dtype=torch.float16)
+    o, lse = plan.run(q, k, k, torch.zeros(4, dtype=torch.int32, device="cuda"), empty,
+                      torch.zeros(3, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))

@@ -4,10 +4,11 @@ with the same rotation: rotate-half pairs (x_i, x_{i+D/2}) turned by
 pos / scale * theta^(-2 i / D), key t of a request at position t, the query
 at kv_len - 1.
 
-The kernel rotates q and each key in fp32 with a (cos, sin) table held as
-f16 pairs and rounds the rotated operands to the q dtype before the score
-MFMAs; the oracle rotates the stored values in fp64.  The same acceptance bar
-as plain decode applies."""
+The kernel turns each key back by its distance from the query (relative
+form: q enters the score MFMAs as stored) in fp32 with an fp32 (cos, sin)
+table, and passes the turned key as a 16-bit high part plus a 16-bit
+residual; the oracle rotates q and every key by their positions in fp64.
+The same acceptance bar as plain decode applies."""
 import numpy as np
 import pytest
 
