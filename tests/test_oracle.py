@@ -410,9 +410,9 @@ def _rope_complex(x, pos, theta=1e4, scale=1.0):
     return np.concatenate([z.real, z.imag])
 
 
-def test_rope_rotation_pins(oracle_lib):
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_rope_rotation_pins(oracle_lib, D):
     rng = np.random.default_rng(31)
-    D = 128
     x = rng.standard_normal(D)
     y = rng.standard_normal(D)
     # position 0 is the identity
@@ -441,13 +441,14 @@ def test_rope_rotation_pins(oracle_lib):
     assert np.abs(wrong - _rope_complex(x, 37)).max() > 1e-3
 
 
-def test_rope_decode_equals_plain_decode_of_prerotated_data(oracle_lib):
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_rope_decode_equals_plain_decode_of_prerotated_data(oracle_lib, D):
     """Decode with RoPE = plain decode (no RoPE) over keys pre-rotated at
     their logical index and queries at kv_len - 1, the rotations done here
     with the complex restatement and stored as fp64 -- pins the position each
     key and query gets and that V is not rotated."""
     rng = np.random.default_rng(32)
-    Hq, Hkv, D, ps = 4, 2, 128, 3
+    Hq, Hkv, ps = 4, 2, 3
     lens = [1, 7, 40]
     kd = [f16_values(rng.standard_normal((L, Hkv, D))) for L in lens]
     vd = [f16_values(rng.standard_normal((L, Hkv, D))) for L in lens]
