@@ -136,9 +136,10 @@ def test_append_planted_key_under_the_mask(fi):
     assert np.abs(o[0] - v_star).max() > 0.1
 
 
+@pytest.mark.parametrize("head_dim", [128, 64, 256])
 @pytest.mark.parametrize("name", W.APPEND_WORKLOADS)
-def test_full_size_append_sampled_parity(fi, name):
-    w = W.make_append(name)
+def test_full_size_append_sampled_parity(fi, name, head_dim):
+    w = W.make_append(name, head_dim=head_dim)
     o, lse, plan = _run(w)
     st = plan.stats
     print(f"{w.name}: tiles {st['num_prefix_tiles']} merge units {st['num_merge_units']} "

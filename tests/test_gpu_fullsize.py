@@ -154,3 +154,20 @@ def fi_lib():
     import paged_kv_decode_fi_amd as m
     yield m
     _CACHE.clear()
+
+
+@pytest.mark.parametrize("head_dim", [64, 256])
+@pytest.mark.parametrize("name", ["batch64_gqa4", "cascade256"])
+def test_full_size_head_dim_sampled_parity(fi_lib, name, head_dim):
+    """The same workloads (seed, lengths, heads, dtypes) at head_dim 64 and
+    256, in the benchmark's launch configuration."""
+    _CACHE.clear()
+    w = W.make(name, head_dim=head_dim)
+    _check(w, f"{name}_d{head_dim}", n_random=12)
+
+
+@pytest.mark.parametrize("head_dim", [64, 256])
+def test_full_size_rope_head_dim_sampled_parity(fi_lib, head_dim):
+    _CACHE.clear()
+    w = W.make("batch64_gqa4", head_dim=head_dim)
+    _check(w, f"rope_batch64_gqa4_d{head_dim}", n_random=12, rope=(1e4, 1.0))
