@@ -981,10 +981,15 @@ static hipError_t launch_decode_f(const DecodeParams& p, int num_tiles, int wave
     return fold ? launch_decode_t<KV, QBF16, true, 1, false, D>(p, num_tiles, waves, s)
                 : launch_decode_t<KV, QBF16, false, 1, false, D>(p, num_tiles, waves, s);
   } else {
-    if (p.rope_table)
-      return getenv_depth() == 1
-                 ? launch_decode_t<KV, QBF16, false, 1, true, D>(p, num_tiles, waves, s)
-                 : launch_decode_t<KV, QBF16, false, 2, true, D>(p, num_tiles, waves, s);
+    if (p.rope_table) {
+      // (RoPE at head_dim 64: one step in flight measured 8 % faster)
+      if constexpr (D == 64)
+        return launch_decode_t<KV, QBF16, false, 1, true, D>(p, num_tiles, waves, s);
+      else
+        return getenv_depth() == 1
+                   ? launch_decode_t<KV, QBF16, false, 1, true, D>(p, num_tiles, waves, s)
+                   : launch_decode_t<KV, QBF16, false, 2, true, D>(p, num_tiles, waves, s);
+    }
     const bool deep = fold && waves <= 4 && getenv_depth() != 1;
     if (fold)
       return deep ? launch_decode_t<KV, QBF16, true, 2, false, D>(p, num_tiles, waves, s)
