@@ -212,7 +212,9 @@ fi_status fi_plan_get_stats(fi_plan_t plan, fi_plan_stats* stats);
  * and 3: paged / vector-sparse attention, head-query fusion for GQA,
  * low-precision KV).  The plan must have been made without a cascade level.
  * kv_indptr, kv_indices, last_page_len are DEVICE copies of the planned
- * table.  sm_scale <= 0 selects 1/sqrt(head_dim).  lse may be NULL.
+ * table.  sm_scale <= 0 selects 1/sqrt(head_dim).  lse may be NULL; when
+ * every planned kv_len is 0, kv_indices, k_pages and v_pages may be NULL
+ * (nothing is read; every row gets o = 0, lse = -inf).
  * Enqueues 1-2 kernels on stream. */
 fi_status fi_decode_run(fi_plan_t plan, const void* q, const void* k_pages,
                         const void* v_pages, const int32_t* kv_indptr,
