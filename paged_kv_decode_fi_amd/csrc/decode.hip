@@ -608,7 +608,8 @@ __device__ __forceinline__ int xcd_tile(int b, int n) {
 }
 
 template <int KV, bool QBF16, int WAVES, bool PS_POW2, bool APPEND, int D>
-__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void prefix_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64 * WAVES, WAVES == 4 && D != 256 ? 2 : 1) void prefix_kernel(
+    DecodeParams p) {
   // row tiles (16 query rows each) per wave: two, one at D = 256
   constexpr int RT = prefix_rows_per_wave(D) / 16;
   using S = PStage<KV, D>;
