@@ -206,8 +206,9 @@ def _check_cover(tiles, lens, Hkv, hpt, has_other_states=None):
             assert r in empty      # empty requests still get their (0, -inf) written
 
 
+@pytest.mark.parametrize("head_dim", [128, 64, 256])
 @pytest.mark.parametrize("seed", range(6))
-def test_plan_covers_every_token_once(fi, seed):
+def test_plan_covers_every_token_once(fi, seed, head_dim):
     rng = np.random.default_rng(seed)
     ps = [1, 16, 7, 16, 32, 2][seed]
     Hkv = [8, 8, 4, 32, 2, 1][seed]
@@ -219,7 +220,8 @@ def test_plan_covers_every_token_once(fi, seed):
     indptr = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
     last = np.where(n > 0, lens - (n - 1) * ps, 0).astype(np.int32)
     tiles = fi.debug_plan_tiles(indptr, last, num_qo_heads=Hkv * G, num_kv_heads=Hkv,
-                                page_size=ps, num_cus=[256, 32, 8, 256, 4, 1][seed])
+                                page_size=ps, num_cus=[256, 32, 8, 256, 4, 1][seed],
+                                head_dim=head_dim)
     _check_cover(tiles, _lens(indptr, last, ps), Hkv, _heads_per_tile(tiles, Hkv))
     # longest tiles first
     d = [t[3] - t[2] for t in tiles if t[5] == 0]
@@ -255,7 +257,8 @@ def test_plan_splits_long_requests(fi):
     assert max(x[3] - x[2] for x in t) <= 2048
 
 
-def test_cascade_plan_covers_prefix_rows_once(fi):
+@pytest.mark.parametrize("head_dim", [128, 256])
+def test_cascade_plan_covers_prefix_rows_once(fi, head_dim):
     G, Hkv, ps = 8, 8, 16
     groups = [(5, 300), (3, 0), (2, 1000)]
     B = sum(g[0] for g in groups)
@@ -269,7 +272,8 @@ def test_cascade_plan_covers_prefix_rows_once(fi):
     pip = np.concatenate([[0], np.cumsum(pn)]).astype(np.int32)
     plast = np.where(pn > 0, plens - (pn - 1) * ps, 0).astype(np.int32)
     tiles = fi.debug_plan_tiles(indptr, last, num_qo_heads=G * Hkv, num_kv_heads=Hkv,
-                                page_size=ps, prefix=(qo, pip, plast), num_cus=16)
+                                page_size=ps, prefix=(qo, pip, plast), num_cus=16,
+                                head_dim=head_dim)
     req_prefix = np.repeat(plens, [g[0] for g in groups]) > 0
     _check_cover(tiles, lens, Hkv, _heads_per_tile(tiles, Hkv), has_other_states=req_prefix)
     seen = set()
@@ -285,6 +289,9 @@ def test_cascade_plan_covers_prefix_rows_once(fi):
                 seen.add(key)
     want = sum(g[0] * G * Hkv * g[1] for g in groups)
     assert len(seen) == want
+    # row tiles: 8 waves x 32 rows, 16 rows per wave at head_dim 256
+    assert max(r1 - r0 for *_, kind, r0, r1 in tiles if kind == 1) <= (
+        128 if head_dim == 256 else 256)
 
 
 def test_cascade_single_chunk_suffix_folds_prefix_states(fi):
