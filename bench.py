@@ -104,7 +104,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1 "
                                    f"(got {args.gpus})"}))
         sys.exit(2)
     import torch
