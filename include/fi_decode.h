@@ -46,9 +46,11 @@
  * kv_indices contents and K/V data may change freely between runs.
  *
  * Ownership: the caller owns every device buffer and the stream.  The
- * library owns only the plan object (host memory plus a pinned staging
- * buffer), released by fi_plan_destroy() once the stream that fi_plan()
- * used has been synchronised.
+ * library owns the plan object (host memory), released by fi_plan_destroy(),
+ * and a small process-wide pool of pinned host buffers through which
+ * fi_plan() uploads work lists: a buffer is reused by a later fi_plan() once
+ * the upload that last used it has completed (checked with an event), so a
+ * re-planning loop allocates no pinned memory after its first plans.
  *
  * Errors: every call returns an fi_status; nothing aborts, throws or prints
  * across the ABI.  Arguments are validated on the host before anything is
@@ -97,6 +99,30 @@ typedef struct {
   const int32_t* kv_indptr;       /* host [num_groups+1] */
   const int32_t* last_page_len;   /* host [num_groups] (NULL when ragged) */
 } fi_cascade_level;
+
+/* Plan tuning, for measurement: how the work is cut, never what is
+ * computed.  A field left 0 takes the built-in default (the measured best);
+ * fi_problem.tuning == NULL leaves every field at its default.  The library
+ * reads no environment variable. */
+typedef struct {
+  int32_t heads_per_tile;       /* kv heads per decode workgroup: 1, 2, 4 or 8 */
+  int32_t waves_per_cu;         /* decode waves the chunk search targets per CU (16) */
+  int32_t chunk_min;            /* smallest decode chunk, tokens (32) */
+  int32_t prefix_waves;         /* waves per multi-row tile: 4 or 8 */
+  int32_t prefix_tiles_per_cu;  /* cascade prefix tiles per CU (1) */
+  int32_t prefix_chunk_min;     /* smallest cascade prefix chunk, tokens (256) */
+  int32_t cascade_fold;         /* 0/1: a one-chunk suffix tile folds its prefix
+                                   states in; -1: every cascade request goes
+                                   through the merge kernel */
+  int32_t fold_max_suffix;      /* longest suffix one fold chunk covers (1024) */
+  int32_t append_tiles_pct;     /* append tiles per resident workgroup x 100 (125) */
+  int32_t append_chunk_min;     /* smallest append key chunk, tokens (128) */
+  int32_t decode_depth;         /* steps of K/V loads in flight: 0 = per kernel
+                                   instance, 1, or 2 where built */
+  int32_t prefix_split_p;       /* bf16 cascade prefix launches pass p to P.V
+                                   with a bf16 residual: 0 = when a level has a
+                                   prefix under 256 keys, 1 = always, -1 = never */
+} fi_tuning;
 
 /* Problem description; every pointer here is HOST memory, read during the
  * fi_plan() call only. */
@@ -163,6 +189,8 @@ typedef struct {
    * fields above; run with fi_cascade_decode_levels.  At most 8 levels. */
   int32_t num_cascade_levels;
   const fi_cascade_level* cascade_levels;   /* host [num_cascade_levels] */
+  /* Optional plan tuning (NULL: defaults). */
+  const fi_tuning* tuning;
 } fi_problem;
 
 enum { FI_POS_NONE = 0, FI_POS_ROPE_LLAMA = 1 };
@@ -184,6 +212,10 @@ typedef struct {
   size_t workspace_bytes;
   int64_t num_folded;        /* cascade requests whose one suffix tile folds in
                                 their prefix states (no merge unit) */
+  uint32_t prefix_split_p;   /* bit l: level l's prefix launch passes p with a
+                                bf16 residual */
+  int32_t staging_buffers;   /* pinned upload buffers the library holds for
+                                all plans of the process (reused, not per plan) */
 } fi_plan_stats;
 
 /* Plan stage (FlashInfer README "core features" item 2).
@@ -202,7 +234,7 @@ fi_status fi_plan(const fi_problem* problem, int32_t num_cus, void* workspace,
                   size_t workspace_bytes, size_t* workspace_needed,
                   void* stream, fi_plan_t* plan_out);
 
-/* Releases a plan (host memory only).  Synchronise the stream first. */
+/* Releases a plan (host memory only; the workspace stays the caller's). */
 fi_status fi_plan_destroy(fi_plan_t plan);
 
 /* Fills *stats (host) for a plan. */
@@ -315,8 +347,11 @@ fi_status fi_debug_plan_tiles(const fi_problem* problem, int32_t num_cus,
 
 /* fi_debug_gather: for every logical token of every request (request-major)
  * writes its physical token slot page * page_size + slot to out_slots
- * (device int64 [total tokens]) using the same device page walk the decode
- * kernel uses.  token_indptr: device [batch+1] exclusive scan of kv_len. */
+ * (device int64 [total tokens]): a plain per-token page-table lookup, the
+ * reference point of the page-table reading (registry quickstart's
+ * kv_indptr / kv_indices / last_page_len).  The kernels' own page walks are
+ * checked by fi_debug_record_walk.  token_indptr: device [batch+1]
+ * exclusive scan of kv_len. */
 fi_status fi_debug_gather(int32_t batch, int32_t page_size,
                           const int32_t* kv_indptr, const int32_t* kv_indices,
                           const int32_t* last_page_len,
@@ -344,6 +379,35 @@ fi_status fi_debug_run_stage(fi_plan_t plan, int32_t stage, const void* q,
                              const int32_t* last_page_len, const float* k_scale,
                              const float* v_scale, float sm_scale, void* o,
                              float* lse, void* stream);
+
+/* fi_debug_record_walk: runs ONE kernel of a planned run (stage 0 = the
+ * decode kernel, 1 = the cascade prefix / append kernel) exactly as the run
+ * launches it -- same work list, workgroup shape and loop -- in an instance
+ * whose loader additionally stores, for every K vector it loads, the byte
+ * offset of that 16-byte vector within the K pool:
+ *   rec[((rec_base[i] + t) * num_kv_heads + h) * (row_bytes / 16) + c]
+ *     = offset of bytes 16c .. 16c+15 of the K row of logical token t,
+ *       kv head h,
+ * with i the tile's request (decode, append) or prefix group (cascade
+ * prefix) and row_bytes = head_dim * element size.  rec (device int64) and
+ * rec_base (device int64 [batch+1] or [groups+1], the token start of each
+ * key list in rec) are the caller's; entries no load reaches are left as
+ * they were.  Outputs are written as by fi_debug_run_stage.  So the page
+ * walk (page index, slot, layout strides, chunk boundaries, tail clamp) can
+ * be compared bit for bit with a plain reading of the page table (registry
+ * quickstart: kv_indptr / kv_indices / last_page_len, kv_layout).
+ * Built for head_dim 128 with fp16 q + fp16 K/V or bf16 q + e4m3 K/V,
+ * 8-wave multi-row tiles, no RoPE; otherwise FI_ERR_UNSUPPORTED.  Plans
+ * with one cascade level at most. */
+fi_status fi_debug_record_walk(fi_plan_t plan, int32_t stage, const void* q,
+                               const void* k_pages, const void* v_pages,
+                               const int32_t* prefix_kv_indptr,
+                               const int32_t* prefix_kv_indices,
+                               const int32_t* prefix_last_page_len,
+                               const int32_t* kv_indptr, const int32_t* kv_indices,
+                               const int32_t* last_page_len, const float* k_scale,
+                               const float* v_scale, float sm_scale, void* o, float* lse,
+                               int64_t* rec, const int64_t* rec_base, void* stream);
 
 /* fi_debug_stream_read: reads `bytes` (multiple of 16) of device memory at
  * src with 16-byte loads from num_blocks workgroups of 256 threads and

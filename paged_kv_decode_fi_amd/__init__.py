@@ -12,7 +12,6 @@ importing this package raises.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from typing import Optional, Sequence
 
@@ -28,7 +27,7 @@ EXPORTS = ("fi_plan", "fi_plan_destroy", "fi_plan_get_stats", "fi_decode_run",
            "fi_cascade_decode", "fi_merge_states", "fi_status_string",
            "fi_last_error", "fi_debug_plan_tiles", "fi_debug_gather",
            "fi_debug_stream_read", "fi_debug_run_stage", "fi_append_run",
-           "fi_cascade_decode_levels")
+           "fi_cascade_decode_levels", "fi_debug_record_walk")
 
 
 class FiError(RuntimeError):
@@ -40,6 +39,15 @@ class FiError(RuntimeError):
 class CascadeLevel(ctypes.Structure):
     _fields_ = [("num_groups", ctypes.c_int32), ("qo_indptr", ctypes.c_void_p),
                 ("kv_indptr", ctypes.c_void_p), ("last_page_len", ctypes.c_void_p)]
+
+
+TUNING_FIELDS = ("heads_per_tile", "waves_per_cu", "chunk_min", "prefix_waves",
+                 "prefix_tiles_per_cu", "prefix_chunk_min", "cascade_fold", "fold_max_suffix",
+                 "append_tiles_pct", "append_chunk_min", "decode_depth", "prefix_split_p")
+
+
+class Tuning(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int32) for f in TUNING_FIELDS]
 
 
 class Problem(ctypes.Structure):
@@ -56,7 +64,7 @@ class Problem(ctypes.Structure):
                 ("rope_theta", ctypes.c_float), ("rope_scale", ctypes.c_float),
                 ("qo_indptr", ctypes.c_void_p), ("causal", ctypes.c_int32),
                 ("kv_layout", ctypes.c_int32), ("num_cascade_levels", ctypes.c_int32),
-                ("cascade_levels", ctypes.c_void_p)]
+                ("cascade_levels", ctypes.c_void_p), ("tuning", ctypes.c_void_p)]
 
 
 class PlanStats(ctypes.Structure):
@@ -64,7 +72,8 @@ class PlanStats(ctypes.Structure):
                 ("num_partials", ctypes.c_int64), ("num_merge_units", ctypes.c_int64),
                 ("chunk_tokens", ctypes.c_int32), ("prefix_chunk_tokens", ctypes.c_int32),
                 ("heads_per_tile", ctypes.c_int32), ("num_cus", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_size_t), ("num_folded", ctypes.c_int64)]
+                ("workspace_bytes", ctypes.c_size_t), ("num_folded", ctypes.c_int64),
+                ("prefix_split_p", ctypes.c_uint32), ("staging_buffers", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -99,6 +108,9 @@ def _load() -> ctypes.CDLL:
     L.fi_cascade_decode.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, F, P, P, P]
     L.fi_debug_run_stage.restype = ctypes.c_int
     L.fi_debug_run_stage.argtypes = [P, I32, P, P, P, P, P, P, P, P, P, P, P, F, P, P, P]
+    L.fi_debug_record_walk.restype = ctypes.c_int
+    L.fi_debug_record_walk.argtypes = [P, I32, P, P, P, P, P, P, P, P, P, P, P, F, P, P, P, P,
+                                       P]
     L.fi_merge_states.restype = ctypes.c_int
     L.fi_merge_states.argtypes = [I32, ctypes.POINTER(P), ctypes.POINTER(P), I64, I32,
                                   ctypes.c_int, P, P, ctypes.c_int, P]
@@ -193,9 +205,16 @@ KV_LAYOUTS = {"paged": 0, "ragged": 1, "paged_hnd": 2}
 
 def _problem(batch, Hq, Hkv, D, ps, q_dtype, kv_dtype, indptr, last, prefix, chunk,
              pos_encoding="none", rope_theta=0.0, rope_scale=0.0, qo_indptr=None, causal=True,
-             kv_layout="paged", levels=None):
+             kv_layout="paged", levels=None, tuning=None):
     pr = Problem()
     lv_keep = []
+    if tuning:
+        bad = set(tuning) - set(TUNING_FIELDS)
+        if bad:
+            raise ValueError(f"unknown tuning fields {sorted(bad)}")
+        tu = Tuning(**{k: int(v) for k, v in tuning.items()})
+        pr.tuning = ctypes.cast(ctypes.pointer(tu), ctypes.c_void_p)
+        lv_keep.append(tu)
     if levels:
         arr = (CascadeLevel * len(levels))()
         for i, (qo, ip, la) in enumerate(levels):
@@ -233,14 +252,14 @@ def debug_plan_tiles(kv_indptr, last_page_len, *, num_qo_heads, num_kv_heads,
                      page_size, head_dim=128, q_dtype="f16", kv_dtype="f16",
                      prefix=None, num_cus=256, chunk_tokens=0,
                      pos_encoding="none", qo_indptr=None, causal=True,
-                     kv_layout="paged", levels=None) -> np.ndarray:
+                     kv_layout="paged", levels=None, tuning=None) -> np.ndarray:
     """Host-only: the plan's work list as an int32 [n, 8] array (request,
     kv_head0, t0, t1, slot, kind, row0, row1)."""
     indptr, last = _host_i32(kv_indptr), _host_i32(last_page_len)
     pr, keep = _problem(len(indptr) - 1, num_qo_heads, num_kv_heads, head_dim,
                         page_size, q_dtype, kv_dtype, indptr, last, prefix, chunk_tokens,
                         pos_encoding, qo_indptr=qo_indptr, causal=causal,
-                        kv_layout=kv_layout, levels=levels)
+                        kv_layout=kv_layout, levels=levels, tuning=tuning)
     n = ctypes.c_int64(0)
     _check(_get_lib().fi_debug_plan_tiles(ctypes.byref(pr), num_cus, None, 0, ctypes.byref(n)))
     out = np.zeros((max(n.value, 1), 8), np.int32)
@@ -266,13 +285,15 @@ class Plan:
     last_page_len and kv_indices may be None); "paged_hnd": head-major pages
     [num_pages][Hkv][page_size][D].  levels = [(qo_indptr, kv_indptr,
     last_page_len), ...] host tables of several shared cascade levels,
-    outermost first (in place of prefix); run with Plan.cascade_run_levels."""
+    outermost first (in place of prefix); run with Plan.cascade_run_levels.
+    tuning: optional dict of fi_tuning fields (how the work is cut, for
+    measurement; never what is computed)."""
 
     def __init__(self, kv_indptr, last_page_len, *, num_qo_heads, num_kv_heads,
                  page_size, head_dim=128, q_dtype="f16", kv_dtype="f16",
                  prefix=None, num_cus=0, chunk_tokens=0, device=None, stream=None,
                  pos_encoding="none", rope_theta=0.0, rope_scale=0.0, qo_indptr=None,
-                 causal=True, kv_layout="paged", levels=None):
+                 causal=True, kv_layout="paged", levels=None, tuning=None):
         import torch
         self.indptr = _host_i32(kv_indptr)
         self.last = _host_i32(last_page_len)
@@ -290,7 +311,7 @@ class Plan:
         pr, keep = _problem(self.batch, num_qo_heads, num_kv_heads, head_dim,
                             page_size, q_dtype, kv_dtype, self.indptr, self.last,
                             prefix, chunk_tokens, pos_encoding, rope_theta, rope_scale,
-                            self.qo_indptr, causal, kv_layout, levels)
+                            self.qo_indptr, causal, kv_layout, levels, tuning)
         need = ctypes.c_size_t(0)
         _check(_get_lib().fi_plan(ctypes.byref(pr), num_cus, None, 0, ctypes.byref(need), None,
                            None))
@@ -432,6 +453,28 @@ class Plan:
             _stream(stream)))
         return o, lse
 
+    def record_walk(self, stage, rec, rec_base, q, k_pages, v_pages, kv_indptr, kv_indices,
+                    last_page_len, prefix_kv_indptr=None, prefix_kv_indices=None,
+                    prefix_last_page_len=None, k_scale=None, v_scale=None,
+                    sm_scale: float = 0.0, o=None, lse=None, stream=None):
+        """Test hook: ONE kernel of the planned run (stage 0 = decode, 1 =
+        multi-row) in its record instance, which also writes the K-pool byte
+        offset of every K vector it loads into rec (device int64) at
+        ((rec_base[list] + token) * Hkv + kv head) * (row bytes / 16) + chunk."""
+        import torch
+        self._check_q(q)
+        self._check_pool(k_pages, v_pages)
+        o, lse = self._outputs(q, o, lse)
+        _check(_get_lib().fi_debug_record_walk(
+            self.handle, int(stage), _ptr(q, "q"), _ptr(k_pages, "k_pages"),
+            _ptr(v_pages, "v_pages"),
+            *_tables(kv_indptr, kv_indices, last_page_len,
+                     (prefix_kv_indptr, prefix_kv_indices, prefix_last_page_len)),
+            *_scales(k_scale, v_scale), float(sm_scale), _ptr(o, "o"), _ptr(lse, "lse"),
+            _ptr(rec, "rec", torch.int64), _ptr(rec_base, "rec_base", torch.int64),
+            _stream(stream)))
+        return o, lse
+
     def destroy(self):
         if getattr(self, "handle", None):
             import torch
@@ -491,6 +534,3 @@ def debug_stream_read(src, sink, num_blocks, stream=None):
     _check(_get_lib().fi_debug_stream_read(_ptr(src), nbytes - nbytes % 16, _ptr(sink),
                                     num_blocks, _stream(stream)))
 
-
-def default_sm_scale(head_dim: int = 128) -> float:
-    return 1.0 / math.sqrt(head_dim)

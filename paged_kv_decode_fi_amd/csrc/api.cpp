@@ -6,22 +6,25 @@
 // into a hipGraph (FlashInfer README, "core features" item 5).
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "fi_decode.h"
 #include "fi_internal.h"
 
 namespace fi {
 hipError_t launch_decode(const DecodeParams& p, int num_tiles, int waves, bool q_bf16,
-                         int kv, bool fold, int head_dim, hipStream_t s);
+                         int kv, bool fold, int depth, int head_dim, hipStream_t s);
 hipError_t launch_prefix(const DecodeParams& p, int num_tiles, int waves, bool append,
-                         bool q_bf16, int kv, int head_dim, hipStream_t s);
+                         bool split, bool q_bf16, int kv, int head_dim, hipStream_t s);
 hipError_t launch_merge_partials(const MergeParams& p, int num_units, bool o_bf16, bool wide,
                                  int head_dim, hipStream_t s);
 hipError_t launch_merge_states(const MergeStatesParams& p, hipStream_t s);
@@ -38,10 +41,102 @@ struct fi_plan_s {
   fi::HostPlan hp;
   char* workspace;
   size_t workspace_bytes;
-  void* staging;  // pinned copy of the work list, merge map and request info
 };
 
 namespace {
+
+// ---- pinned upload buffers, shared by every plan of the process ------------
+// fi_plan() writes the work list, request info and merge map into a pinned
+// host buffer and copies it to the workspace asynchronously.  A buffer is
+// taken again once the event recorded after its last copy has completed, so
+// re-planning does not allocate pinned memory each time; at most kMaxStaging
+// buffers per device are kept (beyond that fi_plan waits for the oldest copy).
+struct Staging {
+  void* ptr;
+  size_t bytes;
+  hipEvent_t done;   // recorded after the copy that last read the buffer
+  int device;
+  bool in_use;       // between acquire and the event record
+  uint64_t last_use;
+};
+constexpr int kMaxStaging = 4;
+std::mutex g_staging_mu;
+std::vector<Staging> g_staging;
+uint64_t g_staging_clock = 0;
+
+// Returns a buffer of >= bytes on `device` whose previous copy is complete,
+// or -1 with *err set.
+int staging_acquire(size_t bytes, int device, hipError_t* err) {
+  std::lock_guard<std::mutex> lk(g_staging_mu);
+  int n_dev = 0, oldest = -1;
+  for (size_t i = 0; i < g_staging.size(); ++i) {
+    Staging& b = g_staging[i];
+    if (b.device != device) continue;
+    ++n_dev;
+    if (b.in_use) continue;
+    if (b.bytes >= bytes && hipEventQuery(b.done) == hipSuccess) {
+      b.in_use = true;
+      return (int)i;
+    }
+    if (oldest < 0 || b.last_use < g_staging[oldest].last_use) oldest = (int)i;
+  }
+  if (n_dev >= kMaxStaging && oldest >= 0) {
+    // reuse the least recently used buffer once its copy is done, growing it
+    Staging& b = g_staging[oldest];
+    hipError_t e = hipEventSynchronize(b.done);
+    if (e == hipSuccess && b.bytes < bytes) {
+      e = hipHostFree(b.ptr);
+      b.ptr = nullptr;
+      b.bytes = 0;
+      if (e == hipSuccess) e = hipHostMalloc(&b.ptr, bytes, hipHostMallocDefault);
+      if (e == hipSuccess) b.bytes = bytes;
+    }
+    if (e != hipSuccess) {
+      *err = e;
+      return -1;
+    }
+    b.in_use = true;
+    return oldest;
+  }
+  Staging b{};
+  b.device = device;
+  hipError_t e = hipHostMalloc(&b.ptr, bytes, hipHostMallocDefault);
+  if (e == hipSuccess) {
+    e = hipEventCreateWithFlags(&b.done, hipEventDisableTiming);
+    if (e != hipSuccess) (void)hipHostFree(b.ptr);
+  }
+  if (e != hipSuccess) {
+    *err = e;
+    return -1;
+  }
+  b.bytes = bytes;
+  b.in_use = true;
+  g_staging.push_back(b);
+  return (int)g_staging.size() - 1;
+}
+
+void* staging_ptr(int i) {
+  std::lock_guard<std::mutex> lk(g_staging_mu);
+  return g_staging[i].ptr;
+}
+
+// Records the buffer's copy on `stream` and hands the buffer back; when
+// `record` is false (the copy was never enqueued) it is free at once.
+hipError_t staging_release(int i, hipStream_t stream, bool record) {
+  std::lock_guard<std::mutex> lk(g_staging_mu);
+  Staging& b = g_staging[i];
+  hipError_t e = record ? hipEventRecord(b.done, stream) : hipSuccess;
+  if (e != hipSuccess) (void)hipStreamSynchronize(stream);   // copy done: free to reuse
+  if (e != hipSuccess) (void)hipEventSynchronize(b.done);
+  b.in_use = false;
+  b.last_use = ++g_staging_clock;
+  return e;
+}
+
+int staging_count() {
+  std::lock_guard<std::mutex> lk(g_staging_mu);
+  return (int)g_staging.size();
+}
 
 thread_local std::string g_last_error;
 
@@ -111,6 +206,14 @@ fi::PlanInput to_input(const fi_problem* p, int num_cus) {
   if (p->kv_layout < 0 || p->kv_layout > FI_KV_PAGED_HND) in.ragged = in.hnd = -1;
   in.rope_theta = p->rope_theta;
   in.rope_scale = p->rope_scale;
+  memset(&in.tune, 0, sizeof(in.tune));
+  if (p->tuning) {
+    const fi_tuning& t = *p->tuning;
+    in.tune = fi::Tuning{t.heads_per_tile,   t.waves_per_cu,     t.chunk_min,
+                         t.prefix_waves,     t.prefix_tiles_per_cu, t.prefix_chunk_min,
+                         t.cascade_fold,     t.fold_max_suffix,  t.append_tiles_pct,
+                         t.append_chunk_min, t.decode_depth,     t.prefix_split_p};
+  }
   return in;
 }
 
@@ -244,12 +347,16 @@ fi_status fi_plan(const fi_problem* problem, int32_t num_cus, void* workspace,
                 workspace_bytes, need);
   }
   const size_t meta_bytes = hp.layout.partial_o_off;
-  void* staging = nullptr;
-  hipError_t e = hipHostMalloc(&staging, meta_bytes, hipHostMallocDefault);
-  if (e != hipSuccess) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  int sb = -1;
+  if (e == hipSuccess) sb = staging_acquire(std::max<size_t>(meta_bytes, 256), dev, &e);
+  if (sb < 0) {
     fi::plan_free(&hp);
-    return hip_fail(e, "hipHostMalloc (plan staging)");
+    return hip_fail(e, "pinned staging buffer for the plan upload");
   }
+  void* staging = staging_ptr(sb);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   char* st8 = reinterpret_cast<char*>(staging);
   memset(st8, 0, meta_bytes);
   memcpy(st8 + hp.layout.tiles_off, hp.tiles,
@@ -261,36 +368,31 @@ fi_status fi_plan(const fi_problem* problem, int32_t num_cus, void* workspace,
   if (hp.num_levels >= 2)
     memcpy(st8 + hp.layout.state_off_off, hp.state_off,
            sizeof(int32_t) * (size_t)hp.num_levels * hp.batch);
-  e = hipMemcpyAsync(workspace, staging, meta_bytes, hipMemcpyHostToDevice,
-                     reinterpret_cast<hipStream_t>(stream));
+  e = hipMemcpyAsync(workspace, staging, meta_bytes, hipMemcpyHostToDevice, hs);
+  const bool copied = e == hipSuccess;
   if (e == hipSuccess && hp.rope)   // the (cos, sin) table, built on the device
     e = fi::launch_rope_table(reinterpret_cast<char*>(workspace) + hp.layout.rope_off,
-                              hp.rope_rows, hp.D, hp.rope_theta, hp.rope_scale,
-                              reinterpret_cast<hipStream_t>(stream));
+                              hp.rope_rows, hp.D, hp.rope_theta, hp.rope_scale, hs);
+  const hipError_t er = staging_release(sb, hs, copied);
+  if (e == hipSuccess) e = er;
   if (e != hipSuccess) {
-    (void)hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
-    (void)hipHostFree(staging);
     fi::plan_free(&hp);
     return hip_fail(e, "uploading the plan");
   }
   fi_plan_s* pl = new (std::nothrow) fi_plan_s;
   if (!pl) {
-    (void)hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));   // staging in use
-    (void)hipHostFree(staging);
     fi::plan_free(&hp);
     return fail(FI_ERR_INVALID_ARG, "out of host memory for the plan object");
   }
   pl->hp = hp;
   pl->workspace = reinterpret_cast<char*>(workspace);
   pl->workspace_bytes = workspace_bytes;
-  pl->staging = staging;
   *plan_out = pl;
   return FI_OK;
 }
 
 fi_status fi_plan_destroy(fi_plan_t plan) {
   if (!plan) return FI_OK;
-  if (plan->staging) (void)hipHostFree(plan->staging);
   fi::plan_free(&plan->hp);
   delete plan;
   return FI_OK;
@@ -309,6 +411,8 @@ fi_status fi_plan_get_stats(fi_plan_t plan, fi_plan_stats* s) {
   s->num_cus = hp.num_cus;
   s->workspace_bytes = hp.layout.total;
   s->num_folded = hp.num_folded;
+  s->prefix_split_p = hp.prefix_split_p;
+  s->staging_buffers = staging_count();
   return FI_OK;
 }
 
@@ -371,11 +475,14 @@ fi_status check_run_args(const fi::HostPlan& hp, const void* q, const void* k_pa
 fi_status enqueue_run(fi_plan_t plan, int stages, const void* q, const void* k_pages,
                       const void* v_pages, const LevelTables& lv, const int32_t* kv_indptr,
                       const int32_t* kv_indices, const float* k_scale, const float* v_scale,
-                      float sm_scale, void* o, float* lse, hipStream_t s) {
+                      float sm_scale, void* o, float* lse, hipStream_t s,
+                      int64_t* rec = nullptr, const int64_t* rec_base = nullptr) {
   const fi::HostPlan& hp = plan->hp;
   const bool qbf = hp.q_dtype == FI_BF16;
   const int kv = hp.kv_dtype == FI_E4M3 ? 2 : (qbf ? 1 : 0);
   fi::DecodeParams p = base_params(plan, q, k_pages, v_pages, k_scale, v_scale, sm_scale, o, lse);
+  p.rec = rec;
+  p.rec_base = rec_base;
   hipError_t e = hipSuccess;
   const bool do_prefix = (stages & kStagePrefix) && hp.num_prefix_tiles > 0;
   const bool do_decode = (stages & kStageDecode) && hp.num_tiles > 0;
@@ -387,8 +494,8 @@ fi_status enqueue_run(fi_plan_t plan, int stages, const void* q, const void* k_p
     pp.kv_indptr = kv_indptr;
     pp.kv_indices = kv_indices;
     pp.qo_indptr = qo_all;
-    e = fi::launch_prefix(pp, (int)hp.num_prefix_tiles, hp.prefix_waves, true, qbf, kv, hp.D,
-                          s);
+    e = fi::launch_prefix(pp, (int)hp.num_prefix_tiles, hp.prefix_waves, true, false, qbf, kv,
+                          hp.D, s);
     if (e != hipSuccess) return hip_fail(e, "append launch");
   } else if (do_prefix) {
     // prefix tiles of level l read that level's table; row -> request = the
@@ -406,7 +513,8 @@ fi_status enqueue_run(fi_plan_t plan, int stages, const void* q, const void* k_p
                                (int64_t)l * hp.batch
                          : nullptr;
       pp.num_tiles = (int32_t)(hp.num_tiles + hp.level_tile_off[l]);
-      e = fi::launch_prefix(pp, (int)n, hp.prefix_waves, false, qbf, kv, hp.D, s);
+      e = fi::launch_prefix(pp, (int)n, hp.prefix_waves, false, (hp.prefix_split_p >> l) & 1u,
+                            qbf, kv, hp.D, s);
       if (e != hipSuccess) return hip_fail(e, "prefix launch");
     }
   }
@@ -414,7 +522,7 @@ fi_status enqueue_run(fi_plan_t plan, int stages, const void* q, const void* k_p
     p.kv_indptr = kv_indptr;
     p.kv_indices = kv_indices;
     e = fi::launch_decode(p, (int)hp.num_tiles, hp.heads_per_tile, qbf, kv, hp.num_folded > 0,
-                          hp.D, s);
+                          hp.decode_depth, hp.D, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
   }
   if (stages & kStageMerge) return launch_merge(plan, o, lse, s);
@@ -550,6 +658,48 @@ fi_status fi_debug_run_stage(fi_plan_t plan, int32_t stage, const void* q, const
   const int which = stage == 0 ? kStageDecode : stage == 1 ? kStagePrefix : kStageMerge;
   return enqueue_run(plan, which, q, k_pages, v_pages, lv, kv_indptr, kv_indices, k_scale,
                      v_scale, sm_scale, o, lse, reinterpret_cast<hipStream_t>(stream));
+}
+
+fi_status fi_debug_record_walk(fi_plan_t plan, int32_t stage, const void* q,
+                               const void* k_pages, const void* v_pages,
+                               const int32_t* prefix_kv_indptr,
+                               const int32_t* prefix_kv_indices,
+                               const int32_t* prefix_last_page_len, const int32_t* kv_indptr,
+                               const int32_t* kv_indices, const int32_t* last_page_len,
+                               const float* k_scale, const float* v_scale, float sm_scale,
+                               void* o, float* lse, int64_t* rec, const int64_t* rec_base,
+                               void* stream) {
+  g_last_error.clear();
+  if (!plan) return fail(FI_ERR_INVALID_ARG, "plan is NULL");
+  const fi::HostPlan& hp = plan->hp;
+  if (stage != 0 && stage != 1)
+    return fail(FI_ERR_INVALID_ARG, "stage must be 0 (decode kernel) or 1 (multi-row kernel)");
+  if (!rec || !rec_base) return fail(FI_ERR_INVALID_ARG, "rec and rec_base must be non-NULL");
+  if (stage == 1 && hp.num_prefix_tiles == 0)
+    return fail(FI_ERR_INVALID_ARG, "the plan has no cascade prefix or append tiles");
+  if (hp.num_levels > 1)
+    return fail(FI_ERR_INVALID_ARG, "record hook: plans with one cascade level at most");
+  if (hp.batch == 0 || (hp.append && hp.total_q == 0)) return FI_OK;
+  const LevelTables lv = hp.num_levels == 1
+                             ? one_level(prefix_kv_indptr, prefix_kv_indices, prefix_last_page_len)
+                             : LevelTables();
+  fi_status st = check_run_args(hp, q, k_pages, v_pages, lv, kv_indptr, kv_indices,
+                                last_page_len, sm_scale, o);
+  if (st != FI_OK) return st;
+  // the record instances that are built
+  const bool f16 = hp.q_dtype == FI_F16 && hp.kv_dtype == FI_F16;
+  const bool fp8 = hp.q_dtype == FI_BF16 && hp.kv_dtype == FI_E4M3;
+  const int depth = hp.decode_depth ? hp.decode_depth
+                                    : (hp.num_folded > 0 && hp.heads_per_tile <= 4 ? 2 : 1);
+  if (hp.D != 128 || hp.rope || !(f16 || fp8) ||
+      (stage == 1 && (hp.prefix_waves != 8 || (fp8 && hp.append))) ||
+      (stage == 0 && fp8 && depth == 2))
+    return fail(FI_ERR_UNSUPPORTED,
+                "record hook: head_dim 128, fp16 q + fp16 K/V or bf16 q + e4m3 K/V (one step "
+                "in flight, no append), 8-wave multi-row tiles, no RoPE");
+  return enqueue_run(plan, stage == 0 ? kStageDecode : kStagePrefix, q, k_pages, v_pages, lv,
+                     kv_indptr, kv_indices, k_scale, v_scale, sm_scale, o, lse,
+                     reinterpret_cast<hipStream_t>(stream), rec, rec_base);
 }
 
 fi_status fi_merge_states(int32_t num_states, const void* const* v_states,

@@ -238,7 +238,11 @@ struct RopeLds {
   static constexpr int BYTES = kStep * STRIDE + kStep * ROW;
   static constexpr int FPL = (FREQ + 63) / 64;       // frequencies per lane
 };
-template <int KV, bool QBF16, bool PS_POW2, bool FOLD, int DEPTH, bool ROPE, int D>
+// REC (a test instance): every K vector load also writes its byte offset in
+// the K pool to p.rec at ((rec_base[request] + token) * Hkv + kv head) * VR +
+// 16-byte chunk -- the page walk exactly as the loads take it.
+template <int KV, bool QBF16, bool PS_POW2, bool FOLD, int DEPTH, bool ROPE, int D,
+          bool REC = false>
 __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams p) {
   static_assert(!ROPE || !FOLD, "RoPE plans have no cascade level to fold");
   using S = Stage<KV, D>;
@@ -288,6 +292,7 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   // vector vin = head vin / VR of the tile's run, 16-byte chunk vin % VR
   const int vh = vin / S::VR, vc = vin - vh * S::VR;
   const int64_t hoff = (int64_t)(h0 + vh) * p.head_stride + 16 * vc;
+  const int64_t rec_tok = REC ? p.rec_base[r] : 0;
   const char* kbase = reinterpret_cast<const char*>(p.k_pages) + hoff;
   const char* vbase = reinterpret_cast<const char*>(p.v_pages) + hoff;
   const int last = t1 - 1;
@@ -363,6 +368,8 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
       const uint64_t off = (uint64_t)page * p.page_bytes + sl * p.slot_stride;
       kq[u] = ld_stream<u32x4>(kbase, off);
       vq[u] = ld_stream<u32x4>(vbase, off);
+      if constexpr (REC)
+        p.rec[((rec_tok + t) * p.Hkv + h0 + vh) * S::VR + vc] = (int64_t)(off + hoff);
     }
   };
   auto stage = [&](const u32x4 (&kq)[S::LOADS], const u32x4 (&vq)[S::LOADS]) {
@@ -607,20 +614,27 @@ __device__ __forceinline__ int xcd_tile(int b, int n) {
   return x * per + min(x, rem) + k;
 }
 
-template <int KV, bool QBF16, int WAVES, bool PS_POW2, bool APPEND, int D>
+// MODE: kPrefixPlain / kPrefixSplitP (cascade prefix tiles) or kPrefixAppend.
+enum { kPrefixPlain = 0, kPrefixSplitP = 1, kPrefixAppend = 2 };
+
+// REC: as decode_kernel's (the token base is that of the tile's group, or of
+// its request for append tiles).
+template <int KV, bool QBF16, int WAVES, bool PS_POW2, int MODE, int D, bool REC = false>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 && D != 256 ? 2 : 1) void prefix_kernel(
     DecodeParams p) {
+  constexpr bool APPEND = MODE == kPrefixAppend;
   // row tiles (16 query rows each) per wave: two, one at D = 256
   constexpr int RT = prefix_rows_per_wave(D) / 16;
   using S = PStage<KV, D>;
-  // bf16 append tiles: P.V takes p as a bf16 high part plus a bf16
-  // residual -- bf16 keeps 8 bits of p, and when a few keys carry
-  // comparable weight (the first rows of a prefill see a handful of keys)
-  // that rounding alone moves o past the accuracy bar.  Cascade prefix tiles
-  // keep one bf16 p: their rows see a long shared prefix, and both the
-  // residual products and a per-tile choice (both paths' registers: 256
-  // VGPRs with spills) cost the MFMA-bound prefix kernel more than a tenth.
-  constexpr bool SPLITP = APPEND && KV == kKvBF16;
+  // bf16 K/V: P.V takes p as a bf16 high part plus a bf16 residual in append
+  // tiles and in the split-p cascade instance -- bf16 keeps 8 bits of p, and
+  // when a few keys carry comparable weight (the first rows of a prefill, a
+  // short shared prefix) that rounding alone moves o past the accuracy bar.
+  // The plan picks the split instance for a cascade level whose shortest
+  // prefix is under kSplitPKeys keys; long prefixes keep one bf16 p (the
+  // residual products cost the MFMA-bound kernel more than a tenth, and over
+  // that many keys the rounding averages out).
+  constexpr bool SPLITP = MODE != kPrefixPlain && KV == kKvBF16;
   __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
   int* ptab = reinterpret_cast<int*>(lds + 2 * S::BUF);
   const int tid = threadIdx.x;
@@ -713,6 +727,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 && D != 256 ? 2 : 1) void pr
       const uint64_t off =
           (uint64_t)page * p.page_bytes + sl * p.slot_stride + 16 * (q % VR);
       vec[u] = ld_global<u32x4>(idx < PV ? kbase : vbase, off);
+      if constexpr (REC) {
+        if (idx < PV)
+          p.rec[((p.rec_base[grp] + t) * p.Hkv + h) * VR + q % VR] =
+              (int64_t)(off + (uint64_t)h * p.head_stride);
+      }
     }
   };
   auto store = [&](int buf, const u32x4 (&vec)[NL]) {
@@ -926,15 +945,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 && D != 256 ? 2 : 1) void pr
 }
 
 // ---- launchers ----------------------------------------------------------------
-// FI_DECODE_DEPTH=1 keeps one step in flight for every workgroup size (for
-// measurement); read once.
-static int getenv_depth() {
-  static const int d = [] {
-    const char* v = getenv("FI_DECODE_DEPTH");
-    return v && *v ? atoi(v) : 0;
-  }();
-  return d;
-}
+// depth (from the plan's tuning): 0 = each instance's own choice below, 1 =
+// one step of loads in flight everywhere, 2 = two where the instance has a
+// two-step form.
 
 constexpr int kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
 
@@ -975,7 +988,7 @@ static hipError_t launch_decode_t(const DecodeParams& p, int num_tiles, int wave
 // VGPRs) and has no RoPE table.
 template <int KV, bool QBF16, int D>
 static hipError_t launch_decode_f(const DecodeParams& p, int num_tiles, int waves, bool fold,
-                                  hipStream_t s) {
+                                  int depth, hipStream_t s) {
   if (num_tiles <= 0) return hipSuccess;
   if constexpr (D == 256) {
     if (p.rope_table) return launch_decode_t<KV, QBF16, false, 1, true, D>(p, num_tiles, waves, s);
@@ -987,11 +1000,11 @@ static hipError_t launch_decode_f(const DecodeParams& p, int num_tiles, int wave
       if constexpr (D == 64)
         return launch_decode_t<KV, QBF16, false, 1, true, D>(p, num_tiles, waves, s);
       else
-        return getenv_depth() == 1
+        return depth == 1
                    ? launch_decode_t<KV, QBF16, false, 1, true, D>(p, num_tiles, waves, s)
                    : launch_decode_t<KV, QBF16, false, 2, true, D>(p, num_tiles, waves, s);
     }
-    const bool deep = fold && waves <= 4 && getenv_depth() != 1;
+    const bool deep = depth == 2 || (depth == 0 && fold && waves <= 4);
     if (fold)
       return deep ? launch_decode_t<KV, QBF16, true, 2, false, D>(p, num_tiles, waves, s)
                   : launch_decode_t<KV, QBF16, true, 1, false, D>(p, num_tiles, waves, s);
@@ -1000,72 +1013,161 @@ static hipError_t launch_decode_f(const DecodeParams& p, int num_tiles, int wave
   }
 }
 
-template <int KV, bool QBF16, int W, bool APPEND, int D>
+template <int KV, bool QBF16, int W, int MODE, int D>
 static void launch_prefix_w(const DecodeParams& p, int num_tiles, hipStream_t s) {
   if (p.ps_shift >= 0)
-    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, W, true, APPEND, D>), dim3(num_tiles),
+    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, W, true, MODE, D>), dim3(num_tiles),
                        dim3(64 * W), 0, s, p);
   else
-    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, W, false, APPEND, D>), dim3(num_tiles),
+    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, W, false, MODE, D>), dim3(num_tiles),
                        dim3(64 * W), 0, s, p);
+}
+
+template <int KV, bool QBF16, int W, int D>
+static void launch_prefix_m(const DecodeParams& p, int num_tiles, bool append, bool split,
+                            hipStream_t s) {
+  if (append) {
+    launch_prefix_w<KV, QBF16, W, kPrefixAppend, D>(p, num_tiles, s);
+    return;
+  }
+  if constexpr (KV == kKvBF16) {   // the split instance exists for bf16 K/V only
+    if (split) {
+      launch_prefix_w<KV, QBF16, W, kPrefixSplitP, D>(p, num_tiles, s);
+      return;
+    }
+  }
+  launch_prefix_w<KV, QBF16, W, kPrefixPlain, D>(p, num_tiles, s);
 }
 
 template <int KV, bool QBF16, int D>
 static hipError_t launch_prefix_t(const DecodeParams& p, int num_tiles, int waves, bool append,
-                                  hipStream_t s) {
+                                  bool split, hipStream_t s) {
   if (num_tiles <= 0) return hipSuccess;
   if (waves == 4)
-    append ? launch_prefix_w<KV, QBF16, 4, true, D>(p, num_tiles, s)
-           : launch_prefix_w<KV, QBF16, 4, false, D>(p, num_tiles, s);
+    launch_prefix_m<KV, QBF16, 4, D>(p, num_tiles, append, split, s);
   else
-    append ? launch_prefix_w<KV, QBF16, 8, true, D>(p, num_tiles, s)
-           : launch_prefix_w<KV, QBF16, 8, false, D>(p, num_tiles, s);
+    launch_prefix_m<KV, QBF16, 8, D>(p, num_tiles, append, split, s);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_decode_d(const DecodeParams& p, int num_tiles, int waves, bool q_bf16,
-                                  int kv, bool fold, hipStream_t s) {
+                                  int kv, bool fold, int depth, hipStream_t s) {
   if (kv == kKvE4M3)
-    return q_bf16 ? launch_decode_f<kKvE4M3, true, D>(p, num_tiles, waves, fold, s)
-                  : launch_decode_f<kKvE4M3, false, D>(p, num_tiles, waves, fold, s);
-  return q_bf16 ? launch_decode_f<kKvBF16, true, D>(p, num_tiles, waves, fold, s)
-                : launch_decode_f<kKvF16, false, D>(p, num_tiles, waves, fold, s);
+    return q_bf16 ? launch_decode_f<kKvE4M3, true, D>(p, num_tiles, waves, fold, depth, s)
+                  : launch_decode_f<kKvE4M3, false, D>(p, num_tiles, waves, fold, depth, s);
+  return q_bf16 ? launch_decode_f<kKvBF16, true, D>(p, num_tiles, waves, fold, depth, s)
+                : launch_decode_f<kKvF16, false, D>(p, num_tiles, waves, fold, depth, s);
 }
 
 template <int D>
 static hipError_t launch_prefix_d(const DecodeParams& p, int num_tiles, int waves, bool append,
-                                  bool q_bf16, int kv, hipStream_t s) {
+                                  bool split, bool q_bf16, int kv, hipStream_t s) {
   if (kv == kKvE4M3)
-    return q_bf16 ? launch_prefix_t<kKvE4M3, true, D>(p, num_tiles, waves, append, s)
-                  : launch_prefix_t<kKvE4M3, false, D>(p, num_tiles, waves, append, s);
-  return q_bf16 ? launch_prefix_t<kKvBF16, true, D>(p, num_tiles, waves, append, s)
-                : launch_prefix_t<kKvF16, false, D>(p, num_tiles, waves, append, s);
+    return q_bf16 ? launch_prefix_t<kKvE4M3, true, D>(p, num_tiles, waves, append, split, s)
+                  : launch_prefix_t<kKvE4M3, false, D>(p, num_tiles, waves, append, split, s);
+  return q_bf16 ? launch_prefix_t<kKvBF16, true, D>(p, num_tiles, waves, append, split, s)
+                : launch_prefix_t<kKvF16, false, D>(p, num_tiles, waves, append, split, s);
+}
+
+// ---- record instances (test hook): head_dim 128, fp16 q + fp16 K/V or bf16
+// q + e4m3 K/V; the loop shapes of one and two steps in flight (fp16), no
+// fold and no RoPE (neither changes the loads' addresses)
+template <int KV, bool QBF16, int DEPTH>
+static hipError_t launch_decode_rec_t(const DecodeParams& p, int num_tiles, int waves,
+                                      hipStream_t s) {
+  const size_t lds = (size_t)Stage<KV, 128>::lds_bytes(waves);
+  static const hipError_t attr = [] {
+    const int max_lds = Stage<KV, 128>::lds_bytes(kWavesPerTile);
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, true, false, DEPTH, false, 128, true>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(
+              &decode_kernel<KV, QBF16, false, false, DEPTH, false, 128, true>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+    return e;
+  }();
+  if (attr != hipSuccess) return attr;
+  if (p.ps_shift >= 0)
+    hipLaunchKernelGGL((decode_kernel<KV, QBF16, true, false, DEPTH, false, 128, true>),
+                       dim3(num_tiles), dim3(64 * waves), lds, s, p);
+  else
+    hipLaunchKernelGGL((decode_kernel<KV, QBF16, false, false, DEPTH, false, 128, true>),
+                       dim3(num_tiles), dim3(64 * waves), lds, s, p);
+  return hipGetLastError();
+}
+
+static hipError_t launch_decode_rec(const DecodeParams& p, int num_tiles, int waves,
+                                    bool q_bf16, int kv, int depth, int head_dim,
+                                    hipStream_t s) {
+  if (head_dim != 128 || p.rope_table) return hipErrorInvalidValue;
+  if (kv == kKvF16 && !q_bf16)
+    return depth == 2 ? launch_decode_rec_t<kKvF16, false, 2>(p, num_tiles, waves, s)
+                      : launch_decode_rec_t<kKvF16, false, 1>(p, num_tiles, waves, s);
+  if (kv == kKvE4M3 && q_bf16 && depth != 2)
+    return launch_decode_rec_t<kKvE4M3, true, 1>(p, num_tiles, waves, s);
+  return hipErrorInvalidValue;
+}
+
+template <int KV, bool QBF16, int MODE>
+static hipError_t launch_prefix_rec_t(const DecodeParams& p, int num_tiles, hipStream_t s) {
+  if (p.ps_shift >= 0)
+    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, 8, true, MODE, 128, true>), dim3(num_tiles),
+                       dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, 8, false, MODE, 128, true>), dim3(num_tiles),
+                       dim3(512), 0, s, p);
+  return hipGetLastError();
+}
+
+static hipError_t launch_prefix_rec(const DecodeParams& p, int num_tiles, int waves,
+                                    bool append, bool q_bf16, int kv, int head_dim,
+                                    hipStream_t s) {
+  if (head_dim != 128 || waves != 8) return hipErrorInvalidValue;
+  if (kv == kKvF16 && !q_bf16)
+    return append ? launch_prefix_rec_t<kKvF16, false, kPrefixAppend>(p, num_tiles, s)
+                  : launch_prefix_rec_t<kKvF16, false, kPrefixPlain>(p, num_tiles, s);
+  if (kv == kKvE4M3 && q_bf16 && !append)
+    return launch_prefix_rec_t<kKvE4M3, true, kPrefixPlain>(p, num_tiles, s);
+  return hipErrorInvalidValue;
 }
 
 // q_bf16: q (and o) are bf16, else fp16.  kv: KvKind.  fold: the work list
-// has tiles that fold earlier states into their output.  head_dim: 64, 128
-// or 256.
+// has tiles that fold earlier states into their output.  depth: 0, 1 or 2
+// (above).  head_dim: 64, 128 or 256.  p.rec != NULL selects the record
+// instances (hipErrorInvalidValue for a configuration they do not cover).
 hipError_t launch_decode(const DecodeParams& p, int num_tiles, int waves, bool q_bf16,
-                         int kv, bool fold, int head_dim, hipStream_t s) {
+                         int kv, bool fold, int depth, int head_dim, hipStream_t s) {
   if (waves < 1 || waves > kWavesPerTile) return hipErrorInvalidValue;
+  if (p.rec) {
+    if (num_tiles <= 0) return hipSuccess;
+    return launch_decode_rec(p, num_tiles, waves, q_bf16, kv,
+                             depth ? depth : (fold && waves <= 4 ? 2 : 1), head_dim, s);
+  }
   switch (head_dim) {
-    case 64: return launch_decode_d<64>(p, num_tiles, waves, q_bf16, kv, fold, s);
-    case 128: return launch_decode_d<128>(p, num_tiles, waves, q_bf16, kv, fold, s);
-    case 256: return launch_decode_d<256>(p, num_tiles, waves, q_bf16, kv, fold, s);
+    case 64: return launch_decode_d<64>(p, num_tiles, waves, q_bf16, kv, fold, depth, s);
+    case 128: return launch_decode_d<128>(p, num_tiles, waves, q_bf16, kv, fold, depth, s);
+    case 256: return launch_decode_d<256>(p, num_tiles, waves, q_bf16, kv, fold, depth, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 // append: append tiles (rows limited by ReqInfo.kv_len), else cascade
-// prefix.  head_dim: 64, 128 or 256.
+// prefix; split: bf16 cascade prefix tiles pass p with a residual.
+// head_dim: 64, 128 or 256.
 hipError_t launch_prefix(const DecodeParams& p, int num_tiles, int waves, bool append,
-                         bool q_bf16, int kv, int head_dim, hipStream_t s) {
+                         bool split, bool q_bf16, int kv, int head_dim, hipStream_t s) {
   if (waves != 4 && waves != 8) return hipErrorInvalidValue;
+  if (p.rec) {
+    if (num_tiles <= 0) return hipSuccess;
+    return launch_prefix_rec(p, num_tiles, waves, append, q_bf16, kv, head_dim, s);
+  }
   switch (head_dim) {
-    case 64: return launch_prefix_d<64>(p, num_tiles, waves, append, q_bf16, kv, s);
-    case 128: return launch_prefix_d<128>(p, num_tiles, waves, append, q_bf16, kv, s);
-    case 256: return launch_prefix_d<256>(p, num_tiles, waves, append, q_bf16, kv, s);
+    case 64: return launch_prefix_d<64>(p, num_tiles, waves, append, split, q_bf16, kv, s);
+    case 128: return launch_prefix_d<128>(p, num_tiles, waves, append, split, q_bf16, kv, s);
+    case 256: return launch_prefix_d<256>(p, num_tiles, waves, append, split, q_bf16, kv, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -20,6 +20,10 @@ constexpr int kPrefixMaxWaves = 8;       // prefix workgroup: 4 or 8 waves
 constexpr int kPrefixMaxChunk = 4096;    // prefix tokens per tile (page table in LDS)
 constexpr int kMaxMergeStates = 64;
 constexpr int kMaxLevels = 8;            // shared cascade levels
+// bf16 P.V rounds p to 8 bits; over fewer keys than this (all of them of
+// comparable weight, nothing else in the row) that rounding alone can move
+// o past 2e-3 + 1e-2 |o|, so such prefixes take p with a bf16 residual
+constexpr int kSplitPKeys = 256;
 
 enum TileKind : int32_t { kDecodeTile = 0, kPrefixTile = 1, kAppendTile = 2 };
 
@@ -106,6 +110,11 @@ struct HostPlan {
   int32_t level_qo_start[kMaxLevels];
   int64_t level_tile_off[kMaxLevels + 1];
   int32_t* state_off;   // num_levels * batch entries when num_levels >= 2
+  int32_t decode_depth; // 0: the launcher's choice per instance; 1 or 2 forced
+  // bf16 cascade prefix launches whose p goes to P.V as a bf16 high part
+  // plus a residual (bit l set: level l has a prefix chunk shorter than
+  // kSplitPKeys keys)
+  uint32_t prefix_split_p;
   int32_t rope;         // FI_POS_ROPE_LLAMA or 0
   int32_t rope_rows;    // positions in the RoPE table (longest request)
   float rope_theta, rope_scale;
@@ -114,6 +123,23 @@ struct HostPlan {
   MergeUnit* merge_units;  // num_merge_units entries
   int32_t* qo_indptr;   // qo_len entries (cascade group starts / append query starts)
   WorkspaceLayout layout;
+};
+
+// Plan tuning: every field 0 selects the built-in default (the measured
+// best); other values only change how the work is cut, never the result.
+struct Tuning {
+  int32_t heads_per_tile;       // kv heads per decode workgroup (1, 2, 4, 8)
+  int32_t waves_per_cu;         // decode waves the chunk search targets per CU (16)
+  int32_t chunk_min;            // smallest decode chunk in tokens (32)
+  int32_t prefix_waves;         // waves per multi-row tile, 4 or 8
+  int32_t prefix_tiles_per_cu;  // cascade prefix tiles per CU (1)
+  int32_t prefix_chunk_min;     // smallest cascade prefix chunk in tokens (256)
+  int32_t cascade_fold;         // 1 fold one-chunk suffixes (default), -1 never
+  int32_t fold_max_suffix;      // longest suffix one fold chunk covers (1024)
+  int32_t append_tiles_pct;     // append tiles per resident workgroup x 100 (125)
+  int32_t append_chunk_min;     // smallest append key chunk in tokens (128)
+  int32_t decode_depth;         // steps of K/V loads in flight, 1 or 2 (per instance)
+  int32_t prefix_split_p;       // bf16 cascade prefix: 1 always split p, -1 never
 };
 
 // Builds the plan on the host.  Returns 0 or an fi_status code with `err`
@@ -139,6 +165,7 @@ struct PlanInput {
   int32_t causal;
   int32_t ragged;   // rows kv_indptr[r] + t, no page indices
   int32_t hnd;      // pages head-major: [page][Hkv][page_size][D]
+  Tuning tune;
 };
 int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen);
 void plan_free(HostPlan* p);
@@ -177,6 +204,10 @@ struct DecodeParams {
   // rows, head_stride = 1 row) or HND pages (slot_stride = 1 row,
   // head_stride = page_size rows)
   uint32_t page_bytes, slot_stride, head_stride;
+  // test instances only: the byte offset of every K vector load, indexed by
+  // (rec_base[request or group] + token, kv head, 16-byte chunk)
+  int64_t* rec;
+  const int64_t* rec_base;
 };
 
 struct MergeParams {

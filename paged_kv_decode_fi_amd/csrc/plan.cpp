@@ -41,11 +41,8 @@
 namespace fi {
 namespace {
 
-int env_int(const char* name, int dflt) {
-  const char* s = getenv(name);
-  if (!s || !*s) return dflt;
-  return atoi(s);
-}
+// a tuning field, or the default when it is 0
+int tune_or(int32_t v, int dflt) { return v != 0 ? v : dflt; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -87,7 +84,7 @@ int plan_append(const PlanInput& in, const std::vector<int64_t>& lens, int num_c
   // (at head_dim 256 the 4-wave instance holds a CU alone: 8 waves)
   const int rpw = prefix_rows_per_wave(in.D);
   const int waves =
-      env_int("FI_PREFIX_WAVES", rows_max <= 4 * rpw && in.D != 256 ? 4 : 8) == 4 ? 4 : 8;
+      tune_or(in.tune.prefix_waves, rows_max <= 4 * rpw && in.D != 256 ? 4 : 8) == 4 ? 4 : 8;
   const int64_t R = (int64_t)rpw * waves;   // rows per tile
   const int64_t slots_per_cu = waves == 4 ? 2 : 1;
   // row tiles: (request, rows [row0, row1), keys needed by the last row)
@@ -116,16 +113,16 @@ int plan_append(const PlanInput& in, const std::vector<int64_t>& lens, int num_c
   if (in.chunk_tokens > 0) {
     chunk = std::min<int64_t>(round_up(in.chunk_tokens, kBlockTokens), kPrefixMaxChunk);
   } else {
-    // about FI_APPEND_TILES_PCT / 100 (1.25) tiles per resident workgroup, so
-    // unequal requests even out; chunks of at least FI_APPEND_CHUNK_MIN keys
+    // about append_tiles_pct / 100 (1.25) tiles per resident workgroup, so
+    // unequal requests even out; chunks of at least append_chunk_min keys
     const int64_t want = std::max<int64_t>(
-        1, (int64_t)num_cus * slots_per_cu * env_int("FI_APPEND_TILES_PCT", 125) / 100);
+        1, (int64_t)num_cus * slots_per_cu * tune_or(in.tune.append_tiles_pct, 125) / 100);
     if (rts.empty() || tiles_for(hi) >= want) {
       chunk = hi;
     } else {
       // smallest c in [lo, hi] (whole 32-token steps) with tiles(c) <= want
       const int64_t lo = std::min<int64_t>(
-          round_up(std::max(env_int("FI_APPEND_CHUNK_MIN", 128), kBlockTokens), kBlockTokens),
+          round_up(std::max(tune_or(in.tune.append_chunk_min, 128), kBlockTokens), kBlockTokens),
           hi);
       int64_t a = lo / kBlockTokens, b = hi / kBlockTokens;
       while (a < b) {
@@ -294,6 +291,19 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
     PLAN_FAIL(1, "kv_indptr and last_page_len (host) are required");
   if (in.chunk_tokens < 0 || in.chunk_tokens % kChunkAlign != 0)
     PLAN_FAIL(1, "chunk_tokens must be 0 or a positive multiple of %d", kChunkAlign);
+  {
+    const Tuning& tu = in.tune;
+    const int32_t counts[] = {tu.heads_per_tile, tu.waves_per_cu, tu.chunk_min,
+                              tu.prefix_waves, tu.prefix_tiles_per_cu, tu.prefix_chunk_min,
+                              tu.fold_max_suffix, tu.append_tiles_pct, tu.append_chunk_min};
+    for (int32_t c : counts)
+      if (c < 0) PLAN_FAIL(1, "tuning values must be >= 0 (0 = default)");
+    if (tu.decode_depth < 0 || tu.decode_depth > 2)
+      PLAN_FAIL(1, "tuning decode_depth must be 0 (automatic), 1 or 2");
+    if (tu.cascade_fold < -1 || tu.cascade_fold > 1 || tu.prefix_split_p < -1 ||
+        tu.prefix_split_p > 1)
+      PLAN_FAIL(1, "tuning cascade_fold and prefix_split_p must be -1, 0 or 1");
+  }
   // paged tables index kv_indices from 0; a ragged table's entries are the
   // requests' first rows in K / V, anywhere
   if (B > 0 && !in.ragged && in.kv_indptr[0] != 0) PLAN_FAIL(1, "kv_indptr[0] must be 0");
@@ -367,22 +377,23 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
     PLAN_FAIL(1, "rope_theta and rope_scale must be finite");
 
   // ---- decode chunk length
-  // heads per tile: the largest of FI_HEADS_PER_TILE (default 8; 4 with
+  // heads per tile: the largest of tune.heads_per_tile (default 8; 4 with
   // RoPE, whose kernel holds 3 waves per SIMD: three 4-wave workgroups fill
   // a CU where one 8-wave workgroup would leave a third of it idle), 4, 2, 1
   // dividing Hkv
   const int hpt_default = rope ? kWavesPerTile / 2 : kWavesPerTile;
-  int hpt = (int)std::min<int64_t>(kWavesPerTile, std::max<int64_t>(1, env_int("FI_HEADS_PER_TILE",
-                                                                              hpt_default)));
+  const bool hpt_forced = in.tune.heads_per_tile > 0;
+  int hpt = (int)std::min<int64_t>(kWavesPerTile,
+                                   std::max<int64_t>(1, tune_or(in.tune.heads_per_tile, hpt_default)));
   // (head_dim 256 with RoPE: the step's K/V rows of 8 heads and the
   // table rows exceed the LDS, so at most 4)
   if (rope && in.D == 256) hpt = std::min(hpt, kWavesPerTile / 2);
   while (hpt & (hpt - 1)) hpt &= hpt - 1;
   while (Hkv % hpt) hpt >>= 1;
-  const int64_t waves_per_cu = env_int("FI_WAVES_PER_CU", 16);
-  const int64_t c_min = round_up(std::max(env_int("FI_CHUNK_MIN", 32), kChunkAlign),
+  const int64_t waves_per_cu = std::max(1, tune_or(in.tune.waves_per_cu, 16));
+  const int64_t c_min = round_up(std::max(tune_or(in.tune.chunk_min, 32), kChunkAlign),
                                  kChunkAlign);
-  if (env_int("FI_HEADS_PER_TILE", 0) == 0) {
+  if (!hpt_forced) {
     // small problems (fewer than 4 tiles per CU even at the minimum chunk):
     // fewer heads per tile, so more, smaller workgroups spread the latency
     auto tiles_at_min = [&](int h) {
@@ -421,16 +432,16 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   }
   // Cascade: a request with prefix states whose suffix is one chunk folds
   // those states into its decode tile's output, so no merge pass is needed.
-  // When every such suffix is short (<= FI_FOLD_MAX_SUFFIX tokens, default
+  // When every such suffix is short (<= tune.fold_max_suffix tokens, default
   // 1024), cover each with one chunk, 2 kv heads per tile (small tiles, two
   // steps of loads in flight), provided that still gives >= 4 waves per CU.
-  const bool fold_ok = env_int("FI_CASCADE_FOLD", 1) != 0;
-  if (NG > 0 && fold_ok && in.chunk_tokens == 0 && env_int("FI_HEADS_PER_TILE", 0) == 0) {
+  const bool fold_ok = in.tune.cascade_fold >= 0;
+  if (NG > 0 && fold_ok && in.chunk_tokens == 0 && !hpt_forced) {
     int64_t ls_max = 0;
     for (int r = 0; r < B; ++r)
       if (has_prefix(r)) ls_max = std::max(ls_max, lens[r]);
     const int hpt_f = Hkv % 2 == 0 ? 2 : 1;
-    if (ls_max > 0 && ls_max <= env_int("FI_FOLD_MAX_SUFFIX", 1024)) {
+    if (ls_max > 0 && ls_max <= tune_or(in.tune.fold_max_suffix, 1024)) {
       const int64_t chunk_f = round_up(ls_max, kChunkAlign);
       int64_t w = 0;
       for (int r = 0; r < B; ++r) w += std::max<int64_t>(1, ceil_div(lens[r], chunk_f));
@@ -443,7 +454,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   const int64_t head_groups = Hkv / hpt;   // decode tiles per (request, chunk)
 
   // ---- cascade prefix chunking
-  const int prefix_waves = env_int("FI_PREFIX_WAVES", kPrefixMaxWaves) == 4 ? 4 : 8;
+  const int prefix_waves = tune_or(in.tune.prefix_waves, kPrefixMaxWaves) == 4 ? 4 : 8;
   const int64_t prefix_rows = (int64_t)prefix_rows_per_wave(in.D) * prefix_waves;
   int64_t prefix_chunk = 0;
   std::vector<std::vector<int64_t>> n_pchunks(NL);   // [level][group] chunks
@@ -457,10 +468,11 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
       Lpmax = std::max(Lpmax, plens[l][g]);
     }
   if (prefix_row_tiles > 0) {
-    const int64_t want = std::max<int64_t>(1, (int64_t)num_cus * env_int("FI_PREFIX_TILES_PER_CU", 1));
+    const int64_t want =
+        std::max<int64_t>(1, (int64_t)num_cus * std::max(1, tune_or(in.tune.prefix_tiles_per_cu, 1)));
     int64_t n_split = std::max<int64_t>(1, ceil_div(want, prefix_row_tiles));
     prefix_chunk = round_up(ceil_div(Lpmax, n_split), kBlockTokens);
-    prefix_chunk = std::max<int64_t>(prefix_chunk, env_int("FI_PREFIX_CHUNK_MIN", 256));
+    prefix_chunk = std::max<int64_t>(prefix_chunk, tune_or(in.tune.prefix_chunk_min, 256));
     prefix_chunk = round_up(prefix_chunk, kBlockTokens);
     // a prefix tile stages its chunk's page indices in LDS (<= 4096 + 2)
     prefix_chunk = std::min<int64_t>(prefix_chunk, kPrefixMaxChunk);
@@ -484,7 +496,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   // A request with prefix states and a suffix that is one decode chunk is
   // "folded": its decode tile reads the prefix states and writes the final
   // output, so only the prefix states need slots and no merge unit is made
-  // (FI_CASCADE_FOLD=0 sends every such request through the merge kernel).
+  // (tune.cascade_fold = -1 sends every such request through the merge kernel).
   std::vector<int64_t> n_dchunks(B);
   std::vector<char> folded(B, 0);
   for (int r = 0; r < B; ++r) n_dchunks[r] = lens[r] > 0 ? ceil_div(lens[r], chunk) : 0;
@@ -576,6 +588,18 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
     }
   }
   out->level_tile_off[NL] = (int64_t)pt.size();
+  // bf16 K/V: a level whose shortest prefix has fewer than kSplitPKeys keys
+  // runs the prefix instance that passes p to P.V with a residual
+  out->prefix_split_p = 0;
+  for (int l = 0; l < NL && in.q_dtype == 1 && in.kv_dtype == 1; ++l) {
+    int64_t shortest = -1;
+    for (int g = 0; g < in.levels[l].num_groups; ++g)
+      if (plens[l][g] > 0 && in.levels[l].qo_indptr[g + 1] > in.levels[l].qo_indptr[g])
+        shortest = shortest < 0 ? plens[l][g] : std::min(shortest, plens[l][g]);
+    const bool split = in.tune.prefix_split_p > 0 ||
+                       (in.tune.prefix_split_p == 0 && shortest >= 0 && shortest < kSplitPKeys);
+    if (split) out->prefix_split_p |= 1u << l;
+  }
   out->qo_indptr = (int32_t*)malloc(sizeof(int32_t) * (size_t)std::max(qo_entries, 1));
   out->state_off = (int32_t*)malloc(sizeof(int32_t) * state_off.size());
   if (!out->qo_indptr || !out->state_off) PLAN_FAIL(1, "out of host memory");
@@ -608,6 +632,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   }
   out->num_folded = 0;
   for (int r = 0; r < B; ++r) out->num_folded += folded[r] ? 1 : 0;
+  out->decode_depth = in.tune.decode_depth;
   out->num_req_info = B;
   out->qo_len = std::max(qo_entries, 1);
   out->ragged = in.ragged;

@@ -60,8 +60,9 @@ def is_hnd(w):
     return bool(w.meta.get("hnd"))
 
 
-def make_plan(w, chunk_tokens=0, cascade=None, rope=None):
-    """rope = None or (theta, scale): a plan with LLaMA-style RoPE."""
+def make_plan(w, chunk_tokens=0, cascade=None, rope=None, tuning=None):
+    """rope = None or (theta, scale): a plan with LLaMA-style RoPE.  tuning:
+    optional dict of fi_tuning fields."""
     import paged_kv_decode_fi_amd as fi
     cascade = (w.prefix_kv_indptr is not None) if cascade is None else cascade
     prefix = ((w.prefix_qo_indptr, w.prefix_kv_indptr, w.prefix_last_page_len)
@@ -74,14 +75,14 @@ def make_plan(w, chunk_tokens=0, cascade=None, rope=None):
                    rope_theta=0.0 if rope is None else rope[0],
                    rope_scale=0.0 if rope is None else rope[1],
                    kv_layout="ragged" if is_ragged(w) else
-                   "paged_hnd" if is_hnd(w) else "paged")
+                   "paged_hnd" if is_hnd(w) else "paged", tuning=tuning)
 
 
-def run_gpu(w, d=None, plan=None, chunk_tokens=0, rope=None):
+def run_gpu(w, d=None, plan=None, chunk_tokens=0, rope=None, tuning=None):
     """Runs the HIP path; returns (o float64 numpy, lse float64 numpy, plan)."""
     torch = torch_mod()
     d = d or Dev(w)
-    plan = plan or make_plan(w, chunk_tokens, rope=rope)
+    plan = plan or make_plan(w, chunk_tokens, rope=rope, tuning=tuning)
     if plan.cascade:
         o, lse = plan.cascade_run(d.q, d.k, d.v, d.p_indptr, d.p_indices, d.p_last,
                                   d.indptr, d.indices, d.last, d.k_scale, d.v_scale,

@@ -470,3 +470,38 @@ def test_multilevel_cascade_plan(fi):
     with pytest.raises(fi.FiError):
         fi.debug_plan_tiles(ip, la, num_qo_heads=Hkv * G, num_kv_heads=Hkv, page_size=ps,
                             levels=[levels[0]] * 9)
+
+
+def test_tuning_is_explicit_and_environment_is_ignored(fi, monkeypatch):
+    """Plans depend on fi_problem.tuning only: the library reads no
+    environment variable, a zero field is the default, and a forced value
+    changes the cut of the work (never its coverage)."""
+    rng = np.random.default_rng(5)
+    lens = rng.integers(1, 3000, size=24)
+    npg = (lens + 15) // 16
+    indptr = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
+    last = (lens - (npg - 1) * 16).astype(np.int32)
+    kw = dict(num_qo_heads=32, num_kv_heads=8, page_size=16)
+    base = fi.debug_plan_tiles(indptr, last, **kw)
+    for name in ("FI_HEADS_PER_TILE", "FI_WAVES_PER_CU", "FI_CHUNK_MIN", "FI_DECODE_DEPTH",
+                 "FI_CASCADE_FOLD", "FI_PREFIX_WAVES"):
+        monkeypatch.setenv(name, "1")
+    assert np.array_equal(fi.debug_plan_tiles(indptr, last, **kw), base)
+    zero = fi.debug_plan_tiles(indptr, last, tuning={f: 0 for f in fi.TUNING_FIELDS}, **kw)
+    assert np.array_equal(zero, base)
+    two = fi.debug_plan_tiles(indptr, last, tuning=dict(heads_per_tile=2), **kw)
+    assert set(np.unique(two[:, 1] % 2)) == {0} and len(two) > len(base)
+    # every (request, kv head, token) is still covered exactly once
+    cover = {}
+    for r, h0, t0, t1 in two[:, :4]:
+        for h in range(h0, h0 + 2):
+            cover[(r, h)] = cover.get((r, h), 0) + (t1 - t0)
+    assert all(cover[(r, h)] == lens[r] for r in range(24) for h in range(8))
+    with pytest.raises(fi.FiError):
+        fi.debug_plan_tiles(indptr, last, tuning=dict(decode_depth=3), **kw)
+    with pytest.raises(fi.FiError):
+        fi.debug_plan_tiles(indptr, last, tuning=dict(chunk_min=-16), **kw)
+    with pytest.raises(fi.FiError):
+        fi.debug_plan_tiles(indptr, last, tuning=dict(cascade_fold=2), **kw)
+    with pytest.raises(ValueError):
+        fi.debug_plan_tiles(indptr, last, tuning=dict(no_such_knob=1), **kw)

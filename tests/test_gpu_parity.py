@@ -248,19 +248,19 @@ def test_merge_of_many_states_single_request(fi):
 
 @pytest.mark.parametrize("kv", ["bf16", "e4m3"])
 @pytest.mark.parametrize("fold", ["1", "0"])
-def test_cascade_fold_and_merge_paths(fi, kv, fold, monkeypatch):
+def test_cascade_fold_and_merge_paths(fi, kv, fold):
     """Three prefix groups (one with an empty prefix) and suffixes shorter and
     longer than the chunk: one-chunk suffixes fold their prefix states in the
     decode tile (fold on), the rest go through the merge kernel; with the
     fold off every request is merged.  e4m3 KV exercises the v_scale of the
     folded prefix states."""
-    monkeypatch.setenv("FI_CASCADE_FOLD", fold)
     rng = np.random.default_rng(11)
     lens = rng.integers(0, 200, size=11)
     lens[3] = 0
     w = W.build("cascade_mix", lens, Hq=32, Hkv=4, ps=16, q_dtype="bf16", kv_dtype=kv,
                 seed=21, prefix_groups=[(4, 700), (3, 0), (4, 333)])
-    o, lse, plan = C.run_gpu(w, chunk_tokens=64)
+    o, lse, plan = C.run_gpu(w, chunk_tokens=64,
+                             tuning=dict(cascade_fold=1 if fold == "1" else -1))
     st = plan.stats
     if fold == "1":
         assert st["num_folded"] > 0 and st["num_merge_units"] > 0
