@@ -312,6 +312,32 @@ fi_status fi_append_run(fi_plan_t plan, const void* q, const void* k_pages,
                         const float* k_scale, const float* v_scale, float sm_scale,
                         void* o, float* lse, void* stream);
 
+/* Plain batch decode for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): fi_plan + fi_decode_run in one call, with no workspace.  The
+ * work list, merge map and fp32 partial states live in a static device
+ * array of the library (32 MiB per GPU, held until the process ends); the
+ * call allocates nothing -- no hipMalloc, no pinned or other host buffer --
+ * and copies nothing from the host: a planner kernel derives the work list
+ * from the device tables.
+ * problem:  as for fi_plan (its host kv_indptr / last_page_len decide the
+ *           split; the device copies must describe the same table); plain
+ *           decode only -- no cascade level, append or RoPE
+ *           (FI_ERR_UNSUPPORTED).  chunk_tokens 0 picks fi_plan's split, or
+ *           longer chunks when its partial states would not fit the static
+ *           array; a forced chunk_tokens whose states do not fit, or a batch
+ *           whose work list alone does not, is FI_ERR_INVALID_ARG with the
+ *           bytes needed in fi_last_error(), before anything is enqueued.
+ * Other arguments as fi_decode_run.  Enqueues 2-3 kernels on stream
+ * (planner, decode, merge when some request is split); capturable.  Every
+ * call on one GPU shares that GPU's array: calls that overlap on a GPU (two
+ * streams or threads) race and must be serialised by the caller. */
+fi_status fi_decode_noalloc(const fi_problem* problem, const void* q, const void* k_pages,
+                           const void* v_pages, const int32_t* kv_indptr,
+                           const int32_t* kv_indices, const int32_t* last_page_len,
+                           const float* k_scale, const float* v_scale, float sm_scale,
+                           void* o, float* lse, void* stream);
+
 /* Merge of attention states computed over DISJOINT key sets of the same
  * query rows (the split-KV / cascade recombination): with
  * M = max_i s_i, s = M + ln sum_i exp(s_i - M), v = sum_i exp(s_i - s) * v_i;

@@ -27,7 +27,7 @@ EXPORTS = ("fi_plan", "fi_plan_destroy", "fi_plan_get_stats", "fi_decode_run",
            "fi_cascade_decode", "fi_merge_states", "fi_status_string",
            "fi_last_error", "fi_debug_plan_tiles", "fi_debug_gather",
            "fi_debug_stream_read", "fi_debug_run_stage", "fi_append_run",
-           "fi_cascade_decode_levels", "fi_debug_record_walk")
+           "fi_cascade_decode_levels", "fi_debug_record_walk", "fi_decode_noalloc")
 
 
 class FiError(RuntimeError):
@@ -108,6 +108,8 @@ def _load() -> ctypes.CDLL:
     L.fi_cascade_decode.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, F, P, P, P]
     L.fi_debug_run_stage.restype = ctypes.c_int
     L.fi_debug_run_stage.argtypes = [P, I32, P, P, P, P, P, P, P, P, P, P, P, F, P, P, P]
+    L.fi_decode_noalloc.restype = ctypes.c_int
+    L.fi_decode_noalloc.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, F, P, P, P]
     L.fi_debug_record_walk.restype = ctypes.c_int
     L.fi_debug_record_walk.argtypes = [P, I32, P, P, P, P, P, P, P, P, P, P, P, F, P, P, P, P,
                                        P]
@@ -487,6 +489,36 @@ class Plan:
             self.destroy()
         except Exception:
             pass
+
+
+def decode_noalloc(q, k_pages, v_pages, kv_indptr, kv_indices, last_page_len, *,
+                   kv_indptr_host, last_page_len_host, num_qo_heads, num_kv_heads,
+                   page_size, head_dim=128, q_dtype="f16", kv_dtype="f16", k_scale=None,
+                   v_scale=None, sm_scale: float = 0.0, chunk_tokens=0, kv_layout="paged",
+                   tuning=None, o=None, lse=None, stream=None):
+    """Plain decode through fi_decode_noalloc (no workspace: the work list and
+    partial states live in the library's static device array).  Host copies
+    of kv_indptr / last_page_len decide the split; the device tables are
+    read by the kernels.  Returns (o, lse)."""
+    import torch
+    indptr, last = _host_i32(kv_indptr_host), _host_i32(last_page_len_host)
+    batch = len(indptr) - 1
+    pr, keep = _problem(batch, num_qo_heads, num_kv_heads, head_dim, page_size, q_dtype,
+                        kv_dtype, indptr, last, None, chunk_tokens, kv_layout=kv_layout,
+                        tuning=tuning)
+    want = {"f16": torch.float16, "bf16": torch.bfloat16}[q_dtype]
+    if q.dtype != want or tuple(q.shape) != (batch, num_qo_heads, head_dim):
+        raise ValueError(f"q must be {want} [{batch}, {num_qo_heads}, {head_dim}]")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((batch, num_qo_heads), dtype=torch.float32, device=q.device)
+    _check(_get_lib().fi_decode_noalloc(
+        ctypes.byref(pr), _ptr(q, "q"), _ptr(k_pages, "k_pages"), _ptr(v_pages, "v_pages"),
+        *_tables(kv_indptr, kv_indices, last_page_len), *_scales(k_scale, v_scale),
+        float(sm_scale), _ptr(o, "o"), _ptr(lse, "lse", torch.float32), _stream(stream)))
+    del keep
+    return o, lse
 
 
 def merge_states(v_states: Sequence, s_states: Sequence, out_dtype=None, v_out=None,

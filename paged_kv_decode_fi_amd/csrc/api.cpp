@@ -35,6 +35,12 @@ hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, in
                               hipStream_t s);
 hipError_t launch_rope_table(void* table, int rows, int head_dim, float theta, float scale,
                              hipStream_t s);
+size_t scratch_capacity();
+hipError_t scratch_address(void** out);
+hipError_t launch_device_plan(const int32_t* kv_indptr, const int32_t* last_page_len,
+                              int batch, int page_size, int chunk, int heads_per_tile, int Hkv,
+                              void* tiles, void* req_info, void* units, int64_t tile_cap,
+                              int64_t unit_cap, hipStream_t s);
 }  // namespace fi
 
 struct fi_plan_s {
@@ -700,6 +706,49 @@ fi_status fi_debug_record_walk(fi_plan_t plan, int32_t stage, const void* q,
   return enqueue_run(plan, stage == 0 ? kStageDecode : kStagePrefix, q, k_pages, v_pages, lv,
                      kv_indptr, kv_indices, k_scale, v_scale, sm_scale, o, lse,
                      reinterpret_cast<hipStream_t>(stream), rec, rec_base);
+}
+
+fi_status fi_decode_noalloc(const fi_problem* problem, const void* q, const void* k_pages,
+                           const void* v_pages, const int32_t* kv_indptr,
+                           const int32_t* kv_indices, const int32_t* last_page_len,
+                           const float* k_scale, const float* v_scale, float sm_scale, void* o,
+                           float* lse, void* stream) {
+  g_last_error.clear();
+  if (!problem) return fail(FI_ERR_INVALID_ARG, "problem is NULL");
+  fi_status st = check_dtypes(problem->q_dtype, problem->kv_dtype);
+  if (st != FI_OK) return st;
+  // sizes first (host only): nothing touches the device before they pass
+  int num_cus = 0, dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess)
+    e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "querying the compute unit count");
+  fi_plan_s pl;   // on the stack: the plan's sizes, its work list in scratch
+  char err[320] = {0};
+  const int rc = fi::plan_decode_static(to_input(problem, num_cus), fi::scratch_capacity(),
+                                        &pl.hp, err, sizeof(err));
+  if (rc != 0) return fail(rc == 2 ? FI_ERR_UNSUPPORTED : FI_ERR_INVALID_ARG, "%s", err);
+  const fi::HostPlan& hp = pl.hp;
+  if (hp.batch == 0) return FI_OK;
+  const LevelTables none;
+  st = check_run_args(hp, q, k_pages, v_pages, none, kv_indptr, kv_indices, last_page_len,
+                      sm_scale, o);
+  if (st != FI_OK) return st;
+  void* base = nullptr;
+  e = fi::scratch_address(&base);
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress (static scratch)");
+  pl.workspace = reinterpret_cast<char*>(base);
+  pl.workspace_bytes = fi::scratch_capacity();
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  e = fi::launch_device_plan(kv_indptr, hp.ragged ? nullptr : last_page_len, hp.batch,
+                             hp.page_size, hp.chunk_tokens, hp.heads_per_tile, hp.Hkv,
+                             pl.workspace + hp.layout.tiles_off,
+                             pl.workspace + hp.layout.req_info_off,
+                             pl.workspace + hp.layout.merge_reqs_off, hp.num_tiles,
+                             hp.num_merge_units, hs);
+  if (e != hipSuccess) return hip_fail(e, "device planner launch");
+  return enqueue_run(&pl, kStageDecode | kStageMerge, q, k_pages, v_pages, none, kv_indptr,
+                     kv_indices, k_scale, v_scale, sm_scale, o, lse, hs);
 }
 
 fi_status fi_merge_states(int32_t num_states, const void* const* v_states,

@@ -169,6 +169,13 @@ struct PlanInput {
 };
 int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen);
 void plan_free(HostPlan* p);
+// Plain decode without host arrays or allocation: validates, picks the same
+// split as plan_build (longer chunks when the partial states would not fit
+// in max_bytes and chunk_tokens is 0) and fills the plan's sizes and a
+// layout of at most max_bytes; the work list itself is written on the device
+// (launch_device_plan).  tiles / req_info / merge_units stay NULL.
+int plan_decode_static(const PlanInput& in, size_t max_bytes, HostPlan* out, char* err,
+                       size_t errlen);
 
 // ---- kernel parameter blocks (passed by value) ----------------------------
 struct DecodeParams {

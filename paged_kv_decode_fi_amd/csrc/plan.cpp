@@ -62,6 +62,73 @@ int64_t table_len(const int32_t* indptr, const int32_t* last, int i, int ps) {
     return code;                             \
   } while (0)
 
+// Decode split policy: kv heads per tile and the chunk length, from the
+// requests' lengths len(r) (no allocation; also used by the allocation-free
+// entry point).
+//  * heads per tile: the largest of tune.heads_per_tile (default 8; 4 with
+//    RoPE, whose kernel holds 3 waves per SIMD: three 4-wave workgroups fill
+//    a CU where one 8-wave workgroup would leave a third of it idle), 4, 2, 1
+//    dividing Hkv; halved (down to 2) for small problems.
+//  * chunk: the smallest multiple of the 16-token step, at least chunk_min,
+//    whose waves stay within num_cus * waves_per_cu (one round of resident
+//    waves), or the longest request when that is already enough work.
+template <class LenFn>
+void decode_split(const PlanInput& in, int num_cus, bool rope, LenFn len, int* hpt_out,
+                  int64_t* chunk_out) {
+  const int B = in.batch, Hkv = in.Hkv;
+  const int hpt_default = rope ? kWavesPerTile / 2 : kWavesPerTile;
+  const bool hpt_forced = in.tune.heads_per_tile > 0;
+  int hpt = (int)std::min<int64_t>(kWavesPerTile,
+                                   std::max<int64_t>(1, tune_or(in.tune.heads_per_tile, hpt_default)));
+  // (head_dim 256 with RoPE: the step's K/V rows of 8 heads and the
+  // table rows exceed the LDS, so at most 4)
+  if (rope && in.D == 256) hpt = std::min(hpt, kWavesPerTile / 2);
+  while (hpt & (hpt - 1)) hpt &= hpt - 1;
+  while (Hkv % hpt) hpt >>= 1;
+  const int64_t waves_per_cu = std::max(1, tune_or(in.tune.waves_per_cu, 16));
+  const int64_t c_min = round_up(std::max(tune_or(in.tune.chunk_min, 32), kChunkAlign),
+                                 kChunkAlign);
+  if (!hpt_forced) {
+    // small problems (fewer than 4 tiles per CU even at the minimum chunk):
+    // fewer heads per tile, so more, smaller workgroups spread the latency
+    auto tiles_at_min = [&](int h) {
+      int64_t t = 0;
+      for (int r = 0; r < B; ++r) t += std::max<int64_t>(1, ceil_div(len(r), c_min));
+      return t * (Hkv / h);
+    };
+    while (hpt > 2 && tiles_at_min(hpt) < 4 * (int64_t)num_cus) hpt >>= 1;
+  }
+  const int64_t target_waves = std::max<int64_t>(1, num_cus * waves_per_cu);
+  int64_t Lmax = 0;
+  for (int r = 0; r < B; ++r) Lmax = std::max(Lmax, len(r));
+  auto waves_for = [&](int64_t c) {
+    int64_t w = 0;
+    for (int r = 0; r < B; ++r) w += std::max<int64_t>(1, ceil_div(len(r), c));
+    return w * Hkv;   // hpt waves per tile, Hkv / hpt tiles per chunk
+  };
+  int64_t chunk;
+  if (in.chunk_tokens > 0) {
+    chunk = in.chunk_tokens;
+  } else {
+    int64_t hi = std::max<int64_t>(round_up(std::max<int64_t>(Lmax, 1), kChunkAlign),
+                                   kChunkAlign);
+    int64_t lo = std::min(c_min, hi);
+    if (waves_for(hi) >= target_waves) {
+      chunk = hi;                       // enough work without splitting
+    } else {
+      // smallest c in [lo, hi] (multiple of the step) with waves(c) <= target
+      int64_t a = lo / kChunkAlign, b = hi / kChunkAlign;
+      while (a < b) {
+        int64_t mid = (a + b) / 2;
+        if (waves_for(mid * kChunkAlign) <= target_waves) b = mid; else a = mid + 1;
+      }
+      chunk = a * kChunkAlign;
+    }
+  }
+  *hpt_out = hpt;
+  *chunk_out = chunk;
+}
+
 int plan_append(const PlanInput& in, const std::vector<int64_t>& lens, int num_cus,
                 HostPlan* out, char* err, size_t errlen) {
   const int B = in.batch, Hkv = in.Hkv, G = in.Hq / in.Hkv;
@@ -267,8 +334,9 @@ int plan_append(const PlanInput& in, const std::vector<int64_t>& lens, int num_c
 
 }  // namespace
 
-int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
-  memset(out, 0, sizeof(*out));
+// Checks the dimensions, layout, tuning and the per-request table (no
+// allocation): 0 or an fi_status code with `err` filled.
+int check_problem(const PlanInput& in, char* err, size_t errlen) {
   const int B = in.batch, Hkv = in.Hkv, ps = in.page_size;
   if (B < 0) PLAN_FAIL(1, "batch must be >= 0 (got %d)", B);
   if (in.Hq <= 0 || Hkv <= 0 || in.Hq % Hkv != 0)
@@ -308,16 +376,29 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   // requests' first rows in K / V, anywhere
   if (B > 0 && !in.ragged && in.kv_indptr[0] != 0) PLAN_FAIL(1, "kv_indptr[0] must be 0");
   if (B > 0 && in.kv_indptr[0] < 0) PLAN_FAIL(1, "kv_indptr[0] must be >= 0");
-  std::vector<int64_t> lens(B);
   for (int r = 0; r < B; ++r) {
     if (in.kv_indptr[r + 1] < in.kv_indptr[r])
       PLAN_FAIL(1, "kv_indptr decreases at request %d", r);
     int64_t n = (int64_t)in.kv_indptr[r + 1] - in.kv_indptr[r];
     if (n > 0 && last_tab && (last_tab[r] < 1 || last_tab[r] > ps))
       PLAN_FAIL(1, "last_page_len[%d] = %d outside [1, %d]", r, last_tab[r], ps);
-    lens[r] = table_len(in.kv_indptr, last_tab, r, ps);
-    if (lens[r] > (int64_t)0x7fffffff - 64) PLAN_FAIL(1, "request %d too long", r);
+    if (table_len(in.kv_indptr, last_tab, r, ps) > (int64_t)0x7fffffff - 64)
+      PLAN_FAIL(1, "request %d too long", r);
   }
+  return 0;
+}
+
+int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
+  memset(out, 0, sizeof(*out));
+  const int B = in.batch, Hkv = in.Hkv, ps = in.page_size;
+  {
+    const int rc = check_problem(in, err, errlen);
+    if (rc) return rc;
+  }
+  const int G = in.Hq / Hkv;
+  const int32_t* last_tab = in.ragged ? nullptr : in.last_page_len;
+  std::vector<int64_t> lens(B);
+  for (int r = 0; r < B; ++r) lens[r] = table_len(in.kv_indptr, last_tab, r, ps);
   // ---- shared (cascade) levels, outermost first; each splits the requests
   // into groups of contiguous requests sharing a prefix table
   const int NL = in.num_levels;
@@ -376,60 +457,12 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
                in.rope_theta > 1e30f || in.rope_scale > 1e30f))
     PLAN_FAIL(1, "rope_theta and rope_scale must be finite");
 
-  // ---- decode chunk length
-  // heads per tile: the largest of tune.heads_per_tile (default 8; 4 with
-  // RoPE, whose kernel holds 3 waves per SIMD: three 4-wave workgroups fill
-  // a CU where one 8-wave workgroup would leave a third of it idle), 4, 2, 1
-  // dividing Hkv
-  const int hpt_default = rope ? kWavesPerTile / 2 : kWavesPerTile;
+  // ---- decode chunk length and heads per tile
   const bool hpt_forced = in.tune.heads_per_tile > 0;
-  int hpt = (int)std::min<int64_t>(kWavesPerTile,
-                                   std::max<int64_t>(1, tune_or(in.tune.heads_per_tile, hpt_default)));
-  // (head_dim 256 with RoPE: the step's K/V rows of 8 heads and the
-  // table rows exceed the LDS, so at most 4)
-  if (rope && in.D == 256) hpt = std::min(hpt, kWavesPerTile / 2);
-  while (hpt & (hpt - 1)) hpt &= hpt - 1;
-  while (Hkv % hpt) hpt >>= 1;
-  const int64_t waves_per_cu = std::max(1, tune_or(in.tune.waves_per_cu, 16));
-  const int64_t c_min = round_up(std::max(tune_or(in.tune.chunk_min, 32), kChunkAlign),
-                                 kChunkAlign);
-  if (!hpt_forced) {
-    // small problems (fewer than 4 tiles per CU even at the minimum chunk):
-    // fewer heads per tile, so more, smaller workgroups spread the latency
-    auto tiles_at_min = [&](int h) {
-      int64_t t = 0;
-      for (int r = 0; r < B; ++r) t += std::max<int64_t>(1, ceil_div(lens[r], c_min));
-      return t * (Hkv / h);
-    };
-    while (hpt > 2 && tiles_at_min(hpt) < 4 * (int64_t)num_cus) hpt >>= 1;
-  }
-  const int64_t target_waves = std::max<int64_t>(1, num_cus * waves_per_cu);
-  int64_t Lmax = 0;
+  int hpt;
+  int64_t chunk, Lmax = 0;
   for (int r = 0; r < B; ++r) Lmax = std::max(Lmax, lens[r]);
-  auto waves_for = [&](int64_t c) {
-    int64_t w = 0;
-    for (int r = 0; r < B; ++r) w += std::max<int64_t>(1, ceil_div(lens[r], c));
-    return w * Hkv;   // hpt waves per tile, Hkv / hpt tiles per chunk
-  };
-  int64_t chunk;
-  if (in.chunk_tokens > 0) {
-    chunk = in.chunk_tokens;
-  } else {
-    int64_t hi = std::max<int64_t>(round_up(std::max<int64_t>(Lmax, 1), kChunkAlign),
-                                   kChunkAlign);
-    int64_t lo = std::min(c_min, hi);
-    if (waves_for(hi) >= target_waves) {
-      chunk = hi;                       // enough work without splitting
-    } else {
-      // smallest c in [lo, hi] (multiple of the step) with waves(c) <= target
-      int64_t a = lo / kChunkAlign, b = hi / kChunkAlign;
-      while (a < b) {
-        int64_t mid = (a + b) / 2;
-        if (waves_for(mid * kChunkAlign) <= target_waves) b = mid; else a = mid + 1;
-      }
-      chunk = a * kChunkAlign;
-    }
-  }
+  decode_split(in, num_cus, rope, [&](int r) { return lens[r]; }, &hpt, &chunk);
   // Cascade: a request with prefix states whose suffix is one chunk folds
   // those states into its decode tile's output, so no merge pass is needed.
   // When every such suffix is short (<= tune.fold_max_suffix tokens, default
@@ -662,6 +695,94 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   L.rope_off = off;
   off = align256(off + (size_t)rope_row_bytes(in.D) * (size_t)out->rope_rows);
   L.total = off;
+  return 0;
+}
+
+int plan_decode_static(const PlanInput& in, size_t max_bytes, HostPlan* out, char* err,
+                       size_t errlen) {
+  memset(out, 0, sizeof(*out));
+  {
+    const int rc = check_problem(in, err, errlen);
+    if (rc) return rc;
+  }
+  if (in.num_levels != 0 || in.append_qo_indptr || in.pos_encoding != 0)
+    PLAN_FAIL(2, "the allocation-free entry point runs plain decode only (no cascade level, "
+                 "append or RoPE)");
+  const int B = in.batch, Hkv = in.Hkv, ps = in.page_size, G = in.Hq / in.Hkv;
+  const int num_cus = in.num_cus > 0 ? in.num_cus : 256;
+  const int32_t* last_tab = in.ragged ? nullptr : in.last_page_len;
+  auto len = [&](int r) { return table_len(in.kv_indptr, last_tab, r, ps); };
+  int hpt;
+  int64_t chunk;
+  decode_split(in, num_cus, false, len, &hpt, &chunk);
+  // the work list in scratch: tiles, request info, merge units, partial
+  // states (the same counts the device planner derives from the tables)
+  auto layout = [&](int64_t c, WorkspaceLayout* L, int64_t* tiles, int64_t* units,
+                    int64_t* slots, int32_t* max_states) {
+    *tiles = *units = *slots = 0;
+    *max_states = 0;
+    for (int r = 0; r < B; ++r) {
+      const int64_t nc = len(r) > 0 ? ceil_div(len(r), c) : 0;
+      *tiles += std::max<int64_t>(nc, 1) * (Hkv / hpt);
+      if (nc >= 2) {
+        *slots += nc * Hkv;
+        *units += 1;
+        *max_states = std::max<int32_t>(*max_states, (int32_t)nc);
+      }
+    }
+    size_t off = 0;
+    L->tiles_off = off;
+    off = align256(off + sizeof(Tile) * (size_t)*tiles);
+    L->req_info_off = off;
+    off = align256(off + sizeof(ReqInfo) * (size_t)std::max(B, 1));
+    L->merge_reqs_off = off;
+    off = align256(off + sizeof(MergeUnit) * (size_t)std::max<int64_t>(*units, 1));
+    L->qo_indptr_off = off;
+    L->state_off_off = off;
+    L->partial_o_off = off;
+    off = align256(off + sizeof(float) * (size_t)*slots * G * in.D);
+    L->partial_lse_off = off;
+    off = align256(off + sizeof(float) * (size_t)*slots * G);
+    L->rope_off = off;
+    L->total = off;
+  };
+  WorkspaceLayout L;
+  int64_t tiles, units, slots;
+  int32_t max_states;
+  layout(chunk, &L, &tiles, &units, &slots, &max_states);
+  if (L.total > max_bytes && in.chunk_tokens == 0) {
+    // fewer, longer chunks until the partial states fit (unsplit needs none)
+    int64_t Lmax = 16;
+    for (int r = 0; r < B; ++r) Lmax = std::max(Lmax, len(r));
+    while (L.total > max_bytes && chunk < Lmax) {
+      chunk = std::min<int64_t>(round_up(2 * chunk, kChunkAlign), round_up(Lmax, kChunkAlign));
+      layout(chunk, &L, &tiles, &units, &slots, &max_states);
+    }
+  }
+  if (L.total > max_bytes)
+    PLAN_FAIL(1, "the allocation-free entry point needs %zu bytes of device scratch for this "
+                 "batch (chunk %lld tokens); its static buffer holds %zu (use a larger "
+                 "chunk_tokens, a smaller batch, or fi_plan with a workspace)",
+              L.total, (long long)chunk, max_bytes);
+  if (slots > (int64_t)0x7fffffff / (G * in.D) || tiles > 0x7fffffff)
+    PLAN_FAIL(2, "too many tiles or partial states; raise chunk_tokens");
+  out->batch = B; out->Hq = in.Hq; out->Hkv = Hkv; out->D = in.D;
+  out->page_size = ps; out->G = G; out->q_dtype = in.q_dtype; out->kv_dtype = in.kv_dtype;
+  out->num_cus = num_cus;
+  out->chunk_tokens = (int32_t)chunk;
+  out->heads_per_tile = hpt;
+  out->prefix_waves = kPrefixMaxWaves;
+  out->num_tiles = tiles;
+  out->num_partials = slots;
+  out->num_merge_units = units;
+  out->merge_wide = units >= 128 && max_states <= 8;
+  out->num_req_info = B;
+  out->qo_len = 1;
+  out->ragged = in.ragged;
+  out->hnd = in.hnd;
+  out->decode_depth = in.tune.decode_depth;
+  for (int r = 0; r < B && !out->has_keys; ++r) out->has_keys = len(r) > 0;
+  out->layout = L;
   return 0;
 }
 
