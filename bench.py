@@ -2,23 +2,32 @@
 """Benchmark of paged decode attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--page-size 1|16] [--rope]
+                    [--page-size 1|16] [--rope] [--eager]
 
-NAME is one of the decode workloads (default batch64_gqa4) or an append
-workload (append_single_q128, append_batch16_q128: multi-token causal
-queries, timed the same way, roofline against MFMA peak).
+NAME is one of the decode workloads (default skewed128: 128 requests, 120
+lognormal lengths clipped to [64, 2048] plus 8 of 32,768 keys, 32 q / 8 kv
+heads, fp16, page size 16 -- the largest single-GPU workload stored in fp16)
+or an append workload (append_single_q128, append_batch16_q128: multi-token
+causal queries, timed the same way, roofline against MFMA peak).
 
 One step = one run stage of the decode path (page walk, K/V loads, scores,
-online softmax, P.V, finalize, split-KV merge) over one batch of the named
-synthetic workload, inputs already resident in HBM.  The plan stage (host)
-is timed separately: it is computed once per batch and reused by every
-layer.  K/V copies are rotated so that the working set exceeds the 256 MB
-Infinity Cache and the measured rate is HBM traffic.
+online softmax, P.V, finalize, split-KV merge; for a cascade workload also
+the shared-prefix kernel) over one batch of the named synthetic workload,
+inputs already resident in HBM.  The plan stage (host) is timed separately:
+it is computed once per batch and reused by every layer.  K/V copies are
+rotated so that the working set exceeds the 256 MB Infinity Cache and the
+measured rate is HBM traffic.  The K timed steps are one replay of a graph
+that captured them (--eager: K launches from the host), between two
+synchronisations; the graph is replayed twice more and the median of the
+three is reported beside it.
 
 Prints ONE JSON line (rank 0).  `value` is achieved KV GB/s of the whole
 step (valid tokens only, once per (token, kv head)); `roofline` reports the
-decode launch against the 8 TB/s HBM peak; `cpu_baseline` times the fp64
-oracle on the host on a bounded sample of the same workload.
+dominant kernel against its peak; `cpu_baseline` times the fp64 oracle on
+the host on a bounded sample of the same workload; `hot` is the same step
+on one resident copy (Infinity-Cache-resident where it fits), labelled as
+such; a cascade workload also reports the same keys decoded through flat
+page tables (`cascade_vs_flat`).
 """
 from __future__ import annotations
 
@@ -79,12 +88,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="batch64_gqa4")
+    ap.add_argument("--workload", default="skewed128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rotate", action="store_true",
                     help="time one resident copy (Infinity-Cache-hot), for context")
-    ap.add_argument("--graph", action="store_true",
-                    help="replay the K steps from one captured hipGraph")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the K timed steps from the host instead of replaying a "
+                         "captured graph")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--page-size", type=int, default=16, choices=(1, 16),
                     help="long32_fp8 only: run the page-size-1 or page-size-16 variant")
@@ -209,24 +219,42 @@ def main():
 
     K = args.steps
     stream = torch.cuda.current_stream()
-    # one event pair around the timed region (per-step events would insert
-    # GPU-side gaps between launches)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    graph = None
-    if args.graph:
-        s = torch.cuda.Stream()
-        s.wait_stream(stream)
-        with torch.cuda.stream(s):
-            step(0)
-        stream.wait_stream(s)
+
+    def capture(fn, n):
+        """A graph of n calls of fn(i) (warmed up on a side stream first)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            fn(0)
+        stream.wait_stream(side)
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(K):
-                step(i)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        torch.cuda.synchronize()
+        return g
+
+    def replay_ms(g, n, reps=3):
+        """Per-call times of `reps` replays of a graph of n calls (events on
+        the launch stream), and their median."""
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) / n)
+        return out, sorted(out)[len(out) // 2]
+
+    graph = None if args.eager else capture(step, K)
+    if graph is not None:
+        graph.replay()                  # the replay path's own first use
         torch.cuda.synchronize()
 
     # ---- timed region: exactly K steps between two synchronisations
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     ev0.record(stream)
@@ -238,9 +266,14 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_start
-    # GPU time per step on the launch stream (decode + merge launches)
+    # GPU time per step on the launch stream
     launch_ms = ev0.elapsed_time(ev1) / K
     ms_per_step = wall_s * 1e3 / K
+    replays = None
+    if graph is not None:
+        more, _ = replay_ms(graph, K, reps=2)
+        replays = [launch_ms] + more
+    median3_ms = sorted(replays)[1] if replays else None
 
     # ---- the dominant kernel (the decode kernel; for a cascade workload the
     # MFMA-bound prefix kernel) timed inside full steps: each step is replayed
@@ -375,6 +408,49 @@ def main():
                "sample": f"{n_units} of {units} (request, kv head) units of {w.name}, "
                          f"{sample_bytes / 1e6:.1f} MB of KV, {dt:.2f} s"}
 
+    # ---- the same step on ONE resident copy (no rotation): Infinity-Cache
+    # resident when the inputs fit its 256 MB, labelled as such
+    hot = None
+    if not args.eager:
+        nh = max(50, min(K, 200))
+        g_hot = capture(lambda i: step(0), nh)
+        hot_list, hot_ms = replay_ms(g_hot, nh)
+        del g_hot
+        hot = {"label": "one resident copy, MALL-hot where it fits (not HBM-bound)",
+               "ms_per_step": round(hot_ms, 5),
+               "kv_gbs": round(w.kv_bytes() / (hot_ms * 1e-3) / 1e9, 1),
+               "resident_bytes": int(pool_bytes + w.q.nbytes), "steps": nh}
+
+    # ---- cascade workloads: the same keys through flat page tables (the
+    # shared prefix re-read by every request), decode plan, same rotation
+    cascade_vs_flat = None
+    if cascade and not args.eager and not args.ragged:
+        fw = W.flatten_cascade(w)
+        fplan = fi.Plan(fw.kv_indptr, fw.last_page_len, num_qo_heads=w.num_qo_heads,
+                        num_kv_heads=w.num_kv_heads, page_size=w.page_size,
+                        head_dim=w.head_dim, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
+                        **rope_extra)
+        ftab = [dict(indptr=dev(fw.kv_indptr), indices=dev(fw.kv_indices),
+                     last=dev(fw.last_page_len))]
+
+        def fstep(i):
+            c = copies[i % R]
+            fplan.run(c["q"], c["k"], c["v"], ftab[0]["indptr"], ftab[0]["indices"],
+                      ftab[0]["last"], c["ks"], c["vs"], sm_scale=w.sm_scale, o=c["o"],
+                      lse=c["lse"])
+
+        nf = 50
+        g_flat = capture(fstep, nf)
+        _, flat_ms = replay_ms(g_flat, nf)
+        del g_flat
+        fplan.destroy()
+        cascade_vs_flat = {"flat_ms_per_step": round(flat_ms, 5),
+                           "cascade_ms_per_step": round(median3_ms, 5),
+                           "speedup": round(flat_ms / median3_ms, 2),
+                           "flat_kv_bytes": int(w.kv_bytes(cascade=False)),
+                           "flat_kv_gbs": round(w.kv_bytes(cascade=False) /
+                                                (flat_ms * 1e-3) / 1e9, 1)}
+
     st = plan.stats
     out = {
         "metric": "paged decode attention achieved KV GB/s and % of MI355X HBM peak",
@@ -388,7 +464,7 @@ def main():
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "page_size": w.page_size, "q_dtype": w.q_dtype, "kv_dtype": w.kv_dtype,
                    "kv_len_total": int(w.kv_lens.sum()), "kv_bytes": kv_bytes,
-                   "rotated_copies": R, "graph": bool(args.graph),
+                   "rotated_copies": R, "graph": not args.eager,
                    "pos_encoding": "rope_llama" if args.rope else "none",
                    "kv_layout": ("ragged" if args.ragged else
                                  "paged_hnd" if args.hnd else "paged"),
@@ -398,12 +474,16 @@ def main():
         "pct_read_ceiling": None if ceiling is None else round(100 * value / ceiling, 2),
         "requests_per_s": round(w.batch / (ms_per_step * 1e-3), 1),
         "launch_ms": round(launch_ms, 5),
+        "graph_replays_ms_per_step": None if replays is None else [round(x, 5) for x in replays],
+        "median3_ms_per_step": None if median3_ms is None else round(median3_ms, 5),
         "plan_ms": round(plan_ms, 3), "plan_first_use_ms": round(plan_first_ms, 3),
         "first_use_ms": round(first_use_ms, 3),
         "plan": {k: st[k] for k in ("num_tiles", "num_prefix_tiles", "num_merge_units",
                                     "chunk_tokens", "prefix_chunk_tokens", "num_cus")},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "hot": hot,
+        "cascade_vs_flat": cascade_vs_flat,
     }
     print(json.dumps(out), flush=True)
     plan.destroy()

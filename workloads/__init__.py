@@ -488,3 +488,31 @@ def build_multilevel(name, kv_lens, levels, *, Hq, Hkv, D=128, ps=16, q_dtype="f
                  v_pages=vp, kv_indptr=ip, kv_indices=ix, last_page_len=last,
                  kv_lens=kv_lens.copy(), sm_scale=float(np.float32(1.0 / math.sqrt(D))),
                  k_scale=k_scale, v_scale=v_scale, meta={"levels": lv})
+
+
+def flatten_cascade(w: Paged) -> Paged:
+    """The same keys as one flat page table per request, with no cascade
+    level: request r's pages are its group's shared prefix pages followed by
+    its own (pages shared, not copied).  Needs whole-page prefixes (config 4's
+    8,192 = 512 x 16 tokens) so the concatenated table is contiguous."""
+    import copy
+    assert w.prefix_kv_indptr is not None
+    ps = w.page_size
+    assert np.all(w.prefix_lens % ps == 0), "prefix lengths must be whole pages"
+    grp = np.repeat(np.arange(len(w.prefix_qo_indptr) - 1), np.diff(w.prefix_qo_indptr))
+    tabs, last = [], np.zeros(w.batch, np.int32)
+    for r in range(w.batch):
+        g = grp[r]
+        pre = w.prefix_kv_indices[w.prefix_kv_indptr[g]:w.prefix_kv_indptr[g + 1]]
+        own = w.kv_indices[w.kv_indptr[r]:w.kv_indptr[r + 1]]
+        tabs.append(np.concatenate([pre, own]))
+        last[r] = w.last_page_len[r] if len(own) else (ps if len(pre) else 0)
+    f = copy.copy(w)
+    f.name = w.name + "_flat"
+    f.kv_indptr = np.concatenate([[0], np.cumsum([len(t) for t in tabs])]).astype(np.int32)
+    f.kv_indices = np.concatenate(tabs).astype(np.int32)
+    f.last_page_len = last
+    f.kv_lens = w.kv_lens + w.prefix_lens[grp]
+    f.prefix_qo_indptr = f.prefix_kv_indptr = f.prefix_kv_indices = None
+    f.prefix_last_page_len = f.prefix_lens = None
+    return f
