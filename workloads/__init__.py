@@ -165,7 +165,7 @@ def _scatter(pool, pages_of_req, L, ps, data):
 
 def build(name, kv_lens, *, Hq, Hkv, D=128, ps=16, q_dtype="f16", kv_dtype="f16",
           seed=0, pool_pages=None, pool_factor=1.25, prefix_len=None,
-          prefix_groups=None, extra_page_sizes=(), poison=True):
+          prefix_groups=None, extra_page_sizes=(), poison=True, tables_only=False):
     """General generator.
 
     kv_lens: per-request own token counts.  prefix_len: if given, one shared
@@ -173,6 +173,9 @@ def build(name, kv_lens, *, Hq, Hkv, D=128, ps=16, q_dtype="f16", kv_dtype="f16"
     groups of contiguous requests).  extra_page_sizes: also return the SAME
     logical data laid out with these page sizes (dict in .meta['variants']).
     Returns a Paged (or a dict of Paged by page size when extra sizes given).
+    tables_only: the same lengths and page tables without drawing any value
+    (q, k_pages, v_pages and the e4m3 scales are None; meta['pool_pages']
+    holds the pool size) -- for checking a workload's structure cheaply.
     """
     rng = np.random.default_rng(seed)
     kv_lens = np.asarray(kv_lens, np.int64)
@@ -184,9 +187,11 @@ def build(name, kv_lens, *, Hq, Hkv, D=128, ps=16, q_dtype="f16", kv_dtype="f16"
         groups = [(B, int(prefix_len))]
     assert sum(g[0] for g in groups) in (0, B)
     seeds = np.random.SeedSequence(seed).spawn(4 + 2 * (B + len(groups)))
-    q_rng = np.random.default_rng(seeds[0])
-    qf = q_rng.standard_normal((B, Hq, D), dtype=np.float32)
-    q_bits = cast_bits(qf, q_dtype)
+    q_bits = None
+    if not tables_only:
+        q_rng = np.random.default_rng(seeds[0])
+        qf = q_rng.standard_normal((B, Hq, D), dtype=np.float32)
+        q_bits = cast_bits(qf, q_dtype)
 
     # logical rows of each key list: groups' prefixes first, then requests
     lists = [("p", g, int(glen)) for g, (_, glen) in enumerate(groups)]
@@ -200,7 +205,7 @@ def build(name, kv_lens, *, Hq, Hkv, D=128, ps=16, q_dtype="f16", kv_dtype="f16"
         return r.standard_normal((lst[2], Hkv, D), dtype=np.float32)
 
     k_scale = v_scale = None
-    if kv_dtype == "e4m3":
+    if kv_dtype == "e4m3" and not tables_only:
         amax_k = np.zeros(Hkv, np.float32)
         amax_v = np.zeros(Hkv, np.float32)
         for lst in lists:
@@ -237,13 +242,13 @@ def build(name, kv_lens, *, Hq, Hkv, D=128, ps=16, q_dtype="f16", kv_dtype="f16"
         fill = NAN_BITS[kv_dtype] if poison else 0
         variants[ps_i] = dict(
             n_req=n_req, last_req=last_req, n_pre=n_pre, last_pre=last_pre,
-            pre_pages=pre_pages, req_pages=req_pages,
-            kp=np.full((P, ps_i, Hkv, D), fill, st),
-            vp=np.full((P, ps_i, Hkv, D), fill, st))
+            pre_pages=pre_pages, req_pages=req_pages, P=P,
+            kp=None if tables_only else np.full((P, ps_i, Hkv, D), fill, st),
+            vp=None if tables_only else np.full((P, ps_i, Hkv, D), fill, st))
     # one pass over the logical key lists, scattered into every variant's pool
     for lst in lists:
         kind, idx, L = lst
-        if L == 0:
+        if L == 0 or tables_only:
             continue
         kd, vd = logical(lst, "k"), logical(lst, "v")
         if kv_dtype == "e4m3":
@@ -277,6 +282,7 @@ def build(name, kv_lens, *, Hq, Hkv, D=128, ps=16, q_dtype="f16", kv_dtype="f16"
                                    else np.zeros(0, np.int32)).astype(np.int32)
             w.prefix_last_page_len = V["last_pre"].astype(np.int32)
             w.prefix_lens = glens
+        w.meta["pool_pages"] = V["P"]
         out[ps_i] = w
     if extra_page_sizes:
         return out
@@ -308,7 +314,8 @@ WORKLOADS = ("single_L2048_h32", "batch64_gqa4", "skewed128", "cascade256",
              "long32_fp8")
 
 
-def make(name: str, seed: Optional[int] = None, small: bool = False, head_dim: int = 128):
+def make(name: str, seed: Optional[int] = None, small: bool = False, head_dim: int = 128,
+         tables_only: bool = False):
     """Named workload at full size, or a SMALL variant with the same structure
     (same heads, dtypes, page sizes, length mix shape; several tiles and a
     ragged tail) that the oracle finishes in seconds.  head_dim other than
@@ -322,28 +329,30 @@ def make(name: str, seed: Optional[int] = None, small: bool = False, head_dim: i
     if name == "single_L2048_h32":
         L = 300 if small else 2048
         return build(name, [L], Hq=32, Hkv=32, D=head_dim, ps=16, seed=seed,
-                     pool_pages=(40 if small else 256))
+                     pool_pages=(40 if small else 256), tables_only=tables_only)
     if name == "batch64_gqa4":
         B, lo, hi = (6, 1, 600) if small else (64, 512, 4096)
         lens = rng.integers(lo, hi + 1, size=B)
-        return build(name, lens, Hq=32, Hkv=8, D=head_dim, ps=16, seed=seed)
+        return build(name, lens, Hq=32, Hkv=8, D=head_dim, ps=16, seed=seed,
+                     tables_only=tables_only)
     if name == "skewed128":
         nshort, nlong, cl, ch, mu, Llong = ((10, 2, 8, 256, math.log(64), 2048) if small
                                             else (120, 8, 64, 2048, math.log(512), 32768))
         short = np.clip(np.round(rng.lognormal(mu, 0.5, size=nshort)), cl, ch).astype(np.int64)
         lens = np.concatenate([short, np.full(nlong, Llong, np.int64)])
         lens = lens[rng.permutation(len(lens))]
-        return build(name, lens, Hq=32, Hkv=8, D=head_dim, ps=16, seed=seed)
+        return build(name, lens, Hq=32, Hkv=8, D=head_dim, ps=16, seed=seed,
+                     tables_only=tables_only)
     if name == "cascade256":
         B, lo, hi, P = (8, 1, 100, 512) if small else (256, 128, 512, 8192)
         lens = rng.integers(lo, hi + 1, size=B)
         return build(name, lens, Hq=64, Hkv=8, D=head_dim, ps=16, q_dtype="bf16",
-                     kv_dtype="bf16", seed=seed, prefix_len=P)
+                     kv_dtype="bf16", seed=seed, prefix_len=P, tables_only=tables_only)
     if name == "long32_fp8":
         B, L = (3, 700) if small else (32, 32768)
         return build(name, np.full(B, L, np.int64), Hq=64, Hkv=8, D=head_dim, ps=16,
                      q_dtype="bf16", kv_dtype="e4m3", seed=seed,
-                     extra_page_sizes=(1,))
+                     extra_page_sizes=(1,), tables_only=tables_only)
     raise KeyError(name)
 
 
