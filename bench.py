@@ -105,6 +105,9 @@ def parse():
                     help="the same workload with head-major pages [P][Hkv][ps][D]")
     ap.add_argument("--head-dim", type=int, default=128, choices=(64, 128, 256),
                     help="the same workload at another head_dim")
+    ap.add_argument("--tuning", default="",
+                    help="plan tuning for measurement, e.g. prefix_waves=4,decode_depth=1 "
+                         "(fi_tuning fields; never changes what is computed)")
     ap.add_argument("--rope", action="store_true",
                     help="plain decode workloads: LLaMA-style RoPE on the fly "
                          "(theta 1e4, scale 1)")
@@ -175,6 +178,9 @@ def main():
     if append:
         rope_extra.update(qo_indptr=w.qo_indptr, causal=w.causal)
     rope_kw = dict(pos_encoding="rope_llama", rope_theta=1e4, rope_scale=1.0) if args.rope else {}
+    if args.tuning:
+        rope_kw["tuning"] = {k: int(v) for k, v in
+                             (kv.split("=") for kv in args.tuning.split(","))}
     traffic_key = (w.name + ("+rope" if args.rope else "") +
                    (f"+d{w.head_dim}" if w.head_dim != 128 else ""))
 
@@ -466,6 +472,7 @@ def main():
                    "kv_len_total": int(w.kv_lens.sum()), "kv_bytes": kv_bytes,
                    "rotated_copies": R, "graph": not args.eager,
                    "pos_encoding": "rope_llama" if args.rope else "none",
+                   **({"tuning": rope_kw["tuning"]} if args.tuning else {}),
                    "kv_layout": ("ragged" if args.ragged else
                                  "paged_hnd" if args.hnd else "paged"),
                    **({"query_tokens": w.num_rows, "causal": w.causal} if append else {})},
@@ -479,7 +486,8 @@ def main():
         "plan_ms": round(plan_ms, 3), "plan_first_use_ms": round(plan_first_ms, 3),
         "first_use_ms": round(first_use_ms, 3),
         "plan": {k: st[k] for k in ("num_tiles", "num_prefix_tiles", "num_merge_units",
-                                    "chunk_tokens", "prefix_chunk_tokens", "num_cus")},
+                                    "chunk_tokens", "prefix_chunk_tokens", "heads_per_tile",
+                                    "num_cus", "prefix_split_p", "rope_single")},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "hot": hot,

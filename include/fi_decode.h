@@ -122,6 +122,11 @@ typedef struct {
   int32_t prefix_split_p;       /* bf16 cascade prefix launches pass p to P.V
                                    with a bf16 residual: 0 = when a level has a
                                    prefix under 256 keys, 1 = always, -1 = never */
+  int32_t rope_split_k;         /* RoPE with fp16 q: a key turned by its distance
+                                   goes to the score as a high part plus a
+                                   residual: 0 = when some request has fewer
+                                   than 64 keys, 1 = always, -1 = never (one
+                                   fp16 value); bf16 q always splits */
 } fi_tuning;
 
 /* Problem description; every pointer here is HOST memory, read during the
@@ -216,6 +221,7 @@ typedef struct {
                                 bf16 residual */
   int32_t staging_buffers;   /* pinned upload buffers the library holds for
                                 all plans of the process (reused, not per plan) */
+  int32_t rope_single;       /* RoPE plan whose turned keys are one fp16 value */
 } fi_plan_stats;
 
 /* Plan stage (FlashInfer README "core features" item 2).

@@ -218,7 +218,8 @@ fi::PlanInput to_input(const fi_problem* p, int num_cus) {
     in.tune = fi::Tuning{t.heads_per_tile,   t.waves_per_cu,     t.chunk_min,
                          t.prefix_waves,     t.prefix_tiles_per_cu, t.prefix_chunk_min,
                          t.cascade_fold,     t.fold_max_suffix,  t.append_tiles_pct,
-                         t.append_chunk_min, t.decode_depth,     t.prefix_split_p};
+                         t.append_chunk_min, t.decode_depth,     t.prefix_split_p,
+                         t.rope_split_k};
   }
   return in;
 }
@@ -270,6 +271,7 @@ fi::DecodeParams base_params(const fi_plan_s* pl, const void* q, const void* k,
   if (hp.rope) {
     p.rope_table = pl->workspace + hp.layout.rope_off;
     p.rope_rows = hp.rope_rows;
+    p.rope_single = hp.rope_single;
   }
   p.ragged = hp.ragged;
   {
@@ -418,6 +420,7 @@ fi_status fi_plan_get_stats(fi_plan_t plan, fi_plan_stats* s) {
   s->workspace_bytes = hp.layout.total;
   s->num_folded = hp.num_folded;
   s->prefix_split_p = hp.prefix_split_p;
+  s->rope_single = hp.rope_single;
   s->staging_buffers = staging_count();
   return FI_OK;
 }

@@ -182,7 +182,7 @@ __device__ __forceinline__ uint32_t residual2(uint32_t h, float x0, float x1) {
 // f..f+7 in cs, in fp32; writes the result as a 16-bit high part plus a
 // 16-bit residual, so that two MFMAs against the same q carry the rotated
 // key to about fp32 accuracy.
-template <bool BF16>
+template <bool BF16, bool SPLIT>
 __device__ __forceinline__ void rope_key8(u32x4 a, u32x4 b, const float4* cs, u32x4& ahi,
                                           u32x4& alo, u32x4& bhi, u32x4& blo) {
 #pragma unroll
@@ -199,8 +199,10 @@ __device__ __forceinline__ void rope_key8(u32x4 a, u32x4 b, const float4* cs, u3
     }
     ahi[k] = pack2<BF16>(ra[0], ra[1]);
     bhi[k] = pack2<BF16>(rb[0], rb[1]);
-    alo[k] = residual2<BF16>(ahi[k], ra[0], ra[1]);
-    blo[k] = residual2<BF16>(bhi[k], rb[0], rb[1]);
+    if constexpr (SPLIT) {
+      alo[k] = residual2<BF16>(ahi[k], ra[0], ra[1]);
+      blo[k] = residual2<BF16>(bhi[k], rb[0], rb[1]);
+    }
   }
 }
 
@@ -226,8 +228,8 @@ hipError_t launch_rope_table(void* table, int rows, int head_dim, float theta, f
 
 // FOLD: the plan has tiles that fold earlier states into their output (a
 // separate instance: the fold costs registers the plain kernel keeps free).
-// DEPTH: steps of K/V loads in flight per workgroup.  ROPE: every key is
-// turned by its distance from the query (LLaMA-style RoPE, relative form)
+// DEPTH: steps of K/V loads in flight per workgroup.  ROPE (1, 2): every key
+// is turned by its distance from the query (LLaMA-style RoPE, relative form)
 // before the score MFMAs; the LDS after K and V holds the step's 16 rows
 // (padded: conflict-free reads of one row per lane) and table rows 0..15.
 template <int D>
@@ -241,7 +243,7 @@ struct RopeLds {
 // REC (a test instance): every K vector load also writes its byte offset in
 // the K pool to p.rec at ((rec_base[request] + token) * Hkv + kv head) * VR +
 // 16-byte chunk -- the page walk exactly as the loads take it.
-template <int KV, bool QBF16, bool PS_POW2, bool FOLD, int DEPTH, bool ROPE, int D,
+template <int KV, bool QBF16, bool PS_POW2, bool FOLD, int DEPTH, int ROPE, int D,
           bool REC = false>
 __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams p) {
   static_assert(!ROPE || !FOLD, "RoPE plans have no cascade level to fold");
@@ -419,11 +421,11 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
         const float4* cs =
             reinterpret_cast<const float4*>(rlds + n * RL::STRIDE + 256 * j + 64 * g);
         u32x4 ahi, alo, bhi, blo;
-        rope_key8<QBF16>(kop_of(j), kop_of(j + HALF), cs, ahi, alo, bhi, blo);
+        rope_key8<QBF16, ROPE == 1>(kop_of(j), kop_of(j + HALF), cs, ahi, alo, bhi, blo);
         sc = mma16x16x32<QBF16>(ahi, qop[j], sc);
-        sc = mma16x16x32<QBF16>(alo, qop[j], sc);
+        if constexpr (ROPE == 1) sc = mma16x16x32<QBF16>(alo, qop[j], sc);
         sc = mma16x16x32<QBF16>(bhi, qop[j + HALF], sc);
-        sc = mma16x16x32<QBF16>(blo, qop[j + HALF], sc);
+        if constexpr (ROPE == 1) sc = mma16x16x32<QBF16>(blo, qop[j + HALF], sc);
       }
     } else {
 #pragma unroll
@@ -951,7 +953,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 && D != 256 ? 2 : 1) void pr
 
 constexpr int kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
 
-template <int KV, bool QBF16, bool FOLD, int DEPTH, bool ROPE, int D>
+template <int KV, bool QBF16, bool FOLD, int DEPTH, int ROPE, int D>
 static hipError_t launch_decode_t(const DecodeParams& p, int num_tiles, int waves,
                                   hipStream_t s) {
   constexpr int rope_lds = ROPE ? RopeLds<D>::BYTES : 0;
@@ -986,30 +988,40 @@ static hipError_t launch_decode_t(const DecodeParams& p, int num_tiles, int wave
 // no faster for the plain workloads).  head_dim 256 keeps one step in
 // flight in both instances (its K/V registers of one step already take 64
 // VGPRs) and has no RoPE table.
+// RoPE plans: two steps of loads in flight at head_dim 128 unless the plan
+// forces one; one step at head_dim 64 (measured 8 % faster) and 256
+// (registers).
+template <int KV, bool QBF16, int ROPE, int D>
+static hipError_t launch_decode_rope(const DecodeParams& p, int num_tiles, int waves, int depth,
+                                     hipStream_t s) {
+  if constexpr (D == 128) {
+    if (depth != 1) return launch_decode_t<KV, QBF16, false, 2, ROPE, D>(p, num_tiles, waves, s);
+  }
+  return launch_decode_t<KV, QBF16, false, 1, ROPE, D>(p, num_tiles, waves, s);
+}
+
 template <int KV, bool QBF16, int D>
 static hipError_t launch_decode_f(const DecodeParams& p, int num_tiles, int waves, bool fold,
                                   int depth, hipStream_t s) {
   if (num_tiles <= 0) return hipSuccess;
-  if constexpr (D == 256) {
-    if (p.rope_table) return launch_decode_t<KV, QBF16, false, 1, true, D>(p, num_tiles, waves, s);
-    return fold ? launch_decode_t<KV, QBF16, true, 1, false, D>(p, num_tiles, waves, s)
-                : launch_decode_t<KV, QBF16, false, 1, false, D>(p, num_tiles, waves, s);
-  } else {
-    if (p.rope_table) {
-      // (RoPE at head_dim 64: one step in flight measured 8 % faster)
-      if constexpr (D == 64)
-        return launch_decode_t<KV, QBF16, false, 1, true, D>(p, num_tiles, waves, s);
-      else
-        return depth == 1
-                   ? launch_decode_t<KV, QBF16, false, 1, true, D>(p, num_tiles, waves, s)
-                   : launch_decode_t<KV, QBF16, false, 2, true, D>(p, num_tiles, waves, s);
+  if (p.rope_table) {
+    // the rotated key as one 16-bit value (fp16 q only) or a high part plus
+    // a residual
+    if constexpr (!QBF16) {
+      if (p.rope_single) return launch_decode_rope<KV, QBF16, 2, D>(p, num_tiles, waves, depth, s);
     }
+    return launch_decode_rope<KV, QBF16, 1, D>(p, num_tiles, waves, depth, s);
+  }
+  if constexpr (D == 256) {
+    return fold ? launch_decode_t<KV, QBF16, true, 1, 0, D>(p, num_tiles, waves, s)
+                : launch_decode_t<KV, QBF16, false, 1, 0, D>(p, num_tiles, waves, s);
+  } else {
     const bool deep = depth == 2 || (depth == 0 && fold && waves <= 4);
     if (fold)
-      return deep ? launch_decode_t<KV, QBF16, true, 2, false, D>(p, num_tiles, waves, s)
-                  : launch_decode_t<KV, QBF16, true, 1, false, D>(p, num_tiles, waves, s);
-    return deep ? launch_decode_t<KV, QBF16, false, 2, false, D>(p, num_tiles, waves, s)
-                : launch_decode_t<KV, QBF16, false, 1, false, D>(p, num_tiles, waves, s);
+      return deep ? launch_decode_t<KV, QBF16, true, 2, 0, D>(p, num_tiles, waves, s)
+                  : launch_decode_t<KV, QBF16, true, 1, 0, D>(p, num_tiles, waves, s);
+    return deep ? launch_decode_t<KV, QBF16, false, 2, 0, D>(p, num_tiles, waves, s)
+                : launch_decode_t<KV, QBF16, false, 1, 0, D>(p, num_tiles, waves, s);
   }
 }
 
@@ -1080,21 +1092,21 @@ static hipError_t launch_decode_rec_t(const DecodeParams& p, int num_tiles, int 
   static const hipError_t attr = [] {
     const int max_lds = Stage<KV, 128>::lds_bytes(kWavesPerTile);
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, true, false, DEPTH, false, 128, true>),
+        reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, true, false, DEPTH, 0, 128, true>),
         hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
     if (e == hipSuccess)
       e = hipFuncSetAttribute(
           reinterpret_cast<const void*>(
-              &decode_kernel<KV, QBF16, false, false, DEPTH, false, 128, true>),
+              &decode_kernel<KV, QBF16, false, false, DEPTH, 0, 128, true>),
           hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
     return e;
   }();
   if (attr != hipSuccess) return attr;
   if (p.ps_shift >= 0)
-    hipLaunchKernelGGL((decode_kernel<KV, QBF16, true, false, DEPTH, false, 128, true>),
+    hipLaunchKernelGGL((decode_kernel<KV, QBF16, true, false, DEPTH, 0, 128, true>),
                        dim3(num_tiles), dim3(64 * waves), lds, s, p);
   else
-    hipLaunchKernelGGL((decode_kernel<KV, QBF16, false, false, DEPTH, false, 128, true>),
+    hipLaunchKernelGGL((decode_kernel<KV, QBF16, false, false, DEPTH, 0, 128, true>),
                        dim3(num_tiles), dim3(64 * waves), lds, s, p);
   return hipGetLastError();
 }

@@ -24,6 +24,11 @@ constexpr int kMaxLevels = 8;            // shared cascade levels
 // comparable weight, nothing else in the row) that rounding alone can move
 // o past 2e-3 + 1e-2 |o|, so such prefixes take p with a bf16 residual
 constexpr int kSplitPKeys = 256;
+// RoPE with fp16 q: a key turned by its distance and rounded once to fp16
+// moves a score by ~2^-12 relative per element; over a single key that alone
+// reaches ~0.85e-3 in lse (CPU simulation, 8,000 rows), so plans whose
+// shortest request has fewer keys than this keep the turned key's residual
+constexpr int kRopeSingleKeys = 64;
 
 enum TileKind : int32_t { kDecodeTile = 0, kPrefixTile = 1, kAppendTile = 2 };
 
@@ -115,6 +120,7 @@ struct HostPlan {
   // plus a residual (bit l set: level l has a prefix chunk shorter than
   // kSplitPKeys keys)
   uint32_t prefix_split_p;
+  int32_t rope_single;  // RoPE, fp16 q: the turned key rounded once (no residual)
   int32_t rope;         // FI_POS_ROPE_LLAMA or 0
   int32_t rope_rows;    // positions in the RoPE table (longest request)
   float rope_theta, rope_scale;
@@ -140,6 +146,7 @@ struct Tuning {
   int32_t append_chunk_min;     // smallest append key chunk in tokens (128)
   int32_t decode_depth;         // steps of K/V loads in flight, 1 or 2 (per instance)
   int32_t prefix_split_p;       // bf16 cascade prefix: 1 always split p, -1 never
+  int32_t rope_split_k;         // RoPE, fp16 q: 1 always split the turned key, -1 never
 };
 
 // Builds the plan on the host.  Returns 0 or an fi_status code with `err`
@@ -200,6 +207,7 @@ struct DecodeParams {
   // RoPE plans: the (cos, sin) table, rope_rows x D / 2 fp32 pairs
   const void* rope_table;
   int32_t rope_rows;
+  int32_t rope_single;        // fp16 q: turned keys as one fp16 value
   // ragged KV: token t of a request is row kv_indptr[r] + t (page size 1,
   // kv_indices not read)
   int32_t ragged;

@@ -369,8 +369,8 @@ int check_problem(const PlanInput& in, char* err, size_t errlen) {
     if (tu.decode_depth < 0 || tu.decode_depth > 2)
       PLAN_FAIL(1, "tuning decode_depth must be 0 (automatic), 1 or 2");
     if (tu.cascade_fold < -1 || tu.cascade_fold > 1 || tu.prefix_split_p < -1 ||
-        tu.prefix_split_p > 1)
-      PLAN_FAIL(1, "tuning cascade_fold and prefix_split_p must be -1, 0 or 1");
+        tu.prefix_split_p > 1 || tu.rope_split_k < -1 || tu.rope_split_k > 1)
+      PLAN_FAIL(1, "tuning cascade_fold, prefix_split_p and rope_split_k must be -1, 0 or 1");
   }
   // paged tables index kv_indices from 0; a ragged table's entries are the
   // requests' first rows in K / V, anywhere
@@ -692,6 +692,15 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   out->rope_scale = in.rope_scale > 0.f ? in.rope_scale : 1.f;
   // distances 0 .. Lmax - 1, and at least the 16 rows every tile stages
   out->rope_rows = rope ? (int32_t)std::max<int64_t>(Lmax, kChunkAlign) : 0;
+  // fp16 q: the turned key as one fp16 value when every request is long
+  // enough for its rounding to stay well inside the lse bar
+  if (rope && in.q_dtype == 0) {
+    int64_t shortest = -1;
+    for (int r = 0; r < B; ++r)
+      if (lens[r] > 0) shortest = shortest < 0 ? lens[r] : std::min(shortest, lens[r]);
+    out->rope_single = in.tune.rope_split_k < 0 ||
+                       (in.tune.rope_split_k == 0 && shortest >= kRopeSingleKeys);
+  }
   L.rope_off = off;
   off = align256(off + (size_t)rope_row_bytes(in.D) * (size_t)out->rope_rows);
   L.total = off;
