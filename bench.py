@@ -487,7 +487,8 @@ def main():
         "first_use_ms": round(first_use_ms, 3),
         "plan": {k: st[k] for k in ("num_tiles", "num_prefix_tiles", "num_merge_units",
                                     "chunk_tokens", "prefix_chunk_tokens", "heads_per_tile",
-                                    "num_cus", "prefix_split_p", "rope_single")},
+                                    "num_cus", "prefix_split_p", "rope_single",
+                                    "valu_heads")},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "hot": hot,

@@ -127,6 +127,10 @@ typedef struct {
                                    residual: 0 = when some request has fewer
                                    than 64 keys, 1 = always, -1 = never (one
                                    fp16 value); bf16 q always splits */
+  int32_t score_path;           /* plain decode: 0 = automatic (MFMA), 1 = MFMA
+                                   for q.K^T and P.V, 2 = VALU dot products and
+                                   FMAs (head_dim 128, <= 4 q heads per kv
+                                   head; else FI_ERR_UNSUPPORTED) */
 } fi_tuning;
 
 /* Problem description; every pointer here is HOST memory, read during the
@@ -222,6 +226,7 @@ typedef struct {
   int32_t staging_buffers;   /* pinned upload buffers the library holds for
                                 all plans of the process (reused, not per plan) */
   int32_t rope_single;       /* RoPE plan whose turned keys are one fp16 value */
+  int32_t valu_heads;        /* > 0: plain decode on the VALU (no MFMA) kernel */
 } fi_plan_stats;
 
 /* Plan stage (FlashInfer README "core features" item 2).

@@ -44,7 +44,7 @@ class CascadeLevel(ctypes.Structure):
 TUNING_FIELDS = ("heads_per_tile", "waves_per_cu", "chunk_min", "prefix_waves",
                  "prefix_tiles_per_cu", "prefix_chunk_min", "cascade_fold", "fold_max_suffix",
                  "append_tiles_pct", "append_chunk_min", "decode_depth", "prefix_split_p",
-                 "rope_split_k")
+                 "rope_split_k", "score_path")
 
 
 class Tuning(ctypes.Structure):
@@ -75,7 +75,7 @@ class PlanStats(ctypes.Structure):
                 ("heads_per_tile", ctypes.c_int32), ("num_cus", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_size_t), ("num_folded", ctypes.c_int64),
                 ("prefix_split_p", ctypes.c_uint32), ("staging_buffers", ctypes.c_int32),
-                ("rope_single", ctypes.c_int32)]
+                ("rope_single", ctypes.c_int32), ("valu_heads", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}

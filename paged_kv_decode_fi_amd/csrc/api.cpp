@@ -219,7 +219,7 @@ fi::PlanInput to_input(const fi_problem* p, int num_cus) {
                          t.prefix_waves,     t.prefix_tiles_per_cu, t.prefix_chunk_min,
                          t.cascade_fold,     t.fold_max_suffix,  t.append_tiles_pct,
                          t.append_chunk_min, t.decode_depth,     t.prefix_split_p,
-                         t.rope_split_k};
+                         t.rope_split_k,     t.score_path};
   }
   return in;
 }
@@ -274,6 +274,7 @@ fi::DecodeParams base_params(const fi_plan_s* pl, const void* q, const void* k,
     p.rope_single = hp.rope_single;
   }
   p.ragged = hp.ragged;
+  p.valu_heads = hp.valu_heads;
   {
     const uint32_t rowb = (uint32_t)hp.D * (hp.kv_dtype == FI_E4M3 ? 1u : 2u);
     const uint32_t ps = (uint32_t)hp.page_size, hkv = (uint32_t)hp.Hkv;
@@ -421,6 +422,7 @@ fi_status fi_plan_get_stats(fi_plan_t plan, fi_plan_stats* s) {
   s->num_folded = hp.num_folded;
   s->prefix_split_p = hp.prefix_split_p;
   s->rope_single = hp.rope_single;
+  s->valu_heads = hp.valu_heads;
   s->staging_buffers = staging_count();
   return FI_OK;
 }

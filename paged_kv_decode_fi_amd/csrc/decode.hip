@@ -226,6 +226,18 @@ hipError_t launch_rope_table(void* table, int rows, int head_dim, float theta, f
   return hipGetLastError();
 }
 
+// Packed 16-bit dot product with fp32 accumulation: c + a.lo * b.lo +
+// a.hi * b.hi (v_dot2_f32_f16 / v_dot2_f32_bf16).
+template <bool BF16>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c,
+                                  false);
+}
+
 // FOLD: the plan has tiles that fold earlier states into their output (a
 // separate instance: the fold costs registers the plain kernel keeps free).
 // DEPTH: steps of K/V loads in flight per workgroup.  ROPE (1, 2): every key
@@ -243,10 +255,23 @@ struct RopeLds {
 // REC (a test instance): every K vector load also writes its byte offset in
 // the K pool to p.rec at ((rec_base[request] + token) * Hkv + kv head) * VR +
 // 16-byte chunk -- the page walk exactly as the loads take it.
+//
+// VG > 0 (the VALU instance, for up to VG q heads per kv head, plain plans):
+// no MFMA.  Lane (g, n) takes key n of the step and dims 32 s + 8 g .. +7
+// (the same LDS reads as the MFMA path); per q head j it accumulates packed
+// 16-bit dot products (v_dot2 with fp32 accumulation) and two cross-lane
+// sums give every lane the score of key n.  The softmax keeps the lazy
+// running max (the exact step max, over the 16 keys, only when some score
+// passes it by more than kLazyMax), and P.V runs as fp32 FMAs: lane i
+// accumulates dims D/64 i .. of each head, reading each key's p with
+// readlane and its V values from LDS.
 template <int KV, bool QBF16, bool PS_POW2, bool FOLD, int DEPTH, int ROPE, int D,
-          bool REC = false>
+          bool REC = false, int VG = 0>
 __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams p) {
   static_assert(!ROPE || !FOLD, "RoPE plans have no cascade level to fold");
+  static_assert(VG == 0 || (!ROPE && !FOLD), "the VALU instance serves plain plans");
+  constexpr int VGX = VG > 0 ? VG : 1;
+  constexpr int NV = D / 64;   // VALU instance: output dims per lane
   using S = Stage<KV, D>;
   using RL = RopeLds<D>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -272,7 +297,21 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
 
   // q of this wave's head group as the B operand of the score MFMAs
   u32x4 qop[D / 32];
-  {
+  // VALU instance: q head j, dims 32 s + 8 g .. +7 (every lane of group g)
+  u32x4 qv[VGX][D / 32];
+  if constexpr (VG > 0) {
+#pragma unroll
+    for (int jj = 0; jj < VG; ++jj) {
+      const bool ok = jj < G;
+      const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
+                             ((int64_t)r * p.Hq + h * G + (ok ? jj : 0)) * D;
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * g);
+        qv[jj][s] = ok ? v : u32x4{0, 0, 0, 0};
+      }
+    }
+  } else {
     const bool ok = n < G;
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
                            ((int64_t)r * p.Hq + h * G + (ok ? n : 0)) * D;
@@ -395,6 +434,16 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   f32x4 oacc[D / 16];
 #pragma unroll
   for (int b = 0; b < D / 16; ++b) oacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // VALU instance: running max (the same in every lane), this lane's key's
+  // share of the sum, and dims NV lane .. of each head's output
+  float mv[VGX], lv[VGX], ov[VGX][NV];
+#pragma unroll
+  for (int jj = 0; jj < VGX; ++jj) {
+    mv[jj] = -INFINITY;
+    lv[jj] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) ov[jj][i] = 0.f;
+  }
   // this lane's LDS addresses: K row of token n; V^T source row 4g + n/4 at
   // d-quad n % 4 (transpose-read layout)
   const uint8_t* krow = klds + n * KS + wave * S::ROWB;
@@ -427,6 +476,66 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
         sc = mma16x16x32<QBF16>(bhi, qop[j + HALF], sc);
         if constexpr (ROPE == 1) sc = mma16x16x32<QBF16>(blo, qop[j + HALF], sc);
       }
+    } else if constexpr (VG > 0) {
+      // ---- VALU instance: scores, softmax and P.V without MFMA
+      float acc[VG];
+#pragma unroll
+      for (int jj = 0; jj < VG; ++jj) acc[jj] = 0.f;
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        const u32x4 k = kop_of(s);
+#pragma unroll
+        for (int jj = 0; jj < VG; ++jj)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) acc[jj] = dot2<QBF16>(k[w], qv[jj][s][w], acc[jj]);
+      }
+      const bool valid = tb + n < t1;
+      float pv[VG];
+#pragma unroll
+      for (int jj = 0; jj < VG; ++jj) {
+        acc[jj] += __shfl_xor(acc[jj], 16);
+        acc[jj] += __shfl_xor(acc[jj], 32);
+        const float xj = valid ? acc[jj] * c : -INFINITY;
+        if (__any(xj > mv[jj] + kLazyMax)) {
+          float mx = xj;
+#pragma unroll
+          for (int o2 = 1; o2 < 16; o2 <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
+          const float alpha = fast_exp2(mv[jj] - mx);   // mv = -inf first: 0
+          lv[jj] *= alpha;
+#pragma unroll
+          for (int i = 0; i < NV; ++i) ov[jj][i] *= alpha;
+          mv[jj] = mx;
+        }
+        pv[jj] = fast_exp2(xj - mv[jj]);
+        lv[jj] += pv[jj];
+      }
+      // P.V: key t's p sits in lane t; V row t of this wave's head in LDS
+      const uint8_t* vrow = vlds + wave * (2 * D) + 2 * NV * lane;
+#pragma unroll
+      for (int t = 0; t < kStep; ++t) {
+        float v[NV];
+        if constexpr (NV == 1) {
+          v[0] = lo16<QBF16>(*reinterpret_cast<const uint16_t*>(vrow + t * VS));
+        } else if constexpr (NV == 2) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(vrow + t * VS);
+          v[0] = lo16<QBF16>(w);
+          v[1] = hi16<QBF16>(w);
+        } else {
+          const u32x2 w = *reinterpret_cast<const u32x2*>(vrow + t * VS);
+          v[0] = lo16<QBF16>(w.x);
+          v[1] = hi16<QBF16>(w.x);
+          v[2] = lo16<QBF16>(w.y);
+          v[3] = hi16<QBF16>(w.y);
+        }
+#pragma unroll
+        for (int jj = 0; jj < VG; ++jj) {
+          const float pt = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv[jj]), t));
+#pragma unroll
+          for (int i = 0; i < NV; ++i) ov[jj][i] = __builtin_fmaf(pt, v[i], ov[jj][i]);
+        }
+      }
+      return;
     } else {
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) sc = mma16x16x32<QBF16>(kop_of(s), qop[s], sc);
@@ -526,9 +635,43 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   }
 
   // ---- finalize
+  const float vs = (KV == kKvE4M3 && p.v_scale) ? p.v_scale[h] : 1.f;
+  if constexpr (VG > 0) {
+    // VALU instance: head j's sum over the 16 keys of the lane group, then
+    // dims NV lane .. of its output (final, or an fp32 partial state)
+#pragma unroll
+    for (int jj = 0; jj < VG; ++jj) {
+      if (jj >= G) break;
+      float lt = lv[jj];
+#pragma unroll
+      for (int o2 = 1; o2 < 16; o2 <<= 1) lt += __shfl_xor(lt, o2);
+      const float inv = (lt > 0.f ? 1.f / lt : 0.f) * vs;
+      const float lse2 = lt > 0.f ? mv[jj] + fast_log2(lt) : -INFINITY;
+      const int jq = h * G + jj;
+      if (tile.slot < 0) {
+        uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)r * p.Hq + jq) * D;
+        if constexpr (NV == 1) {
+          orow[lane] = (uint16_t)(pack2<QBF16>(ov[jj][0] * inv, 0.f) & 0xffffu);
+        } else if constexpr (NV == 2) {
+          reinterpret_cast<uint32_t*>(orow)[lane] = pack2<QBF16>(ov[jj][0] * inv, ov[jj][1] * inv);
+        } else {
+          reinterpret_cast<u32x2*>(orow)[lane] =
+              u32x2{pack2<QBF16>(ov[jj][0] * inv, ov[jj][1] * inv),
+                    pack2<QBF16>(ov[jj][2] * inv, ov[jj][3] * inv)};
+        }
+        if (lane == 0 && p.lse) p.lse[(int64_t)r * p.Hq + jq] = lse2 * kLn2;
+      } else {
+        const int64_t slot = tile.slot + wave;
+        float* po = p.partial_o + (slot * G + jj) * D + NV * lane;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) po[i] = ov[jj][i] * inv;
+        if (lane == 0) p.partial_lse[slot * G + jj] = lse2;
+      }
+    }
+    return;
+  }
   float lt = l + __shfl_xor(l, 16);
   lt += __shfl_xor(lt, 32);
-  const float vs = (KV == kKvE4M3 && p.v_scale) ? p.v_scale[h] : 1.f;
   const int j = h * G + n;
   if (tile.slot < 0) {
     // final output; a cascade request whose suffix is this one tile first
@@ -1000,10 +1143,55 @@ static hipError_t launch_decode_rope(const DecodeParams& p, int num_tiles, int w
   return launch_decode_t<KV, QBF16, false, 1, ROPE, D>(p, num_tiles, waves, s);
 }
 
+// VALU instances (plain plans, head_dim 128, one step of loads in flight):
+// vg = 1, 2 or 4 q heads per kv head at most.
+template <int KV, bool QBF16, int VG>
+static hipError_t launch_decode_valu_t(const DecodeParams& p, int num_tiles, int waves,
+                                       hipStream_t s) {
+  const size_t lds = (size_t)Stage<KV, 128>::lds_bytes(waves);
+  static const hipError_t attr = [] {
+    const int max_lds = Stage<KV, 128>::lds_bytes(kWavesPerTile);
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, true, false, 1, 0, 128, false, VG>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(
+              &decode_kernel<KV, QBF16, false, false, 1, 0, 128, false, VG>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+    return e;
+  }();
+  if (attr != hipSuccess) return attr;
+  if (p.ps_shift >= 0)
+    hipLaunchKernelGGL((decode_kernel<KV, QBF16, true, false, 1, 0, 128, false, VG>),
+                       dim3(num_tiles), dim3(64 * waves), lds, s, p);
+  else
+    hipLaunchKernelGGL((decode_kernel<KV, QBF16, false, false, 1, 0, 128, false, VG>),
+                       dim3(num_tiles), dim3(64 * waves), lds, s, p);
+  return hipGetLastError();
+}
+
+template <int KV, bool QBF16>
+static hipError_t launch_decode_valu(const DecodeParams& p, int num_tiles, int waves,
+                                     hipStream_t s) {
+  switch (p.valu_heads) {
+    case 1: return launch_decode_valu_t<KV, QBF16, 1>(p, num_tiles, waves, s);
+    case 2: return launch_decode_valu_t<KV, QBF16, 2>(p, num_tiles, waves, s);
+    case 4: return launch_decode_valu_t<KV, QBF16, 4>(p, num_tiles, waves, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int KV, bool QBF16, int D>
 static hipError_t launch_decode_f(const DecodeParams& p, int num_tiles, int waves, bool fold,
                                   int depth, hipStream_t s) {
   if (num_tiles <= 0) return hipSuccess;
+  if (p.valu_heads > 0) {
+    if constexpr (D == 128) {
+      if (!fold && !p.rope_table) return launch_decode_valu<KV, QBF16>(p, num_tiles, waves, s);
+    }
+    return hipErrorInvalidValue;
+  }
   if (p.rope_table) {
     // the rotated key as one 16-bit value (fp16 q only) or a high part plus
     // a residual

@@ -121,6 +121,8 @@ struct HostPlan {
   // kSplitPKeys keys)
   uint32_t prefix_split_p;
   int32_t rope_single;  // RoPE, fp16 q: the turned key rounded once (no residual)
+  int32_t valu_heads;   // plain decode on the VALU instance for this many q heads per
+                        // kv head (1, 2 or 4), 0 = MFMA
   int32_t rope;         // FI_POS_ROPE_LLAMA or 0
   int32_t rope_rows;    // positions in the RoPE table (longest request)
   float rope_theta, rope_scale;
@@ -147,6 +149,7 @@ struct Tuning {
   int32_t decode_depth;         // steps of K/V loads in flight, 1 or 2 (per instance)
   int32_t prefix_split_p;       // bf16 cascade prefix: 1 always split p, -1 never
   int32_t rope_split_k;         // RoPE, fp16 q: 1 always split the turned key, -1 never
+  int32_t score_path;           // plain decode: 1 MFMA scores and P.V, 2 VALU (G <= 4, D 128)
 };
 
 // Builds the plan on the host.  Returns 0 or an fi_status code with `err`
@@ -208,6 +211,7 @@ struct DecodeParams {
   const void* rope_table;
   int32_t rope_rows;
   int32_t rope_single;        // fp16 q: turned keys as one fp16 value
+  int32_t valu_heads;         // > 0: the VALU decode instance (q heads per kv head)
   // ragged KV: token t of a request is row kv_indptr[r] + t (page size 1,
   // kv_indices not read)
   int32_t ragged;

@@ -371,6 +371,8 @@ int check_problem(const PlanInput& in, char* err, size_t errlen) {
     if (tu.cascade_fold < -1 || tu.cascade_fold > 1 || tu.prefix_split_p < -1 ||
         tu.prefix_split_p > 1 || tu.rope_split_k < -1 || tu.rope_split_k > 1)
       PLAN_FAIL(1, "tuning cascade_fold, prefix_split_p and rope_split_k must be -1, 0 or 1");
+    if (tu.score_path < 0 || tu.score_path > 2)
+      PLAN_FAIL(1, "tuning score_path must be 0 (automatic), 1 (MFMA) or 2 (VALU)");
   }
   // paged tables index kv_indices from 0; a ragged table's entries are the
   // requests' first rows in K / V, anywhere
@@ -692,6 +694,13 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   out->rope_scale = in.rope_scale > 0.f ? in.rope_scale : 1.f;
   // distances 0 .. Lmax - 1, and at least the 16 rows every tile stages
   out->rope_rows = rope ? (int32_t)std::max<int64_t>(Lmax, kChunkAlign) : 0;
+  // score path of plain decode: MFMA (default) or the VALU instance
+  if (in.tune.score_path == 2) {
+    if (rope || NG > 0 || in.D != 128 || G > 4)
+      PLAN_FAIL(2, "the VALU score path serves plain decode at head_dim 128 with at most 4 "
+                   "q heads per kv head");
+    out->valu_heads = G == 1 ? 1 : G == 2 ? 2 : 4;
+  }
   // fp16 q: the turned key as one fp16 value when every request is long
   // enough for its rounding to stay well inside the lse bar
   if (rope && in.q_dtype == 0) {
