@@ -87,7 +87,12 @@ struct Stage {
   static constexpr int VR = ROWB / 16;                    // 16-B vectors per row
   static constexpr int LOADS = ROWB / 64;                 // vectors per thread per pool per step
   static constexpr int TOK_PER_U = 64 / VR;               // token advance per load index u
-  static __host__ __device__ constexpr int k_stride(int W) { return W * ROWB + 16; }
+  // K row stride in LDS: a 16-bit K row run padded by 32 bytes (SQ_LDS_BANK_CONFLICT
+  // reads 0 for the score operand reads at this stride, 12 % of LDS-active
+  // cycles at 16 bytes); e4m3 rows by 16 (32 measured more conflicts there)
+  static __host__ __device__ constexpr int k_stride(int W) {
+    return W * ROWB + (KV == kKvE4M3 ? 16 : 32);
+  }
   static __host__ __device__ constexpr int v_stride(int W) { return W * 2 * D + 32; }
   static __host__ __device__ constexpr int lds_bytes(int W) {
     return kStep * (k_stride(W) + v_stride(W));
@@ -745,7 +750,10 @@ constexpr float kPrefixLazySum = 256.f;
 template <int KV, int D>
 struct PStage {
   static constexpr int ROWB = KV == kKvE4M3 ? D : 2 * D;    // K row bytes kept in LDS
-  static constexpr int KS = ROWB + 16;                      // K LDS row stride
+  // K LDS row stride: 16-bit rows padded by 32 bytes (the score operand
+  // reads then show no bank conflict; at 16 bytes they took 28 % of the
+  // LDS-active cycles), e4m3 rows by 16
+  static constexpr int KS = ROWB + (KV == kKvE4M3 ? 16 : 32);
   static constexpr int VS = 2 * D + 32;                     // V LDS row stride (16-bit values)
   static constexpr int BUF = kPStep * (KS + VS);
   static constexpr int PTAB = kPrefixMaxChunk + 2;          // page-table slots (page_size 1)

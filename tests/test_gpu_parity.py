@@ -469,3 +469,39 @@ def test_all_requests_empty(fi, rope):
                       torch.zeros(3, dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+@pytest.mark.parametrize("L", [0, 1, 15, 16, 17, 300, 2048])
+@pytest.mark.parametrize("chunk", [0, 16, 48, 512])
+def test_one_request_plans(fi, L, chunk):
+    """Plans of one request at every length / chunk edge (empty, one key,
+    page and chunk boundaries, a single chunk) against the oracle."""
+    w = W.build("one_req", [L], Hq=32, Hkv=8, ps=16, seed=L + 3)
+    o, lse, plan = C.run_gpu(w, chunk_tokens=chunk)
+    ro, rl = C.run_oracle(w)
+    C.assert_parity(w, o, lse, ro, rl, label=f"one request L={L} chunk={chunk} {plan.stats}")
+    plan.destroy()
+
+
+def test_replan_loop_reuses_pinned_staging(fi):
+    """Re-planning every step (lengths change between decode steps) takes
+    its pinned upload buffer from the library's pool: after the first plans
+    the pool stops growing (at most 4 buffers per GPU), and every plan's
+    work list is the one its lengths ask for."""
+    import torch
+    base = W.make("batch64_gqa4", small=True)
+    counts = []
+    for i in range(40):
+        lens = base.kv_lens + (i % 7)
+        w = W.build("replan", lens, Hq=32, Hkv=8, ps=16, seed=1, tables_only=(i % 10 != 0))
+        plan = fi.Plan(w.kv_indptr, w.last_page_len, num_qo_heads=32, num_kv_heads=8,
+                       page_size=16, chunk_tokens=[0, 32, 64][i % 3])
+        counts.append(plan.stats["staging_buffers"])
+        if i % 10 == 0:
+            o, lse, _ = C.run_gpu(w, plan=plan)
+            ro, rl = C.run_oracle(w)
+            C.assert_parity(w, o, lse, ro, rl, label=f"replan {i}")
+        torch.cuda.synchronize()
+        plan.destroy()
+    assert max(counts) <= 4, counts
+    assert len(set(counts[5:])) == 1, counts

@@ -167,3 +167,15 @@ def test_record_hook_refuses_what_is_not_built(fi):
         _walk(fi, w, plan, 0)
     assert e.value.status == 2
     plan.destroy()
+
+
+@pytest.mark.parametrize("ps", [1, 7, 16])
+@pytest.mark.parametrize("chunk,hpt", [(0, 0), (32, 1), (48, 8), (1024, 2)])
+def test_decode_walk_one_request(fi, ps, chunk, hpt):
+    """One request split into chunks (the single-request decode shape): the
+    loads cover every key exactly as the page table says, at every chunk and
+    heads-per-tile cut."""
+    w = W.build("walk_one", [1337], Hq=32, Hkv=8, ps=ps, seed=70 + ps)
+    plan = C.make_plan(w, chunk_tokens=chunk, tuning=dict(heads_per_tile=hpt))
+    _walk(fi, w, plan, 0)
+    plan.destroy()
