@@ -126,7 +126,9 @@ typedef struct {
                                    goes to the score as a high part plus a
                                    residual: 0 = when some request has fewer
                                    than 64 keys, 1 = always, -1 = never (one
-                                   fp16 value); bf16 q always splits */
+                                   fp16 value, turned in packed fp16 against
+                                   an fp16 table); bf16 q, and tiles of fewer
+                                   than head_dim / 32 kv heads, always split */
   int32_t score_path;           /* plain decode: 0 = automatic (MFMA), 1 = MFMA
                                    for q.K^T and P.V, 2 = VALU dot products and
                                    FMAs (head_dim 128, <= 4 q heads per kv

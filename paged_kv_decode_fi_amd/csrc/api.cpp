@@ -34,7 +34,7 @@ hipError_t launch_gather(const int32_t* kv_indptr, const int32_t* kv_indices,
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int blocks,
                               hipStream_t s);
 hipError_t launch_rope_table(void* table, int rows, int head_dim, float theta, float scale,
-                             hipStream_t s);
+                             bool f16, hipStream_t s);
 size_t scratch_capacity();
 hipError_t scratch_address(void** out);
 hipError_t launch_device_plan(const int32_t* kv_indptr, const int32_t* last_page_len,
@@ -381,7 +381,8 @@ fi_status fi_plan(const fi_problem* problem, int32_t num_cus, void* workspace,
   const bool copied = e == hipSuccess;
   if (e == hipSuccess && hp.rope)   // the (cos, sin) table, built on the device
     e = fi::launch_rope_table(reinterpret_cast<char*>(workspace) + hp.layout.rope_off,
-                              hp.rope_rows, hp.D, hp.rope_theta, hp.rope_scale, hs);
+                              hp.rope_rows, hp.D, hp.rope_theta, hp.rope_scale,
+                              hp.rope_single != 0, hs);
   const hipError_t er = staging_release(sb, hs, copied);
   if (e == hipSuccess) e = er;
   if (e != hipSuccess) {

@@ -211,23 +211,44 @@ __device__ __forceinline__ void rope_key8(u32x4 a, u32x4 b, const float4* cs, u3
   }
 }
 
+// Two fp16 pairs (x, y) = (a.lo, b.lo), (a.hi, b.hi) turned back by fp16
+// (cos, sin) in packed fp16: x' = x c + f16(y s), y' = y c - f16(x s), each
+// a fused multiply-add of a rounded product.  With every request at least
+// kRopeSingleKeys long this moves lse by no more than the single-rounded
+// fp32 turn does (CPU simulation: 2.7e-4 against 2.4e-4 at 64 keys).
+__device__ __forceinline__ void rope_pair_f16(uint32_t a, uint32_t b, uint32_t c, uint32_t s,
+                                              uint32_t& ra, uint32_t& rb) {
+  const f16x2 x = __builtin_bit_cast(f16x2, a), y = __builtin_bit_cast(f16x2, b);
+  const f16x2 cc = __builtin_bit_cast(f16x2, c), ss = __builtin_bit_cast(f16x2, s);
+  const f16x2 ys = y * ss, xs = x * ss;
+  ra = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(x, cc, ys));
+  rb = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(y, cc, -xs));
+}
+
 // (cos, sin) table of the plan: one thread per (distance, frequency), angle
-// in fp64 from the definition, stored as two fp32.
-__global__ void rope_table_kernel(float2* table, int rows, int D, double theta, double scale) {
+// in fp64 from the definition, stored as two fp32 (row d: D/2 pairs), or --
+// f16 -- rounded once to fp16, row d = D/2 cosines then D/2 sines.
+__global__ void rope_table_kernel(void* table, int rows, int D, double theta, double scale,
+                                  int f16) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (int64_t)rows * (D / 2)) return;
   const int d = (int)(i / (D / 2)), f = (int)(i % (D / 2));
   const double ang = (d / scale) * pow(theta, -2.0 * f / D);
-  table[i] = float2{(float)cos(ang), (float)sin(ang)};
+  if (f16) {
+    _Float16* row = reinterpret_cast<_Float16*>(table) + (int64_t)d * D;
+    row[f] = (_Float16)cos(ang);
+    row[D / 2 + f] = (_Float16)sin(ang);
+  } else {
+    reinterpret_cast<float2*>(table)[i] = float2{(float)cos(ang), (float)sin(ang)};
+  }
 }
 
 hipError_t launch_rope_table(void* table, int rows, int head_dim, float theta, float scale,
-                             hipStream_t s) {
+                             bool f16, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   const int64_t n = (int64_t)rows * (head_dim / 2);
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     reinterpret_cast<float2*>(table), rows, head_dim, (double)theta,
-                     (double)scale);
+                     table, rows, head_dim, (double)theta, (double)scale, f16 ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -256,6 +277,13 @@ struct RopeLds {
   static constexpr int STRIDE = ROW + 16;            // the step's rows in LDS (padded)
   static constexpr int BYTES = kStep * STRIDE + kStep * ROW;
   static constexpr int FPL = (FREQ + 63) / 64;       // frequencies per lane
+  // fp16 table (ROPE == 2): a row is D/2 fp16 cosines then D/2 fp16 sines
+  // (2 D bytes), copied per step straight from the table into LDS rows
+  // padded to 2 D + 32 bytes (conflict-free for the reads of the turn)
+  static constexpr int ROW16 = 2 * D;
+  static constexpr int STRIDE16 = ROW16 + 32;
+  static constexpr int BYTES16 = kStep * STRIDE16;
+  static constexpr int VEC16 = kStep * ROW16 / 16;   // 16-byte vectors per step
 };
 // REC (a test instance): every K vector load also writes its byte offset in
 // the K pool to p.rec at ((rec_base[request] + token) * Hkv + kv head) * VR +
@@ -362,8 +390,34 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   };
   const float2* rtab = reinterpret_cast<const float2*>(p.rope_table);
   RopeRow rr[DEPTH];
+  // fp16 table (ROPE == 2): thread tid < VEC16 copies 16-byte vector tid
+  // of the step's 16 rows (row n = distance d0 - n, clamped at 0 for the
+  // masked tokens past the tile) from the table to LDS
+  struct RopeRow16 {
+    u32x4 v;
+  };
+  RopeRow16 rr16[DEPTH];
+  auto issue_rope16 = [&](int step, RopeRow16& rq) {
+    if constexpr (ROPE == 2) {
+      constexpr int VPR = RL::ROW16 / 16;   // vectors per row
+      if (tid < RL::VEC16) {
+        const int nn = tid / VPR, vv = tid - nn * VPR;
+        const int dist = max(qpos - t0 - kStep * step - nn, 0);
+        rq.v = reinterpret_cast<const u32x4*>(p.rope_table)[(int64_t)dist * VPR + vv];
+      }
+    }
+  };
+  auto stage_rope16 = [&](const RopeRow16& rq) {
+    if constexpr (ROPE == 2) {
+      constexpr int VPR = RL::ROW16 / 16;
+      if (tid < RL::VEC16) {
+        const int nn = tid / VPR, vv = tid - nn * VPR;
+        *reinterpret_cast<u32x4*>(rlds + nn * RL::STRIDE16 + 16 * vv) = rq.v;
+      }
+    }
+  };
   auto issue_rope = [&](int step, RopeRow& rq) {
-    if constexpr (ROPE) {
+    if constexpr (ROPE == 1) {
 #pragma unroll
       for (int k = 0; k < RL::FPL; ++k) {
         const int f = lane + 64 * k;
@@ -373,7 +427,7 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
     }
   };
   auto stage_rope = [&](const RopeRow& rq) {
-    if constexpr (ROPE) {
+    if constexpr (ROPE == 1) {
       for (int nn = wave; nn < kStep; nn += W) {
 #pragma unroll
         for (int k = 0; k < RL::FPL; ++k) {
@@ -389,7 +443,7 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
       }
     }
   };
-  if constexpr (ROPE) {
+  if constexpr (ROPE == 1) {
     constexpr int kVec = kStep * RL::ROW / 16;   // rows 0..15 in 16-byte vectors
     constexpr int kPer = (kVec + 63) / 64;       // per thread at W = 1
     const u32x4* src = reinterpret_cast<const u32x4*>(p.rope_table);
@@ -472,14 +526,33 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
       constexpr int HALF = D / 64;
 #pragma unroll
       for (int j = 0; j < HALF; ++j) {
-        const float4* cs =
-            reinterpret_cast<const float4*>(rlds + n * RL::STRIDE + 256 * j + 64 * g);
-        u32x4 ahi, alo, bhi, blo;
-        rope_key8<QBF16, ROPE == 1>(kop_of(j), kop_of(j + HALF), cs, ahi, alo, bhi, blo);
-        sc = mma16x16x32<QBF16>(ahi, qop[j], sc);
-        if constexpr (ROPE == 1) sc = mma16x16x32<QBF16>(alo, qop[j], sc);
-        sc = mma16x16x32<QBF16>(bhi, qop[j + HALF], sc);
-        if constexpr (ROPE == 1) sc = mma16x16x32<QBF16>(blo, qop[j + HALF], sc);
+        if constexpr (ROPE == 2) {
+          // fp16 q: the pairs turned in packed fp16 (product rounded, then
+          // the fused add) against fp16 (cos, sin), the key rounded once
+          const uint8_t* row = rlds + n * RL::STRIDE16 + 2 * (32 * j + 8 * g);
+          const u32x4 c8 = *reinterpret_cast<const u32x4*>(row);
+          const u32x4 s8 = *reinterpret_cast<const u32x4*>(row + 2 * RL::FREQ);
+          const u32x4 a = kop_of(j), b = kop_of(j + HALF);
+          u32x4 ra, rb;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            uint32_t x, y;
+            rope_pair_f16(a[k], b[k], c8[k], s8[k], x, y);
+            ra[k] = x;
+            rb[k] = y;
+          }
+          sc = mma16x16x32<QBF16>(ra, qop[j], sc);
+          sc = mma16x16x32<QBF16>(rb, qop[j + HALF], sc);
+        } else {
+          const float4* cs =
+              reinterpret_cast<const float4*>(rlds + n * RL::STRIDE + 256 * j + 64 * g);
+          u32x4 ahi, alo, bhi, blo;
+          rope_key8<QBF16, true>(kop_of(j), kop_of(j + HALF), cs, ahi, alo, bhi, blo);
+          sc = mma16x16x32<QBF16>(ahi, qop[j], sc);
+          sc = mma16x16x32<QBF16>(alo, qop[j], sc);
+          sc = mma16x16x32<QBF16>(bhi, qop[j + HALF], sc);
+          sc = mma16x16x32<QBF16>(blo, qop[j + HALF], sc);
+        }
       }
     } else if constexpr (VG > 0) {
       // ---- VALU instance: scores, softmax and P.V without MFMA
@@ -594,14 +667,17 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
       int pg1 = nsteps > 1 ? load_page(1) : 0;
       issue(0, load_page(0), kr[0], vr[0]);
       issue_rope(0, rr[0]);
+      issue_rope16(0, rr16[0]);
       for (int step = 0; step < nsteps; ++step) {
         const int pg2 = step + 2 < nsteps ? load_page(step + 2) : 0;
         stage(kr[0], vr[0]);
         stage_rope(rr[0]);
+        stage_rope16(rr16[0]);
         __syncthreads();
         if (step + 1 < nsteps) {
           issue(step + 1, pg1, kr[0], vr[0]);
           issue_rope(step + 1, rr[0]);
+          issue_rope16(step + 1, rr16[0]);
         }
         compute(step);
         __syncthreads();
@@ -612,29 +688,33 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
     if (nsteps > 0) {
       issue(0, load_page(0), kr[0], vr[0]);
       issue_rope(0, rr[0]);
+      issue_rope16(0, rr16[0]);
       if (nsteps > 1) {
         issue(1, load_page(1), kr[1], vr[1]);
         issue_rope(1, rr[DEPTH - 1]);
+        issue_rope16(1, rr16[DEPTH - 1]);
       }
       int pga = nsteps > 2 ? load_page(2) : 0;   // page of the next even step to issue
       int pgb = nsteps > 3 ? load_page(3) : 0;   // ... odd step
       // one body per register set: set d stages step s and refills with s + 2
       auto body = [&](int step, int& pgn, u32x4 (&kq)[S::LOADS], u32x4 (&vq)[S::LOADS],
-                      RopeRow& rq) {
+                      RopeRow& rq, RopeRow16& rq16) {
         stage(kq, vq);
         stage_rope(rq);
+        stage_rope16(rq16);
         __syncthreads();
         if (step + 2 < nsteps) {
           issue(step + 2, pgn, kq, vq);
           issue_rope(step + 2, rq);
+          issue_rope16(step + 2, rq16);
         }
         pgn = step + 4 < nsteps ? load_page(step + 4) : 0;
         compute(step);
         __syncthreads();
       };
       for (int step = 0; step < nsteps; step += 2) {
-        body(step, pga, kr[0], vr[0], rr[0]);
-        if (step + 1 < nsteps) body(step + 1, pgb, kr[1], vr[1], rr[DEPTH - 1]);
+        body(step, pga, kr[0], vr[0], rr[0], rr16[0]);
+        if (step + 1 < nsteps) body(step + 1, pgb, kr[1], vr[1], rr[DEPTH - 1], rr16[DEPTH - 1]);
       }
     }
   }
@@ -1107,7 +1187,7 @@ constexpr int kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
 template <int KV, bool QBF16, bool FOLD, int DEPTH, int ROPE, int D>
 static hipError_t launch_decode_t(const DecodeParams& p, int num_tiles, int waves,
                                   hipStream_t s) {
-  constexpr int rope_lds = ROPE ? RopeLds<D>::BYTES : 0;
+  constexpr int rope_lds = ROPE == 2 ? RopeLds<D>::BYTES16 : ROPE ? RopeLds<D>::BYTES : 0;
   const size_t lds = (size_t)Stage<KV, D>::lds_bytes(waves) + rope_lds;
   // (head_dim 256 with RoPE: at most 4 kv heads per tile fit)
   if (lds > (size_t)kMaxLds) return hipErrorInvalidValue;

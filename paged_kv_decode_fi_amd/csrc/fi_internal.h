@@ -66,7 +66,9 @@ struct ReqInfo {
 static_assert(sizeof(ReqInfo) == 16, "request info is 16 bytes");
 
 // RoPE table: for distance d < rows and frequency i < D / 2, the fp32 pair
-// (cos, sin) of d / scale * theta^(-2 i / D); a row is D / 2 pairs.
+// (cos, sin) of d / scale * theta^(-2 i / D); a row is D / 2 pairs.  Plans
+// whose turned keys are one fp16 value keep fp16 rows (D / 2 cosines, then
+// D / 2 sines: half as many bytes) in the same space.
 constexpr int rope_row_bytes(int D) { return D / 2 * 8; }
 
 // One merge work item: request r's states slot_base + c * Hkv + h,

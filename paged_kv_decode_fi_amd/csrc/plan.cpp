@@ -707,8 +707,11 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
     int64_t shortest = -1;
     for (int r = 0; r < B; ++r)
       if (lens[r] > 0) shortest = shortest < 0 ? lens[r] : std::min(shortest, lens[r]);
-    out->rope_single = in.tune.rope_split_k < 0 ||
-                       (in.tune.rope_split_k == 0 && shortest >= kRopeSingleKeys);
+    // (the step's fp16 table rows are copied by one 16-byte vector per
+    // thread: 2 D bytes x 16 rows need 32 D / 16 threads, W >= D / 32)
+    out->rope_single = hpt * 32 >= in.D &&
+                       (in.tune.rope_split_k < 0 ||
+                        (in.tune.rope_split_k == 0 && shortest >= kRopeSingleKeys));
   }
   L.rope_off = off;
   off = align256(off + (size_t)rope_row_bytes(in.D) * (size_t)out->rope_rows);

@@ -91,8 +91,10 @@ def test_rope_cascade_plan_is_rejected(fi):
 @pytest.mark.parametrize("case", range(8))
 def test_rope_single_rounded_fp16_key(fi, case):
     """fp16 q with every request at least 64 keys long: the plan passes each
-    turned key to the score as one fp16 value (no residual), whose rounding
-    stays well inside the lse bar over that many keys."""
+    turned key to the score as one fp16 value (turned in packed fp16 against
+    an fp16 (cos, sin) table, no residual), whose rounding stays well inside
+    the lse bar over that many keys; tiles of fewer than head_dim / 32 kv
+    heads keep the residual form."""
     rng = np.random.default_rng(900 + case)
     G = [1, 4, 8, 4, 16, 2, 8, 4][case]
     Hkv = [8, 8, 4, 2, 1, 4, 8, 8][case]
@@ -104,28 +106,35 @@ def test_rope_single_rounded_fp16_key(fi, case):
                 kv_dtype=kv, seed=50 + case)
     rope = (float(rng.choice([1e4, 5e5])), 1.0)
     o, lse, plan = C.run_gpu(w, chunk_tokens=[0, 64][case % 2], rope=rope)
-    assert plan.stats["rope_single"] == 1, plan.stats
+    # (the fp16 table rows of a step are copied one 16-byte vector per
+    # thread, which needs head_dim / 32 kv heads per tile)
+    want = int(plan.stats["heads_per_tile"] * 32 >= D)
+    assert plan.stats["rope_single"] == want, plan.stats
     ro, rl = C.run_oracle(w, rope=rope)
     C.assert_parity(w, o, lse, ro, rl, label=f"rope single {case} lens {list(lens)}")
 
 
 def test_rope_residual_kept_where_needed(fi):
-    """A request shorter than 64 keys, or bf16 q, keeps the turned key's
-    residual; forcing it on a long-request plan computes the same function."""
+    """A request shorter than 64 keys, bf16 q, or tiles of fewer than
+    head_dim / 32 kv heads keep the turned key's residual; forcing either
+    form on a long-request plan computes the same function."""
     short = W.build("rope_short", [700, 20], Hq=8, Hkv=2, ps=16, q_dtype="f16",
                     kv_dtype="f16", seed=4)
     bf = W.build("rope_bf16", [700, 200], Hq=8, Hkv=2, ps=16, q_dtype="bf16",
                  kv_dtype="bf16", seed=4)
     rope = (1e4, 1.0)
-    for w in (short, bf):
-        o, lse, plan = C.run_gpu(w, rope=rope)
+    for w in (short, bf, W.build("rope_narrow", [700, 300], Hq=8, Hkv=2, ps=16,
+                                  q_dtype="f16", kv_dtype="f16", seed=4)):
+        o, lse, plan = C.run_gpu(w, rope=rope, tuning=dict(rope_split_k=-1)
+                                 if w.name == "rope_narrow" else None)
         assert plan.stats["rope_single"] == 0
         ro, rl = C.run_oracle(w, rope=rope)
         C.assert_parity(w, o, lse, ro, rl, label=f"{w.name} residual kept")
-    lng = W.build("rope_long", [700, 300], Hq=8, Hkv=2, ps=16, q_dtype="f16",
+    lng = W.build("rope_long", [700, 300], Hq=16, Hkv=4, ps=16, q_dtype="f16",
                   kv_dtype="f16", seed=4)
     ro, rl = C.run_oracle(lng, rope=rope)
     for force, want in ((1, 0), (0, 1), (-1, 1)):
-        o, lse, plan = C.run_gpu(lng, rope=rope, tuning=dict(rope_split_k=force))
+        o, lse, plan = C.run_gpu(lng, rope=rope,
+                                 tuning=dict(rope_split_k=force, heads_per_tile=4))
         assert plan.stats["rope_single"] == want, (force, plan.stats)
         C.assert_parity(lng, o, lse, ro, rl, label=f"rope_split_k={force}")
