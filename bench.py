@@ -170,9 +170,6 @@ def main():
     prefix = ((w.prefix_qo_indptr, w.prefix_kv_indptr, w.prefix_last_page_len)
               if cascade else None)
 
-    if args.rope and (cascade or append):
-        print(json.dumps({"error": "--rope applies to plain decode workloads only"}))
-        sys.exit(2)
     rope_extra = (dict(kv_layout="ragged") if args.ragged else
                   dict(kv_layout="paged_hnd") if args.hnd else {})
     if append:
@@ -435,7 +432,7 @@ def main():
         fplan = fi.Plan(fw.kv_indptr, fw.last_page_len, num_qo_heads=w.num_qo_heads,
                         num_kv_heads=w.num_kv_heads, page_size=w.page_size,
                         head_dim=w.head_dim, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
-                        **rope_extra)
+                        **{k: v for k, v in rope_kw.items() if k != "tuning"}, **rope_extra)
         ftab = [dict(indptr=dev(fw.kv_indptr), indices=dev(fw.kv_indices),
                      last=dev(fw.last_page_len))]
 

@@ -23,7 +23,7 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["decode.hip", "merge.hip", "noalloc.hip"]
+HIP_SOURCES = ["decode.hip", "prefix.hip", "prefix_rope.hip", "merge.hip", "noalloc.hip"]
 CXX_SOURCES = ["plan.cpp", "api.cpp"]
 
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

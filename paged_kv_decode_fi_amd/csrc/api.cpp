@@ -377,6 +377,8 @@ fi_status fi_plan(const fi_problem* problem, int32_t num_cus, void* workspace,
   if (hp.num_levels >= 2)
     memcpy(st8 + hp.layout.state_off_off, hp.state_off,
            sizeof(int32_t) * (size_t)hp.num_levels * hp.batch);
+  if (hp.num_rope_qpos > 0)
+    memcpy(st8 + hp.layout.rope_qpos_off, hp.rope_qpos, sizeof(int32_t) * hp.num_rope_qpos);
   e = hipMemcpyAsync(workspace, staging, meta_bytes, hipMemcpyHostToDevice, hs);
   const bool copied = e == hipSuccess;
   if (e == hipSuccess && hp.rope)   // the (cos, sin) table, built on the device
@@ -506,6 +508,8 @@ fi_status enqueue_run(fi_plan_t plan, int stages, const void* q, const void* k_p
     pp.kv_indptr = kv_indptr;
     pp.kv_indices = kv_indices;
     pp.qo_indptr = qo_all;
+    if (hp.num_rope_qpos > 0)
+      pp.rope_qpos = reinterpret_cast<const int32_t*>(plan->workspace + hp.layout.rope_qpos_off);
     e = fi::launch_prefix(pp, (int)hp.num_prefix_tiles, hp.prefix_waves, true, false, qbf, kv,
                           hp.D, s);
     if (e != hipSuccess) return hip_fail(e, "append launch");
@@ -525,6 +529,10 @@ fi_status enqueue_run(fi_plan_t plan, int stages, const void* q, const void* k_p
                                (int64_t)l * hp.batch
                          : nullptr;
       pp.num_tiles = (int32_t)(hp.num_tiles + hp.level_tile_off[l]);
+      if (hp.num_rope_qpos > 0)
+        pp.rope_qpos =
+            reinterpret_cast<const int32_t*>(plan->workspace + hp.layout.rope_qpos_off) +
+            (int64_t)l * hp.batch;
       e = fi::launch_prefix(pp, (int)n, hp.prefix_waves, false, (hp.prefix_split_p >> l) & 1u,
                             qbf, kv, hp.D, s);
       if (e != hipSuccess) return hip_fail(e, "prefix launch");

@@ -1,5 +1,6 @@
-// decode.hip -- gfx950 paged decode attention, cascade prefix and append
-// kernels.
+// decode.hip -- gfx950 paged decode attention kernel (the multi-row kernel of
+// cascade prefix and append tiles is in fi_prefix.h, launched from
+// prefix.hip and prefix_rope.hip).
 //
 // Computes, for one query token per head, exact attention over the keys a
 // request reaches through its page table (FlashInfer README "core features"
@@ -34,16 +35,10 @@
 //  * LLaMA-style RoPE (README decode example, pos_encoding_mode): the
 //    decode kernel turns each key by its distance from the query before the
 //    score MFMAs (described above rope_key8).
-//  * prefix_kernel: many query rows against one chunk of one key list, K/V
-//    staged in LDS and shared by 8 waves x 32 rows (16 at head_dim 256) --
-//    the G heads of every request of a cascade group against the shared
-//    prefix, or the query tokens of an append request (README append
-//    example, causal mask) against its own keys; described above the kernel.
 //  * K/V rows are addressed by page, slot and head strides: NHD or HND
 //    pages, or the ragged layout (page size 1, no page table).
 //  * head_dim D (64, 128, 256) is a template parameter: D / 32 q operands
-//    and D / 16 output blocks per lane; at 256 prefix_kernel gives each wave
-//    one 16-row column tile instead of two (registers).
+//    and D / 16 output blocks per lane.
 #include <algorithm>
 #include <type_traits>
 
@@ -51,14 +46,6 @@
 
 namespace fi {
 
-// gfx950 transpose read of 16-bit LDS data (ds_read_b64_tr_b16), used for
-// the V^T operand of P.V.  It works per 16-lane group: lane i's element k is
-// element i % 4 of the 4 x 16-bit row addressed by lane i / 4 + 4 k of its
-// group (layout measured with a probe).  So a lane that addresses the d-quad
-// n % 4 of the row holding contraction element kk = n / 4 receives, over its
-// four elements, that d column for four consecutive contraction elements.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // ============================================================================
 // decode tiles (page-staged)
@@ -154,34 +141,6 @@ __device__ __forceinline__ void fold_states(const float* __restrict__ partial_o,
 // distances d0 - n, n < 16 (d0 = p - first token of the step); the
 // workgroup builds them in LDS from row d0 and rows 0..15 by the
 // angle-difference identities, each (n, i) once.
-template <bool BF16>
-__device__ __forceinline__ float lo16(uint32_t w) {
-  if constexpr (BF16) return __builtin_bit_cast(float, w << 16);
-  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffff));
-}
-template <bool BF16>
-__device__ __forceinline__ float hi16(uint32_t w) {
-  if constexpr (BF16) return __builtin_bit_cast(float, w & 0xffff0000u);
-  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-}
-
-// (x0 - h.lo, x1 - h.hi) rounded to the 16-bit type, h = the pair (x0, x1)
-// already rounded.  f16: one mixed-precision FMA per half (the f16 operand
-// is widened inside the instruction, the result rounded to f16 in place).
-template <bool BF16>
-__device__ __forceinline__ uint32_t residual2(uint32_t h, float x0, float x1) {
-  if constexpr (BF16) {
-    return pack2<true>(x0 - lo16<true>(h), x1 - hi16<true>(h));
-  } else {
-    uint32_t r;
-    asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]\n\t"
-        "v_fma_mixhi_f16 %0, -%1, 1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-        : "=&v"(r)
-        : "v"(h), "v"(x0), "v"(x1));
-    return r;
-  }
-}
-
 // Turns 8 + 8 partner elements of one key (a: dims f..f+7, b: dims
 // f+64..f+71, 16-bit) back by its distance, (cos, sin) of frequencies
 // f..f+7 in cs, in fp32; writes the result as a 16-bit high part plus a
@@ -797,386 +756,6 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   }
 }
 
-// ============================================================================
-// cascade prefix tiles: many query rows x one prefix chunk of one kv head.
-// ============================================================================
-// Workgroup = WAVES waves; wave w owns query rows row0 + 16 RT w + 16 rt + n
-// (rt < RT: 2 row tiles, 1 at head_dim 256) as the N columns of its MFMAs,
-// so each K/V element staged in LDS serves 16 RT WAVES rows.  The tile's slice of the page table is copied to LDS
-// once.  Per 32-token step the workgroup loads the step's K and V rows of the
-// tile's kv head (NL 16-byte vectors per thread) two steps ahead into
-// registers, stores them to one of two LDS buffers after computing from the
-// other, one barrier per step.  Scores: MFMA 16x16x32 with every K operand of
-// the step read from LDS up front; the V^T operands (transpose reads) are
-// issued before the softmax so their latency hides under it.  Softmax: the
-// probabilities are formed against the running max m; only when a lane's sum
-// of them exceeds kPrefixLazySum (or is not finite: the first step, where m =
-// -inf) does the wave take the exact row max, rescale and recompute, so the
-// common step carries no max reduction.  P.V: MFMA 16x16x32.  The prefix is
-// reused across row tiles, so its loads use the default (cached) policy, and
-// the block -> tile map puts all row tiles of one (head, chunk) on the same
-// XCD (workgroups are dispatched to the 8 XCDs round-robin) so they share
-// that XCD's L2.
-//
-// The same kernel runs append tiles (APPEND): the rows are the query tokens
-// of one request (token-major, G heads each) over that request's own pages;
-// row i may attend keys below its limit (ReqInfo.kv_len of its token: its
-// causal limit, or all keys without the mask), so a step that reaches past
-// the smallest limit of the wave's rows masks per row, and a wave skips
-// steps past the largest limit of its rows.
-constexpr int kPStep = 32;
-constexpr float kPrefixLazySum = 256.f;
-
-template <int KV, int D>
-struct PStage {
-  static constexpr int ROWB = KV == kKvE4M3 ? D : 2 * D;    // K row bytes kept in LDS
-  // K LDS row stride: 16-bit rows padded by 32 bytes (the score operand
-  // reads then show no bank conflict; at 16 bytes they took 28 % of the
-  // LDS-active cycles), e4m3 rows by 16
-  static constexpr int KS = ROWB + (KV == kKvE4M3 ? 16 : 32);
-  static constexpr int VS = 2 * D + 32;                     // V LDS row stride (16-bit values)
-  static constexpr int BUF = kPStep * (KS + VS);
-  static constexpr int PTAB = kPrefixMaxChunk + 2;          // page-table slots (page_size 1)
-  static constexpr int LDS = 2 * BUF + 4 * PTAB;
-};
-
-// XCD-aware map: block b runs on XCD b % 8; give each XCD a contiguous range
-// of the (chunk, head, row tile)-ordered tile list.
-__device__ __forceinline__ int xcd_tile(int b, int n) {
-  const int x = b & 7, k = b >> 3, per = n >> 3, rem = n & 7;
-  return x * per + min(x, rem) + k;
-}
-
-// MODE: kPrefixPlain / kPrefixSplitP (cascade prefix tiles) or kPrefixAppend.
-enum { kPrefixPlain = 0, kPrefixSplitP = 1, kPrefixAppend = 2 };
-
-// REC: as decode_kernel's (the token base is that of the tile's group, or of
-// its request for append tiles).
-template <int KV, bool QBF16, int WAVES, bool PS_POW2, int MODE, int D, bool REC = false>
-__global__ __launch_bounds__(64 * WAVES, WAVES == 4 && D != 256 ? 2 : 1) void prefix_kernel(
-    DecodeParams p) {
-  constexpr bool APPEND = MODE == kPrefixAppend;
-  // row tiles (16 query rows each) per wave: two, one at D = 256
-  constexpr int RT = prefix_rows_per_wave(D) / 16;
-  using S = PStage<KV, D>;
-  // bf16 K/V: P.V takes p as a bf16 high part plus a bf16 residual in append
-  // tiles and in the split-p cascade instance -- bf16 keeps 8 bits of p, and
-  // when a few keys carry comparable weight (the first rows of a prefill, a
-  // short shared prefix) that rounding alone moves o past the accuracy bar.
-  // The plan picks the split instance for a cascade level whose shortest
-  // prefix is under kSplitPKeys keys; long prefixes keep one bf16 p (the
-  // residual products cost the MFMA-bound kernel more than a tenth, and over
-  // that many keys the rounding averages out).
-  constexpr bool SPLITP = MODE != kPrefixPlain && KV == kKvBF16;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
-  int* ptab = reinterpret_cast<int*>(lds + 2 * S::BUF);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, n = lane & 15;
-  // cascade: contiguous tile ranges per XCD; append: the plan interleaves
-  // its list so that block b and b + 8 (same XCD) share a key chunk
-  const Tile tile =
-      p.tiles[p.num_tiles + (APPEND ? (int)blockIdx.x : xcd_tile(blockIdx.x, gridDim.x))];
-  const int grp = tile.req, h = tile.kv_head0, t0 = tile.t0, t1 = tile.t1;
-  const int G = p.G;
-  const int qo0 = p.qo_indptr[grp];
-  const int page_base = p.kv_indptr[grp];
-  const int ps = p.page_size, ps_shift = p.ps_shift;
-  auto page_idx = [&](int t) { return PS_POW2 ? (t >> ps_shift) : (t / ps); };
-  const int nsteps = (t1 - t0 + kPStep - 1) / kPStep;
-  if (nsteps <= 0) return;   // the plan emits no empty prefix tiles
-  const int pfirst = page_idx(t0);
-  {
-    const int np = page_idx(t1 - 1) - pfirst + 1;   // <= chunk / page_size + 1 < PTAB
-    for (int i = tid; i < np; i += 64 * WAVES)
-      ptab[i] = p.ragged ? page_base + pfirst + i : p.kv_indices[page_base + pfirst + i];
-  }
-
-  // query rows of this lane's two column tiles (B operands of the scores)
-  u32x4 qop[RT][D / 32];
-  bool rok[RT];
-  int rreq[RT], rj[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = tile.row0 + 16 * RT * wave + 16 * rt + n;   // < row0 + 16 RT WAVES
-    rok[rt] = row < tile.row1;
-    const int rr = rok[rt] ? row : tile.row0;
-    rreq[rt] = qo0 + rr / G;
-    rj[rt] = h * G + rr % G;
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
-                           ((int64_t)rreq[rt] * p.Hq + rj[rt]) * D;
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * g);
-      qop[rt][s] = rok[rt] ? v : u32x4{0, 0, 0, 0};
-    }
-  }
-  // key limit of each of this lane's rows within the tile (t1, or the
-  // row's causal limit), and over the wave's valid rows the smallest (steps
-  // reaching past it mask per row) and the largest (steps from there on
-  // have no key for any row: skipped)
-  int lim[RT], lo = 0x7fffffff, hi = -0x7fffffff - 1;
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    lim[rt] = APPEND ? min(p.req_info[rreq[rt]].kv_len, t1) : t1;
-    if (rok[rt]) {
-      lo = min(lo, lim[rt]);
-      hi = max(hi, lim[rt]);
-    }
-  }
-#pragma unroll
-  for (int k = 1; k < 16; k <<= 1) {
-    lo = min(lo, __shfl_xor(lo, k));
-    hi = max(hi, __shfl_xor(hi, k));
-  }
-  const int wave_lo = __builtin_amdgcn_readfirstlane(lo);
-  const int wave_hi = __builtin_amdgcn_readfirstlane(hi);
-  float c = p.sm_scale_log2;
-  if (KV == kKvE4M3 && p.k_scale) c *= p.k_scale[h];
-
-  // cooperative loader: a step is 32 rows of K and 32 rows of V, i.e.
-  // 2 x 32 x VR 16-byte vectors (VR per row).  Thread tid loads vectors
-  // idx = tid + u T (T threads, u < NL): pool idx / (32 VR) (0 = K, 1 = V),
-  // token (idx % (32 VR)) / VR, chunk idx % VR.
-  constexpr bool F8 = KV == kKvE4M3;
-  constexpr int VR = S::ROWB / 16;
-  constexpr int T = 64 * WAVES;
-  constexpr int PV = 32 * VR;                       // vectors per pool per step
-  constexpr int NL = (2 * PV + T - 1) / T;
-  const char* kbase = reinterpret_cast<const char*>(p.k_pages) + (int64_t)h * p.head_stride;
-  const char* vbase = reinterpret_cast<const char*>(p.v_pages) + (int64_t)h * p.head_stride;
-  const int last = t1 - 1;
-  auto load = [&](int tb, u32x4 (&vec)[NL]) {
-#pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      const int idx = tid + u * T;
-      if (2 * PV % T != 0 && idx >= 2 * PV) continue;
-      const int q = idx % PV;
-      const int t = min(tb + q / VR, last);
-      const int pi = page_idx(t);
-      const uint32_t sl = PS_POW2 ? (uint32_t)(t & (ps - 1)) : (uint32_t)(t - pi * ps);
-      const uint32_t page = (uint32_t)ptab[pi - pfirst];
-      const uint64_t off =
-          (uint64_t)page * p.page_bytes + sl * p.slot_stride + 16 * (q % VR);
-      vec[u] = ld_global<u32x4>(idx < PV ? kbase : vbase, off);
-      if constexpr (REC) {
-        if (idx < PV)
-          p.rec[((p.rec_base[grp] + t) * p.Hkv + h) * VR + q % VR] =
-              (int64_t)(off + (uint64_t)h * p.head_stride);
-      }
-    }
-  };
-  auto store = [&](int buf, const u32x4 (&vec)[NL]) {
-    uint8_t* kt = lds + buf * S::BUF;
-    uint8_t* vt = kt + kPStep * S::KS;
-#pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      const int idx = tid + u * T;
-      if (2 * PV % T != 0 && idx >= 2 * PV) continue;
-      const int q = idx % PV;
-      const int tok = q / VR, chk = q % VR;
-      if (idx < PV) {
-        *reinterpret_cast<u32x4*>(kt + tok * S::KS + 16 * chk) = vec[u];
-      } else if constexpr (F8) {
-        const u32x2 a = e4m3x4_to_16<QBF16>(vec[u].x), b = e4m3x4_to_16<QBF16>(vec[u].y);
-        const u32x2 c2 = e4m3x4_to_16<QBF16>(vec[u].z), d = e4m3x4_to_16<QBF16>(vec[u].w);
-        uint8_t* dv = vt + tok * S::VS + 32 * chk;
-        *reinterpret_cast<u32x4*>(dv) = u32x4{a.x, a.y, b.x, b.y};
-        *reinterpret_cast<u32x4*>(dv + 16) = u32x4{c2.x, c2.y, d.x, d.y};
-      } else {
-        *reinterpret_cast<u32x4*>(vt + tok * S::VS + 16 * chk) = vec[u];
-      }
-    }
-  };
-
-  float m[RT], l[RT];
-  f32x4 oacc[RT][D / 16];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    m[rt] = -INFINITY;
-    l[rt] = 0.f;
-  }
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int b = 0; b < D / 16; ++b) oacc[rt][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // one 32-token step from LDS buffer buf; a step reaching past the
-  // smallest row limit masks tokens at or past each row's limit (a uniform
-  // branch around the masking only: one copy of the step body keeps the
-  // accumulators in place across iterations)
-  auto compute = [&](int tb, int buf, bool tail) {
-    const uint8_t* kt = lds + buf * S::BUF;
-    const uint8_t* vt = kt + kPStep * S::KS;
-    // ---- K operands of both token tiles (tokens 16 tt + n), all k slices
-    u32x4 kop[2][D / 32];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const uint8_t* krow = kt + (16 * tt + n) * S::KS;
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s) {
-        if constexpr (F8) {
-          const u32x2 w8 = *reinterpret_cast<const u32x2*>(krow + 32 * s + 8 * g);
-          const u32x2 a = e4m3x4_to_16<QBF16>(w8.x), b = e4m3x4_to_16<QBF16>(w8.y);
-          kop[tt][s] = u32x4{a.x, a.y, b.x, b.y};
-        } else {
-          kop[tt][s] = *reinterpret_cast<const u32x4*>(krow + 64 * s + 16 * g);
-        }
-      }
-    }
-    // ---- V^T operands: contraction element kk of lane group g is token
-    // 4 g + (kk & 3) + 16 (kk >> 2); two transpose reads per dim block b
-    u32x4 vop[D / 16];
-    const uint8_t* vsrc = vt + (4 * g + (n >> 2)) * S::VS + 8 * (n & 3);
-#pragma unroll
-    for (int b = 0; b < D / 16; ++b) {
-      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vsrc + 32 * b));
-      const s16x4 v1 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vsrc + 16 * S::VS + 32 * b));
-      const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
-      vop[b] = u32x4{w0.x, w0.y, w1.x, w1.y};
-    }
-    // ---- scores: S[tt][rt] = K(tokens 16 tt ..) . Q^T(rows of tile rt);
-    // the four accumulators are independent, so consecutive MFMAs never wait
-    f32x4 sc[2][RT];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) sc[tt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          sc[tt][rt] = mma16x16x32<QBF16>(kop[tt][s], qop[rt][s], sc[tt][rt]);
-    // ---- softmax per row tile: lane (g, n) holds tokens 4 g + i and
-    // 16 + 4 g + i (i < 4) of row n
-    u32x4 pop[RT], plo[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      float x[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = sc[0][rt][i];
-        x[4 + i] = sc[1][rt][i];
-      }
-      if (__builtin_expect(tail, 0)) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (tb + 4 * g + i >= lim[rt]) x[i] = -INFINITY;
-          if (tb + 16 + 4 * g + i >= lim[rt]) x[4 + i] = -INFINITY;
-        }
-      }
-      float pr[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(__builtin_fmaf(x[i], c, -m[rt]));
-      float sum = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-      if (__builtin_expect(__any(!(sum <= kPrefixLazySum)), 0)) {
-        // exact row max of this step, rescale, recompute (a row with no key
-        // so far -- all masked -- keeps m = -inf and gets p = 0)
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) mx = fmaxf(mx, x[i] * c);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m[rt], mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m[rt] - m_use);
-        l[rt] *= alpha;
-#pragma unroll
-        for (int b = 0; b < D / 16; ++b) oacc[rt][b] *= alpha;
-        m[rt] = m_new;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(__builtin_fmaf(x[i], c, -m_use));
-        sum = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-      }
-      l[rt] += sum;
-      pop[rt] = u32x4{pack2<QBF16>(pr[0], pr[1]), pack2<QBF16>(pr[2], pr[3]),
-                      pack2<QBF16>(pr[4], pr[5]), pack2<QBF16>(pr[6], pr[7])};
-      if constexpr (SPLITP) {
-        // bf16 keeps 8 bits of p: the residual p - bf16(p) goes through a
-        // second P.V product
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          plo[rt][k] = pack2<true>(pr[2 * k] - lo16<true>(pop[rt][k]),
-                                   pr[2 * k + 1] - hi16<true>(pop[rt][k]));
-      }
-    }
-    // ---- P.V on MFMA 16x16x32
-    if constexpr (SPLITP) {
-#pragma unroll
-      for (int b = 0; b < D / 16; ++b) {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          oacc[rt][b] = mma16x16x32<QBF16>(vop[b], pop[rt], oacc[rt][b]);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          oacc[rt][b] = mma16x16x32<QBF16>(vop[b], plo[rt], oacc[rt][b]);
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < D / 16; ++b)
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          oacc[rt][b] = mma16x16x32<QBF16>(vop[b], pop[rt], oacc[rt][b]);
-    }
-  };
-
-  // two register sets: the one for step s + 1 is in flight while step s is
-  // computed, the one for step s + 2 is issued at the start of step s
-  u32x4 va[NL], vb[NL];
-  __syncthreads();   // page table
-  load(t0, va);
-  store(0, va);
-  if (nsteps > 1) load(t0 + kPStep, vb);
-  __syncthreads();
-  auto step_body = [&](int step, u32x4 (&nxt)[NL], u32x4 (&aft)[NL]) {
-    const int tb = t0 + kPStep * step;
-    if (step + 2 < nsteps) load(tb + 2 * kPStep, aft);
-    if (tb < wave_hi) compute(tb, step & 1, tb + kPStep > wave_lo);
-    if (step + 1 < nsteps) store((step + 1) & 1, nxt);
-    __syncthreads();
-  };
-  for (int step = 0; step < nsteps; step += 2) {
-    step_body(step, vb, va);
-    if (step + 1 < nsteps) step_body(step + 1, va, vb);
-  }
-
-  // ---- finalize each row tile
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    float lt = l[rt] + __shfl_xor(l[rt], 16);
-    lt += __shfl_xor(lt, 32);
-    float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (KV == kKvE4M3 && p.v_scale) inv *= p.v_scale[h];
-    const float lse2 = lt > 0.f ? m[rt] + fast_log2(lt) : -INFINITY;
-    if (!rok[rt]) continue;
-    const int r = rreq[rt], j = rj[rt];
-    const ReqInfo ri = p.req_info[r];
-    if (ri.n_states <= 1) {
-      uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)r * p.Hq + j) * D;
-#pragma unroll
-      for (int b = 0; b < D / 16; ++b) {
-        u32x2 w = {pack2<QBF16>(oacc[rt][b][0] * inv, oacc[rt][b][1] * inv),
-                   pack2<QBF16>(oacc[rt][b][2] * inv, oacc[rt][b][3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + 16 * b + 4 * g) = w;
-      }
-      if (g == 0 && p.lse) p.lse[(int64_t)r * p.Hq + j] = lse2 * kLn2;
-    } else {
-      // state index: this level's chunk after the request's earlier levels
-      const int c = tile.slot + (p.state_off ? p.state_off[r] : 0);
-      const int64_t slot = ri.slot_base + (int64_t)c * p.Hkv + h;
-      float* po = p.partial_o + (slot * G + (j - h * G)) * D;
-#pragma unroll
-      for (int b = 0; b < D / 16; ++b)
-        *reinterpret_cast<f32x4*>(po + 16 * b + 4 * g) = oacc[rt][b] * inv;
-      if (g == 0) p.partial_lse[slot * G + (j - h * G)] = lse2;
-    }
-  }
-}
-
 // ---- launchers ----------------------------------------------------------------
 // depth (from the plan's tuning): 0 = each instance's own choice below, 1 =
 // one step of loads in flight everywhere, 2 = two where the instance has a
@@ -1301,43 +880,6 @@ static hipError_t launch_decode_f(const DecodeParams& p, int num_tiles, int wave
   }
 }
 
-template <int KV, bool QBF16, int W, int MODE, int D>
-static void launch_prefix_w(const DecodeParams& p, int num_tiles, hipStream_t s) {
-  if (p.ps_shift >= 0)
-    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, W, true, MODE, D>), dim3(num_tiles),
-                       dim3(64 * W), 0, s, p);
-  else
-    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, W, false, MODE, D>), dim3(num_tiles),
-                       dim3(64 * W), 0, s, p);
-}
-
-template <int KV, bool QBF16, int W, int D>
-static void launch_prefix_m(const DecodeParams& p, int num_tiles, bool append, bool split,
-                            hipStream_t s) {
-  if (append) {
-    launch_prefix_w<KV, QBF16, W, kPrefixAppend, D>(p, num_tiles, s);
-    return;
-  }
-  if constexpr (KV == kKvBF16) {   // the split instance exists for bf16 K/V only
-    if (split) {
-      launch_prefix_w<KV, QBF16, W, kPrefixSplitP, D>(p, num_tiles, s);
-      return;
-    }
-  }
-  launch_prefix_w<KV, QBF16, W, kPrefixPlain, D>(p, num_tiles, s);
-}
-
-template <int KV, bool QBF16, int D>
-static hipError_t launch_prefix_t(const DecodeParams& p, int num_tiles, int waves, bool append,
-                                  bool split, hipStream_t s) {
-  if (num_tiles <= 0) return hipSuccess;
-  if (waves == 4)
-    launch_prefix_m<KV, QBF16, 4, D>(p, num_tiles, append, split, s);
-  else
-    launch_prefix_m<KV, QBF16, 8, D>(p, num_tiles, append, split, s);
-  return hipGetLastError();
-}
-
 template <int D>
 static hipError_t launch_decode_d(const DecodeParams& p, int num_tiles, int waves, bool q_bf16,
                                   int kv, bool fold, int depth, hipStream_t s) {
@@ -1346,16 +888,6 @@ static hipError_t launch_decode_d(const DecodeParams& p, int num_tiles, int wave
                   : launch_decode_f<kKvE4M3, false, D>(p, num_tiles, waves, fold, depth, s);
   return q_bf16 ? launch_decode_f<kKvBF16, true, D>(p, num_tiles, waves, fold, depth, s)
                 : launch_decode_f<kKvF16, false, D>(p, num_tiles, waves, fold, depth, s);
-}
-
-template <int D>
-static hipError_t launch_prefix_d(const DecodeParams& p, int num_tiles, int waves, bool append,
-                                  bool split, bool q_bf16, int kv, hipStream_t s) {
-  if (kv == kKvE4M3)
-    return q_bf16 ? launch_prefix_t<kKvE4M3, true, D>(p, num_tiles, waves, append, split, s)
-                  : launch_prefix_t<kKvE4M3, false, D>(p, num_tiles, waves, append, split, s);
-  return q_bf16 ? launch_prefix_t<kKvBF16, true, D>(p, num_tiles, waves, append, split, s)
-                : launch_prefix_t<kKvF16, false, D>(p, num_tiles, waves, append, split, s);
 }
 
 // ---- record instances (test hook): head_dim 128, fp16 q + fp16 K/V or bf16
@@ -1399,29 +931,6 @@ static hipError_t launch_decode_rec(const DecodeParams& p, int num_tiles, int wa
   return hipErrorInvalidValue;
 }
 
-template <int KV, bool QBF16, int MODE>
-static hipError_t launch_prefix_rec_t(const DecodeParams& p, int num_tiles, hipStream_t s) {
-  if (p.ps_shift >= 0)
-    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, 8, true, MODE, 128, true>), dim3(num_tiles),
-                       dim3(512), 0, s, p);
-  else
-    hipLaunchKernelGGL((prefix_kernel<KV, QBF16, 8, false, MODE, 128, true>), dim3(num_tiles),
-                       dim3(512), 0, s, p);
-  return hipGetLastError();
-}
-
-static hipError_t launch_prefix_rec(const DecodeParams& p, int num_tiles, int waves,
-                                    bool append, bool q_bf16, int kv, int head_dim,
-                                    hipStream_t s) {
-  if (head_dim != 128 || waves != 8) return hipErrorInvalidValue;
-  if (kv == kKvF16 && !q_bf16)
-    return append ? launch_prefix_rec_t<kKvF16, false, kPrefixAppend>(p, num_tiles, s)
-                  : launch_prefix_rec_t<kKvF16, false, kPrefixPlain>(p, num_tiles, s);
-  if (kv == kKvE4M3 && q_bf16 && !append)
-    return launch_prefix_rec_t<kKvE4M3, true, kPrefixPlain>(p, num_tiles, s);
-  return hipErrorInvalidValue;
-}
-
 // q_bf16: q (and o) are bf16, else fp16.  kv: KvKind.  fold: the work list
 // has tiles that fold earlier states into their output.  depth: 0, 1 or 2
 // (above).  head_dim: 64, 128 or 256.  p.rec != NULL selects the record
@@ -1438,24 +947,6 @@ hipError_t launch_decode(const DecodeParams& p, int num_tiles, int waves, bool q
     case 64: return launch_decode_d<64>(p, num_tiles, waves, q_bf16, kv, fold, depth, s);
     case 128: return launch_decode_d<128>(p, num_tiles, waves, q_bf16, kv, fold, depth, s);
     case 256: return launch_decode_d<256>(p, num_tiles, waves, q_bf16, kv, fold, depth, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-// append: append tiles (rows limited by ReqInfo.kv_len), else cascade
-// prefix; split: bf16 cascade prefix tiles pass p with a residual.
-// head_dim: 64, 128 or 256.
-hipError_t launch_prefix(const DecodeParams& p, int num_tiles, int waves, bool append,
-                         bool split, bool q_bf16, int kv, int head_dim, hipStream_t s) {
-  if (waves != 4 && waves != 8) return hipErrorInvalidValue;
-  if (p.rec) {
-    if (num_tiles <= 0) return hipSuccess;
-    return launch_prefix_rec(p, num_tiles, waves, append, q_bf16, kv, head_dim, s);
-  }
-  switch (head_dim) {
-    case 64: return launch_prefix_d<64>(p, num_tiles, waves, append, split, q_bf16, kv, s);
-    case 128: return launch_prefix_d<128>(p, num_tiles, waves, append, split, q_bf16, kv, s);
-    case 256: return launch_prefix_d<256>(p, num_tiles, waves, append, split, q_bf16, kv, s);
     default: return hipErrorInvalidValue;
   }
 }

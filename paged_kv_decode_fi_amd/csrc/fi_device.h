@@ -83,6 +83,43 @@ __device__ __forceinline__ u32x2 e4m3x4_to_16(uint32_t w) {
   return r;
 }
 
+// gfx950 transpose read of 16-bit LDS data (ds_read_b64_tr_b16), used for
+// the V^T operand of P.V.  It works per 16-lane group: lane i's element k is
+// element i % 4 of the 4 x 16-bit row addressed by lane i / 4 + 4 k of its
+// group (layout measured with a probe).  So a lane that addresses the d-quad
+// n % 4 of the row holding contraction element kk = n / 4 receives, over its
+// four elements, that d column for four consecutive contraction elements.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <bool BF16>
+__device__ __forceinline__ float lo16(uint32_t w) {
+  if constexpr (BF16) return __builtin_bit_cast(float, w << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffff));
+}
+template <bool BF16>
+__device__ __forceinline__ float hi16(uint32_t w) {
+  if constexpr (BF16) return __builtin_bit_cast(float, w & 0xffff0000u);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// (x0 - h.lo, x1 - h.hi) rounded to the 16-bit type, h = the pair (x0, x1)
+// already rounded.  f16: one mixed-precision FMA per half (the f16 operand
+// is widened inside the instruction, the result rounded to f16 in place).
+template <bool BF16>
+__device__ __forceinline__ uint32_t residual2(uint32_t h, float x0, float x1) {
+  if constexpr (BF16) {
+    return pack2<true>(x0 - lo16<true>(h), x1 - hi16<true>(h));
+  } else {
+    uint32_t r;
+    asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, -%1, 1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=&v"(r)
+        : "v"(h), "v"(x0), "v"(x1));
+    return r;
+  }
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

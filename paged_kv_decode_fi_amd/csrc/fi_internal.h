@@ -14,8 +14,10 @@ constexpr int kChunkAlign = 16;    // decode chunks are whole 16-token steps
 constexpr int kWavesPerTile = 8;   // waves (= kv heads) per decode workgroup
 constexpr int kPrefixRowsPerWave = 32;   // 2 MFMA column tiles per wave
 // query rows per wave of the multi-row kernel at head_dim D: two 16-row
-// column tiles, one at D = 256 (registers)
-constexpr int prefix_rows_per_wave(int D) { return D == 256 ? 16 : kPrefixRowsPerWave; }
+// column tiles, one at D = 256 or with RoPE (registers)
+constexpr int prefix_rows_per_wave(int D, bool rope = false) {
+  return D == 256 || rope ? 16 : kPrefixRowsPerWave;
+}
 constexpr int kPrefixMaxWaves = 8;       // prefix workgroup: 4 or 8 waves
 constexpr int kPrefixMaxChunk = 4096;    // prefix tokens per tile (page table in LDS)
 constexpr int kMaxMergeStates = 64;
@@ -84,6 +86,7 @@ struct WorkspaceLayout {
   size_t merge_reqs_off;   // MergeUnit[num_merge_units]
   size_t qo_indptr_off;    // int32[qo_len]: cascade group starts or append query starts
   size_t state_off_off;    // int32[num_levels * batch] (levels >= 2)
+  size_t rope_qpos_off;    // int32[num_rope_qpos] (RoPE cascade / append plans)
   size_t partial_o_off;    // float[num_partials][G][D]
   size_t partial_lse_off;  // float[num_partials][G]   (log2 domain)
   size_t rope_off;         // float2[rope_rows][D / 2] (RoPE plans)
@@ -126,7 +129,14 @@ struct HostPlan {
   int32_t valu_heads;   // plain decode on the VALU instance for this many q heads per
                         // kv head (1, 2 or 4), 0 = MFMA
   int32_t rope;         // FI_POS_ROPE_LLAMA or 0
-  int32_t rope_rows;    // positions in the RoPE table (longest request)
+  int32_t rope_rows;    // positions in the RoPE table (longest key list)
+  // RoPE cascade / append plans: the position each query row is turned by
+  // in the multi-row kernel, relative to the start of the key list its tile
+  // reads -- cascade: [level * batch + request] = (the request's keys over
+  // all levels - 1) - (keys of its earlier levels); append: [query token] =
+  // its position in the request
+  int32_t* rope_qpos;
+  int64_t num_rope_qpos;
   float rope_theta, rope_scale;
   Tile* tiles;          // num_tiles + num_prefix_tiles entries
   ReqInfo* req_info;    // batch entries
@@ -220,6 +230,9 @@ struct DecodeParams {
   // prefix tiles of a cascade with several levels: request r's states from
   // this level start at state index state_off[r] (NULL: 0)
   const int32_t* state_off;
+  // RoPE multi-row tiles: the position query rows of request (cascade) or
+  // query token (append) i are turned by, rope_qpos[i]
+  const int32_t* rope_qpos;
   // K/V row of (page, slot, kv head) at page * page_bytes + slot *
   // slot_stride + head * head_stride bytes: NHD pages (slot_stride = Hkv
   // rows, head_stride = 1 row) or HND pages (slot_stride = 1 row,

@@ -148,10 +148,14 @@ int plan_append(const PlanInput& in, const std::vector<int64_t>& lens, int num_c
   // workgroups fit a CU
   int64_t rows_max = 0;
   for (int r = 0; r < B; ++r) rows_max = std::max<int64_t>(rows_max, (int64_t)(qo[r + 1] - qo[r]) * G);
-  // (at head_dim 256 the 4-wave instance holds a CU alone: 8 waves)
-  const int rpw = prefix_rows_per_wave(in.D);
+  // (at head_dim 256 the 4-wave instance holds a CU alone: 8 waves; RoPE
+  // tiles are built with 8 waves only)
+  const bool rope = in.pos_encoding == 1;
+  const int rpw = prefix_rows_per_wave(in.D, rope);
   const int waves =
-      tune_or(in.tune.prefix_waves, rows_max <= 4 * rpw && in.D != 256 ? 4 : 8) == 4 ? 4 : 8;
+      rope ? 8
+           : tune_or(in.tune.prefix_waves, rows_max <= 4 * rpw && in.D != 256 ? 4 : 8) == 4 ? 4
+                                                                                           : 8;
   const int64_t R = (int64_t)rpw * waves;   // rows per tile
   const int64_t slots_per_cu = waves == 4 ? 2 : 1;
   // row tiles: (request, rows [row0, row1), keys needed by the last row)
@@ -323,11 +327,31 @@ int plan_append(const PlanInput& in, const std::vector<int64_t>& lens, int num_c
   off = align256(off + sizeof(MergeUnit) * std::max<size_t>(mu.size(), 1));
   L.qo_indptr_off = off;
   off = align256(off + sizeof(int32_t) * (size_t)(B + 1));
+  // RoPE: query token i of request r (n tokens, L keys) sits at L - n + i
+  // and key t at t; both are turned by those positions
+  if (rope) {
+    out->num_rope_qpos = total_q;
+    out->rope_qpos = (int32_t*)malloc(sizeof(int32_t) * (size_t)std::max<int64_t>(total_q, 1));
+    if (!out->rope_qpos) PLAN_FAIL(1, "out of host memory");
+    for (int r = 0; r < B; ++r) {
+      const int64_t n = (int64_t)qo[r + 1] - qo[r];
+      for (int64_t i = 0; i < n; ++i) out->rope_qpos[qo[r] + i] = (int32_t)(lens[r] - n + i);
+    }
+  }
+  L.rope_qpos_off = off;
+  off = align256(off + sizeof(int32_t) * (size_t)out->num_rope_qpos);
   L.partial_o_off = off;
   off = align256(off + sizeof(float) * (size_t)slots * G * in.D);
   L.partial_lse_off = off;
   off = align256(off + sizeof(float) * (size_t)slots * G);
+  out->rope = rope ? 1 : 0;
+  out->rope_theta = in.rope_theta > 0.f ? in.rope_theta : 1e4f;
+  out->rope_scale = in.rope_scale > 0.f ? in.rope_scale : 1.f;
+  int64_t Lmax = 0;
+  for (int r = 0; r < B; ++r) Lmax = std::max(Lmax, lens[r]);
+  out->rope_rows = rope ? (int32_t)std::max<int64_t>(Lmax, kChunkAlign) : 0;
   L.rope_off = off;
+  off = align256(off + (size_t)rope_row_bytes(in.D) * (size_t)out->rope_rows);
   L.total = off;
   return 0;
 }
@@ -444,33 +468,38 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
     return false;
   };
   const int num_cus = in.num_cus > 0 ? in.num_cus : 256;
-  if (in.append_qo_indptr) {
-    if (NG > 0) PLAN_FAIL(2, "append with a cascade level is not built");
-    if (in.pos_encoding != 0) PLAN_FAIL(2, "append with RoPE is not built");
-    return plan_append(in, lens, num_cus, out, err, errlen);
-  }
   if (in.pos_encoding != 0 && in.pos_encoding != 1)
     PLAN_FAIL(1, "pos_encoding must be FI_POS_NONE or FI_POS_ROPE_LLAMA (got %d)",
               in.pos_encoding);
   const bool rope = in.pos_encoding == 1;
-  if (rope && NG > 0)
-    PLAN_FAIL(2, "RoPE with a cascade level is not built (plain decode only)");
   if (rope && (!(in.rope_theta == in.rope_theta) || !(in.rope_scale == in.rope_scale) ||
                in.rope_theta > 1e30f || in.rope_scale > 1e30f))
     PLAN_FAIL(1, "rope_theta and rope_scale must be finite");
+  if (in.append_qo_indptr) {
+    if (NG > 0) PLAN_FAIL(2, "append with a cascade level is not built");
+    return plan_append(in, lens, num_cus, out, err, errlen);
+  }
+  // RoPE with cascade levels: every key's index in its request's whole key
+  // list (earlier levels, then own pages) must fit the table's int32 rows
+  std::vector<int64_t> total_len(lens);
+  for (int r = 0; r < B; ++r) {
+    for (int l = 0; l < NL; ++l)
+      if (group_of[l][r] >= 0) total_len[r] += plens[l][group_of[l][r]];
+    if (rope && total_len[r] > (int64_t)0x7fffffff - 64)
+      PLAN_FAIL(1, "request %d: its keys over all cascade levels are too many", r);
+  }
 
   // ---- decode chunk length and heads per tile
   const bool hpt_forced = in.tune.heads_per_tile > 0;
   int hpt;
-  int64_t chunk, Lmax = 0;
-  for (int r = 0; r < B; ++r) Lmax = std::max(Lmax, lens[r]);
+  int64_t chunk;
   decode_split(in, num_cus, rope, [&](int r) { return lens[r]; }, &hpt, &chunk);
   // Cascade: a request with prefix states whose suffix is one chunk folds
   // those states into its decode tile's output, so no merge pass is needed.
   // When every such suffix is short (<= tune.fold_max_suffix tokens, default
   // 1024), cover each with one chunk, 2 kv heads per tile (small tiles, two
   // steps of loads in flight), provided that still gives >= 4 waves per CU.
-  const bool fold_ok = in.tune.cascade_fold >= 0;
+  const bool fold_ok = in.tune.cascade_fold >= 0 && !rope;   // no RoPE fold instance
   if (NG > 0 && fold_ok && in.chunk_tokens == 0 && !hpt_forced) {
     int64_t ls_max = 0;
     for (int r = 0; r < B; ++r)
@@ -489,8 +518,10 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   const int64_t head_groups = Hkv / hpt;   // decode tiles per (request, chunk)
 
   // ---- cascade prefix chunking
-  const int prefix_waves = tune_or(in.tune.prefix_waves, kPrefixMaxWaves) == 4 ? 4 : 8;
-  const int64_t prefix_rows = (int64_t)prefix_rows_per_wave(in.D) * prefix_waves;
+  // (RoPE multi-row tiles are built with 8 waves only)
+  const int prefix_waves =
+      rope ? kPrefixMaxWaves : tune_or(in.tune.prefix_waves, kPrefixMaxWaves) == 4 ? 4 : 8;
+  const int64_t prefix_rows = (int64_t)prefix_rows_per_wave(in.D, rope) * prefix_waves;
   int64_t prefix_chunk = 0;
   std::vector<std::vector<int64_t>> n_pchunks(NL);   // [level][group] chunks
   int64_t prefix_row_tiles = 0;  // sum over levels and groups of row tiles x Hkv
@@ -685,6 +716,22 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   off = align256(off + sizeof(int32_t) * (size_t)out->qo_len);
   L.state_off_off = off;
   off = align256(off + sizeof(int32_t) * state_off.size());
+  // RoPE with cascade levels: request r's rows in level l's tiles are turned
+  // by their position counted from the start of that level's prefix
+  if (rope && NL > 0) {
+    out->num_rope_qpos = (int64_t)NL * B;
+    out->rope_qpos = (int32_t*)malloc(sizeof(int32_t) * (size_t)std::max<int64_t>(NL * B, 1));
+    if (!out->rope_qpos) PLAN_FAIL(1, "out of host memory");
+    for (int r = 0; r < B; ++r) {
+      int64_t before = 0;   // keys of the request's earlier levels
+      for (int l = 0; l < NL; ++l) {
+        out->rope_qpos[(size_t)l * B + r] = (int32_t)std::max<int64_t>(total_len[r] - 1 - before, 0);
+        if (group_of[l][r] >= 0) before += plens[l][group_of[l][r]];
+      }
+    }
+  }
+  L.rope_qpos_off = off;
+  off = align256(off + sizeof(int32_t) * (size_t)out->num_rope_qpos);
   L.partial_o_off = off;
   off = align256(off + sizeof(float) * (size_t)slots * G * in.D);
   L.partial_lse_off = off;
@@ -692,8 +739,11 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   out->rope = rope ? 1 : 0;
   out->rope_theta = in.rope_theta > 0.f ? in.rope_theta : 1e4f;
   out->rope_scale = in.rope_scale > 0.f ? in.rope_scale : 1.f;
-  // distances 0 .. Lmax - 1, and at least the 16 rows every tile stages
-  out->rope_rows = rope ? (int32_t)std::max<int64_t>(Lmax, kChunkAlign) : 0;
+  // distances / positions 0 .. (longest key list over all levels) - 1, and
+  // at least the 16 rows every decode tile stages
+  int64_t Ltot = 0;
+  for (int r = 0; r < B; ++r) Ltot = std::max(Ltot, total_len[r]);
+  out->rope_rows = rope ? (int32_t)std::max<int64_t>(Ltot, kChunkAlign) : 0;
   // score path of plain decode: MFMA (default) or the VALU instance
   if (in.tune.score_path == 2) {
     if (rope || NG > 0 || in.D != 128 || G > 4)
@@ -702,8 +752,9 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
     out->valu_heads = G == 1 ? 1 : G == 2 ? 2 : 4;
   }
   // fp16 q: the turned key as one fp16 value when every request is long
-  // enough for its rounding to stay well inside the lse bar
-  if (rope && in.q_dtype == 0) {
+  // enough for its rounding to stay well inside the lse bar (plain decode:
+  // a cascade's multi-row tiles read the fp32 table)
+  if (rope && in.q_dtype == 0 && NL == 0) {
     int64_t shortest = -1;
     for (int r = 0; r < B; ++r)
       if (lens[r] > 0) shortest = shortest < 0 ? lens[r] : std::min(shortest, lens[r]);
@@ -814,6 +865,8 @@ void plan_free(HostPlan* p) {
   free(p->merge_units);
   free(p->qo_indptr);
   free(p->state_off);
+  free(p->rope_qpos);
+  p->rope_qpos = nullptr;
   p->qo_indptr = nullptr;
   p->state_off = nullptr;
   p->tiles = nullptr;

@@ -118,10 +118,11 @@ def _workspace(fi, indptr, last, **kw):
 
 
 def test_rope_plan_rules(fi):
-    """RoPE plans: the mode is validated, a cascade level is refused as not
-    built, non-finite parameters are refused, and the workspace grows by one
-    (cos, sin) table row of 64 fp32 pairs per distance 0 .. longest - 1 (at
-    least 16 rows: every tile stages rows 0..15)."""
+    """RoPE plans: the mode is validated, non-finite parameters are refused,
+    and the workspace grows by one (cos, sin) table row of 64 fp32 pairs per
+    position 0 .. longest key list - 1 (at least 16 rows: every decode tile
+    stages rows 0..15); a cascade plan's table covers the prefix and the
+    suffix together, plus one query position per (level, request)."""
     indptr, last = [0, 2, 5], [3, 16]           # lengths 19 and 48
     assert _status(fi, indptr, last, pos_encoding="rope_llama") == 0
     pr, keep = _problem(fi, indptr, last)
@@ -131,8 +132,13 @@ def test_rope_plan_rules(fi):
     assert "pos_encoding" in fi.lib.fi_last_error().decode()
     prefix = (np.array([0, 2], np.int32), np.array([0, 1], np.int32),
               np.array([16], np.int32))
-    assert _status(fi, indptr, last, pos_encoding="rope_llama", prefix=prefix) == 2
-    assert "RoPE" in fi.lib.fi_last_error().decode()
+    assert _status(fi, indptr, last, pos_encoding="rope_llama", prefix=prefix) == 0
+    st0, ws0 = _workspace(fi, indptr, last, prefix=prefix)
+    st1, ws1 = _workspace(fi, indptr, last, pos_encoding="rope_llama", prefix=prefix)
+    assert st0 == 0 and st1 == 0
+    # (16 + 48 keys) x 512 B of table, the positions (256-B aligned), and
+    # the partial states the fold no longer saves (RoPE plans merge)
+    assert 64 * 512 + 256 <= ws1 - ws0
     assert _status(fi, indptr, last, pos_encoding="rope_llama", rope_theta=float("nan")) == 1
     assert _status(fi, indptr, last, pos_encoding="rope_llama", rope_scale=float("inf")) == 1
     st0, ws0 = _workspace(fi, indptr, last)
@@ -397,8 +403,9 @@ def test_append_plan_rules(fi):
         pr.qo_indptr = q_bad.ctypes.data
         assert fi.lib.fi_debug_plan_tiles(ctypes.byref(pr), 256, None, 0, ctypes.byref(n)) == 1
     pr.qo_indptr = q_ok.ctypes.data
-    pr.pos_encoding = 1
-    assert fi.lib.fi_debug_plan_tiles(ctypes.byref(pr), 256, None, 0, ctypes.byref(n)) == 2
+    pr.pos_encoding = 1                               # RoPE append: 8-wave, 128-row tiles
+    assert fi.lib.fi_debug_plan_tiles(ctypes.byref(pr), 256, None, 0, ctypes.byref(n)) == 0
+    pr.pos_encoding = 0
     prefix = (np.array([0, 2], np.int32), np.array([0, 1], np.int32), np.array([16], np.int32))
     pr2, keep2 = _problem(fi, ip, la, prefix=prefix)
     pr2.qo_indptr, pr2.causal = q_ok.ctypes.data, 1

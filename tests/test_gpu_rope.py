@@ -82,10 +82,153 @@ def test_rope_split_equals_unsplit(fi):
     assert np.abs(o0 - o1).max() < 2e-3 and np.abs(l0 - l1).max() < 1e-4
 
 
-def test_rope_cascade_plan_is_rejected(fi):
+# ---- RoPE on the multi-row kernel: cascade levels and batch append ---------
+# The oracle rotates q and every key by their positions in the request's
+# whole key list (cascade: the group's prefix tokens first, then the own
+# tokens; append: query token i of n at L - n + i).  The prefix / append
+# tiles turn each query row by its position relative to the start of the
+# tile's key list and each key by its index there, in fp32, and carry both
+# as a 16-bit high part plus residual through three score MFMAs.
+
+
+@pytest.mark.parametrize("chunk", [0, 32])
+def test_small_cascade_rope_parity(fi, chunk):
+    rope = (1e4, 1.0)
     w = W.make("cascade256", small=True)
-    with pytest.raises(RuntimeError, match="RoPE"):
-        C.make_plan(w, rope=(1e4, 1.0))
+    o, lse, plan = C.run_gpu(w, chunk_tokens=chunk, rope=rope)
+    assert plan.stats["num_prefix_tiles"] > 0 and plan.stats["num_folded"] == 0
+    ro, rl = C.run_oracle(w, rope=rope)
+    C.assert_parity(w, o, lse, ro, rl, label=f"cascade rope chunk {chunk} {plan.stats}")
+    po, _ = C.run_oracle(w)
+    assert np.abs(po - ro).max() > 10 * (C.TOL_ABS + C.TOL_REL), "RoPE had no effect"
+
+
+def _cascade_rope_case(seed):
+    rng = np.random.default_rng(7300 + seed)
+    ps = int(rng.choice([1, 3, 16]))
+    G = int(rng.choice([1, 4, 8]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    D = [64, 128, 256][seed % 3]
+    groups, B = [], 0
+    for _ in range(int(rng.integers(1, 4))):
+        nr = int(rng.integers(1, 5))
+        plen = int(rng.choice([1, 2, 5, ps + 1, 40, int(rng.integers(60, 700))]))
+        groups.append((nr, plen))
+        B += nr
+    lens = [int(rng.choice([0, 1, 3, ps + 1, int(rng.integers(2, 400))])) for _ in range(B)]
+    q_dtype = str(rng.choice(["f16", "bf16"]))
+    kv_dtype = str(rng.choice([q_dtype, "e4m3"]))
+    rope = (float(rng.choice([1e4, 5e5])), float(rng.choice([1.0, 8.0, 0.5])))
+    w = W.build(f"rope_cascade{seed}", lens, Hq=Hkv * G, Hkv=Hkv, D=D, ps=ps, q_dtype=q_dtype,
+                kv_dtype=kv_dtype, seed=seed, prefix_groups=groups)
+    return w, rope, groups
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_cascade_rope_fuzz_parity(fi, seed):
+    w, rope, groups = _cascade_rope_case(seed)
+    chunk = [0, 32, 48][seed % 3]
+    o, lse, plan = C.run_gpu(w, chunk_tokens=chunk, rope=rope)
+    ro, rl = C.run_oracle(w, rope=rope)
+    C.assert_parity(w, o, lse, ro, rl,
+                    label=f"cascade rope fuzz{seed} {rope} D{w.head_dim} G{w.group_size} "
+                          f"Hkv{w.num_kv_heads} ps{w.page_size} {w.q_dtype}/{w.kv_dtype} "
+                          f"groups {groups} lens {list(w.kv_lens)} {plan.stats}")
+
+
+def test_cascade_rope_equals_flat_rope(fi):
+    """A cascade with RoPE computes what flat RoPE decode of the concatenated
+    key lists does (prefix at positions 0.., the own tokens after it)."""
+    rope = (1e4, 1.0)
+    w = W.make("cascade256", small=True)
+    flat = W.flatten_cascade(w)
+    o1, l1, _ = C.run_gpu(w, rope=rope)
+    o2, l2, _ = C.run_gpu(flat, rope=rope)
+    assert np.abs(o1 - o2).max() < C.TOL_ABS and np.abs(l1 - l2).max() < C.TOL_LSE
+
+
+def _append_rope_run(w, rope, chunk_tokens=0):
+    import paged_kv_decode_fi_amd as m
+    import torch
+    d = C.Dev(w)
+    plan = m.Plan(w.kv_indptr, w.last_page_len, num_qo_heads=w.num_qo_heads,
+                  num_kv_heads=w.num_kv_heads, page_size=w.page_size, head_dim=w.head_dim,
+                  q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, chunk_tokens=chunk_tokens,
+                  qo_indptr=w.qo_indptr, causal=w.causal, pos_encoding="rope_llama",
+                  rope_theta=rope[0], rope_scale=rope[1])
+    o = torch.full((w.num_rows, w.num_qo_heads, w.head_dim), float("nan"), dtype=C.qdtype(w),
+                   device="cuda")
+    lse = torch.full((w.num_rows, w.num_qo_heads), float("nan"), dtype=torch.float32,
+                     device="cuda")
+    plan.append_run(d.q, d.k, d.v, d.indptr, d.indices, d.last, d.k_scale, d.v_scale,
+                    sm_scale=w.sm_scale, o=o, lse=lse)
+    torch.cuda.synchronize()
+    return o.float().cpu().double().numpy(), lse.cpu().double().numpy(), plan
+
+
+def _append_rope_oracle(w, rope):
+    import oracle
+    return oracle.append(w.q, w.k_pages, w.v_pages, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                         w.last_page_len, num_qo_heads=w.num_qo_heads,
+                         num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                         page_size=w.page_size, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
+                         sm_scale=w.sm_scale, causal=w.causal, k_scale=w.k_scale,
+                         v_scale=w.v_scale, rope=rope)
+
+
+@pytest.mark.parametrize("name", W.APPEND_WORKLOADS)
+def test_small_append_rope_parity(fi, name):
+    rope = (1e4, 1.0)
+    w = W.make_append(name, small=True)
+    o, lse, plan = _append_rope_run(w, rope)
+    ro, rl = _append_rope_oracle(w, rope)
+    rows = np.ones((w.num_rows, w.num_qo_heads), bool)
+    C.assert_parity(w, o, lse, ro, rl, rows=rows, label=f"{w.name} rope {plan.stats}")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_append_rope_fuzz_parity(fi, seed):
+    rng = np.random.default_rng(7600 + seed)
+    ps = int(rng.choice([1, 3, 16]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    D = [64, 128, 256][seed % 3]
+    B = int(rng.integers(1, 6))
+    lens = rng.integers(1, 500, size=B)
+    kind = rng.integers(0, 4, size=B)
+    q_lens = np.where(kind == 0, 1, np.where(kind == 1, lens,
+                      np.where(kind == 2, rng.integers(1, lens + 1), 0)))
+    q_dtype = str(rng.choice(["f16", "bf16"]))
+    kv_dtype = str(rng.choice([q_dtype, "e4m3"]))
+    causal = bool(rng.integers(0, 4) != 0)
+    rope = (float(rng.choice([1e4, 5e5])), float(rng.choice([1.0, 8.0, 0.5])))
+    w = W.build_append(f"append_rope{seed}", lens, q_lens, Hq=Hkv * G, Hkv=Hkv, D=D, ps=ps,
+                       q_dtype=q_dtype, kv_dtype=kv_dtype, seed=seed, causal=causal)
+    chunk = [0, 32, 96][seed % 3]
+    o, lse, plan = _append_rope_run(w, rope, chunk_tokens=chunk)
+    ro, rl = _append_rope_oracle(w, rope)
+    rows = np.ones((w.num_rows, w.num_qo_heads), bool)
+    C.assert_parity(w, o, lse, ro, rl, rows=rows,
+                    label=f"append rope fuzz{seed} {rope} causal={causal} D{D} G{G} Hkv{Hkv} "
+                          f"ps{ps} {q_dtype}/{kv_dtype} lens {list(lens)} q {list(q_lens)}")
+
+
+def test_one_token_rope_append_equals_rope_decode(fi):
+    """A one-token causal append with RoPE is RoPE decode (the query at the
+    last position): the multi-row kernel's absolute turns and the decode
+    kernel's relative turns agree within the bar."""
+    rope = (1e4, 1.0)
+    w = W.make("batch64_gqa4", small=True)
+    wa = W.build_append("rope_append_as_decode", w.kv_lens, np.ones(w.batch, np.int64),
+                        Hq=32, Hkv=8, ps=16, seed=1001)
+    wa.q = w.q.copy()
+    wa.k_pages, wa.v_pages = w.k_pages, w.v_pages
+    wa.kv_indptr, wa.kv_indices, wa.last_page_len = w.kv_indptr, w.kv_indices, w.last_page_len
+    o, lse, _ = _append_rope_run(wa, rope)
+    od, ld, _ = C.run_gpu(w, rope=rope)
+    ro, rl = C.run_oracle(w, rope=rope)
+    C.assert_parity(w, o, lse, ro, rl, label="one-token rope append")
+    C.assert_parity(w, od, ld, ro, rl, label="rope decode")
 
 
 @pytest.mark.parametrize("case", range(8))
