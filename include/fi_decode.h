@@ -61,8 +61,8 @@
  *
  * Supported: head_dim 64, 128 or 256; q in fp16 or bf16;
  * KV in the q dtype or OCP E4M3 (e4m3fn); 1 <= num_qo_heads / num_kv_heads
- * <= 16; any page_size >= 1; LLaMA-style RoPE on the fly for plain decode;
- * batch append (causal or not) on the same page tables.
+ * <= 16; any page_size >= 1; LLaMA-style RoPE on the fly (decode, cascade
+ * levels and append); batch append (causal or not) on the same page tables.
  */
 #ifndef FI_DECODE_H_
 #define FI_DECODE_H_
@@ -164,9 +164,11 @@ typedef struct {
    * FI_POS_ROPE_LLAMA, LLaMA-style RoPE applied on the fly to q and to the
    * cached (unrotated) keys: rotate-half over head_dim, the pair
    * (x_i, x_{i+D/2}) turned by angle_i = pos / rope_scale *
-   * rope_theta^(-2 i / D); key t of a request sits at position t, the query
-   * at kv_len - 1.  Plain decode only (a cascade plan with RoPE is
-   * FI_ERR_UNSUPPORTED). */
+   * rope_theta^(-2 i / D); key t of a request's key list sits at position
+   * t (with cascade levels: the groups' prefixes, outermost first, then the
+   * request's own keys), the query at (number of keys) - 1; append query i
+   * of n at kv_len - n + i.  A cascade plan with RoPE merges its prefix
+   * states in a separate pass (no fold). */
   int32_t pos_encoding;
   float rope_theta;       /* <= 0: 1e4 */
   float rope_scale;       /* <= 0: 1 */
@@ -178,8 +180,9 @@ typedef struct {
    * n_r = qo_indptr[r+1] - qo_indptr[r] <= kv_len_r tokens of its keys:
    * query i sits at position kv_len_r - n_r + i and, with causal != 0,
    * attends keys 0 .. kv_len_r - n_r + i (all kv_len_r keys otherwise).
-   * Run with fi_append_run.  Not combined with a cascade level or RoPE
-   * (FI_ERR_UNSUPPORTED).  NULL = decode (one query per request). */
+   * Run with fi_append_run.  Not combined with a cascade level
+   * (FI_ERR_UNSUPPORTED); RoPE applies (above).  NULL = decode (one query
+   * per request). */
   const int32_t* qo_indptr;   /* host [B+1], [0] = 0, non-decreasing, or NULL */
   int32_t causal;
   /* KV layout (README "core features" item 1: paged and ragged KV cache):

@@ -280,8 +280,8 @@ class Plan:
     torch CPU).  prefix = (prefix_qo_indptr, prefix_kv_indptr,
     prefix_last_page_len) host arrays for cascade decoding.  head_dim: 64,
     128 or 256.  pos_encoding = "rope_llama" applies LLaMA-style RoPE to q
-    and the keys on the fly, plain decode plans (rope_theta / rope_scale
-    <= 0: 1e4 / 1).  qo_indptr (host [B+1]) makes an
+    and the keys on the fly, in decode, cascade and append plans
+    (rope_theta / rope_scale <= 0: 1e4 / 1).  qo_indptr (host [B+1]) makes an
     append plan: request r's query tokens qo_indptr[r] .. qo_indptr[r+1]-1
     are the last ones of its keys (causal mask unless causal=False); run it
     with Plan.append_run.  kv_layout="ragged": each request's tokens are
