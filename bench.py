@@ -46,15 +46,16 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0      # dense bf16 / fp16 MFMA
 ROTATE_BYTES = 1 << 30          # >= 1 GiB referenced per rotation cycle
-DECODE_SRC = os.path.join(ROOT, "paged_kv_decode_fi_amd", "csrc", "decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SRCS = [DECODE_SRC] + [os.path.join(ROOT, "paged_kv_decode_fi_amd", "csrc", f)
-                              for f in ("fi_device.h", "fi_internal.h")]
+KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_decode_fi_amd", "csrc", f)
+               for f in ("decode.hip", "fi_prefix.h", "prefix.hip", "prefix_rope.hip",
+                         "fi_device.h", "fi_internal.h")]
 
 
 def kernel_source_hash() -> str:
-    """sha256[:16] of the kernels' code (decode.hip and the two headers it
-    includes): every line with its // comment and trailing blanks removed,
+    """sha256[:16] of the decode and multi-row kernels' code (decode.hip,
+    fi_prefix.h, prefix.hip, prefix_rope.hip and the two headers they
+    include): every line with its // comment and trailing blanks removed,
     blank lines dropped -- a comment edit keeps the hash, any change to the
     code does not."""
     import hashlib
