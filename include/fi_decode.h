@@ -108,7 +108,7 @@ typedef struct {
   int32_t heads_per_tile;       /* kv heads per decode workgroup: 1, 2, 4 or 8 */
   int32_t waves_per_cu;         /* decode waves the chunk search targets per CU (16) */
   int32_t chunk_min;            /* smallest decode chunk, tokens (32) */
-  int32_t prefix_waves;         /* waves per multi-row tile: 4 or 8 */
+  int32_t prefix_waves;         /* waves per multi-row tile: 4 or 8 (RoPE: 8) */
   int32_t prefix_tiles_per_cu;  /* cascade prefix tiles per CU (1) */
   int32_t prefix_chunk_min;     /* smallest cascade prefix chunk, tokens (256) */
   int32_t cascade_fold;         /* 0/1: a one-chunk suffix tile folds its prefix
