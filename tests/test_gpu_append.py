@@ -21,19 +21,22 @@ def fi():
     return m
 
 
-def _plan(w, chunk_tokens=0, num_cus=0):
+def _plan(w, chunk_tokens=0, num_cus=0, rope=None):
     import paged_kv_decode_fi_amd as fi
     return fi.Plan(w.kv_indptr, w.last_page_len, num_qo_heads=w.num_qo_heads,
                    num_kv_heads=w.num_kv_heads, page_size=w.page_size, head_dim=w.head_dim,
                    q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, chunk_tokens=chunk_tokens,
-                   num_cus=num_cus, qo_indptr=w.qo_indptr, causal=w.causal)
+                   num_cus=num_cus, qo_indptr=w.qo_indptr, causal=w.causal,
+                   pos_encoding="none" if rope is None else "rope_llama",
+                   rope_theta=0.0 if rope is None else rope[0],
+                   rope_scale=0.0 if rope is None else rope[1])
 
 
-def _run(w, plan=None, chunk_tokens=0, num_cus=0):
+def _run(w, plan=None, chunk_tokens=0, num_cus=0, rope=None):
     """Outputs pre-filled with NaN, so an unwritten row shows."""
     import torch
     d = C.Dev(w)
-    plan = plan or _plan(w, chunk_tokens, num_cus)
+    plan = plan or _plan(w, chunk_tokens, num_cus, rope)
     o = torch.full((w.num_rows, w.num_qo_heads, w.head_dim), float("nan"), dtype=C.qdtype(w),
                    device="cuda")
     lse = torch.full((w.num_rows, w.num_qo_heads), float("nan"), dtype=torch.float32,
@@ -44,14 +47,14 @@ def _run(w, plan=None, chunk_tokens=0, num_cus=0):
     return o.float().cpu().double().numpy(), lse.cpu().double().numpy(), plan
 
 
-def _oracle(w, unit_mask=None):
+def _oracle(w, unit_mask=None, rope=None):
     import oracle
     return oracle.append(w.q, w.k_pages, w.v_pages, w.qo_indptr, w.kv_indptr, w.kv_indices,
                          w.last_page_len, num_qo_heads=w.num_qo_heads,
                          num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
                          page_size=w.page_size, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
                          sm_scale=w.sm_scale, causal=w.causal, k_scale=w.k_scale,
-                         v_scale=w.v_scale, unit_mask=unit_mask)
+                         v_scale=w.v_scale, unit_mask=unit_mask, rope=rope)
 
 
 def _compare(w, o, lse, ro, rl, rows=None, label=""):
@@ -138,9 +141,9 @@ def test_append_planted_key_under_the_mask(fi):
 
 @pytest.mark.parametrize("head_dim", [128, 64, 256])
 @pytest.mark.parametrize("name", W.APPEND_WORKLOADS)
-def test_full_size_append_sampled_parity(fi, name, head_dim):
+def test_full_size_append_sampled_parity(fi, name, head_dim, rope=None):
     w = W.make_append(name, head_dim=head_dim)
-    o, lse, plan = _run(w)
+    o, lse, plan = _run(w, rope=rope)
     st = plan.stats
     print(f"{w.name}: tiles {st['num_prefix_tiles']} merge units {st['num_merge_units']} "
           f"chunk {st['prefix_chunk_tokens']}", flush=True)
@@ -155,7 +158,7 @@ def test_full_size_append_sampled_parity(fi, name, head_dim):
     free = np.flatnonzero(flat == 0)
     if free.size:
         flat[rng.choice(free, size=min(8, free.size), replace=False)] = 1
-    ro, rl = _oracle(w, unit_mask=flat)
+    ro, rl = _oracle(w, unit_mask=flat, rope=rope)
     G = w.group_size
     rows = np.zeros((w.num_rows, w.num_qo_heads), bool)
     for r in range(B):
@@ -164,3 +167,10 @@ def test_full_size_append_sampled_parity(fi, name, head_dim):
                 rows[w.qo_indptr[r]:w.qo_indptr[r + 1], h * G:(h + 1) * G] = True
     _compare(w, o, lse, ro, rl, rows=rows, label=f"{w.name} full size, sampled units")
     plan.destroy()
+
+
+@pytest.mark.parametrize("name", W.APPEND_WORKLOADS)
+def test_full_size_append_rope_sampled_parity(fi, name):
+    """The append workloads at full size with LLaMA-style RoPE (query token i
+    of n at L - n + i), in the benchmark's launch configuration."""
+    test_full_size_append_sampled_parity(fi, name, 128, rope=(1e4, 1.0))

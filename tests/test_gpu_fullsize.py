@@ -106,10 +106,12 @@ def test_full_size_long_fp8_sampled_parity(fi_lib, ps):
     _check(ws[ps], f"long32_fp8_ps{ps}", n_random=8)
 
 
-@pytest.mark.parametrize("name", ["batch64_gqa4", "skewed128"])
+@pytest.mark.parametrize("name", ["batch64_gqa4", "skewed128", "cascade256"])
 def test_full_size_rope_sampled_parity(fi_lib, name):
     """The same launches with LLaMA-style RoPE on the fly (skewed128 reaches
-    position 32767 and splits those requests over many tiles)."""
+    position 32767 and splits those requests over many tiles; cascade256
+    turns the shared prefix's keys and the query rows by their positions on
+    the multi-row kernel)."""
     _check(_workload(name), name + "_rope", n_random=12, rope=(1e4, 1.0))
 
 

@@ -1,7 +1,7 @@
 """Graph capture of every run entry point beyond plain decode and the
 single-level cascade (those two are covered with the parity suite): append,
-RoPE decode, cascades of several levels, head_dim 64 and 256, the ragged
-layout.  The run stage only enqueues kernels (FlashInfer README core
+RoPE decode, RoPE cascade and append, cascades of several levels, head_dim 64
+and 256, the ragged layout.  The run stage only enqueues kernels (FlashInfer README core
 features, graph-capturable run stage), so each call is captured once and
 replayed several times with eager work and synchronisations in between;
 every replay must equal the eager result bit for bit."""
@@ -72,6 +72,29 @@ def test_rope_decode_graph(fi):
     ro, rl = C.run_oracle(w, rope=(1e4, 1.0))
     C.assert_parity(w, o.float().cpu().double().numpy(), lse.cpu().double().numpy(), ro, rl,
                     label="RoPE decode, graph")
+
+
+def test_rope_cascade_and_append_graph(fi):
+    """RoPE on the multi-row kernel (cascade prefix tiles with their query
+    positions, then the RoPE suffix decode and the merge; an append plan)."""
+    rope = (1e4, 1.0)
+    w = W.make("cascade256", small=True)
+    d = C.Dev(w)
+    plan = C.make_plan(w, rope=rope)
+    o, lse = _check_graph(lambda o, lse: plan.cascade_run(
+        d.q, d.k, d.v, d.p_indptr, d.p_indices, d.p_last, d.indptr, d.indices, d.last,
+        sm_scale=w.sm_scale, o=o, lse=lse))
+    ro, rl = C.run_oracle(w, rope=rope)
+    C.assert_parity(w, o.float().cpu().double().numpy(), lse.cpu().double().numpy(), ro, rl,
+                    label="RoPE cascade, graph")
+    wa = W.make_append("append_batch16_q128", small=True)
+    da = C.Dev(wa)
+    pa = fi.Plan(wa.kv_indptr, wa.last_page_len, num_qo_heads=wa.num_qo_heads,
+                 num_kv_heads=wa.num_kv_heads, page_size=wa.page_size, q_dtype=wa.q_dtype,
+                 kv_dtype=wa.kv_dtype, qo_indptr=wa.qo_indptr, causal=wa.causal,
+                 pos_encoding="rope_llama", rope_theta=rope[0], rope_scale=rope[1])
+    _check_graph(lambda o, lse: pa.append_run(da.q, da.k, da.v, da.indptr, da.indices,
+                                              da.last, sm_scale=wa.sm_scale, o=o, lse=lse))
 
 
 def test_cascade_levels_graph(fi):
