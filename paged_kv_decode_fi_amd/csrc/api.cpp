@@ -23,6 +23,8 @@
 namespace fi {
 hipError_t launch_decode(const DecodeParams& p, int num_tiles, int waves, bool q_bf16,
                          int kv, bool fold, int depth, int head_dim, hipStream_t s);
+hipError_t decode_occupancy(const DecodeParams& p, int waves, bool q_bf16, int kv, bool fold,
+                            int depth, int head_dim, int* blocks);
 hipError_t launch_prefix(const DecodeParams& p, int num_tiles, int waves, bool append,
                          bool split, bool q_bf16, int kv, int head_dim, hipStream_t s);
 hipError_t launch_merge_partials(const MergeParams& p, int num_units, bool o_bf16, bool wide,
@@ -224,14 +226,52 @@ fi::PlanInput to_input(const fi_problem* p, int num_cus) {
   return in;
 }
 
-fi_status build_host_plan(const fi_problem* problem, int num_cus, fi::HostPlan* hp) {
+// Waves per compute unit that the current device holds at once of the decode
+// instance a plan of *ctx (an fi_problem) launches with tiles of hpt kv heads
+// (PlanInput::resident_waves); 0 when there is no device or the problem's
+// fields are out of range (the plan validates them itself).
+int resident_decode_waves(const void* ctx, int hpt, int rope_form, int fold) {
+  const fi_problem* pr = static_cast<const fi_problem*>(ctx);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (pr->q_dtype != FI_F16 && pr->q_dtype != FI_BF16) return 0;
+  const bool ragged = pr->kv_layout == FI_KV_RAGGED;
+  const int ps = ragged ? 1 : pr->page_size;
+  if (ps < 1) return 0;
+  fi::DecodeParams p;
+  memset(&p, 0, sizeof(p));
+  p.ps_shift = ps_shift_of(ps);
+  static const float kTableStandIn = 0.f;   // selects the RoPE instances only
+  p.rope_table = rope_form ? &kTableStandIn : nullptr;
+  p.rope_single = rope_form == 2 ? 1 : 0;
+  const bool qbf = pr->q_dtype == FI_BF16;
+  const int kv = pr->kv_dtype == FI_E4M3 ? 2 : (qbf ? 1 : 0);
+  const int depth = pr->tuning ? pr->tuning->decode_depth : 0;
+  int blocks = 0;
+  if (fi::decode_occupancy(p, hpt, qbf, kv, fold != 0, depth, pr->head_dim, &blocks) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return blocks * hpt;
+}
+
+// device_occupancy: size the decode wave target by what the current device
+// holds of the instance (fi_plan); the test hook plans without it.
+fi_status build_host_plan(const fi_problem* problem, int num_cus, fi::HostPlan* hp,
+                          bool device_occupancy = false) {
   if (!problem) return fail(FI_ERR_INVALID_ARG, "problem is NULL");
   fi_status st = check_dtypes(problem->q_dtype, problem->kv_dtype);
   if (st != FI_OK) return st;
   char err[256] = {0};
   int rc;
   try {   // no exception crosses the C ABI
-    rc = fi::plan_build(to_input(problem, num_cus), hp, err, sizeof(err));
+    fi::PlanInput in = to_input(problem, num_cus);
+    if (device_occupancy) {
+      in.resident_waves = resident_decode_waves;
+      in.resident_ctx = problem;
+    }
+    rc = fi::plan_build(in, hp, err, sizeof(err));
   } catch (const std::bad_alloc&) {
     fi::plan_free(hp);
     return fail(FI_ERR_INVALID_ARG, "out of host memory while planning");
@@ -334,7 +374,7 @@ fi_status fi_plan(const fi_problem* problem, int32_t num_cus, void* workspace,
     num_cus = cus;
   }
   fi::HostPlan hp;
-  fi_status st = build_host_plan(problem, num_cus, &hp);
+  fi_status st = build_host_plan(problem, num_cus, &hp, true);
   if (st != FI_OK) return st;
   if (workspace_needed) *workspace_needed = hp.layout.total;
   if (!workspace) {
@@ -739,8 +779,10 @@ fi_status fi_decode_noalloc(const fi_problem* problem, const void* q, const void
   if (e != hipSuccess) return hip_fail(e, "querying the compute unit count");
   fi_plan_s pl;   // on the stack: the plan's sizes, its work list in scratch
   char err[320] = {0};
-  const int rc = fi::plan_decode_static(to_input(problem, num_cus), fi::scratch_capacity(),
-                                        &pl.hp, err, sizeof(err));
+  fi::PlanInput in = to_input(problem, num_cus);
+  in.resident_waves = resident_decode_waves;
+  in.resident_ctx = problem;
+  const int rc = fi::plan_decode_static(in, fi::scratch_capacity(), &pl.hp, err, sizeof(err));
   if (rc != 0) return fail(rc == 2 ? FI_ERR_UNSUPPORTED : FI_ERR_INVALID_ARG, "%s", err);
   const fi::HostPlan& hp = pl.hp;
   if (hp.batch == 0) return FI_OK;

@@ -763,9 +763,12 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
 
 constexpr int kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
 
+// occ != NULL: nothing is launched; *occ receives the workgroups of this
+// instance that one compute unit holds at once (the same kernel, block size
+// and dynamic LDS as the launch).
 template <int KV, bool QBF16, bool FOLD, int DEPTH, int ROPE, int D>
 static hipError_t launch_decode_t(const DecodeParams& p, int num_tiles, int waves,
-                                  hipStream_t s) {
+                                  hipStream_t s, int* occ = nullptr) {
   constexpr int rope_lds = ROPE == 2 ? RopeLds<D>::BYTES16 : ROPE ? RopeLds<D>::BYTES : 0;
   const size_t lds = (size_t)Stage<KV, D>::lds_bytes(waves) + rope_lds;
   // (head_dim 256 with RoPE: at most 4 kv heads per tile fit)
@@ -783,6 +786,12 @@ static hipError_t launch_decode_t(const DecodeParams& p, int num_tiles, int wave
     return e;
   }();
   if (attr != hipSuccess) return attr;
+  if (occ)
+    return p.ps_shift >= 0
+               ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                     occ, decode_kernel<KV, QBF16, true, FOLD, DEPTH, ROPE, D>, 64 * waves, lds)
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                     occ, decode_kernel<KV, QBF16, false, FOLD, DEPTH, ROPE, D>, 64 * waves, lds);
   if (p.ps_shift >= 0)
     hipLaunchKernelGGL((decode_kernel<KV, QBF16, true, FOLD, DEPTH, ROPE, D>), dim3(num_tiles),
                        dim3(64 * waves), lds, s, p);
@@ -803,18 +812,19 @@ static hipError_t launch_decode_t(const DecodeParams& p, int num_tiles, int wave
 // (registers).
 template <int KV, bool QBF16, int ROPE, int D>
 static hipError_t launch_decode_rope(const DecodeParams& p, int num_tiles, int waves, int depth,
-                                     hipStream_t s) {
+                                     hipStream_t s, int* occ) {
   if constexpr (D == 128) {
-    if (depth != 1) return launch_decode_t<KV, QBF16, false, 2, ROPE, D>(p, num_tiles, waves, s);
+    if (depth != 1)
+      return launch_decode_t<KV, QBF16, false, 2, ROPE, D>(p, num_tiles, waves, s, occ);
   }
-  return launch_decode_t<KV, QBF16, false, 1, ROPE, D>(p, num_tiles, waves, s);
+  return launch_decode_t<KV, QBF16, false, 1, ROPE, D>(p, num_tiles, waves, s, occ);
 }
 
 // VALU instances (plain plans, head_dim 128, one step of loads in flight):
 // vg = 1, 2 or 4 q heads per kv head at most.
 template <int KV, bool QBF16, int VG>
 static hipError_t launch_decode_valu_t(const DecodeParams& p, int num_tiles, int waves,
-                                       hipStream_t s) {
+                                       hipStream_t s, int* occ) {
   const size_t lds = (size_t)Stage<KV, 128>::lds_bytes(waves);
   static const hipError_t attr = [] {
     const int max_lds = Stage<KV, 128>::lds_bytes(kWavesPerTile);
@@ -829,6 +839,14 @@ static hipError_t launch_decode_valu_t(const DecodeParams& p, int num_tiles, int
     return e;
   }();
   if (attr != hipSuccess) return attr;
+  if (occ)
+    return p.ps_shift >= 0
+               ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                     occ, decode_kernel<KV, QBF16, true, false, 1, 0, 128, false, VG>,
+                     64 * waves, lds)
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                     occ, decode_kernel<KV, QBF16, false, false, 1, 0, 128, false, VG>,
+                     64 * waves, lds);
   if (p.ps_shift >= 0)
     hipLaunchKernelGGL((decode_kernel<KV, QBF16, true, false, 1, 0, 128, false, VG>),
                        dim3(num_tiles), dim3(64 * waves), lds, s, p);
@@ -840,22 +858,23 @@ static hipError_t launch_decode_valu_t(const DecodeParams& p, int num_tiles, int
 
 template <int KV, bool QBF16>
 static hipError_t launch_decode_valu(const DecodeParams& p, int num_tiles, int waves,
-                                     hipStream_t s) {
+                                     hipStream_t s, int* occ) {
   switch (p.valu_heads) {
-    case 1: return launch_decode_valu_t<KV, QBF16, 1>(p, num_tiles, waves, s);
-    case 2: return launch_decode_valu_t<KV, QBF16, 2>(p, num_tiles, waves, s);
-    case 4: return launch_decode_valu_t<KV, QBF16, 4>(p, num_tiles, waves, s);
+    case 1: return launch_decode_valu_t<KV, QBF16, 1>(p, num_tiles, waves, s, occ);
+    case 2: return launch_decode_valu_t<KV, QBF16, 2>(p, num_tiles, waves, s, occ);
+    case 4: return launch_decode_valu_t<KV, QBF16, 4>(p, num_tiles, waves, s, occ);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int KV, bool QBF16, int D>
 static hipError_t launch_decode_f(const DecodeParams& p, int num_tiles, int waves, bool fold,
-                                  int depth, hipStream_t s) {
-  if (num_tiles <= 0) return hipSuccess;
+                                  int depth, hipStream_t s, int* occ) {
+  if (num_tiles <= 0 && !occ) return hipSuccess;
   if (p.valu_heads > 0) {
     if constexpr (D == 128) {
-      if (!fold && !p.rope_table) return launch_decode_valu<KV, QBF16>(p, num_tiles, waves, s);
+      if (!fold && !p.rope_table)
+        return launch_decode_valu<KV, QBF16>(p, num_tiles, waves, s, occ);
     }
     return hipErrorInvalidValue;
   }
@@ -863,31 +882,32 @@ static hipError_t launch_decode_f(const DecodeParams& p, int num_tiles, int wave
     // the rotated key as one 16-bit value (fp16 q only) or a high part plus
     // a residual
     if constexpr (!QBF16) {
-      if (p.rope_single) return launch_decode_rope<KV, QBF16, 2, D>(p, num_tiles, waves, depth, s);
+      if (p.rope_single)
+        return launch_decode_rope<KV, QBF16, 2, D>(p, num_tiles, waves, depth, s, occ);
     }
-    return launch_decode_rope<KV, QBF16, 1, D>(p, num_tiles, waves, depth, s);
+    return launch_decode_rope<KV, QBF16, 1, D>(p, num_tiles, waves, depth, s, occ);
   }
   if constexpr (D == 256) {
-    return fold ? launch_decode_t<KV, QBF16, true, 1, 0, D>(p, num_tiles, waves, s)
-                : launch_decode_t<KV, QBF16, false, 1, 0, D>(p, num_tiles, waves, s);
+    return fold ? launch_decode_t<KV, QBF16, true, 1, 0, D>(p, num_tiles, waves, s, occ)
+                : launch_decode_t<KV, QBF16, false, 1, 0, D>(p, num_tiles, waves, s, occ);
   } else {
     const bool deep = depth == 2 || (depth == 0 && fold && waves <= 4);
     if (fold)
-      return deep ? launch_decode_t<KV, QBF16, true, 2, 0, D>(p, num_tiles, waves, s)
-                  : launch_decode_t<KV, QBF16, true, 1, 0, D>(p, num_tiles, waves, s);
-    return deep ? launch_decode_t<KV, QBF16, false, 2, 0, D>(p, num_tiles, waves, s)
-                : launch_decode_t<KV, QBF16, false, 1, 0, D>(p, num_tiles, waves, s);
+      return deep ? launch_decode_t<KV, QBF16, true, 2, 0, D>(p, num_tiles, waves, s, occ)
+                  : launch_decode_t<KV, QBF16, true, 1, 0, D>(p, num_tiles, waves, s, occ);
+    return deep ? launch_decode_t<KV, QBF16, false, 2, 0, D>(p, num_tiles, waves, s, occ)
+                : launch_decode_t<KV, QBF16, false, 1, 0, D>(p, num_tiles, waves, s, occ);
   }
 }
 
 template <int D>
 static hipError_t launch_decode_d(const DecodeParams& p, int num_tiles, int waves, bool q_bf16,
-                                  int kv, bool fold, int depth, hipStream_t s) {
+                                  int kv, bool fold, int depth, hipStream_t s, int* occ) {
   if (kv == kKvE4M3)
-    return q_bf16 ? launch_decode_f<kKvE4M3, true, D>(p, num_tiles, waves, fold, depth, s)
-                  : launch_decode_f<kKvE4M3, false, D>(p, num_tiles, waves, fold, depth, s);
-  return q_bf16 ? launch_decode_f<kKvBF16, true, D>(p, num_tiles, waves, fold, depth, s)
-                : launch_decode_f<kKvF16, false, D>(p, num_tiles, waves, fold, depth, s);
+    return q_bf16 ? launch_decode_f<kKvE4M3, true, D>(p, num_tiles, waves, fold, depth, s, occ)
+                  : launch_decode_f<kKvE4M3, false, D>(p, num_tiles, waves, fold, depth, s, occ);
+  return q_bf16 ? launch_decode_f<kKvBF16, true, D>(p, num_tiles, waves, fold, depth, s, occ)
+                : launch_decode_f<kKvF16, false, D>(p, num_tiles, waves, fold, depth, s, occ);
 }
 
 // ---- record instances (test hook): head_dim 128, fp16 q + fp16 K/V or bf16
@@ -944,9 +964,24 @@ hipError_t launch_decode(const DecodeParams& p, int num_tiles, int waves, bool q
                              depth ? depth : (fold && waves <= 4 ? 2 : 1), head_dim, s);
   }
   switch (head_dim) {
-    case 64: return launch_decode_d<64>(p, num_tiles, waves, q_bf16, kv, fold, depth, s);
-    case 128: return launch_decode_d<128>(p, num_tiles, waves, q_bf16, kv, fold, depth, s);
-    case 256: return launch_decode_d<256>(p, num_tiles, waves, q_bf16, kv, fold, depth, s);
+    case 64: return launch_decode_d<64>(p, num_tiles, waves, q_bf16, kv, fold, depth, s, nullptr);
+    case 128: return launch_decode_d<128>(p, num_tiles, waves, q_bf16, kv, fold, depth, s, nullptr);
+    case 256: return launch_decode_d<256>(p, num_tiles, waves, q_bf16, kv, fold, depth, s, nullptr);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Workgroups of `waves` waves per compute unit that the instance
+// launch_decode picks for the same arguments holds at once (its registers,
+// LDS and block size, as the device reports them); nothing is launched.
+hipError_t decode_occupancy(const DecodeParams& p, int waves, bool q_bf16, int kv, bool fold,
+                            int depth, int head_dim, int* blocks) {
+  *blocks = 0;
+  if (waves < 1 || waves > kWavesPerTile) return hipErrorInvalidValue;
+  switch (head_dim) {
+    case 64: return launch_decode_d<64>(p, 0, waves, q_bf16, kv, fold, depth, nullptr, blocks);
+    case 128: return launch_decode_d<128>(p, 0, waves, q_bf16, kv, fold, depth, nullptr, blocks);
+    case 256: return launch_decode_d<256>(p, 0, waves, q_bf16, kv, fold, depth, nullptr, blocks);
     default: return hipErrorInvalidValue;
   }
 }

@@ -188,6 +188,13 @@ struct PlanInput {
   int32_t ragged;   // rows kv_indptr[r] + t, no page indices
   int32_t hnd;      // pages head-major: [page][Hkv][page_size][D]
   Tuning tune;
+  // Waves per compute unit that the decode instance of a plan with these
+  // arguments holds at once, for tiles of hpt kv heads (rope_form: 0 none,
+  // 1 turned key as high part + residual, 2 as one fp16 value; fold: the
+  // cascade fold instance), or 0 when unknown (no device): the default
+  // decode wave target is min(16, this).  NULL: unknown.
+  int (*resident_waves)(const void* ctx, int hpt, int rope_form, int fold) = nullptr;
+  const void* resident_ctx = nullptr;
 };
 int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen);
 void plan_free(HostPlan* p);

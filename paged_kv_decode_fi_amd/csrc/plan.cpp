@@ -12,8 +12,10 @@
 // token chunk [t0, t1) (W = 8 when Hkv allows, fewer for small problems).
 // The chunk length c is one value for the whole batch: the smallest
 // multiple of the 16-token step, at least c_min, such that the waves
-// launched stay within target = num_cus * waves_per_cu, one round of
-// resident waves (more chunks than that only adds partial states to merge).
+// launched stay within target = num_cus * waves_per_cu, one round of the
+// waves the launched instance keeps resident (more chunks than that only
+// adds partial states to merge) -- or two rounds when lengths are so skewed
+// that one round would leave the long requests' tiles running alone.
 // Tiles are emitted longest first so short tails fill in behind long tiles.
 //
 // Cascade: the shared prefix of group g is attended once per (g, kv head) by
@@ -66,15 +68,22 @@ int64_t table_len(const int32_t* indptr, const int32_t* last, int i, int ps) {
 // requests' lengths len(r) (no allocation; also used by the allocation-free
 // entry point).
 //  * heads per tile: the largest of tune.heads_per_tile (default 8; 4 with
-//    RoPE, whose kernel holds 3 waves per SIMD: three 4-wave workgroups fill
-//    a CU where one 8-wave workgroup would leave a third of it idle), 4, 2, 1
-//    dividing Hkv; halved (down to 2) for small problems.
+//    RoPE: smaller workgroups of the register-heavier RoPE instances), 4,
+//    2, 1 dividing Hkv; halved (down to 2) for small problems.
 //  * chunk: the smallest multiple of the 16-token step, at least chunk_min,
 //    whose waves stay within num_cus * waves_per_cu (one round of resident
 //    waves), or the longest request when that is already enough work.
-template <class LenFn>
-void decode_split(const PlanInput& in, int num_cus, bool rope, LenFn len, int* hpt_out,
-                  int64_t* chunk_out) {
+//    waves_per_cu: tune.waves_per_cu, else 16 or, when fewer, the waves per
+//    CU that the instance to be launched holds at once (resident(hpt); 0 =
+//    unknown) -- a target past what is resident splits the work into a
+//    second round of workgroups.  When that chunk is over 1.25x the mean
+//    tokens per resident workgroup (skewed lengths: many short requests
+//    force long chunks of the long ones, which then run alone at the end),
+//    the chunk is sized for two rounds instead, so the long requests' tiles
+//    fill in behind the short ones.
+template <class LenFn, class ResidentFn>
+void decode_split(const PlanInput& in, int num_cus, bool rope, LenFn len, ResidentFn resident,
+                  int* hpt_out, int64_t* chunk_out) {
   const int B = in.batch, Hkv = in.Hkv;
   const int hpt_default = rope ? kWavesPerTile / 2 : kWavesPerTile;
   const bool hpt_forced = in.tune.heads_per_tile > 0;
@@ -85,7 +94,6 @@ void decode_split(const PlanInput& in, int num_cus, bool rope, LenFn len, int* h
   if (rope && in.D == 256) hpt = std::min(hpt, kWavesPerTile / 2);
   while (hpt & (hpt - 1)) hpt &= hpt - 1;
   while (Hkv % hpt) hpt >>= 1;
-  const int64_t waves_per_cu = std::max(1, tune_or(in.tune.waves_per_cu, 16));
   const int64_t c_min = round_up(std::max(tune_or(in.tune.chunk_min, 32), kChunkAlign),
                                  kChunkAlign);
   if (!hpt_forced) {
@@ -97,6 +105,13 @@ void decode_split(const PlanInput& in, int num_cus, bool rope, LenFn len, int* h
       return t * (Hkv / h);
     };
     while (hpt > 2 && tiles_at_min(hpt) < 4 * (int64_t)num_cus) hpt >>= 1;
+  }
+  int64_t waves_per_cu = 16;
+  if (in.tune.waves_per_cu > 0) {
+    waves_per_cu = in.tune.waves_per_cu;
+  } else {
+    const int res = resident(hpt);
+    if (res > 0) waves_per_cu = std::max<int64_t>(hpt, std::min<int64_t>(16, res));
   }
   const int64_t target_waves = std::max<int64_t>(1, num_cus * waves_per_cu);
   int64_t Lmax = 0;
@@ -110,20 +125,27 @@ void decode_split(const PlanInput& in, int num_cus, bool rope, LenFn len, int* h
   if (in.chunk_tokens > 0) {
     chunk = in.chunk_tokens;
   } else {
-    int64_t hi = std::max<int64_t>(round_up(std::max<int64_t>(Lmax, 1), kChunkAlign),
-                                   kChunkAlign);
-    int64_t lo = std::min(c_min, hi);
-    if (waves_for(hi) >= target_waves) {
-      chunk = hi;                       // enough work without splitting
-    } else {
+    const int64_t hi = std::max<int64_t>(round_up(std::max<int64_t>(Lmax, 1), kChunkAlign),
+                                         kChunkAlign);
+    const int64_t lo = std::min(c_min, hi);
+    auto chunk_for = [&](int64_t target) -> int64_t {
+      if (waves_for(hi) >= target) return hi;   // enough work without splitting
       // smallest c in [lo, hi] (multiple of the step) with waves(c) <= target
       int64_t a = lo / kChunkAlign, b = hi / kChunkAlign;
       while (a < b) {
         int64_t mid = (a + b) / 2;
-        if (waves_for(mid * kChunkAlign) <= target_waves) b = mid; else a = mid + 1;
+        if (waves_for(mid * kChunkAlign) <= target) b = mid; else a = mid + 1;
       }
-      chunk = a * kChunkAlign;
-    }
+      return a * kChunkAlign;
+    };
+    chunk = chunk_for(target_waves);
+    // mean tokens per resident workgroup (Hkv / hpt tiles per chunk)
+    int64_t tokens = 0;
+    for (int r = 0; r < B; ++r) tokens += std::max<int64_t>(0, len(r));
+    const double slots = (double)target_waves / hpt;
+    const double mean = (double)tokens * (Hkv / hpt) / slots;
+    if (in.tune.waves_per_cu == 0 && (double)chunk > 1.25 * mean)
+      chunk = chunk_for(2 * target_waves);
   }
   *hpt_out = hpt;
   *chunk_out = chunk;
@@ -490,16 +512,33 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   }
 
   // ---- decode chunk length and heads per tile
+  // fp16 q: the turned key as one fp16 value when every request is long
+  // enough for its rounding to stay well inside the lse bar (plain decode:
+  // a cascade's multi-row tiles read the fp32 table); (the step's fp16 table
+  // rows are copied by one 16-byte vector per thread: 2 D bytes x 16 rows
+  // need 32 D / 16 threads, so tiles of hpt >= D / 32 waves)
+  int64_t shortest = -1;
+  for (int r = 0; r < B; ++r)
+    if (lens[r] > 0) shortest = shortest < 0 ? lens[r] : std::min(shortest, lens[r]);
+  auto rope_single_at = [&](int h) {
+    return rope && in.q_dtype == 0 && NL == 0 && h * 32 >= in.D &&
+           (in.tune.rope_split_k < 0 || (in.tune.rope_split_k == 0 && shortest >= kRopeSingleKeys));
+  };
+  const bool fold_ok = in.tune.cascade_fold >= 0 && !rope;   // no RoPE fold instance
+  auto resident = [&](int h) {
+    if (!in.resident_waves) return 0;
+    return in.resident_waves(in.resident_ctx, h, !rope ? 0 : rope_single_at(h) ? 2 : 1,
+                             NG > 0 && fold_ok ? 1 : 0);
+  };
   const bool hpt_forced = in.tune.heads_per_tile > 0;
   int hpt;
   int64_t chunk;
-  decode_split(in, num_cus, rope, [&](int r) { return lens[r]; }, &hpt, &chunk);
+  decode_split(in, num_cus, rope, [&](int r) { return lens[r]; }, resident, &hpt, &chunk);
   // Cascade: a request with prefix states whose suffix is one chunk folds
   // those states into its decode tile's output, so no merge pass is needed.
   // When every such suffix is short (<= tune.fold_max_suffix tokens, default
   // 1024), cover each with one chunk, 2 kv heads per tile (small tiles, two
   // steps of loads in flight), provided that still gives >= 4 waves per CU.
-  const bool fold_ok = in.tune.cascade_fold >= 0 && !rope;   // no RoPE fold instance
   if (NG > 0 && fold_ok && in.chunk_tokens == 0 && !hpt_forced) {
     int64_t ls_max = 0;
     for (int r = 0; r < B; ++r)
@@ -751,19 +790,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
                    "q heads per kv head");
     out->valu_heads = G == 1 ? 1 : G == 2 ? 2 : 4;
   }
-  // fp16 q: the turned key as one fp16 value when every request is long
-  // enough for its rounding to stay well inside the lse bar (plain decode:
-  // a cascade's multi-row tiles read the fp32 table)
-  if (rope && in.q_dtype == 0 && NL == 0) {
-    int64_t shortest = -1;
-    for (int r = 0; r < B; ++r)
-      if (lens[r] > 0) shortest = shortest < 0 ? lens[r] : std::min(shortest, lens[r]);
-    // (the step's fp16 table rows are copied by one 16-byte vector per
-    // thread: 2 D bytes x 16 rows need 32 D / 16 threads, W >= D / 32)
-    out->rope_single = hpt * 32 >= in.D &&
-                       (in.tune.rope_split_k < 0 ||
-                        (in.tune.rope_split_k == 0 && shortest >= kRopeSingleKeys));
-  }
+  out->rope_single = rope_single_at(hpt);
   L.rope_off = off;
   off = align256(off + (size_t)rope_row_bytes(in.D) * (size_t)out->rope_rows);
   L.total = off;
@@ -786,7 +813,10 @@ int plan_decode_static(const PlanInput& in, size_t max_bytes, HostPlan* out, cha
   auto len = [&](int r) { return table_len(in.kv_indptr, last_tab, r, ps); };
   int hpt;
   int64_t chunk;
-  decode_split(in, num_cus, false, len, &hpt, &chunk);
+  decode_split(
+      in, num_cus, false, len,
+      [&](int h) { return in.resident_waves ? in.resident_waves(in.resident_ctx, h, 0, 0) : 0; },
+      &hpt, &chunk);
   // the work list in scratch: tiles, request info, merge units, partial
   // states (the same counts the device planner derives from the tables)
   auto layout = [&](int64_t c, WorkspaceLayout* L, int64_t* tiles, int64_t* units,
