@@ -106,7 +106,11 @@ typedef struct {
  * reads no environment variable. */
 typedef struct {
   int32_t heads_per_tile;       /* kv heads per decode workgroup: 1, 2, 4 or 8 */
-  int32_t waves_per_cu;         /* decode waves the chunk search targets per CU (16) */
+  int32_t waves_per_cu;         /* decode waves the chunk search targets per CU
+                                   (default: 16, or fewer when fi_plan finds the
+                                   device keeps fewer of the decode kernel it
+                                   will launch resident; one round of them, or
+                                   two when the lengths are skewed) */
   int32_t chunk_min;            /* smallest decode chunk, tokens (32) */
   int32_t prefix_waves;         /* waves per multi-row tile: 4 or 8 (RoPE: 8) */
   int32_t prefix_tiles_per_cu;  /* cascade prefix tiles per CU (1) */
@@ -232,6 +236,10 @@ typedef struct {
                                 all plans of the process (reused, not per plan) */
   int32_t rope_single;       /* RoPE plan whose turned keys are one fp16 value */
   int32_t valu_heads;        /* > 0: plain decode on the VALU (no MFMA) kernel */
+  int32_t decode_waves_per_cu; /* decode waves per CU the chunking targeted: the
+                                tuning's, else 16 or, when fewer, what the
+                                current device keeps resident of the decode
+                                kernel the run launches (16 without a device) */
 } fi_plan_stats;
 
 /* Plan stage (FlashInfer README "core features" item 2).

@@ -75,7 +75,8 @@ class PlanStats(ctypes.Structure):
                 ("heads_per_tile", ctypes.c_int32), ("num_cus", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_size_t), ("num_folded", ctypes.c_int64),
                 ("prefix_split_p", ctypes.c_uint32), ("staging_buffers", ctypes.c_int32),
-                ("rope_single", ctypes.c_int32), ("valu_heads", ctypes.c_int32)]
+                ("rope_single", ctypes.c_int32), ("valu_heads", ctypes.c_int32),
+                ("decode_waves_per_cu", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}

@@ -466,6 +466,7 @@ fi_status fi_plan_get_stats(fi_plan_t plan, fi_plan_stats* s) {
   s->prefix_split_p = hp.prefix_split_p;
   s->rope_single = hp.rope_single;
   s->valu_heads = hp.valu_heads;
+  s->decode_waves_per_cu = hp.decode_waves_per_cu;
   s->staging_buffers = staging_count();
   return FI_OK;
 }

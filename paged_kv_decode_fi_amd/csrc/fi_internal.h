@@ -126,6 +126,7 @@ struct HostPlan {
   // kSplitPKeys keys)
   uint32_t prefix_split_p;
   int32_t rope_single;  // RoPE, fp16 q: the turned key rounded once (no residual)
+  int32_t decode_waves_per_cu;  // the decode wave target the chunking used
   int32_t valu_heads;   // plain decode on the VALU instance for this many q heads per
                         // kv head (1, 2 or 4), 0 = MFMA
   int32_t rope;         // FI_POS_ROPE_LLAMA or 0

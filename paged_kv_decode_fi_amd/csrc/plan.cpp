@@ -83,7 +83,7 @@ int64_t table_len(const int32_t* indptr, const int32_t* last, int i, int ps) {
 //    fill in behind the short ones.
 template <class LenFn, class ResidentFn>
 void decode_split(const PlanInput& in, int num_cus, bool rope, LenFn len, ResidentFn resident,
-                  int* hpt_out, int64_t* chunk_out) {
+                  int* hpt_out, int64_t* chunk_out, int* waves_per_cu_out) {
   const int B = in.batch, Hkv = in.Hkv;
   const int hpt_default = rope ? kWavesPerTile / 2 : kWavesPerTile;
   const bool hpt_forced = in.tune.heads_per_tile > 0;
@@ -149,6 +149,7 @@ void decode_split(const PlanInput& in, int num_cus, bool rope, LenFn len, Reside
   }
   *hpt_out = hpt;
   *chunk_out = chunk;
+  *waves_per_cu_out = (int)waves_per_cu;
 }
 
 int plan_append(const PlanInput& in, const std::vector<int64_t>& lens, int num_cus,
@@ -533,7 +534,9 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   const bool hpt_forced = in.tune.heads_per_tile > 0;
   int hpt;
   int64_t chunk;
-  decode_split(in, num_cus, rope, [&](int r) { return lens[r]; }, resident, &hpt, &chunk);
+  int wpc = 16;
+  decode_split(in, num_cus, rope, [&](int r) { return lens[r]; }, resident, &hpt, &chunk, &wpc);
+  out->decode_waves_per_cu = wpc;
   // Cascade: a request with prefix states whose suffix is one chunk folds
   // those states into its decode tile's output, so no merge pass is needed.
   // When every such suffix is short (<= tune.fold_max_suffix tokens, default
@@ -816,7 +819,7 @@ int plan_decode_static(const PlanInput& in, size_t max_bytes, HostPlan* out, cha
   decode_split(
       in, num_cus, false, len,
       [&](int h) { return in.resident_waves ? in.resident_waves(in.resident_ctx, h, 0, 0) : 0; },
-      &hpt, &chunk);
+      &hpt, &chunk, &out->decode_waves_per_cu);
   // the work list in scratch: tiles, request info, merge units, partial
   // states (the same counts the device planner derives from the tables)
   auto layout = [&](int64_t c, WorkspaceLayout* L, int64_t* tiles, int64_t* units,

@@ -512,3 +512,35 @@ def test_tuning_is_explicit_and_environment_is_ignored(fi, monkeypatch):
         fi.debug_plan_tiles(indptr, last, tuning=dict(cascade_fold=2), **kw)
     with pytest.raises(ValueError):
         fi.debug_plan_tiles(indptr, last, tuning=dict(no_such_knob=1), **kw)
+
+
+def _table(lens, ps=16):
+    lens = np.asarray(lens)
+    n = (lens + ps - 1) // ps
+    indptr = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    last = np.where(n > 0, lens - (n - 1) * ps, 0).astype(np.int32)
+    return indptr, last
+
+
+def test_plan_sizes_skewed_batches_for_two_rounds(fi):
+    """Many short requests and a few very long ones: one round of 16 waves
+    per CU (512 eight-head tiles on 256 CUs) leaves room for only 32 tiles of
+    the 8 long requests (8192-token chunks, each running alone long after
+    the short tiles end), over 1.25x the mean tokens per workgroup slot, so
+    the chunk is sized for two rounds (1024 tiles: 8 x ceil(32768 / c) <= 544,
+    c = 496).  With the wave target given explicitly the rule is off."""
+    lens = np.array([64] * 480 + [32768] * 8)
+    indptr, last = _table(lens)
+    t = fi.debug_plan_tiles(indptr, last, num_qo_heads=32, num_kv_heads=8, page_size=16)
+    chunk = max(int(x[3] - x[2]) for x in t if x[5] == 0)
+    assert chunk == 496, chunk
+    _check_cover(t, lens, 8, _heads_per_tile(t, 8))
+    t = fi.debug_plan_tiles(indptr, last, num_qo_heads=32, num_kv_heads=8, page_size=16,
+                            tuning={"waves_per_cu": 16})
+    chunk = max(int(x[3] - x[2]) for x in t if x[5] == 0)
+    assert chunk == 8192, chunk
+    # uniform lengths keep the one-round chunk: 64 x 2048 keys, 512 slots,
+    # mean 256 tokens per slot, chunk 256
+    indptr, last = _table(np.full(64, 2048))
+    t = fi.debug_plan_tiles(indptr, last, num_qo_heads=32, num_kv_heads=8, page_size=16)
+    assert max(int(x[3] - x[2]) for x in t if x[5] == 0) == 256
