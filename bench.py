@@ -486,7 +486,7 @@ def main():
         "plan": {k: st[k] for k in ("num_tiles", "num_prefix_tiles", "num_merge_units",
                                     "chunk_tokens", "prefix_chunk_tokens", "heads_per_tile",
                                     "num_cus", "prefix_split_p", "rope_single",
-                                    "valu_heads")},
+                                    "valu_heads", "decode_waves_per_cu")},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "hot": hot,
