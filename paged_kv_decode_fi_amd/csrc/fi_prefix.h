@@ -522,6 +522,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 && D != 256 ? 2 : 1) void pr
     if constexpr (ROPE) store_rope(buf, st);
     else store(buf, st);
   };
+  // The loads and stores run unconditionally, past the last step too: the
+  // loader clamps every token to the tile's last key (in bounds, already
+  // cached), the store goes to the buffer the step does not read, and
+  // steps past the tile compute nothing (tb >= wave_hi).  Conditional loads
+  // would make the compiler's wait counts merge over the branch and wait
+  // for every load in flight -- including the ones just issued for two
+  // steps ahead -- before each LDS store.
   __syncthreads();   // page table
   load_set(t0, va);
   store_set(0, va);
@@ -529,24 +536,25 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 && D != 256 ? 2 : 1) void pr
     __syncthreads();
     for (int step = 0; step < nsteps; ++step) {
       const int tb = t0 + kPStep * step;
-      if (step + 1 < nsteps) load_set(tb + kPStep, va);
+      load_set(tb + kPStep, va);
       if (tb < wave_hi) compute(tb, step & 1, tb + kPStep > wave_lo);
-      if (step + 1 < nsteps) store_set((step + 1) & 1, va);
+      store_set((step + 1) & 1, va);
       __syncthreads();
     }
   } else {
-    if (nsteps > 1) load_set(t0 + kPStep, vb);
+    load_set(t0 + kPStep, vb);
     __syncthreads();
     auto step_body = [&](int step, Set& nxt, Set& aft) {
       const int tb = t0 + kPStep * step;
-      if (step + 2 < nsteps) load_set(tb + 2 * kPStep, aft);
+      load_set(tb + 2 * kPStep, aft);
       if (tb < wave_hi) compute(tb, step & 1, tb + kPStep > wave_lo);
-      if (step + 1 < nsteps) store_set((step + 1) & 1, nxt);
+      store_set((step + 1) & 1, nxt);
       __syncthreads();
     };
+    // (an odd step count runs one empty step at the end)
     for (int step = 0; step < nsteps; step += 2) {
       step_body(step, vb, va);
-      if (step + 1 < nsteps) step_body(step + 1, va, vb);
+      step_body(step + 1, va, vb);
     }
   }
 
