@@ -47,22 +47,27 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0      # dense bf16 / fp16 MFMA
 ROTATE_BYTES = 1 << 30          # >= 1 GiB referenced per rotation cycle
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_decode_fi_amd", "csrc", f)
-               for f in ("decode.hip", "fi_prefix.h", "prefix.hip", "prefix_rope.hip",
-                         "fi_device.h", "fi_internal.h")]
+_CSRC = os.path.join(ROOT, "paged_kv_decode_fi_amd", "csrc")
+# the sources each kernel family's code object is compiled from: the decode
+# kernel (decode.hip) and the multi-row kernel (cascade prefix / append:
+# fi_prefix.h, prefix.hip, prefix_rope.hip) share only the two headers
+KERNEL_SRCS = {
+    "decode": ("decode.hip", "fi_device.h", "fi_internal.h"),
+    "multirow": ("fi_prefix.h", "prefix.hip", "prefix_rope.hip", "fi_device.h",
+                 "fi_internal.h"),
+}
 
 
-def kernel_source_hash() -> str:
-    """sha256[:16] of the decode and multi-row kernels' code (decode.hip,
-    fi_prefix.h, prefix.hip, prefix_rope.hip and the two headers they
-    include): every line with its // comment and trailing blanks removed,
-    blank lines dropped -- a comment edit keeps the hash, any change to the
-    code does not."""
+def kernel_source_hash(family: str) -> str:
+    """sha256[:16] of one kernel family's code (the files KERNEL_SRCS names):
+    every line with its // comment and trailing blanks removed, blank lines
+    dropped -- a comment edit keeps the hash, any change to the code does
+    not."""
     import hashlib
     import re
     lines = []
-    for path in KERNEL_SRCS:
-        for ln in open(path, encoding="utf-8").read().splitlines():
+    for name in KERNEL_SRCS[family]:
+        for ln in open(os.path.join(_CSRC, name), encoding="utf-8").read().splitlines():
             ln = re.sub(r"//.*$", "", ln).rstrip()
             if ln:
                 lines.append(ln)
@@ -70,13 +75,14 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE runs (already scaled by the streaming-read calibration), or
-    None when there is no measurement for this workload or the kernels'
-    code has changed since it was taken."""
+    """HBM bytes per launch of the workload's dominant kernel from the
+    committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs (already scaled by the
+    streaming-read calibration), or None when there is no measurement for
+    this workload or that kernel family's code has changed since it was
+    taken."""
     try:
         rec = json.load(open(TRAFFIC_FILE))[workload]
-        sha = kernel_source_hash()
+        sha = kernel_source_hash(rec["kernel_family"])
     except (OSError, KeyError, ValueError):
         return None
     if rec.get("kernel_code_sha256_16") != sha:
