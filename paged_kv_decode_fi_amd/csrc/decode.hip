@@ -257,11 +257,20 @@ struct RopeLds {
 // passes it by more than kLazyMax), and P.V runs as fp32 FMAs: lane i
 // accumulates dims D/64 i .. of each head, reading each key's p with
 // readlane and its V values from LDS.
+//
+// QCVT (bf16 q over e4m3 K/V, RoPE plans with the turned key as one value):
+// the tile computes in fp16 -- e4m3 K/V convert to fp16 as exactly as to
+// bf16, and fp16 carries the turned key and p to 11 bits -- with q read as
+// bf16 and scaled into fp16 by a power of two per wave (below); o is
+// written as bf16.
 template <int KV, bool QBF16, bool PS_POW2, bool FOLD, int DEPTH, int ROPE, int D,
-          bool REC = false, int VG = 0>
+          bool REC = false, int VG = 0, bool QCVT = false>
 __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams p) {
   static_assert(!ROPE || !FOLD, "RoPE plans have no cascade level to fold");
   static_assert(VG == 0 || (!ROPE && !FOLD), "the VALU instance serves plain plans");
+  static_assert(!QCVT || (!QBF16 && KV == kKvE4M3 && VG == 0 && !FOLD && !REC),
+                "the converted-q instance computes in fp16 over e4m3 K/V, plain or RoPE");
+  constexpr bool OBF16 = QBF16 || QCVT;   // o's type: q's type in memory
   constexpr int VGX = VG > 0 ? VG : 1;
   constexpr int NV = D / 64;   // VALU instance: output dims per lane
   using S = Stage<KV, D>;
@@ -313,10 +322,34 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
       qop[s] = ok ? v : u32x4{0, 0, 0, 0};
     }
   }
+  // QCVT: the wave's bf16 q times 2^qexp, chosen so that its largest
+  // magnitude lands in [2^14, 2^15): every bf16 value (8 significant bits)
+  // is then an exact fp16 value unless it lies more than 2^28 below that
+  // maximum (an fp16 subnormal, off by < 2^-39 of the maximum); the score
+  // scale takes the 2^-qexp back exactly
+  int qexp = 0;
+  if constexpr (QCVT) {
+    float mx = 0.f;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        mx = fmaxf(mx, fmaxf(fabsf(lo16<true>(qop[s][k])), fabsf(hi16<true>(qop[s][k]))));
+    mx = wave_max(mx);
+    qexp = __builtin_amdgcn_readfirstlane(
+        mx > 0.f ? min(15 - __builtin_amdgcn_frexp_expf(mx), 64) : 0);
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        qop[s][k] = pack2<false>(__builtin_ldexpf(lo16<true>(qop[s][k]), qexp),
+                                 __builtin_ldexpf(hi16<true>(qop[s][k]), qexp));
+  }
   // RoPE: the query sits at position kv_len - 1
   const int qpos = ROPE ? p.req_info[r].kv_len - 1 : 0;
   float c = p.sm_scale_log2;
   if (KV == kKvE4M3 && p.k_scale) c *= p.k_scale[h];
+  if constexpr (QCVT) c = __builtin_ldexpf(c, -qexp);
 
   // cooperative loader: load u of thread tid covers token tk0 + u * TOK_PER_U
   // of the step and 16-byte vector vin of that token's W-head run
@@ -736,8 +769,8 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
       uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)r * p.Hq + j) * D;
 #pragma unroll
       for (int b = 0; b < D / 16; ++b) {
-        u32x2 w = {pack2<QBF16>(oacc[b][0] * inv, oacc[b][1] * inv),
-                   pack2<QBF16>(oacc[b][2] * inv, oacc[b][3] * inv)};
+        u32x2 w = {pack2<OBF16>(oacc[b][0] * inv, oacc[b][1] * inv),
+                   pack2<OBF16>(oacc[b][2] * inv, oacc[b][3] * inv)};
         *reinterpret_cast<u32x2*>(orow + 16 * b + 4 * g) = w;
       }
       if (g == 0 && p.lse) p.lse[(int64_t)r * p.Hq + j] = lse2 * kLn2;
@@ -766,7 +799,7 @@ constexpr int kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
 // occ != NULL: nothing is launched; *occ receives the workgroups of this
 // instance that one compute unit holds at once (the same kernel, block size
 // and dynamic LDS as the launch).
-template <int KV, bool QBF16, bool FOLD, int DEPTH, int ROPE, int D>
+template <int KV, bool QBF16, bool FOLD, int DEPTH, int ROPE, int D, bool QCVT = false>
 static hipError_t launch_decode_t(const DecodeParams& p, int num_tiles, int waves,
                                   hipStream_t s, int* occ = nullptr) {
   constexpr int rope_lds = ROPE == 2 ? RopeLds<D>::BYTES16 : ROPE ? RopeLds<D>::BYTES : 0;
@@ -777,11 +810,11 @@ static hipError_t launch_decode_t(const DecodeParams& p, int num_tiles, int wave
   static const hipError_t attr = [] {
     const int max_lds = std::min(Stage<KV, D>::lds_bytes(kWavesPerTile) + rope_lds, kMaxLds);
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, true, FOLD, DEPTH, ROPE, D>),
+        reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, true, FOLD, DEPTH, ROPE, D, false, 0, QCVT>),
         hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
     if (e == hipSuccess)
       e = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, false, FOLD, DEPTH, ROPE, D>),
+          reinterpret_cast<const void*>(&decode_kernel<KV, QBF16, false, FOLD, DEPTH, ROPE, D, false, 0, QCVT>),
           hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
     return e;
   }();
@@ -789,14 +822,14 @@ static hipError_t launch_decode_t(const DecodeParams& p, int num_tiles, int wave
   if (occ)
     return p.ps_shift >= 0
                ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                     occ, decode_kernel<KV, QBF16, true, FOLD, DEPTH, ROPE, D>, 64 * waves, lds)
+                     occ, decode_kernel<KV, QBF16, true, FOLD, DEPTH, ROPE, D, false, 0, QCVT>, 64 * waves, lds)
                : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                     occ, decode_kernel<KV, QBF16, false, FOLD, DEPTH, ROPE, D>, 64 * waves, lds);
+                     occ, decode_kernel<KV, QBF16, false, FOLD, DEPTH, ROPE, D, false, 0, QCVT>, 64 * waves, lds);
   if (p.ps_shift >= 0)
-    hipLaunchKernelGGL((decode_kernel<KV, QBF16, true, FOLD, DEPTH, ROPE, D>), dim3(num_tiles),
+    hipLaunchKernelGGL((decode_kernel<KV, QBF16, true, FOLD, DEPTH, ROPE, D, false, 0, QCVT>), dim3(num_tiles),
                        dim3(64 * waves), lds, s, p);
   else
-    hipLaunchKernelGGL((decode_kernel<KV, QBF16, false, FOLD, DEPTH, ROPE, D>), dim3(num_tiles),
+    hipLaunchKernelGGL((decode_kernel<KV, QBF16, false, FOLD, DEPTH, ROPE, D, false, 0, QCVT>), dim3(num_tiles),
                        dim3(64 * waves), lds, s, p);
   return hipGetLastError();
 }
@@ -810,14 +843,14 @@ static hipError_t launch_decode_t(const DecodeParams& p, int num_tiles, int wave
 // RoPE plans: two steps of loads in flight at head_dim 128 unless the plan
 // forces one; one step at head_dim 64 (measured 8 % faster) and 256
 // (registers).
-template <int KV, bool QBF16, int ROPE, int D>
+template <int KV, bool QBF16, int ROPE, int D, bool QCVT = false>
 static hipError_t launch_decode_rope(const DecodeParams& p, int num_tiles, int waves, int depth,
                                      hipStream_t s, int* occ) {
   if constexpr (D == 128) {
     if (depth != 1)
-      return launch_decode_t<KV, QBF16, false, 2, ROPE, D>(p, num_tiles, waves, s, occ);
+      return launch_decode_t<KV, QBF16, false, 2, ROPE, D, QCVT>(p, num_tiles, waves, s, occ);
   }
-  return launch_decode_t<KV, QBF16, false, 1, ROPE, D>(p, num_tiles, waves, s, occ);
+  return launch_decode_t<KV, QBF16, false, 1, ROPE, D, QCVT>(p, num_tiles, waves, s, occ);
 }
 
 // VALU instances (plain plans, head_dim 128, one step of loads in flight):
@@ -879,11 +912,14 @@ static hipError_t launch_decode_f(const DecodeParams& p, int num_tiles, int wave
     return hipErrorInvalidValue;
   }
   if (p.rope_table) {
-    // the rotated key as one 16-bit value (fp16 q only) or a high part plus
-    // a residual
+    // the rotated key as one fp16 value (fp16 q; bf16 q over e4m3 K/V on
+    // the converted-q fp16 instance) or a high part plus a residual
     if constexpr (!QBF16) {
       if (p.rope_single)
         return launch_decode_rope<KV, QBF16, 2, D>(p, num_tiles, waves, depth, s, occ);
+    } else if constexpr (KV == kKvE4M3) {
+      if (p.rope_single)
+        return launch_decode_rope<KV, false, 2, D, true>(p, num_tiles, waves, depth, s, occ);
     }
     return launch_decode_rope<KV, QBF16, 1, D>(p, num_tiles, waves, depth, s, occ);
   }

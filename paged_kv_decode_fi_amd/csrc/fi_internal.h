@@ -125,7 +125,8 @@ struct HostPlan {
   // plus a residual (bit l set: level l has a prefix chunk shorter than
   // kSplitPKeys keys)
   uint32_t prefix_split_p;
-  int32_t rope_single;  // RoPE, fp16 q: the turned key rounded once (no residual)
+  int32_t rope_single;  // RoPE, fp16 q or bf16 q over e4m3 K/V (fp16 compute): the
+                        // turned key rounded once (no residual)
   int32_t decode_waves_per_cu;  // the decode wave target the chunking used
   int32_t valu_heads;   // plain decode on the VALU instance for this many q heads per
                         // kv head (1, 2 or 4), 0 = MFMA
@@ -230,7 +231,7 @@ struct DecodeParams {
   // RoPE plans: the (cos, sin) table, rope_rows x D / 2 fp32 pairs
   const void* rope_table;
   int32_t rope_rows;
-  int32_t rope_single;        // fp16 q: turned keys as one fp16 value
+  int32_t rope_single;        // fp16 q or bf16 q over e4m3: turned keys as one fp16 value
   int32_t valu_heads;         // > 0: the VALU decode instance (q heads per kv head)
   // ragged KV: token t of a request is row kv_indptr[r] + t (page size 1,
   // kv_indices not read)

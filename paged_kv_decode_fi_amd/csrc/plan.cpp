@@ -513,7 +513,8 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   }
 
   // ---- decode chunk length and heads per tile
-  // fp16 q: the turned key as one fp16 value when every request is long
+  // fp16 q (or bf16 q over e4m3 K/V, which the decode kernel then computes
+  // in fp16): the turned key as one fp16 value when every request is long
   // enough for its rounding to stay well inside the lse bar (plain decode:
   // a cascade's multi-row tiles read the fp32 table); (the step's fp16 table
   // rows are copied by one 16-byte vector per thread: 2 D bytes x 16 rows
@@ -522,7 +523,7 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   for (int r = 0; r < B; ++r)
     if (lens[r] > 0) shortest = shortest < 0 ? lens[r] : std::min(shortest, lens[r]);
   auto rope_single_at = [&](int h) {
-    return rope && in.q_dtype == 0 && NL == 0 && h * 32 >= in.D &&
+    return rope && (in.q_dtype == 0 || in.kv_dtype == 2) && NL == 0 && h * 32 >= in.D &&
            (in.tune.rope_split_k < 0 || (in.tune.rope_split_k == 0 && shortest >= kRopeSingleKeys));
   };
   const bool fold_ok = in.tune.cascade_fold >= 0 && !rope;   // no RoPE fold instance

@@ -257,8 +257,61 @@ def test_rope_single_rounded_fp16_key(fi, case):
     C.assert_parity(w, o, lse, ro, rl, label=f"rope single {case} lens {list(lens)}")
 
 
+def _bf16_to_f32(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _f32_to_bf16_exact(x):
+    """float32 values that are already bf16 values (scaled by powers of two)
+    back to their bf16 bits (exact: the low 16 bits are zero)."""
+    b = np.asarray(x, np.float32).view(np.uint32)
+    assert not np.any(b & 0xFFFF)
+    return (b >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_rope_single_bf16_q_over_e4m3(fi, case):
+    """bf16 q over e4m3 K/V, every request at least 64 keys long: the decode
+    kernel computes in fp16 -- q scaled into fp16 by a power of two per kv
+    head, the turned key as one fp16 value, o written as bf16 -- and matches
+    the oracle, as does the residual form forced on the same problem.
+    Case 4 spreads the q heads of every kv head over magnitudes 2^-20 .. 2^3
+    (the small ones become fp16 subnormals after the wave's scaling); case 5
+    multiplies kv head 0's q by 2^16 and its k_scale by 2^-16 (same scores,
+    the power of two taken out of q instead of put in)."""
+    rng = np.random.default_rng(1900 + case)
+    G = [4, 8, 1, 16, 4, 8][case]
+    Hkv = [8, 4, 8, 1, 8, 2][case]
+    ps = [16, 1, 16, 7, 16, 1][case]
+    D = [128, 128, 64, 128, 256, 128][case]
+    lens = rng.integers(64, 3000, size=int(rng.integers(1, 9)))
+    w = W.build(f"rope_bf16q_e4m3_{case}", lens, Hq=G * Hkv, Hkv=Hkv, D=D, ps=ps,
+                q_dtype="bf16", kv_dtype="e4m3", seed=70 + case)
+    if case == 4:
+        qf = _bf16_to_f32(w.q).reshape(w.batch, w.num_qo_heads, D)
+        e = (np.arange(w.num_qo_heads) * 7) % 24 - 20
+        w.q = _f32_to_bf16_exact(qf * np.exp2(e)[None, :, None].astype(np.float32))
+    if case == 5:
+        qf = _bf16_to_f32(w.q).reshape(w.batch, w.num_qo_heads, D).copy()
+        qf[:, :G] *= np.float32(2.0 ** 16)
+        w.q = _f32_to_bf16_exact(qf)
+        w.k_scale = w.k_scale.copy()
+        w.k_scale[0] *= np.float32(2.0 ** -16)
+    rope = (float(rng.choice([1e4, 5e5])), 1.0)
+    ro, rl = C.run_oracle(w, rope=rope)
+    o, lse, plan = C.run_gpu(w, chunk_tokens=[0, 64][case % 2], rope=rope)
+    want = int(plan.stats["heads_per_tile"] * 32 >= D)
+    assert plan.stats["rope_single"] == want, plan.stats
+    C.assert_parity(w, o, lse, ro, rl, label=f"bf16 q / e4m3 rope single {case}")
+    o2, lse2, plan2 = C.run_gpu(w, rope=rope, tuning=dict(rope_split_k=1))
+    assert plan2.stats["rope_single"] == 0
+    C.assert_parity(w, o2, lse2, ro, rl, label=f"bf16 q / e4m3 rope residual {case}")
+    # the two forms compute the same function: closer to each other than to the bar
+    assert np.abs(o - o2).max() < 1e-2 and np.abs(lse - lse2).max() < 1e-3
+
+
 def test_rope_residual_kept_where_needed(fi):
-    """A request shorter than 64 keys, bf16 q, or tiles of fewer than
+    """A request shorter than 64 keys, bf16 q over bf16 K/V, or tiles of fewer than
     head_dim / 32 kv heads keep the turned key's residual; forcing either
     form on a long-request plan computes the same function."""
     short = W.build("rope_short", [700, 20], Hq=8, Hkv=2, ps=16, q_dtype="f16",
