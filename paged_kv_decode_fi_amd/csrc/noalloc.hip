@@ -125,6 +125,13 @@ __global__ __launch_bounds__(1024) void device_plan_kernel(DevicePlanArgs a) {
       a.req_info[r] = ReqInfo{split ? (int32_t)sb : -1, (int32_t)nc, (int32_t)len, 0};
       if (split && ub < a.unit_cap) a.units[ub] = MergeUnit{r, (int32_t)sb, (int32_t)nc, 0};
       const int64_t ncx = nc > 1 ? nc : 1;
+      // the request's 16-token steps shared out evenly over its chunks (the
+      // first ones one step longer), as the host plan does
+      const int64_t nst = (len + kChunkAlign - 1) / kChunkAlign;
+      const int64_t per = nst / ncx, extra = nst % ncx;
+      auto bound = [&](int64_t c) {
+        return (int32_t)min((int64_t)kChunkAlign * (c * per + min(c, extra)), len);
+      };
       for (int64_t c = 0; c < ncx; ++c)
         for (int hg = 0; hg < HG; ++hg) {
           const int64_t ti = tb + c * HG + hg;
@@ -132,8 +139,8 @@ __global__ __launch_bounds__(1024) void device_plan_kernel(DevicePlanArgs a) {
           Tile t;
           t.req = r;
           t.kv_head0 = hg * a.heads_per_tile;
-          t.t0 = (int32_t)min(c * a.chunk, len);
-          t.t1 = (int32_t)min((c + 1) * a.chunk, len);
+          t.t0 = bound(c);
+          t.t1 = bound(c + 1);
           t.slot = split ? (int32_t)(sb + c * a.Hkv + t.kv_head0) : -1;
           t.kind = kDecodeTile;
           t.row0 = (int32_t)page_base;   // the request's first page-table entry

@@ -645,13 +645,21 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
     const ReqInfo& ri = out->req_info[r];
     int64_t nc = n_dchunks[r];
     bool need_empty = (nc == 0 && ri.n_states == 0);
+    // the request's steps shared out over its nc chunks as evenly as whole
+    // steps allow (the first ones one step longer), so no chunk is a short
+    // remainder: each is at most the chunk length and at least one step
+    const int64_t nsteps = ceil_div(lens[r], (int64_t)kChunkAlign);
+    const int64_t per = nc > 0 ? nsteps / nc : 0, extra = nc > 0 ? nsteps % nc : 0;
+    auto bound = [&](int64_t c) {
+      return std::min<int64_t>((int64_t)kChunkAlign * (c * per + std::min(c, extra)), lens[r]);
+    };
     for (int64_t c = 0; c < std::max<int64_t>(nc, need_empty ? 1 : 0); ++c) {
       for (int64_t hg = 0; hg < head_groups; ++hg) {
         Tile t;
         t.req = r;
         t.kv_head0 = (int32_t)(hg * hpt);
-        t.t0 = (int32_t)std::min<int64_t>(c * chunk, lens[r]);
-        t.t1 = (int32_t)std::min<int64_t>((c + 1) * chunk, lens[r]);
+        t.t0 = (int32_t)bound(c);
+        t.t1 = (int32_t)bound(c + 1);
         t.slot = ri.n_states >= 2 && !folded[r]
                      ? (int32_t)(ri.slot_base + (c_off + c) * Hkv + t.kv_head0) : -1;
         t.kind = kDecodeTile;

@@ -239,6 +239,42 @@ def test_plan_covers_every_token_once(fi, seed, head_dim):
     for t in tiles:
         if t[5] == 0:
             assert t[6] == indptr[t[0]]
+    _check_even_split(tiles, _lens(indptr, last, ps))
+
+
+def _check_even_split(tiles, lens, chunk=None):
+    """A split request's chunks share its 16-token steps out evenly: chunk
+    starts on step boundaries, step counts differ by at most one (the longer
+    ones first), and none exceeds the plan's chunk length."""
+    by_req = {}
+    for t in tiles:
+        if t[5] == 0:
+            by_req.setdefault(int(t[0]), set()).add((int(t[2]), int(t[3])))
+    for r, spans in by_req.items():
+        spans = sorted(spans)
+        steps = [(-(-(b - a) // 16)) for a, b in spans]
+        assert all(a % 16 == 0 for a, _ in spans), (r, spans)
+        assert max(steps) - min(steps) <= 1, (r, spans)
+        assert steps == sorted(steps, reverse=True), (r, spans)
+        if chunk is not None:
+            assert max(b - a for a, b in spans) <= chunk, (r, spans, chunk)
+
+
+@pytest.mark.parametrize("chunk", [32, 48, 304])
+def test_forced_chunk_splits_evenly(fi, chunk):
+    """chunk_tokens given: every request is cut into ceil(len / chunk)
+    chunks of near-equal whole steps, none longer than chunk."""
+    lens = np.array([0, 1, 15, 16, 17, 31, 33, 100, 303, 304, 305, 1000, 4097])
+    n = (lens + 15) // 16
+    indptr = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    last = np.where(n > 0, lens - (n - 1) * 16, 0).astype(np.int32)
+    tiles = fi.debug_plan_tiles(indptr, last, num_qo_heads=8, num_kv_heads=2, page_size=16,
+                                chunk_tokens=chunk)
+    _check_cover(tiles, lens, 2, _heads_per_tile(tiles, 2))
+    _check_even_split(tiles, lens, chunk)
+    for r, L in enumerate(lens):
+        if L > 0:
+            assert len({t[2] for t in tiles if t[0] == r and t[5] == 0}) == -(-L // chunk)
 
 
 def test_plan_is_deterministic_and_depends_only_on_lengths(fi):
