@@ -36,6 +36,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
 #include <vector>
 
 #include "fi_internal.h"
@@ -69,7 +70,8 @@ int64_t table_len(const int32_t* indptr, const int32_t* last, int i, int ps) {
 // entry point).
 //  * heads per tile: the largest of tune.heads_per_tile (default 8; 4 with
 //    RoPE: smaller workgroups of the register-heavier RoPE instances), 4,
-//    2, 1 dividing Hkv; halved (down to 2) for small problems.
+//    2, 1 dividing Hkv; halved (down to 2) for small problems; halved once
+//    more for uneven work (below, once the chunk is known).
 //  * chunk: the smallest multiple of the 16-token step, at least chunk_min,
 //    whose waves stay within num_cus * waves_per_cu (one round of resident
 //    waves), or the longest request when that is already enough work.
@@ -97,14 +99,14 @@ void decode_split(const PlanInput& in, int num_cus, bool rope, LenFn len, Reside
   const int64_t c_min = round_up(std::max(tune_or(in.tune.chunk_min, 32), kChunkAlign),
                                  kChunkAlign);
   if (!hpt_forced) {
-    // small problems (fewer than 4 tiles per CU even at the minimum chunk):
+    // small problems (fewer than 2 tiles per CU even at the minimum chunk):
     // fewer heads per tile, so more, smaller workgroups spread the latency
     auto tiles_at_min = [&](int h) {
       int64_t t = 0;
       for (int r = 0; r < B; ++r) t += std::max<int64_t>(1, ceil_div(len(r), c_min));
       return t * (Hkv / h);
     };
-    while (hpt > 2 && tiles_at_min(hpt) < 4 * (int64_t)num_cus) hpt >>= 1;
+    while (hpt > 2 && tiles_at_min(hpt) < 2 * (int64_t)num_cus) hpt >>= 1;
   }
   int64_t waves_per_cu = 16;
   if (in.tune.waves_per_cu > 0) {
@@ -146,6 +148,39 @@ void decode_split(const PlanInput& in, int num_cus, bool rope, LenFn len, Reside
     const double mean = (double)tokens * (Hkv / hpt) / slots;
     if (in.tune.waves_per_cu == 0 && (double)chunk > 1.25 * mean)
       chunk = chunk_for(2 * target_waves);
+  }
+  // Narrower tiles for uneven work.  Tiles run longest first and the
+  // hardware hands workgroups to the CUs in turn, so CU c runs tiles c,
+  // c + num_cus, ...; the CU holding the most bytes ends the kernel.  Tiles
+  // of half the kv heads cut the same chunks into twice as many workgroups,
+  // which evens that out when a few long requests dominate, at a measured
+  // cost of ~4 % per byte (each token's K/V rows of the tile are half as
+  // long a contiguous run).  They are taken when the modelled most-loaded
+  // CU, relative to the mean, drops by more than that (skewed128: 1.138 ->
+  // 1.076, step 217.7 -> 210.7 us; batch64_gqa4: 1.094 -> 1.064, 95.5 ->
+  // 96.6 us, kept at 8 heads).
+  if (!hpt_forced && !rope && hpt == kWavesPerTile && in.chunk_tokens == 0 &&
+      Hkv % (hpt / 2) == 0 && resident(hpt / 2) == resident(hpt)) {
+    std::vector<int64_t> steps;   // per (request, chunk): 16-token steps
+    for (int r = 0; r < B; ++r) {
+      const int64_t L = len(r);
+      if (L <= 0) continue;
+      const int64_t nc = ceil_div(L, chunk), nst = ceil_div(L, (int64_t)kChunkAlign);
+      for (int64_t c = 0; c < nc; ++c) steps.push_back(nst / nc + (c < nst % nc ? 1 : 0));
+    }
+    std::sort(steps.begin(), steps.end(), std::greater<int64_t>());
+    auto imbalance = [&](int h) {
+      std::vector<int64_t> load(num_cus, 0);
+      int64_t i = 0, total = 0;
+      for (int64_t st : steps)
+        for (int k = 0; k < Hkv / h; ++k, ++i) {
+          load[i % num_cus] += st * h;
+          total += st * h;
+        }
+      const int64_t mx = *std::max_element(load.begin(), load.end());
+      return total > 0 ? (double)mx * num_cus / (double)total : 1.0;
+    };
+    if (!steps.empty() && num_cus > 0 && imbalance(hpt / 2) * 1.04 < imbalance(hpt)) hpt /= 2;
   }
   *hpt_out = hpt;
   *chunk_out = chunk;
