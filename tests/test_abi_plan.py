@@ -580,3 +580,41 @@ def test_plan_sizes_skewed_batches_for_two_rounds(fi):
     indptr, last = _table(np.full(64, 2048))
     t = fi.debug_plan_tiles(indptr, last, num_qo_heads=32, num_kv_heads=8, page_size=16)
     assert max(int(x[3] - x[2]) for x in t if x[5] == 0) == 256
+
+
+def _roundrobin_imbalance(tiles, num_cus, hpt):
+    """Most-loaded CU over the mean when tile i runs on CU i mod num_cus,
+    load = 16-token steps x kv heads of the tile."""
+    d = [t for t in tiles if t[5] == 0]
+    load = np.zeros(num_cus)
+    for i, t in enumerate(d):
+        load[i % num_cus] += -(-(int(t[3]) - int(t[2])) // 16) * hpt
+    return load.max() / load.mean()
+
+
+def test_plan_narrows_tiles_for_uneven_work(fi):
+    """Four-head decode tiles when they even out the per-CU load by more than
+    their ~4 % per-byte cost: the skewed mix (a few 32K-token requests among
+    short ones) gets them, the uniform batch of 64 and the 32K batch keep
+    eight-head tiles, and a forced width or chunk is left alone."""
+    import workloads as W
+    want = {"skewed128": 4, "batch64_gqa4": 8, "long32_fp8": 8}
+    for name, hpt_want in want.items():
+        w = W.make(name, tables_only=True)
+        w = w[16] if isinstance(w, dict) else w
+        kw = dict(num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
+                  page_size=w.page_size, num_cus=256)
+        t = fi.debug_plan_tiles(w.kv_indptr, w.last_page_len, **kw)
+        hpt = _heads_per_tile(t, w.num_kv_heads)
+        assert hpt == hpt_want, (name, hpt)
+        _check_cover(t, _lens(w.kv_indptr, w.last_page_len, w.page_size), w.num_kv_heads, hpt)
+        t8 = fi.debug_plan_tiles(w.kv_indptr, w.last_page_len, tuning=dict(heads_per_tile=8), **kw)
+        assert _heads_per_tile(t8, w.num_kv_heads) == 8
+        i8, i4 = _roundrobin_imbalance(t8, 256, 8), _roundrobin_imbalance(
+            fi.debug_plan_tiles(w.kv_indptr, w.last_page_len, tuning=dict(heads_per_tile=4), **kw),
+            256, 4)
+        assert (i4 * 1.04 < i8) == (hpt_want == 4), (name, i8, i4)
+    w = W.make("skewed128", tables_only=True)
+    t = fi.debug_plan_tiles(w.kv_indptr, w.last_page_len, num_qo_heads=32, num_kv_heads=8,
+                            page_size=16, chunk_tokens=736)
+    assert _heads_per_tile(t, 8) == 8
