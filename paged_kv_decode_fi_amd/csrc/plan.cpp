@@ -49,6 +49,53 @@ int tune_or(int32_t v, int dflt) { return v != 0 ? v : dflt; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// Decode tiles for the dispatcher.  When every tile of a launch is resident
+// at once, the hardware hands workgroup i to CU i mod num_cus, so position
+// j * num_cus + c is CU c's j-th tile and the CU holding the most work ends
+// the kernel.  Longest processing time first: each tile, longest first,
+// goes to the least-loaded CU that still has a free position (ceil(n /
+// num_cus) positions for the first n mod num_cus CUs, one fewer for the
+// rest, so the positions are 0 .. n - 1).  w: work per tile, non-increasing.
+// Returns each tile's position in *pos (when pos != NULL) and the most
+// loaded CU's work over the mean.
+double dispatch_order(const std::vector<int64_t>& w, int num_cus, std::vector<int64_t>* pos) {
+  const int64_t n = (int64_t)w.size();
+  if (pos) pos->resize(n);
+  if (n == 0 || num_cus <= 0) return 1.0;
+  if (n <= num_cus) {   // one tile per CU: the order stays
+    if (pos)
+      for (int64_t i = 0; i < n; ++i) (*pos)[i] = i;
+    int64_t total = 0;
+    for (int64_t x : w) total += x;
+    return total > 0 ? (double)w[0] * num_cus / (double)total : 1.0;
+  }
+  const int64_t rounds = ceil_div(n, num_cus), full = n - (rounds - 1) * num_cus;
+  std::vector<int64_t> load(num_cus, 0), cnt(num_cus, 0);
+  // min-heap of (load, cu) over CUs with a free position
+  std::vector<std::pair<int64_t, int>> heap;
+  heap.reserve(num_cus);
+  for (int c = 0; c < num_cus; ++c) heap.push_back({0, c});
+  auto cmp = [](const std::pair<int64_t, int>& a, const std::pair<int64_t, int>& b) {
+    return a > b;
+  };
+  std::make_heap(heap.begin(), heap.end(), cmp);
+  int64_t total = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    std::pop_heap(heap.begin(), heap.end(), cmp);
+    const int c = heap.back().second;
+    heap.pop_back();
+    if (pos) (*pos)[i] = cnt[c] * num_cus + c;   // CU c's tiles stay longest first
+    load[c] += w[i];
+    total += w[i];
+    if (++cnt[c] < (c < full ? rounds : rounds - 1)) {
+      heap.push_back({load[c], c});
+      std::push_heap(heap.begin(), heap.end(), cmp);
+    }
+  }
+  const int64_t mx = *std::max_element(load.begin(), load.end());
+  return total > 0 ? (double)mx * num_cus / (double)total : 1.0;
+}
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // kv_len from a CSR page table row (ragged: last == NULL, indptr counts
@@ -169,16 +216,11 @@ void decode_split(const PlanInput& in, int num_cus, bool rope, LenFn len, Reside
       for (int64_t c = 0; c < nc; ++c) steps.push_back(nst / nc + (c < nst % nc ? 1 : 0));
     }
     std::sort(steps.begin(), steps.end(), std::greater<int64_t>());
-    auto imbalance = [&](int h) {
-      std::vector<int64_t> load(num_cus, 0);
-      int64_t i = 0, total = 0;
+    auto imbalance = [&](int h) {   // the tiles of h kv heads, as dispatch_order places them
+      std::vector<int64_t> w;
       for (int64_t st : steps)
-        for (int k = 0; k < Hkv / h; ++k, ++i) {
-          load[i % num_cus] += st * h;
-          total += st * h;
-        }
-      const int64_t mx = *std::max_element(load.begin(), load.end());
-      return total > 0 ? (double)mx * num_cus / (double)total : 1.0;
+        for (int k = 0; k < Hkv / h; ++k) w.push_back(st);
+      return dispatch_order(w, num_cus, nullptr);
     };
     if (!steps.empty() && num_cus > 0 && imbalance(hpt / 2) * 1.04 < imbalance(hpt)) hpt /= 2;
   }
@@ -707,6 +749,14 @@ int plan_build(const PlanInput& in, HostPlan* out, char* err, size_t errlen) {
   std::stable_sort(dt.begin(), dt.end(), [](const Tile& a, const Tile& b) {
     return (a.t1 - a.t0) > (b.t1 - b.t0);
   });
+  {
+    std::vector<int64_t> w(dt.size()), pos;
+    for (size_t i = 0; i < dt.size(); ++i) w[i] = dt[i].t1 - dt[i].t0;
+    dispatch_order(w, num_cus, &pos);
+    std::vector<Tile> placed(dt.size());
+    for (size_t i = 0; i < dt.size(); ++i) placed[pos[i]] = dt[i];
+    dt.swap(placed);
+  }
   // ---- prefix tiles, level by level: chunk-major, row tiles of one
   // (group, head, chunk) adjacent so they run together and share the chunk's
   // K/V in cache

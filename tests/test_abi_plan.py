@@ -229,9 +229,8 @@ def test_plan_covers_every_token_once(fi, seed, head_dim):
                                 page_size=ps, num_cus=[256, 32, 8, 256, 4, 1][seed],
                                 head_dim=head_dim)
     _check_cover(tiles, _lens(indptr, last, ps), Hkv, _heads_per_tile(tiles, Hkv))
-    # longest tiles first
-    d = [t[3] - t[2] for t in tiles if t[5] == 0]
-    assert d == sorted(d, reverse=True)
+    _check_dispatch_order([t[3] - t[2] for t in tiles if t[5] == 0],
+                          [256, 32, 8, 256, 4, 1][seed])
     # split requests: every (req, chunk, head) has its own slot; unsplit: -1
     slots = [t[4] for t in tiles if t[4] >= 0]
     assert len(slots) == len(set(slots))
@@ -240,6 +239,22 @@ def test_plan_covers_every_token_once(fi, seed, head_dim):
         if t[5] == 0:
             assert t[6] == indptr[t[0]]
     _check_even_split(tiles, _lens(indptr, last, ps))
+
+
+def _check_dispatch_order(d, num_cus):
+    """Decode tiles placed for in-order dispatch (tile i on CU i mod
+    num_cus): the first round holds the longest tiles, each CU's tiles run
+    longest first, and the most loaded CU carries no more than under plain
+    longest-first order."""
+    d = [int(x) for x in d]
+    n = len(d)
+    k = min(n, num_cus)
+    assert sorted(d[:k], reverse=True) == sorted(d, reverse=True)[:k]
+    cols = [d[c::num_cus] for c in range(num_cus)]
+    for col in cols:
+        assert col == sorted(col, reverse=True)
+    srt = sorted(d, reverse=True)
+    assert max(sum(col) for col in cols) <= max(sum(srt[c::num_cus]) for c in range(num_cus))
 
 
 def _check_even_split(tiles, lens, chunk=None):
