@@ -9,14 +9,16 @@
 //
 // Work model.  Each (request r, kv head h) has L_r keys.  A decode tile is one
 // workgroup of W waves = W consecutive kv heads of one request over one
-// token chunk [t0, t1) (W = 8 when Hkv allows, fewer for small problems).
+// token chunk [t0, t1) (W = 8 when Hkv allows; fewer for small problems,
+// and 4 where narrower tiles even out the load over the CUs).
 // The chunk length c is one value for the whole batch: the smallest
 // multiple of the 16-token step, at least c_min, such that the waves
 // launched stay within target = num_cus * waves_per_cu, one round of the
 // waves the launched instance keeps resident (more chunks than that only
 // adds partial states to merge) -- or two rounds when lengths are so skewed
 // that one round would leave the long requests' tiles running alone.
-// Tiles are emitted longest first so short tails fill in behind long tiles.
+// Tiles are placed for in-order dispatch (dispatch_order): the longest run
+// first and each CU's share of the work evens out.
 //
 // Cascade: the shared prefix of group g is attended once per (g, kv head) by
 // prefix tiles covering prefix_rows query rows each (rows = the group's
