@@ -325,8 +325,10 @@ __global__ __launch_bounds__(64 * kWavesPerTile) void decode_kernel(DecodeParams
   // QCVT: the wave's bf16 q times 2^qexp, chosen so that its largest
   // magnitude lands in [2^14, 2^15): every bf16 value (8 significant bits)
   // is then an exact fp16 value unless it lies more than 2^28 below that
-  // maximum (an fp16 subnormal, off by < 2^-39 of the maximum); the score
-  // scale takes the 2^-qexp back exactly
+  // maximum (an fp16 subnormal, off by < 2^-39 of the maximum); qexp is at
+  // most 64 (so the score scale stays a normal fp32 number): a wave whose
+  // q is all below 2^-49 lands in fp16 subnormals, each off by < 2^-89.
+  // The score scale takes the 2^-qexp back exactly
   int qexp = 0;
   if constexpr (QCVT) {
     float mx = 0.f;
