@@ -56,3 +56,19 @@ def test_occupancy_sized_plans_match_the_oracle(fi, rope):
     o, lse, plan = C.run_gpu(w, rope=r)
     ro, rl = C.run_oracle(w, rope=r)
     C.assert_parity(w, o, lse, ro, rl, label=f"occupancy plan rope={rope} {plan.stats}")
+
+
+def test_device_plans_choose_tile_width_by_load(fi):
+    """On the device (occupancy-sized wave targets) the skewed mix gets
+    four-head tiles and the uniform batch of 64 and the 32K batch keep
+    eight."""
+    want = {"skewed128": 4, "batch64_gqa4": 8, "long32_fp8": 8}
+    for name, hpt in want.items():
+        w = W.make(name, tables_only=True)
+        w = w[16] if isinstance(w, dict) else w
+        plan = fi.Plan(w.kv_indptr, w.last_page_len, num_qo_heads=w.num_qo_heads,
+                       num_kv_heads=w.num_kv_heads, page_size=w.page_size,
+                       q_dtype=w.q_dtype, kv_dtype=w.kv_dtype)
+        st = plan.stats
+        assert st["heads_per_tile"] == hpt, (name, st)
+        plan.destroy()
