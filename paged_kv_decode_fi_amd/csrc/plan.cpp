@@ -198,16 +198,16 @@ void decode_split(const PlanInput& in, int num_cus, bool rope, LenFn len, Reside
     if (in.tune.waves_per_cu == 0 && (double)chunk > 1.25 * mean)
       chunk = chunk_for(2 * target_waves);
   }
-  // Narrower tiles for uneven work.  Tiles run longest first and the
-  // hardware hands workgroups to the CUs in turn, so CU c runs tiles c,
-  // c + num_cus, ...; the CU holding the most bytes ends the kernel.  Tiles
+  // Narrower tiles for uneven work.  The hardware hands workgroups to the
+  // CUs in turn, so the tiles' placement (dispatch_order) decides how much
+  // work each CU holds, and the CU holding the most ends the kernel.  Tiles
   // of half the kv heads cut the same chunks into twice as many workgroups,
   // which evens that out when a few long requests dominate, at a measured
   // cost of ~4 % per byte (each token's K/V rows of the tile are half as
   // long a contiguous run).  They are taken when the modelled most-loaded
   // CU, relative to the mean, drops by more than that (skewed128: 1.138 ->
-  // 1.076, step 217.7 -> 210.7 us; batch64_gqa4: 1.094 -> 1.064, 95.5 ->
-  // 96.6 us, kept at 8 heads).
+  // 1.045, step 217.7 -> 210.7 us; batch64_gqa4: 1.094 -> 1.064, 95.5 ->
+  // 96.6 us measured, so kept at 8 heads).
   if (!hpt_forced && !rope && hpt == kWavesPerTile && in.chunk_tokens == 0 &&
       Hkv % (hpt / 2) == 0 && resident(hpt / 2) == resident(hpt)) {
     std::vector<int64_t> steps;   // per (request, chunk): 16-token steps
