@@ -262,21 +262,37 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 && D != 256 ? 2 : 1) void pr
     const uint32_t page = (uint32_t)ptab[pi - pfirst];
     return (uint64_t)page * p.page_bytes + sl * p.slot_stride;
   };
-  auto load = [&](int tb, u32x4 (&vec)[NL]) {
+  // byte offsets of this thread's NL vectors of the step at tb: the page
+  // lookup (an LDS read of the tile's page table) is taken a step before
+  // the loads that use it, so no step starts waiting on it
+  auto offs = [&](int tb, uint64_t (&o)[NL]) {
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
       const int idx = tid + u * T;
       if (2 * PV % T != 0 && idx >= 2 * PV) continue;
       const int q = idx % PV;
-      const int t = min(tb + q / VR, last);
-      const uint64_t off = row_off(t) + 16 * (q % VR);
-      vec[u] = ld_global<u32x4>(idx < PV ? kbase : vbase, off);
+      o[u] = row_off(min(tb + q / VR, last)) + 16 * (q % VR);
+    }
+  };
+  auto load_at = [&](int tb, const uint64_t (&o)[NL], u32x4 (&vec)[NL]) {
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int idx = tid + u * T;
+      if (2 * PV % T != 0 && idx >= 2 * PV) continue;
+      vec[u] = ld_global<u32x4>(idx < PV ? kbase : vbase, o[u]);
       if constexpr (REC) {
+        const int q = idx % PV;
         if (idx < PV)
-          p.rec[((p.rec_base[grp] + t) * p.Hkv + h) * VR + q % VR] =
-              (int64_t)(off + (uint64_t)h * p.head_stride);
+          p.rec[((p.rec_base[grp] + min(tb + q / VR, last)) * p.Hkv + h) * VR + q % VR] =
+              (int64_t)(o[u] + (uint64_t)h * p.head_stride);
       }
     }
+    (void)tb;
+  };
+  auto load = [&](int tb, u32x4 (&vec)[NL]) {
+    uint64_t o[NL];
+    offs(tb, o);
+    load_at(tb, o, vec);
   };
   auto load_rope = [&](int tb, RopeSet& st) {
 #pragma unroll
@@ -543,10 +559,19 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 && D != 256 ? 2 : 1) void pr
     }
   } else {
     load_set(t0 + kPStep, vb);
+    // (plain instances) offsets of the loads two steps ahead, looked up one
+    // step before they are issued
+    uint64_t on[NL];
+    if constexpr (!ROPE) offs(t0 + 2 * kPStep, on);
     __syncthreads();
     auto step_body = [&](int step, Set& nxt, Set& aft) {
       const int tb = t0 + kPStep * step;
-      load_set(tb + 2 * kPStep, aft);
+      if constexpr (ROPE) {
+        load_set(tb + 2 * kPStep, aft);
+      } else {
+        load_at(tb + 2 * kPStep, on, aft);
+        offs(tb + 3 * kPStep, on);
+      }
       if (tb < wave_hi) compute(tb, step & 1, tb + kPStep > wave_lo);
       store_set((step + 1) & 1, nxt);
       __syncthreads();
