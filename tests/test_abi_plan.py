@@ -633,3 +633,25 @@ def test_plan_narrows_tiles_for_uneven_work(fi):
     t = fi.debug_plan_tiles(w.kv_indptr, w.last_page_len, num_qo_heads=32, num_kv_heads=8,
                             page_size=16, chunk_tokens=736)
     assert _heads_per_tile(t, 8) == 8
+
+
+def test_cascade_suffix_tiles_are_dispatch_ordered(fi):
+    """The folded suffix tiles of the cascade workload (1,024 tiles of
+    uniform 128-512-key suffixes on 256 CUs) are placed for in-order
+    dispatch: longest first per CU column, the first round the longest
+    tiles, and the most loaded column well below plain longest-first order."""
+    import workloads as W
+    w = W.make("cascade256", tables_only=True)
+    t = fi.debug_plan_tiles(w.kv_indptr, w.last_page_len, num_qo_heads=w.num_qo_heads,
+                            num_kv_heads=w.num_kv_heads, page_size=w.page_size,
+                            q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, num_cus=256,
+                            prefix=(w.prefix_qo_indptr, w.prefix_kv_indptr,
+                                    w.prefix_last_page_len))
+    d = [int(x[3] - x[2]) for x in t if x[5] == 0]
+    assert len(d) == 1024
+    _check_dispatch_order(d, 256)
+    cols = [sum(d[c::256]) for c in range(256)]
+    srt = sorted(d, reverse=True)
+    rr = [sum(srt[c::256]) for c in range(256)]
+    mean = sum(d) / 256
+    assert max(cols) / mean < 1.03 < max(rr) / mean
